@@ -1,0 +1,254 @@
+/*
+ * rlt.h -- C ABI of the MI355X (gfx950) implementation of the Recurrent
+ * Looped Transformer's batched recurrent decoder state transition.
+ *
+ * Source of the operations: "Recurrent Looped Transformer" (Y. Zhang,
+ * technical report, 2026), cited as [RLT §x, eq. (y)].
+ *
+ *   H_t = (s_t, C_t^D) = D(Merge(e_t, s_{t-1}); M_{<=t}, C_{t-1}^D, t)
+ *                                                  [RLT §2.3, eqs. (2.4)-(2.5)]
+ *   p(x_{t+1} | x_{1:t}) = softmax(W_o RMSNorm_o(s_t))_{x_{t+1}}   [eq. (2.6)]
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers unless a field says HOST.
+ *  - The caller owns every buffer it passes; the library keeps the weight
+ *    pointers given to rlt_create (they must outlive the context) and owns
+ *    only its internal workspace.
+ *  - Calls enqueue work on `stream` (a hipStream_t passed as void*; NULL is
+ *    the default stream) and return without waiting for it, except where
+ *    a call says otherwise.
+ *  - Return value: RLT_OK (0) or a negative status below. Host-checkable
+ *    errors are returned before anything is enqueued. Errors the device
+ *    detects (a row whose memory is too short, a pending-token mismatch)
+ *    skip that row's update (its state is left unchanged), are recorded in
+ *    the context, and are returned by the first call made after the
+ *    detecting kernel completed (or by rlt_sync_error). No C++ exception
+ *    crosses this interface. rlt_last_error() gives a message.
+ *  - Element types: dtype RLT_BF16 means bfloat16 for weight matrices,
+ *    the SWA cache, encoder memory and e; RLT_F32 means float32 for all of
+ *    them. Gains, biases, s_star, the state s and all scores/log-probs are
+ *    always float32.
+ *  - Matrices use the natural [out][in] row-major layout (y = W x).
+ */
+#ifndef RLT_H
+#define RLT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  RLT_OK = 0,
+  RLT_EINVAL = -1,       /* null pointer or out-of-range argument */
+  RLT_ESHAPE = -2,       /* sizes inconsistent with the config or capacities */
+  RLT_EPREFIX = -3,      /* memory shorter than the position being consumed */
+  RLT_ESTALE = -4,       /* state version differs from the weights version */
+  RLT_EPENDING = -5,     /* consumed token differs from the pending token */
+  RLT_EHIP = -6,         /* HIP runtime failure */
+  RLT_ENOMEM = -7,       /* device allocation failed */
+  RLT_EUNSUPPORTED = -8  /* shape or option the kernels do not implement */
+};
+
+enum { RLT_F32 = 0, RLT_BF16 = 1 };
+enum { RLT_MERGE_GATED = 0, RLT_MERGE_CONVEX = 1 };
+enum { RLT_POS_NONE = 0, RLT_POS_ROPE = 1 };
+
+/* Model configuration.
+ * merge_kind GATED:  r = RMSNorm_s(s_{t-1}); g = sigmoid(W_g [e; r] + b_g);
+ *                    u = e + alpha * g (.) W_s r         [RLT §2.5, eqs. (2.9)-(2.11)]
+ * merge_kind CONVEX: g = sigmoid(W_g [e; s] + b_g); u = g (.) e + (1 - g) (.) s
+ * pos_kind ROPE: rotary transform (rotate-half pairing (i, i+dh/2), angle
+ *   t * rope_theta^(-2i/dh), t the 1-based position) inside the SWA query
+ *   and key maps and the cross-attention query map [RLT §2.5, text after
+ *   eq. (2.16): query/key maps include positional transformations].
+ * Supported shapes: d = n_heads * d_head; d_head in {16, 32, 64, 128}
+ * (16 only with RLT_F32); d, d_ffn, vocab multiples of 32; window >= 1;
+ * n_groups = 1 or n_layers (layer l reads group floor(l * G / L_D)). */
+typedef struct rlt_config {
+  int32_t n_layers;    /* L_D */
+  int32_t d_model;     /* d */
+  int32_t n_heads;     /* H */
+  int32_t d_head;      /* dh */
+  int32_t window;      /* W, includes the current token; cache keeps W-1 */
+  int32_t n_groups;    /* G */
+  int32_t d_ffn;       /* SwiGLU hidden width F */
+  int32_t vocab;       /* V */
+  int32_t merge_kind;  /* RLT_MERGE_* */
+  int32_t pos_kind;    /* RLT_POS_* */
+  int32_t dtype;       /* RLT_F32 | RLT_BF16 */
+  float alpha;         /* feedback scale of the gated merge */
+  float rms_eps;       /* RMSNorm: x / sqrt(mean(x^2) + eps) * gain */
+  float rope_theta;
+  uint64_t weights_version; /* states must carry the same version */
+} rlt_config;
+
+/* Parameters (device pointers, natural layout). Per-layer fields are HOST
+ * arrays of n_layers device pointers. */
+typedef struct rlt_weights {
+  const float* s_star;      /* [d]     learned initial state [RLT §2.3, eq. (2.3)] */
+  const float* merge_norm;  /* [d]     gain of RMSNorm_s (gated only) */
+  const void* merge_wg;     /* [d][2d] W_g, input [e; r] (gated) or [e; s] (convex) */
+  const float* merge_bg;    /* [d]     b_g */
+  const void* merge_ws;     /* [d][d]  W_s (gated only) */
+  const float* const* norm_s;  /* [d] gain of RMSNorm_{S,l}, feeds SWA q, k, v */
+  const void* const* wq;       /* [d][d] SWA query  [RLT §2.5, eq. (2.12)] */
+  const void* const* wk;       /* [d][d] SWA key    [eq. (2.13)] */
+  const void* const* wv;       /* [d][d] SWA value  [eq. (2.13)] */
+  const void* const* wo;       /* [d][d] SWA output projection [eq. (2.14)] */
+  const float* const* norm_m;  /* [d] gain of RMSNorm_{M,l} (cross query) */
+  const void* const* wqm;      /* [d][d] cross-attention query [eq. (2.15)] */
+  const void* const* wom;      /* [d][d] cross-attention output projection */
+  const float* const* norm_d;  /* [d] gain of RMSNorm_{D,l} [eq. (2.16)] */
+  const void* const* w_gate;   /* [F][d] */
+  const void* const* w_up;     /* [F][d] */
+  const void* const* w_down;   /* [d][F]: FFN(h) = W_down(silu(W_gate h) (.) W_up h) */
+  const float* out_norm;       /* [d]    gain of RMSNorm_o [eq. (2.6)] */
+  const void* w_out;           /* [V][d] W_o */
+} rlt_weights;
+
+/* Decoder state of B_cap independent rows [RLT §2.1: H_t = (s_t, C_t^D)].
+ * Sizes from rlt_state_layout. Row r after consuming t tokens:
+ *   s[r][0..d)                         s_t (float32)
+ *   pos[r] = t                         number of consumed tokens
+ *   pending[r]                         a sampled token recorded but not yet
+ *                                      consumed, or -1 [RLT App. A.2]
+ *   ring_k/ring_v[l][r][slot][0..d)    layer-l SWA keys/values of the
+ *                                      retained positions j = max(1,t-W+2)..t
+ *                                      at slot (j-1) mod (W-1); W-1 slots,
+ *                                      none when W = 1 [RLT §2.5]. */
+typedef struct rlt_state {
+  float* s;
+  void* ring_k;
+  void* ring_v;
+  int32_t* pos;
+  int32_t* pending;
+  int32_t B_cap;
+  uint64_t version;   /* must equal rlt_config.weights_version [RLT §5.4, §6] */
+} rlt_state;
+
+/* Encoder memory M_{<=t} [RLT §2.2, eq. (2.2)], read-only. Key of group g,
+ * state row r, position j (1-based) starts at element
+ *   k[g * stride_g + r * stride_b + (j - 1) * stride_t]   (likewise v)
+ * and holds d contiguous elements of the config dtype. Only positions
+ * j <= t are read at step t [RLT §4.2]; mem_len[r] (device) is the number
+ * of valid positions of row r; a step needing t > mem_len[r] is a
+ * device-detected RLT_EPREFIX. Strides are in elements. */
+typedef struct rlt_memory {
+  const void* k;
+  const void* v;
+  int64_t stride_g, stride_b, stride_t;
+  const int32_t* mem_len;
+} rlt_memory;
+
+/* One transition for a ready set of rows [RLT §4.1]. */
+enum { RLT_STEP_GRAPH = 1,  /* capture the step in a hipGraph on the first
+                               call with these exact arguments and replay it
+                               on later identical calls */
+       RLT_STEP_DEFER = 2   /* record the sampled (or argmax) token as the
+                               row's pending token [RLT App. A.2] */ };
+typedef struct rlt_step_io {
+  int32_t n;                 /* rows in this call, 0 < n <= max_rows */
+  const int32_t* rows;       /* [n] distinct state rows */
+  const void* e;             /* [n][d] e_t of the token each row consumes */
+  rlt_memory mem;
+  const int32_t* consume_tok;  /* [n] id of the consumed token, or NULL; must
+                                  equal pending[row] when that is >= 0 */
+  /* optional outputs (NULL = not produced) */
+  float* s_out;              /* [n][d]   s_t */
+  float* logits;             /* [n][V]   W_o RMSNorm_o(s_t) */
+  int32_t* argmax;           /* [n]      lowest id among the largest logits */
+  const int32_t* score_tok;  /* [n]      tokens to score ... */
+  float* logp;               /* [n]      ... log p(score_tok | x_{1:t}) */
+  /* behaviour sampler: tau, top-k truncation, renormalisation [RLT §5.3];
+     draw = first id in (logit desc, id asc) order whose cumulative weight
+     exp((z - z_max)/tau) exceeds u * total */
+  const float* uniform;      /* [n] u in [0,1), or NULL = no sampling */
+  float temperature;         /* tau > 0 */
+  int32_t top_k;             /* 1 .. 1024 */
+  int32_t* sample_tok;       /* [n] */
+  float* sample_logmu;       /* [n] log mu(sample_tok) */
+  float* z_trace;            /* [L_D][n][d] z after each block (debug), or NULL */
+  int32_t flags;             /* RLT_STEP_* */
+} rlt_step_io;
+
+/* Current-policy replay from H_0 [RLT App. A.4, eq. (2.7)]: for each
+ * sequence b, re-initialise its row, consume x_1 .. x_{len_b - 1} in order
+ * and, for split_b <= t <= len_b - 1, read log p(x_{t+1} | x_{1:t}) from s_t
+ * before x_{t+1} is consumed. x_{len_b} is left as the row's pending token.
+ * Sequences are advanced together; at tick t the active set is every b with
+ * len_b - 1 >= t. */
+typedef struct rlt_replay_io {
+  int32_t B;                   /* sequences */
+  const int32_t* rows_host;    /* HOST [B] state row of each sequence, or NULL = b */
+  const int32_t* len_host;     /* HOST [B] tokens x_1..x_len, 2 <= len */
+  const int32_t* split_host;   /* HOST [B] first scored position, 1 <= split */
+  const void* e;               /* e_t of sequence b at e[b*e_stride_b + (t-1)*e_stride_t] */
+  int64_t e_stride_b, e_stride_t;
+  rlt_memory mem;              /* indexed by state row */
+  const int32_t* tokens;       /* x_t of sequence b at tokens[b*tok_stride_b + t-1] */
+  int64_t tok_stride_b;
+  float* logp;                 /* logp[b*logp_stride_b + t] = log p(x_{t+1}|x_{1:t}) */
+  int64_t logp_stride_b;
+  float* s_trace;              /* optional: s_t at s_trace[(b*s_stride_b) + (t-1)*d] */
+  int64_t s_stride_b;
+} rlt_replay_io;
+
+/* Scoring of given states [RLT §5.3, eq. (5.5)]: raw log-probabilities of
+ * given tokens and, optionally, their behaviour log-probabilities under
+ * (tau, top-k) and the ratios exp(log p - log mu_behaviour). */
+typedef struct rlt_score_io {
+  int32_t n;
+  const float* s;            /* [n][d] states s_t */
+  const int32_t* tokens;     /* [n] */
+  float* logp;               /* [n] log p_Theta(token) */
+  float temperature;         /* used when logmu != NULL */
+  int32_t top_k;             /* 0 = no truncation; else 1 .. 1024 */
+  float* logmu;              /* [n] log mu(token) under (tau, top_k), -inf off-support; or NULL */
+  const float* logmu_behaviour; /* [n] recorded behaviour log-probs, or NULL */
+  float* ratio;              /* [n] exp(logp - logmu_behaviour), or NULL */
+} rlt_score_io;
+
+typedef struct rlt_ctx rlt_ctx;
+
+/* Create a context on the current HIP device. Validates the config,
+ * precomputes position tables and allocates workspace for up to max_rows
+ * rows per call and memory prefixes up to max_ctx positions. */
+int rlt_create(const rlt_config* cfg, const rlt_weights* w, int32_t max_rows, int32_t max_ctx,
+               rlt_ctx** out);
+void rlt_destroy(rlt_ctx* ctx);
+
+/* HOST: bytes of the five state buffers for B_cap rows, in the order
+ * s, ring_k, ring_v, pos, pending. */
+int rlt_state_layout(const rlt_config* cfg, int32_t B_cap, size_t bytes_out[5]);
+
+/* Message of the last error on the calling thread (static storage). */
+const char* rlt_last_error(void);
+
+/* H_0 = (s_star, empty) for the given rows [RLT §2.3, eq. (2.3)]: s = s_star,
+ * pos = 0, pending = -1. rows: device [n]. flags bit 1 (RLT_INIT_POISON)
+ * fills the rows' cache slots with NaN (any read of a slot outside the
+ * window then shows in the outputs). */
+enum { RLT_INIT_POISON = 1 };
+int rlt_init_state(rlt_ctx* ctx, rlt_state* st, const int32_t* rows, int32_t n, int32_t flags,
+                   void* stream);
+
+/* One transition F_t for each listed row, t = pos[row] + 1, then the
+ * readout and optional scoring/sampling from s_t. Advances pos[row]. */
+int rlt_decoder_step(rlt_ctx* ctx, rlt_state* st, const rlt_step_io* io, void* stream);
+
+/* See rlt_replay_io. Synchronises the stream once at the start (upload of
+ * the schedule). */
+int rlt_replay_sequence(rlt_ctx* ctx, rlt_state* st, const rlt_replay_io* io, void* stream);
+
+int rlt_score_logprobs(rlt_ctx* ctx, const rlt_score_io* io, void* stream);
+
+/* Wait for `stream`, then return (and clear) any device-detected error. */
+int rlt_sync_error(rlt_ctx* ctx, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RLT_H */

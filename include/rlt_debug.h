@@ -1,0 +1,30 @@
+/*
+ * rlt_debug.h -- test-only entry point for kernel-level parity checks of the
+ * library's matrix-product kernel (the kernel behind every projection of
+ * "Recurrent Looped Transformer" §2.5 eqs. (2.9)-(2.16) and the readout of
+ * §2.3 eq. (2.6)). Not part of the method's interface.
+ */
+#ifndef RLT_DEBUG_H
+#define RLT_DEBUG_H
+
+#include <stdint.h>
+
+#include "rlt.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* out[m][n] = sum_k A[m][k] * W[n][k] for m < M, n < N (float32 output),
+ * computed by the same kernel, K split and reduction order the decoder step
+ * uses for an M-row call. A [M][K] and W [N][K] are device buffers of the
+ * context's dtype; out is a device [M][N] float32 buffer. Requires
+ * 1 <= M <= max_rows, N and K multiples of 32, K <= 2 * d_model.
+ * Enqueued on `stream`; returns RLT_ESHAPE / RLT_EINVAL on bad sizes. */
+int rlt_dbg_gemm(rlt_ctx* ctx, const void* A, const void* W, int32_t M, int32_t N, int32_t K, float* out,
+                 void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RLT_DEBUG_H */

@@ -1,0 +1,343 @@
+// Attention kernels of the decoder block ("Recurrent Looped Transformer",
+// §2.5 eqs. (2.14)-(2.15) and the cache rule after eq. (2.16)).
+//
+// Both attentions are one query per (row, head) against stored keys/values,
+// i.e. streaming work of about 1 flop per byte: they are bound by HBM
+// bandwidth, so they run on the vector ALU (no MFMA) and are organised for
+// coalesced, contiguous reads:
+//   * a workgroup handles one row and `hpw` consecutive heads, so every key
+//     read is hpw*dh contiguous elements;
+//   * each lane owns E consecutive elements (32 bytes) of one head; the
+//     dh/E lanes of a head reduce the q.k dot with xor-shuffles (all lanes
+//     end with the identical sum);
+//   * the 256 threads form 256/(hpw*dh/E) key groups that walk the keys with
+//     an online softmax (base-2, the log2(e)/sqrt(dh) scale folded into q),
+//     and the groups' (max, sum, output) partials are merged in LDS in group
+//     order. Every order is fixed, so results do not depend on timing.
+//
+// SWA (eq. 2.14): keys are the retained positions max(1, t-W+1) .. t-1 from
+// the ring (slot (j-1) mod (W-1)) plus the current (k, v); after all reads
+// of the workgroup the current (k, v) is written to slot (t-1) mod (W-1),
+// the slot of position t-W+1 which leaves the window (nothing else reads
+// those columns of this row).
+// Cross-attention (eq. 2.15): keys are memory positions 1..t only; the
+// range is split into chunks of `chunk` positions (boundaries depend on t
+// only), each chunk writes an unnormalised (o, max, sum) partial, and a
+// combine kernel merges the chunks in chunk order.
+#include "rlt_internal.h"
+
+namespace rlt {
+
+template <typename T> struct LaneVec;
+template <> struct LaneVec<uint16_t> {
+  static constexpr int E = 16;
+  __device__ static __forceinline__ void load(const uint16_t* p, float* f) {
+    const uint4 a = *(const uint4*)p, b = *(const uint4*)(p + 8);
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ static __forceinline__ void store(uint16_t* p, const float* f) {
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = (uint32_t)f2bf(f[2 * i]) | ((uint32_t)f2bf(f[2 * i + 1]) << 16);
+    *(uint4*)p = make_uint4(w[0], w[1], w[2], w[3]);
+    *(uint4*)(p + 8) = make_uint4(w[4], w[5], w[6], w[7]);
+  }
+  __device__ static __forceinline__ void copy(uint16_t* d, const uint16_t* s) {
+    *(uint4*)d = *(const uint4*)s;
+    *(uint4*)(d + 8) = *(const uint4*)(s + 8);
+  }
+};
+template <> struct LaneVec<float> {
+  static constexpr int E = 8;
+  __device__ static __forceinline__ void load(const float* p, float* f) {
+    const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  }
+  __device__ static __forceinline__ void store(float* p, const float* f) {
+    *(float4*)p = make_float4(f[0], f[1], f[2], f[3]);
+    *(float4*)(p + 4) = make_float4(f[4], f[5], f[6], f[7]);
+  }
+  __device__ static __forceinline__ void copy(float* d, const float* s) {
+    *(float4*)d = *(const float4*)s;
+    *(float4*)(d + 4) = *(const float4*)(s + 4);
+  }
+};
+
+// online-softmax accumulator of one lane (E output elements)
+template <int E>
+struct Acc {
+  float m, l, o[E];
+  __device__ __forceinline__ void init() {
+    m = -INFINITY;
+    l = 0.f;
+#pragma unroll
+    for (int i = 0; i < E; ++i) o[i] = 0.f;
+  }
+  __device__ __forceinline__ void add(float s, const float* v) {
+    const float mn = fmaxf(m, s);
+    const float c = exp2f(m - mn);
+    const float p = exp2f(s - mn);
+    l = l * c + p;
+#pragma unroll
+    for (int i = 0; i < E; ++i) o[i] = fmaf(p, v[i], o[i] * c);
+    m = mn;
+  }
+};
+
+template <int LPK>
+__device__ __forceinline__ float group_sum(float s) {
+#pragma unroll
+  for (int off = 1; off < LPK; off <<= 1) s += __shfl_xor(s, off);
+  return s;
+}
+
+// Merge the key groups' partials of the workgroup (fixed group order).
+// Returns true on the lanes of key group 0, which then hold the merged
+// (m, l, o) of their (head, element range).
+template <int E>
+__device__ __forceinline__ bool merge_groups(Acc<E>& acc, int kg, int G, int KPW, float* s_o,
+                                             float* s_ml) {
+  const int li = threadIdx.x - kg * G;  // lane index within the key group
+#pragma unroll
+  for (int i = 0; i < E; ++i) s_o[threadIdx.x * E + i] = acc.o[i];
+  s_ml[2 * threadIdx.x] = acc.m;
+  s_ml[2 * threadIdx.x + 1] = acc.l;
+  __syncthreads();
+  if (kg != 0) return false;
+  float M = -INFINITY;
+  for (int g = 0; g < KPW; ++g) M = fmaxf(M, s_ml[2 * (g * G + li)]);
+  float L = 0.f, o[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) o[i] = 0.f;
+  for (int g = 0; g < KPW; ++g) {
+    const int th = g * G + li;
+    const float w = exp2f(s_ml[2 * th] - M);
+    L += s_ml[2 * th + 1] * w;
+#pragma unroll
+    for (int i = 0; i < E; ++i) o[i] = fmaf(s_o[th * E + i], w, o[i]);
+  }
+  acc.m = M;
+  acc.l = L;
+#pragma unroll
+  for (int i = 0; i < E; ++i) acc.o[i] = o[i];
+  return true;
+}
+
+// grid: x = slot, y = head group; block 256
+template <typename T, int DH>
+__global__ __launch_bounds__(256) void k_swa(AttnArgs a) {
+  using LV = LaneVec<T>;
+  constexpr int E = LV::E;
+  constexpr int LPK = DH / E;
+  __shared__ float s_o[256 * E];
+  __shared__ float s_ml[512];
+  const int slot = blockIdx.x;
+  const int t = a.rows.t_row[slot];
+  if (t <= 0) return;
+  const int row = a.rows.rows[slot];
+  const int G = a.hpw * LPK;
+  const int KPW = 256 / G;
+  const int kg = threadIdx.x / G;
+  const int hh = (threadIdx.x % G) / LPK;
+  const int jl = threadIdx.x % LPK;
+  const int col = (blockIdx.y * a.hpw + hh) * DH + jl * E;
+  const int d = a.d;
+
+  float q[E];
+  {
+    const float* qp = a.q + (int64_t)slot * d + col;
+#pragma unroll
+    for (int i = 0; i < E; ++i) q[i] = qp[i] * a.qscale;
+  }
+  const int W1 = a.W - 1;
+  const int nh = min(t - 1, W1);
+  const int nkeys = nh + 1;
+  const T* rk = (const T*)a.ring_k + (int64_t)row * W1 * d + col;
+  const T* rv = (const T*)a.ring_v + (int64_t)row * W1 * d + col;
+  const T* ck = (const T*)a.kc + (int64_t)slot * d + col;
+  const T* cv = (const T*)a.vc + (int64_t)slot * d + col;
+
+  Acc<E> acc;
+  acc.init();
+  if (kg < KPW) {
+    for (int r = kg; r < nkeys; r += KPW) {
+      const T *kp, *vp;
+      if (r < nh) {
+        const int j = t - nh + r;                 // absolute position
+        const int sl = (j - 1) % W1;
+        kp = rk + (int64_t)sl * d;
+        vp = rv + (int64_t)sl * d;
+      } else {
+        kp = ck;
+        vp = cv;
+      }
+      float kf[E], vf[E];
+      LV::load(kp, kf);
+      LV::load(vp, vf);
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < E; ++i) s = fmaf(q[i], kf[i], s);
+      s = group_sum<LPK>(s);
+      acc.add(s, vf);
+    }
+  }
+  const bool lead = merge_groups<E>(acc, kg, G, KPW, s_o, s_ml);
+  if (lead) {
+    const float inv = 1.f / acc.l;
+    float o[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) o[i] = acc.o[i] * inv;
+    LV::store((T*)a.out + (int64_t)slot * d + col, o);
+  }
+  // cache insert after every read of this workgroup
+  __syncthreads();
+  if (W1 > 0 && kg == 0) {
+    const int sl = (t - 1) % W1;
+    LV::copy((T*)a.ring_k + ((int64_t)row * W1 + sl) * d + col, ck);
+    LV::copy((T*)a.ring_v + ((int64_t)row * W1 + sl) * d + col, cv);
+  }
+}
+
+// grid: x = slot, y = chunk, z = head group; block 256
+template <typename T, int DH>
+__global__ __launch_bounds__(256) void k_xattn(AttnArgs a) {
+  using LV = LaneVec<T>;
+  constexpr int E = LV::E;
+  constexpr int LPK = DH / E;
+  __shared__ float s_o[256 * E];
+  __shared__ float s_ml[512];
+  const int slot = blockIdx.x;
+  const int t = a.rows.t_row[slot];
+  const int j0 = blockIdx.y * a.chunk;
+  if (t <= 0 || j0 >= t) return;
+  const int j1 = min(j0 + a.chunk, t);
+  const int row = a.rows.rows[slot];
+  const int G = a.hpw * LPK;
+  const int KPW = 256 / G;
+  const int kg = threadIdx.x / G;
+  const int hh = (threadIdx.x % G) / LPK;
+  const int jl = threadIdx.x % LPK;
+  const int head = blockIdx.z * a.hpw + hh;
+  const int col = head * DH + jl * E;
+  const int d = a.d;
+
+  float q[E];
+  {
+    const float* qp = a.q + (int64_t)slot * d + col;
+#pragma unroll
+    for (int i = 0; i < E; ++i) q[i] = qp[i] * a.qscale;
+  }
+  const T* mk = (const T*)a.mk + (int64_t)row * a.sb + col;
+  const T* mv = (const T*)a.mv + (int64_t)row * a.sb + col;
+
+  Acc<E> acc;
+  acc.init();
+  if (kg < KPW) {
+    int r = j0 + kg;
+    // two keys per iteration: both loads issued before the math
+    for (; r + KPW < j1; r += 2 * KPW) {
+      float k0[E], v0[E], k1[E], v1[E];
+      LV::load(mk + (int64_t)r * a.st, k0);
+      LV::load(mv + (int64_t)r * a.st, v0);
+      LV::load(mk + (int64_t)(r + KPW) * a.st, k1);
+      LV::load(mv + (int64_t)(r + KPW) * a.st, v1);
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        s0 = fmaf(q[i], k0[i], s0);
+        s1 = fmaf(q[i], k1[i], s1);
+      }
+      s0 = group_sum<LPK>(s0);
+      s1 = group_sum<LPK>(s1);
+      acc.add(s0, v0);
+      acc.add(s1, v1);
+    }
+    if (r < j1) {
+      float k0[E], v0[E];
+      LV::load(mk + (int64_t)r * a.st, k0);
+      LV::load(mv + (int64_t)r * a.st, v0);
+      float s0 = 0.f;
+#pragma unroll
+      for (int i = 0; i < E; ++i) s0 = fmaf(q[i], k0[i], s0);
+      s0 = group_sum<LPK>(s0);
+      acc.add(s0, v0);
+    }
+  }
+  const bool lead = merge_groups<E>(acc, kg, G, KPW, s_o, s_ml);
+  if (lead) {
+    float* P = a.part + (((int64_t)slot * a.nch + blockIdx.y) * a.H + head) * (DH + 2);
+#pragma unroll
+    for (int i = 0; i < E; ++i) P[jl * E + i] = acc.o[i];
+    if (jl == 0) {
+      P[DH] = acc.m;
+      P[DH + 1] = acc.l;
+    }
+  }
+}
+
+// grid: x = slot, y = head; block 64
+template <typename T, int DH>
+__global__ __launch_bounds__(64) void k_xcombine(AttnArgs a) {
+  const int slot = blockIdx.x, head = blockIdx.y;
+  const int t = a.rows.t_row[slot];
+  if (t <= 0) return;
+  const int nc = (t + a.chunk - 1) / a.chunk;
+  const float* P = a.part + ((int64_t)slot * a.nch * a.H + head) * (DH + 2);
+  const int64_t cs = (int64_t)a.H * (DH + 2);  // chunk stride
+  float M = -INFINITY;
+  for (int c = 0; c < nc; ++c) M = fmaxf(M, P[c * cs + DH]);
+  float L = 0.f;
+  for (int c = 0; c < nc; ++c) L += P[c * cs + DH + 1] * exp2f(P[c * cs + DH] - M);
+  const float inv = 1.f / L;
+  T* out = (T*)a.out + (int64_t)slot * a.d + head * DH;
+  for (int e = threadIdx.x; e < DH; e += 64) {
+    float o = 0.f;
+    for (int c = 0; c < nc; ++c) o = fmaf(P[c * cs + e], exp2f(P[c * cs + DH] - M), o);
+    out[e] = from_f<T>(o * inv);
+  }
+}
+
+template <typename T, int DH>
+static void swa_t(const AttnArgs& a, hipStream_t s) {
+  dim3 grid(a.rows.n, a.H / a.hpw);
+  hipLaunchKernelGGL((k_swa<T, DH>), grid, dim3(256), 0, s, a);
+}
+template <typename T, int DH>
+static void xattn_t(const AttnArgs& a, hipStream_t s) {
+  dim3 grid(a.rows.n, a.nch, a.H / a.hpw);
+  hipLaunchKernelGGL((k_xattn<T, DH>), grid, dim3(256), 0, s, a);
+}
+template <typename T, int DH>
+static void xcomb_t(const AttnArgs& a, hipStream_t s) {
+  dim3 grid(a.rows.n, a.H);
+  hipLaunchKernelGGL((k_xcombine<T, DH>), grid, dim3(64), 0, s, a);
+}
+
+#define RLT_DISPATCH_DH(FN, T, a, s)            \
+  switch ((a).dh) {                             \
+    case 16: FN<T, 16>(a, s); break;            \
+    case 32: FN<T, 32>(a, s); break;            \
+    case 64: FN<T, 64>(a, s); break;            \
+    default: FN<T, 128>(a, s); break;           \
+  }
+
+void launch_swa(int dtype, const AttnArgs& a, hipStream_t s) {
+  if (dtype == 0) { RLT_DISPATCH_DH(swa_t, float, a, s); }
+  else { RLT_DISPATCH_DH(swa_t, uint16_t, a, s); }
+}
+void launch_xattn(int dtype, const AttnArgs& a, hipStream_t s) {
+  if (dtype == 0) { RLT_DISPATCH_DH(xattn_t, float, a, s); }
+  else { RLT_DISPATCH_DH(xattn_t, uint16_t, a, s); }
+}
+void launch_xcombine(int dtype, const AttnArgs& a, hipStream_t s) {
+  if (dtype == 0) { RLT_DISPATCH_DH(xcomb_t, float, a, s); }
+  else { RLT_DISPATCH_DH(xcomb_t, uint16_t, a, s); }
+}
+
+}  // namespace rlt

@@ -1,0 +1,273 @@
+// Matrix products of the decoder transition with fused epilogues.
+//
+// Every projection of the step is Y = A W^T with A the [rows][K] activations
+// and W a natural-layout [out][in] weight ("Recurrent Looped Transformer",
+// §2.5 eqs. (2.9)-(2.16) and §2.3 eq. (2.6)). Weights are streamed once per
+// call; the batch is the M dimension, so these products are HBM-bound for
+// the batch sizes of a decoder step.
+//
+// bf16 path (gfx950 MFMA v_mfma_f32_16x16x32_bf16):
+//   workgroup = 4 waves; all 4 waves own the same output tile (16*MB rows x
+//   one pair of 16-column blocks) and each streams a disjoint quarter of the
+//   workgroup's K range, so A and W are each read once per workgroup; the
+//   four partial tiles are summed in LDS in wave order. Optional split of K
+//   across S workgroups writes partial tiles that a second kernel sums in
+//   split order. Both orders are fixed, so results are deterministic.
+//   Accumulation is fp32; A (activations) arrive rounded to bf16.
+// fp32 path: one thread per output pair, sequential K loop (used by the
+//   float32 configuration, where precision rather than speed is the point).
+//
+// Output columns are handled as pairs of 16-column blocks so that epilogues
+// needing two columns of the same row see both in one lane: the rotary
+// transform pairs column i with i + dh/2 of the same head, SwiGLU pairs a
+// gate column with its up column.
+#include "rlt_internal.h"
+
+namespace rlt {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+template <typename T>
+struct Epi {
+  EpiArgs a;
+
+  __device__ __forceinline__ float e_at(int m, int c) const {
+    const int t = a.rows.t_row[m];
+    if (t <= 0) return 0.f;
+    const T* p = (const T*)a.e.p + (int64_t)a.rows.src[m] * a.e.sb + (int64_t)(t - 1) * a.e.st;
+    return to_f<T>(p[c]);
+  }
+
+  // rotary transform of the pair (x_i, x_{i+dh/2}) of one head at position t
+  __device__ __forceinline__ void rotate(int m, int c_in_head, float& x, float& y) const {
+    const int t = a.rows.t_row[m];
+    double sn, cs;
+    sincos((double)t * a.inv_freq[c_in_head], &sn, &cs);
+    const float c = (float)cs, s = (float)sn;
+    const float xr = x * c - y * s;
+    const float yr = y * c + x * s;
+    x = xr;
+    y = yr;
+  }
+
+  __device__ __forceinline__ void operator()(int m, int ca, float va, int cb, float vb) const {
+    switch (a.kind) {
+      case EPI_STORE:
+        a.out_f[(int64_t)m * a.ldo + ca] = va;
+        a.out_f[(int64_t)m * a.ldo + cb] = vb;
+        break;
+      case EPI_QKV: {
+        const int seg = ca / a.d;
+        const int xa = ca - seg * a.d, xb = cb - seg * a.d;
+        if (seg < 2 && a.rope) rotate(m, xa % a.dh, va, vb);
+        const int64_t o = (int64_t)m * a.d;
+        if (seg == 0) {
+          a.out_f[o + xa] = va;
+          a.out_f[o + xb] = vb;
+        } else {
+          T* dst = (T*)(seg == 1 ? a.out_k : a.out_v);
+          dst[o + xa] = from_f<T>(va);
+          dst[o + xb] = from_f<T>(vb);
+        }
+        break;
+      }
+      case EPI_QROT: {
+        if (a.rope) rotate(m, ca % a.dh, va, vb);
+        a.out_f[(int64_t)m * a.d + ca] = va;
+        a.out_f[(int64_t)m * a.d + cb] = vb;
+        break;
+      }
+      case EPI_RESID: {
+        float* z = a.out_f + (int64_t)m * a.ldo;
+        z[ca] += va;
+        z[cb] += vb;
+        break;
+      }
+      case EPI_SWIGLU: {
+        const float act = va * sigmoidf_(va) * vb;
+        ((T*)a.out_k)[(int64_t)m * a.ldo + ca] = from_f<T>(act);
+        break;
+      }
+      case EPI_MGATE: {
+        float* g = a.out_f + (int64_t)m * a.ldo;
+        g[ca] = sigmoidf_(va + a.bias[ca]);
+        g[cb] = sigmoidf_(vb + a.bias[cb]);
+        break;
+      }
+      case EPI_MOUT: {
+        float* z = a.out_f + (int64_t)m * a.ldo;
+        const float* g = a.gbuf + (int64_t)m * a.ldo;
+        z[ca] = e_at(m, ca) + a.alpha * g[ca] * va;
+        z[cb] = e_at(m, cb) + a.alpha * g[cb] * vb;
+        break;
+      }
+      case EPI_CONVEX: {
+        if (a.rows.t_row[m] <= 0) break;
+        float* z = a.out_f + (int64_t)m * a.ldo;
+        const float* s = a.s_state + (int64_t)a.rows.rows[m] * a.d;
+        const float ga = sigmoidf_(va + a.bias[ca]);
+        const float gb = sigmoidf_(vb + a.bias[cb]);
+        z[ca] = ga * e_at(m, ca) + (1.f - ga) * s[ca];
+        z[cb] = gb * e_at(m, cb) + (1.f - gb) * s[cb];
+        break;
+      }
+      default:
+        break;
+    }
+  }
+};
+
+template <typename T>
+__device__ __forceinline__ const T* weight_row(const GemmArgs& g, int vc) {
+  const int seg = vc / g.seg_rows;
+  const int r = vc - seg * g.seg_rows;
+  return (const T*)g.W[seg] + (int64_t)r * g.K;
+}
+
+__device__ __forceinline__ bf16x8_t load8(const uint16_t* p) {
+  const uint4 u = *(const uint4*)p;
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
+// grid: x = pair, y = split, z = m-tile; block 256 (4 waves)
+template <int MB>
+__global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs g, Epi<uint16_t> epi) {
+  __shared__ float red[4][MB * 16][32];
+  const int pair = blockIdx.x, split = blockIdx.y, mt = blockIdx.z;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int ba, bb;
+  pair_blocks(g, pair, ba, bb);
+  const int r16 = lane & 15;
+  const int kq = (lane >> 4) * 8;
+  const uint16_t* wa = weight_row<uint16_t>(g, ba * 16 + r16) + kq;
+  const uint16_t* wb = weight_row<uint16_t>(g, bb * 16 + r16) + kq;
+  const int m0 = mt * MB * 16;
+  const uint16_t* ap[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+    ap[mb] = (const uint16_t*)g.A + (int64_t)(m0 + mb * 16 + r16) * g.lda + kq;
+
+  f32x4_t acc[MB][2];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    acc[mb][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    acc[mb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  const int k0 = (split * 4 + wave) * g.kslice;
+  const int k1 = min(k0 + g.kslice, g.K);
+  for (int kb = k0; kb < k1; kb += 32) {
+    const bf16x8_t b0 = load8(wa + kb);
+    const bf16x8_t b1 = load8(wb + kb);
+    bf16x8_t av[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) av[mb] = load8(ap[mb] + kb);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      acc[mb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mb], b0, acc[mb][0], 0, 0, 0);
+      acc[mb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mb], b1, acc[mb][1], 0, 0, 0);
+    }
+  }
+  // C layout: lane holds rows 4*(lane/16)+i, column lane%16
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      red[wave][mb * 16 + (lane >> 4) * 4 + i][r16] = acc[mb][0][i];
+      red[wave][mb * 16 + (lane >> 4) * 4 + i][16 + r16] = acc[mb][1][i];
+    }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < MB * 16 * 16; idx += 256) {
+    const int m = idx >> 4, r = idx & 15;
+    const int slot = m0 + m;
+    const float va = ((red[0][m][r] + red[1][m][r]) + red[2][m][r]) + red[3][m][r];
+    const float vb = ((red[0][m][16 + r] + red[1][m][16 + r]) + red[2][m][16 + r]) + red[3][m][16 + r];
+    if (g.S == 1) {
+      if (slot < g.M) epi(slot, ba * 16 + r, va, bb * 16 + r, vb);
+    } else if (slot < g.M) {
+      float* P = g.partial + ((int64_t)split * g.M_pad + slot) * g.Nv;
+      P[ba * 16 + r] = va;
+      P[bb * 16 + r] = vb;
+    }
+  }
+}
+
+// sum of the S split partials in split order, then the epilogue
+// grid: x = pair, y = ceil(M/16); block 256
+template <typename T>
+__global__ __launch_bounds__(256) void k_splitk_epi(GemmArgs g, Epi<T> epi) {
+  int ba, bb;
+  pair_blocks(g, blockIdx.x, ba, bb);
+  const int m = blockIdx.y * 16 + (threadIdx.x >> 4), r = threadIdx.x & 15;
+  if (m >= g.M) return;
+  float va = 0.f, vb = 0.f;
+  for (int s = 0; s < g.S; ++s) {
+    const float* P = g.partial + ((int64_t)s * g.M_pad + m) * g.Nv;
+    va += P[ba * 16 + r];
+    vb += P[bb * 16 + r];
+  }
+  epi(m, ba * 16 + r, va, bb * 16 + r, vb);
+}
+
+// fp32: one thread per (row, column pair); columns paired per element:
+// rotary pairs (i, i+dh/2) of a head, gate/up pairs, or adjacent columns.
+__device__ __forceinline__ void pair_cols(const GemmArgs& g, int q, int& ca, int& cb) {
+  if (g.pairing == PAIR_PLAIN) {
+    ca = 2 * q;
+    cb = 2 * q + 1;
+  } else if (g.pairing == PAIR_ROPE) {
+    const int half = g.dh / 2;
+    const int h = q / half, i = q - h * half;
+    ca = h * g.dh + i;
+    cb = ca + half;
+  } else {
+    ca = q;
+    cb = q + g.seg_rows;
+  }
+}
+
+// grid: x = ceil(Nv/2 / 64), y = row; block 64
+__global__ __launch_bounds__(64) void k_gemm_f32(GemmArgs g, Epi<float> epi) {
+  const int q = blockIdx.x * 64 + threadIdx.x;
+  const int m = blockIdx.y;
+  if (q >= g.Nv / 2 || m >= g.M) return;
+  int ca, cb;
+  pair_cols(g, q, ca, cb);
+  const float* a = (const float*)g.A + (int64_t)m * g.lda;
+  const float* wa = weight_row<float>(g, ca);
+  const float* wb = weight_row<float>(g, cb);
+  float sa = 0.f, sb = 0.f;
+  for (int k = 0; k < g.K; k += 4) {
+    const float4 x = *(const float4*)(a + k);
+    const float4 p = *(const float4*)(wa + k);
+    const float4 r = *(const float4*)(wb + k);
+    sa = fmaf(x.x, p.x, sa); sa = fmaf(x.y, p.y, sa); sa = fmaf(x.z, p.z, sa); sa = fmaf(x.w, p.w, sa);
+    sb = fmaf(x.x, r.x, sb); sb = fmaf(x.y, r.y, sb); sb = fmaf(x.z, r.z, sb); sb = fmaf(x.w, r.w, sb);
+  }
+  epi(m, ca, sa, cb, sb);
+}
+
+void launch_gemm(int dtype, const GemmArgs& g0, const EpiArgs& e, hipStream_t s) {
+  GemmArgs g = g0;
+  if (dtype == 0) {
+    dim3 grid((g.Nv / 2 + 63) / 64, g.M);
+    hipLaunchKernelGGL(k_gemm_f32, grid, dim3(64), 0, s, g, Epi<float>{e});
+    return;
+  }
+  const int MB = g.M <= 16 ? 1 : g.M <= 32 ? 2 : g.M <= 64 ? 4 : 8;
+  const int mt = (g.M + 16 * MB - 1) / (16 * MB);
+  dim3 grid(g.npairs, g.S, mt);
+  Epi<uint16_t> epi{e};
+  switch (MB) {
+    case 1: hipLaunchKernelGGL(k_gemm_bf16<1>, grid, dim3(256), 0, s, g, epi); break;
+    case 2: hipLaunchKernelGGL(k_gemm_bf16<2>, grid, dim3(256), 0, s, g, epi); break;
+    case 4: hipLaunchKernelGGL(k_gemm_bf16<4>, grid, dim3(256), 0, s, g, epi); break;
+    default: hipLaunchKernelGGL(k_gemm_bf16<8>, grid, dim3(256), 0, s, g, epi); break;
+  }
+  if (g.S > 1) {
+    dim3 g2(g.npairs, (g.M + 15) / 16);
+    hipLaunchKernelGGL(k_splitk_epi<uint16_t>, g2, dim3(256), 0, s, g, epi);
+  }
+}
+
+}  // namespace rlt

@@ -1,0 +1,439 @@
+// Row bookkeeping, normalisation, merge preparation, state write-back and
+// readout ("Recurrent Looped Transformer", §2.3 eqs. (2.3)-(2.6), §2.5
+// eqs. (2.9)-(2.11), §5.3, App. A.2).
+#include "rlt_internal.h"
+
+namespace rlt {
+
+static constexpr int ERR_PREFIX = -3;   // RLT_EPREFIX
+static constexpr int ERR_PENDING = -5;  // RLT_EPENDING
+static constexpr int ERR_INVAL = -1;    // RLT_EINVAL
+
+// ---------------------------------------------------------------------------
+// bookkeeping
+// ---------------------------------------------------------------------------
+
+// t = pos + 1 per slot; rows whose memory is shorter than t, or whose
+// consumed token differs from a recorded pending token, get t = 0 (skipped)
+// and raise the error word.
+__global__ void k_prestep(MiscArgs a) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= a.n) return;
+  const int row = a.rows.rows[i];
+  if (row < 0 || row >= a.B_cap) {
+    a.t_row_out[i] = 0;
+    *(volatile int*)a.err = ERR_INVAL;
+    return;
+  }
+  const int t = a.pos[row] + 1;
+  int code = 0;
+  if (t > a.max_t || (a.mem_len && t > a.mem_len[row])) code = ERR_PREFIX;
+  if (a.consume_tok && a.pending[row] >= 0 && a.consume_tok[i] != a.pending[row]) code = ERR_PENDING;
+  a.t_row_out[i] = code ? 0 : t;
+  if (code) *(volatile int*)a.err = code;
+}
+
+// replay tick: every active slot is at position `tick`
+__global__ void k_replay_rows(const int* rows, int n, int tick, int* t_row, const int* pos,
+                              const int* mem_len, int* err) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int row = rows[i];
+  int code = 0;
+  if (pos[row] + 1 != tick) code = ERR_PENDING;
+  if (mem_len && tick > mem_len[row]) code = ERR_PREFIX;
+  t_row[i] = code ? 0 : tick;
+  if (code) *(volatile int*)err = code;
+}
+
+__global__ void k_poststep(PostArgs a) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= a.n) return;
+  const int t = a.rows.t_row[i];
+  if (t <= 0) return;
+  const int row = a.rows.rows[i];
+  a.pos[row] = t;
+  a.pending[row] = a.next_tok ? a.next_tok[i] : -1;
+}
+
+template <typename T>
+__global__ void k_init(const int* rows, int n, const float* s_star, float* s, int* pos, int* pending,
+                       T* ring_k, T* ring_v, int L, int B_cap, int W1, int d, int poison) {
+  const int i = blockIdx.x;
+  if (i >= n) return;
+  const int row = rows[i];
+  if (row < 0 || row >= B_cap) return;
+  for (int c = threadIdx.x; c < d; c += blockDim.x) s[(int64_t)row * d + c] = s_star[c];
+  if (threadIdx.x == 0) {
+    pos[row] = 0;
+    pending[row] = -1;
+  }
+  if (poison && W1 > 0) {
+    const T nanv = from_f<T>(__uint_as_float(0x7fc00000u));
+    for (int l = 0; l < L; ++l) {
+      const int64_t base = ((int64_t)l * B_cap + row) * W1 * d;
+      for (int64_t c = threadIdx.x; c < (int64_t)W1 * d; c += blockDim.x) {
+        ring_k[base + c] = nanv;
+        ring_v[base + c] = nanv;
+      }
+    }
+  }
+}
+
+// pending[row] = x_len after a replay (the scored but unconsumed token)
+__global__ void k_set_pending(const int* rows, const int* src, int n, const int* tokens, int64_t tok_sb,
+                              const int* last_index, int* pending) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int b = src[i];
+  pending[rows[i]] = tokens[(int64_t)b * tok_sb + last_index[b]];
+}
+
+// ---------------------------------------------------------------------------
+// normalisation and merge preparation (one workgroup per slot)
+// ---------------------------------------------------------------------------
+
+// RMSNorm(x) = x / sqrt(mean(x^2) + eps) * gain
+template <typename T>
+__global__ __launch_bounds__(256) void k_rmsnorm(MiscArgs a) {
+  __shared__ float scratch[16];
+  const int slot = blockIdx.x;
+  const float* z = a.z + (int64_t)slot * a.d;
+  float ss = 0.f;
+  for (int c = threadIdx.x; c < a.d; c += 256) ss = fmaf(z[c], z[c], ss);
+  ss = block_sum(ss, scratch);
+  const float r = 1.0f / sqrtf(ss / (float)a.d + a.eps);
+  T* out = (T*)a.out + (int64_t)slot * a.ld_out;
+  for (int c = threadIdx.x; c < a.d; c += 256) out[c] = from_f<T>(z[c] * r * a.gain[c]);
+}
+
+// gated: X = [e ; RMSNorm_s(s_{t-1})]  (eq. 2.10 input); convex: X = [e ; s]
+template <typename T>
+__global__ __launch_bounds__(256) void k_merge_prep(MiscArgs a) {
+  __shared__ float scratch[16];
+  const int slot = blockIdx.x;
+  const int t = a.rows.t_row[slot];
+  T* X = (T*)a.out + (int64_t)slot * a.ld_out;
+  if (t <= 0) {
+    for (int c = threadIdx.x; c < 2 * a.d; c += 256) X[c] = from_f<T>(0.f);
+    return;
+  }
+  const float* s = a.s_state + (int64_t)a.rows.rows[slot] * a.d;
+  const T* e = (const T*)a.e.p + (int64_t)a.rows.src[slot] * a.e.sb + (int64_t)(t - 1) * a.e.st;
+  for (int c = threadIdx.x; c < a.d; c += 256) X[c] = e[c];
+  if (a.merge_kind == 0) {
+    float ss = 0.f;
+    for (int c = threadIdx.x; c < a.d; c += 256) ss = fmaf(s[c], s[c], ss);
+    ss = block_sum(ss, scratch);
+    const float r = 1.0f / sqrtf(ss / (float)a.d + a.eps);
+    for (int c = threadIdx.x; c < a.d; c += 256) X[a.d + c] = from_f<T>(s[c] * r * a.gain[c]);
+  } else {
+    for (int c = threadIdx.x; c < a.d; c += 256) X[a.d + c] = from_f<T>(s[c]);
+  }
+}
+
+// s_t write-back (state, optional outputs) and RMSNorm_o for the readout
+template <typename T>
+__global__ __launch_bounds__(256) void k_final(MiscArgs a) {
+  __shared__ float scratch[16];
+  const int slot = blockIdx.x;
+  const int t = a.rows.t_row[slot];
+  const float* z = a.z + (int64_t)slot * a.d;
+  if (t > 0) {
+    float* s = a.s_state + (int64_t)a.rows.rows[slot] * a.d;
+    for (int c = threadIdx.x; c < a.d; c += 256) s[c] = z[c];
+    if (a.s_out)
+      for (int c = threadIdx.x; c < a.d; c += 256) a.s_out[(int64_t)slot * a.d + c] = z[c];
+    if (a.s_trace) {
+      float* st = a.s_trace + (int64_t)a.rows.src[slot] * a.s_trace_sb + (int64_t)(t - 1) * a.d;
+      for (int c = threadIdx.x; c < a.d; c += 256) st[c] = z[c];
+    }
+  }
+  float ss = 0.f;
+  for (int c = threadIdx.x; c < a.d; c += 256) ss = fmaf(z[c], z[c], ss);
+  ss = block_sum(ss, scratch);
+  const float r = 1.0f / sqrtf(ss / (float)a.d + a.eps);
+  T* out = (T*)a.out + (int64_t)slot * a.ld_out;
+  for (int c = threadIdx.x; c < a.d; c += 256) out[c] = from_f<T>(z[c] * r * a.gain[c]);
+}
+
+__global__ void k_copy_f32(const float* src, float* dst, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = src[i];
+}
+
+// ---------------------------------------------------------------------------
+// readout: log-sum-exp, argmax, top-k behaviour distribution, sampling
+// one workgroup of RB threads per slot; thread i owns logits
+// [i*per, (i+1)*per) so that scans over thread order follow id order.
+// ---------------------------------------------------------------------------
+
+static constexpr int RB = 1024;
+static constexpr int KMAX = 1024;
+
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// exclusive prefix sum over the block of one int per thread (thread order)
+__device__ int block_excl_scan(int v, int* sh /* RB + 32 */, int* total) {
+  sh[threadIdx.x] = v;
+  __syncthreads();
+  for (int off = 1; off < RB; off <<= 1) {
+    const int x = threadIdx.x >= off ? sh[threadIdx.x - off] : 0;
+    __syncthreads();
+    sh[threadIdx.x] += x;
+    __syncthreads();
+  }
+  const int incl = sh[threadIdx.x];
+  *total = sh[RB - 1];
+  __syncthreads();
+  return incl - v;
+}
+
+__global__ __launch_bounds__(RB) void k_readout(ReadoutArgs a) {
+  __shared__ float s_f[RB / 64];
+  __shared__ int s_i[RB / 64];
+  __shared__ int s_scan[RB];
+  __shared__ int s_hist[256];
+  __shared__ float c_val[KMAX];
+  __shared__ int c_id[KMAX];
+  __shared__ int c_ord[KMAX];
+  __shared__ float s_bcast[4];
+  __shared__ int s_ibcast[4];
+
+  const int slot = blockIdx.x;
+  const int t = a.rows.t_row[slot];
+  if (t <= 0) return;
+  const int V = a.V;
+  const float* z = a.logits + (int64_t)slot * V;
+  const int per = (V + RB - 1) / RB;
+  const int lo = min(V, threadIdx.x * per), hi = min(V, lo + per);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+
+  // ---- max and argmax (lowest id among equal maxima) ----
+  float bm = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int i = lo; i < hi; ++i) {
+    const float v = z[i];
+    if (v > bm) { bm = v; bi = i; }
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    const float om = __shfl_xor(bm, off);
+    const int oi = __shfl_xor(bi, off);
+    if (om > bm || (om == bm && oi < bi)) { bm = om; bi = oi; }
+  }
+  if (lane == 0) { s_f[w] = bm; s_i[w] = bi; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float m = s_f[0];
+    int id = s_i[0];
+    for (int k = 1; k < RB / 64; ++k)
+      if (s_f[k] > m || (s_f[k] == m && s_i[k] < id)) { m = s_f[k]; id = s_i[k]; }
+    s_bcast[0] = m;
+    s_ibcast[0] = id;
+  }
+  __syncthreads();
+  const float zmax = s_bcast[0];
+  const int amax = s_ibcast[0];
+  if (threadIdx.x == 0 && a.argmax) a.argmax[slot] = amax;
+
+  // ---- score token ----
+  int tok = -1;
+  float* lp_out = nullptr;
+  if (a.logp) {
+    if (a.mode == 0) {
+      tok = a.score_tok[slot];
+      lp_out = a.logp + slot;
+    } else {
+      const int b = a.rows.src[slot];
+      if (t >= a.split[b]) {
+        tok = a.score_tok[(int64_t)b * a.tok_sb + t];  // x_{t+1}
+        lp_out = a.logp + (int64_t)b * a.logp_sb + t;
+      }
+    }
+  }
+  // ---- log-sum-exp of the raw distribution ----
+  if (lp_out || a.ratio) {
+    float se = 0.f;
+    for (int i = lo; i < hi; ++i) se += __expf(z[i] - zmax);
+    float sum = 0.f;
+    {
+      for (int off = 32; off > 0; off >>= 1) se += __shfl_xor(se, off);
+      if (lane == 0) s_f[w] = se;
+      __syncthreads();
+      for (int k = 0; k < RB / 64; ++k) sum += s_f[k];
+      __syncthreads();
+    }
+    const float lse = zmax + logf(sum);
+    if (threadIdx.x == 0 && lp_out && tok >= 0 && tok < V) {
+      const float lp = z[tok] - lse;
+      *lp_out = lp;
+      if (a.ratio && a.logmu_beh) a.ratio[slot] = expf(lp - a.logmu_beh[slot]);
+    }
+  }
+
+  // ---- behaviour distribution: temperature, top-k, renormalisation ----
+  const bool want_sample = a.uniform != nullptr;
+  const bool want_mu = a.logmu != nullptr;
+  if (!want_sample && !want_mu) return;
+  const float inv_tau = 1.0f / a.temperature;
+  int K = a.top_k;
+  if (K <= 0 || K > V) {
+    // no truncation (scoring only): log mu(tok) = (z_tok - zmax)/tau - log sum exp((z - zmax)/tau)
+    float se = 0.f;
+    for (int i = lo; i < hi; ++i) se += __expf((z[i] - zmax) * inv_tau);
+    for (int off = 32; off > 0; off >>= 1) se += __shfl_xor(se, off);
+    if (lane == 0) s_f[w] = se;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float sum = 0.f;
+      for (int k = 0; k < RB / 64; ++k) sum += s_f[k];
+      const int tk = a.score_tok[slot];
+      a.logmu[slot] = (tk >= 0 && tk < V) ? (z[tk] - zmax) * inv_tau - logf(sum) : -INFINITY;
+    }
+    return;
+  }
+  K = min(K, KMAX);
+  // radix select of the K-th largest key, 8 bits per pass from the top
+  uint32_t prefix = 0, mask = 0;
+  int remaining = K;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int b = threadIdx.x; b < 256; b += RB) s_hist[b] = 0;
+    __syncthreads();
+    for (int i = lo; i < hi; ++i) {
+      const uint32_t k = order_key(z[i]);
+      if ((k & mask) == prefix) atomicAdd(&s_hist[(k >> shift) & 0xff], 1);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int cum = 0, dg = 0;
+      for (int b = 255; b >= 0; --b) {
+        if (cum + s_hist[b] >= remaining) { dg = b; break; }
+        cum += s_hist[b];
+      }
+      s_ibcast[1] = dg;
+      s_ibcast[2] = remaining - cum;
+    }
+    __syncthreads();
+    prefix |= (uint32_t)s_ibcast[1] << shift;
+    mask |= 0xffu << shift;
+    remaining = s_ibcast[2];
+    __syncthreads();
+  }
+  const uint32_t thr = prefix;  // key of the K-th largest logit
+  // collect: all keys > thr, then the first `remaining` keys == thr in id order
+  int ngt = 0, neq = 0;
+  for (int i = lo; i < hi; ++i) {
+    const uint32_t k = order_key(z[i]);
+    ngt += k > thr;
+    neq += k == thr;
+  }
+  int tot_gt, tot_eq;
+  int pgt = block_excl_scan(ngt, s_scan, &tot_gt);
+  int peq = block_excl_scan(neq, s_scan, &tot_eq);
+  for (int i = lo; i < hi; ++i) {
+    const uint32_t k = order_key(z[i]);
+    if (k > thr) {
+      c_val[pgt] = z[i];
+      c_id[pgt] = i;
+      ++pgt;
+    } else if (k == thr) {
+      if (peq < remaining) {
+        c_val[tot_gt + peq] = z[i];
+        c_id[tot_gt + peq] = i;
+      }
+      ++peq;
+    }
+  }
+  __syncthreads();
+  // order candidates by (logit desc, id asc)
+  for (int c = threadIdx.x; c < K; c += RB) {
+    const float v = c_val[c];
+    const int id = c_id[c];
+    int rank = 0;
+    for (int o = 0; o < K; ++o) {
+      const float u = c_val[o];
+      rank += (u > v) || (u == v && c_id[o] < id);
+    }
+    c_ord[rank] = c;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float top = c_val[c_ord[0]];
+    float total = 0.f;
+    for (int r = 0; r < K; ++r) total += __expf((c_val[c_ord[r]] - top) * inv_tau);
+    const float ltot = logf(total);
+    if (want_sample) {
+      const float target = a.uniform[slot] * total;
+      float cum = 0.f;
+      int pick = K - 1;
+      for (int r = 0; r < K; ++r) {
+        cum += __expf((c_val[c_ord[r]] - top) * inv_tau);
+        if (cum > target) { pick = r; break; }
+      }
+      const int c = c_ord[pick];
+      if (a.sample_tok) a.sample_tok[slot] = c_id[c];
+      if (a.sample_logmu) a.sample_logmu[slot] = (c_val[c] - top) * inv_tau - ltot;
+    }
+    if (want_mu) {
+      const int tk = a.score_tok[slot];
+      float lm = -INFINITY;
+      for (int r = 0; r < K; ++r)
+        if (c_id[c_ord[r]] == tk) lm = (c_val[c_ord[r]] - top) * inv_tau - ltot;
+      a.logmu[slot] = lm;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+
+void launch_prestep(const MiscArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_prestep, dim3((a.n + 255) / 256), dim3(256), 0, s, a);
+}
+void launch_replay_rows(const int* rows, const int* src, int n, int tick, int* t_row, int* pos,
+                        const int* mem_len, int* err, hipStream_t s) {
+  (void)src;
+  hipLaunchKernelGGL(k_replay_rows, dim3((n + 255) / 256), dim3(256), 0, s, rows, n, tick, t_row,
+                     (const int*)pos, mem_len, err);
+}
+void launch_poststep(const PostArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_poststep, dim3((a.n + 255) / 256), dim3(256), 0, s, a);
+}
+void launch_init(int dtype, const int* rows, int n, const float* s_star, float* st, int* pos, int* pending,
+                 void* ring_k, void* ring_v, int L, int B_cap, int W, int d, int poison, hipStream_t s) {
+  if (dtype == 0)
+    hipLaunchKernelGGL(k_init<float>, dim3(n), dim3(256), 0, s, rows, n, s_star, st, pos, pending,
+                       (float*)ring_k, (float*)ring_v, L, B_cap, W - 1, d, poison);
+  else
+    hipLaunchKernelGGL(k_init<uint16_t>, dim3(n), dim3(256), 0, s, rows, n, s_star, st, pos, pending,
+                       (uint16_t*)ring_k, (uint16_t*)ring_v, L, B_cap, W - 1, d, poison);
+}
+void launch_set_pending(const int* rows, const int* src, int n, const int* tokens, int64_t tok_sb,
+                        const int* last_index, int* pending, hipStream_t s) {
+  hipLaunchKernelGGL(k_set_pending, dim3((n + 255) / 256), dim3(256), 0, s, rows, src, n, tokens,
+                     tok_sb, last_index, pending);
+}
+void launch_merge_prep(int dtype, const MiscArgs& a, hipStream_t s) {
+  if (dtype == 0) hipLaunchKernelGGL(k_merge_prep<float>, dim3(a.n), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(k_merge_prep<uint16_t>, dim3(a.n), dim3(256), 0, s, a);
+}
+void launch_rmsnorm(int dtype, const MiscArgs& a, hipStream_t s) {
+  if (dtype == 0) hipLaunchKernelGGL(k_rmsnorm<float>, dim3(a.n), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(k_rmsnorm<uint16_t>, dim3(a.n), dim3(256), 0, s, a);
+}
+void launch_final(int dtype, const MiscArgs& a, hipStream_t s) {
+  if (dtype == 0) hipLaunchKernelGGL(k_final<float>, dim3(a.n), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(k_final<uint16_t>, dim3(a.n), dim3(256), 0, s, a);
+}
+void launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s) {
+  hipLaunchKernelGGL(k_copy_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src, dst, n);
+}
+void launch_readout(const ReadoutArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_readout, dim3(a.n), dim3(RB), 0, s, a);
+}
+
+}  // namespace rlt

@@ -1,0 +1,786 @@
+// Host side of the C ABI declared in include/rlt.h: validation, workspace,
+// the launch sequence of one transition, the replay schedule and the
+// captured-graph cache. No arithmetic of the method happens here; every
+// step runs in the HIP kernels.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "../../include/rlt.h"
+#include "../../include/rlt_debug.h"
+#include "rlt_internal.h"
+
+using namespace rlt;
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+#define HIP_TRY(expr)                                                                  \
+  do {                                                                                 \
+    hipError_t e_ = (expr);                                                            \
+    if (e_ != hipSuccess) return fail(RLT_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+size_t elt_size(int dtype) { return dtype == RLT_BF16 ? 2 : 4; }
+
+}  // namespace
+
+struct rlt_ctx {
+  rlt_config cfg;
+  int dt;          // 0 = f32, 1 = bf16
+  size_t es;       // element size
+  // parameters (caller-owned device memory)
+  const float *s_star, *merge_norm, *merge_bg, *out_norm;
+  const void *merge_wg, *merge_ws, *w_out;
+  std::vector<const float*> norm_s, norm_m, norm_d;
+  std::vector<const void*> wq, wk, wv, wo, wqm, wom, w_gate, w_up, w_down;
+  // capacities
+  int max_rows, max_ctx, M_pad;
+  int chunk, nch;
+  int hpw;
+  // workspace (device)
+  int *t_row, *ident, *ones, *rows_buf, *src_buf, *split_buf, *last_buf;
+  void *X, *kc, *vc, *o, *h, *act;
+  float *gbuf, *z, *q, *qm, *part, *partial, *logits;
+  size_t partial_cap;  // floats
+  double* inv_freq;
+  // pinned host staging for replay schedules
+  int* host_stage;
+  // error word: host-mapped pinned memory written by kernels
+  int* err_host;
+  int* err_dev;
+  // captured step graph
+  hipGraph_t graph;
+  hipGraphExec_t graph_exec;
+  std::vector<unsigned char> graph_key;
+};
+
+// ----------------------------------------------------------------------------
+// helpers
+// ----------------------------------------------------------------------------
+
+static int check_config(const rlt_config* c) {
+  if (!c) return fail(RLT_EINVAL, "null config");
+  if (c->n_layers < 1 || c->d_model < 1 || c->n_heads < 1 || c->d_head < 1 || c->window < 1 ||
+      c->n_groups < 1 || c->d_ffn < 1 || c->vocab < 2)
+    return fail(RLT_EINVAL, "config sizes must be positive");
+  if (c->n_heads * c->d_head != c->d_model) return fail(RLT_ESHAPE, "d_model != n_heads * d_head");
+  if (c->dtype != RLT_F32 && c->dtype != RLT_BF16) return fail(RLT_EINVAL, "dtype");
+  if (c->merge_kind != RLT_MERGE_GATED && c->merge_kind != RLT_MERGE_CONVEX)
+    return fail(RLT_EINVAL, "merge_kind");
+  if (c->pos_kind != RLT_POS_NONE && c->pos_kind != RLT_POS_ROPE) return fail(RLT_EINVAL, "pos_kind");
+  const int dh = c->d_head;
+  if (dh != 16 && dh != 32 && dh != 64 && dh != 128)
+    return fail(RLT_EUNSUPPORTED, "d_head %d not in {16,32,64,128}", dh);
+  if (dh == 16 && c->dtype == RLT_BF16) return fail(RLT_EUNSUPPORTED, "d_head 16 needs RLT_F32");
+  if (c->d_model % 32 || c->d_ffn % 32 || c->vocab % 32)
+    return fail(RLT_EUNSUPPORTED, "d_model, d_ffn and vocab must be multiples of 32");
+  if (c->n_groups != 1 && c->n_groups != c->n_layers)
+    return fail(RLT_EUNSUPPORTED, "n_groups must be 1 or n_layers");
+  if (!(c->rms_eps > 0.f) || !(c->rope_theta > 0.f)) return fail(RLT_EINVAL, "rms_eps, rope_theta");
+  return RLT_OK;
+}
+
+static int elems_per_lane(int dt) { return dt == 1 ? 16 : 8; }
+
+// heads per attention workgroup: hpw * (dh / E) lanes per key, at most 32
+static int choose_hpw(const rlt_config& c, int dt) {
+  const int lpk = c.d_head / elems_per_lane(dt);
+  int best = 1;
+  for (int h = 1; h <= c.n_heads; ++h)
+    if (c.n_heads % h == 0 && h * lpk <= 32 && 256 % (h * lpk) == 0) best = h;
+  return best;
+}
+
+template <typename P>
+static int dev_alloc(P** p, size_t bytes) {
+  void* v = nullptr;
+  if (bytes == 0) bytes = 16;
+  if (hipMalloc(&v, bytes) != hipSuccess) return fail(RLT_ENOMEM, "hipMalloc(%zu) failed", bytes);
+  *p = (P*)v;
+  return RLT_OK;
+}
+
+// ----------------------------------------------------------------------------
+// create / destroy / layout / errors
+// ----------------------------------------------------------------------------
+
+extern "C" const char* rlt_last_error(void) { return g_msg; }
+
+extern "C" int rlt_state_layout(const rlt_config* cfg, int32_t B_cap, size_t bytes_out[5]) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (B_cap < 1 || !bytes_out) return fail(RLT_EINVAL, "B_cap < 1 or null output");
+  const size_t es = elt_size(cfg->dtype);
+  const size_t ring = (size_t)cfg->n_layers * B_cap * (size_t)(cfg->window - 1) * cfg->d_model * es;
+  bytes_out[0] = (size_t)B_cap * cfg->d_model * sizeof(float);
+  bytes_out[1] = ring;
+  bytes_out[2] = ring;
+  bytes_out[3] = (size_t)B_cap * sizeof(int32_t);
+  bytes_out[4] = (size_t)B_cap * sizeof(int32_t);
+  return RLT_OK;
+}
+
+extern "C" void rlt_destroy(rlt_ctx* c) {
+  if (!c) return;
+  void* ptrs[] = {c->t_row, c->ident, c->ones, c->rows_buf, c->src_buf, c->split_buf, c->last_buf,
+                  c->X, c->kc, c->vc, c->o, c->h, c->act, c->gbuf, c->z, c->q, c->qm, c->part,
+                  c->partial, c->logits, c->inv_freq};
+  for (void* p : ptrs)
+    if (p) (void)hipFree(p);
+  if (c->graph_exec) (void)hipGraphExecDestroy(c->graph_exec);
+  if (c->graph) (void)hipGraphDestroy(c->graph);
+  if (c->err_host) (void)hipHostFree(c->err_host);
+  if (c->host_stage) (void)hipHostFree(c->host_stage);
+  delete c;
+}
+
+extern "C" int rlt_create(const rlt_config* cfg, const rlt_weights* w, int32_t max_rows, int32_t max_ctx,
+                          rlt_ctx** out) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!w || !out) return fail(RLT_EINVAL, "null weights or output");
+  if (max_rows < 1 || max_rows > 65536 || max_ctx < 1) return fail(RLT_EINVAL, "max_rows/max_ctx");
+  const int L = cfg->n_layers;
+  const bool gated = cfg->merge_kind == RLT_MERGE_GATED;
+  if (!w->s_star || !w->merge_wg || !w->merge_bg || !w->out_norm || !w->w_out ||
+      (gated && (!w->merge_norm || !w->merge_ws)))
+    return fail(RLT_EINVAL, "missing global weight");
+  const void* const* per[] = {(const void* const*)w->norm_s, w->wq, w->wk, w->wv, w->wo,
+                              (const void* const*)w->norm_m, w->wqm, w->wom,
+                              (const void* const*)w->norm_d, w->w_gate, w->w_up, w->w_down};
+  for (auto arr : per) {
+    if (!arr) return fail(RLT_EINVAL, "missing per-layer weight array");
+    for (int l = 0; l < L; ++l)
+      if (!arr[l]) return fail(RLT_EINVAL, "missing per-layer weight of layer %d", l);
+  }
+  rlt_ctx* c = new rlt_ctx();  // value-initialised: every pointer starts null
+  c->cfg = *cfg;
+  c->dt = cfg->dtype == RLT_BF16 ? 1 : 0;
+  c->es = elt_size(cfg->dtype);
+  c->s_star = w->s_star;
+  c->merge_norm = w->merge_norm;
+  c->merge_bg = w->merge_bg;
+  c->out_norm = w->out_norm;
+  c->merge_wg = w->merge_wg;
+  c->merge_ws = w->merge_ws;
+  c->w_out = w->w_out;
+  c->norm_s.assign(w->norm_s, w->norm_s + L);
+  c->norm_m.assign(w->norm_m, w->norm_m + L);
+  c->norm_d.assign(w->norm_d, w->norm_d + L);
+  c->wq.assign(w->wq, w->wq + L);
+  c->wk.assign(w->wk, w->wk + L);
+  c->wv.assign(w->wv, w->wv + L);
+  c->wo.assign(w->wo, w->wo + L);
+  c->wqm.assign(w->wqm, w->wqm + L);
+  c->wom.assign(w->wom, w->wom + L);
+  c->w_gate.assign(w->w_gate, w->w_gate + L);
+  c->w_up.assign(w->w_up, w->w_up + L);
+  c->w_down.assign(w->w_down, w->w_down + L);
+
+  const int d = cfg->d_model, F = cfg->d_ffn, V = cfg->vocab, H = cfg->n_heads, dh = cfg->d_head;
+  c->max_rows = max_rows;
+  c->max_ctx = max_ctx;
+  c->M_pad = (max_rows + 127) / 128 * 128;
+  c->chunk = d <= 512 ? 128 : 256;
+  c->nch = (max_ctx + c->chunk - 1) / c->chunk;
+  c->hpw = choose_hpw(*cfg, c->dt);
+  const size_t M = c->M_pad, es = c->es;
+  const int Nv_max = std::max(3 * d, 2 * F);
+  c->partial_cap = (size_t)8 * M * Nv_max;
+
+#define ALLOC(p, bytes)                     \
+  do {                                      \
+    int r_ = dev_alloc(&(p), (bytes));      \
+    if (r_) { rlt_destroy(c); return r_; }  \
+  } while (0)
+  ALLOC(c->t_row, M * 4);
+  ALLOC(c->ident, M * 4);
+  ALLOC(c->ones, M * 4);
+  ALLOC(c->rows_buf, M * 4);
+  ALLOC(c->src_buf, M * 4);
+  ALLOC(c->split_buf, M * 4);
+  ALLOC(c->last_buf, M * 4);
+  ALLOC(c->X, M * 2 * d * es);
+  ALLOC(c->kc, M * d * es);
+  ALLOC(c->vc, M * d * es);
+  ALLOC(c->o, M * d * es);
+  ALLOC(c->h, M * d * es);
+  ALLOC(c->act, M * F * es);
+  ALLOC(c->gbuf, M * d * 4);
+  ALLOC(c->z, M * d * 4);
+  ALLOC(c->q, M * d * 4);
+  ALLOC(c->qm, M * d * 4);
+  ALLOC(c->part, M * (size_t)c->nch * H * (dh + 2) * 4);
+  ALLOC(c->partial, c->partial_cap * 4);
+  ALLOC(c->logits, M * (size_t)V * 4);
+  ALLOC(c->inv_freq, (size_t)(dh / 2) * sizeof(double));
+#undef ALLOC
+  // workspace contents that never change: identity slots, unit positions,
+  // zeroed A rows (rows beyond n are read by the MFMA tiles and discarded)
+  std::vector<int> iv(M), ov(M, 1);
+  std::iota(iv.begin(), iv.end(), 0);
+  std::vector<double> fr(dh / 2);
+  for (int i = 0; i < dh / 2; ++i) fr[i] = std::pow((double)cfg->rope_theta, -2.0 * i / dh);
+  if (hipMemcpy(c->ident, iv.data(), M * 4, hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(c->ones, ov.data(), M * 4, hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(c->inv_freq, fr.data(), fr.size() * sizeof(double), hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemset(c->X, 0, M * 2 * d * es) != hipSuccess || hipMemset(c->o, 0, M * d * es) != hipSuccess ||
+      hipMemset(c->h, 0, M * d * es) != hipSuccess || hipMemset(c->act, 0, M * F * es) != hipSuccess) {
+    rlt_destroy(c);
+    return fail(RLT_EHIP, "workspace initialisation failed");
+  }
+  if (hipHostMalloc((void**)&c->err_host, sizeof(int), hipHostMallocMapped) != hipSuccess ||
+      hipHostGetDevicePointer((void**)&c->err_dev, c->err_host, 0) != hipSuccess) {
+    rlt_destroy(c);
+    return fail(RLT_EHIP, "pinned error word allocation failed");
+  }
+  *(volatile int*)c->err_host = 0;
+  if (hipHostMalloc((void**)&c->host_stage, M * 4 * 4, hipHostMallocDefault) != hipSuccess) {
+    rlt_destroy(c);
+    return fail(RLT_EHIP, "pinned staging allocation failed");
+  }
+  *out = c;
+  return RLT_OK;
+}
+
+// a device-detected error from earlier work, if any (cleared when returned)
+static int take_device_error(rlt_ctx* c) {
+  const int e = *(volatile int*)c->err_host;
+  if (e) {
+    *(volatile int*)c->err_host = 0;
+    return fail(e, "device-detected error from an earlier call (code %d): rows were skipped", e);
+  }
+  return RLT_OK;
+}
+
+extern "C" int rlt_sync_error(rlt_ctx* c, void* stream) {
+  if (!c) return fail(RLT_EINVAL, "null context");
+  HIP_TRY(hipStreamSynchronize((hipStream_t)stream));
+  return take_device_error(c);
+}
+
+// ----------------------------------------------------------------------------
+// matrix product wrapper: picks the K split for the bf16 path
+// ----------------------------------------------------------------------------
+
+namespace {
+
+struct Gemm {
+  rlt_ctx* c;
+  hipStream_t s;
+
+  void run(const void* A, int64_t lda, std::initializer_list<const void*> W, int seg_rows, int K, int pairing,
+           int n, EpiArgs e) {
+    GemmArgs g{};
+    g.A = A;
+    g.lda = lda;
+    int i = 0;
+    for (const void* p : W) g.W[i++] = p;
+    g.nseg = i;
+    g.seg_rows = seg_rows;
+    g.K = K;
+    g.pairing = pairing;
+    g.dh = c->cfg.d_head;
+    g.M = n;
+    g.M_pad = c->M_pad;
+    g.Nv = g.nseg * seg_rows;
+    g.npairs = g.Nv / 32;
+    g.S = 1;
+    g.kslice = (K + 4 * 32 - 1) / (4 * 32) * 32;
+    g.partial = c->partial;
+    if (c->dt == 1) {
+      const int MB = n <= 16 ? 1 : n <= 32 ? 2 : n <= 64 ? 4 : 8;
+      const int mt = (n + 16 * MB - 1) / (16 * MB);
+      const int tiles = g.npairs * mt;
+      int S = std::max(1, (512 + tiles - 1) / tiles);   // fill the chip
+      S = std::min(S, std::max(1, K / 256));             // >= 64 K per wave
+      S = std::min(S, std::max(1, K / (8 * n)));         // partial traffic <= half the weights
+      while (S > 1 && (size_t)S * c->M_pad * g.Nv > c->partial_cap) --S;
+      g.S = S;
+      const int per = (K + 4 * S - 1) / (4 * S);
+      g.kslice = (per + 31) / 32 * 32;
+    }
+    launch_gemm(c->dt, g, e, s);
+  }
+};
+
+struct StepPlan {
+  Rows R;                 // rows / src / t_row (t_row filled by the pre-step)
+  int n;
+  EIn e;
+  rlt_memory mem;
+  rlt_state* st;
+  // outputs
+  float* s_out;
+  float* s_trace;
+  int64_t s_trace_sb;
+  float* z_trace;
+  bool need_logits;
+  float* logits;          // where the logits go
+  ReadoutArgs ro;
+  bool do_readout;
+};
+
+// the transition for n slots: merge, L_D blocks, final norm, readout
+void enqueue_transition(rlt_ctx* c, const StepPlan& P, hipStream_t s) {
+  const rlt_config& cf = c->cfg;
+  const int d = cf.d_model, F = cf.d_ffn, H = cf.n_heads, dh = cf.d_head, L = cf.n_layers;
+  const int n = P.n;
+  const size_t es = c->es;
+  Gemm gm{c, s};
+
+  EpiArgs E0{};
+  E0.rows = P.R;
+  E0.d = d;
+  E0.dh = dh;
+  E0.H = H;
+  E0.rope = cf.pos_kind == RLT_POS_ROPE;
+  E0.inv_freq = c->inv_freq;
+  E0.alpha = cf.alpha;
+  E0.e = P.e;
+  E0.s_state = P.st->s;
+
+  MiscArgs m{};
+  m.rows = P.R;
+  m.n = n;
+  m.d = d;
+  m.eps = cf.rms_eps;
+  m.s_state = P.st->s;
+  m.e = P.e;
+  m.merge_kind = cf.merge_kind;
+
+  // ---- merge [eqs. (2.9)-(2.11)] ----
+  m.gain = c->merge_norm;
+  m.out = c->X;
+  m.ld_out = 2 * d;
+  launch_merge_prep(c->dt, m, s);
+  if (cf.merge_kind == RLT_MERGE_GATED) {
+    EpiArgs e = E0;
+    e.kind = EPI_MGATE;
+    e.out_f = c->gbuf;
+    e.ldo = d;
+    e.bias = c->merge_bg;
+    gm.run(c->X, 2 * d, {c->merge_wg}, d, 2 * d, PAIR_PLAIN, n, e);
+    e.kind = EPI_MOUT;
+    e.out_f = c->z;
+    e.gbuf = c->gbuf;
+    gm.run((const char*)c->X + d * es, 2 * d, {c->merge_ws}, d, d, PAIR_PLAIN, n, e);
+  } else {
+    EpiArgs e = E0;
+    e.kind = EPI_CONVEX;
+    e.out_f = c->z;
+    e.ldo = d;
+    e.bias = c->merge_bg;
+    gm.run(c->X, 2 * d, {c->merge_wg}, d, 2 * d, PAIR_PLAIN, n, e);
+  }
+
+  AttnArgs at{};
+  at.rows = P.R;
+  at.d = d;
+  at.H = H;
+  at.dh = dh;
+  at.hpw = c->hpw;
+  at.qscale = (float)(1.4426950408889634 / std::sqrt((double)dh));
+  at.W = cf.window;
+  at.chunk = c->chunk;
+  at.nch = std::min(c->nch, (c->max_ctx + c->chunk - 1) / c->chunk);
+  at.part = c->part;
+  at.sb = P.mem.stride_b;
+  at.st = P.mem.stride_t;
+
+  const size_t ring_layer = (size_t)P.st->B_cap * (cf.window - 1) * d * es;
+  for (int l = 0; l < L; ++l) {
+    // ---- SWA sublayer [eqs. (2.12)-(2.14)] ----
+    m.z = c->z;
+    m.gain = c->norm_s[l];
+    m.out = c->h;
+    m.ld_out = d;
+    launch_rmsnorm(c->dt, m, s);
+    {
+      EpiArgs e = E0;
+      e.kind = EPI_QKV;
+      e.out_f = c->q;
+      e.out_k = c->kc;
+      e.out_v = c->vc;
+      gm.run(c->h, d, {c->wq[l], c->wk[l], c->wv[l]}, d, d, PAIR_ROPE, n, e);
+    }
+    at.q = c->q;
+    at.kc = c->kc;
+    at.vc = c->vc;
+    at.ring_k = (char*)P.st->ring_k + l * ring_layer;
+    at.ring_v = (char*)P.st->ring_v + l * ring_layer;
+    at.out = c->o;
+    launch_swa(c->dt, at, s);
+    {
+      EpiArgs e = E0;
+      e.kind = EPI_RESID;
+      e.out_f = c->z;
+      e.ldo = d;
+      gm.run(c->o, d, {c->wo[l]}, d, d, PAIR_PLAIN, n, e);
+    }
+    // ---- cross-attention sublayer [eq. (2.15)] ----
+    m.gain = c->norm_m[l];
+    launch_rmsnorm(c->dt, m, s);
+    {
+      EpiArgs e = E0;
+      e.kind = EPI_QROT;
+      e.out_f = c->qm;
+      gm.run(c->h, d, {c->wqm[l]}, d, d, PAIR_ROPE, n, e);
+    }
+    const int g = (l * cf.n_groups) / L;
+    at.q = c->qm;
+    at.mk = (const char*)P.mem.k + (size_t)g * P.mem.stride_g * es;
+    at.mv = (const char*)P.mem.v + (size_t)g * P.mem.stride_g * es;
+    launch_xattn(c->dt, at, s);
+    launch_xcombine(c->dt, at, s);
+    {
+      EpiArgs e = E0;
+      e.kind = EPI_RESID;
+      e.out_f = c->z;
+      e.ldo = d;
+      gm.run(c->o, d, {c->wom[l]}, d, d, PAIR_PLAIN, n, e);
+    }
+    // ---- FFN sublayer [eq. (2.16)] ----
+    m.gain = c->norm_d[l];
+    launch_rmsnorm(c->dt, m, s);
+    {
+      EpiArgs e = E0;
+      e.kind = EPI_SWIGLU;
+      e.out_k = c->act;
+      e.ldo = F;
+      gm.run(c->h, d, {c->w_gate[l], c->w_up[l]}, F, d, PAIR_DUAL, n, e);
+      e.kind = EPI_RESID;
+      e.out_f = c->z;
+      e.ldo = d;
+      gm.run(c->act, F, {c->w_down[l]}, d, F, PAIR_PLAIN, n, e);
+    }
+    if (P.z_trace) launch_copy_f32(c->z, P.z_trace + (size_t)l * n * d, (int64_t)n * d, s);
+  }
+  // ---- s_t write-back, RMSNorm_o [eq. (2.6)] ----
+  m.gain = c->out_norm;
+  m.out = c->h;
+  m.ld_out = d;
+  m.s_out = P.s_out;
+  m.s_trace = P.s_trace;
+  m.s_trace_sb = P.s_trace_sb;
+  launch_final(c->dt, m, s);
+  if (P.need_logits) {
+    EpiArgs e = E0;
+    e.kind = EPI_STORE;
+    e.out_f = P.logits;
+    e.ldo = cf.vocab;
+    gm.run(c->h, d, {c->w_out}, cf.vocab, d, PAIR_PLAIN, n, e);
+  }
+  if (P.do_readout) launch_readout(P.ro, s);
+}
+
+int check_state(rlt_ctx* c, const rlt_state* st) {
+  if (!st || !st->s || !st->pos || !st->pending) return fail(RLT_EINVAL, "null state buffer");
+  if (c->cfg.window > 1 && (!st->ring_k || !st->ring_v)) return fail(RLT_EINVAL, "null cache buffer");
+  if (st->B_cap < 1) return fail(RLT_EINVAL, "B_cap < 1");
+  if (st->version != c->cfg.weights_version)
+    return fail(RLT_ESTALE, "state version %llu differs from weights version %llu",
+                (unsigned long long)st->version, (unsigned long long)c->cfg.weights_version);
+  return RLT_OK;
+}
+
+int check_memory(const rlt_memory& m) {
+  if (!m.k || !m.v || !m.mem_len) return fail(RLT_EINVAL, "null memory pointer");
+  if (m.stride_t < 1 || m.stride_b < 0 || m.stride_g < 0) return fail(RLT_EINVAL, "memory strides");
+  return RLT_OK;
+}
+
+}  // namespace
+
+// ----------------------------------------------------------------------------
+// entry points
+// ----------------------------------------------------------------------------
+
+extern "C" int rlt_init_state(rlt_ctx* c, rlt_state* st, const int32_t* rows, int32_t n, int32_t flags,
+                              void* stream) {
+  if (!c) return fail(RLT_EINVAL, "null context");
+  int rc = check_state(c, st);
+  if (rc) return rc;
+  if (!rows || n < 1 || n > st->B_cap) return fail(RLT_EINVAL, "rows/n");
+  launch_init(c->dt, rows, n, c->s_star, st->s, st->pos, st->pending, st->ring_k, st->ring_v,
+              c->cfg.n_layers, st->B_cap, c->cfg.window, c->cfg.d_model, flags & RLT_INIT_POISON,
+              (hipStream_t)stream);
+  HIP_TRY(hipGetLastError());
+  return RLT_OK;
+}
+
+static int step_enqueue(rlt_ctx* c, rlt_state* st, const rlt_step_io* io, hipStream_t s) {
+  const int n = io->n;
+  StepPlan P{};
+  P.R = Rows{io->rows, c->ident, c->t_row, n};
+  P.n = n;
+  P.e = EIn{io->e, (int64_t)c->cfg.d_model, 0};
+  P.mem = io->mem;
+  P.st = st;
+  P.s_out = io->s_out;
+  P.z_trace = io->z_trace;
+  const bool sampling = io->uniform != nullptr;
+  P.need_logits = io->logits || io->argmax || io->logp || sampling;
+  P.logits = io->logits ? io->logits : c->logits;
+  P.do_readout = io->argmax || io->logp || sampling;
+  ReadoutArgs& ro = P.ro;
+  ro.rows = P.R;
+  ro.n = n;
+  ro.V = c->cfg.vocab;
+  ro.logits = P.logits;
+  ro.argmax = io->argmax;
+  ro.mode = 0;
+  ro.score_tok = io->score_tok;
+  ro.logp = io->logp;
+  ro.uniform = io->uniform;
+  ro.temperature = io->temperature;
+  ro.top_k = io->top_k;
+  ro.sample_tok = io->sample_tok;
+  ro.sample_logmu = io->sample_logmu;
+
+  MiscArgs m{};
+  m.rows = P.R;
+  m.n = n;
+  m.pos = st->pos;
+  m.pending = st->pending;
+  m.mem_len = io->mem.mem_len;
+  m.consume_tok = io->consume_tok;
+  m.t_row_out = c->t_row;
+  m.err = c->err_dev;
+  m.max_t = c->max_ctx;
+  m.B_cap = st->B_cap;
+  launch_prestep(m, s);
+  enqueue_transition(c, P, s);
+  PostArgs pa{P.R, n, st->pos, st->pending, nullptr};
+  if (io->flags & RLT_STEP_DEFER) pa.next_tok = sampling ? io->sample_tok : io->argmax;
+  launch_poststep(pa, s);
+  HIP_TRY(hipGetLastError());
+  return RLT_OK;
+}
+
+extern "C" int rlt_decoder_step(rlt_ctx* c, rlt_state* st, const rlt_step_io* io, void* stream) {
+  if (!c || !io) return fail(RLT_EINVAL, "null context or io");
+  int rc = check_state(c, st);
+  if (rc) return rc;
+  if (io->n < 1 || io->n > c->max_rows) return fail(RLT_ESHAPE, "n=%d outside 1..max_rows=%d", io->n, c->max_rows);
+  if (io->n > st->B_cap) return fail(RLT_ESHAPE, "n > B_cap");
+  if (!io->rows || !io->e) return fail(RLT_EINVAL, "null rows or e");
+  if ((rc = check_memory(io->mem))) return rc;
+  if (io->logp && !io->score_tok) return fail(RLT_EINVAL, "logp needs score_tok");
+  if (io->uniform) {
+    if (!(io->temperature > 0.f)) return fail(RLT_EINVAL, "temperature must be > 0");
+    if (io->top_k < 1 || io->top_k > 1024 || io->top_k > c->cfg.vocab)
+      return fail(RLT_EUNSUPPORTED, "sampling needs 1 <= top_k <= min(1024, vocab)");
+    if (!io->sample_tok && !io->sample_logmu) return fail(RLT_EINVAL, "sampling without outputs");
+  }
+  if ((io->flags & RLT_STEP_DEFER) && !(io->uniform ? io->sample_tok : io->argmax))
+    return fail(RLT_EINVAL, "RLT_STEP_DEFER needs sample_tok (sampling) or argmax");
+  if ((rc = take_device_error(c))) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  if (!(io->flags & RLT_STEP_GRAPH)) return step_enqueue(c, st, io, s);
+  if (!stream) return fail(RLT_EINVAL, "RLT_STEP_GRAPH needs a non-default stream");
+
+  // captured step: replay when the arguments are identical to the capture
+  std::vector<unsigned char> key(sizeof(rlt_step_io) + sizeof(rlt_state) + sizeof(void*));
+  std::memcpy(key.data(), io, sizeof(rlt_step_io));
+  std::memcpy(key.data() + sizeof(rlt_step_io), st, sizeof(rlt_state));
+  std::memcpy(key.data() + sizeof(rlt_step_io) + sizeof(rlt_state), &stream, sizeof(void*));
+  if (!c->graph_exec || key != c->graph_key) {
+    if (c->graph_exec) {
+      (void)hipGraphExecDestroy(c->graph_exec);
+      c->graph_exec = nullptr;
+    }
+    if (c->graph) {
+      (void)hipGraphDestroy(c->graph);
+      c->graph = nullptr;
+    }
+    HIP_TRY(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
+    rc = step_enqueue(c, st, io, s);
+    hipGraph_t g = nullptr;
+    hipError_t ec = hipStreamEndCapture(s, &g);
+    if (rc) {
+      if (g) (void)hipGraphDestroy(g);
+      return rc;
+    }
+    if (ec != hipSuccess) return fail(RLT_EHIP, "hipStreamEndCapture: %s", hipGetErrorString(ec));
+    c->graph = g;
+    HIP_TRY(hipGraphInstantiate(&c->graph_exec, g, nullptr, nullptr, 0));
+    c->graph_key = key;
+  }
+  HIP_TRY(hipGraphLaunch(c->graph_exec, s));
+  return RLT_OK;
+}
+
+extern "C" int rlt_replay_sequence(rlt_ctx* c, rlt_state* st, const rlt_replay_io* io, void* stream) {
+  if (!c || !io) return fail(RLT_EINVAL, "null context or io");
+  int rc = check_state(c, st);
+  if (rc) return rc;
+  const int B = io->B;
+  if (B < 1 || B > c->max_rows || B > st->B_cap) return fail(RLT_ESHAPE, "B outside 1..max_rows/B_cap");
+  if (!io->len_host || !io->split_host || !io->e || !io->tokens || !io->logp)
+    return fail(RLT_EINVAL, "null replay input");
+  if ((rc = check_memory(io->mem))) return rc;
+  int maxlen = 0;
+  std::vector<int> rows(B);
+  for (int b = 0; b < B; ++b) {
+    const int len = io->len_host[b], sp = io->split_host[b];
+    if (len < 2) return fail(RLT_ESHAPE, "len[%d]=%d < 2", b, len);
+    if (len - 1 > c->max_ctx) return fail(RLT_ESHAPE, "len[%d]-1 exceeds max_ctx", b);
+    if (sp < 1) return fail(RLT_EINVAL, "split[%d] < 1", b);
+    rows[b] = io->rows_host ? io->rows_host[b] : b;
+    if (rows[b] < 0 || rows[b] >= st->B_cap) return fail(RLT_EINVAL, "row of sequence %d out of range", b);
+    maxlen = std::max(maxlen, len);
+  }
+  {
+    std::vector<int> seen(rows);
+    std::sort(seen.begin(), seen.end());
+    if (std::adjacent_find(seen.begin(), seen.end()) != seen.end()) return fail(RLT_EINVAL, "duplicate rows");
+  }
+  if ((rc = take_device_error(c))) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  // schedule: sequences by length, longest first (stable), so that the
+  // active set at tick t (len - 1 >= t) is a prefix of the order
+  std::vector<int> order(B);
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int a, int b) { return io->len_host[a] > io->len_host[b]; });
+  int* stg = c->host_stage;
+  const size_t M = c->M_pad;
+  for (int i = 0; i < B; ++i) {
+    stg[i] = rows[order[i]];
+    stg[M + i] = order[i];
+    stg[2 * M + i] = io->split_host[i];
+    stg[3 * M + i] = io->len_host[i] - 1;
+  }
+  HIP_TRY(hipMemcpyAsync(c->rows_buf, stg, B * 4, hipMemcpyHostToDevice, s));
+  HIP_TRY(hipMemcpyAsync(c->src_buf, stg + M, B * 4, hipMemcpyHostToDevice, s));
+  HIP_TRY(hipMemcpyAsync(c->split_buf, stg + 2 * M, B * 4, hipMemcpyHostToDevice, s));
+  HIP_TRY(hipMemcpyAsync(c->last_buf, stg + 3 * M, B * 4, hipMemcpyHostToDevice, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  launch_init(c->dt, c->rows_buf, B, c->s_star, st->s, st->pos, st->pending, st->ring_k, st->ring_v,
+              c->cfg.n_layers, st->B_cap, c->cfg.window, c->cfg.d_model, 0, s);
+  std::vector<int> lens_sorted(B);
+  for (int i = 0; i < B; ++i) lens_sorted[i] = io->len_host[order[i]];
+  for (int t = 1; t <= maxlen - 1; ++t) {
+    int nt = 0;
+    while (nt < B && lens_sorted[nt] - 1 >= t) ++nt;
+    StepPlan P{};
+    P.R = Rows{c->rows_buf, c->src_buf, c->t_row, nt};
+    P.n = nt;
+    P.e = EIn{io->e, io->e_stride_b, io->e_stride_t};
+    P.mem = io->mem;
+    P.st = st;
+    P.s_trace = io->s_trace;
+    P.s_trace_sb = io->s_stride_b;
+    P.need_logits = true;
+    P.logits = c->logits;
+    P.do_readout = true;
+    ReadoutArgs& ro = P.ro;
+    ro.rows = P.R;
+    ro.n = nt;
+    ro.V = c->cfg.vocab;
+    ro.logits = c->logits;
+    ro.mode = 1;
+    ro.score_tok = io->tokens;
+    ro.tok_sb = io->tok_stride_b;
+    ro.logp = io->logp;
+    ro.logp_sb = io->logp_stride_b;
+    ro.split = c->split_buf;
+    launch_replay_rows(c->rows_buf, c->src_buf, nt, t, c->t_row, st->pos, io->mem.mem_len, c->err_dev, s);
+    enqueue_transition(c, P, s);
+    PostArgs pa{P.R, nt, st->pos, st->pending, nullptr};
+    launch_poststep(pa, s);
+  }
+  launch_set_pending(c->rows_buf, c->src_buf, B, io->tokens, io->tok_stride_b, c->last_buf, st->pending, s);
+  HIP_TRY(hipGetLastError());
+  return RLT_OK;
+}
+
+extern "C" int rlt_score_logprobs(rlt_ctx* c, const rlt_score_io* io, void* stream) {
+  if (!c || !io) return fail(RLT_EINVAL, "null context or io");
+  if (io->n < 1 || io->n > c->max_rows) return fail(RLT_ESHAPE, "n outside 1..max_rows");
+  if (!io->s || !io->tokens || !io->logp) return fail(RLT_EINVAL, "null s, tokens or logp");
+  if (io->logmu && !(io->temperature > 0.f)) return fail(RLT_EINVAL, "temperature must be > 0");
+  if (io->logmu && (io->top_k < 0 || io->top_k > 1024)) return fail(RLT_EUNSUPPORTED, "top_k outside 0..1024");
+  if (io->ratio && !io->logmu_behaviour) return fail(RLT_EINVAL, "ratio needs logmu_behaviour");
+  int rc = take_device_error(c);
+  if (rc) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  const int n = io->n, d = c->cfg.d_model;
+  Rows R{c->ident, c->ident, c->ones, n};
+  MiscArgs m{};
+  m.rows = R;
+  m.n = n;
+  m.d = d;
+  m.eps = c->cfg.rms_eps;
+  m.z = io->s;
+  m.gain = c->out_norm;
+  m.out = c->h;
+  m.ld_out = d;
+  launch_rmsnorm(c->dt, m, s);
+  EpiArgs e{};
+  e.kind = EPI_STORE;
+  e.rows = R;
+  e.d = d;
+  e.out_f = c->logits;
+  e.ldo = c->cfg.vocab;
+  Gemm gm{c, s};
+  gm.run(c->h, d, {c->w_out}, c->cfg.vocab, d, PAIR_PLAIN, n, e);
+  ReadoutArgs ro{};
+  ro.rows = R;
+  ro.n = n;
+  ro.V = c->cfg.vocab;
+  ro.logits = c->logits;
+  ro.mode = 0;
+  ro.score_tok = io->tokens;
+  ro.logp = io->logp;
+  ro.temperature = io->temperature;
+  ro.top_k = io->top_k;
+  ro.logmu = io->logmu;
+  ro.logmu_beh = io->logmu_behaviour;
+  ro.ratio = io->ratio;
+  launch_readout(ro, s);
+  HIP_TRY(hipGetLastError());
+  return RLT_OK;
+}
+
+// ----------------------------------------------------------------------------
+// kernel-level parity hook (test-only)
+// ----------------------------------------------------------------------------
+
+extern "C" int rlt_dbg_gemm(rlt_ctx* c, const void* A, const void* W, int32_t M, int32_t N, int32_t K,
+                            float* out, void* stream) {
+  if (!c || !A || !W || !out) return fail(RLT_EINVAL, "null argument");
+  if (M < 1 || M > c->max_rows || N < 32 || N % 32 || K < 32 || K % 32 || K > 2 * c->cfg.d_model)
+    return fail(RLT_ESHAPE, "need 1 <= M <= max_rows, N and K multiples of 32, K <= 2*d_model");
+  hipStream_t s = (hipStream_t)stream;
+  // A goes through the padded workspace: the MFMA tiles read whole 16-row blocks
+  HIP_TRY(hipMemcpyAsync(c->X, A, (size_t)M * K * c->es, hipMemcpyDeviceToDevice, s));
+  Rows R{c->ident, c->ident, c->ones, M};
+  EpiArgs e{};
+  e.kind = EPI_STORE;
+  e.rows = R;
+  e.out_f = out;
+  e.ldo = N;
+  Gemm gm{c, s};
+  gm.run(c->X, K, {W}, N, K, PAIR_PLAIN, M, e);
+  HIP_TRY(hipGetLastError());
+  return RLT_OK;
+}

@@ -1,0 +1,238 @@
+// Internal declarations shared by the HIP kernels and the host side of the
+// library. Element type T is `float` (RLT_F32) or `uint16_t` holding bf16
+// bit patterns (RLT_BF16); the same T is used for weights, SWA cache,
+// encoder memory, e and the activations fed to matrix products.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rlt {
+
+// ----------------------------------------------------------------------------
+// device helpers
+// ----------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// round-to-nearest-even float -> bf16 (finite inputs; NaN stays NaN)
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x7fffffu)) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float to_f(T x);
+template <> __device__ __forceinline__ float to_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ float to_f<uint16_t>(uint16_t x) { return bf2f(x); }
+
+template <typename T> __device__ __forceinline__ T from_f(float x);
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ uint16_t from_f<uint16_t>(float x) { return f2bf(x); }
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+// Block-wide sum of one float per thread, fixed reduction order (wave
+// butterfly then waves in index order). blockDim.x must be a multiple of 64.
+__device__ __forceinline__ float block_sum(float v, float* scratch /* >= 16 floats */) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) scratch[w] = v;
+  __syncthreads();
+  float s = 0.f;
+  for (int i = 0; i < nw; ++i) s += scratch[i];
+  return s;
+}
+
+// ----------------------------------------------------------------------------
+// per-call row bookkeeping
+// ----------------------------------------------------------------------------
+
+// Slot i of a launch processes state row rows[i] at 1-based position
+// t_row[i] (0 = skip: the row had a device-detected error). src[i] indexes
+// the caller's per-sequence inputs/outputs (i itself for a decoder step,
+// the sequence id for a replay).
+struct Rows {
+  const int* rows;
+  const int* src;
+  const int* t_row;
+  int n;
+};
+
+// e_t of slot i: e + src[i] * sb + (t - 1) * st elements.
+struct EIn {
+  const void* p;
+  int64_t sb, st;
+};
+
+// ----------------------------------------------------------------------------
+// matrix products  Y[m][c] = sum_k A[m][k] W(c)[k]
+// ----------------------------------------------------------------------------
+
+enum Pairing { PAIR_PLAIN = 0, PAIR_ROPE = 1, PAIR_DUAL = 2 };
+
+struct GemmArgs {
+  const void* A;          // [M_pad][lda] activations (T)
+  int64_t lda;
+  const void* W[3];       // weight segments, each [seg_rows][K] (T), natural layout
+  int nseg, seg_rows;
+  int K;
+  int npairs;             // output handled as pairs of 16-column blocks
+  int pairing;            // Pairing
+  int dh;                 // head width for PAIR_ROPE
+  int M, M_pad;           // valid rows / allocated rows of A
+  int S;                  // splits of K across workgroups (bf16 path)
+  int kslice;             // K elements per (split, wave) slice, multiple of 32
+  float* partial;         // [S][M_pad][Nv] when S > 1
+  int Nv;                 // nseg * seg_rows
+};
+
+// virtual column blocks (16 columns each) of pair p
+__device__ __forceinline__ void pair_blocks(const GemmArgs& g, int p, int& ba, int& bb) {
+  if (g.pairing == PAIR_PLAIN) {
+    ba = 2 * p;
+    bb = 2 * p + 1;
+  } else if (g.pairing == PAIR_ROPE) {
+    const int per = g.dh / 32;           // pairs per head
+    const int h = p / per, j = p - h * per;
+    ba = h * (g.dh / 16) + j;
+    bb = ba + per;
+  } else {
+    ba = p;
+    bb = p + g.seg_rows / 16;
+  }
+}
+
+// Epilogue kinds (functors live in the GEMM translation unit).
+enum EpiKind {
+  EPI_STORE = 0,   // out[m][c] = v                          (logits)
+  EPI_QKV = 1,     // q (f32, rotary), k (T, rotary), v (T)   eqs (2.12)-(2.13)
+  EPI_QROT = 2,    // q (f32, rotary)                          eq (2.15) query
+  EPI_RESID = 3,   // z[m][c] += v                             residual adds
+  EPI_SWIGLU = 4,  // act[m][c] = silu(gate) * up              eq (2.16)
+  EPI_MGATE = 5,   // g[m][c] = sigmoid(v + b_g[c])           eq (2.10)
+  EPI_MOUT = 6,    // z[m][c] = e + alpha * g * v              eq (2.11)
+  EPI_CONVEX = 7   // g = sigmoid(v + b); z = g e + (1-g) s
+};
+
+struct EpiArgs {
+  int kind;
+  Rows rows;
+  int d, dh, H;
+  int rope;                 // apply rotary transform
+  const double* inv_freq;   // [dh/2] theta^(-2i/dh)
+  float* out_f;             // f32 output (q, logits, z, g)
+  int64_t ldo;
+  void* out_k;              // T outputs (k, act)
+  void* out_v;
+  const float* bias;        // b_g
+  const float* gbuf;        // merge gate
+  float alpha;
+  EIn e;                    // merge: e_t
+  const float* s_state;     // convex merge: s_{t-1} rows
+};
+
+// ----------------------------------------------------------------------------
+// host-side launchers (defined in the .hip translation units)
+// ----------------------------------------------------------------------------
+
+struct AttnArgs {
+  Rows rows;
+  int d, H, dh;
+  int hpw;                  // heads per workgroup
+  float qscale;             // log2(e) / sqrt(dh)
+  const float* q;           // [n][d]
+  // SWA
+  const void* kc;           // [n][d] current k (T)
+  const void* vc;
+  void* ring_k;             // layer base: [B_cap][W-1][d]
+  void* ring_v;
+  int W;
+  // cross-attention
+  const void* mk;           // group base (row stride sb, position stride st)
+  const void* mv;
+  int64_t sb, st;
+  int chunk;                // positions per partial
+  int nch;                  // chunk slots per row in `part`
+  float* part;              // [n][nch][H][dh + 2]
+  void* out;                // [n][d] (T) attention output
+};
+
+void launch_gemm(int dtype, const GemmArgs& g, const EpiArgs& e, hipStream_t s);
+void launch_swa(int dtype, const AttnArgs& a, hipStream_t s);
+void launch_xattn(int dtype, const AttnArgs& a, hipStream_t s);
+void launch_xcombine(int dtype, const AttnArgs& a, hipStream_t s);
+
+struct MiscArgs {
+  Rows rows;
+  int n, d;
+  float eps;
+  float* s_state;                 // [B_cap][d]
+  int* pos;
+  int* pending;
+  const int* mem_len;
+  const int* consume_tok;
+  int* t_row_out;
+  int* err;                       // device-visible error word (host mapped)
+  const float* gain;
+  const float* z;                 // [n][d]
+  void* out;                      // T [n][ld_out]
+  int64_t ld_out;
+  EIn e;
+  int merge_kind;
+  float* s_out;                   // optional [n][d]
+  float* s_trace;                 // optional replay trace
+  int64_t s_trace_sb;
+  int max_t;                      // largest position the workspace supports
+  int B_cap;                      // rows in the state buffers
+};
+
+void launch_prestep(const MiscArgs& a, hipStream_t s);
+void launch_merge_prep(int dtype, const MiscArgs& a, hipStream_t s);
+void launch_rmsnorm(int dtype, const MiscArgs& a, hipStream_t s);
+void launch_final(int dtype, const MiscArgs& a, hipStream_t s);
+void launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s);
+
+struct ReadoutArgs {
+  Rows rows;
+  int n, V;
+  const float* logits;       // [n][V]
+  int32_t* argmax;
+  // scoring: token/out located per slot
+  int mode;                  // 0: step (arrays by slot), 1: replay (by src,t)
+  const int* score_tok;      // step: [n]; replay: tokens base
+  int64_t tok_sb;
+  float* logp;               // step: [n]; replay: base
+  int64_t logp_sb;
+  const int* split;          // replay: [B] first scored position
+  // sampling / behaviour
+  const float* uniform;      // [n] or null
+  float temperature;
+  int top_k;
+  int32_t* sample_tok;
+  float* sample_logmu;
+  float* logmu;              // behaviour log-prob of score_tok (score call)
+  const float* logmu_beh;    // recorded behaviour log-probs (score call)
+  float* ratio;
+};
+void launch_readout(const ReadoutArgs& a, hipStream_t s);
+
+struct PostArgs {
+  Rows rows;
+  int n;
+  int* pos;
+  int* pending;
+  const int32_t* next_tok;   // token to record as pending (DEFER) or null
+};
+void launch_poststep(const PostArgs& a, hipStream_t s);
+void launch_init(int dtype, const int* rows, int n, const float* s_star, float* s_state, int* pos,
+                 int* pending, void* ring_k, void* ring_v, int L, int B_cap, int W, int d,
+                 int poison, hipStream_t s);
+void launch_set_pending(const int* rows, const int* src, int n, const int* tokens, int64_t tok_sb,
+                        const int* last_index, int* pending, hipStream_t s);
+void launch_replay_rows(const int* rows, const int* src, int n, int tick, int* t_row, int* pos,
+                        const int* mem_len, int* err, hipStream_t s);
+
+}  // namespace rlt

@@ -1,0 +1,227 @@
+"""Device-memory plumbing around the C ABI.
+
+PyTorch provides device buffers and the stream handle; every step of the
+decoder transition runs in ``librlt.so``. Nothing here computes any part of
+the method.
+
+Parameter names (natural [out, in] layout):
+  s_star [d]; merge.norm [d] (gated); merge.wg [d, 2d]; merge.bg [d];
+  merge.ws [d, d] (gated); layer.{l}.{norm_s, wq, wk, wv, wo, norm_m, wqm, wom,
+  norm_d, w_gate, w_up, w_down}; out.norm [d]; out.w [V, d].
+Matrices are float32 (dtype "f32") or bfloat16 ("bf16"); vectors float32.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import _abi as A
+
+_MATRICES = ("wq", "wk", "wv", "wo", "wqm", "wom", "w_gate", "w_up", "w_down")
+_LAYER_VECS = ("norm_s", "norm_m", "norm_d")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def to_device(a, dtype: str, device="cuda") -> torch.Tensor:
+    """numpy (float32, or uint16 bf16 bit patterns) or tensor -> device tensor."""
+    if isinstance(a, torch.Tensor):
+        return a.to(device)
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    if a.dtype == np.float32:
+        return torch.from_numpy(a).to(device)
+    if a.dtype == np.int32:
+        return torch.from_numpy(a).to(device)
+    raise TypeError("unsupported array dtype %s" % a.dtype)
+
+
+def current_stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+@dataclass
+class ModelConfig:
+    L: int
+    d: int
+    H: int
+    dh: int
+    W: int
+    G: int
+    F: int
+    V: int
+    dtype: str = "bf16"
+    merge: str = "gated"
+    alpha: float = 0.5
+    eps: float = 1e-6
+    rope_theta: float = 10000.0
+    pos: str = "rope"
+    version: int = 1
+
+    def to_c(self) -> A.rlt_config:
+        return A.rlt_config(self.L, self.d, self.H, self.dh, self.W, self.G, self.F, self.V,
+                            A.RLT_MERGE_GATED if self.merge == "gated" else A.RLT_MERGE_CONVEX,
+                            A.RLT_POS_ROPE if self.pos == "rope" else A.RLT_POS_NONE,
+                            A.RLT_BF16 if self.dtype == "bf16" else A.RLT_F32,
+                            self.alpha, self.eps, self.rope_theta, self.version)
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+
+class DecoderState:
+    """Device buffers of B_cap rows: s, SWA ring, pos, pending."""
+
+    def __init__(self, cfg: ModelConfig, B_cap: int, device="cuda"):
+        self.cfg = cfg
+        self.B_cap = B_cap
+        sizes = A.rlt_state_layout(cfg.to_c(), B_cap)
+        es = 2 if cfg.dtype == "bf16" else 4
+        ring_elems = sizes[1] // es
+        self.s = torch.empty((B_cap, cfg.d), dtype=torch.float32, device=device)
+        self.ring_k = torch.empty(max(ring_elems, 1), dtype=cfg.torch_dtype, device=device)
+        self.ring_v = torch.empty(max(ring_elems, 1), dtype=cfg.torch_dtype, device=device)
+        self.pos = torch.zeros(B_cap, dtype=torch.int32, device=device)
+        self.pending = torch.full((B_cap,), -1, dtype=torch.int32, device=device)
+        self.version = cfg.version
+
+    def c(self) -> A.rlt_state:
+        return A.rlt_state(self.s.data_ptr(), self.ring_k.data_ptr(), self.ring_v.data_ptr(),
+                           self.pos.data_ptr(), self.pending.data_ptr(), self.B_cap, self.version)
+
+    def ring(self, which: str) -> torch.Tensor:
+        """View [L, B_cap, W-1, d] of the keys ("k") or values ("v")."""
+        c = self.cfg
+        t = self.ring_k if which == "k" else self.ring_v
+        return t[: c.L * self.B_cap * (c.W - 1) * c.d].view(c.L, self.B_cap, c.W - 1, c.d)
+
+
+class Decoder:
+    """A context (``rlt_create``) over device copies of the parameters."""
+
+    def __init__(self, cfg: ModelConfig, params: Dict[str, object], max_rows: int, max_ctx: int,
+                 device="cuda"):
+        self.cfg = cfg
+        self.device = device
+        self.params = {}
+        for k, v in params.items():
+            self.params[k] = to_device(v, cfg.dtype, device).contiguous()
+        p = self.params
+        L = cfg.L
+        self._arrays = {}
+        for name in _MATRICES + _LAYER_VECS:
+            arr = (A.P * L)(*[p["layer.%d.%s" % (l, name)].data_ptr() for l in range(L)])
+            self._arrays[name] = arr
+        gated = cfg.merge == "gated"
+        w = A.rlt_weights()
+        w.s_star = p["s_star"].data_ptr()
+        w.merge_norm = p["merge.norm"].data_ptr() if gated else None
+        w.merge_wg = p["merge.wg"].data_ptr()
+        w.merge_bg = p["merge.bg"].data_ptr()
+        w.merge_ws = p["merge.ws"].data_ptr() if gated else None
+        for name, arr in self._arrays.items():
+            setattr(w, name, C.cast(arr, C.POINTER(A.P)))
+        w.out_norm = p["out.norm"].data_ptr()
+        w.w_out = p["out.w"].data_ptr()
+        self._w = w
+        self._cfg_c = cfg.to_c()
+        self.max_rows, self.max_ctx = max_rows, max_ctx
+        self.ctx = A.rlt_create(self._cfg_c, w, max_rows, max_ctx)
+
+    def close(self):
+        if getattr(self, "ctx", None):
+            A.rlt_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- entry points --------------------------------------------------------
+    def init_state(self, st: DecoderState, rows: torch.Tensor, poison: bool = False, stream=None):
+        stc = st.c()
+        A.check(A.rlt_init_state(self.ctx, stc, rows.data_ptr(), rows.numel(),
+                                 A.RLT_INIT_POISON if poison else 0,
+                                 current_stream() if stream is None else stream), "rlt_init_state")
+
+    @staticmethod
+    def memory(k: torch.Tensor, v: torch.Tensor, mem_len: torch.Tensor) -> A.rlt_memory:
+        """k, v shaped [G, B, T, d] (contiguous); mem_len int32 [B]."""
+        G, B, T, d = k.shape
+        return A.rlt_memory(k.data_ptr(), v.data_ptr(), B * T * d, T * d, d, mem_len.data_ptr())
+
+    def step(self, st: DecoderState, rows: torch.Tensor, e: torch.Tensor, mem: A.rlt_memory, *,
+             consume_tok=None, s_out=None, logits=None, argmax=None, score_tok=None, logp=None,
+             uniform=None, temperature=1.0, top_k=0, sample_tok=None, sample_logmu=None,
+             z_trace=None, graph=False, defer=False, stream=None) -> int:
+        io = A.rlt_step_io()
+        io.n = rows.numel()
+        io.rows = rows.data_ptr()
+        io.e = e.data_ptr()
+        io.mem = mem
+        io.consume_tok = _ptr(consume_tok)
+        io.s_out = _ptr(s_out)
+        io.logits = _ptr(logits)
+        io.argmax = _ptr(argmax)
+        io.score_tok = _ptr(score_tok)
+        io.logp = _ptr(logp)
+        io.uniform = _ptr(uniform)
+        io.temperature = temperature
+        io.top_k = top_k
+        io.sample_tok = _ptr(sample_tok)
+        io.sample_logmu = _ptr(sample_logmu)
+        io.z_trace = _ptr(z_trace)
+        io.flags = (A.RLT_STEP_GRAPH if graph else 0) | (A.RLT_STEP_DEFER if defer else 0)
+        self._keep = (io, st.c())
+        return A.rlt_decoder_step(self.ctx, self._keep[1], io, current_stream() if stream is None else stream)
+
+    def replay(self, st: DecoderState, lens: np.ndarray, splits: np.ndarray, e: torch.Tensor,
+               mem: A.rlt_memory, tokens: torch.Tensor, logp: torch.Tensor, rows: Optional[np.ndarray] = None,
+               s_trace: Optional[torch.Tensor] = None, stream=None) -> int:
+        """e [B, T, d]; tokens int32 [B, T]; logp float32 [B, T]; s_trace [B, T, d]."""
+        lens = np.ascontiguousarray(lens, dtype=np.int32)
+        splits = np.ascontiguousarray(splits, dtype=np.int32)
+        io = A.rlt_replay_io()
+        io.B = len(lens)
+        rows_keep = None if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
+        io.rows_host = None if rows_keep is None else rows_keep.ctypes.data
+        io.len_host = lens.ctypes.data
+        io.split_host = splits.ctypes.data
+        io.e = e.data_ptr()
+        io.e_stride_b = e.stride(0)
+        io.e_stride_t = e.stride(1)
+        io.mem = mem
+        io.tokens = tokens.data_ptr()
+        io.tok_stride_b = tokens.stride(0)
+        io.logp = logp.data_ptr()
+        io.logp_stride_b = logp.stride(0)
+        if s_trace is not None:
+            io.s_trace = s_trace.data_ptr()
+            io.s_stride_b = s_trace.stride(0)
+        stc = st.c()
+        return A.rlt_replay_sequence(self.ctx, stc, io, current_stream() if stream is None else stream)
+
+    def score(self, s: torch.Tensor, tokens: torch.Tensor, logp: torch.Tensor, *, temperature=1.0, top_k=0,
+              logmu=None, logmu_behaviour=None, ratio=None, stream=None) -> int:
+        io = A.rlt_score_io(s.shape[0], s.data_ptr(), tokens.data_ptr(), logp.data_ptr(), temperature, top_k,
+                            _ptr(logmu), _ptr(logmu_behaviour), _ptr(ratio))
+        return A.rlt_score_logprobs(self.ctx, io, current_stream() if stream is None else stream)
+
+    def sync_error(self, stream=None) -> int:
+        return A.rlt_sync_error(self.ctx, current_stream() if stream is None else stream)
+
+    def dbg_gemm(self, Amat: torch.Tensor, W: torch.Tensor, out: torch.Tensor, stream=None) -> int:
+        M, K = Amat.shape
+        N = W.shape[0]
+        return A.rlt_dbg_gemm(self.ctx, Amat.data_ptr(), W.data_ptr(), M, N, K, out.data_ptr(),
+                              current_stream() if stream is None else stream)
