@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Benchmark of the batched recurrent decoder state transition on one MI355X.
+
+Workload (default ``reference_depth``): L_D=48, d=2048, 16 heads x 128,
+W=256, G=1, SwiGLU 5504, vocab 32000, B=128 sequences, T=4096, bf16 weights
+N(0, 0.02/sqrt(96)), bf16 encoder memory [B, T, d]. One step = one
+``rlt_decoder_step`` over all B rows (merge, 48 decoder blocks, final norm,
+vocabulary projection, argmax), captured once in a hipGraph and replayed.
+
+The per-step cost is affine in the position t (the prefix cross-attention
+reads t memory entries per row and layer), so the mean cost over a full run
+t = 1..T equals the cost at t = T/2: the timed steps are centred on T/2,
+starting from a synthetically pre-filled state (full SWA ring, pos set).
+
+Printed: one JSON line with the metric, the dominant kernel's roofline
+(algorithmic bytes / live HIP-event duration) and the CPU oracle baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def matrix_params(wl) -> int:
+    d, F, V, L = wl.d, wl.F, wl.V, wl.L
+    merge = 3 * d * d if wl.merge == "gated" else 2 * d * d
+    return merge + L * (6 * d * d + 3 * d * F) + V * d
+
+
+def step_bytes(wl, B: int, t: int, es: int) -> dict:
+    """Algorithmic HBM bytes of one step over B rows at position t."""
+    weights = matrix_params(wl) * es
+    hist = min(t - 1, wl.W - 1)
+    ring = wl.L * B * (hist * 2 * wl.d * es + (2 * wl.d * es if wl.W > 1 else 0))
+    memory = wl.L * B * t * 2 * wl.d * es
+    small = B * (wl.d * es + 2 * wl.d * 4)
+    return dict(weights=weights, ring=ring, memory=memory, small=small,
+                total=weights + ring + memory + small)
+
+
+def cpu_baseline(wl, t0: int, budget_s: float, raw) -> dict:
+    """The float64 oracle timed on this host on a bounded sample: one
+    sequence, consecutive transitions from a pre-filled state at t0."""
+    import numpy as np
+    import synth
+    from oracle import Config, Memory, Oracle, state_from_ring
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+
+    def widen(a):
+        return synth.bf16_bits_to_f32(a).astype(np.float64) if a.dtype == np.uint16 else a.astype(np.float64)
+
+    cfg = Config(L=wl.L, d=wl.d, H=wl.H, dh=wl.dh, W=wl.W, G=wl.G, F=wl.F, V=wl.V, merge=wl.merge,
+                 alpha=wl.alpha, eps=wl.eps, rope_theta=wl.rope_theta, pos=wl.pos)
+    orc = Oracle(cfg, {k: widen(v) for k, v in raw.items()})
+    nT = t0 + 64
+    mem = Memory([widen(synth.make_memory(wl, "k", g, 0, 1, nT)[0]) for g in range(wl.G)],
+                 [widen(synth.make_memory(wl, "v", g, 0, 1, nT)[0]) for g in range(wl.G)])
+    rk = np.stack([widen(synth.make_ring_prefill(wl, "k", l, 0, 1)[0]) for l in range(wl.L)])
+    rv = np.stack([widen(synth.make_ring_prefill(wl, "v", l, 0, 1)[0]) for l in range(wl.L)])
+    s0 = widen(synth.normal(wl.seed, "s_prefill", (wl.d,)))
+    st = state_from_ring(cfg, s0, t0 - 1, rk, rv)
+    E = widen(synth.make_e(wl, 0, 1, nT)[0])
+    n = 0
+    t_start = time.perf_counter()
+    while True:
+        st = orc.transition(st, E[st.pos], mem)
+        orc.logits(st.s)
+        n += 1
+        el = time.perf_counter() - t_start
+        if el >= budget_s or n >= 60:
+            break
+    return {"value": n / el, "unit": "transitions/s", "cores": int(cores), "kind": "oracle",
+            "sample": "float64 oracle, 1 sequence x %d transitions (incl. readout) at t=%d..%d from a "
+                      "pre-filled state, %.1f s" % (n, t0, t0 + n - 1, el)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="reference_depth")
+    ap.add_argument("--batch", type=int, default=0, help="override B")
+    ap.add_argument("--t-center", type=int, default=0, help="centre of the timed positions (default T/2)")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--profile-steps", type=int, default=8)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        log("bench.py measures one GPU only: this build has no multi-GPU path "
+            "(sequences shard across GPUs with no per-step exchange; see DESIGN.md). Use --gpus 1.")
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import synth
+    from stateful_sequence_model_amd import Decoder, DecoderState, ModelConfig, _abi, to_device
+
+    wl = synth.PRESETS[args.workload]
+    if args.batch:
+        wl = wl.with_(B=args.batch)
+    B, T = wl.B, wl.T
+    es = 2 if wl.dtype == "bf16" else 4
+    K, Wu = args.steps, args.warmup
+    t_center = args.t_center or T // 2
+    pos0 = max(0, t_center - K // 2 - Wu)
+    assert pos0 + Wu + K <= T, "timed positions exceed T"
+    torch.cuda.set_device(0)
+    dev = "cuda"
+
+    tg = time.perf_counter()
+    raw = synth.make_weights(wl)
+    log("weights generated in %.1fs" % (time.perf_counter() - tg))
+    cfg = ModelConfig(L=wl.L, d=wl.d, H=wl.H, dh=wl.dh, W=wl.W, G=wl.G, F=wl.F, V=wl.V, dtype=wl.dtype,
+                      merge=wl.merge, alpha=wl.alpha, eps=wl.eps, rope_theta=wl.rope_theta, pos=wl.pos)
+    dec = Decoder(cfg, raw, max_rows=B, max_ctx=T)
+    st = DecoderState(cfg, B)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wl.seed)
+    tdt = cfg.torch_dtype
+    # encoder memory [G, B, T, d] and a pre-filled state (values N(0,1))
+    mk = torch.randn((wl.G, B, T, wl.d), generator=gen, device=dev, dtype=torch.float32).to(tdt)
+    mv = torch.randn((wl.G, B, T, wl.d), generator=gen, device=dev, dtype=torch.float32).to(tdt)
+    for l in range(wl.L):
+        st.ring("k")[l].copy_(torch.randn(st.ring("k")[l].shape, generator=gen, device=dev).to(tdt))
+        st.ring("v")[l].copy_(torch.randn(st.ring("v")[l].shape, generator=gen, device=dev).to(tdt))
+    e = torch.randn((B, wl.d), generator=gen, device=dev).to(tdt)
+    mem_len = torch.full((B,), T, dtype=torch.int32, device=dev)
+    mem = Decoder.memory(mk, mv, mem_len)
+    rows = torch.arange(B, dtype=torch.int32, device=dev)
+    argmax = torch.empty(B, dtype=torch.int32, device=dev)
+
+    def reset(pos):
+        st.s.copy_(torch.randn(st.s.shape, generator=gen, device=dev))
+        st.pos.fill_(pos)
+        st.pending.fill_(-1)
+
+    stream = torch.cuda.Stream()
+    graph = not args.no_graph
+    with torch.cuda.stream(stream):
+        reset(pos0)
+        torch.cuda.synchronize()
+        for _ in range(Wu):
+            _abi.check(dec.step(st, rows, e, mem, argmax=argmax, graph=graph), "rlt_decoder_step")
+        torch.cuda.synchronize()
+        t_first = int(st.pos[0].item()) + 1
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(K):
+            _abi.check(dec.step(st, rows, e, mem, argmax=argmax, graph=graph), "rlt_decoder_step")
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1)
+        _abi.check(dec.sync_error(), "device error")
+        assert int(st.pos[0].item()) == t_first + K - 1
+        # live per-kernel timing (direct launches, same positions as the timed steps)
+        P = max(1, min(args.profile_steps, K))
+        reset(t_first - 1)
+        torch.cuda.synchronize()
+        _abi.check(_abi.rlt_dbg_profile(dec.ctx, 1), "profile")
+        for _ in range(P):
+            _abi.check(dec.step(st, rows, e, mem, argmax=argmax, graph=False), "rlt_decoder_step")
+        torch.cuda.synchronize()
+        prof = {name: _abi.rlt_dbg_profile_read(dec.ctx, i) for i, name in enumerate(_abi.PROF_NAMES)}
+        _abi.check(_abi.rlt_dbg_profile(dec.ctx, 0), "profile")
+
+    ms_step = ms / K
+    t_mid = t_first + (K - 1) / 2.0
+    value = B * K / (ms / 1e3)
+    sb = step_bytes(wl, B, int(round(t_mid)), es)
+    # dominant kernel: prefix cross-attention partials; unit = one memory
+    # position of one row (K and V, 2*d elements)
+    x_ms, x_n = prof["xattn"]
+    x_avg_ms = x_ms / max(x_n, 1)
+    t_prof_mid = t_first + (P - 1) / 2.0
+    x_bytes = B * t_prof_mid * 2 * wl.d * es
+    achieved = x_bytes / (x_avg_ms / 1e3) / 1e9
+    breakdown = {k: round(v[0] / P, 4) for k, v in prof.items()}
+    log("ms/step %.3f  transitions/s %.1f  step algorithmic GB/s %.1f (%.1f%% of 8 TB/s)" %
+        (ms_step, value, sb["total"] / (ms_step / 1e3) / 1e9, 100 * sb["total"] / (ms_step / 1e3) / 8e12))
+    log("per-step kernel ms (direct launches):", breakdown)
+    log("xattn: %d launches, avg %.4f ms, %.1f GB/s" % (x_n, x_avg_ms, achieved))
+
+    out = {
+        "metric": "decoder state-transitions/sec (seq*token) at L_D=%d" % wl.L,
+        "value": round(value, 2),
+        "unit": "transitions/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wu,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "L_D": wl.L, "d": wl.d, "heads": "%dx%d" % (wl.H, wl.dh), "W": wl.W,
+                   "G": wl.G, "ffn": wl.F, "vocab": wl.V, "batch": B, "T": T,
+                   "timed_positions": [t_first, t_first + K - 1], "hipgraph": graph},
+        "roofline": {"bound": "hbm", "kernel": "k_xattn (prefix cross-attention)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_ms": round(x_avg_ms, 5), "algorithmic_bytes_per_launch": int(x_bytes)},
+        "step_roofline": {"algorithmic_bytes": int(sb["total"]),
+                          "achieved_GBs": round(sb["total"] / (ms_step / 1e3) / 1e9, 1),
+                          "frac": round(sb["total"] / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                          "bytes_split": {k: int(v) for k, v in sb.items() if k != "total"}},
+        "kernel_ms_per_step": breakdown,
+    }
+    if not args.no_cpu_baseline:
+        del mk, mv
+        torch.cuda.empty_cache()
+        log("timing the CPU oracle (%.0f s budget)..." % args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(wl, t_center, args.cpu_seconds, raw)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -24,6 +24,26 @@ extern "C" {
 int rlt_dbg_gemm(rlt_ctx* ctx, const void* A, const void* W, int32_t M, int32_t N, int32_t K, float* out,
                  void* stream);
 
+/* Kernel classes for the timing hook below. */
+enum {
+  RLT_PROF_XATTN = 0,     /* prefix cross-attention partials (eq. 2.15) */
+  RLT_PROF_XCOMBINE = 1,  /* ordered merge of the cross-attention partials */
+  RLT_PROF_SWA = 2,       /* SWA over the ring cache + insert (eq. 2.14) */
+  RLT_PROF_GEMM = 3,      /* every matrix product incl. its split reduction */
+  RLT_PROF_NORM = 4,      /* RMSNorms, merge preparation, state write-back */
+  RLT_PROF_READOUT = 5,   /* log-sum-exp / argmax / sampling */
+  RLT_PROF_NCLASS = 6
+};
+
+/* Timing hook for benchmarks: while enabled, every launch of a kernel class
+ * made by non-captured calls is bracketed by two HIP events recorded on the
+ * launch stream. enable != 0 also clears previous records. */
+int rlt_dbg_profile(rlt_ctx* ctx, int32_t enable);
+
+/* HOST, synchronising: total milliseconds and number of bracketed launches of
+ * one kernel class since profiling was enabled. */
+int rlt_dbg_profile_read(rlt_ctx* ctx, int32_t kernel_class, double* total_ms, int64_t* launches);
+
 #ifdef __cplusplus
 }
 #endif

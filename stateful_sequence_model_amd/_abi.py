@@ -84,7 +84,12 @@ _SIGS = {
     "rlt_score_logprobs": (C.c_int, [P, C.POINTER(rlt_score_io), P]),
     "rlt_sync_error": (C.c_int, [P, P]),
     "rlt_dbg_gemm": (C.c_int, [P, P, P, i32, i32, i32, P, P]),
+    "rlt_dbg_profile": (C.c_int, [P, i32]),
+    "rlt_dbg_profile_read": (C.c_int, [P, i32, C.POINTER(C.c_double), C.POINTER(C.c_int64)]),
 }
+
+RLT_PROF_XATTN, RLT_PROF_XCOMBINE, RLT_PROF_SWA, RLT_PROF_GEMM, RLT_PROF_NORM, RLT_PROF_READOUT = range(6)
+PROF_NAMES = ["xattn", "xcombine", "swa", "gemm", "norm", "readout"]
 
 
 def lib():
@@ -160,6 +165,16 @@ def rlt_sync_error(ctx: int, stream: int) -> int:
 
 def rlt_dbg_gemm(ctx: int, A: int, W: int, M: int, N: int, K: int, out: int, stream: int) -> int:
     return lib().rlt_dbg_gemm(ctx, A, W, M, N, K, out, stream)
+
+
+def rlt_dbg_profile(ctx: int, enable: int) -> int:
+    return lib().rlt_dbg_profile(ctx, enable)
+
+
+def rlt_dbg_profile_read(ctx: int, kind: int):
+    ms, n = C.c_double(), C.c_int64()
+    check(lib().rlt_dbg_profile_read(ctx, kind, C.byref(ms), C.byref(n)), "rlt_dbg_profile_read")
+    return ms.value, n.value
 
 
 def exported_symbols():

@@ -69,7 +69,48 @@ struct rlt_ctx {
   hipGraph_t graph;
   hipGraphExec_t graph_exec;
   std::vector<unsigned char> graph_key;
+  // optional per-kernel-class timing (HIP events on the launch stream)
+  bool prof_on;
+  std::vector<hipEvent_t> prof_ev;
+  size_t prof_next;
+  std::vector<std::pair<int, size_t>> prof_rec;  // (class, index of the start event)
 };
+
+namespace {
+
+// Brackets the launches of one kernel class with two events when timing
+// is on (never inside a graph capture).
+struct Prof {
+  rlt_ctx* c;
+  int kind;
+  hipStream_t s;
+  size_t i0 = 0;
+  bool on;
+  size_t take() {
+    if (c->prof_next >= c->prof_ev.size()) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) return (size_t)-1;
+      c->prof_ev.push_back(e);
+    }
+    return c->prof_next++;
+  }
+  Prof(rlt_ctx* c_, int k, hipStream_t s_) : c(c_), kind(k), s(s_), on(c_->prof_on) {
+    if (on) {
+      i0 = take();
+      if (i0 == (size_t)-1) on = false;
+      else (void)hipEventRecord(c->prof_ev[i0], s);
+    }
+  }
+  ~Prof() {
+    if (!on) return;
+    const size_t i1 = take();
+    if (i1 != i0 + 1) return;
+    (void)hipEventRecord(c->prof_ev[i1], s);
+    c->prof_rec.push_back({kind, i0});
+  }
+};
+
+}  // namespace
 
 // ----------------------------------------------------------------------------
 // helpers
@@ -148,6 +189,7 @@ extern "C" void rlt_destroy(rlt_ctx* c) {
   if (c->graph) (void)hipGraphDestroy(c->graph);
   if (c->err_host) (void)hipHostFree(c->err_host);
   if (c->host_stage) (void)hipHostFree(c->host_stage);
+  for (hipEvent_t e : c->prof_ev) (void)hipEventDestroy(e);
   delete c;
 }
 
@@ -317,6 +359,7 @@ struct Gemm {
       const int per = (K + 4 * S - 1) / (4 * S);
       g.kslice = (per + 31) / 32 * 32;
     }
+    Prof pf(c, RLT_PROF_GEMM, s);
     launch_gemm(c->dt, g, e, s);
   }
 };
@@ -370,7 +413,7 @@ void enqueue_transition(rlt_ctx* c, const StepPlan& P, hipStream_t s) {
   m.gain = c->merge_norm;
   m.out = c->X;
   m.ld_out = 2 * d;
-  launch_merge_prep(c->dt, m, s);
+  { Prof pf(c, RLT_PROF_NORM, s); launch_merge_prep(c->dt, m, s); }
   if (cf.merge_kind == RLT_MERGE_GATED) {
     EpiArgs e = E0;
     e.kind = EPI_MGATE;
@@ -412,7 +455,7 @@ void enqueue_transition(rlt_ctx* c, const StepPlan& P, hipStream_t s) {
     m.gain = c->norm_s[l];
     m.out = c->h;
     m.ld_out = d;
-    launch_rmsnorm(c->dt, m, s);
+    { Prof pf(c, RLT_PROF_NORM, s); launch_rmsnorm(c->dt, m, s); }
     {
       EpiArgs e = E0;
       e.kind = EPI_QKV;
@@ -427,7 +470,7 @@ void enqueue_transition(rlt_ctx* c, const StepPlan& P, hipStream_t s) {
     at.ring_k = (char*)P.st->ring_k + l * ring_layer;
     at.ring_v = (char*)P.st->ring_v + l * ring_layer;
     at.out = c->o;
-    launch_swa(c->dt, at, s);
+    { Prof pf(c, RLT_PROF_SWA, s); launch_swa(c->dt, at, s); }
     {
       EpiArgs e = E0;
       e.kind = EPI_RESID;
@@ -437,7 +480,7 @@ void enqueue_transition(rlt_ctx* c, const StepPlan& P, hipStream_t s) {
     }
     // ---- cross-attention sublayer [eq. (2.15)] ----
     m.gain = c->norm_m[l];
-    launch_rmsnorm(c->dt, m, s);
+    { Prof pf(c, RLT_PROF_NORM, s); launch_rmsnorm(c->dt, m, s); }
     {
       EpiArgs e = E0;
       e.kind = EPI_QROT;
@@ -448,8 +491,8 @@ void enqueue_transition(rlt_ctx* c, const StepPlan& P, hipStream_t s) {
     at.q = c->qm;
     at.mk = (const char*)P.mem.k + (size_t)g * P.mem.stride_g * es;
     at.mv = (const char*)P.mem.v + (size_t)g * P.mem.stride_g * es;
-    launch_xattn(c->dt, at, s);
-    launch_xcombine(c->dt, at, s);
+    { Prof pf(c, RLT_PROF_XATTN, s); launch_xattn(c->dt, at, s); }
+    { Prof pf(c, RLT_PROF_XCOMBINE, s); launch_xcombine(c->dt, at, s); }
     {
       EpiArgs e = E0;
       e.kind = EPI_RESID;
@@ -459,7 +502,7 @@ void enqueue_transition(rlt_ctx* c, const StepPlan& P, hipStream_t s) {
     }
     // ---- FFN sublayer [eq. (2.16)] ----
     m.gain = c->norm_d[l];
-    launch_rmsnorm(c->dt, m, s);
+    { Prof pf(c, RLT_PROF_NORM, s); launch_rmsnorm(c->dt, m, s); }
     {
       EpiArgs e = E0;
       e.kind = EPI_SWIGLU;
@@ -480,7 +523,7 @@ void enqueue_transition(rlt_ctx* c, const StepPlan& P, hipStream_t s) {
   m.s_out = P.s_out;
   m.s_trace = P.s_trace;
   m.s_trace_sb = P.s_trace_sb;
-  launch_final(c->dt, m, s);
+  { Prof pf(c, RLT_PROF_NORM, s); launch_final(c->dt, m, s); }
   if (P.need_logits) {
     EpiArgs e = E0;
     e.kind = EPI_STORE;
@@ -488,7 +531,7 @@ void enqueue_transition(rlt_ctx* c, const StepPlan& P, hipStream_t s) {
     e.ldo = cf.vocab;
     gm.run(c->h, d, {c->w_out}, cf.vocab, d, PAIR_PLAIN, n, e);
   }
-  if (P.do_readout) launch_readout(P.ro, s);
+  if (P.do_readout) { Prof pf(c, RLT_PROF_READOUT, s); launch_readout(P.ro, s); }
 }
 
 int check_state(rlt_ctx* c, const rlt_state* st) {
@@ -612,7 +655,10 @@ extern "C" int rlt_decoder_step(rlt_ctx* c, rlt_state* st, const rlt_step_io* io
       c->graph = nullptr;
     }
     HIP_TRY(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
+    const bool prof = c->prof_on;
+    c->prof_on = false;
     rc = step_enqueue(c, st, io, s);
+    c->prof_on = prof;
     hipGraph_t g = nullptr;
     hipError_t ec = hipStreamEndCapture(s, &g);
     if (rc) {
@@ -782,5 +828,33 @@ extern "C" int rlt_dbg_gemm(rlt_ctx* c, const void* A, const void* W, int32_t M,
   Gemm gm{c, s};
   gm.run(c->X, K, {W}, N, K, PAIR_PLAIN, M, e);
   HIP_TRY(hipGetLastError());
+  return RLT_OK;
+}
+
+extern "C" int rlt_dbg_profile(rlt_ctx* c, int32_t enable) {
+  if (!c) return fail(RLT_EINVAL, "null context");
+  c->prof_on = enable != 0;
+  if (enable) {
+    c->prof_rec.clear();
+    c->prof_next = 0;
+  }
+  return RLT_OK;
+}
+
+extern "C" int rlt_dbg_profile_read(rlt_ctx* c, int32_t kind, double* total_ms, int64_t* launches) {
+  if (!c || !total_ms || !launches) return fail(RLT_EINVAL, "null argument");
+  if (kind < 0 || kind >= RLT_PROF_NCLASS) return fail(RLT_EINVAL, "kernel class");
+  double ms = 0.0;
+  int64_t cnt = 0;
+  for (const auto& r : c->prof_rec) {
+    if (r.first != kind) continue;
+    HIP_TRY(hipEventSynchronize(c->prof_ev[r.second + 1]));
+    float e = 0.f;
+    HIP_TRY(hipEventElapsedTime(&e, c->prof_ev[r.second], c->prof_ev[r.second + 1]));
+    ms += e;
+    ++cnt;
+  }
+  *total_ms = ms;
+  *launches = cnt;
   return RLT_OK;
 }
