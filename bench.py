@@ -91,6 +91,28 @@ def cpu_baseline(wl, t0: int, budget_s: float, raw) -> dict:
                       "pre-filled state, %.1f s" % (n, t0, t0 + n - 1, el)}
 
 
+def calibrate(torch, nbytes: int = 4 << 30, reps: int = 10) -> dict:
+    """Achievable HBM rates on this device: a plain copy (read + write) and
+    a read-only reduction over nbytes of bf16."""
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    res = {}
+    for name, fn, moved in (("copy", lambda: dst.copy_(src), 2 * nbytes),
+                            ("read_sum", lambda: src.sum(dtype=torch.float32), nbytes)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name + "_GBs"] = round(moved * reps / (e0.elapsed_time(e1) / 1e3) / 1e9, 1)
+    del src, dst
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -103,6 +125,8 @@ def main():
     ap.add_argument("--profile-steps", type=int, default=8)
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="also time a plain 4 GiB device copy and read-only sum (achievable HBM rates)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -227,6 +251,8 @@ def main():
                           "bytes_split": {k: int(v) for k, v in sb.items() if k != "total"}},
         "kernel_ms_per_step": breakdown,
     }
+    if args.calibrate:
+        out["calibration"] = calibrate(torch)
     if not args.no_cpu_baseline:
         del mk, mv
         torch.cuda.empty_cache()

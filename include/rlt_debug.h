@@ -19,7 +19,7 @@ extern "C" {
  * computed by the same kernel, K split and reduction order the decoder step
  * uses for an M-row call. A [M][K] and W [N][K] are device buffers of the
  * context's dtype; out is a device [M][N] float32 buffer. Requires
- * 1 <= M <= max_rows, N and K multiples of 32, K <= 2 * d_model.
+ * 1 <= M <= max_rows, N and K multiples of 32, K <= max(2 * d_model, d_ffn).
  * Enqueued on `stream`; returns RLT_ESHAPE / RLT_EINVAL on bad sizes. */
 int rlt_dbg_gemm(rlt_ctx* ctx, const void* A, const void* W, int32_t M, int32_t N, int32_t K, float* out,
                  void* stream);

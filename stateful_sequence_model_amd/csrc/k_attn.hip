@@ -6,14 +6,18 @@
 // bandwidth, so they run on the vector ALU (no MFMA) and are organised for
 // coalesced, contiguous reads:
 //   * a workgroup handles one row and `hpw` consecutive heads, so every key
-//     read is hpw*dh contiguous elements;
+//     read is hpw*dh contiguous elements; the head groups of one row are
+//     the fastest grid dimension, so the workgroups that together read a
+//     full key row are dispatched next to each other;
 //   * each lane owns E consecutive elements (32 bytes) of one head; the
 //     dh/E lanes of a head reduce the q.k dot with xor-shuffles (all lanes
 //     end with the identical sum);
-//   * the 256 threads form 256/(hpw*dh/E) key groups that walk the keys with
-//     an online softmax (base-2, the log2(e)/sqrt(dh) scale folded into q),
-//     and the groups' (max, sum, output) partials are merged in LDS in group
-//     order. Every order is fixed, so results do not depend on timing.
+//   * the 256 threads form 256/(hpw*dh/E) key groups; a key group takes
+//     U keys at a time (all loads issued first), then one running-max update
+//     and rescale for the U keys (online softmax in base 2, the
+//     log2(e)/sqrt(dh) scale folded into q); the key groups' (max, sum,
+//     output) partials are merged in LDS in group order. Every order is a
+//     function of t only, so results do not depend on timing or batch.
 //
 // SWA (eq. 2.14): keys are the retained positions max(1, t-W+1) .. t-1 from
 // the ring (slot (j-1) mod (W-1)) plus the current (k, v); after all reads
@@ -28,16 +32,35 @@
 
 namespace rlt {
 
+// 32 bytes of one head's keys or values held by one lane, unconverted
+struct Raw {
+  uint4 a, b;
+};
+
 template <typename T> struct LaneVec;
 template <> struct LaneVec<uint16_t> {
   static constexpr int E = 16;
-  __device__ static __forceinline__ void load(const uint16_t* p, float* f) {
-    const uint4 a = *(const uint4*)p, b = *(const uint4*)(p + 8);
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  __device__ static __forceinline__ Raw load(const uint16_t* p) {
+    return Raw{*(const uint4*)p, *(const uint4*)(p + 8)};
+  }
+  __device__ static __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
+  __device__ static __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+  __device__ static __forceinline__ float dot(const float* q, const Raw& r) {
+    const uint32_t w[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
+    float s = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      f[2 * i] = __uint_as_float(w[i] << 16);
-      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+      s = fmaf(q[2 * i], lo(w[i]), s);
+      s = fmaf(q[2 * i + 1], hi(w[i]), s);
+    }
+    return s;
+  }
+  __device__ static __forceinline__ void axpy(float* o, float p, const Raw& r) {
+    const uint32_t w[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      o[2 * i] = fmaf(p, lo(w[i]), o[2 * i]);
+      o[2 * i + 1] = fmaf(p, hi(w[i]), o[2 * i + 1]);
     }
   }
   __device__ static __forceinline__ void store(uint16_t* p, const float* f) {
@@ -54,10 +77,20 @@ template <> struct LaneVec<uint16_t> {
 };
 template <> struct LaneVec<float> {
   static constexpr int E = 8;
-  __device__ static __forceinline__ void load(const float* p, float* f) {
-    const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
-    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  __device__ static __forceinline__ Raw load(const float* p) {
+    return Raw{*(const uint4*)p, *(const uint4*)(p + 4)};
+  }
+  __device__ static __forceinline__ float dot(const float* q, const Raw& r) {
+    const uint32_t w[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s = fmaf(q[i], __uint_as_float(w[i]), s);
+    return s;
+  }
+  __device__ static __forceinline__ void axpy(float* o, float p, const Raw& r) {
+    const uint32_t w[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = fmaf(p, __uint_as_float(w[i]), o[i]);
   }
   __device__ static __forceinline__ void store(float* p, const float* f) {
     *(float4*)p = make_float4(f[0], f[1], f[2], f[3]);
@@ -69,27 +102,6 @@ template <> struct LaneVec<float> {
   }
 };
 
-// online-softmax accumulator of one lane (E output elements)
-template <int E>
-struct Acc {
-  float m, l, o[E];
-  __device__ __forceinline__ void init() {
-    m = -INFINITY;
-    l = 0.f;
-#pragma unroll
-    for (int i = 0; i < E; ++i) o[i] = 0.f;
-  }
-  __device__ __forceinline__ void add(float s, const float* v) {
-    const float mn = fmaxf(m, s);
-    const float c = exp2f(m - mn);
-    const float p = exp2f(s - mn);
-    l = l * c + p;
-#pragma unroll
-    for (int i = 0; i < E; ++i) o[i] = fmaf(p, v[i], o[i] * c);
-    m = mn;
-  }
-};
-
 template <int LPK>
 __device__ __forceinline__ float group_sum(float s) {
 #pragma unroll
@@ -97,12 +109,72 @@ __device__ __forceinline__ float group_sum(float s) {
   return s;
 }
 
+// online-softmax accumulator of one lane (E output elements)
+template <typename T>
+struct Acc {
+  static constexpr int E = LaneVec<T>::E;
+  float m, l, o[E];
+  __device__ __forceinline__ void init() {
+    m = -INFINITY;
+    l = 0.f;
+#pragma unroll
+    for (int i = 0; i < E; ++i) o[i] = 0.f;
+  }
+  // fold N keys (scores s[], values v[]) with one max update
+  template <int N>
+  __device__ __forceinline__ void fold(const float* s, const Raw* v) {
+    float mx = m;
+#pragma unroll
+    for (int u = 0; u < N; ++u) mx = fmaxf(mx, s[u]);
+    const float c = exp2f(m - mx);
+    l *= c;
+#pragma unroll
+    for (int i = 0; i < E; ++i) o[i] *= c;
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+      const float p = exp2f(s[u] - mx);
+      l += p;
+      LaneVec<T>::axpy(o, p, v[u]);
+    }
+    m = mx;
+  }
+};
+
+// Walk keys r = r0, r0 + step, ... < r1 (addressed by kv(r) -> (k, v)
+// pointers), U at a time.
+template <typename T, int LPK, int U, class KV>
+__device__ __forceinline__ void walk(Acc<T>& acc, const float* q, int r0, int r1, int step, const KV& kv) {
+  using LV = LaneVec<T>;
+  int r = r0;
+  for (; r + (U - 1) * step < r1; r += U * step) {
+    Raw kr[U], vr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const T *kp, *vp;
+      kv(r + u * step, kp, vp);
+      kr[u] = LV::load(kp);
+      vr[u] = LV::load(vp);
+    }
+    float s[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) s[u] = group_sum<LPK>(LV::dot(q, kr[u]));
+    acc.template fold<U>(s, vr);
+  }
+  for (; r < r1; r += step) {
+    const T *kp, *vp;
+    kv(r, kp, vp);
+    Raw kr[1] = {LV::load(kp)}, vr[1] = {LV::load(vp)};
+    float s[1] = {group_sum<LPK>(LV::dot(q, kr[0]))};
+    acc.template fold<1>(s, vr);
+  }
+}
+
 // Merge the key groups' partials of the workgroup (fixed group order).
 // Returns true on the lanes of key group 0, which then hold the merged
 // (m, l, o) of their (head, element range).
-template <int E>
-__device__ __forceinline__ bool merge_groups(Acc<E>& acc, int kg, int G, int KPW, float* s_o,
-                                             float* s_ml) {
+template <typename T>
+__device__ __forceinline__ bool merge_groups(Acc<T>& acc, int kg, int G, int KPW, float* s_o, float* s_ml) {
+  constexpr int E = Acc<T>::E;
   const int li = threadIdx.x - kg * G;  // lane index within the key group
 #pragma unroll
   for (int i = 0; i < E; ++i) s_o[threadIdx.x * E + i] = acc.o[i];
@@ -129,7 +201,36 @@ __device__ __forceinline__ bool merge_groups(Acc<E>& acc, int kg, int G, int KPW
   return true;
 }
 
-// grid: x = slot, y = head group; block 256
+template <typename T>
+struct RingKV {
+  const T *rk, *rv, *ck, *cv;
+  int t, nh, W1;
+  int64_t d;
+  __device__ __forceinline__ void operator()(int r, const T*& kp, const T*& vp) const {
+    if (r < nh) {
+      const int sl = (t - nh + r - 1) % W1;  // slot of absolute position t - nh + r
+      kp = rk + sl * d;
+      vp = rv + sl * d;
+    } else {
+      kp = ck;
+      vp = cv;
+    }
+  }
+};
+
+template <typename T>
+struct MemKV {
+  const T *mk, *mv;
+  int64_t st;
+  __device__ __forceinline__ void operator()(int r, const T*& kp, const T*& vp) const {
+    kp = mk + r * st;
+    vp = mv + r * st;
+  }
+};
+
+constexpr int UNROLL = 4;
+
+// grid: x = head group, y = slot; block 256
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void k_swa(AttnArgs a) {
   using LV = LaneVec<T>;
@@ -137,7 +238,7 @@ __global__ __launch_bounds__(256) void k_swa(AttnArgs a) {
   constexpr int LPK = DH / E;
   __shared__ float s_o[256 * E];
   __shared__ float s_ml[512];
-  const int slot = blockIdx.x;
+  const int slot = blockIdx.y;
   const int t = a.rows.t_row[slot];
   if (t <= 0) return;
   const int row = a.rows.rows[slot];
@@ -146,7 +247,7 @@ __global__ __launch_bounds__(256) void k_swa(AttnArgs a) {
   const int kg = threadIdx.x / G;
   const int hh = (threadIdx.x % G) / LPK;
   const int jl = threadIdx.x % LPK;
-  const int col = (blockIdx.y * a.hpw + hh) * DH + jl * E;
+  const int col = (blockIdx.x * a.hpw + hh) * DH + jl * E;
   const int d = a.d;
 
   float q[E];
@@ -157,37 +258,20 @@ __global__ __launch_bounds__(256) void k_swa(AttnArgs a) {
   }
   const int W1 = a.W - 1;
   const int nh = min(t - 1, W1);
-  const int nkeys = nh + 1;
-  const T* rk = (const T*)a.ring_k + (int64_t)row * W1 * d + col;
-  const T* rv = (const T*)a.ring_v + (int64_t)row * W1 * d + col;
-  const T* ck = (const T*)a.kc + (int64_t)slot * d + col;
-  const T* cv = (const T*)a.vc + (int64_t)slot * d + col;
+  RingKV<T> kv;
+  kv.rk = (const T*)a.ring_k + (int64_t)row * W1 * d + col;
+  kv.rv = (const T*)a.ring_v + (int64_t)row * W1 * d + col;
+  kv.ck = (const T*)a.kc + (int64_t)slot * d + col;
+  kv.cv = (const T*)a.vc + (int64_t)slot * d + col;
+  kv.t = t;
+  kv.nh = nh;
+  kv.W1 = W1;
+  kv.d = d;
 
-  Acc<E> acc;
+  Acc<T> acc;
   acc.init();
-  if (kg < KPW) {
-    for (int r = kg; r < nkeys; r += KPW) {
-      const T *kp, *vp;
-      if (r < nh) {
-        const int j = t - nh + r;                 // absolute position
-        const int sl = (j - 1) % W1;
-        kp = rk + (int64_t)sl * d;
-        vp = rv + (int64_t)sl * d;
-      } else {
-        kp = ck;
-        vp = cv;
-      }
-      float kf[E], vf[E];
-      LV::load(kp, kf);
-      LV::load(vp, vf);
-      float s = 0.f;
-#pragma unroll
-      for (int i = 0; i < E; ++i) s = fmaf(q[i], kf[i], s);
-      s = group_sum<LPK>(s);
-      acc.add(s, vf);
-    }
-  }
-  const bool lead = merge_groups<E>(acc, kg, G, KPW, s_o, s_ml);
+  walk<T, LPK, UNROLL>(acc, q, kg, nh + 1, KPW, kv);
+  const bool lead = merge_groups<T>(acc, kg, G, KPW, s_o, s_ml);
   if (lead) {
     const float inv = 1.f / acc.l;
     float o[E];
@@ -199,12 +283,12 @@ __global__ __launch_bounds__(256) void k_swa(AttnArgs a) {
   __syncthreads();
   if (W1 > 0 && kg == 0) {
     const int sl = (t - 1) % W1;
-    LV::copy((T*)a.ring_k + ((int64_t)row * W1 + sl) * d + col, ck);
-    LV::copy((T*)a.ring_v + ((int64_t)row * W1 + sl) * d + col, cv);
+    LV::copy((T*)a.ring_k + ((int64_t)row * W1 + sl) * d + col, kv.ck);
+    LV::copy((T*)a.ring_v + ((int64_t)row * W1 + sl) * d + col, kv.cv);
   }
 }
 
-// grid: x = slot, y = chunk, z = head group; block 256
+// grid: x = head group, y = chunk, z = slot; block 256
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void k_xattn(AttnArgs a) {
   using LV = LaneVec<T>;
@@ -212,7 +296,7 @@ __global__ __launch_bounds__(256) void k_xattn(AttnArgs a) {
   constexpr int LPK = DH / E;
   __shared__ float s_o[256 * E];
   __shared__ float s_ml[512];
-  const int slot = blockIdx.x;
+  const int slot = blockIdx.z;
   const int t = a.rows.t_row[slot];
   const int j0 = blockIdx.y * a.chunk;
   if (t <= 0 || j0 >= t) return;
@@ -223,7 +307,7 @@ __global__ __launch_bounds__(256) void k_xattn(AttnArgs a) {
   const int kg = threadIdx.x / G;
   const int hh = (threadIdx.x % G) / LPK;
   const int jl = threadIdx.x % LPK;
-  const int head = blockIdx.z * a.hpw + hh;
+  const int head = blockIdx.x * a.hpw + hh;
   const int col = head * DH + jl * E;
   const int d = a.d;
 
@@ -233,43 +317,11 @@ __global__ __launch_bounds__(256) void k_xattn(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < E; ++i) q[i] = qp[i] * a.qscale;
   }
-  const T* mk = (const T*)a.mk + (int64_t)row * a.sb + col;
-  const T* mv = (const T*)a.mv + (int64_t)row * a.sb + col;
-
-  Acc<E> acc;
+  MemKV<T> kv{(const T*)a.mk + (int64_t)row * a.sb + col, (const T*)a.mv + (int64_t)row * a.sb + col, a.st};
+  Acc<T> acc;
   acc.init();
-  if (kg < KPW) {
-    int r = j0 + kg;
-    // two keys per iteration: both loads issued before the math
-    for (; r + KPW < j1; r += 2 * KPW) {
-      float k0[E], v0[E], k1[E], v1[E];
-      LV::load(mk + (int64_t)r * a.st, k0);
-      LV::load(mv + (int64_t)r * a.st, v0);
-      LV::load(mk + (int64_t)(r + KPW) * a.st, k1);
-      LV::load(mv + (int64_t)(r + KPW) * a.st, v1);
-      float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-      for (int i = 0; i < E; ++i) {
-        s0 = fmaf(q[i], k0[i], s0);
-        s1 = fmaf(q[i], k1[i], s1);
-      }
-      s0 = group_sum<LPK>(s0);
-      s1 = group_sum<LPK>(s1);
-      acc.add(s0, v0);
-      acc.add(s1, v1);
-    }
-    if (r < j1) {
-      float k0[E], v0[E];
-      LV::load(mk + (int64_t)r * a.st, k0);
-      LV::load(mv + (int64_t)r * a.st, v0);
-      float s0 = 0.f;
-#pragma unroll
-      for (int i = 0; i < E; ++i) s0 = fmaf(q[i], k0[i], s0);
-      s0 = group_sum<LPK>(s0);
-      acc.add(s0, v0);
-    }
-  }
-  const bool lead = merge_groups<E>(acc, kg, G, KPW, s_o, s_ml);
+  walk<T, LPK, UNROLL>(acc, q, j0 + kg, j1, KPW, kv);
+  const bool lead = merge_groups<T>(acc, kg, G, KPW, s_o, s_ml);
   if (lead) {
     float* P = a.part + (((int64_t)slot * a.nch + blockIdx.y) * a.H + head) * (DH + 2);
 #pragma unroll
@@ -281,10 +333,10 @@ __global__ __launch_bounds__(256) void k_xattn(AttnArgs a) {
   }
 }
 
-// grid: x = slot, y = head; block 64
+// grid: x = head, y = slot; block 64
 template <typename T, int DH>
 __global__ __launch_bounds__(64) void k_xcombine(AttnArgs a) {
-  const int slot = blockIdx.x, head = blockIdx.y;
+  const int head = blockIdx.x, slot = blockIdx.y;
   const int t = a.rows.t_row[slot];
   if (t <= 0) return;
   const int nc = (t + a.chunk - 1) / a.chunk;
@@ -305,17 +357,17 @@ __global__ __launch_bounds__(64) void k_xcombine(AttnArgs a) {
 
 template <typename T, int DH>
 static void swa_t(const AttnArgs& a, hipStream_t s) {
-  dim3 grid(a.rows.n, a.H / a.hpw);
+  dim3 grid(a.H / a.hpw, a.rows.n);
   hipLaunchKernelGGL((k_swa<T, DH>), grid, dim3(256), 0, s, a);
 }
 template <typename T, int DH>
 static void xattn_t(const AttnArgs& a, hipStream_t s) {
-  dim3 grid(a.rows.n, a.nch, a.H / a.hpw);
+  dim3 grid(a.H / a.hpw, a.nch, a.rows.n);
   hipLaunchKernelGGL((k_xattn<T, DH>), grid, dim3(256), 0, s, a);
 }
 template <typename T, int DH>
 static void xcomb_t(const AttnArgs& a, hipStream_t s) {
-  dim3 grid(a.rows.n, a.H);
+  dim3 grid(a.H, a.rows.n);
   hipLaunchKernelGGL((k_xcombine<T, DH>), grid, dim3(64), 0, s, a);
 }
 

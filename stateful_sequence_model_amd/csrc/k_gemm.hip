@@ -156,16 +156,49 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs g, Epi<uint16_t> epi
   }
   const int k0 = (split * 4 + wave) * g.kslice;
   const int k1 = min(k0 + g.kslice, g.K);
-  for (int kb = k0; kb < k1; kb += 32) {
-    const bf16x8_t b0 = load8(wa + kb);
-    const bf16x8_t b1 = load8(wb + kb);
-    bf16x8_t av[MB];
+  // PF K-steps of loads in flight: step i is multiplied while steps
+  // i+1 .. i+PF-1 are still arriving (a register ring, statically indexed).
+  // The steady-state loop is branch-free so that each step waits only for
+  // its own loads: the refill of step i+PF is always issued, its address
+  // clamped to the last step (a harmless re-read) near the end.
+  constexpr int PF = MB >= 4 ? 4 : 6;
+  const int nsteps = (k1 - k0) / 32;
+  bf16x8_t bufa[PF][MB], bufb[PF][2];
+  if (nsteps > 0) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) av[mb] = load8(ap[mb] + kb);
+    for (int p = 0; p < PF; ++p) {
+      const int k = k0 + 32 * min(p, nsteps - 1);
+      bufb[p][0] = load8(wa + k);
+      bufb[p][1] = load8(wb + k);
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      acc[mb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mb], b0, acc[mb][0], 0, 0, 0);
-      acc[mb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mb], b1, acc[mb][1], 0, 0, 0);
+      for (int mb = 0; mb < MB; ++mb) bufa[p][mb] = load8(ap[mb] + k);
+    }
+  }
+  int i = 0;
+  for (; i + PF <= nsteps; i += PF) {
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        acc[mb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bufa[p][mb], bufb[p][0], acc[mb][0], 0, 0, 0);
+        acc[mb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bufa[p][mb], bufb[p][1], acc[mb][1], 0, 0, 0);
+      }
+      const int kn = k0 + 32 * min(i + p + PF, nsteps - 1);
+      bufb[p][0] = load8(wa + kn);
+      bufb[p][1] = load8(wb + kn);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) bufa[p][mb] = load8(ap[mb] + kn);
+    }
+  }
+  // tail: the remaining nsteps - i (< PF) steps are already in the ring
+#pragma unroll
+  for (int p = 0; p < PF; ++p) {
+    if (i + p < nsteps) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        acc[mb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bufa[p][mb], bufb[p][0], acc[mb][0], 0, 0, 0);
+        acc[mb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bufa[p][mb], bufb[p][1], acc[mb][1], 0, 0, 0);
+      }
     }
   }
   // C layout: lane holds rows 4*(lane/16)+i, column lane%16
@@ -254,15 +287,14 @@ void launch_gemm(int dtype, const GemmArgs& g0, const EpiArgs& e, hipStream_t s)
     hipLaunchKernelGGL(k_gemm_f32, grid, dim3(64), 0, s, g, Epi<float>{e});
     return;
   }
-  const int MB = g.M <= 16 ? 1 : g.M <= 32 ? 2 : g.M <= 64 ? 4 : 8;
+  const int MB = g.mb;
   const int mt = (g.M + 16 * MB - 1) / (16 * MB);
   dim3 grid(g.npairs, g.S, mt);
   Epi<uint16_t> epi{e};
   switch (MB) {
     case 1: hipLaunchKernelGGL(k_gemm_bf16<1>, grid, dim3(256), 0, s, g, epi); break;
     case 2: hipLaunchKernelGGL(k_gemm_bf16<2>, grid, dim3(256), 0, s, g, epi); break;
-    case 4: hipLaunchKernelGGL(k_gemm_bf16<4>, grid, dim3(256), 0, s, g, epi); break;
-    default: hipLaunchKernelGGL(k_gemm_bf16<8>, grid, dim3(256), 0, s, g, epi); break;
+    default: hipLaunchKernelGGL(k_gemm_bf16<4>, grid, dim3(256), 0, s, g, epi); break;
   }
   if (g.S > 1) {
     dim3 g2(g.npairs, (g.M + 15) / 16);

@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <numeric>
 #include <string>
@@ -53,7 +54,7 @@ struct rlt_ctx {
   // capacities
   int max_rows, max_ctx, M_pad;
   int chunk, nch;
-  int hpw;
+  int hpw, hpw_x;   // heads per workgroup: SWA, cross-attention
   // workspace (device)
   int *t_row, *ident, *ones, *rows_buf, *src_buf, *split_buf, *last_buf;
   void *X, *kc, *vc, *o, *h, *act;
@@ -140,13 +141,22 @@ static int check_config(const rlt_config* c) {
 
 static int elems_per_lane(int dt) { return dt == 1 ? 16 : 8; }
 
-// heads per attention workgroup: hpw * (dh / E) lanes per key, at most 32
-static int choose_hpw(const rlt_config& c, int dt) {
+// heads per attention workgroup: hpw * (dh / E) lanes per key group, which
+// must divide 256; default: the widest group of at most 32 lanes. A
+// requested value (tuning) is used when valid.
+static int choose_hpw(const rlt_config& c, int dt, int requested) {
   const int lpk = c.d_head / elems_per_lane(dt);
+  auto ok = [&](int h) { return h >= 1 && h <= c.n_heads && c.n_heads % h == 0 && 256 % (h * lpk) == 0; };
+  if (requested > 0 && ok(requested)) return requested;
   int best = 1;
   for (int h = 1; h <= c.n_heads; ++h)
-    if (c.n_heads % h == 0 && h * lpk <= 32 && 256 % (h * lpk) == 0) best = h;
+    if (ok(h) && h * lpk <= 32) best = h;
   return best;
+}
+
+static int env_int(const char* name, int dflt) {
+  const char* v = std::getenv(name);
+  return (v && *v) ? std::atoi(v) : dflt;
 }
 
 template <typename P>
@@ -240,9 +250,11 @@ extern "C" int rlt_create(const rlt_config* cfg, const rlt_weights* w, int32_t m
   c->max_rows = max_rows;
   c->max_ctx = max_ctx;
   c->M_pad = (max_rows + 127) / 128 * 128;
-  c->chunk = d <= 512 ? 128 : 256;
+  c->chunk = env_int("RLT_XATTN_CHUNK", d <= 512 ? 128 : 256);
+  if (c->chunk < 16 || c->chunk > 4096) c->chunk = d <= 512 ? 128 : 256;
   c->nch = (max_ctx + c->chunk - 1) / c->chunk;
-  c->hpw = choose_hpw(*cfg, c->dt);
+  c->hpw = choose_hpw(*cfg, c->dt, env_int("RLT_SWA_HPW", 0));
+  c->hpw_x = choose_hpw(*cfg, c->dt, env_int("RLT_XATTN_HPW", 0));
   const size_t M = c->M_pad, es = c->es;
   const int Nv_max = std::max(3 * d, 2 * F);
   c->partial_cap = (size_t)8 * M * Nv_max;
@@ -348,14 +360,19 @@ struct Gemm {
     g.kslice = (K + 4 * 32 - 1) / (4 * 32) * 32;
     g.partial = c->partial;
     if (c->dt == 1) {
-      const int MB = n <= 16 ? 1 : n <= 32 ? 2 : n <= 64 ? 4 : 8;
+      int MB = gemm_row_blocks(n);
+      const int mb_env = env_int("RLT_GEMM_MB", 0);  // tuning override: 1, 2 or 4
+      if (mb_env == 1 || mb_env == 2 || mb_env == 4) MB = mb_env;
       const int mt = (n + 16 * MB - 1) / (16 * MB);
       const int tiles = g.npairs * mt;
       int S = std::max(1, (512 + tiles - 1) / tiles);   // fill the chip
       S = std::min(S, std::max(1, K / 256));             // >= 64 K per wave
-      S = std::min(S, std::max(1, K / (8 * n)));         // partial traffic <= half the weights
+      S = std::min(S, std::max(1, K / (4 * n)));         // partial traffic <= the weights'
+      const int s_env = env_int("RLT_GEMM_S", 0);    // tuning override
+      if (s_env > 0) S = std::min(s_env, std::max(1, K / 128));
       while (S > 1 && (size_t)S * c->M_pad * g.Nv > c->partial_cap) --S;
       g.S = S;
+      g.mb = MB;
       const int per = (K + 4 * S - 1) / (4 * S);
       g.kslice = (per + 31) / 32 * 32;
     }
@@ -470,6 +487,7 @@ void enqueue_transition(rlt_ctx* c, const StepPlan& P, hipStream_t s) {
     at.ring_k = (char*)P.st->ring_k + l * ring_layer;
     at.ring_v = (char*)P.st->ring_v + l * ring_layer;
     at.out = c->o;
+    at.hpw = c->hpw;
     { Prof pf(c, RLT_PROF_SWA, s); launch_swa(c->dt, at, s); }
     {
       EpiArgs e = E0;
@@ -491,6 +509,7 @@ void enqueue_transition(rlt_ctx* c, const StepPlan& P, hipStream_t s) {
     at.q = c->qm;
     at.mk = (const char*)P.mem.k + (size_t)g * P.mem.stride_g * es;
     at.mv = (const char*)P.mem.v + (size_t)g * P.mem.stride_g * es;
+    at.hpw = c->hpw_x;
     { Prof pf(c, RLT_PROF_XATTN, s); launch_xattn(c->dt, at, s); }
     { Prof pf(c, RLT_PROF_XCOMBINE, s); launch_xcombine(c->dt, at, s); }
     {
@@ -814,11 +833,13 @@ extern "C" int rlt_score_logprobs(rlt_ctx* c, const rlt_score_io* io, void* stre
 extern "C" int rlt_dbg_gemm(rlt_ctx* c, const void* A, const void* W, int32_t M, int32_t N, int32_t K,
                             float* out, void* stream) {
   if (!c || !A || !W || !out) return fail(RLT_EINVAL, "null argument");
-  if (M < 1 || M > c->max_rows || N < 32 || N % 32 || K < 32 || K % 32 || K > 2 * c->cfg.d_model)
-    return fail(RLT_ESHAPE, "need 1 <= M <= max_rows, N and K multiples of 32, K <= 2*d_model");
+  const int kmax = std::max(2 * c->cfg.d_model, c->cfg.d_ffn);
+  if (M < 1 || M > c->max_rows || N < 32 || N % 32 || K < 32 || K % 32 || K > kmax)
+    return fail(RLT_ESHAPE, "need 1 <= M <= max_rows, N and K multiples of 32, K <= max(2*d_model, d_ffn)");
   hipStream_t s = (hipStream_t)stream;
-  // A goes through the padded workspace: the MFMA tiles read whole 16-row blocks
-  HIP_TRY(hipMemcpyAsync(c->X, A, (size_t)M * K * c->es, hipMemcpyDeviceToDevice, s));
+  // A goes through a padded workspace buffer: the MFMA tiles read whole 16-row blocks
+  void* stage = K <= 2 * c->cfg.d_model ? c->X : c->act;
+  HIP_TRY(hipMemcpyAsync(stage, A, (size_t)M * K * c->es, hipMemcpyDeviceToDevice, s));
   Rows R{c->ident, c->ident, c->ones, M};
   EpiArgs e{};
   e.kind = EPI_STORE;
@@ -826,7 +847,7 @@ extern "C" int rlt_dbg_gemm(rlt_ctx* c, const void* A, const void* W, int32_t M,
   e.out_f = out;
   e.ldo = N;
   Gemm gm{c, s};
-  gm.run(c->X, K, {W}, N, K, PAIR_PLAIN, M, e);
+  gm.run(stage, K, {W}, N, K, PAIR_PLAIN, M, e);
   HIP_TRY(hipGetLastError());
   return RLT_OK;
 }

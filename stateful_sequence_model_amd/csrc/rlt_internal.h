@@ -84,10 +84,15 @@ struct GemmArgs {
   int dh;                 // head width for PAIR_ROPE
   int M, M_pad;           // valid rows / allocated rows of A
   int S;                  // splits of K across workgroups (bf16 path)
+  int mb;                 // 16-row blocks per tile (bf16 path): 1, 2 or 4
   int kslice;             // K elements per (split, wave) slice, multiple of 32
   float* partial;         // [S][M_pad][Nv] when S > 1
   int Nv;                 // nseg * seg_rows
 };
+
+// 16-row blocks per matrix-product tile for an M-row call (tile <= 64 rows;
+// larger M runs several row tiles)
+__host__ __device__ inline int gemm_row_blocks(int M) { return M <= 16 ? 1 : M <= 32 ? 2 : 4; }
 
 // virtual column blocks (16 columns each) of pair p
 __device__ __forceinline__ void pair_blocks(const GemmArgs& g, int p, int& ba, int& bb) {

@@ -1,0 +1,198 @@
+"""GPU parity at the workloads' real dimensions (bf16 gates: relative L2
+<= 2e-2 per checked (row, step), top-1 >= 99 %; integer state exact).
+
+The oracle is float64 on the identical bf16-valued inputs, so it checks a
+sample: chosen rows of the batch, or a few steps from a synthetically
+pre-filled state (full ring, long prefix) for the long-context behaviour.
+Rows are independent, so rows the oracle does not check may hold any data;
+they are filled with seeded random values for speed.
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import Memory, Oracle, replay as oracle_replay, state_from_ring
+from tests.gpu_common import GpuRun, model_config, require_gpu, torch
+from tests.helpers import oracle_config, oracle_weights, rel_l2, widen
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+
+
+def _check(S, Z, So, Zo, tag):
+    for i in range(len(So)):
+        assert rel_l2(S[i], So[i]) < TOL, (tag, i, rel_l2(S[i], So[i]))
+        assert rel_l2(Z[i], Zo[i]) < TOL, (tag, i, rel_l2(Z[i], Zo[i]))
+    return np.mean([np.argmax(Z[i]) == np.argmax(Zo[i]) for i in range(len(So))])
+
+
+def test_mid_from_h0_sampled_rows():
+    """L_D=12, d=1024, 16x64 heads, W=128: all 64 rows for 40 steps from
+    H_0; the oracle replays rows 0 and 41."""
+    require_gpu()
+    wl = synth.MID.with_(T=64)
+    run = GpuRun(wl, B=64, T=64)
+    run.init()
+    S, Z = run.run(40)
+    orc = Oracle(oracle_config(wl), oracle_weights(run.raw))
+    agree = []
+    for b in (0, 41):
+        mem = Memory([widen(run.mk[g, b]) for g in range(wl.G)], [widen(run.mv[g, b]) for g in range(wl.G)])
+        st = orc.initial_state()
+        So, Zo = [], []
+        for t in range(1, 41):
+            st = orc.transition(st, widen(run.E[b, t - 1]), mem)
+            So.append(st.s)
+            Zo.append(orc.logits(st.s))
+        agree.append(_check(S[:, b], Z[:, b], So, Zo, "mid b=%d" % b))
+    assert np.mean(agree) >= 0.99
+
+
+def _prefilled(wl, B, t0, check_rows, graph=False, nsteps=3, seed=0):
+    """GPU run of nsteps from a pre-filled state at pos t0-1 (ring full,
+    memory of length T); rows in check_rows get synth values (the oracle
+    rebuilds them), the rest seeded torch values. Returns GPU s/logits and
+    the oracle's for check_rows."""
+    from stateful_sequence_model_amd import Decoder, DecoderState, to_device
+    raw = synth.make_weights(wl)
+    cfg = model_config(wl)
+    T = wl.T
+    dec = Decoder(cfg, raw, max_rows=B, max_ctx=T)
+    st = DecoderState(cfg, B)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    tdt = cfg.torch_dtype
+    mk = torch.randn((wl.G, B, T, wl.d), generator=g, device="cuda").to(tdt)
+    mv = torch.randn((wl.G, B, T, wl.d), generator=g, device="cuda").to(tdt)
+    for l in range(wl.L):
+        st.ring("k")[l].copy_(torch.randn(st.ring("k")[l].shape, generator=g, device="cuda").to(tdt))
+        st.ring("v")[l].copy_(torch.randn(st.ring("v")[l].shape, generator=g, device="cuda").to(tdt))
+    st.s.copy_(torch.randn(st.s.shape, generator=g, device="cuda"))
+    E = torch.randn((B, nsteps, wl.d), generator=g, device="cuda").to(tdt)
+    host = {}
+    for b in check_rows:
+        mkb = [synth.make_memory(wl, "k", gg, b, 1)[0] for gg in range(wl.G)]
+        mvb = [synth.make_memory(wl, "v", gg, b, 1)[0] for gg in range(wl.G)]
+        rk = np.stack([synth.make_ring_prefill(wl, "k", l, b, 1)[0] for l in range(wl.L)])
+        rv = np.stack([synth.make_ring_prefill(wl, "v", l, b, 1)[0] for l in range(wl.L)])
+        s0 = synth.normal(wl.seed, "s_prefill", (wl.d,), start=b * wl.d)
+        Eb = synth.normal(wl.seed, "e_steps", (nsteps, wl.d), dtype=wl.dtype, start=b * nsteps * wl.d)
+        for gg in range(wl.G):
+            mk[gg, b].copy_(to_device(mkb[gg], wl.dtype))
+            mv[gg, b].copy_(to_device(mvb[gg], wl.dtype))
+        st.ring("k")[:, b].copy_(to_device(rk, wl.dtype))
+        st.ring("v")[:, b].copy_(to_device(rv, wl.dtype))
+        st.s[b].copy_(torch.from_numpy(s0).cuda())
+        E[b].copy_(to_device(Eb, wl.dtype))
+        host[b] = (mkb, mvb, rk, rv, s0, Eb)
+    st.pos.fill_(t0 - 1)
+    st.pending.fill_(-1)
+    mem_len = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    mem = Decoder.memory(mk, mv, mem_len)
+    rows = torch.arange(B, dtype=torch.int32, device="cuda")
+    s_out = torch.empty((B, wl.d), device="cuda")
+    logits = torch.empty((B, wl.V), device="cuda")
+    S = np.empty((nsteps, B, wl.d))
+    Z = np.empty((nsteps, B, wl.V))
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        e_buf = torch.empty((B, wl.d), dtype=tdt, device="cuda")
+        for i in range(nsteps):
+            e_buf.copy_(E[:, i])
+            assert dec.step(st, rows, e_buf, mem, s_out=s_out, logits=logits, graph=graph) == 0
+            stream.synchronize()
+            S[i] = s_out.double().cpu().numpy()
+            Z[i] = logits.double().cpu().numpy()
+    assert dec.sync_error() == 0
+    assert st.pos.tolist() == [t0 - 1 + nsteps] * B
+    del mk, mv
+    orc = Oracle(oracle_config(wl), oracle_weights(raw))
+    ref = {}
+    for b in check_rows:
+        mkb, mvb, rk, rv, s0, Eb = host[b]
+        ost = state_from_ring(orc.cfg, s0.astype(np.float64), t0 - 1, widen(rk), widen(rv))
+        omem = Memory([widen(m) for m in mkb], [widen(m) for m in mvb])
+        So, Zo = [], []
+        for i in range(nsteps):
+            ost = orc.transition(ost, widen(Eb[i]), omem)
+            So.append(ost.s)
+            Zo.append(orc.logits(ost.s))
+        ref[b] = (So, Zo)
+    dec.close()
+    return S, Z, ref
+
+
+@pytest.mark.timeout(900)
+def test_mid_long_context_prefilled():
+    """L_D=12 at t = 1901..1903 (ring full, 8 cross-attention chunks)."""
+    require_gpu()
+    wl = synth.MID
+    S, Z, ref = _prefilled(wl, 64, 1901, (0, 63))
+    for b, (So, Zo) in ref.items():
+        _check(S[:, b], Z[:, b], So, Zo, "mid-long b=%d" % b)
+
+
+@pytest.mark.timeout(1200)
+def test_reference_depth_bench_configuration():
+    """L_D=48, d=2048, 16x128, W=256, B=128 at t = 2048..2050 through the
+    captured graph: the launch configuration the benchmark times."""
+    require_gpu()
+    wl = synth.REF
+    S, Z, ref = _prefilled(wl, 128, 2048, (0, 127), graph=True)
+    for b, (So, Zo) in ref.items():
+        _check(S[:, b], Z[:, b], So, Zo, "ref b=%d" % b)
+
+
+@pytest.mark.timeout(900)
+def test_ragged_rollout_then_replay():
+    """Ragged RL workload dims (L_D=24, d=1536, 12x128, W=512, G=L_D):
+    a temperature-0.7 / top-50 rollout records actions and behaviour
+    log-probs; replay from H_0 (App. A.4) rebuilds states and scores the
+    actions; the oracle replays the two shortest sequences."""
+    require_gpu()
+    B = 10
+    wl = synth.RAGGED.with_(B=B, T=160, len_lo=40, len_hi=160)
+    lens, splits = synth.make_lengths(wl)
+    run = GpuRun(wl, B=B, T=wl.T)
+    run.init()
+    tokens = synth.make_tokens(wl, 0, B, wl.T)   # prompt tokens; actions overwrite positions > split
+    tok = torch.from_numpy(tokens).cuda()
+    logmu = torch.zeros((B, wl.T), device="cuda")
+    sample_tok = torch.empty(B, dtype=torch.int32, device="cuda")
+    sample_lmu = torch.empty(B, device="cuda")
+    order = np.argsort(-lens, kind="stable")
+    # rollout: every sequence consumes x_1..x_{len-1}; at t >= split the next
+    # token x_{t+1} is sampled from s_t (prompt tokens are kept before split)
+    for t in range(1, int(lens.max())):
+        act = [int(b) for b in order if lens[b] - 1 >= t]
+        u = torch.from_numpy(synth.uniform01(wl.seed, "rollout_u", len(act), start=t * B)).cuda()
+        assert run.step(act, t, uniform=u, temperature=0.7, top_k=50, sample_tok=sample_tok[:len(act)],
+                        sample_logmu=sample_lmu[:len(act)]) == 0
+        torch.cuda.synchronize()
+        for j, b in enumerate(act):
+            if t >= splits[b]:
+                tok[b, t] = sample_tok[j]
+                logmu[b, t] = sample_lmu[j]
+    assert run.dec.sync_error() == 0
+    # replay from H_0 with the recorded actions
+    rep = GpuRun(wl, B=B, T=wl.T)
+    logp = torch.full((B, wl.T), float("nan"), device="cuda")
+    assert rep.dec.replay(rep.st, lens, splits, rep.Ed, rep.mem, tok, logp) == 0
+    torch.cuda.synchronize()
+    assert rep.dec.sync_error() == 0
+    assert rep.st.pos.cpu().numpy().tolist() == (lens - 1).tolist()
+    assert rep.st.pending.cpu().numpy().tolist() == [int(tok[b, lens[b] - 1]) for b in range(B)]
+    lp = logp.cpu().numpy()
+    for b in range(B):
+        sc = lp[b, splits[b]:lens[b]]
+        assert np.isfinite(sc).all() and (sc <= 0).all()
+        assert np.isnan(lp[b, :splits[b]]).all()
+    ratio = np.exp(lp - logmu.cpu().numpy())
+    assert np.isfinite(ratio[lp == lp]).all()
+    # oracle replay of the two shortest sequences
+    orc = Oracle(oracle_config(wl), oracle_weights(run.raw))
+    for b in np.argsort(lens, kind="stable")[:2]:
+        mem = Memory([widen(run.mk[g, b]) for g in range(wl.G)], [widen(run.mv[g, b]) for g in range(wl.G)])
+        _, lpo, _ = oracle_replay(orc, widen(run.E[b]), mem, tok[b].cpu().numpy(), int(lens[b]), int(splits[b]))
+        for t, v in lpo.items():
+            assert abs(lp[b, t] - v) < 5e-2, (b, t, lp[b, t], v)
