@@ -91,6 +91,23 @@ def cpu_baseline(wl, t0: int, budget_s: float, raw) -> dict:
                       "pre-filled state, %.1f s" % (n, t0, t0 + n - 1, el)}
 
 
+def measured_traffic(x_bytes: float):
+    """HBM bytes per cross-attention launch from the committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE summary (calibrated on a plain copy), scaled to
+    this launch's algorithmic bytes -- or None when the kernel source has
+    changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "k_xattn_reference_depth_traffic.json")
+    try:
+        rec = json.load(open(path))
+        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+    except (OSError, ValueError, KeyError):
+        return None
+    if hashlib.sha256(src).hexdigest()[:16] != rec.get("source_sha256_16"):
+        return None
+    return int(rec["traffic_over_algorithmic"] * x_bytes)
+
+
 def calibrate(torch, nbytes: int = 4 << 30, reps: int = 10) -> dict:
     """Achievable HBM rates on this device: a plain copy (read + write) and
     a read-only reduction over nbytes of bf16."""
@@ -243,7 +260,7 @@ def main():
                    "timed_positions": [t_first, t_first + K - 1], "hipgraph": graph},
         "roofline": {"bound": "hbm", "kernel": "k_xattn (prefix cross-attention)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(x_bytes),
                      "avg_launch_ms": round(x_avg_ms, 5), "algorithmic_bytes_per_launch": int(x_bytes)},
         "step_roofline": {"algorithmic_bytes": int(sb["total"]),
                           "achieved_GBs": round(sb["total"] / (ms_step / 1e3) / 1e9, 1),
