@@ -234,7 +234,8 @@ def main():
     x_ms, x_n = prof["xattn"]
     x_avg_ms = x_ms / max(x_n, 1)
     t_prof_mid = t_first + (P - 1) / 2.0
-    x_bytes = B * t_prof_mid * 2 * wl.d * es
+    rows_per_launch = B * wl.L * P / max(x_n, 1)   # B, or B/2 when a call runs as two streams
+    x_bytes = rows_per_launch * t_prof_mid * 2 * wl.d * es
     achieved = x_bytes / (x_avg_ms / 1e3) / 1e9
     breakdown = {k: round(v[0] / P, 4) for k, v in prof.items()}
     log("ms/step %.3f  transitions/s %.1f  step algorithmic GB/s %.1f (%.1f%% of 8 TB/s)" %

@@ -154,20 +154,26 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs g, Epi<uint16_t> epi
     acc[mb][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     acc[mb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  const int k0 = (split * 4 + wave) * g.kslice;
-  const int k1 = min(k0 + g.kslice, g.K);
+  // The workgroup's K range [kw0, kw1) is cut in 32-wide steps dealt to the
+  // four waves round-robin (wave w takes steps w, w+4, ...): at any moment
+  // the waves read adjacent 64-byte pieces of each weight row, so rows are
+  // streamed in long contiguous runs.
+  const int kw0 = split * 4 * g.kslice;
+  const int kw1 = min(kw0 + 4 * g.kslice, g.K);
+  const int all_steps = max(0, (kw1 - kw0) / 32);
+  const int k0 = kw0 + 32 * wave;  // step j of this wave is at k0 + 128 j
   // PF K-steps of loads in flight: step i is multiplied while steps
   // i+1 .. i+PF-1 are still arriving (a register ring, statically indexed).
   // The steady-state loop is branch-free so that each step waits only for
   // its own loads: the refill of step i+PF is always issued, its address
   // clamped to the last step (a harmless re-read) near the end.
   constexpr int PF = MB >= 4 ? 4 : 6;
-  const int nsteps = (k1 - k0) / 32;
+  const int nsteps = (all_steps - wave + 3) / 4;
   bf16x8_t bufa[PF][MB], bufb[PF][2];
   if (nsteps > 0) {
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
-      const int k = k0 + 32 * min(p, nsteps - 1);
+      const int k = k0 + 128 * min(p, nsteps - 1);
       bufb[p][0] = load8(wa + k);
       bufb[p][1] = load8(wb + k);
 #pragma unroll
@@ -183,7 +189,7 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs g, Epi<uint16_t> epi
         acc[mb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bufa[p][mb], bufb[p][0], acc[mb][0], 0, 0, 0);
         acc[mb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bufa[p][mb], bufb[p][1], acc[mb][1], 0, 0, 0);
       }
-      const int kn = k0 + 32 * min(i + p + PF, nsteps - 1);
+      const int kn = k0 + 128 * min(i + p + PF, nsteps - 1);
       bufb[p][0] = load8(wa + kn);
       bufb[p][1] = load8(wb + kn);
 #pragma unroll

@@ -2,6 +2,13 @@
 // the launch sequence of one transition, the replay schedule and the
 // captured-graph cache. No arithmetic of the method happens here; every
 // step runs in the HIP kernels.
+//
+// Concurrency: rows of one call are independent sequences ("Recurrent
+// Looped Transformer" §4.1), so a call with enough rows is split into two
+// row ranges whose transitions run on two streams (the caller's and one
+// the context owns), each with its own workspace, joined with events before
+// the bookkeeping kernel. The bandwidth-bound attention of one range then
+// overlaps the short matrix-product and normalisation kernels of the other.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -40,6 +47,17 @@ int fail(int code, const char* fmt, ...) {
 
 size_t elt_size(int dtype) { return dtype == RLT_BF16 ? 2 : 4; }
 
+int env_int(const char* name, int dflt) {
+  const char* v = std::getenv(name);
+  return (v && *v) ? std::atoi(v) : dflt;
+}
+
+// Per-stream scratch of one transition pipeline (rows indexed by slot).
+struct Workspace {
+  void *X, *kc, *vc, *o, *h, *act;
+  float *gbuf, *z, *q, *qm, *part, *partial, *logits;
+};
+
 }  // namespace
 
 struct rlt_ctx {
@@ -51,16 +69,20 @@ struct rlt_ctx {
   const void *merge_wg, *merge_ws, *w_out;
   std::vector<const float*> norm_s, norm_m, norm_d;
   std::vector<const void*> wq, wk, wv, wo, wqm, wom, w_gate, w_up, w_down;
-  // capacities
+  // capacities and launch shapes
   int max_rows, max_ctx, M_pad;
   int chunk, nch;
-  int hpw, hpw_x;   // heads per workgroup: SWA, cross-attention
-  // workspace (device)
+  int hpw, hpw_x;      // heads per workgroup: SWA, cross-attention
+  int gemm_mb_force;   // 0 or 1/2/4 (tuning)
+  int gemm_s_force;    // 0 or forced K split (tuning)
+  int split_min_rows;  // calls with at least this many rows run as two streams (0 = never)
+  size_t partial_cap;  // floats per workspace
+  // shared device buffers
   int *t_row, *ident, *ones, *rows_buf, *src_buf, *split_buf, *last_buf;
-  void *X, *kc, *vc, *o, *h, *act;
-  float *gbuf, *z, *q, *qm, *part, *partial, *logits;
-  size_t partial_cap;  // floats
   double* inv_freq;
+  Workspace ws[2];
+  hipStream_t aux;
+  hipEvent_t ev_fork, ev_join;
   // pinned host staging for replay schedules
   int* host_stage;
   // error word: host-mapped pinned memory written by kernels
@@ -111,13 +133,7 @@ struct Prof {
   }
 };
 
-}  // namespace
-
-// ----------------------------------------------------------------------------
-// helpers
-// ----------------------------------------------------------------------------
-
-static int check_config(const rlt_config* c) {
+int check_config(const rlt_config* c) {
   if (!c) return fail(RLT_EINVAL, "null config");
   if (c->n_layers < 1 || c->d_model < 1 || c->n_heads < 1 || c->d_head < 1 || c->window < 1 ||
       c->n_groups < 1 || c->d_ffn < 1 || c->vocab < 2)
@@ -139,12 +155,12 @@ static int check_config(const rlt_config* c) {
   return RLT_OK;
 }
 
-static int elems_per_lane(int dt) { return dt == 1 ? 16 : 8; }
+int elems_per_lane(int dt) { return dt == 1 ? 16 : 8; }
 
 // heads per attention workgroup: hpw * (dh / E) lanes per key group, which
 // must divide 256; default: the widest group of at most 32 lanes. A
 // requested value (tuning) is used when valid.
-static int choose_hpw(const rlt_config& c, int dt, int requested) {
+int choose_hpw(const rlt_config& c, int dt, int requested) {
   const int lpk = c.d_head / elems_per_lane(dt);
   auto ok = [&](int h) { return h >= 1 && h <= c.n_heads && c.n_heads % h == 0 && 256 % (h * lpk) == 0; };
   if (requested > 0 && ok(requested)) return requested;
@@ -154,19 +170,16 @@ static int choose_hpw(const rlt_config& c, int dt, int requested) {
   return best;
 }
 
-static int env_int(const char* name, int dflt) {
-  const char* v = std::getenv(name);
-  return (v && *v) ? std::atoi(v) : dflt;
-}
-
 template <typename P>
-static int dev_alloc(P** p, size_t bytes) {
+int dev_alloc(P** p, size_t bytes) {
   void* v = nullptr;
   if (bytes == 0) bytes = 16;
   if (hipMalloc(&v, bytes) != hipSuccess) return fail(RLT_ENOMEM, "hipMalloc(%zu) failed", bytes);
   *p = (P*)v;
   return RLT_OK;
 }
+
+}  // namespace
 
 // ----------------------------------------------------------------------------
 // create / destroy / layout / errors
@@ -190,17 +203,44 @@ extern "C" int rlt_state_layout(const rlt_config* cfg, int32_t B_cap, size_t byt
 
 extern "C" void rlt_destroy(rlt_ctx* c) {
   if (!c) return;
-  void* ptrs[] = {c->t_row, c->ident, c->ones, c->rows_buf, c->src_buf, c->split_buf, c->last_buf,
-                  c->X, c->kc, c->vc, c->o, c->h, c->act, c->gbuf, c->z, c->q, c->qm, c->part,
-                  c->partial, c->logits, c->inv_freq};
+  std::vector<void*> ptrs = {c->t_row, c->ident, c->ones, c->rows_buf, c->src_buf, c->split_buf, c->last_buf,
+                             c->inv_freq};
+  for (Workspace& w : c->ws) {
+    void* p[] = {w.X, w.kc, w.vc, w.o, w.h, w.act, w.gbuf, w.z, w.q, w.qm, w.part, w.partial, w.logits};
+    ptrs.insert(ptrs.end(), std::begin(p), std::end(p));
+  }
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   if (c->graph_exec) (void)hipGraphExecDestroy(c->graph_exec);
   if (c->graph) (void)hipGraphDestroy(c->graph);
+  if (c->aux) (void)hipStreamDestroy(c->aux);
+  if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
+  if (c->ev_join) (void)hipEventDestroy(c->ev_join);
   if (c->err_host) (void)hipHostFree(c->err_host);
   if (c->host_stage) (void)hipHostFree(c->host_stage);
   for (hipEvent_t e : c->prof_ev) (void)hipEventDestroy(e);
   delete c;
+}
+
+static int alloc_workspace(rlt_ctx* c, Workspace& w, bool full) {
+  const rlt_config& cf = c->cfg;
+  const size_t M = c->M_pad, es = c->es, d = cf.d_model, F = cf.d_ffn;
+  int rc = 0;
+  if ((rc = dev_alloc(&w.X, M * 2 * d * es)) || (rc = dev_alloc(&w.kc, M * d * es)) ||
+      (rc = dev_alloc(&w.vc, M * d * es)) || (rc = dev_alloc(&w.o, M * d * es)) ||
+      (rc = dev_alloc(&w.h, M * d * es)) || (rc = dev_alloc(&w.act, M * F * es)) ||
+      (rc = dev_alloc(&w.gbuf, M * d * 4)) || (rc = dev_alloc(&w.z, M * d * 4)) ||
+      (rc = dev_alloc(&w.q, M * d * 4)) || (rc = dev_alloc(&w.qm, M * d * 4)) ||
+      (rc = dev_alloc(&w.part, M * (size_t)c->nch * cf.n_heads * (cf.d_head + 2) * 4)) ||
+      (rc = dev_alloc(&w.partial, c->partial_cap * 4)) ||
+      (rc = dev_alloc(&w.logits, (full ? M : 16) * (size_t)cf.vocab * 4)))
+    return rc;
+  // rows beyond a call's n are read by the MFMA tiles and discarded: keep
+  // them finite
+  if (hipMemset(w.X, 0, M * 2 * d * es) != hipSuccess || hipMemset(w.o, 0, M * d * es) != hipSuccess ||
+      hipMemset(w.h, 0, M * d * es) != hipSuccess || hipMemset(w.act, 0, M * F * es) != hipSuccess)
+    return fail(RLT_EHIP, "workspace initialisation failed");
+  return RLT_OK;
 }
 
 extern "C" int rlt_create(const rlt_config* cfg, const rlt_weights* w, int32_t max_rows, int32_t max_ctx,
@@ -246,18 +286,22 @@ extern "C" int rlt_create(const rlt_config* cfg, const rlt_weights* w, int32_t m
   c->w_up.assign(w->w_up, w->w_up + L);
   c->w_down.assign(w->w_down, w->w_down + L);
 
-  const int d = cfg->d_model, F = cfg->d_ffn, V = cfg->vocab, H = cfg->n_heads, dh = cfg->d_head;
+  const int d = cfg->d_model, F = cfg->d_ffn, dh = cfg->d_head;
   c->max_rows = max_rows;
   c->max_ctx = max_ctx;
   c->M_pad = (max_rows + 127) / 128 * 128;
-  c->chunk = env_int("RLT_XATTN_CHUNK", d <= 512 ? 128 : 256);
-  if (c->chunk < 16 || c->chunk > 4096) c->chunk = d <= 512 ? 128 : 256;
+  // launch shapes (environment overrides exist for tuning sweeps only)
+  const int ch_default = d <= 512 ? 128 : 512;
+  c->chunk = env_int("RLT_XATTN_CHUNK", ch_default);
+  if (c->chunk < 16 || c->chunk > 4096) c->chunk = ch_default;
   c->nch = (max_ctx + c->chunk - 1) / c->chunk;
   c->hpw = choose_hpw(*cfg, c->dt, env_int("RLT_SWA_HPW", 0));
-  c->hpw_x = choose_hpw(*cfg, c->dt, env_int("RLT_XATTN_HPW", 0));
-  const size_t M = c->M_pad, es = c->es;
-  const int Nv_max = std::max(3 * d, 2 * F);
-  c->partial_cap = (size_t)8 * M * Nv_max;
+  c->hpw_x = choose_hpw(*cfg, c->dt, env_int("RLT_XATTN_HPW", 2));
+  c->gemm_mb_force = env_int("RLT_GEMM_MB", 0);
+  c->gemm_s_force = env_int("RLT_GEMM_S", 0);
+  c->split_min_rows = env_int("RLT_SPLIT_MIN_ROWS", 0);
+  c->partial_cap = (size_t)8 * c->M_pad * std::max(3 * d, 2 * F);
+  const size_t M = c->M_pad;
 
 #define ALLOC(p, bytes)                     \
   do {                                      \
@@ -271,34 +315,31 @@ extern "C" int rlt_create(const rlt_config* cfg, const rlt_weights* w, int32_t m
   ALLOC(c->src_buf, M * 4);
   ALLOC(c->split_buf, M * 4);
   ALLOC(c->last_buf, M * 4);
-  ALLOC(c->X, M * 2 * d * es);
-  ALLOC(c->kc, M * d * es);
-  ALLOC(c->vc, M * d * es);
-  ALLOC(c->o, M * d * es);
-  ALLOC(c->h, M * d * es);
-  ALLOC(c->act, M * F * es);
-  ALLOC(c->gbuf, M * d * 4);
-  ALLOC(c->z, M * d * 4);
-  ALLOC(c->q, M * d * 4);
-  ALLOC(c->qm, M * d * 4);
-  ALLOC(c->part, M * (size_t)c->nch * H * (dh + 2) * 4);
-  ALLOC(c->partial, c->partial_cap * 4);
-  ALLOC(c->logits, M * (size_t)V * 4);
   ALLOC(c->inv_freq, (size_t)(dh / 2) * sizeof(double));
 #undef ALLOC
-  // workspace contents that never change: identity slots, unit positions,
-  // zeroed A rows (rows beyond n are read by the MFMA tiles and discarded)
+  for (int i = 0; i < 2; ++i) {
+    if (i == 1 && c->split_min_rows <= 0) break;
+    if ((rc = alloc_workspace(c, c->ws[i], true))) {
+      rlt_destroy(c);
+      return rc;
+    }
+  }
   std::vector<int> iv(M), ov(M, 1);
   std::iota(iv.begin(), iv.end(), 0);
   std::vector<double> fr(dh / 2);
   for (int i = 0; i < dh / 2; ++i) fr[i] = std::pow((double)cfg->rope_theta, -2.0 * i / dh);
   if (hipMemcpy(c->ident, iv.data(), M * 4, hipMemcpyHostToDevice) != hipSuccess ||
       hipMemcpy(c->ones, ov.data(), M * 4, hipMemcpyHostToDevice) != hipSuccess ||
-      hipMemcpy(c->inv_freq, fr.data(), fr.size() * sizeof(double), hipMemcpyHostToDevice) != hipSuccess ||
-      hipMemset(c->X, 0, M * 2 * d * es) != hipSuccess || hipMemset(c->o, 0, M * d * es) != hipSuccess ||
-      hipMemset(c->h, 0, M * d * es) != hipSuccess || hipMemset(c->act, 0, M * F * es) != hipSuccess) {
+      hipMemcpy(c->inv_freq, fr.data(), fr.size() * sizeof(double), hipMemcpyHostToDevice) != hipSuccess) {
     rlt_destroy(c);
     return fail(RLT_EHIP, "workspace initialisation failed");
+  }
+  if (c->split_min_rows > 0 &&
+      (hipStreamCreateWithFlags(&c->aux, hipStreamNonBlocking) != hipSuccess ||
+       hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming) != hipSuccess ||
+       hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming) != hipSuccess)) {
+    rlt_destroy(c);
+    return fail(RLT_EHIP, "auxiliary stream creation failed");
   }
   if (hipHostMalloc((void**)&c->err_host, sizeof(int), hipHostMallocMapped) != hipSuccess ||
       hipHostGetDevicePointer((void**)&c->err_dev, c->err_host, 0) != hipSuccess) {
@@ -331,13 +372,14 @@ extern "C" int rlt_sync_error(rlt_ctx* c, void* stream) {
 }
 
 // ----------------------------------------------------------------------------
-// matrix product wrapper: picks the K split for the bf16 path
+// matrix product wrapper: picks the tile height and K split for the bf16 path
 // ----------------------------------------------------------------------------
 
 namespace {
 
 struct Gemm {
   rlt_ctx* c;
+  const Workspace* w;
   hipStream_t s;
 
   void run(const void* A, int64_t lda, std::initializer_list<const void*> W, int seg_rows, int K, int pairing,
@@ -357,19 +399,19 @@ struct Gemm {
     g.Nv = g.nseg * seg_rows;
     g.npairs = g.Nv / 32;
     g.S = 1;
+    g.mb = 1;
     g.kslice = (K + 4 * 32 - 1) / (4 * 32) * 32;
-    g.partial = c->partial;
+    g.partial = w->partial;
     if (c->dt == 1) {
       int MB = gemm_row_blocks(n);
-      const int mb_env = env_int("RLT_GEMM_MB", 0);  // tuning override: 1, 2 or 4
-      if (mb_env == 1 || mb_env == 2 || mb_env == 4) MB = mb_env;
+      const int mbf = c->gemm_mb_force;
+      if (mbf == 1 || mbf == 2 || mbf == 4) MB = mbf;
       const int mt = (n + 16 * MB - 1) / (16 * MB);
       const int tiles = g.npairs * mt;
       int S = std::max(1, (512 + tiles - 1) / tiles);   // fill the chip
       S = std::min(S, std::max(1, K / 256));             // >= 64 K per wave
       S = std::min(S, std::max(1, K / (4 * n)));         // partial traffic <= the weights'
-      const int s_env = env_int("RLT_GEMM_S", 0);    // tuning override
-      if (s_env > 0) S = std::min(s_env, std::max(1, K / 128));
+      if (c->gemm_s_force > 0) S = std::min(c->gemm_s_force, std::max(1, K / 128));
       while (S > 1 && (size_t)S * c->M_pad * g.Nv > c->partial_cap) --S;
       g.S = S;
       g.mb = MB;
@@ -387,24 +429,25 @@ struct StepPlan {
   EIn e;
   rlt_memory mem;
   rlt_state* st;
-  // outputs
+  // outputs (slot-indexed pointers start at this plan's first slot)
   float* s_out;
   float* s_trace;
   int64_t s_trace_sb;
-  float* z_trace;
+  float* z_trace;         // [L][z_trace_ld][d], this plan's rows at z_trace
+  int z_trace_ld;
   bool need_logits;
-  float* logits;          // where the logits go
+  float* logits;          // caller's [n][V] or null (workspace)
   ReadoutArgs ro;
   bool do_readout;
 };
 
-// the transition for n slots: merge, L_D blocks, final norm, readout
-void enqueue_transition(rlt_ctx* c, const StepPlan& P, hipStream_t s) {
+// the transition for the plan's slots: merge, L_D blocks, final norm, readout
+void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipStream_t s) {
   const rlt_config& cf = c->cfg;
   const int d = cf.d_model, F = cf.d_ffn, H = cf.n_heads, dh = cf.d_head, L = cf.n_layers;
   const int n = P.n;
   const size_t es = c->es;
-  Gemm gm{c, s};
+  Gemm gm{c, &w, s};
 
   EpiArgs E0{};
   E0.rows = P.R;
@@ -428,27 +471,27 @@ void enqueue_transition(rlt_ctx* c, const StepPlan& P, hipStream_t s) {
 
   // ---- merge [eqs. (2.9)-(2.11)] ----
   m.gain = c->merge_norm;
-  m.out = c->X;
+  m.out = w.X;
   m.ld_out = 2 * d;
   { Prof pf(c, RLT_PROF_NORM, s); launch_merge_prep(c->dt, m, s); }
   if (cf.merge_kind == RLT_MERGE_GATED) {
     EpiArgs e = E0;
     e.kind = EPI_MGATE;
-    e.out_f = c->gbuf;
+    e.out_f = w.gbuf;
     e.ldo = d;
     e.bias = c->merge_bg;
-    gm.run(c->X, 2 * d, {c->merge_wg}, d, 2 * d, PAIR_PLAIN, n, e);
+    gm.run(w.X, 2 * d, {c->merge_wg}, d, 2 * d, PAIR_PLAIN, n, e);
     e.kind = EPI_MOUT;
-    e.out_f = c->z;
-    e.gbuf = c->gbuf;
-    gm.run((const char*)c->X + d * es, 2 * d, {c->merge_ws}, d, d, PAIR_PLAIN, n, e);
+    e.out_f = w.z;
+    e.gbuf = w.gbuf;
+    gm.run((const char*)w.X + d * es, 2 * d, {c->merge_ws}, d, d, PAIR_PLAIN, n, e);
   } else {
     EpiArgs e = E0;
     e.kind = EPI_CONVEX;
-    e.out_f = c->z;
+    e.out_f = w.z;
     e.ldo = d;
     e.bias = c->merge_bg;
-    gm.run(c->X, 2 * d, {c->merge_wg}, d, 2 * d, PAIR_PLAIN, n, e);
+    gm.run(w.X, 2 * d, {c->merge_wg}, d, 2 * d, PAIR_PLAIN, n, e);
   }
 
   AttnArgs at{};
@@ -456,45 +499,44 @@ void enqueue_transition(rlt_ctx* c, const StepPlan& P, hipStream_t s) {
   at.d = d;
   at.H = H;
   at.dh = dh;
-  at.hpw = c->hpw;
   at.qscale = (float)(1.4426950408889634 / std::sqrt((double)dh));
   at.W = cf.window;
   at.chunk = c->chunk;
-  at.nch = std::min(c->nch, (c->max_ctx + c->chunk - 1) / c->chunk);
-  at.part = c->part;
+  at.nch = c->nch;
+  at.part = w.part;
   at.sb = P.mem.stride_b;
   at.st = P.mem.stride_t;
 
   const size_t ring_layer = (size_t)P.st->B_cap * (cf.window - 1) * d * es;
+  m.z = w.z;
+  m.out = w.h;
+  m.ld_out = d;
   for (int l = 0; l < L; ++l) {
     // ---- SWA sublayer [eqs. (2.12)-(2.14)] ----
-    m.z = c->z;
     m.gain = c->norm_s[l];
-    m.out = c->h;
-    m.ld_out = d;
     { Prof pf(c, RLT_PROF_NORM, s); launch_rmsnorm(c->dt, m, s); }
     {
       EpiArgs e = E0;
       e.kind = EPI_QKV;
-      e.out_f = c->q;
-      e.out_k = c->kc;
-      e.out_v = c->vc;
-      gm.run(c->h, d, {c->wq[l], c->wk[l], c->wv[l]}, d, d, PAIR_ROPE, n, e);
+      e.out_f = w.q;
+      e.out_k = w.kc;
+      e.out_v = w.vc;
+      gm.run(w.h, d, {c->wq[l], c->wk[l], c->wv[l]}, d, d, PAIR_ROPE, n, e);
     }
-    at.q = c->q;
-    at.kc = c->kc;
-    at.vc = c->vc;
+    at.q = w.q;
+    at.kc = w.kc;
+    at.vc = w.vc;
     at.ring_k = (char*)P.st->ring_k + l * ring_layer;
     at.ring_v = (char*)P.st->ring_v + l * ring_layer;
-    at.out = c->o;
+    at.out = w.o;
     at.hpw = c->hpw;
     { Prof pf(c, RLT_PROF_SWA, s); launch_swa(c->dt, at, s); }
     {
       EpiArgs e = E0;
       e.kind = EPI_RESID;
-      e.out_f = c->z;
+      e.out_f = w.z;
       e.ldo = d;
-      gm.run(c->o, d, {c->wo[l]}, d, d, PAIR_PLAIN, n, e);
+      gm.run(w.o, d, {c->wo[l]}, d, d, PAIR_PLAIN, n, e);
     }
     // ---- cross-attention sublayer [eq. (2.15)] ----
     m.gain = c->norm_m[l];
@@ -502,11 +544,11 @@ void enqueue_transition(rlt_ctx* c, const StepPlan& P, hipStream_t s) {
     {
       EpiArgs e = E0;
       e.kind = EPI_QROT;
-      e.out_f = c->qm;
-      gm.run(c->h, d, {c->wqm[l]}, d, d, PAIR_ROPE, n, e);
+      e.out_f = w.qm;
+      gm.run(w.h, d, {c->wqm[l]}, d, d, PAIR_ROPE, n, e);
     }
     const int g = (l * cf.n_groups) / L;
-    at.q = c->qm;
+    at.q = w.qm;
     at.mk = (const char*)P.mem.k + (size_t)g * P.mem.stride_g * es;
     at.mv = (const char*)P.mem.v + (size_t)g * P.mem.stride_g * es;
     at.hpw = c->hpw_x;
@@ -515,9 +557,9 @@ void enqueue_transition(rlt_ctx* c, const StepPlan& P, hipStream_t s) {
     {
       EpiArgs e = E0;
       e.kind = EPI_RESID;
-      e.out_f = c->z;
+      e.out_f = w.z;
       e.ldo = d;
-      gm.run(c->o, d, {c->wom[l]}, d, d, PAIR_PLAIN, n, e);
+      gm.run(w.o, d, {c->wom[l]}, d, d, PAIR_PLAIN, n, e);
     }
     // ---- FFN sublayer [eq. (2.16)] ----
     m.gain = c->norm_d[l];
@@ -525,32 +567,80 @@ void enqueue_transition(rlt_ctx* c, const StepPlan& P, hipStream_t s) {
     {
       EpiArgs e = E0;
       e.kind = EPI_SWIGLU;
-      e.out_k = c->act;
+      e.out_k = w.act;
       e.ldo = F;
-      gm.run(c->h, d, {c->w_gate[l], c->w_up[l]}, F, d, PAIR_DUAL, n, e);
+      gm.run(w.h, d, {c->w_gate[l], c->w_up[l]}, F, d, PAIR_DUAL, n, e);
       e.kind = EPI_RESID;
-      e.out_f = c->z;
+      e.out_f = w.z;
       e.ldo = d;
-      gm.run(c->act, F, {c->w_down[l]}, d, F, PAIR_PLAIN, n, e);
+      gm.run(w.act, F, {c->w_down[l]}, d, F, PAIR_PLAIN, n, e);
     }
-    if (P.z_trace) launch_copy_f32(c->z, P.z_trace + (size_t)l * n * d, (int64_t)n * d, s);
+    if (P.z_trace) launch_copy_f32(w.z, P.z_trace + (size_t)l * P.z_trace_ld * d, (int64_t)n * d, s);
   }
   // ---- s_t write-back, RMSNorm_o [eq. (2.6)] ----
   m.gain = c->out_norm;
-  m.out = c->h;
-  m.ld_out = d;
   m.s_out = P.s_out;
   m.s_trace = P.s_trace;
   m.s_trace_sb = P.s_trace_sb;
   { Prof pf(c, RLT_PROF_NORM, s); launch_final(c->dt, m, s); }
+  float* logits = P.logits ? P.logits : w.logits;
   if (P.need_logits) {
     EpiArgs e = E0;
     e.kind = EPI_STORE;
-    e.out_f = P.logits;
+    e.out_f = logits;
     e.ldo = cf.vocab;
-    gm.run(c->h, d, {c->w_out}, cf.vocab, d, PAIR_PLAIN, n, e);
+    gm.run(w.h, d, {c->w_out}, cf.vocab, d, PAIR_PLAIN, n, e);
   }
-  if (P.do_readout) { Prof pf(c, RLT_PROF_READOUT, s); launch_readout(P.ro, s); }
+  if (P.do_readout) {
+    ReadoutArgs ro = P.ro;
+    ro.logits = logits;
+    Prof pf(c, RLT_PROF_READOUT, s);
+    launch_readout(ro, s);
+  }
+}
+
+template <typename T>
+T* off_ptr(T* p, int64_t off) {
+  return p ? p + off : p;
+}
+
+// The plan restricted to slots [off, off + cnt).
+StepPlan slice(const StepPlan& P, int off, int cnt, int d, int V) {
+  StepPlan Q = P;
+  Q.R = Rows{P.R.rows + off, P.R.src + off, P.R.t_row + off, cnt};
+  Q.n = cnt;
+  Q.s_out = off_ptr(P.s_out, (int64_t)off * d);
+  Q.z_trace = off_ptr(P.z_trace, (int64_t)off * d);
+  Q.logits = off_ptr(P.logits, (int64_t)off * V);
+  ReadoutArgs& ro = Q.ro;
+  ro.rows = Q.R;
+  ro.n = cnt;
+  ro.argmax = off_ptr(P.ro.argmax, off);
+  if (P.ro.mode == 0) {
+    ro.score_tok = off_ptr(P.ro.score_tok, off);
+    ro.logp = off_ptr(P.ro.logp, off);
+  }
+  ro.uniform = off_ptr(P.ro.uniform, off);
+  ro.sample_tok = off_ptr(P.ro.sample_tok, off);
+  ro.sample_logmu = off_ptr(P.ro.sample_logmu, off);
+  return Q;
+}
+
+// Run the plan, as two concurrent row ranges when it has enough rows.
+void enqueue_rows(rlt_ctx* c, const StepPlan& P, hipStream_t s) {
+  const int n = P.n;
+  if (c->split_min_rows <= 0 || n < c->split_min_rows || !c->aux) {
+    enqueue_transition(c, c->ws[0], P, s);
+    return;
+  }
+  const int d = c->cfg.d_model, V = c->cfg.vocab;
+  const int n0 = ((n + 1) / 2 + 15) / 16 * 16 < n ? ((n + 1) / 2 + 15) / 16 * 16 : (n + 1) / 2;
+  (void)hipEventRecord(c->ev_fork, s);
+  (void)hipStreamWaitEvent(c->aux, c->ev_fork, 0);
+  enqueue_transition(c, c->ws[0], slice(P, 0, n0, d, V), s);
+  enqueue_transition(c, c->ws[1], slice(P, n0, n - n0, d, V), c->aux);
+  (void)hipEventRecord(c->ev_join, c->aux);
+  (void)hipStreamWaitEvent(s, c->ev_join, 0);
 }
 
 int check_state(rlt_ctx* c, const rlt_state* st) {
@@ -598,15 +688,15 @@ static int step_enqueue(rlt_ctx* c, rlt_state* st, const rlt_step_io* io, hipStr
   P.st = st;
   P.s_out = io->s_out;
   P.z_trace = io->z_trace;
+  P.z_trace_ld = n;
   const bool sampling = io->uniform != nullptr;
   P.need_logits = io->logits || io->argmax || io->logp || sampling;
-  P.logits = io->logits ? io->logits : c->logits;
+  P.logits = io->logits;
   P.do_readout = io->argmax || io->logp || sampling;
   ReadoutArgs& ro = P.ro;
   ro.rows = P.R;
   ro.n = n;
   ro.V = c->cfg.vocab;
-  ro.logits = P.logits;
   ro.argmax = io->argmax;
   ro.mode = 0;
   ro.score_tok = io->score_tok;
@@ -629,7 +719,7 @@ static int step_enqueue(rlt_ctx* c, rlt_state* st, const rlt_step_io* io, hipStr
   m.max_t = c->max_ctx;
   m.B_cap = st->B_cap;
   launch_prestep(m, s);
-  enqueue_transition(c, P, s);
+  enqueue_rows(c, P, s);
   PostArgs pa{P.R, n, st->pos, st->pending, nullptr};
   if (io->flags & RLT_STEP_DEFER) pa.next_tok = sampling ? io->sample_tok : io->argmax;
   launch_poststep(pa, s);
@@ -755,13 +845,11 @@ extern "C" int rlt_replay_sequence(rlt_ctx* c, rlt_state* st, const rlt_replay_i
     P.s_trace = io->s_trace;
     P.s_trace_sb = io->s_stride_b;
     P.need_logits = true;
-    P.logits = c->logits;
     P.do_readout = true;
     ReadoutArgs& ro = P.ro;
     ro.rows = P.R;
     ro.n = nt;
     ro.V = c->cfg.vocab;
-    ro.logits = c->logits;
     ro.mode = 1;
     ro.score_tok = io->tokens;
     ro.tok_sb = io->tok_stride_b;
@@ -769,7 +857,7 @@ extern "C" int rlt_replay_sequence(rlt_ctx* c, rlt_state* st, const rlt_replay_i
     ro.logp_sb = io->logp_stride_b;
     ro.split = c->split_buf;
     launch_replay_rows(c->rows_buf, c->src_buf, nt, t, c->t_row, st->pos, io->mem.mem_len, c->err_dev, s);
-    enqueue_transition(c, P, s);
+    enqueue_rows(c, P, s);
     PostArgs pa{P.R, nt, st->pos, st->pending, nullptr};
     launch_poststep(pa, s);
   }
@@ -788,6 +876,7 @@ extern "C" int rlt_score_logprobs(rlt_ctx* c, const rlt_score_io* io, void* stre
   int rc = take_device_error(c);
   if (rc) return rc;
   hipStream_t s = (hipStream_t)stream;
+  const Workspace& w = c->ws[0];
   const int n = io->n, d = c->cfg.d_model;
   Rows R{c->ident, c->ident, c->ones, n};
   MiscArgs m{};
@@ -797,22 +886,22 @@ extern "C" int rlt_score_logprobs(rlt_ctx* c, const rlt_score_io* io, void* stre
   m.eps = c->cfg.rms_eps;
   m.z = io->s;
   m.gain = c->out_norm;
-  m.out = c->h;
+  m.out = w.h;
   m.ld_out = d;
   launch_rmsnorm(c->dt, m, s);
   EpiArgs e{};
   e.kind = EPI_STORE;
   e.rows = R;
   e.d = d;
-  e.out_f = c->logits;
+  e.out_f = w.logits;
   e.ldo = c->cfg.vocab;
-  Gemm gm{c, s};
-  gm.run(c->h, d, {c->w_out}, c->cfg.vocab, d, PAIR_PLAIN, n, e);
+  Gemm gm{c, &w, s};
+  gm.run(w.h, d, {c->w_out}, c->cfg.vocab, d, PAIR_PLAIN, n, e);
   ReadoutArgs ro{};
   ro.rows = R;
   ro.n = n;
   ro.V = c->cfg.vocab;
-  ro.logits = c->logits;
+  ro.logits = w.logits;
   ro.mode = 0;
   ro.score_tok = io->tokens;
   ro.logp = io->logp;
@@ -827,7 +916,7 @@ extern "C" int rlt_score_logprobs(rlt_ctx* c, const rlt_score_io* io, void* stre
 }
 
 // ----------------------------------------------------------------------------
-// kernel-level parity hook (test-only)
+// test / benchmark hooks (include/rlt_debug.h)
 // ----------------------------------------------------------------------------
 
 extern "C" int rlt_dbg_gemm(rlt_ctx* c, const void* A, const void* W, int32_t M, int32_t N, int32_t K,
@@ -837,8 +926,9 @@ extern "C" int rlt_dbg_gemm(rlt_ctx* c, const void* A, const void* W, int32_t M,
   if (M < 1 || M > c->max_rows || N < 32 || N % 32 || K < 32 || K % 32 || K > kmax)
     return fail(RLT_ESHAPE, "need 1 <= M <= max_rows, N and K multiples of 32, K <= max(2*d_model, d_ffn)");
   hipStream_t s = (hipStream_t)stream;
+  const Workspace& w = c->ws[0];
   // A goes through a padded workspace buffer: the MFMA tiles read whole 16-row blocks
-  void* stage = K <= 2 * c->cfg.d_model ? c->X : c->act;
+  void* stage = K <= 2 * c->cfg.d_model ? w.X : w.act;
   HIP_TRY(hipMemcpyAsync(stage, A, (size_t)M * K * c->es, hipMemcpyDeviceToDevice, s));
   Rows R{c->ident, c->ident, c->ones, M};
   EpiArgs e{};
@@ -846,7 +936,7 @@ extern "C" int rlt_dbg_gemm(rlt_ctx* c, const void* A, const void* W, int32_t M,
   e.rows = R;
   e.out_f = out;
   e.ldo = N;
-  Gemm gm{c, s};
+  Gemm gm{c, &w, s};
   gm.run(stage, K, {W}, N, K, PAIR_PLAIN, M, e);
   HIP_TRY(hipGetLastError());
   return RLT_OK;

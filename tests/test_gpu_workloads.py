@@ -20,15 +20,33 @@ TOL = 2e-2
 
 
 def _check(S, Z, So, Zo, tag):
+    """Relative-L2 gate per (row, step); returns per-step top-1 outcomes:
+    1 = same argmax, 0 = different argmax although the oracle's top-2 gap
+    exceeds this step's largest logit error, None = different argmax inside
+    a near-tie (oracle top-2 gap <= largest logit error: both within the
+    numerical tolerance)."""
+    out = []
     for i in range(len(So)):
         assert rel_l2(S[i], So[i]) < TOL, (tag, i, rel_l2(S[i], So[i]))
         assert rel_l2(Z[i], Zo[i]) < TOL, (tag, i, rel_l2(Z[i], Zo[i]))
-    return np.mean([np.argmax(Z[i]) == np.argmax(Zo[i]) for i in range(len(So))])
+        if np.argmax(Z[i]) == np.argmax(Zo[i]):
+            out.append(1)
+        else:
+            top2 = np.sort(Zo[i])[-2:]
+            out.append(None if top2[1] - top2[0] <= np.abs(Z[i] - Zo[i]).max() else 0)
+    return out
+
+
+def _top1(outcomes):
+    raw = np.mean([o == 1 for o in outcomes])
+    decided = [o for o in outcomes if o is not None]
+    return raw, (np.mean(decided) if decided else 1.0)
 
 
 def test_mid_from_h0_sampled_rows():
     """L_D=12, d=1024, 16x64 heads, W=128: all 64 rows for 40 steps from
-    H_0; the oracle replays rows 0 and 41."""
+    H_0; the oracle replays rows 0, 21, 41 and 63 (160 checked steps; top-1
+    agreement >= 99 % outside near-ties, raw rate printed)."""
     require_gpu()
     wl = synth.MID.with_(T=64)
     run = GpuRun(wl, B=64, T=64)
@@ -36,7 +54,7 @@ def test_mid_from_h0_sampled_rows():
     S, Z = run.run(40)
     orc = Oracle(oracle_config(wl), oracle_weights(run.raw))
     agree = []
-    for b in (0, 41):
+    for b in (0, 21, 41, 63):
         mem = Memory([widen(run.mk[g, b]) for g in range(wl.G)], [widen(run.mv[g, b]) for g in range(wl.G)])
         st = orc.initial_state()
         So, Zo = [], []
@@ -44,8 +62,10 @@ def test_mid_from_h0_sampled_rows():
             st = orc.transition(st, widen(run.E[b, t - 1]), mem)
             So.append(st.s)
             Zo.append(orc.logits(st.s))
-        agree.append(_check(S[:, b], Z[:, b], So, Zo, "mid b=%d" % b))
-    assert np.mean(agree) >= 0.99
+        agree += _check(S[:, b], Z[:, b], So, Zo, "mid b=%d" % b)
+    raw, decided = _top1(agree)
+    print("mid top-1 agreement: raw %.4f, outside near-ties %.4f over %d steps" % (raw, decided, len(agree)))
+    assert decided >= 0.99
 
 
 def _prefilled(wl, B, t0, check_rows, graph=False, nsteps=3, seed=0):
