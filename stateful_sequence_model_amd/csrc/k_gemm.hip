@@ -51,13 +51,26 @@ struct Epi {
     y = yr;
   }
 
-  __device__ __forceinline__ void operator()(int m, int ca, float va, int cb, float vb) const {
+  // next RMSNorm's input: zb = z * gain (the rstd is applied by the consumer)
+  __device__ __forceinline__ float produce(int m, int ca, float za, int cb, float zb) const {
+    T* o = (T*)a.zb + (int64_t)m * a.d;
+    o[ca] = from_f<T>(za * a.gnext[ca]);
+    o[cb] = from_f<T>(zb * a.gnext[cb]);
+    return za * za + zb * zb;
+  }
+
+  // Epilogue of one column pair of row m. rs scales the accumulators of
+  // products whose input is z * gain of an RMSNorm (1 otherwise). Returns
+  // the squared sum of the produced residual values (0 for non-producers).
+  __device__ __forceinline__ float operator()(int m, int ca, float va, int cb, float vb, float rs) const {
     switch (a.kind) {
       case EPI_STORE:
-        a.out_f[(int64_t)m * a.ldo + ca] = va;
-        a.out_f[(int64_t)m * a.ldo + cb] = vb;
-        break;
+        a.out_f[(int64_t)m * a.ldo + ca] = va * rs;
+        a.out_f[(int64_t)m * a.ldo + cb] = vb * rs;
+        return 0.f;
       case EPI_QKV: {
+        va *= rs;
+        vb *= rs;
         const int seg = ca / a.d;
         const int xa = ca - seg * a.d, xb = cb - seg * a.d;
         if (seg < 2 && a.rope) rotate(m, xa % a.dh, va, vb);
@@ -70,50 +83,61 @@ struct Epi {
           dst[o + xa] = from_f<T>(va);
           dst[o + xb] = from_f<T>(vb);
         }
-        break;
+        return 0.f;
       }
       case EPI_QROT: {
+        va *= rs;
+        vb *= rs;
         if (a.rope) rotate(m, ca % a.dh, va, vb);
         a.out_f[(int64_t)m * a.d + ca] = va;
         a.out_f[(int64_t)m * a.d + cb] = vb;
-        break;
+        return 0.f;
       }
       case EPI_RESID: {
         float* z = a.out_f + (int64_t)m * a.ldo;
-        z[ca] += va;
-        z[cb] += vb;
-        break;
+        const float za = z[ca] + va, zb = z[cb] + vb;
+        z[ca] = za;
+        z[cb] = zb;
+        return produce(m, ca, za, cb, zb);
       }
       case EPI_SWIGLU: {
+        va *= rs;
+        vb *= rs;
         const float act = va * sigmoidf_(va) * vb;
         ((T*)a.out_k)[(int64_t)m * a.ldo + ca] = from_f<T>(act);
-        break;
+        return 0.f;
       }
       case EPI_MGATE: {
         float* g = a.out_f + (int64_t)m * a.ldo;
         g[ca] = sigmoidf_(va + a.bias[ca]);
         g[cb] = sigmoidf_(vb + a.bias[cb]);
-        break;
+        return 0.f;
       }
       case EPI_MOUT: {
         float* z = a.out_f + (int64_t)m * a.ldo;
         const float* g = a.gbuf + (int64_t)m * a.ldo;
-        z[ca] = e_at(m, ca) + a.alpha * g[ca] * va;
-        z[cb] = e_at(m, cb) + a.alpha * g[cb] * vb;
-        break;
+        const float za = e_at(m, ca) + a.alpha * g[ca] * va;
+        const float zb = e_at(m, cb) + a.alpha * g[cb] * vb;
+        z[ca] = za;
+        z[cb] = zb;
+        return produce(m, ca, za, cb, zb);
       }
       case EPI_CONVEX: {
-        if (a.rows.t_row[m] <= 0) break;
+        float za = 0.f, zb = 0.f;
+        if (a.rows.t_row[m] > 0) {
+          const float* s = a.s_state + (int64_t)a.rows.rows[m] * a.d;
+          const float ga = sigmoidf_(va + a.bias[ca]);
+          const float gb = sigmoidf_(vb + a.bias[cb]);
+          za = ga * e_at(m, ca) + (1.f - ga) * s[ca];
+          zb = gb * e_at(m, cb) + (1.f - gb) * s[cb];
+        }
         float* z = a.out_f + (int64_t)m * a.ldo;
-        const float* s = a.s_state + (int64_t)a.rows.rows[m] * a.d;
-        const float ga = sigmoidf_(va + a.bias[ca]);
-        const float gb = sigmoidf_(vb + a.bias[cb]);
-        z[ca] = ga * e_at(m, ca) + (1.f - ga) * s[ca];
-        z[cb] = gb * e_at(m, cb) + (1.f - gb) * s[cb];
-        break;
+        z[ca] = za;
+        z[cb] = zb;
+        return produce(m, ca, za, cb, zb);
       }
       default:
-        break;
+        return 0.f;
     }
   }
 };
@@ -148,6 +172,9 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs g, Epi<uint16_t> epi
   for (int mb = 0; mb < MB; ++mb)
     ap[mb] = (const uint16_t*)g.A + (int64_t)(m0 + mb * 16 + r16) * g.lda + kq;
 
+  // folded RMSNorm: this tile's row sums of squares, loads in flight with the K loop
+  const bool norm_here = g.S == 1 && g.ssq_in != nullptr;
+  RowRstd<MB * 16> rr(g, norm_here ? m0 : 0);
   f32x4_t acc[MB][2];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
@@ -215,14 +242,23 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs g, Epi<uint16_t> epi
       red[wave][mb * 16 + (lane >> 4) * 4 + i][r16] = acc[mb][0][i];
       red[wave][mb * 16 + (lane >> 4) * 4 + i][16 + r16] = acc[mb][1][i];
     }
+  __shared__ float s_rstd[MB * 16];
+  __shared__ float s_part[256];
+  if (norm_here) rr.finish(g, m0, s_part, s_rstd);  // uniform branch: contains a barrier
   __syncthreads();
+  // every lane runs the same trip count (the 16 lanes of a row reduce together)
   for (int idx = threadIdx.x; idx < MB * 16 * 16; idx += 256) {
     const int m = idx >> 4, r = idx & 15;
     const int slot = m0 + m;
     const float va = ((red[0][m][r] + red[1][m][r]) + red[2][m][r]) + red[3][m][r];
     const float vb = ((red[0][m][16 + r] + red[1][m][16 + r]) + red[2][m][16 + r]) + red[3][m][16 + r];
     if (g.S == 1) {
-      if (slot < g.M) epi(slot, ba * 16 + r, va, bb * 16 + r, vb);
+      float sq = 0.f;
+      if (slot < g.M) sq = epi(slot, ba * 16 + r, va, bb * 16 + r, vb, g.ssq_in ? s_rstd[m] : 1.f);
+      if (g.ssq_out) {
+        sq = sum16(sq);
+        if (r == 0 && slot < g.M) g.ssq_out[(int64_t)pair * g.M_pad + slot] = sq;
+      }
     } else if (slot < g.M) {
       float* P = g.partial + ((int64_t)split * g.M_pad + slot) * g.Nv;
       P[ba * 16 + r] = va;
@@ -235,17 +271,30 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs g, Epi<uint16_t> epi
 // grid: x = pair, y = ceil(M/16); block 256
 template <typename T>
 __global__ __launch_bounds__(256) void k_splitk_epi(GemmArgs g, Epi<T> epi) {
+  __shared__ float s_rstd[16];
+  __shared__ float s_part[256];
   int ba, bb;
   pair_blocks(g, blockIdx.x, ba, bb);
   const int m = blockIdx.y * 16 + (threadIdx.x >> 4), r = threadIdx.x & 15;
-  if (m >= g.M) return;
-  float va = 0.f, vb = 0.f;
-  for (int s = 0; s < g.S; ++s) {
-    const float* P = g.partial + ((int64_t)s * g.M_pad + m) * g.Nv;
-    va += P[ba * 16 + r];
-    vb += P[bb * 16 + r];
+  if (g.ssq_in) {
+    RowRstd<16> rr(g, blockIdx.y * 16);
+    rr.finish(g, blockIdx.y * 16, s_part, s_rstd);
   }
-  epi(m, ba * 16 + r, va, bb * 16 + r, vb);
+  __syncthreads();
+  float sq = 0.f;
+  if (m < g.M) {
+    float va = 0.f, vb = 0.f;
+    for (int s = 0; s < g.S; ++s) {
+      const float* P = g.partial + ((int64_t)s * g.M_pad + m) * g.Nv;
+      va += P[ba * 16 + r];
+      vb += P[bb * 16 + r];
+    }
+    sq = epi(m, ba * 16 + r, va, bb * 16 + r, vb, g.ssq_in ? s_rstd[threadIdx.x >> 4] : 1.f);
+  }
+  if (g.ssq_out) {
+    sq = sum16(sq);
+    if (r == 0 && m < g.M) g.ssq_out[(int64_t)blockIdx.x * g.M_pad + m] = sq;
+  }
 }
 
 // fp32: one thread per (row, column pair); columns paired per element:
@@ -283,7 +332,9 @@ __global__ __launch_bounds__(64) void k_gemm_f32(GemmArgs g, Epi<float> epi) {
     sa = fmaf(x.x, p.x, sa); sa = fmaf(x.y, p.y, sa); sa = fmaf(x.z, p.z, sa); sa = fmaf(x.w, p.w, sa);
     sb = fmaf(x.x, r.x, sb); sb = fmaf(x.y, r.y, sb); sb = fmaf(x.z, r.z, sb); sb = fmaf(x.w, r.w, sb);
   }
-  epi(m, ca, sa, cb, sb);
+  // one column pair per thread: the pair is the unit of the squared sums
+  const float sq = epi(m, ca, sa, cb, sb, g.ssq_in ? row_rstd(g, m) : 1.f);
+  if (g.ssq_out) g.ssq_out[(int64_t)q * g.M_pad + m] = sq;
 }
 
 void launch_gemm(int dtype, const GemmArgs& g0, const EpiArgs& e, hipStream_t s) {

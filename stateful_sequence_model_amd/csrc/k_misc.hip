@@ -132,29 +132,22 @@ __global__ __launch_bounds__(256) void k_merge_prep(MiscArgs a) {
   }
 }
 
-// s_t write-back (state, optional outputs) and RMSNorm_o for the readout
+// s_t write-back to the state and the optional outputs (the readout's
+// RMSNorm_o input was produced by the last block's down projection)
 template <typename T>
 __global__ __launch_bounds__(256) void k_final(MiscArgs a) {
-  __shared__ float scratch[16];
   const int slot = blockIdx.x;
   const int t = a.rows.t_row[slot];
   const float* z = a.z + (int64_t)slot * a.d;
-  if (t > 0) {
-    float* s = a.s_state + (int64_t)a.rows.rows[slot] * a.d;
-    for (int c = threadIdx.x; c < a.d; c += 256) s[c] = z[c];
-    if (a.s_out)
-      for (int c = threadIdx.x; c < a.d; c += 256) a.s_out[(int64_t)slot * a.d + c] = z[c];
-    if (a.s_trace) {
-      float* st = a.s_trace + (int64_t)a.rows.src[slot] * a.s_trace_sb + (int64_t)(t - 1) * a.d;
-      for (int c = threadIdx.x; c < a.d; c += 256) st[c] = z[c];
-    }
+  if (t <= 0) return;
+  float* s = a.s_state + (int64_t)a.rows.rows[slot] * a.d;
+  for (int c = threadIdx.x; c < a.d; c += 256) s[c] = z[c];
+  if (a.s_out)
+    for (int c = threadIdx.x; c < a.d; c += 256) a.s_out[(int64_t)slot * a.d + c] = z[c];
+  if (a.s_trace) {
+    float* st = a.s_trace + (int64_t)a.rows.src[slot] * a.s_trace_sb + (int64_t)(t - 1) * a.d;
+    for (int c = threadIdx.x; c < a.d; c += 256) st[c] = z[c];
   }
-  float ss = 0.f;
-  for (int c = threadIdx.x; c < a.d; c += 256) ss = fmaf(z[c], z[c], ss);
-  ss = block_sum(ss, scratch);
-  const float r = 1.0f / sqrtf(ss / (float)a.d + a.eps);
-  T* out = (T*)a.out + (int64_t)slot * a.ld_out;
-  for (int c = threadIdx.x; c < a.d; c += 256) out[c] = from_f<T>(z[c] * r * a.gain[c]);
 }
 
 __global__ void k_copy_f32(const float* src, float* dst, int64_t n) {

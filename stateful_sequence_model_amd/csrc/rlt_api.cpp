@@ -56,6 +56,7 @@ int env_int(const char* name, int dflt) {
 struct Workspace {
   void *X, *kc, *vc, *o, *h, *act;
   float *gbuf, *z, *q, *qm, *part, *partial, *logits;
+  float* ssq;  // [d/2][M_pad] partial sums of squares of z (folded RMSNorm)
 };
 
 }  // namespace
@@ -206,7 +207,7 @@ extern "C" void rlt_destroy(rlt_ctx* c) {
   std::vector<void*> ptrs = {c->t_row, c->ident, c->ones, c->rows_buf, c->src_buf, c->split_buf, c->last_buf,
                              c->inv_freq};
   for (Workspace& w : c->ws) {
-    void* p[] = {w.X, w.kc, w.vc, w.o, w.h, w.act, w.gbuf, w.z, w.q, w.qm, w.part, w.partial, w.logits};
+    void* p[] = {w.X, w.kc, w.vc, w.o, w.h, w.act, w.gbuf, w.z, w.q, w.qm, w.part, w.partial, w.logits, w.ssq};
     ptrs.insert(ptrs.end(), std::begin(p), std::end(p));
   }
   for (void* p : ptrs)
@@ -233,7 +234,8 @@ static int alloc_workspace(rlt_ctx* c, Workspace& w, bool full) {
       (rc = dev_alloc(&w.q, M * d * 4)) || (rc = dev_alloc(&w.qm, M * d * 4)) ||
       (rc = dev_alloc(&w.part, M * (size_t)c->nch * cf.n_heads * (cf.d_head + 2) * 4)) ||
       (rc = dev_alloc(&w.partial, c->partial_cap * 4)) ||
-      (rc = dev_alloc(&w.logits, (full ? M : 16) * (size_t)cf.vocab * 4)))
+      (rc = dev_alloc(&w.logits, (full ? M : 16) * (size_t)cf.vocab * 4)) ||
+      (rc = dev_alloc(&w.ssq, M * (size_t)(d / 2) * 4)))
     return rc;
   // rows beyond a call's n are read by the MFMA tiles and discarded: keep
   // them finite
@@ -383,7 +385,7 @@ struct Gemm {
   hipStream_t s;
 
   void run(const void* A, int64_t lda, std::initializer_list<const void*> W, int seg_rows, int K, int pairing,
-           int n, EpiArgs e) {
+           int n, EpiArgs e, const float* ssq_in = nullptr, float* ssq_out = nullptr) {
     GemmArgs g{};
     g.A = A;
     g.lda = lda;
@@ -402,6 +404,11 @@ struct Gemm {
     g.mb = 1;
     g.kslice = (K + 4 * 32 - 1) / (4 * 32) * 32;
     g.partial = w->partial;
+    g.ssq_in = ssq_in;
+    g.ssq_out = ssq_out;
+    g.ssq_units = c->cfg.d_model / (c->dt == 1 ? 32 : 2);  // column units of the producers
+    g.inv_d = 1.0f / (float)c->cfg.d_model;
+    g.eps = c->cfg.rms_eps;
     if (c->dt == 1) {
       int MB = gemm_row_blocks(n);
       const int mbf = c->gemm_mb_force;
@@ -470,10 +477,18 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
   m.merge_kind = cf.merge_kind;
 
   // ---- merge [eqs. (2.9)-(2.11)] ----
+  // Every RMSNorm is folded into the matrix products: the producer of z
+  // (merge or residual epilogue) writes z * gain_next into w.h and per-row
+  // partial sums of squares into w.ssq; the consumer scales by rstd.
   m.gain = c->merge_norm;
   m.out = w.X;
   m.ld_out = 2 * d;
   { Prof pf(c, RLT_PROF_NORM, s); launch_merge_prep(c->dt, m, s); }
+  auto producer = [&](EpiArgs e, const float* gnext) {
+    e.gnext = gnext;
+    e.zb = w.h;
+    return e;
+  };
   if (cf.merge_kind == RLT_MERGE_GATED) {
     EpiArgs e = E0;
     e.kind = EPI_MGATE;
@@ -484,14 +499,15 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
     e.kind = EPI_MOUT;
     e.out_f = w.z;
     e.gbuf = w.gbuf;
-    gm.run((const char*)w.X + d * es, 2 * d, {c->merge_ws}, d, d, PAIR_PLAIN, n, e);
+    gm.run((const char*)w.X + d * es, 2 * d, {c->merge_ws}, d, d, PAIR_PLAIN, n, producer(e, c->norm_s[0]),
+           nullptr, w.ssq);
   } else {
     EpiArgs e = E0;
     e.kind = EPI_CONVEX;
     e.out_f = w.z;
     e.ldo = d;
     e.bias = c->merge_bg;
-    gm.run(w.X, 2 * d, {c->merge_wg}, d, 2 * d, PAIR_PLAIN, n, e);
+    gm.run(w.X, 2 * d, {c->merge_wg}, d, 2 * d, PAIR_PLAIN, n, producer(e, c->norm_s[0]), nullptr, w.ssq);
   }
 
   AttnArgs at{};
@@ -508,20 +524,15 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
   at.st = P.mem.stride_t;
 
   const size_t ring_layer = (size_t)P.st->B_cap * (cf.window - 1) * d * es;
-  m.z = w.z;
-  m.out = w.h;
-  m.ld_out = d;
   for (int l = 0; l < L; ++l) {
-    // ---- SWA sublayer [eqs. (2.12)-(2.14)] ----
-    m.gain = c->norm_s[l];
-    { Prof pf(c, RLT_PROF_NORM, s); launch_rmsnorm(c->dt, m, s); }
+    // ---- SWA sublayer [eqs. (2.12)-(2.14)]: RMSNorm_S folded into QKV ----
     {
       EpiArgs e = E0;
       e.kind = EPI_QKV;
       e.out_f = w.q;
       e.out_k = w.kc;
       e.out_v = w.vc;
-      gm.run(w.h, d, {c->wq[l], c->wk[l], c->wv[l]}, d, d, PAIR_ROPE, n, e);
+      gm.run(w.h, d, {c->wq[l], c->wk[l], c->wv[l]}, d, d, PAIR_ROPE, n, e, w.ssq);
     }
     at.q = w.q;
     at.kc = w.kc;
@@ -536,16 +547,14 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
       e.kind = EPI_RESID;
       e.out_f = w.z;
       e.ldo = d;
-      gm.run(w.o, d, {c->wo[l]}, d, d, PAIR_PLAIN, n, e);
+      gm.run(w.o, d, {c->wo[l]}, d, d, PAIR_PLAIN, n, producer(e, c->norm_m[l]), nullptr, w.ssq);
     }
-    // ---- cross-attention sublayer [eq. (2.15)] ----
-    m.gain = c->norm_m[l];
-    { Prof pf(c, RLT_PROF_NORM, s); launch_rmsnorm(c->dt, m, s); }
+    // ---- cross-attention sublayer [eq. (2.15)]: RMSNorm_M folded into the query ----
     {
       EpiArgs e = E0;
       e.kind = EPI_QROT;
       e.out_f = w.qm;
-      gm.run(w.h, d, {c->wqm[l]}, d, d, PAIR_ROPE, n, e);
+      gm.run(w.h, d, {c->wqm[l]}, d, d, PAIR_ROPE, n, e, w.ssq);
     }
     const int g = (l * cf.n_groups) / L;
     at.q = w.qm;
@@ -559,26 +568,25 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
       e.kind = EPI_RESID;
       e.out_f = w.z;
       e.ldo = d;
-      gm.run(w.o, d, {c->wom[l]}, d, d, PAIR_PLAIN, n, e);
+      gm.run(w.o, d, {c->wom[l]}, d, d, PAIR_PLAIN, n, producer(e, c->norm_d[l]), nullptr, w.ssq);
     }
-    // ---- FFN sublayer [eq. (2.16)] ----
-    m.gain = c->norm_d[l];
-    { Prof pf(c, RLT_PROF_NORM, s); launch_rmsnorm(c->dt, m, s); }
+    // ---- FFN sublayer [eq. (2.16)]: RMSNorm_D folded into gate/up ----
     {
       EpiArgs e = E0;
       e.kind = EPI_SWIGLU;
       e.out_k = w.act;
       e.ldo = F;
-      gm.run(w.h, d, {c->w_gate[l], c->w_up[l]}, F, d, PAIR_DUAL, n, e);
+      gm.run(w.h, d, {c->w_gate[l], c->w_up[l]}, F, d, PAIR_DUAL, n, e, w.ssq);
       e.kind = EPI_RESID;
       e.out_f = w.z;
       e.ldo = d;
-      gm.run(w.act, F, {c->w_down[l]}, d, F, PAIR_PLAIN, n, e);
+      const float* gnext = l + 1 < L ? c->norm_s[l + 1] : c->out_norm;  // next block, or RMSNorm_o
+      gm.run(w.act, F, {c->w_down[l]}, d, F, PAIR_PLAIN, n, producer(e, gnext), nullptr, w.ssq);
     }
     if (P.z_trace) launch_copy_f32(w.z, P.z_trace + (size_t)l * P.z_trace_ld * d, (int64_t)n * d, s);
   }
-  // ---- s_t write-back, RMSNorm_o [eq. (2.6)] ----
-  m.gain = c->out_norm;
+  // ---- s_t write-back [eq. (2.5)] ----
+  m.z = w.z;
   m.s_out = P.s_out;
   m.s_trace = P.s_trace;
   m.s_trace_sb = P.s_trace_sb;
@@ -589,7 +597,7 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
     e.kind = EPI_STORE;
     e.out_f = logits;
     e.ldo = cf.vocab;
-    gm.run(w.h, d, {c->w_out}, cf.vocab, d, PAIR_PLAIN, n, e);
+    gm.run(w.h, d, {c->w_out}, cf.vocab, d, PAIR_PLAIN, n, e, w.ssq);  // RMSNorm_o folded in [eq. (2.6)]
   }
   if (P.do_readout) {
     ReadoutArgs ro = P.ro;

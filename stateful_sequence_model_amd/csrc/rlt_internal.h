@@ -88,6 +88,67 @@ struct GemmArgs {
   int kslice;             // K elements per (split, wave) slice, multiple of 32
   float* partial;         // [S][M_pad][Nv] when S > 1
   int Nv;                 // nseg * seg_rows
+  // RMSNorm folded into the products (RMSNorm(z) W^T = rstd * ((z * gain) W^T)):
+  // a consumer reads per-row partial sums of squares of z and scales its
+  // accumulators by rstd = 1/sqrt(sum/d + eps) before the epilogue; a
+  // producer (residual / merge epilogue) writes those partial sums, one per
+  // (column unit, row), for the next consumer.
+  const float* ssq_in;    // [ssq_units][M_pad] or null
+  float* ssq_out;         // [units of this product][M_pad] or null
+  int ssq_units;
+  float inv_d, eps;
+};
+
+// 16-lane sum (lanes 16q .. 16q+15 of a wave), fixed butterfly order
+__device__ __forceinline__ float sum16(float v) {
+  v += __shfl_xor(v, 1);
+  v += __shfl_xor(v, 2);
+  v += __shfl_xor(v, 4);
+  v += __shfl_xor(v, 8);
+  return v;
+}
+
+// rstd of row m from the per-unit partial sums of squares (one thread)
+__device__ __forceinline__ float row_rstd(const GemmArgs& g, int m) {
+  float a = 0.f;
+#pragma unroll 8
+  for (int u = 0; u < g.ssq_units; ++u) a += g.ssq_in[(int64_t)u * g.M_pad + m];
+  return 1.0f / sqrtf(a * g.inv_d + g.eps);
+}
+
+// Per-row rstd for R rows starting at m0, computed by all 256 threads of a
+// workgroup: thread (part, row) loads units part, part + P, ... (P = 256/R)
+// into registers when constructed (before the main loop, so the loads are in
+// flight with it), and finish() sums them in a fixed order through LDS.
+// Units beyond P*RU (only for very wide d) are summed in finish() directly.
+template <int R>
+struct RowRstd {
+  static constexpr int P = 256 / R;
+  static constexpr int RU = 16;
+  float v[RU];
+  __device__ __forceinline__ RowRstd(const GemmArgs& g, int m0) {
+    const int row = threadIdx.x % R, part = threadIdx.x / R;
+#pragma unroll
+    for (int j = 0; j < RU; ++j) {
+      const int u = part + j * P;
+      v[j] = (g.ssq_in && u < g.ssq_units) ? g.ssq_in[(int64_t)u * g.M_pad + m0 + row] : 0.f;
+    }
+  }
+  // s_part: LDS [P][R]; s_rstd: LDS [R]; contains one __syncthreads
+  __device__ __forceinline__ void finish(const GemmArgs& g, int m0, float* s_part, float* s_rstd) {
+    const int row = threadIdx.x % R, part = threadIdx.x / R;
+    float a = 0.f;
+#pragma unroll
+    for (int j = 0; j < RU; ++j) a += v[j];
+    for (int u = part + RU * P; u < g.ssq_units; u += P) a += g.ssq_in[(int64_t)u * g.M_pad + m0 + row];
+    s_part[part * R + row] = a;
+    __syncthreads();
+    if (threadIdx.x < R) {
+      float s = 0.f;
+      for (int p = 0; p < P; ++p) s += s_part[p * R + threadIdx.x];
+      s_rstd[threadIdx.x] = 1.0f / sqrtf(s * g.inv_d + g.eps);
+    }
+  }
 };
 
 // 16-row blocks per matrix-product tile for an M-row call (tile <= 64 rows;
@@ -137,6 +198,10 @@ struct EpiArgs {
   float alpha;
   EIn e;                    // merge: e_t
   const float* s_state;     // convex merge: s_{t-1} rows
+  // producers (EPI_RESID, EPI_MOUT, EPI_CONVEX): gain of the next RMSNorm and
+  // the [M][d] (T) buffer receiving z * gain, the next product's input
+  const float* gnext;
+  void* zb;
 };
 
 // ----------------------------------------------------------------------------
