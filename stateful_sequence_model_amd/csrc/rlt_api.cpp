@@ -76,6 +76,7 @@ struct rlt_ctx {
   int hpw, hpw_x;      // heads per workgroup: SWA, cross-attention
   int gemm_mb_force;   // 0 or 1/2/4 (tuning)
   int gemm_s_force;    // 0 or forced K split (tuning)
+  int gemm_wide;       // wide-tile products for calls above 32 rows (1 = on)
   int split_min_rows;  // calls with at least this many rows run as two streams (0 = never)
   size_t partial_cap;  // floats per workspace
   // shared device buffers
@@ -301,6 +302,7 @@ extern "C" int rlt_create(const rlt_config* cfg, const rlt_weights* w, int32_t m
   c->hpw_x = choose_hpw(*cfg, c->dt, env_int("RLT_XATTN_HPW", 2));
   c->gemm_mb_force = env_int("RLT_GEMM_MB", 0);
   c->gemm_s_force = env_int("RLT_GEMM_S", 0);
+  c->gemm_wide = env_int("RLT_GEMM_WIDE", 1);
   c->split_min_rows = env_int("RLT_SPLIT_MIN_ROWS", 0);
   c->partial_cap = (size_t)8 * c->M_pad * std::max(3 * d, 2 * F);
   const size_t M = c->M_pad;
@@ -409,7 +411,22 @@ struct Gemm {
     g.ssq_units = c->cfg.d_model / (c->dt == 1 ? 32 : 2);  // column units of the producers
     g.inv_d = 1.0f / (float)c->cfg.d_model;
     g.eps = c->cfg.rms_eps;
-    if (c->dt == 1) {
+    if (c->dt == 1 && c->gemm_wide && n > 32 && g.npairs % 4 == 0 && K % 64 == 0) {
+      // wide tile: 4 pairs x (64 or 128) rows per workgroup, K split so that
+      // about one workgroup per compute unit is resident
+      const int MB = c->gemm_mb_force == 8 ? 8 : 4;
+      const int mt = (n + 16 * MB - 1) / (16 * MB);
+      const int tiles = g.npairs / 4 * mt;
+      const int kst = K / 64;
+      int S = std::max(1, (256 + tiles - 1) / tiles);
+      S = std::min(S, std::max(1, kst / 4));              // >= 4 stages per workgroup
+      if (c->gemm_s_force > 0) S = std::min(c->gemm_s_force, kst);
+      while (S > 1 && (size_t)S * c->M_pad * g.Nv > c->partial_cap) --S;
+      g.wide = 1;
+      g.mb = MB;
+      g.S = S;
+      g.kslice = (kst + S - 1) / S * 64;
+    } else if (c->dt == 1) {
       int MB = gemm_row_blocks(n);
       const int mbf = c->gemm_mb_force;
       if (mbf == 1 || mbf == 2 || mbf == 4) MB = mbf;

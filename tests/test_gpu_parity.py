@@ -53,8 +53,11 @@ def test_gemm_kernel_parity():
     wl = synth.SMALL
     run = GpuRun(wl, B=1, T=4, max_rows=200)
     rng = np.random.default_rng(0)
+    # above 32 rows with 4 | N/32 and 64 | K the wide-tile kernel runs: its K
+    # loop has a 4-stage body and a tail of 0-3 stages of 64 (K = 192, 448
+    # and 704 give tails of 3, 3 and 2/1 stages, the last with a K split)
     for M, N, K in [(1, 256, 512), (5, 64, 256), (16, 768, 256), (33, 96, 512), (70, 256, 384), (128, 512, 512),
-                    (200, 128, 256)]:
+                    (200, 128, 256), (70, 256, 192), (128, 512, 448), (96, 1024, 704)]:
         Abits = synth.normal(7, "dbgA%d" % M, (M, K), dtype="bf16")
         Wbits = synth.normal(7, "dbgW%d" % M, (N, K), sigma=0.05, dtype="bf16")
         Ad, Wd = to_device(Abits, "bf16"), to_device(Wbits, "bf16")
