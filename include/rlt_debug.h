@@ -32,7 +32,9 @@ enum {
   RLT_PROF_GEMM = 3,      /* every matrix product incl. its split reduction */
   RLT_PROF_NORM = 4,      /* RMSNorms, merge preparation, state write-back */
   RLT_PROF_READOUT = 5,   /* log-sum-exp / argmax / sampling */
-  RLT_PROF_NCLASS = 6
+  RLT_PROF_FUSED = 6,     /* persistent step kernel (small calls: every class above
+                             except the readout, in one launch) */
+  RLT_PROF_NCLASS = 7
 };
 
 /* Timing hook for benchmarks: while enabled, every launch of a kernel class

@@ -88,8 +88,8 @@ _SIGS = {
     "rlt_dbg_profile_read": (C.c_int, [P, i32, C.POINTER(C.c_double), C.POINTER(C.c_int64)]),
 }
 
-RLT_PROF_XATTN, RLT_PROF_XCOMBINE, RLT_PROF_SWA, RLT_PROF_GEMM, RLT_PROF_NORM, RLT_PROF_READOUT = range(6)
-PROF_NAMES = ["xattn", "xcombine", "swa", "gemm", "norm", "readout"]
+RLT_PROF_XATTN, RLT_PROF_XCOMBINE, RLT_PROF_SWA, RLT_PROF_GEMM, RLT_PROF_NORM, RLT_PROF_READOUT, RLT_PROF_FUSED = range(7)
+PROF_NAMES = ["xattn", "xcombine", "swa", "gemm", "norm", "readout", "fused"]
 
 
 def lib():

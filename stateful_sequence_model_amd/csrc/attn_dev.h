@@ -1,0 +1,332 @@
+// Device-side bodies of the attention kernels; included by the stand-alone
+// attention kernels and by the persistent step kernel.
+#pragma once
+#include "rlt_internal.h"
+
+namespace rlt {
+
+// 32 bytes of one head's keys or values held by one lane, unconverted
+struct Raw {
+  uint4 a, b;
+};
+
+template <typename T> struct LaneVec;
+template <> struct LaneVec<uint16_t> {
+  static constexpr int E = 16;
+  __device__ static __forceinline__ Raw load(const uint16_t* p) {
+    return Raw{*(const uint4*)p, *(const uint4*)(p + 8)};
+  }
+  __device__ static __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
+  __device__ static __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+  __device__ static __forceinline__ float dot(const float* q, const Raw& r) {
+    const uint32_t w[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      s = fmaf(q[2 * i], lo(w[i]), s);
+      s = fmaf(q[2 * i + 1], hi(w[i]), s);
+    }
+    return s;
+  }
+  __device__ static __forceinline__ void axpy(float* o, float p, const Raw& r) {
+    const uint32_t w[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      o[2 * i] = fmaf(p, lo(w[i]), o[2 * i]);
+      o[2 * i + 1] = fmaf(p, hi(w[i]), o[2 * i + 1]);
+    }
+  }
+  __device__ static __forceinline__ void store(uint16_t* p, const float* f) {
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = (uint32_t)f2bf(f[2 * i]) | ((uint32_t)f2bf(f[2 * i + 1]) << 16);
+    *(uint4*)p = make_uint4(w[0], w[1], w[2], w[3]);
+    *(uint4*)(p + 8) = make_uint4(w[4], w[5], w[6], w[7]);
+  }
+  __device__ static __forceinline__ void copy(uint16_t* d, const uint16_t* s) {
+    *(uint4*)d = *(const uint4*)s;
+    *(uint4*)(d + 8) = *(const uint4*)(s + 8);
+  }
+};
+template <> struct LaneVec<float> {
+  static constexpr int E = 8;
+  __device__ static __forceinline__ Raw load(const float* p) {
+    return Raw{*(const uint4*)p, *(const uint4*)(p + 4)};
+  }
+  __device__ static __forceinline__ float dot(const float* q, const Raw& r) {
+    const uint32_t w[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s = fmaf(q[i], __uint_as_float(w[i]), s);
+    return s;
+  }
+  __device__ static __forceinline__ void axpy(float* o, float p, const Raw& r) {
+    const uint32_t w[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = fmaf(p, __uint_as_float(w[i]), o[i]);
+  }
+  __device__ static __forceinline__ void store(float* p, const float* f) {
+    *(float4*)p = make_float4(f[0], f[1], f[2], f[3]);
+    *(float4*)(p + 4) = make_float4(f[4], f[5], f[6], f[7]);
+  }
+  __device__ static __forceinline__ void copy(float* d, const float* s) {
+    *(float4*)d = *(const float4*)s;
+    *(float4*)(d + 4) = *(const float4*)(s + 4);
+  }
+};
+
+template <int LPK>
+__device__ __forceinline__ float group_sum(float s) {
+#pragma unroll
+  for (int off = 1; off < LPK; off <<= 1) s += __shfl_xor(s, off);
+  return s;
+}
+
+// online-softmax accumulator of one lane (E output elements)
+template <typename T>
+struct Acc {
+  static constexpr int E = LaneVec<T>::E;
+  float m, l, o[E];
+  __device__ __forceinline__ void init() {
+    m = -INFINITY;
+    l = 0.f;
+#pragma unroll
+    for (int i = 0; i < E; ++i) o[i] = 0.f;
+  }
+  // fold N keys (scores s[], values v[]) with one max update
+  template <int N>
+  __device__ __forceinline__ void fold(const float* s, const Raw* v) {
+    float mx = m;
+#pragma unroll
+    for (int u = 0; u < N; ++u) mx = fmaxf(mx, s[u]);
+    const float c = exp2f(m - mx);
+    l *= c;
+#pragma unroll
+    for (int i = 0; i < E; ++i) o[i] *= c;
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+      const float p = exp2f(s[u] - mx);
+      l += p;
+      LaneVec<T>::axpy(o, p, v[u]);
+    }
+    m = mx;
+  }
+};
+
+// Walk keys r = r0, r0 + step, ... < r1 (addressed by kv(r) -> (k, v)
+// pointers), U at a time.
+template <typename T, int LPK, int U, class KV>
+__device__ __forceinline__ void walk(Acc<T>& acc, const float* q, int r0, int r1, int step, const KV& kv) {
+  using LV = LaneVec<T>;
+  int r = r0;
+  for (; r + (U - 1) * step < r1; r += U * step) {
+    Raw kr[U], vr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const T *kp, *vp;
+      kv(r + u * step, kp, vp);
+      kr[u] = LV::load(kp);
+      vr[u] = LV::load(vp);
+    }
+    float s[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) s[u] = group_sum<LPK>(LV::dot(q, kr[u]));
+    acc.template fold<U>(s, vr);
+  }
+  for (; r < r1; r += step) {
+    const T *kp, *vp;
+    kv(r, kp, vp);
+    Raw kr[1] = {LV::load(kp)}, vr[1] = {LV::load(vp)};
+    float s[1] = {group_sum<LPK>(LV::dot(q, kr[0]))};
+    acc.template fold<1>(s, vr);
+  }
+}
+
+// Merge the key groups' partials of the workgroup (fixed group order).
+// Returns true on the lanes of key group 0, which then hold the merged
+// (m, l, o) of their (head, element range).
+template <typename T>
+__device__ __forceinline__ bool merge_groups(Acc<T>& acc, int kg, int G, int KPW, float* s_o, float* s_ml) {
+  constexpr int E = Acc<T>::E;
+  const int li = threadIdx.x - kg * G;  // lane index within the key group
+#pragma unroll
+  for (int i = 0; i < E; ++i) s_o[threadIdx.x * E + i] = acc.o[i];
+  s_ml[2 * threadIdx.x] = acc.m;
+  s_ml[2 * threadIdx.x + 1] = acc.l;
+  __syncthreads();
+  if (kg != 0) return false;
+  float M = -INFINITY;
+  for (int g = 0; g < KPW; ++g) M = fmaxf(M, s_ml[2 * (g * G + li)]);
+  float L = 0.f, o[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) o[i] = 0.f;
+  for (int g = 0; g < KPW; ++g) {
+    const int th = g * G + li;
+    const float w = exp2f(s_ml[2 * th] - M);
+    L += s_ml[2 * th + 1] * w;
+#pragma unroll
+    for (int i = 0; i < E; ++i) o[i] = fmaf(s_o[th * E + i], w, o[i]);
+  }
+  acc.m = M;
+  acc.l = L;
+#pragma unroll
+  for (int i = 0; i < E; ++i) acc.o[i] = o[i];
+  return true;
+}
+
+template <typename T>
+struct RingKV {
+  const T *rk, *rv, *ck, *cv;
+  int t, nh, W1;
+  int64_t d;
+  __device__ __forceinline__ void operator()(int r, const T*& kp, const T*& vp) const {
+    if (r < nh) {
+      const int sl = (t - nh + r - 1) % W1;  // slot of absolute position t - nh + r
+      kp = rk + sl * d;
+      vp = rv + sl * d;
+    } else {
+      kp = ck;
+      vp = cv;
+    }
+  }
+};
+
+template <typename T>
+struct MemKV {
+  const T *mk, *mv;
+  int64_t st;
+  __device__ __forceinline__ void operator()(int r, const T*& kp, const T*& vp) const {
+    kp = mk + r * st;
+    vp = mv + r * st;
+  }
+};
+
+constexpr int UNROLL = 4;
+
+// LDS floats used by the attention bodies
+template <typename T>
+constexpr int attn_lds_floats() { return 256 * LaneVec<T>::E + 512; }
+
+// SWA for (head group hg, slot); block 256
+template <typename T, int DH>
+__device__ __forceinline__ void swa_body(const AttnArgs& a, int hg, int slot, float* lds) {
+  using LV = LaneVec<T>;
+  constexpr int E = LV::E;
+  constexpr int LPK = DH / E;
+  float* s_o = lds;
+  float* s_ml = lds + 256 * E;
+  const int t = a.rows.t_row[slot];
+  if (t <= 0) return;
+  const int row = a.rows.rows[slot];
+  const int G = a.hpw * LPK;
+  const int KPW = 256 / G;
+  const int kg = threadIdx.x / G;
+  const int hh = (threadIdx.x % G) / LPK;
+  const int jl = threadIdx.x % LPK;
+  const int col = (hg * a.hpw + hh) * DH + jl * E;
+  const int d = a.d;
+
+  float q[E];
+  {
+    const float* qp = a.q + (int64_t)slot * d + col;
+#pragma unroll
+    for (int i = 0; i < E; ++i) q[i] = qp[i] * a.qscale;
+  }
+  const int W1 = a.W - 1;
+  const int nh = min(t - 1, W1);
+  RingKV<T> kv;
+  kv.rk = (const T*)a.ring_k + (int64_t)row * W1 * d + col;
+  kv.rv = (const T*)a.ring_v + (int64_t)row * W1 * d + col;
+  kv.ck = (const T*)a.kc + (int64_t)slot * d + col;
+  kv.cv = (const T*)a.vc + (int64_t)slot * d + col;
+  kv.t = t;
+  kv.nh = nh;
+  kv.W1 = W1;
+  kv.d = d;
+
+  Acc<T> acc;
+  acc.init();
+  walk<T, LPK, UNROLL>(acc, q, kg, nh + 1, KPW, kv);
+  const bool lead = merge_groups<T>(acc, kg, G, KPW, s_o, s_ml);
+  if (lead) {
+    const float inv = 1.f / acc.l;
+    float o[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) o[i] = acc.o[i] * inv;
+    LV::store((T*)a.out + (int64_t)slot * d + col, o);
+  }
+  // cache insert after every read of this workgroup
+  __syncthreads();
+  if (W1 > 0 && kg == 0) {
+    const int sl = (t - 1) % W1;
+    LV::copy((T*)a.ring_k + ((int64_t)row * W1 + sl) * d + col, kv.ck);
+    LV::copy((T*)a.ring_v + ((int64_t)row * W1 + sl) * d + col, kv.cv);
+  }
+}
+
+// cross-attention partial of (head group hg, chunk ch, slot); block 256
+template <typename T, int DH>
+__device__ __forceinline__ void xattn_body(const AttnArgs& a, int hg, int ch, int slot, float* lds) {
+  using LV = LaneVec<T>;
+  constexpr int E = LV::E;
+  constexpr int LPK = DH / E;
+  float* s_o = lds;
+  float* s_ml = lds + 256 * E;
+  const int t = a.rows.t_row[slot];
+  const int j0 = ch * a.chunk;
+  if (t <= 0 || j0 >= t) return;
+  const int j1 = min(j0 + a.chunk, t);
+  const int row = a.rows.rows[slot];
+  const int G = a.hpw * LPK;
+  const int KPW = 256 / G;
+  const int kg = threadIdx.x / G;
+  const int hh = (threadIdx.x % G) / LPK;
+  const int jl = threadIdx.x % LPK;
+  const int head = hg * a.hpw + hh;
+  const int col = head * DH + jl * E;
+  const int d = a.d;
+
+  float q[E];
+  {
+    const float* qp = a.q + (int64_t)slot * d + col;
+#pragma unroll
+    for (int i = 0; i < E; ++i) q[i] = qp[i] * a.qscale;
+  }
+  MemKV<T> kv{(const T*)a.mk + (int64_t)row * a.sb + col, (const T*)a.mv + (int64_t)row * a.sb + col, a.st};
+  Acc<T> acc;
+  acc.init();
+  walk<T, LPK, UNROLL>(acc, q, j0 + kg, j1, KPW, kv);
+  const bool lead = merge_groups<T>(acc, kg, G, KPW, s_o, s_ml);
+  if (lead) {
+    float* P = a.part + (((int64_t)slot * a.nch + ch) * a.H + head) * (DH + 2);
+#pragma unroll
+    for (int i = 0; i < E; ++i) P[jl * E + i] = acc.o[i];
+    if (jl == 0) {
+      P[DH] = acc.m;
+      P[DH + 1] = acc.l;
+    }
+  }
+}
+
+// chunk combine of (head, slot) by `nt` threads with index `tid`
+template <typename T, int DH>
+__device__ __forceinline__ void xcombine_body(const AttnArgs& a, int head, int slot, int tid, int nt) {
+  const int t = a.rows.t_row[slot];
+  if (t <= 0) return;
+  const int nc = (t + a.chunk - 1) / a.chunk;
+  const float* P = a.part + ((int64_t)slot * a.nch * a.H + head) * (DH + 2);
+  const int64_t cs = (int64_t)a.H * (DH + 2);  // chunk stride
+  float M = -INFINITY;
+  for (int c = 0; c < nc; ++c) M = fmaxf(M, P[c * cs + DH]);
+  float L = 0.f;
+  for (int c = 0; c < nc; ++c) L += P[c * cs + DH + 1] * exp2f(P[c * cs + DH] - M);
+  const float inv = 1.f / L;
+  T* out = (T*)a.out + (int64_t)slot * a.d + head * DH;
+  for (int e = tid; e < DH; e += nt) {
+    float o = 0.f;
+    for (int c = 0; c < nc; ++c) o = fmaf(P[c * cs + e], exp2f(P[c * cs + DH] - M), o);
+    out[e] = from_f<T>(o * inv);
+  }
+}
+
+}  // namespace rlt

@@ -1,0 +1,286 @@
+// Device-side building blocks of the matrix products (epilogue functor and
+// the per-tile bodies); included by the stand-alone product kernels and by
+// the persistent step kernel.
+#pragma once
+#include "rlt_internal.h"
+
+namespace rlt {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+template <typename T>
+struct Epi {
+  EpiArgs a;
+
+  __device__ __forceinline__ float e_at(int m, int c) const {
+    const int t = a.rows.t_row[m];
+    if (t <= 0) return 0.f;
+    const T* p = (const T*)a.e.p + (int64_t)a.rows.src[m] * a.e.sb + (int64_t)(t - 1) * a.e.st;
+    return to_f<T>(p[c]);
+  }
+
+  // rotary transform of the pair (x_i, x_{i+dh/2}) of one head at position t
+  __device__ __forceinline__ void rotate(int m, int c_in_head, float& x, float& y) const {
+    const int t = a.rows.t_row[m];
+    double sn, cs;
+    sincos((double)t * a.inv_freq[c_in_head], &sn, &cs);
+    const float c = (float)cs, s = (float)sn;
+    const float xr = x * c - y * s;
+    const float yr = y * c + x * s;
+    x = xr;
+    y = yr;
+  }
+
+  // next RMSNorm's input: zb = z * gain (the rstd is applied by the consumer)
+  __device__ __forceinline__ float produce(int m, int ca, float za, int cb, float zb) const {
+    T* o = (T*)a.zb + (int64_t)m * a.d;
+    o[ca] = from_f<T>(za * a.gnext[ca]);
+    o[cb] = from_f<T>(zb * a.gnext[cb]);
+    return za * za + zb * zb;
+  }
+
+  // Epilogue of one column pair of row m. rs scales the accumulators of
+  // products whose input is z * gain of an RMSNorm (1 otherwise). Returns
+  // the squared sum of the produced residual values (0 for non-producers).
+  __device__ __forceinline__ float operator()(int m, int ca, float va, int cb, float vb, float rs) const {
+    switch (a.kind) {
+      case EPI_STORE:
+        a.out_f[(int64_t)m * a.ldo + ca] = va * rs;
+        a.out_f[(int64_t)m * a.ldo + cb] = vb * rs;
+        return 0.f;
+      case EPI_QKV: {
+        va *= rs;
+        vb *= rs;
+        const int seg = ca / a.d;
+        const int xa = ca - seg * a.d, xb = cb - seg * a.d;
+        if (seg < 2 && a.rope) rotate(m, xa % a.dh, va, vb);
+        const int64_t o = (int64_t)m * a.d;
+        if (seg == 0) {
+          a.out_f[o + xa] = va;
+          a.out_f[o + xb] = vb;
+        } else {
+          T* dst = (T*)(seg == 1 ? a.out_k : a.out_v);
+          dst[o + xa] = from_f<T>(va);
+          dst[o + xb] = from_f<T>(vb);
+        }
+        return 0.f;
+      }
+      case EPI_QROT: {
+        va *= rs;
+        vb *= rs;
+        if (a.rope) rotate(m, ca % a.dh, va, vb);
+        a.out_f[(int64_t)m * a.d + ca] = va;
+        a.out_f[(int64_t)m * a.d + cb] = vb;
+        return 0.f;
+      }
+      case EPI_RESID: {
+        float* z = a.out_f + (int64_t)m * a.ldo;
+        const float za = z[ca] + va, zb = z[cb] + vb;
+        z[ca] = za;
+        z[cb] = zb;
+        return produce(m, ca, za, cb, zb);
+      }
+      case EPI_SWIGLU: {
+        va *= rs;
+        vb *= rs;
+        const float act = va * sigmoidf_(va) * vb;
+        ((T*)a.out_k)[(int64_t)m * a.ldo + ca] = from_f<T>(act);
+        return 0.f;
+      }
+      case EPI_MGATE: {
+        float* g = a.out_f + (int64_t)m * a.ldo;
+        g[ca] = sigmoidf_(va + a.bias[ca]);
+        g[cb] = sigmoidf_(vb + a.bias[cb]);
+        return 0.f;
+      }
+      case EPI_MOUT: {
+        float* z = a.out_f + (int64_t)m * a.ldo;
+        const float* g = a.gbuf + (int64_t)m * a.ldo;
+        const float za = e_at(m, ca) + a.alpha * g[ca] * va;
+        const float zb = e_at(m, cb) + a.alpha * g[cb] * vb;
+        z[ca] = za;
+        z[cb] = zb;
+        return produce(m, ca, za, cb, zb);
+      }
+      case EPI_CONVEX: {
+        float za = 0.f, zb = 0.f;
+        if (a.rows.t_row[m] > 0) {
+          const float* s = a.s_state + (int64_t)a.rows.rows[m] * a.d;
+          const float ga = sigmoidf_(va + a.bias[ca]);
+          const float gb = sigmoidf_(vb + a.bias[cb]);
+          za = ga * e_at(m, ca) + (1.f - ga) * s[ca];
+          zb = gb * e_at(m, cb) + (1.f - gb) * s[cb];
+        }
+        float* z = a.out_f + (int64_t)m * a.ldo;
+        z[ca] = za;
+        z[cb] = zb;
+        return produce(m, ca, za, cb, zb);
+      }
+      default:
+        return 0.f;
+    }
+  }
+};
+
+template <typename T>
+__device__ __forceinline__ const T* weight_row(const GemmArgs& g, int vc) {
+  const int seg = vc / g.seg_rows;
+  const int r = vc - seg * g.seg_rows;
+  return (const T*)g.W[seg] + (int64_t)r * g.K;
+}
+
+__device__ __forceinline__ bf16x8_t load8(const uint16_t* p) {
+  const uint4 u = *(const uint4*)p;
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
+// LDS floats used by gemm_bf16_body<MB>
+constexpr int gemm_lds_floats(int MB) { return 4 * MB * 16 * 32 + MB * 16 + 256; }
+
+// One (pair, split, m-tile) tile of the product; block 256 (4 waves).
+template <int MB>
+__device__ __forceinline__ void gemm_bf16_body(const GemmArgs& g, const Epi<uint16_t>& epi, int pair, int split,
+                                               int mt, float* lds) {
+  float(*red)[MB * 16][32] = reinterpret_cast<float(*)[MB * 16][32]>(lds);
+  float* s_rstd = lds + 4 * MB * 16 * 32;
+  float* s_part = s_rstd + MB * 16;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int ba, bb;
+  pair_blocks(g, pair, ba, bb);
+  const int r16 = lane & 15;
+  const int kq = (lane >> 4) * 8;
+  const uint16_t* wa = weight_row<uint16_t>(g, ba * 16 + r16) + kq;
+  const uint16_t* wb = weight_row<uint16_t>(g, bb * 16 + r16) + kq;
+  const int m0 = mt * MB * 16;
+  const uint16_t* ap[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+    ap[mb] = (const uint16_t*)g.A + (int64_t)(m0 + mb * 16 + r16) * g.lda + kq;
+
+  // folded RMSNorm: this tile's row sums of squares, loads in flight with the K loop
+  const bool norm_here = g.S == 1 && g.ssq_in != nullptr;
+  RowRstd<MB * 16> rr(g, norm_here ? m0 : 0);
+  f32x4_t acc[MB][2];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    acc[mb][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    acc[mb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  // The workgroup's K range [kw0, kw1) is cut in 32-wide steps dealt to the
+  // four waves round-robin (wave w takes steps w, w+4, ...): at any moment
+  // the waves read adjacent 64-byte pieces of each weight row, so rows are
+  // streamed in long contiguous runs.
+  const int kw0 = split * 4 * g.kslice;
+  const int kw1 = min(kw0 + 4 * g.kslice, g.K);
+  const int all_steps = max(0, (kw1 - kw0) / 32);
+  const int k0 = kw0 + 32 * wave;  // step j of this wave is at k0 + 128 j
+  // PF K-steps of loads in flight: step i is multiplied while steps
+  // i+1 .. i+PF-1 are still arriving (a register ring, statically indexed).
+  // The steady-state loop is branch-free so that each step waits only for
+  // its own loads: the refill of step i+PF is always issued, its address
+  // clamped to the last step (a harmless re-read) near the end.
+  constexpr int PF = MB >= 4 ? 4 : 6;
+  const int nsteps = (all_steps - wave + 3) / 4;
+  bf16x8_t bufa[PF][MB], bufb[PF][2];
+  if (nsteps > 0) {
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      const int k = k0 + 128 * min(p, nsteps - 1);
+      bufb[p][0] = load8(wa + k);
+      bufb[p][1] = load8(wb + k);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) bufa[p][mb] = load8(ap[mb] + k);
+    }
+  }
+  int i = 0;
+  for (; i + PF <= nsteps; i += PF) {
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        acc[mb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bufa[p][mb], bufb[p][0], acc[mb][0], 0, 0, 0);
+        acc[mb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bufa[p][mb], bufb[p][1], acc[mb][1], 0, 0, 0);
+      }
+      const int kn = k0 + 128 * min(i + p + PF, nsteps - 1);
+      bufb[p][0] = load8(wa + kn);
+      bufb[p][1] = load8(wb + kn);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) bufa[p][mb] = load8(ap[mb] + kn);
+    }
+  }
+  // tail: the remaining nsteps - i (< PF) steps are already in the ring
+#pragma unroll
+  for (int p = 0; p < PF; ++p) {
+    if (i + p < nsteps) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        acc[mb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bufa[p][mb], bufb[p][0], acc[mb][0], 0, 0, 0);
+        acc[mb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bufa[p][mb], bufb[p][1], acc[mb][1], 0, 0, 0);
+      }
+    }
+  }
+  // C layout: lane holds rows 4*(lane/16)+i, column lane%16
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      red[wave][mb * 16 + (lane >> 4) * 4 + i][r16] = acc[mb][0][i];
+      red[wave][mb * 16 + (lane >> 4) * 4 + i][16 + r16] = acc[mb][1][i];
+    }
+  if (norm_here) rr.finish(g, m0, s_part, s_rstd);  // uniform branch: contains a barrier
+  __syncthreads();
+  // every lane runs the same trip count (the 16 lanes of a row reduce together)
+  for (int idx = threadIdx.x; idx < MB * 16 * 16; idx += 256) {
+    const int m = idx >> 4, r = idx & 15;
+    const int slot = m0 + m;
+    const float va = ((red[0][m][r] + red[1][m][r]) + red[2][m][r]) + red[3][m][r];
+    const float vb = ((red[0][m][16 + r] + red[1][m][16 + r]) + red[2][m][16 + r]) + red[3][m][16 + r];
+    if (g.S == 1) {
+      float sq = 0.f;
+      if (slot < g.M) sq = epi(slot, ba * 16 + r, va, bb * 16 + r, vb, g.ssq_in ? s_rstd[m] : 1.f);
+      if (g.ssq_out) {
+        sq = sum16(sq);
+        if (r == 0 && slot < g.M) g.ssq_out[(int64_t)pair * g.M_pad + slot] = sq;
+      }
+    } else if (slot < g.M) {
+      float* P = g.partial + ((int64_t)split * g.M_pad + slot) * g.Nv;
+      P[ba * 16 + r] = va;
+      P[bb * 16 + r] = vb;
+    }
+  }
+}
+
+constexpr int SPLITK_LDS_FLOATS = 16 + 256;
+
+// Sum of the S split partials of (pair, 16-row block mt) in split order, then
+// the epilogue; block 256.
+template <typename T>
+__device__ __forceinline__ void splitk_epi_body(const GemmArgs& g, const Epi<T>& epi, int pair, int mt, float* lds) {
+  float* s_rstd = lds;
+  float* s_part = lds + 16;
+  int ba, bb;
+  pair_blocks(g, pair, ba, bb);
+  const int m = mt * 16 + (threadIdx.x >> 4), r = threadIdx.x & 15;
+  if (g.ssq_in) {
+    RowRstd<16> rr(g, mt * 16);
+    rr.finish(g, mt * 16, s_part, s_rstd);
+  }
+  __syncthreads();
+  float sq = 0.f;
+  if (m < g.M) {
+    float va = 0.f, vb = 0.f;
+    for (int s = 0; s < g.S; ++s) {
+      const float* P = g.partial + ((int64_t)s * g.M_pad + m) * g.Nv;
+      va += P[ba * 16 + r];
+      vb += P[bb * 16 + r];
+    }
+    sq = epi(m, ba * 16 + r, va, bb * 16 + r, vb, g.ssq_in ? s_rstd[threadIdx.x >> 4] : 1.f);
+  }
+  if (g.ssq_out) {
+    sq = sum16(sq);
+    if (r == 0 && m < g.M) g.ssq_out[(int64_t)pair * g.M_pad + m] = sq;
+  }
+}
+
+}  // namespace rlt

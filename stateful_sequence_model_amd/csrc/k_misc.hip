@@ -1,7 +1,7 @@
 // Row bookkeeping, normalisation, merge preparation, state write-back and
 // readout ("Recurrent Looped Transformer", §2.3 eqs. (2.3)-(2.6), §2.5
 // eqs. (2.9)-(2.11), §5.3, App. A.2).
-#include "rlt_internal.h"
+#include "misc_dev.h"
 
 namespace rlt {
 
@@ -107,47 +107,15 @@ __global__ __launch_bounds__(256) void k_rmsnorm(MiscArgs a) {
   for (int c = threadIdx.x; c < a.d; c += 256) out[c] = from_f<T>(z[c] * r * a.gain[c]);
 }
 
-// gated: X = [e ; RMSNorm_s(s_{t-1})]  (eq. 2.10 input); convex: X = [e ; s]
 template <typename T>
 __global__ __launch_bounds__(256) void k_merge_prep(MiscArgs a) {
   __shared__ float scratch[16];
-  const int slot = blockIdx.x;
-  const int t = a.rows.t_row[slot];
-  T* X = (T*)a.out + (int64_t)slot * a.ld_out;
-  if (t <= 0) {
-    for (int c = threadIdx.x; c < 2 * a.d; c += 256) X[c] = from_f<T>(0.f);
-    return;
-  }
-  const float* s = a.s_state + (int64_t)a.rows.rows[slot] * a.d;
-  const T* e = (const T*)a.e.p + (int64_t)a.rows.src[slot] * a.e.sb + (int64_t)(t - 1) * a.e.st;
-  for (int c = threadIdx.x; c < a.d; c += 256) X[c] = e[c];
-  if (a.merge_kind == 0) {
-    float ss = 0.f;
-    for (int c = threadIdx.x; c < a.d; c += 256) ss = fmaf(s[c], s[c], ss);
-    ss = block_sum(ss, scratch);
-    const float r = 1.0f / sqrtf(ss / (float)a.d + a.eps);
-    for (int c = threadIdx.x; c < a.d; c += 256) X[a.d + c] = from_f<T>(s[c] * r * a.gain[c]);
-  } else {
-    for (int c = threadIdx.x; c < a.d; c += 256) X[a.d + c] = from_f<T>(s[c]);
-  }
+  merge_prep_body<T>(a, blockIdx.x, scratch);
 }
 
-// s_t write-back to the state and the optional outputs (the readout's
-// RMSNorm_o input was produced by the last block's down projection)
 template <typename T>
 __global__ __launch_bounds__(256) void k_final(MiscArgs a) {
-  const int slot = blockIdx.x;
-  const int t = a.rows.t_row[slot];
-  const float* z = a.z + (int64_t)slot * a.d;
-  if (t <= 0) return;
-  float* s = a.s_state + (int64_t)a.rows.rows[slot] * a.d;
-  for (int c = threadIdx.x; c < a.d; c += 256) s[c] = z[c];
-  if (a.s_out)
-    for (int c = threadIdx.x; c < a.d; c += 256) a.s_out[(int64_t)slot * a.d + c] = z[c];
-  if (a.s_trace) {
-    float* st = a.s_trace + (int64_t)a.rows.src[slot] * a.s_trace_sb + (int64_t)(t - 1) * a.d;
-    for (int c = threadIdx.x; c < a.d; c += 256) st[c] = z[c];
-  }
+  final_body<T>(a, blockIdx.x);
 }
 
 __global__ void k_copy_f32(const float* src, float* dst, int64_t n) {
@@ -411,6 +379,14 @@ void launch_set_pending(const int* rows, const int* src, int n, const int* token
                      tok_sb, last_index, pending);
 }
 void launch_merge_prep(int dtype, const MiscArgs& a, hipStream_t s) {
+  if (dtype == 1) {
+    Phase p{};
+    p.kind = PH_MERGE_PREP;
+    p.gx = a.n;
+    p.gy = p.gz = 1;
+    p.u.mi = a;
+    if (record_phase(p)) return;
+  }
   if (dtype == 0) hipLaunchKernelGGL(k_merge_prep<float>, dim3(a.n), dim3(256), 0, s, a);
   else hipLaunchKernelGGL(k_merge_prep<uint16_t>, dim3(a.n), dim3(256), 0, s, a);
 }
@@ -419,10 +395,26 @@ void launch_rmsnorm(int dtype, const MiscArgs& a, hipStream_t s) {
   else hipLaunchKernelGGL(k_rmsnorm<uint16_t>, dim3(a.n), dim3(256), 0, s, a);
 }
 void launch_final(int dtype, const MiscArgs& a, hipStream_t s) {
+  if (dtype == 1) {
+    Phase p{};
+    p.kind = PH_FINAL;
+    p.gx = a.n;
+    p.gy = p.gz = 1;
+    p.u.mi = a;
+    if (record_phase(p)) return;
+  }
   if (dtype == 0) hipLaunchKernelGGL(k_final<float>, dim3(a.n), dim3(256), 0, s, a);
   else hipLaunchKernelGGL(k_final<uint16_t>, dim3(a.n), dim3(256), 0, s, a);
 }
 void launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s) {
+  {
+    Phase p{};
+    p.kind = PH_COPY;
+    p.gx = (int)((n + 255) / 256);
+    p.gy = p.gz = 1;
+    p.u.cp = CopyArgs{src, dst, n};
+    if (record_phase(p)) return;
+  }
   hipLaunchKernelGGL(k_copy_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src, dst, n);
 }
 void launch_readout(const ReadoutArgs& a, hipStream_t s) {

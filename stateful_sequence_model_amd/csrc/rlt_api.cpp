@@ -78,7 +78,19 @@ struct rlt_ctx {
   int gemm_s_force;    // 0 or forced K split (tuning)
   int gemm_wide;       // wide-tile products for calls above 32 rows (1 = on)
   int split_min_rows;  // calls with at least this many rows run as two streams (0 = never)
+  int gemm_target;     // workgroups a matrix product aims to fill (K split heuristic)
   size_t partial_cap;  // floats per workspace
+  // persistent step for calls of at most fused_rows rows (bf16; 0 = off)
+  int fused_rows;
+  int fused_grid;      // workgroups = compute units
+  int fused_target;    // workgroups a product aims to fill inside the persistent step
+  int64_t fused_spin;  // barrier wait limit in s_memrealtime ticks
+  unsigned* fused_sync;
+  struct FusedEntry {
+    std::vector<Phase> host;
+    Phase* dev;
+  };
+  std::vector<FusedEntry> fused_cache;
   // shared device buffers
   int *t_row, *ident, *ones, *rows_buf, *src_buf, *split_buf, *last_buf;
   double* inv_freq;
@@ -102,9 +114,19 @@ struct rlt_ctx {
 };
 
 namespace {
+thread_local std::vector<Phase>* t_rec = nullptr;
+}  // namespace
+
+bool rlt::record_phase(const Phase& p) {
+  if (!t_rec) return false;
+  t_rec->push_back(p);
+  return true;
+}
+
+namespace {
 
 // Brackets the launches of one kernel class with two events when timing
-// is on (never inside a graph capture).
+// is on (never inside a graph capture, never while recording phases).
 struct Prof {
   rlt_ctx* c;
   int kind;
@@ -119,7 +141,7 @@ struct Prof {
     }
     return c->prof_next++;
   }
-  Prof(rlt_ctx* c_, int k, hipStream_t s_) : c(c_), kind(k), s(s_), on(c_->prof_on) {
+  Prof(rlt_ctx* c_, int k, hipStream_t s_) : c(c_), kind(k), s(s_), on(c_->prof_on && !t_rec) {
     if (on) {
       i0 = take();
       if (i0 == (size_t)-1) on = false;
@@ -213,6 +235,8 @@ extern "C" void rlt_destroy(rlt_ctx* c) {
   }
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
+  if (c->fused_sync) (void)hipFree(c->fused_sync);
+  for (auto& e : c->fused_cache) (void)hipFree(e.dev);
   if (c->graph_exec) (void)hipGraphExecDestroy(c->graph_exec);
   if (c->graph) (void)hipGraphDestroy(c->graph);
   if (c->aux) (void)hipStreamDestroy(c->aux);
@@ -304,6 +328,12 @@ extern "C" int rlt_create(const rlt_config* cfg, const rlt_weights* w, int32_t m
   c->gemm_s_force = env_int("RLT_GEMM_S", 0);
   c->gemm_wide = env_int("RLT_GEMM_WIDE", 1);
   c->split_min_rows = env_int("RLT_SPLIT_MIN_ROWS", 0);
+  c->gemm_target = 512;
+  // Off by default: on MI355X a device-scope grid barrier costs 3.5-8.7 us,
+  // so ~15 phases per block make the persistent step slower than the
+  // separate kernels at every batch size measured (1-16 rows).
+  c->fused_rows = c->dt == 1 ? std::min(32, std::max(0, env_int("RLT_FUSED_ROWS", 0))) : 0;
+  c->fused_spin = (int64_t)200000000;  // 2 s of the 100 MHz real-time counter
   c->partial_cap = (size_t)8 * c->M_pad * std::max(3 * d, 2 * F);
   const size_t M = c->M_pad;
 
@@ -351,6 +381,22 @@ extern "C" int rlt_create(const rlt_config* cfg, const rlt_weights* w, int32_t m
     return fail(RLT_EHIP, "pinned error word allocation failed");
   }
   *(volatile int*)c->err_host = 0;
+  if (c->fused_rows > 0) {
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu < 1 ||
+        fused_blocks_per_cu() < 1)
+      c->fused_rows = 0;  // no persistent path on this device: separate kernels only
+    c->fused_grid = ncu;
+    const int gf = env_int("RLT_FUSED_GRID", 0);
+    if (gf > 0 && gf < ncu) c->fused_grid = gf;
+    c->fused_target = env_int("RLT_FUSED_TARGET", c->fused_grid);
+  }
+  if (c->fused_rows > 0 && (dev_alloc(&c->fused_sync, 2 * sizeof(unsigned)) != RLT_OK ||
+                            hipMemset(c->fused_sync, 0, 2 * sizeof(unsigned)) != hipSuccess)) {
+    rlt_destroy(c);
+    return fail(RLT_EHIP, "barrier word allocation failed");
+  }
   if (hipHostMalloc((void**)&c->host_stage, M * 4 * 4, hipHostMallocDefault) != hipSuccess) {
     rlt_destroy(c);
     return fail(RLT_EHIP, "pinned staging allocation failed");
@@ -364,6 +410,13 @@ static int take_device_error(rlt_ctx* c) {
   const int e = *(volatile int*)c->err_host;
   if (e) {
     *(volatile int*)c->err_host = 0;
+    if (e == RLT_EHIP && c->fused_sync) {
+      // a persistent step gave up at a barrier: rearm the barrier words
+      (void)hipDeviceSynchronize();
+      (void)hipMemset(c->fused_sync, 0, 2 * sizeof(unsigned));
+      (void)hipDeviceSynchronize();
+      return fail(e, "device-detected error from an earlier call: a persistent step timed out at a barrier");
+    }
     return fail(e, "device-detected error from an earlier call (code %d): rows were skipped", e);
   }
   return RLT_OK;
@@ -418,7 +471,7 @@ struct Gemm {
       const int mt = (n + 16 * MB - 1) / (16 * MB);
       const int tiles = g.npairs / 4 * mt;
       const int kst = K / 64;
-      int S = std::max(1, (256 + tiles - 1) / tiles);
+      int S = std::max(1, (c->gemm_target / 2 + tiles - 1) / tiles);
       S = std::min(S, std::max(1, kst / 4));              // >= 4 stages per workgroup
       if (c->gemm_s_force > 0) S = std::min(c->gemm_s_force, kst);
       while (S > 1 && (size_t)S * c->M_pad * g.Nv > c->partial_cap) --S;
@@ -432,7 +485,7 @@ struct Gemm {
       if (mbf == 1 || mbf == 2 || mbf == 4) MB = mbf;
       const int mt = (n + 16 * MB - 1) / (16 * MB);
       const int tiles = g.npairs * mt;
-      int S = std::max(1, (512 + tiles - 1) / tiles);   // fill the chip
+      int S = std::max(1, (c->gemm_target + tiles - 1) / tiles);   // fill the chip
       S = std::min(S, std::max(1, K / 256));             // >= 64 K per wave
       S = std::min(S, std::max(1, K / (4 * n)));         // partial traffic <= the weights'
       if (c->gemm_s_force > 0) S = std::min(c->gemm_s_force, std::max(1, K / 128));
@@ -651,9 +704,68 @@ StepPlan slice(const StepPlan& P, int off, int cnt, int d, int V) {
   return Q;
 }
 
-// Run the plan, as two concurrent row ranges when it has enough rows.
+// The device copy of a recorded phase list: found in the cache, or
+// uploaded (synchronously; never while `s` is being captured). Null when
+// unavailable.
+const Phase* fused_phases(rlt_ctx* c, const std::vector<Phase>& rec, hipStream_t s) {
+  const size_t bytes = rec.size() * sizeof(Phase);
+  for (const auto& e : c->fused_cache)
+    if (e.host.size() == rec.size() && std::memcmp(e.host.data(), rec.data(), bytes) == 0) return e.dev;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+  if (c->fused_cache.size() >= 64) {
+    if (hipDeviceSynchronize() != hipSuccess) return nullptr;
+    for (auto& e : c->fused_cache) (void)hipFree(e.dev);
+    c->fused_cache.clear();
+  }
+  Phase* dev = nullptr;
+  if (hipMalloc((void**)&dev, bytes) != hipSuccess) return nullptr;
+  if (hipMemcpy(dev, rec.data(), bytes, hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipFree(dev);
+    return nullptr;
+  }
+  c->fused_cache.push_back({rec, dev});
+  return dev;
+}
+
+// Record the transition of the plan as phases (the readout stays a kernel
+// of its own); returns the device phase list or null.
+const Phase* fused_prepare(rlt_ctx* c, const StepPlan& P, hipStream_t s, int* nphase) {
+  std::vector<Phase> rec;
+  StepPlan Q = P;
+  Q.do_readout = false;
+  t_rec = &rec;
+  c->gemm_target = c->fused_target;
+  enqueue_transition(c, c->ws[0], Q, s);
+  t_rec = nullptr;
+  c->gemm_target = 512;
+  *nphase = (int)rec.size();
+  for (const Phase& p : rec)
+    if (p.kind == PH_INVALID) return nullptr;
+  return fused_phases(c, rec, s);
+}
+
+// Run the plan: one persistent kernel for small calls, otherwise the
+// separate kernels, as two concurrent row ranges when it has enough rows.
 void enqueue_rows(rlt_ctx* c, const StepPlan& P, hipStream_t s) {
   const int n = P.n;
+  if (c->fused_rows > 0 && n <= c->fused_rows) {
+    int nph = 0;
+    const Phase* ph = fused_prepare(c, P, s, &nph);
+    if (ph) {
+      {
+        Prof pf(c, RLT_PROF_FUSED, s);
+        launch_fused(ph, nph, c->fused_sync, c->err_dev, c->fused_grid, c->fused_spin, s);
+      }
+      if (P.do_readout) {
+        ReadoutArgs ro = P.ro;
+        ro.logits = P.logits ? P.logits : c->ws[0].logits;
+        Prof pf(c, RLT_PROF_READOUT, s);
+        launch_readout(ro, s);
+      }
+      return;
+    }
+  }
   if (c->split_min_rows <= 0 || n < c->split_min_rows || !c->aux) {
     enqueue_transition(c, c->ws[0], P, s);
     return;
@@ -703,7 +815,9 @@ extern "C" int rlt_init_state(rlt_ctx* c, rlt_state* st, const int32_t* rows, in
   return RLT_OK;
 }
 
-static int step_enqueue(rlt_ctx* c, rlt_state* st, const rlt_step_io* io, hipStream_t s) {
+// dry: only record and upload the persistent step's phases (before a graph
+// capture, which cannot upload them)
+static int step_enqueue(rlt_ctx* c, rlt_state* st, const rlt_step_io* io, hipStream_t s, bool dry = false) {
   const int n = io->n;
   StepPlan P{};
   P.R = Rows{io->rows, c->ident, c->t_row, n};
@@ -743,6 +857,11 @@ static int step_enqueue(rlt_ctx* c, rlt_state* st, const rlt_step_io* io, hipStr
   m.err = c->err_dev;
   m.max_t = c->max_ctx;
   m.B_cap = st->B_cap;
+  if (dry) {
+    int nph = 0;
+    if (c->fused_rows > 0 && n <= c->fused_rows) (void)fused_prepare(c, P, s, &nph);
+    return RLT_OK;
+  }
   launch_prestep(m, s);
   enqueue_rows(c, P, s);
   PostArgs pa{P.R, n, st->pos, st->pending, nullptr};
@@ -788,6 +907,7 @@ extern "C" int rlt_decoder_step(rlt_ctx* c, rlt_state* st, const rlt_step_io* io
       (void)hipGraphDestroy(c->graph);
       c->graph = nullptr;
     }
+    if ((rc = step_enqueue(c, st, io, s, true))) return rc;
     HIP_TRY(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
     const bool prof = c->prof_on;
     c->prof_on = false;

@@ -299,6 +299,60 @@ struct PostArgs {
   const int32_t* next_tok;   // token to record as pending (DEFER) or null
 };
 void launch_poststep(const PostArgs& a, hipStream_t s);
+
+// ----------------------------------------------------------------------------
+// persistent step: the launches of a transition are recorded as phases and
+// run by one kernel that keeps one workgroup per compute unit and crosses a
+// grid-wide barrier between phases (small calls, where launch latency rather
+// than bandwidth bounds the separate kernels)
+// ----------------------------------------------------------------------------
+
+enum PhaseKind {
+  PH_GEMM = 0,        // k_gemm_bf16 tile (bf16, 1 or 2 row blocks)
+  PH_SPLITK = 1,      // split-K sum + epilogue
+  PH_SWA = 2,
+  PH_XATTN = 3,
+  PH_XCOMBINE = 4,
+  PH_MERGE_PREP = 5,
+  PH_FINAL = 6,
+  PH_COPY = 7,
+  PH_INVALID = -1     // marks a recording that contains a launch the persistent kernel cannot run
+};
+
+struct CopyArgs {
+  const float* src;
+  float* dst;
+  int64_t n;
+};
+
+struct GemmPhase {
+  GemmArgs g;
+  EpiArgs e;
+};
+
+// One recorded launch: a virtual grid of (gx, gy, gz) blocks of 256 threads.
+struct Phase {
+  int kind;
+  int gx, gy, gz;
+  union {
+    GemmPhase gm;
+    AttnArgs at;
+    MiscArgs mi;
+    CopyArgs cp;
+  } u;
+};
+
+// Host: while a recorder is installed, the recordable launchers (bf16
+// products with up to 2 row blocks, attention, merge preparation, state
+// write-back, copies) append a phase and return true instead of launching.
+bool record_phase(const Phase& p);
+
+// Grid-barrier words: [0] arrival counter (self-resetting), [1] abort flag.
+void launch_fused(const Phase* phases, int nphase, unsigned* sync, int* err, int grid, int64_t spin_ticks,
+                  hipStream_t s);
+// workgroups of the persistent kernel that fit on one compute unit
+int fused_blocks_per_cu();
+
 void launch_init(int dtype, const int* rows, int n, const float* s_star, float* s_state, int* pos,
                  int* pending, void* ring_k, void* ring_v, int L, int B_cap, int W, int d,
                  int poison, hipStream_t s);

@@ -269,3 +269,50 @@ def test_argmax_sampling_and_scoring_against_oracle_on_gpu_logits():
         if int(toks[b]) in set(ids.tolist()):
             assert abs(float(logmu[b]) - lm[list(ids).index(int(toks[b]))]) < 2e-2
         assert abs(float(ratio[b]) - math.exp(float(logp[b]) - float(lmu[b]))) < 1e-4 * max(1, float(ratio[b]))
+
+
+def test_persistent_step_equals_separate_kernels():
+    """The persistent step (one kernel, grid barriers between the recorded
+    phases; enabled per context with RLT_FUSED_ROWS) reproduces the separate
+    kernels bit for bit: same bodies, launch shapes and reduction orders.
+    Covers plain steps, hipGraph-captured steps and a replay from H_0."""
+    require_gpu()
+    import os
+    wl = SMALL.with_(B=8, T=40)
+    ref = GpuRun(wl)
+    old = os.environ.get("RLT_FUSED_ROWS")
+    os.environ["RLT_FUSED_ROWS"] = "16"
+    try:
+        fz = GpuRun(wl, raw=ref.raw)
+    finally:
+        if old is None:
+            del os.environ["RLT_FUSED_ROWS"]
+        else:
+            os.environ["RLT_FUSED_ROWS"] = old
+    for run in (ref, fz):
+        run.init()
+    S0, Z0 = ref.run(10)
+    S1, Z1 = fz.run(10)
+    assert np.array_equal(S0, S1) and np.array_equal(Z0, Z1)
+    # captured steps
+    stream = torch.cuda.Stream()
+    rows = ref.rows()
+    e_fixed = ref.Ed[:, 0].contiguous()
+    am = [torch.empty(wl.B, dtype=torch.int32, device="cuda") for _ in range(2)]
+    with torch.cuda.stream(stream):
+        for i in range(3):
+            for run, out in zip((ref, fz), am):
+                assert run.dec.step(run.st, rows, e_fixed, run.mem, argmax=out, graph=True) == 0
+            stream.synchronize()
+            assert torch.equal(ref.st.s, fz.st.s) and torch.equal(am[0], am[1]), i
+    # replay from H_0 with an active set that shrinks over the ticks
+    lens = np.array([12, 9, 5, 12, 3, 7, 2, 10], dtype=np.int32)
+    splits = np.ones(wl.B, dtype=np.int32)
+    tokens = torch.from_numpy(synth.make_tokens(wl, 0, wl.B, wl.T)).cuda()
+    lp = [torch.full((wl.B, wl.T), float("nan"), device="cuda") for _ in range(2)]
+    for run, out in zip((ref, fz), lp):
+        assert run.dec.replay(run.st, lens, splits, run.Ed, run.mem, tokens, out) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(lp[0].isnan(), lp[1].isnan())
+    assert torch.equal(torch.nan_to_num(lp[0]), torch.nan_to_num(lp[1]))
+    assert torch.equal(ref.st.s, fz.st.s)
