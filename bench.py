@@ -100,10 +100,10 @@ def measured_traffic(x_bytes: float):
     path = os.path.join(ROOT, "profiles", "k_xattn_reference_depth_traffic.json")
     try:
         rec = json.load(open(path))
-        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+        src = b"".join(open(os.path.join(ROOT, f), "rb").read() for f in rec["sources"])
     except (OSError, ValueError, KeyError):
         return None
-    if hashlib.sha256(src).hexdigest()[:16] != rec.get("source_sha256_16"):
+    if hashlib.sha256(src).hexdigest()[:16] != rec.get("sources_sha256_16"):
         return None
     return int(rec["traffic_over_algorithmic"] * x_bytes)
 
