@@ -27,6 +27,11 @@ itself and are fixed here as a specification):
   * FFN is SwiGLU: W_down (silu(W_gate h) * (W_up h)).
   * Projections carry no bias; the merge gate carries b_g.
   * Memory group of layer l (0-based): floor(l * G / L_D).
+  * Memory construction [RLT §2.2, eq. (2.2)]: one RMSNorm_E per group g
+    (gain norm_e^g) feeds both maps; the key map is W_K^g followed by the
+    same rotary transform as the decoder queries, at the entry's own
+    position t, so cross-attention scores depend on the query and key
+    positions only through their difference.
 """
 from __future__ import annotations
 
@@ -136,6 +141,37 @@ class Memory:
     positions 1..T [RLT §2.2, eq. (2.2)]. Row j-1 holds position j."""
     k: Sequence[np.ndarray]
     v: Sequence[np.ndarray]
+
+
+def memory_entry(cfg: Config, e: np.ndarray, t: int, norm_e: np.ndarray, wk: np.ndarray,
+                 wv: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """One memory entry of one group at 1-based position t [RLT §2.2, eq. (2.2)]:
+    k_t = P_K(e_t, t) = RoPE(W_K RMSNorm_E(e_t), t), v_t = W_V RMSNorm_E(e_t)."""
+    h = rms_norm(e, norm_e, cfg.eps)
+    k = wk @ h
+    if cfg.pos == "rope":
+        k = rope(k, t, cfg.H, cfg.dh, cfg.rope_theta)
+    return k, wv @ h
+
+
+def build_memory(cfg: Config, E: np.ndarray, mw: Dict[str, np.ndarray], n: Optional[int] = None) -> Memory:
+    """Memory of one sequence for positions 1..n from its encoder
+    representations E [T, d] and the memory weights ``mw`` keyed
+    "memory.{g}.norm_e" / ".wk" / ".wv" [RLT §2.2, eq. (2.2)]: every group,
+    every position, one entry at a time (the token-parallel form computes
+    the same values, each position being independent of the others)."""
+    n = E.shape[0] if n is None else n
+    ks, vs = [], []
+    for g in range(cfg.G):
+        k = np.empty((n, cfg.d))
+        v = np.empty((n, cfg.d))
+        for t in range(1, n + 1):
+            k[t - 1], v[t - 1] = memory_entry(cfg, np.asarray(E[t - 1], dtype=np.float64), t,
+                                              mw["memory.%d.norm_e" % g], mw["memory.%d.wk" % g],
+                                              mw["memory.%d.wv" % g])
+        ks.append(k)
+        vs.append(v)
+    return Memory(ks, vs)
 
 
 def retained_positions(t: int, W: int) -> List[int]:

@@ -203,6 +203,22 @@ def make_weights(wl: Workload) -> Dict[str, np.ndarray]:
     return {n: make_weight(wl, n, s) for n, s in weight_shapes(wl).items()}
 
 
+def memory_weight_shapes(wl: Workload) -> Dict[str, tuple]:
+    """Parameters of the encoder-memory maps, per group g: the RMSNorm_E gain
+    and the key / value projections ([out, in])."""
+    d = wl.d
+    shapes = {}
+    for g in range(wl.G):
+        shapes.update({"memory.%d.norm_e" % g: (d,), "memory.%d.wk" % g: (d, d), "memory.%d.wv" % g: (d, d)})
+    return shapes
+
+
+def make_memory_weights(wl: Workload) -> Dict[str, np.ndarray]:
+    """Memory-map weights: matrices N(0, w_std) in the workload dtype, gains
+    1 + gain_std * N(0, 1) in fp32 (same recipe as the decoder weights)."""
+    return {n: make_weight(wl, n, s) for n, s in memory_weight_shapes(wl).items()}
+
+
 def make_e(wl: Workload, b0: int = 0, nb: Optional[int] = None, T: Optional[int] = None) -> np.ndarray:
     """Encoder representations e[b][t][d] for sequences b0..b0+nb-1, positions 1..T.
 

@@ -483,3 +483,97 @@ def test_sampler_boundary_rule():
     assert sample(z, 1.0, 0, 0.5)[0] == 1
     assert sample(z, 1.0, 0, 0.0)[0] == 0
     assert sample(z, 1.0, 0, 0.4999)[0] == 0
+
+
+# ---------------------------------------------------------------------------
+# encoder-memory construction [RLT §2.2, eq. (2.2)]
+# ---------------------------------------------------------------------------
+
+def _mem_cfg(**kw):
+    base = dict(L=1, d=32, H=2, dh=16, W=4, G=1, F=64, V=16)
+    base.update(kw)
+    return Config(**base)
+
+
+def test_memory_entry_basis_vector_closed_form():
+    """W_K = I, W_V = 2 I, unit gain, e = c * u_i: v is twice the normalised
+    basis vector c / sqrt(c^2/d + eps) u_i and k puts the normalised value on
+    the rotary pair of coordinate i at the angle t * theta^(-2 i'/dh) (i' = i
+    within the head, i' < dh/2: cos on i, sin on i + dh/2) -- written out,
+    not through rope()."""
+    from oracle import memory_entry
+    cfg = _mem_cfg()
+    d, dh, I = cfg.d, cfg.dh, np.eye(cfg.d)
+    c = 3.0
+    for i, t in ((0, 1), (5, 9), (dh + 3, 4096)):
+        e = np.zeros(d)
+        e[i] = c
+        k, v = memory_entry(cfg, e, t, np.ones(d), I, 2.0 * I)
+        mag = c / math.sqrt(c * c / d + cfg.eps)
+        ev = np.zeros(d)
+        ev[i] = 2.0 * mag
+        assert np.allclose(v, ev, atol=1e-12)
+        h, ii = divmod(i, dh)
+        ang = t * cfg.rope_theta ** (-2.0 * ii / dh)
+        ek = np.zeros(d)
+        ek[h * dh + ii] = mag * math.cos(ang)
+        ek[h * dh + ii + dh // 2] = mag * math.sin(ang)
+        assert np.allclose(k, ek, atol=1e-12), (i, t)
+
+
+def test_memory_entry_scale_and_norm_invariants():
+    """RMSNorm_E removes the scale of e (up to eps); the rotary transform
+    keeps the norm of W_K RMSNorm_E(e); the gain scales the columns."""
+    from oracle import memory_entry
+    cfg = _mem_cfg()
+    d = cfg.d
+    e = _rand(d, 11)
+    wk, wv = _rand((d, d), 12, 0.2), _rand((d, d), 13, 0.2)
+    g = 1 + 0.1 * _rand(d, 14)
+    k1, v1 = memory_entry(cfg, e, 17, g, wk, wv)
+    k2, v2 = memory_entry(cfg, 7.0 * e, 17, g, wk, wv)
+    assert rel_l2(k2, k1) < 1e-6 and rel_l2(v2, v1) < 1e-6
+    h = e / np.sqrt(np.mean(e * e) + cfg.eps) * g
+    assert abs(np.linalg.norm(k1) - np.linalg.norm(wk @ h)) < 1e-10 * np.linalg.norm(k1)
+    # without the positional transform the key is the plain projection
+    k0, _ = memory_entry(_mem_cfg(pos="none"), e, 17, g, wk, wv)
+    assert np.allclose(k0, wk @ h, atol=1e-12)
+
+
+def test_memory_keys_relative_position_with_decoder_query():
+    """A decoder query rotated at s against a memory key built at t: the score
+    depends on s - t only (same rotary form on both sides)."""
+    from oracle import memory_entry
+    cfg = _mem_cfg()
+    d, H, dh = cfg.d, cfg.H, cfg.dh
+    e = _rand(d, 21)
+    wk, wv = _rand((d, d), 22, 0.3), _rand((d, d), 23, 0.3)
+    q = _rand(d, 24)
+    for s, t, delta in ((9, 4, 100), (30, 30, 7), (2, 50, 1000)):
+        ka, _ = memory_entry(cfg, e, t, np.ones(d), wk, wv)
+        kb, _ = memory_entry(cfg, e, t + delta, np.ones(d), wk, wv)
+        qa = rope(q, s, H, dh, cfg.rope_theta).reshape(H, dh)
+        qb = rope(q, s + delta, H, dh, cfg.rope_theta).reshape(H, dh)
+        sa = (qa * ka.reshape(H, dh)).sum(-1)
+        sb = (qb * kb.reshape(H, dh)).sum(-1)
+        assert np.allclose(sa, sb, rtol=1e-9, atol=1e-9)
+
+
+def test_build_memory_groups_and_positions():
+    """build_memory: group g uses its own weights; row t-1 holds position t."""
+    from oracle import build_memory, memory_entry
+    cfg = _mem_cfg(G=2)
+    d = cfg.d
+    E = _rand((6, d), 31)
+    mw = {}
+    for g in range(2):
+        mw["memory.%d.norm_e" % g] = 1 + 0.1 * _rand(d, 40 + g)
+        mw["memory.%d.wk" % g] = _rand((d, d), 50 + g, 0.2)
+        mw["memory.%d.wv" % g] = _rand((d, d), 60 + g, 0.2)
+    mem = build_memory(cfg, E, mw)
+    for g in range(2):
+        for t in (1, 4, 6):
+            k, v = memory_entry(cfg, E[t - 1], t, mw["memory.%d.norm_e" % g], mw["memory.%d.wk" % g],
+                                mw["memory.%d.wv" % g])
+            assert np.array_equal(mem.k[g][t - 1], k) and np.array_equal(mem.v[g][t - 1], v)
+    assert not np.allclose(mem.v[0], mem.v[1])
