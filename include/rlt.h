@@ -129,7 +129,8 @@ typedef struct rlt_state {
   uint64_t version;   /* must equal rlt_config.weights_version [RLT §5.4, §6] */
 } rlt_state;
 
-/* Encoder memory M_{<=t} [RLT §2.2, eq. (2.2)], read-only. Key of group g,
+/* Encoder memory M_{<=t} [RLT §2.2, eq. (2.2)]: read by the decoder calls,
+ * written by rlt_memory_append / rlt_memory_prefill. Key of group g,
  * state row r, position j (1-based) starts at element
  *   k[g * stride_g + r * stride_b + (j - 1) * stride_t]   (likewise v)
  * and holds d contiguous elements of the config dtype. Only positions
@@ -247,6 +248,39 @@ int rlt_score_logprobs(rlt_ctx* ctx, const rlt_score_io* io, void* stream);
 
 /* Wait for `stream`, then return (and clear) any device-detected error. */
 int rlt_sync_error(rlt_ctx* ctx, void* stream);
+
+/* Parameters of the encoder-memory maps [RLT §2.2, eq. (2.2)], one set per
+ * group g < G; arrays of G device pointers, caller-owned, valid during the
+ * call: RMSNorm_E gain [d] fp32, W_K^g and W_V^g [d][d] of the config dtype
+ * (natural [out][in] layout). The key map is RoPE(W_K^g RMSNorm_E(e_t), t)
+ * with the decoder's rotary convention (pos_kind, rope_theta); the value
+ * map is W_V^g RMSNorm_E(e_t). */
+typedef struct rlt_memory_weights {
+  const float* const* norm_e;
+  const void* const* wk;
+  const void* const* wv;
+} rlt_memory_weights;
+
+/* Memory append, the step before a transition [RLT §2.2 eq. (2.2), §2.3
+ * eq. (2.8), App. A.2]: slot i < n writes, for every group, the entry of
+ * memory row rows[i] (device [n], distinct) at position
+ * t = mem_len[rows[i]] + 1 from e[i] (device [n][d], config dtype), then
+ * sets mem_len[rows[i]] = t. The buffers of `mem` are written (k, v) and
+ * updated (mem_len); B_cap and T_cap are their row and position
+ * capacities. A row outside 0..B_cap-1 raises a device-detected
+ * RLT_EINVAL, a row already holding T_cap entries RLT_EPREFIX; such slots
+ * are skipped. Enqueued on `stream`. */
+int rlt_memory_append(rlt_ctx* ctx, const rlt_memory_weights* mw, const rlt_memory* mem, int32_t B_cap,
+                      int32_t T_cap, const int32_t* rows, int32_t n, const void* e, void* stream);
+
+/* Token-parallel memory prefill [RLT §2.2 eq. (2.2), §4.1]: for sequences
+ * b < B (memory row b) every entry t = 1 .. len_host[b] (HOST array, each
+ * 1 <= len <= T_cap) from e[b * e_stride_b + (t - 1) * e_stride_t] (device,
+ * strides in elements), then mem_len[b] = len_host[b]. Enqueued on
+ * `stream` after one synchronous upload of the schedule. */
+int rlt_memory_prefill(rlt_ctx* ctx, const rlt_memory_weights* mw, const rlt_memory* mem, int32_t T_cap,
+                       int32_t B, const int32_t* len_host, const void* e, int64_t e_stride_b, int64_t e_stride_t,
+                       void* stream);
 
 #ifdef __cplusplus
 }

@@ -8,6 +8,6 @@ manages device buffers with PyTorch. Build with
 is missing.
 """
 from . import _abi  # noqa: F401
-from .runtime import Decoder, DecoderState, ModelConfig, current_stream, to_device  # noqa: F401
+from .runtime import Decoder, DecoderState, MemoryWeights, ModelConfig, current_stream, to_device  # noqa: F401
 
-__all__ = ["Decoder", "DecoderState", "ModelConfig", "current_stream", "to_device"]
+__all__ = ["Decoder", "DecoderState", "MemoryWeights", "ModelConfig", "current_stream", "to_device"]

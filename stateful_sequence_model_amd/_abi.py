@@ -70,6 +70,10 @@ class rlt_score_io(C.Structure):
                 ("logmu", P), ("logmu_behaviour", P), ("ratio", P)]
 
 
+class rlt_memory_weights(C.Structure):
+    _fields_ = [("norm_e", C.POINTER(P)), ("wk", C.POINTER(P)), ("wv", C.POINTER(P))]
+
+
 _lib = None
 
 # name -> (restype, argtypes)
@@ -83,6 +87,9 @@ _SIGS = {
     "rlt_replay_sequence": (C.c_int, [P, C.POINTER(rlt_state), C.POINTER(rlt_replay_io), P]),
     "rlt_score_logprobs": (C.c_int, [P, C.POINTER(rlt_score_io), P]),
     "rlt_sync_error": (C.c_int, [P, P]),
+    "rlt_memory_append": (C.c_int, [P, C.POINTER(rlt_memory_weights), C.POINTER(rlt_memory), i32, i32, P, i32, P, P]),
+    "rlt_memory_prefill": (C.c_int, [P, C.POINTER(rlt_memory_weights), C.POINTER(rlt_memory), i32, i32, P, P, i64,
+                                     i64, P]),
     "rlt_dbg_gemm": (C.c_int, [P, P, P, i32, i32, i32, P, P]),
     "rlt_dbg_profile": (C.c_int, [P, i32]),
     "rlt_dbg_profile_read": (C.c_int, [P, i32, C.POINTER(C.c_double), C.POINTER(C.c_int64)]),
@@ -161,6 +168,17 @@ def rlt_score_logprobs(ctx: int, io: rlt_score_io, stream: int) -> int:
 
 def rlt_sync_error(ctx: int, stream: int) -> int:
     return lib().rlt_sync_error(ctx, stream)
+
+
+def rlt_memory_append(ctx: int, mw: rlt_memory_weights, mem: rlt_memory, B_cap: int, T_cap: int, rows: int, n: int,
+                      e: int, stream: int) -> int:
+    return lib().rlt_memory_append(ctx, C.byref(mw), C.byref(mem), B_cap, T_cap, rows, n, e, stream)
+
+
+def rlt_memory_prefill(ctx: int, mw: rlt_memory_weights, mem: rlt_memory, T_cap: int, B: int, len_host, e: int,
+                       e_stride_b: int, e_stride_t: int, stream: int) -> int:
+    return lib().rlt_memory_prefill(ctx, C.byref(mw), C.byref(mem), T_cap, B, len_host, e, e_stride_b, e_stride_t,
+                                    stream)
 
 
 def rlt_dbg_gemm(ctx: int, A: int, W: int, M: int, N: int, K: int, out: int, stream: int) -> int:

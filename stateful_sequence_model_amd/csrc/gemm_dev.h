@@ -117,6 +117,19 @@ struct Epi {
         z[cb] = zb;
         return produce(m, ca, za, cb, zb);
       }
+      case EPI_MEMKV: {
+        const int t = a.rows.t_row[m];
+        if (t <= 0) return 0.f;
+        va *= rs;
+        vb *= rs;
+        const int seg = ca / a.d;
+        const int xa = ca - seg * a.d, xb = cb - seg * a.d;
+        if (seg == 0 && a.rope) rotate(m, xa % a.dh, va, vb);
+        T* dst = (T*)(seg == 0 ? a.mk : a.mv) + (int64_t)a.rows.rows[m] * a.msb + (int64_t)(t - 1) * a.mst;
+        dst[xa] = from_f<T>(va);
+        dst[xb] = from_f<T>(vb);
+        return 0.f;
+      }
       default:
         return 0.f;
     }

@@ -124,6 +124,80 @@ __global__ void k_copy_f32(const float* src, float* dst, int64_t n) {
 }
 
 // ---------------------------------------------------------------------------
+// encoder memory entries [RLT §2.2, eq. (2.2)]
+// ---------------------------------------------------------------------------
+
+// append: slot i writes position mem_len[rows[i]] + 1 (0 = skip: bad row or full)
+__global__ void k_mem_slots(const int* rows, int n, const int* mem_len, int B_cap, int T_cap, int* t_out, int* err) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int row = rows[i];
+  if (row < 0 || row >= B_cap) {
+    t_out[i] = 0;
+    *(volatile int*)err = ERR_INVAL;
+    return;
+  }
+  const int t = mem_len[row] + 1;
+  if (t > T_cap) {
+    t_out[i] = 0;
+    *(volatile int*)err = ERR_PREFIX;
+    return;
+  }
+  t_out[i] = t;
+}
+
+// prefill: flattened entry r0 + i -> (sequence b, position t) with
+// offs[b] <= r0 + i < offs[b + 1] (offs: prefix sums of the lengths)
+__global__ void k_mem_rows(const int* offs, int B, int64_t r0, int n, int* src_out, int* t_out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int64_t g = r0 + i;
+  int lo = 0, hi = B;  // largest b with offs[b] <= g
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (offs[mid] <= g) lo = mid;
+    else hi = mid;
+  }
+  src_out[i] = lo;
+  t_out[i] = (int)(g - offs[lo]) + 1;
+}
+
+// one workgroup per slot: the product input e * gain (the consumer applies
+// 1/sqrt(mean(e^2) + eps)) and the sum of squares of e
+template <typename T>
+__global__ __launch_bounds__(256) void k_mem_prep(Rows rows, EIn e, int d, const float* gain, T* A, float* ssq) {
+  __shared__ float scratch[16];
+  const int slot = blockIdx.x;
+  const int t = rows.t_row[slot];
+  T* out = A + (int64_t)slot * d;
+  if (t <= 0) {
+    for (int c = threadIdx.x; c < d; c += 256) out[c] = from_f<T>(0.f);
+    if (threadIdx.x == 0) ssq[slot] = (float)d;
+    return;
+  }
+  const T* x = (const T*)e.p + (int64_t)rows.src[slot] * e.sb + (int64_t)(t - 1) * e.st;
+  float ss = 0.f;
+  for (int c = threadIdx.x; c < d; c += 256) {
+    const float v = to_f<T>(x[c]);
+    ss = fmaf(v, v, ss);
+    out[c] = from_f<T>(v * gain[c]);
+  }
+  ss = block_sum(ss, scratch);
+  if (threadIdx.x == 0) ssq[slot] = ss;
+}
+
+__global__ void k_mem_setlen(const int* len, int B, int* mem_len) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < B) mem_len[b] = len[b];
+}
+
+__global__ void k_mem_commit(const int* rows, int n, const int* t_row, int* mem_len) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  if (t_row[i] > 0) mem_len[rows[i]] = t_row[i];
+}
+
+// ---------------------------------------------------------------------------
 // readout: log-sum-exp, argmax, top-k behaviour distribution, sampling
 // one workgroup of RB threads per slot; thread i owns logits
 // [i*per, (i+1)*per) so that scans over thread order follow id order.
@@ -416,6 +490,27 @@ void launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s) {
     if (record_phase(p)) return;
   }
   hipLaunchKernelGGL(k_copy_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src, dst, n);
+}
+void launch_mem_slots(const int* rows, int n, const int* mem_len, int B_cap, int T_cap, int* t_out, int* err,
+                      hipStream_t s) {
+  hipLaunchKernelGGL(k_mem_slots, dim3((n + 255) / 256), dim3(256), 0, s, rows, n, mem_len, B_cap, T_cap, t_out,
+                     err);
+}
+void launch_mem_rows(const int* offs, int B, int64_t r0, int n, int* src_out, int* t_out, hipStream_t s) {
+  hipLaunchKernelGGL(k_mem_rows, dim3((n + 255) / 256), dim3(256), 0, s, offs, B, r0, n, src_out, t_out);
+}
+void launch_mem_prep(int dtype, const Rows& rows, EIn e, int d, const float* gain, void* A, float* ssq,
+                     hipStream_t s) {
+  if (dtype == 0)
+    hipLaunchKernelGGL(k_mem_prep<float>, dim3(rows.n), dim3(256), 0, s, rows, e, d, gain, (float*)A, ssq);
+  else
+    hipLaunchKernelGGL(k_mem_prep<uint16_t>, dim3(rows.n), dim3(256), 0, s, rows, e, d, gain, (uint16_t*)A, ssq);
+}
+void launch_mem_setlen(const int* len, int B, int* mem_len, hipStream_t s) {
+  hipLaunchKernelGGL(k_mem_setlen, dim3((B + 255) / 256), dim3(256), 0, s, len, B, mem_len);
+}
+void launch_mem_commit(const int* rows, int n, const int* t_row, int* mem_len, hipStream_t s) {
+  hipLaunchKernelGGL(k_mem_commit, dim3((n + 255) / 256), dim3(256), 0, s, rows, n, t_row, mem_len);
 }
 void launch_readout(const ReadoutArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_readout, dim3(a.n), dim3(RB), 0, s, a);

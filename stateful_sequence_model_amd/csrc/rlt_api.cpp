@@ -91,6 +91,14 @@ struct rlt_ctx {
     Phase* dev;
   };
   std::vector<FusedEntry> fused_cache;
+  // encoder-memory construction scratch (allocated on first use)
+  int mem_rows;        // rows per chunk (multiple of 128)
+  void* mem_A;         // [mem_rows][d] product input
+  float* mem_ssq;      // [mem_rows]
+  int *mem_src, *mem_t;  // [mem_rows]
+  int* mem_offs;       // [mem_B + 1] prefill schedule
+  int* mem_lens;       // [mem_B]
+  int mem_B;
   // shared device buffers
   int *t_row, *ident, *ones, *rows_buf, *src_buf, *split_buf, *last_buf;
   double* inv_freq;
@@ -236,6 +244,9 @@ extern "C" void rlt_destroy(rlt_ctx* c) {
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   if (c->fused_sync) (void)hipFree(c->fused_sync);
+  for (void* p : {c->mem_A, (void*)c->mem_ssq, (void*)c->mem_src, (void*)c->mem_t, (void*)c->mem_offs,
+                  (void*)c->mem_lens})
+    if (p) (void)hipFree(p);
   for (auto& e : c->fused_cache) (void)hipFree(e.dev);
   if (c->graph_exec) (void)hipGraphExecDestroy(c->graph_exec);
   if (c->graph) (void)hipGraphDestroy(c->graph);
@@ -438,6 +449,8 @@ struct Gemm {
   rlt_ctx* c;
   const Workspace* w;
   hipStream_t s;
+  int m_pad = 0;       // rows allocated in A (default: the context's M_pad)
+  int ssq_units = 0;   // units of ssq_in (default: the decoder producers' units)
 
   void run(const void* A, int64_t lda, std::initializer_list<const void*> W, int seg_rows, int K, int pairing,
            int n, EpiArgs e, const float* ssq_in = nullptr, float* ssq_out = nullptr) {
@@ -452,7 +465,7 @@ struct Gemm {
     g.pairing = pairing;
     g.dh = c->cfg.d_head;
     g.M = n;
-    g.M_pad = c->M_pad;
+    g.M_pad = m_pad ? m_pad : c->M_pad;
     g.Nv = g.nseg * seg_rows;
     g.npairs = g.Nv / 32;
     g.S = 1;
@@ -461,7 +474,7 @@ struct Gemm {
     g.partial = w->partial;
     g.ssq_in = ssq_in;
     g.ssq_out = ssq_out;
-    g.ssq_units = c->cfg.d_model / (c->dt == 1 ? 32 : 2);  // column units of the producers
+    g.ssq_units = ssq_units ? ssq_units : c->cfg.d_model / (c->dt == 1 ? 32 : 2);  // producers' column units
     g.inv_d = 1.0f / (float)c->cfg.d_model;
     g.eps = c->cfg.rms_eps;
     if (c->dt == 1 && c->gemm_wide && n > 32 && g.npairs % 4 == 0 && K % 64 == 0) {
@@ -474,7 +487,7 @@ struct Gemm {
       int S = std::max(1, (c->gemm_target / 2 + tiles - 1) / tiles);
       S = std::min(S, std::max(1, kst / 4));              // >= 4 stages per workgroup
       if (c->gemm_s_force > 0) S = std::min(c->gemm_s_force, kst);
-      while (S > 1 && (size_t)S * c->M_pad * g.Nv > c->partial_cap) --S;
+      while (S > 1 && (size_t)S * g.M_pad * g.Nv > c->partial_cap) --S;
       g.wide = 1;
       g.mb = MB;
       g.S = S;
@@ -489,7 +502,7 @@ struct Gemm {
       S = std::min(S, std::max(1, K / 256));             // >= 64 K per wave
       S = std::min(S, std::max(1, K / (4 * n)));         // partial traffic <= the weights'
       if (c->gemm_s_force > 0) S = std::min(c->gemm_s_force, std::max(1, K / 128));
-      while (S > 1 && (size_t)S * c->M_pad * g.Nv > c->partial_cap) --S;
+      while (S > 1 && (size_t)S * g.M_pad * g.Nv > c->partial_cap) --S;
       g.S = S;
       g.mb = MB;
       const int per = (K + 4 * S - 1) / (4 * S);
@@ -1063,6 +1076,124 @@ extern "C" int rlt_score_logprobs(rlt_ctx* c, const rlt_score_io* io, void* stre
 // ----------------------------------------------------------------------------
 // test / benchmark hooks (include/rlt_debug.h)
 // ----------------------------------------------------------------------------
+
+// ----------------------------------------------------------------------------
+// encoder memory [RLT §2.2, eq. (2.2)]
+// ----------------------------------------------------------------------------
+
+namespace {
+
+int check_memory_weights(const rlt_ctx* c, const rlt_memory_weights* mw) {
+  if (!mw || !mw->norm_e || !mw->wk || !mw->wv) return fail(RLT_EINVAL, "null memory weights");
+  for (int g = 0; g < c->cfg.n_groups; ++g)
+    if (!mw->norm_e[g] || !mw->wk[g] || !mw->wv[g]) return fail(RLT_EINVAL, "missing memory weight of group %d", g);
+  return RLT_OK;
+}
+
+// scratch for up to mem_rows entries per chunk and B prefill sequences
+int ensure_mem_ws(rlt_ctx* c, int B) {
+  if (!c->mem_A) {
+    c->mem_rows = std::max(c->M_pad, 8192);
+    const size_t R = c->mem_rows;
+    int rc = 0;
+    if ((rc = dev_alloc(&c->mem_A, R * c->cfg.d_model * c->es)) || (rc = dev_alloc(&c->mem_ssq, R * 4)) ||
+        (rc = dev_alloc(&c->mem_src, R * 4)) || (rc = dev_alloc(&c->mem_t, R * 4)))
+      return rc;
+    if (hipMemset(c->mem_A, 0, R * c->cfg.d_model * c->es) != hipSuccess)
+      return fail(RLT_EHIP, "memory scratch initialisation failed");
+  }
+  if (B > c->mem_B) {
+    if (c->mem_offs) (void)hipFree(c->mem_offs);
+    if (c->mem_lens) (void)hipFree(c->mem_lens);
+    c->mem_offs = c->mem_lens = nullptr;
+    c->mem_B = 0;
+    int rc = 0;
+    if ((rc = dev_alloc(&c->mem_offs, (size_t)(B + 1) * 4)) || (rc = dev_alloc(&c->mem_lens, (size_t)B * 4))) return rc;
+    c->mem_B = B;
+  }
+  return RLT_OK;
+}
+
+// entries of the n slots of R (t_row already set) for every group
+void enqueue_mem_entries(rlt_ctx* c, const rlt_memory_weights* mw, const rlt_memory* mem, const Rows& R, EIn e,
+                         hipStream_t s) {
+  const rlt_config& cf = c->cfg;
+  const int d = cf.d_model;
+  for (int g = 0; g < cf.n_groups; ++g) {
+    launch_mem_prep(c->dt, R, e, d, mw->norm_e[g], c->mem_A, c->mem_ssq, s);
+    EpiArgs ep{};
+    ep.kind = EPI_MEMKV;
+    ep.rows = R;
+    ep.d = d;
+    ep.dh = cf.d_head;
+    ep.H = cf.n_heads;
+    ep.rope = cf.pos_kind == RLT_POS_ROPE;
+    ep.inv_freq = c->inv_freq;
+    ep.mk = (char*)mem->k + (size_t)g * mem->stride_g * c->es;
+    ep.mv = (char*)mem->v + (size_t)g * mem->stride_g * c->es;
+    ep.msb = mem->stride_b;
+    ep.mst = mem->stride_t;
+    Gemm gm{c, &c->ws[0], s};
+    gm.m_pad = c->mem_rows;
+    gm.ssq_units = 1;
+    gm.run(c->mem_A, d, {mw->wk[g], mw->wv[g]}, d, d, PAIR_ROPE, R.n, ep, c->mem_ssq, nullptr);
+  }
+}
+
+}  // namespace
+
+extern "C" int rlt_memory_append(rlt_ctx* c, const rlt_memory_weights* mw, const rlt_memory* mem, int32_t B_cap,
+                                 int32_t T_cap, const int32_t* rows, int32_t n, const void* e, void* stream) {
+  if (!c || !mem) return fail(RLT_EINVAL, "null context or memory");
+  int rc = check_memory_weights(c, mw);
+  if (rc) return rc;
+  if ((rc = check_memory(*mem))) return rc;
+  if (!rows || !e) return fail(RLT_EINVAL, "null rows or e");
+  if (n < 1 || n > c->max_rows) return fail(RLT_ESHAPE, "n=%d outside 1..max_rows=%d", n, c->max_rows);
+  if (B_cap < 1 || T_cap < 1) return fail(RLT_EINVAL, "B_cap < 1 or T_cap < 1");
+  if ((rc = ensure_mem_ws(c, 0))) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  int* mem_len = const_cast<int*>(mem->mem_len);
+  launch_mem_slots(rows, n, mem_len, B_cap, T_cap, c->mem_t, c->err_dev, s);
+  const Rows R{rows, c->ident, c->mem_t, n};  // output row rows[i], input e[i]
+  enqueue_mem_entries(c, mw, mem, R, EIn{e, (int64_t)c->cfg.d_model, 0}, s);
+  launch_mem_commit(rows, n, c->mem_t, mem_len, s);
+  HIP_TRY(hipGetLastError());
+  return RLT_OK;
+}
+
+extern "C" int rlt_memory_prefill(rlt_ctx* c, const rlt_memory_weights* mw, const rlt_memory* mem, int32_t T_cap,
+                                  int32_t B, const int32_t* len_host, const void* e, int64_t e_stride_b,
+                                  int64_t e_stride_t, void* stream) {
+  if (!c || !mem) return fail(RLT_EINVAL, "null context or memory");
+  int rc = check_memory_weights(c, mw);
+  if (rc) return rc;
+  if ((rc = check_memory(*mem))) return rc;
+  if (!len_host || !e) return fail(RLT_EINVAL, "null lengths or e");
+  if (B < 1 || T_cap < 1) return fail(RLT_ESHAPE, "B < 1 or T_cap < 1");
+  if (e_stride_b < 0 || e_stride_t < 1) return fail(RLT_EINVAL, "e strides");
+  std::vector<int> offs(B + 1, 0);
+  for (int b = 0; b < B; ++b) {
+    if (len_host[b] < 1 || len_host[b] > T_cap) return fail(RLT_ESHAPE, "len[%d]=%d outside 1..T_cap", b, len_host[b]);
+    if ((int64_t)offs[b] + len_host[b] > INT32_MAX) return fail(RLT_ESHAPE, "more than 2^31 entries");
+    offs[b + 1] = offs[b] + len_host[b];
+  }
+  if ((rc = ensure_mem_ws(c, B))) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  HIP_TRY(hipStreamSynchronize(s));  // the schedule buffers may still be read by earlier work
+  HIP_TRY(hipMemcpy(c->mem_offs, offs.data(), (size_t)(B + 1) * 4, hipMemcpyHostToDevice));
+  HIP_TRY(hipMemcpy(c->mem_lens, len_host, (size_t)B * 4, hipMemcpyHostToDevice));
+  const int64_t total = offs[B];
+  for (int64_t r0 = 0; r0 < total; r0 += c->mem_rows) {
+    const int nrow = (int)std::min<int64_t>(c->mem_rows, total - r0);
+    launch_mem_rows(c->mem_offs, B, r0, nrow, c->mem_src, c->mem_t, s);
+    const Rows R{c->mem_src, c->mem_src, c->mem_t, nrow};  // sequence b is both memory row and e row
+    enqueue_mem_entries(c, mw, mem, R, EIn{e, e_stride_b, e_stride_t}, s);
+  }
+  launch_mem_setlen(c->mem_lens, B, const_cast<int*>(mem->mem_len), s);
+  HIP_TRY(hipGetLastError());
+  return RLT_OK;
+}
 
 extern "C" int rlt_dbg_gemm(rlt_ctx* c, const void* A, const void* W, int32_t M, int32_t N, int32_t K,
                             float* out, void* stream) {

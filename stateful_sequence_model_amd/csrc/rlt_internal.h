@@ -182,7 +182,8 @@ enum EpiKind {
   EPI_SWIGLU = 4,  // act[m][c] = silu(gate) * up              eq (2.16)
   EPI_MGATE = 5,   // g[m][c] = sigmoid(v + b_g[c])           eq (2.10)
   EPI_MOUT = 6,    // z[m][c] = e + alpha * g * v              eq (2.11)
-  EPI_CONVEX = 7   // g = sigmoid(v + b); z = g e + (1-g) s
+  EPI_CONVEX = 7,  // g = sigmoid(v + b); z = g e + (1-g) s
+  EPI_MEMKV = 8    // memory entry: k (T, rotary at t) and v (T)   eq (2.2)
 };
 
 struct EpiArgs {
@@ -204,6 +205,11 @@ struct EpiArgs {
   // the [M][d] (T) buffer receiving z * gain, the next product's input
   const float* gnext;
   void* zb;
+  // memory entries (EPI_MEMKV): one group's K / V buffers; the entry of slot
+  // m is at rows[m] * msb + (t_row[m] - 1) * mst elements
+  void* mk;
+  void* mv;
+  int64_t msb, mst;
 };
 
 // ----------------------------------------------------------------------------
@@ -266,6 +272,16 @@ void launch_merge_prep(int dtype, const MiscArgs& a, hipStream_t s);
 void launch_rmsnorm(int dtype, const MiscArgs& a, hipStream_t s);
 void launch_final(int dtype, const MiscArgs& a, hipStream_t s);
 void launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s);
+
+// encoder memory [RLT §2.2, eq. (2.2)]
+void launch_mem_slots(const int* rows, int n, const int* mem_len, int B_cap, int T_cap, int* t_out, int* err,
+                      hipStream_t s);
+void launch_mem_rows(const int* offs, int B, int64_t r0, int n, int* src_out, int* t_out, hipStream_t s);
+// A[slot] = e(slot) * gain (dtype), ssq[slot] = sum of squares of e(slot)
+void launch_mem_prep(int dtype, const Rows& rows, EIn e, int d, const float* gain, void* A, float* ssq,
+                     hipStream_t s);
+void launch_mem_commit(const int* rows, int n, const int* t_row, int* mem_len, hipStream_t s);
+void launch_mem_setlen(const int* len, int B, int* mem_len, hipStream_t s);
 
 struct ReadoutArgs {
   Rows rows;

@@ -220,8 +220,39 @@ class Decoder:
     def sync_error(self, stream=None) -> int:
         return A.rlt_sync_error(self.ctx, current_stream() if stream is None else stream)
 
+    # -- encoder memory ------------------------------------------------------
+    def memory_weights(self, params: Dict[str, object]) -> "MemoryWeights":
+        """Device copies of the memory-map weights keyed "memory.{g}.norm_e",
+        ".wk", ".wv" (one set per group)."""
+        return MemoryWeights(self.cfg, params, self.device)
+
+    def memory_append(self, mw: "MemoryWeights", mem: A.rlt_memory, B_cap: int, T_cap: int, rows: torch.Tensor,
+                      e: torch.Tensor, stream=None) -> int:
+        """Append one entry per listed memory row from e [n, d] (next position)."""
+        return A.rlt_memory_append(self.ctx, mw.c, mem, B_cap, T_cap, rows.data_ptr(), rows.numel(), e.data_ptr(),
+                                   current_stream() if stream is None else stream)
+
+    def memory_prefill(self, mw: "MemoryWeights", mem: A.rlt_memory, T_cap: int, lens: np.ndarray,
+                       e: torch.Tensor, stream=None) -> int:
+        """Entries 1..lens[b] of memory rows b < len(lens) from e [B, T, d]."""
+        lens = np.ascontiguousarray(lens, dtype=np.int32)
+        return A.rlt_memory_prefill(self.ctx, mw.c, mem, T_cap, len(lens), lens.ctypes.data, e.data_ptr(),
+                                    e.stride(0), e.stride(1), current_stream() if stream is None else stream)
+
     def dbg_gemm(self, Amat: torch.Tensor, W: torch.Tensor, out: torch.Tensor, stream=None) -> int:
         M, K = Amat.shape
         N = W.shape[0]
         return A.rlt_dbg_gemm(self.ctx, Amat.data_ptr(), W.data_ptr(), M, N, K, out.data_ptr(),
                               current_stream() if stream is None else stream)
+
+
+class MemoryWeights:
+    """Device copies of the encoder-memory maps' parameters and the pointer
+    arrays of ``rlt_memory_weights``."""
+
+    def __init__(self, cfg: ModelConfig, params: Dict[str, object], device="cuda"):
+        self.params = {k: to_device(v, cfg.dtype, device).contiguous() for k, v in params.items()}
+        G = cfg.G
+        self._arrays = {n: (A.P * G)(*[self.params["memory.%d.%s" % (g, n)].data_ptr() for g in range(G)])
+                        for n in ("norm_e", "wk", "wv")}
+        self.c = A.rlt_memory_weights(*[C.cast(self._arrays[n], C.POINTER(A.P)) for n in ("norm_e", "wk", "wv")])
