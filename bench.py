@@ -144,6 +144,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate", action="store_true",
                     help="also time a plain 4 GiB device copy and read-only sum (achievable HBM rates)")
+    ap.add_argument("--mode", choices=("step", "memory_prefill"), default="step",
+                    help="step: the decoder transition (default); memory_prefill: token-parallel "
+                         "construction of the encoder memory of the whole batch")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -159,6 +162,8 @@ def main():
     wl = synth.PRESETS[args.workload]
     if args.batch:
         wl = wl.with_(B=args.batch)
+    if args.mode == "memory_prefill":
+        return bench_memory_prefill(args, wl)
     B, T = wl.B, wl.T
     es = 2 if wl.dtype == "bf16" else 4
     K, Wu = args.steps, args.warmup
@@ -291,6 +296,68 @@ def main():
         log("timing the CPU oracle (%.0f s budget)..." % args.cpu_seconds)
         out["cpu_baseline"] = cpu_baseline(wl, t_center, args.cpu_seconds, raw)
     print(json.dumps(out), flush=True)
+
+
+def bench_memory_prefill(args, wl):
+    """Token-parallel memory construction [eq. (2.2)] of all B x T entries of
+    every group: one rlt_memory_prefill call per timed step. Dominated by the
+    [B*T, d] x [d, 2d] products per group (MFMA-bound), reported against
+    the dense bf16 peak."""
+    import numpy as np
+    import torch
+    import synth
+    from stateful_sequence_model_amd import Decoder, ModelConfig, _abi
+
+    B, T, d, G = wl.B, wl.T, wl.d, wl.G
+    es = 2 if wl.dtype == "bf16" else 4
+    torch.cuda.set_device(0)
+    cfg = ModelConfig(L=wl.L, d=wl.d, H=wl.H, dh=wl.dh, W=wl.W, G=wl.G, F=wl.F, V=wl.V, dtype=wl.dtype,
+                      merge=wl.merge, alpha=wl.alpha, eps=wl.eps, rope_theta=wl.rope_theta, pos=wl.pos)
+    # the decoder weights are not used by the memory maps: with one memory
+    # group a one-layer context of the same widths suffices
+    ctx_wl = wl.with_(L=1) if G == 1 else wl
+    ctx_cfg = ModelConfig(**{**cfg.__dict__, "L": ctx_wl.L})
+    dec = Decoder(ctx_cfg, synth.make_weights(ctx_wl), max_rows=128, max_ctx=T)
+    mw = dec.memory_weights(synth.make_memory_weights(wl))
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(wl.seed)
+    tdt = cfg.torch_dtype
+    e = torch.randn((B, T, d), generator=gen, device="cuda").to(tdt)
+    K = torch.empty((G, B, T, d), dtype=tdt, device="cuda")
+    V = torch.empty_like(K)
+    mem_len = torch.zeros(B, dtype=torch.int32, device="cuda")
+    mem = Decoder.memory(K, V, mem_len)
+    lens = np.full(B, T, dtype=np.int32)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            _abi.check(dec.memory_prefill(mw, mem, T, lens, e), "rlt_memory_prefill")
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            _abi.check(dec.memory_prefill(mw, mem, T, lens, e), "rlt_memory_prefill")
+        e1.record(stream)
+        torch.cuda.synchronize()
+    _abi.check(dec.sync_error(), "device error")
+    ms = e0.elapsed_time(e1) / args.steps
+    entries = B * T
+    flops = 2.0 * entries * d * (2 * d) * G
+    tflops = flops / (ms / 1e3) / 1e12
+    peak = 2500.0 if wl.dtype == "bf16" else 157.3
+    moved = entries * d * es * (1 + 2 * G) + G * 2 * d * d * es  # e read, K and V written, weights read
+    log("memory prefill: %.3f ms per call, %.1f M entries/s, %.1f TFLOP/s (%.1f%% of the dense peak)" %
+        (ms, entries / (ms / 1e3) / 1e6, tflops, 100 * tflops / peak))
+    print(json.dumps({
+        "metric": "encoder-memory entries/sec (token-parallel prefill, all %d groups)" % G,
+        "value": round(entries / (ms / 1e3), 1), "unit": "entries/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name + " memory prefill", "batch": B, "T": T, "d": d, "G": G},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4), "traffic": None,
+                     "algorithmic_flops_per_call": flops, "hbm_bytes_min_per_call": int(moved)},
+    }), flush=True)
 
 
 if __name__ == "__main__":
