@@ -249,6 +249,41 @@ int rlt_score_logprobs(rlt_ctx* ctx, const rlt_score_io* io, void* stream);
 /* Wait for `stream`, then return (and clear) any device-detected error. */
 int rlt_sync_error(rlt_ctx* ctx, void* stream);
 
+/* Exact prefix snapshot of decoder rows [RLT §6]: the complete decoder
+ * state H_t = (s_t, C_t^D) of a row with its position metadata and the model
+ * version, so that a restored row continues bit for bit as if it had never
+ * been saved (the encoder memory M_{<=t} is the caller's buffer and is kept
+ * by the caller). One row's snapshot is the header below followed by
+ *   s [d] float32, ring_k [L_D][W-1][d], ring_v [L_D][W-1][d] (config dtype),
+ * slots as in rlt_state (slot (j-1) mod (W-1) holds position j). */
+#define RLT_SNAPSHOT_MAGIC 0x53544c52u /* "RLTS" */
+typedef struct rlt_snapshot_header {
+  uint32_t magic;            /* RLT_SNAPSHOT_MAGIC */
+  uint32_t layout;           /* 1 */
+  uint64_t weights_version;  /* rlt_config.weights_version of the saving context */
+  int32_t n_layers, d_model, window, dtype;
+  int32_t pos;               /* consumed tokens t */
+  int32_t pending;           /* pending token or -1 [RLT App. A.2] */
+  int32_t reserved[6];
+} rlt_snapshot_header;
+
+/* HOST: bytes of one row's snapshot for this config. */
+int rlt_snapshot_bytes(const rlt_config* cfg, size_t* bytes_per_row);
+
+/* Copy rows rows_host[i] (HOST array) of `st` into the HOST buffer dst,
+ * row i at dst + i * rlt_snapshot_bytes. Waits for `stream` (the copies
+ * follow the work already enqueued on it) and returns when dst is complete. */
+int rlt_state_snapshot(rlt_ctx* ctx, const rlt_state* st, const int32_t* rows_host, int32_t n, void* dst,
+                       void* stream);
+
+/* Restore snapshot i of the HOST buffer src into row rows_host[i] of `st`
+ * (s, cache, pos, pending). Every header is checked before anything is
+ * written: bad magic/layout RLT_EINVAL, another config RLT_ESHAPE, another
+ * weights version (or a state of another version) RLT_ESTALE. Waits for
+ * `stream`. */
+int rlt_state_restore(rlt_ctx* ctx, rlt_state* st, const int32_t* rows_host, int32_t n, const void* src,
+                      void* stream);
+
 /* Parameters of the encoder-memory maps [RLT §2.2, eq. (2.2)], one set per
  * group g < G; arrays of G device pointers, caller-owned, valid during the
  * call: RMSNorm_E gain [d] fp32, W_K^g and W_V^g [d][d] of the config dtype

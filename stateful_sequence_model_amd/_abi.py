@@ -70,6 +70,15 @@ class rlt_score_io(C.Structure):
                 ("logmu", P), ("logmu_behaviour", P), ("ratio", P)]
 
 
+class rlt_snapshot_header(C.Structure):
+    _fields_ = [("magic", C.c_uint32), ("layout", C.c_uint32), ("weights_version", u64), ("n_layers", i32),
+                ("d_model", i32), ("window", i32), ("dtype", i32), ("pos", i32), ("pending", i32),
+                ("reserved", i32 * 6)]
+
+
+RLT_SNAPSHOT_MAGIC = 0x53544C52
+
+
 class rlt_memory_weights(C.Structure):
     _fields_ = [("norm_e", C.POINTER(P)), ("wk", C.POINTER(P)), ("wv", C.POINTER(P))]
 
@@ -87,6 +96,9 @@ _SIGS = {
     "rlt_replay_sequence": (C.c_int, [P, C.POINTER(rlt_state), C.POINTER(rlt_replay_io), P]),
     "rlt_score_logprobs": (C.c_int, [P, C.POINTER(rlt_score_io), P]),
     "rlt_sync_error": (C.c_int, [P, P]),
+    "rlt_snapshot_bytes": (C.c_int, [C.POINTER(rlt_config), C.POINTER(C.c_size_t)]),
+    "rlt_state_snapshot": (C.c_int, [P, C.POINTER(rlt_state), P, i32, P, P]),
+    "rlt_state_restore": (C.c_int, [P, C.POINTER(rlt_state), P, i32, P, P]),
     "rlt_memory_append": (C.c_int, [P, C.POINTER(rlt_memory_weights), C.POINTER(rlt_memory), i32, i32, P, i32, P, P]),
     "rlt_memory_prefill": (C.c_int, [P, C.POINTER(rlt_memory_weights), C.POINTER(rlt_memory), i32, i32, P, P, i64,
                                      i64, P]),
@@ -168,6 +180,20 @@ def rlt_score_logprobs(ctx: int, io: rlt_score_io, stream: int) -> int:
 
 def rlt_sync_error(ctx: int, stream: int) -> int:
     return lib().rlt_sync_error(ctx, stream)
+
+
+def rlt_snapshot_bytes(cfg: rlt_config) -> int:
+    out = C.c_size_t(0)
+    check(lib().rlt_snapshot_bytes(C.byref(cfg), C.byref(out)), "rlt_snapshot_bytes")
+    return out.value
+
+
+def rlt_state_snapshot(ctx: int, st: rlt_state, rows_host, n: int, dst, stream: int) -> int:
+    return lib().rlt_state_snapshot(ctx, C.byref(st), rows_host, n, dst, stream)
+
+
+def rlt_state_restore(ctx: int, st: rlt_state, rows_host, n: int, src, stream: int) -> int:
+    return lib().rlt_state_restore(ctx, C.byref(st), rows_host, n, src, stream)
 
 
 def rlt_memory_append(ctx: int, mw: rlt_memory_weights, mem: rlt_memory, B_cap: int, T_cap: int, rows: int, n: int,

@@ -1078,6 +1078,126 @@ extern "C" int rlt_score_logprobs(rlt_ctx* c, const rlt_score_io* io, void* stre
 // ----------------------------------------------------------------------------
 
 // ----------------------------------------------------------------------------
+// exact prefix snapshots [RLT §6]
+// ----------------------------------------------------------------------------
+
+extern "C" int rlt_snapshot_bytes(const rlt_config* cfg, size_t* bytes_per_row) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!bytes_per_row) return fail(RLT_EINVAL, "null output");
+  const size_t es = elt_size(cfg->dtype);
+  *bytes_per_row = sizeof(rlt_snapshot_header) + (size_t)cfg->d_model * sizeof(float) +
+                   2 * (size_t)cfg->n_layers * (size_t)(cfg->window - 1) * cfg->d_model * es;
+  return RLT_OK;
+}
+
+namespace {
+
+// the rows' ring bytes: L blocks of (W-1)*d elements, layer stride B_cap*(W-1)*d
+struct RingGeom {
+  size_t width, pitch;
+  int height;
+};
+
+RingGeom ring_geom(const rlt_ctx* c, const rlt_state* st) {
+  const size_t blk = (size_t)(c->cfg.window - 1) * c->cfg.d_model * c->es;
+  return RingGeom{blk, blk * st->B_cap, c->cfg.n_layers};
+}
+
+int check_rows_host(const rlt_state* st, const int32_t* rows, int32_t n) {
+  if (!rows || n < 1) return fail(RLT_EINVAL, "rows/n");
+  std::vector<int> seen(rows, rows + n);
+  std::sort(seen.begin(), seen.end());
+  if (seen.front() < 0 || seen.back() >= st->B_cap) return fail(RLT_EINVAL, "row outside 0..B_cap-1");
+  if (std::adjacent_find(seen.begin(), seen.end()) != seen.end()) return fail(RLT_EINVAL, "duplicate rows");
+  return RLT_OK;
+}
+
+}  // namespace
+
+extern "C" int rlt_state_snapshot(rlt_ctx* c, const rlt_state* st, const int32_t* rows_host, int32_t n, void* dst,
+                                  void* stream) {
+  if (!c || !dst) return fail(RLT_EINVAL, "null context or destination");
+  int rc = check_state(c, st);
+  if (rc) return rc;
+  if ((rc = check_rows_host(st, rows_host, n))) return rc;
+  size_t per = 0;
+  if ((rc = rlt_snapshot_bytes(&c->cfg, &per))) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  const rlt_config& cf = c->cfg;
+  const RingGeom rg = ring_geom(c, st);
+  for (int i = 0; i < n; ++i) {
+    const int r = rows_host[i];
+    char* base = (char*)dst + (size_t)i * per;
+    rlt_snapshot_header* h = (rlt_snapshot_header*)base;
+    std::memset(h, 0, sizeof(*h));
+    h->magic = RLT_SNAPSHOT_MAGIC;
+    h->layout = 1;
+    h->weights_version = cf.weights_version;
+    h->n_layers = cf.n_layers;
+    h->d_model = cf.d_model;
+    h->window = cf.window;
+    h->dtype = cf.dtype;
+    char* p = base + sizeof(rlt_snapshot_header);
+    HIP_TRY(hipMemcpyAsync(&h->pos, st->pos + r, 4, hipMemcpyDeviceToHost, s));
+    HIP_TRY(hipMemcpyAsync(&h->pending, st->pending + r, 4, hipMemcpyDeviceToHost, s));
+    HIP_TRY(hipMemcpyAsync(p, st->s + (size_t)r * cf.d_model, (size_t)cf.d_model * 4, hipMemcpyDeviceToHost, s));
+    p += (size_t)cf.d_model * 4;
+    if (rg.width) {
+      for (const void* ring : {(const void*)st->ring_k, (const void*)st->ring_v}) {
+        HIP_TRY(hipMemcpy2DAsync(p, rg.width, (const char*)ring + (size_t)r * rg.width, rg.pitch, rg.width,
+                                 rg.height, hipMemcpyDeviceToHost, s));
+        p += rg.width * rg.height;
+      }
+    }
+  }
+  HIP_TRY(hipStreamSynchronize(s));
+  return RLT_OK;
+}
+
+extern "C" int rlt_state_restore(rlt_ctx* c, rlt_state* st, const int32_t* rows_host, int32_t n, const void* src,
+                                 void* stream) {
+  if (!c || !src) return fail(RLT_EINVAL, "null context or source");
+  int rc = check_state(c, st);
+  if (rc) return rc;
+  if ((rc = check_rows_host(st, rows_host, n))) return rc;
+  size_t per = 0;
+  if ((rc = rlt_snapshot_bytes(&c->cfg, &per))) return rc;
+  const rlt_config& cf = c->cfg;
+  for (int i = 0; i < n; ++i) {
+    const rlt_snapshot_header* h = (const rlt_snapshot_header*)((const char*)src + (size_t)i * per);
+    if (h->magic != RLT_SNAPSHOT_MAGIC || h->layout != 1) return fail(RLT_EINVAL, "snapshot %d: not a snapshot", i);
+    if (h->n_layers != cf.n_layers || h->d_model != cf.d_model || h->window != cf.window || h->dtype != cf.dtype)
+      return fail(RLT_ESHAPE, "snapshot %d was taken under another configuration", i);
+    if (h->weights_version != cf.weights_version)
+      return fail(RLT_ESTALE, "snapshot %d has weights version %llu, the context %llu", i,
+                  (unsigned long long)h->weights_version, (unsigned long long)cf.weights_version);
+    if (h->pos < 0 || h->pos > c->max_ctx) return fail(RLT_EINVAL, "snapshot %d: position %d", i, h->pos);
+  }
+  hipStream_t s = (hipStream_t)stream;
+  const RingGeom rg = ring_geom(c, st);
+  for (int i = 0; i < n; ++i) {
+    const int r = rows_host[i];
+    const char* base = (const char*)src + (size_t)i * per;
+    const rlt_snapshot_header* h = (const rlt_snapshot_header*)base;
+    const char* p = base + sizeof(rlt_snapshot_header);
+    HIP_TRY(hipMemcpyAsync(st->pos + r, &h->pos, 4, hipMemcpyHostToDevice, s));
+    HIP_TRY(hipMemcpyAsync(st->pending + r, &h->pending, 4, hipMemcpyHostToDevice, s));
+    HIP_TRY(hipMemcpyAsync(st->s + (size_t)r * cf.d_model, p, (size_t)cf.d_model * 4, hipMemcpyHostToDevice, s));
+    p += (size_t)cf.d_model * 4;
+    if (rg.width) {
+      for (void* ring : {st->ring_k, st->ring_v}) {
+        HIP_TRY(hipMemcpy2DAsync((char*)ring + (size_t)r * rg.width, rg.pitch, p, rg.width, rg.width, rg.height,
+                                 hipMemcpyHostToDevice, s));
+        p += rg.width * rg.height;
+      }
+    }
+  }
+  HIP_TRY(hipStreamSynchronize(s));
+  return RLT_OK;
+}
+
+// ----------------------------------------------------------------------------
 // encoder memory [RLT §2.2, eq. (2.2)]
 // ----------------------------------------------------------------------------
 

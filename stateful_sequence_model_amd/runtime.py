@@ -220,6 +220,24 @@ class Decoder:
     def sync_error(self, stream=None) -> int:
         return A.rlt_sync_error(self.ctx, current_stream() if stream is None else stream)
 
+    # -- exact prefix snapshots ---------------------------------------------------
+    def snapshot(self, st: DecoderState, rows, stream=None) -> np.ndarray:
+        """Snapshots of the listed rows: a uint8 array [n, bytes per row]
+        (header, s, SWA cache), complete when this returns."""
+        rows = np.ascontiguousarray(rows, dtype=np.int32)
+        per = A.rlt_snapshot_bytes(self._cfg_c)
+        buf = np.zeros((len(rows), per), dtype=np.uint8)
+        A.check(A.rlt_state_snapshot(self.ctx, st.c(), rows.ctypes.data, len(rows), buf.ctypes.data,
+                                     current_stream() if stream is None else stream), "rlt_state_snapshot")
+        return buf
+
+    def restore(self, st: DecoderState, rows, snap: np.ndarray, stream=None) -> int:
+        """Restore snapshot i into row rows[i]; returns the status code."""
+        rows = np.ascontiguousarray(rows, dtype=np.int32)
+        snap = np.ascontiguousarray(snap, dtype=np.uint8)
+        return A.rlt_state_restore(self.ctx, st.c(), rows.ctypes.data, len(rows), snap.ctypes.data,
+                                   current_stream() if stream is None else stream)
+
     # -- encoder memory ------------------------------------------------------
     def memory_weights(self, params: Dict[str, object]) -> "MemoryWeights":
         """Device copies of the memory-map weights keyed "memory.{g}.norm_e",

@@ -28,7 +28,8 @@ def test_library_exports_every_declared_function():
     decl = _declared()
     assert {"rlt_create", "rlt_destroy", "rlt_state_layout", "rlt_last_error", "rlt_init_state",
             "rlt_decoder_step", "rlt_replay_sequence", "rlt_score_logprobs", "rlt_sync_error",
-            "rlt_memory_append", "rlt_memory_prefill", "rlt_dbg_gemm"} <= decl
+            "rlt_memory_append", "rlt_memory_prefill", "rlt_snapshot_bytes", "rlt_state_snapshot",
+            "rlt_state_restore", "rlt_dbg_gemm"} <= decl
     for name in decl:
         assert hasattr(L, name), name
     assert decl == set(_abi.exported_symbols())
@@ -41,7 +42,7 @@ def test_ctypes_layout_matches_header(tmp_path):
     structs = {"rlt_config": _abi.rlt_config, "rlt_weights": _abi.rlt_weights, "rlt_state": _abi.rlt_state,
                "rlt_memory": _abi.rlt_memory, "rlt_step_io": _abi.rlt_step_io,
                "rlt_replay_io": _abi.rlt_replay_io, "rlt_score_io": _abi.rlt_score_io,
-               "rlt_memory_weights": _abi.rlt_memory_weights}
+               "rlt_memory_weights": _abi.rlt_memory_weights, "rlt_snapshot_header": _abi.rlt_snapshot_header}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "rlt.h"', "int main(void){"]
     for sname, cls in structs.items():
         lines.append('printf("%s %%zu\\n", sizeof(%s));' % (sname, sname))
@@ -108,4 +109,18 @@ def test_null_arguments_are_rejected():
     assert L.rlt_init_state(None, None, None, 0, 0, None) == _abi.RLT_EINVAL
     assert L.rlt_sync_error(None, None) == _abi.RLT_EINVAL
     assert L.rlt_memory_append(None, None, None, 0, 0, None, 0, None, None) == _abi.RLT_EINVAL
+    assert L.rlt_state_snapshot(None, None, None, 0, None, None) == _abi.RLT_EINVAL
+    assert L.rlt_state_restore(None, None, None, 0, None, None) == _abi.RLT_EINVAL
     assert L.rlt_memory_prefill(None, None, None, 0, 0, None, None, 0, 0, None) == _abi.RLT_EINVAL
+
+
+def test_snapshot_size_and_magic():
+    """One row's snapshot: header, s (float32), both SWA caches; the magic
+    constant spells "RLTS" in memory order."""
+    from stateful_sequence_model_amd import _abi
+    import ctypes as C
+    cfg = _cfg()
+    per = _abi.rlt_snapshot_bytes(cfg)
+    assert C.sizeof(_abi.rlt_snapshot_header) == 64
+    assert per == 64 + 64 * 4 + 2 * 2 * 3 * 64 * 4   # L=2, W-1=3, d=64, float32
+    assert _abi.RLT_SNAPSHOT_MAGIC.to_bytes(4, "little") == b"RLTS"

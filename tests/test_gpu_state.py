@@ -316,3 +316,37 @@ def test_persistent_step_equals_separate_kernels():
     assert torch.equal(lp[0].isnan(), lp[1].isnan())
     assert torch.equal(torch.nan_to_num(lp[0]), torch.nan_to_num(lp[1]))
     assert torch.equal(ref.st.s, fz.st.s)
+
+
+def test_snapshot_restore_resumes_bit_exact():
+    """§6 exact prefix snapshot: rows saved after 12 transitions and restored
+    into a fresh state continue bit for bit like the uninterrupted rows
+    (same launch shape); the restored bytes re-snapshot identically; bad
+    headers are rejected before anything is written."""
+    require_gpu()
+    from stateful_sequence_model_amd import _abi
+    wl = synth.SMALL.with_(B=4, T=40)
+    a = GpuRun(wl)
+    a.init()
+    a.run(12)
+    rows = [1, 3]
+    snap = a.dec.snapshot(a.st, rows)
+    hdr = _abi.rlt_snapshot_header.from_buffer_copy(bytes(snap[0, :64]))
+    assert hdr.magic == _abi.RLT_SNAPSHOT_MAGIC and hdr.pos == 12 and hdr.pending == -1
+    SA, ZA = a.run(8, idx=rows)
+    b = GpuRun(wl, raw=a.raw)
+    b.init()
+    assert b.dec.restore(b.st, rows, snap) == 0
+    assert np.array_equal(b.dec.snapshot(b.st, rows), snap)
+    SB, ZB = b.run(8, idx=rows)
+    assert np.array_equal(SA, SB) and np.array_equal(ZA, ZB)
+    assert torch.equal(a.st.s[rows], b.st.s[rows])
+    # rejected headers leave the state untouched
+    before = b.dec.snapshot(b.st, rows)
+    for field, value, code in (("magic", 0, _abi.RLT_EINVAL), ("n_layers", wl.L + 1, _abi.RLT_ESHAPE),
+                               ("weights_version", 99, _abi.RLT_ESTALE)):
+        bad = snap.copy()
+        h = _abi.rlt_snapshot_header.from_buffer(bad[1])
+        setattr(h, field, value)
+        assert b.dec.restore(b.st, rows, bad) == code, field
+    assert np.array_equal(b.dec.snapshot(b.st, rows), before)
