@@ -7,4 +7,4 @@ with the GPU library; see ``rlt_oracle`` for the readings it fixes.
 from .rlt_oracle import (Config, Memory, Oracle, State, attend, behaviour_logprobs, build_memory,
                          importance_ratio, memory_entry, replay, retained_positions, ring_slot, rms_norm,
                          rope, rope_angles, sample, sigmoid, silu, state_from_ring,
-                         state_to_ring, topk_order, window_positions)
+                         state_to_ring, topk_order, trajectory_log_ratio, window_positions)

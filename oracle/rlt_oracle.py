@@ -27,6 +27,18 @@ itself and are fixed here as a specification):
   * FFN is SwiGLU: W_down (silu(W_gate h) * (W_up h)).
   * Projections carry no bias; the merge gate carries b_g.
   * Memory group of layer l (0-based): floor(l * G / L_D).
+  * Merge variants [RLT §2.5, text after eq. (2.11)]: a scalar gate is one
+    gate value per token, sigmoid(w_g . [e; r] + b_g) with w_g a single row,
+    shared by every channel; a low-rank W_s is the product U V (U [d, k],
+    V [k, d]), applied as U (V r).
+  * Sublayer orders [RLT §2.5, text after eq. (2.16)]: a block applies its
+    SWA ("s"), cross-attention ("x") and FFN ("f") sublayers, each a pre-norm
+    residual update with its own RMSNorm, in the order of a permutation
+    string; "sxf" is eqs. (2.14)-(2.16). The SWA key/value of the current
+    token are formed from the SWA sublayer's own input.
+  * Top-p behaviour sampling [RLT §5.3]: temperature first, then top-k, then
+    the nucleus: the shortest prefix of the (logit desc, id asc) order whose
+    renormalised probability mass reaches p; mu renormalises over it.
   * Memory construction [RLT §2.2, eq. (2.2)]: one RMSNorm_E per group g
     (gain norm_e^g) feeds both maps; the key map is W_K^g followed by the
     same rotary transform as the decoder queries, at the entry's own
@@ -114,6 +126,9 @@ class Config:
     eps: float = 1e-6
     rope_theta: float = 10000.0
     pos: str = "rope"          # "rope" or "none"
+    gate: str = "vector"       # merge gate: "vector" [eq. (2.10)] or "scalar"
+    ws_rank: int = 0           # 0: full W_s; k > 0: W_s = U V of rank k
+    order: str = "sxf"         # sublayer order of a block
 
     def group_of(self, layer: int) -> int:
         return (layer * self.G) // self.L
@@ -223,12 +238,20 @@ class Oracle:
         c, w = self.cfg, self.w
         if c.merge == "gated":
             r = rms_norm(s_prev, w["merge.norm"], c.eps)
-            g = sigmoid(w["merge.wg"] @ np.concatenate([e, r]) + w["merge.bg"])
-            return e + c.alpha * g * (w["merge.ws"] @ r)
+            g = self._gate(np.concatenate([e, r]))
+            proj = w["merge.ws"] @ r if c.ws_rank == 0 else w["merge.ws_u"] @ (w["merge.ws_v"] @ r)
+            return e + c.alpha * g * proj
         if c.merge == "convex":
-            g = sigmoid(w["merge.wg"] @ np.concatenate([e, s_prev]) + w["merge.bg"])
+            g = self._gate(np.concatenate([e, s_prev]))
             return g * e + (1.0 - g) * s_prev
         raise ValueError(c.merge)
+
+    def _gate(self, x: np.ndarray):
+        """sigmoid(W_g x + b_g): a vector [d], or one scalar for the scalar gate."""
+        w = self.w
+        if self.cfg.gate == "scalar":
+            return float(sigmoid(np.reshape(w["merge.wg"], -1) @ x + float(np.reshape(w["merge.bg"], -1)[0])))
+        return sigmoid(w["merge.wg"] @ x + w["merge.bg"])
 
     def _pos(self, x: np.ndarray, t: int) -> np.ndarray:
         c = self.cfg
@@ -238,7 +261,17 @@ class Oracle:
     def block(self, l: int, z: np.ndarray, t: int, hist: Dict[int, Tuple[np.ndarray, np.ndarray]],
               mem: Memory, trace: Optional[dict] = None) -> np.ndarray:
         """Decoder block l at position t: SWA, then cross-attention, then FFN
-        [RLT §2.5, eqs. (2.12)-(2.16)]. Updates ``hist`` (the layer's cache)."""
+        [RLT §2.5, eqs. (2.12)-(2.16)], or the sublayers in the configured
+        order. Updates ``hist`` (the layer's cache)."""
+        if self.cfg.order != "sxf":
+            for kind in self.cfg.order:
+                if kind == "s":
+                    z = self._swa(l, z, t, hist)
+                elif kind == "x":
+                    z = self._cross(l, z, t, mem)
+                else:
+                    z = self._ffn(l, z)
+            return z
         c, w = self.cfg, self.w
         p = "layer.%d." % l
         # (2.12)-(2.13): current KV formed first, from the layer input
@@ -279,6 +312,37 @@ class Oracle:
             trace.setdefault("a", []).append(a)
             trace.setdefault("z", []).append(z_out)
         return z_out
+
+    # sublayers (each a pre-norm residual update) for the other orders
+    def _swa(self, l: int, z: np.ndarray, t: int, hist) -> np.ndarray:
+        c, w = self.cfg, self.w
+        p = "layer.%d." % l
+        h = rms_norm(z, w[p + "norm_s"], c.eps)
+        q, k, v = self._pos(w[p + "wq"] @ h, t), self._pos(w[p + "wk"] @ h, t), w[p + "wv"] @ h
+        win = window_positions(t, c.W)
+        o = attend(q, np.stack([hist[j][0] for j in win[:-1]] + [k]),
+                   np.stack([hist[j][1] for j in win[:-1]] + [v]), c.H, c.dh)
+        hist[t] = (k, v)
+        keep = set(retained_positions(t, c.W))
+        for j in list(hist.keys()):
+            if j not in keep:
+                del hist[j]
+        return z + w[p + "wo"] @ o
+
+    def _cross(self, l: int, z: np.ndarray, t: int, mem: Memory) -> np.ndarray:
+        c, w = self.cfg, self.w
+        p = "layer.%d." % l
+        g = c.group_of(l)
+        qm = self._pos(w[p + "wqm"] @ rms_norm(z, w[p + "norm_m"], c.eps), t)
+        om = attend(qm, np.asarray(mem.k[g][:t], dtype=self.dtype), np.asarray(mem.v[g][:t], dtype=self.dtype),
+                    c.H, c.dh)
+        return z + w[p + "wom"] @ om
+
+    def _ffn(self, l: int, z: np.ndarray) -> np.ndarray:
+        c, w = self.cfg, self.w
+        p = "layer.%d." % l
+        hd = rms_norm(z, w[p + "norm_d"], c.eps)
+        return z + w[p + "w_down"] @ (silu(w[p + "w_gate"] @ hd) * (w[p + "w_up"] @ hd))
 
     # -- F_t --------------------------------------------------------------
     def transition(self, state: State, e: np.ndarray, mem: Memory,
@@ -337,25 +401,33 @@ def topk_order(z: np.ndarray, k: int) -> np.ndarray:
     return ids[:k]
 
 
-def behaviour_logprobs(z: np.ndarray, tau: float, k: int) -> Tuple[np.ndarray, np.ndarray]:
+def behaviour_logprobs(z: np.ndarray, tau: float, k: int, p: float = 1.0) -> Tuple[np.ndarray, np.ndarray]:
     """mu over the truncated support: temperature tau, top-k truncation,
-    renormalisation (all three enter the behaviour probability, [RLT §5.3]).
+    optional nucleus (top-p) truncation, renormalisation (all of them enter
+    the behaviour probability, [RLT §5.3]). p outside (0, 1) means no
+    nucleus.
 
-    Returns (support ids in top-k order, log mu of each)."""
+    Returns (support ids in (logit desc, id asc) order, log mu of each)."""
     V = z.shape[0]
     k = V if (k <= 0 or k > V) else k
     ids = topk_order(z, k)
     zz = z[ids].astype(np.float64) / tau
     m = np.max(zz)
     lse = m + np.log(np.sum(np.exp(zz - m)))
+    if 0.0 < p < 1.0:
+        mass = np.cumsum(np.exp(zz - lse))
+        n = int(np.searchsorted(mass, p, side="left")) + 1   # shortest prefix with mass >= p
+        n = min(n, len(ids))
+        ids, zz = ids[:n], zz[:n]
+        lse = m + np.log(np.sum(np.exp(zz - m)))
     return ids, zz - lse
 
 
-def sample(z: np.ndarray, tau: float, k: int, u: float) -> Tuple[int, float]:
+def sample(z: np.ndarray, tau: float, k: int, u: float, p: float = 1.0) -> Tuple[int, float]:
     """Inverse-CDF draw from mu with a given uniform u in [0, 1): the first
-    support id (in top-k order) whose cumulative unnormalised weight exceeds
-    u times the total. Returns (token, log mu(token))."""
-    ids, lmu = behaviour_logprobs(z, tau, k)
+    support id (in support order) whose cumulative unnormalised weight
+    exceeds u times the total. Returns (token, log mu(token))."""
+    ids, lmu = behaviour_logprobs(z, tau, k, p)
     w = np.exp(lmu - np.max(lmu))
     cum = np.cumsum(w)
     i = int(np.searchsorted(cum, u * cum[-1], side="right"))
@@ -366,6 +438,15 @@ def sample(z: np.ndarray, tau: float, k: int, u: float) -> Tuple[int, float]:
 def importance_ratio(logp: float, logmu: float) -> float:
     """r_i = exp(log p_Theta(y_i|.) - log mu(y_i|.)) [RLT §5.3, eq. (5.5)]."""
     return math.exp(logp - logmu)
+
+
+def trajectory_log_ratio(logp: Sequence[float], logmu: Sequence[float]) -> float:
+    """log of the trajectory importance weight prod_i r_i over a response
+    [RLT §5.3]: sum_i (log p_i - log mu_i), in response order."""
+    acc = 0.0
+    for a, b in zip(logp, logmu):
+        acc += float(a) - float(b)
+    return acc
 
 
 # ----------------------------------------------------------------------------

@@ -140,6 +140,10 @@ class Workload:
     temperature: float = 1.0
     top_k: int = 0
     gain_std: float = 0.1  # norm gains are 1 + gain_std * normal
+    gate: str = "vector"   # merge gate: "vector" (eq 2.10) or "scalar"
+    ws_rank: int = 0       # 0: full W_s; k > 0: W_s = U V of rank k
+    order: str = "sxf"     # sublayer order of a block
+    top_p: float = 1.0     # nucleus of the behaviour sampler (1 = none)
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
@@ -167,10 +171,15 @@ PRESETS = {w.name: w for w in (TINY, SMALL, MID, REF, RAGGED)}
 def weight_shapes(wl: Workload) -> Dict[str, tuple]:
     """Natural ([out, in]) shapes of every parameter, keyed by name."""
     d, F, V = wl.d, wl.F, wl.V
-    shapes = {"s_star": (d,), "merge.wg": (d, 2 * d), "merge.bg": (d,)}
+    gw = 1 if wl.gate == "scalar" else d
+    shapes = {"s_star": (d,), "merge.wg": (gw, 2 * d), "merge.bg": (gw,)}
     if wl.merge == "gated":
         shapes["merge.norm"] = (d,)
-        shapes["merge.ws"] = (d, d)
+        if wl.ws_rank:
+            shapes["merge.ws_u"] = (d, wl.ws_rank)
+            shapes["merge.ws_v"] = (wl.ws_rank, d)
+        else:
+            shapes["merge.ws"] = (d, d)
     for l in range(wl.L):
         p = "layer.%d." % l
         shapes.update({p + "norm_s": (d,), p + "wq": (d, d), p + "wk": (d, d), p + "wv": (d, d),
@@ -183,7 +192,7 @@ def weight_shapes(wl: Workload) -> Dict[str, tuple]:
 
 
 def is_matrix(name: str) -> bool:
-    return name.split(".")[-1] in ("wg", "ws", "wq", "wk", "wv", "wo", "wqm", "wom",
+    return name.split(".")[-1] in ("wg", "ws", "ws_u", "ws_v", "wq", "wk", "wv", "wo", "wqm", "wom",
                                    "w_gate", "w_up", "w_down", "w")
 
 

@@ -22,7 +22,8 @@ def widen(a: np.ndarray) -> np.ndarray:
 
 def oracle_config(wl: synth.Workload, **over) -> Config:
     kw = dict(L=wl.L, d=wl.d, H=wl.H, dh=wl.dh, W=wl.W, G=wl.G, F=wl.F, V=wl.V, merge=wl.merge,
-              alpha=wl.alpha, eps=wl.eps, rope_theta=wl.rope_theta, pos=wl.pos)
+              alpha=wl.alpha, eps=wl.eps, rope_theta=wl.rope_theta, pos=wl.pos, gate=wl.gate,
+              ws_rank=wl.ws_rank, order=wl.order)
     kw.update(over)
     return Config(**kw)
 

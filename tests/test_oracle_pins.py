@@ -577,3 +577,120 @@ def test_build_memory_groups_and_positions():
                                 mw["memory.%d.wv" % g])
             assert np.array_equal(mem.k[g][t - 1], k) and np.array_equal(mem.v[g][t - 1], v)
     assert not np.allclose(mem.v[0], mem.v[1])
+
+
+# ---------------------------------------------------------------------------
+# variants: merge gate / rank [RLT §2.5], sublayer order, top-p and the
+# trajectory weight [RLT §5.3]
+# ---------------------------------------------------------------------------
+
+def _variant_oracle(wl, raw):
+    from tests.helpers import oracle_config, oracle_weights
+    return Oracle(oracle_config(wl), oracle_weights(raw))
+
+
+def test_scalar_gate_equals_constant_vector_gate():
+    """A scalar gate with w_g = 0, b_g = beta is the vector gate with W_g = 0
+    and b_g = beta in every channel (both give sigmoid(beta) everywhere)."""
+    wl_v = synth.SMALL.with_(L=1, d=64, H=2, dh=32, F=128, V=64, G=1, dtype="f32")
+    wl_s = wl_v.with_(gate="scalar")
+    rv, rs = synth.make_weights(wl_v), synth.make_weights(wl_s)
+    beta = 0.37
+    rv["merge.wg"][:] = 0
+    rv["merge.bg"][:] = beta
+    rs["merge.wg"][:] = 0
+    rs["merge.bg"][:] = beta
+    for k in rv:
+        if k not in ("merge.wg", "merge.bg"):
+            rs[k] = rv[k]
+    ov, os_ = _variant_oracle(wl_v, rv), _variant_oracle(wl_s, rs)
+    e, s = _rand(64, 71), _rand(64, 72)
+    assert np.allclose(ov.merge(e, s), os_.merge(e, s), rtol=1e-13, atol=1e-13)
+    # and the scalar really is one value: scaling one channel of W_s r
+    # scales that channel's feedback only
+    u0 = os_.merge(e, s) - e
+    rs2 = dict(rs)
+    rs2["merge.ws"] = rs["merge.ws"].copy()
+    rs2["merge.ws"][5] *= 2
+    u1 = _variant_oracle(wl_s, rs2).merge(e, s) - e
+    assert np.allclose(u1[5], 2 * u0[5]) and np.allclose(np.delete(u1, 5), np.delete(u0, 5))
+
+
+def test_low_rank_ws_equals_full_product():
+    """W_s = U V given as factors equals the full matrix U @ V (the full path
+    is pinned by the merge tests above)."""
+    wl_f = synth.SMALL.with_(L=1, d=64, H=2, dh=32, F=128, V=64, G=1, dtype="f32")
+    wl_r = wl_f.with_(ws_rank=32)
+    rf, rr = synth.make_weights(wl_f), synth.make_weights(wl_r)
+    for k in rf:
+        if k != "merge.ws":
+            rr[k] = rf[k]
+    rf["merge.ws"] = (rr["merge.ws_u"].astype(np.float64) @ rr["merge.ws_v"].astype(np.float64)).astype(np.float32)
+    e, s = _rand(64, 81), _rand(64, 82)
+    a = _variant_oracle(wl_f, rf).merge(e, s)
+    b = _variant_oracle(wl_r, rr).merge(e, s)
+    assert np.allclose(a, b, rtol=1e-6, atol=1e-7)
+
+
+def _run_steps(orc, wl, n=5):
+    mem = memory_of(wl, 0, T=n)
+    st = orc.initial_state()
+    out = []
+    for t in range(1, n + 1):
+        st = orc.transition(st, e_of(wl, 0, T=n)[t - 1], mem)
+        out.append(st.s)
+    return np.array(out)
+
+
+def test_sublayer_order_with_identity_sublayers():
+    """With the FFN switched off (W_down = 0) the FFN sublayer is the
+    identity, so "sfx" equals "sxf"; with the cross-attention output
+    projection zero, "xsf" equals "sxf". Orders whose non-trivial sublayers
+    are permuted differ."""
+    wl = synth.SMALL.with_(L=2, d=64, H=2, dh=32, F=128, V=64, G=1, W=4, dtype="f32")
+    raw = synth.make_weights(wl)
+    no_ffn = dict(raw)
+    no_x = dict(raw)
+    for l in range(wl.L):
+        no_ffn["layer.%d.w_down" % l] = np.zeros_like(raw["layer.%d.w_down" % l])
+        no_x["layer.%d.wom" % l] = np.zeros_like(raw["layer.%d.wom" % l])
+    ref_f = _run_steps(_variant_oracle(wl, no_ffn), wl)
+    assert np.allclose(_run_steps(_variant_oracle(wl.with_(order="sfx"), no_ffn), wl), ref_f, rtol=1e-12, atol=1e-12)
+    ref_x = _run_steps(_variant_oracle(wl, no_x), wl)
+    assert np.allclose(_run_steps(_variant_oracle(wl.with_(order="xsf"), no_x), wl), ref_x, rtol=1e-12, atol=1e-12)
+    full = _run_steps(_variant_oracle(wl, raw), wl)
+    assert rel_l2(_run_steps(_variant_oracle(wl.with_(order="fxs"), raw), wl), full) > 1e-4
+
+
+def test_top_p_closed_forms():
+    """Uniform logits: the nucleus at p = 1/2 is the first V/2 ids (id order)
+    with mu = 2/V each; p -> 0 keeps the argmax only (mu = 1); p = 1 is no
+    nucleus; p is applied after top-k (mass renormalised over the top-k)."""
+    V = 16
+    ids, lmu = behaviour_logprobs(np.zeros(V), 1.0, 0, 0.5)
+    assert ids.tolist() == list(range(V // 2)) and np.allclose(lmu, math.log(2.0 / V))
+    z = _rand(V, 91)
+    ids, lmu = behaviour_logprobs(z, 0.7, 0, 1e-9)
+    assert ids.tolist() == [int(np.argmax(z))] and abs(lmu[0]) < 1e-15
+    a = behaviour_logprobs(z, 0.7, 5, 1.0)
+    b = behaviour_logprobs(z, 0.7, 5)
+    assert np.array_equal(a[0], b[0]) and np.allclose(a[1], b[1])
+    # explicit: logits 3, 2, 1, 0 at tau = 1 -> p = e^3, e^2, e^1, 1 over S
+    z4 = np.array([0.0, 3.0, 1.0, 2.0])
+    w = np.exp([3.0, 2.0, 1.0, 0.0])
+    P = w / w.sum()                        # ordered ids 1, 3, 2, 0
+    ids, lmu = behaviour_logprobs(z4, 1.0, 0, P[0] + P[1] - 1e-12)
+    assert ids.tolist() == [1, 3] and np.allclose(np.exp(lmu), w[:2] / w[:2].sum())
+    ids, lmu = behaviour_logprobs(z4, 1.0, 3, 0.999)  # top-3 first, then all 3 needed
+    assert ids.tolist() == [1, 3, 2]
+
+
+def test_trajectory_log_ratio_is_log_of_product():
+    from oracle import trajectory_log_ratio
+    lp = _rand(7, 101) - 3
+    lm = _rand(7, 102) - 3
+    prod = 1.0
+    for a, b in zip(lp, lm):
+        prod *= importance_ratio(a, b)
+    assert math.isclose(math.exp(trajectory_log_ratio(lp, lm)), prod, rel_tol=1e-12)
+    assert trajectory_log_ratio([], []) == 0.0
