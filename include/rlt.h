@@ -55,6 +55,14 @@ enum {
 enum { RLT_F32 = 0, RLT_BF16 = 1 };
 enum { RLT_MERGE_GATED = 0, RLT_MERGE_CONVEX = 1 };
 enum { RLT_POS_NONE = 0, RLT_POS_ROPE = 1 };
+/* merge gate [RLT §2.5, text after eq. (2.11)]: one gate per channel
+ * (eq. (2.10)) or one scalar gate per token, sigmoid(w_g . [e; r] + b_g) */
+enum { RLT_GATE_VECTOR = 0, RLT_GATE_SCALAR = 1 };
+/* sublayer order of every block [RLT §2.5, text after eq. (2.16)]: S = SWA,
+ * X = cross-attention, F = FFN, each a pre-norm residual update with its own
+ * RMSNorm; SXF is eqs. (2.14)-(2.16) */
+enum { RLT_ORDER_SXF = 0, RLT_ORDER_SFX = 1, RLT_ORDER_XSF = 2, RLT_ORDER_XFS = 3, RLT_ORDER_FSX = 4,
+       RLT_ORDER_FXS = 5 };
 
 /* Model configuration.
  * merge_kind GATED:  r = RMSNorm_s(s_{t-1}); g = sigmoid(W_g [e; r] + b_g);
@@ -83,6 +91,9 @@ typedef struct rlt_config {
   float rms_eps;       /* RMSNorm: x / sqrt(mean(x^2) + eps) * gain */
   float rope_theta;
   uint64_t weights_version; /* states must carry the same version */
+  int32_t merge_gate;  /* RLT_GATE_* (SCALAR: gated merge only) */
+  int32_t merge_rank;  /* 0: full W_s; k > 0 (multiple of 32, <= d_ffn): W_s = U V of rank k */
+  int32_t block_order; /* RLT_ORDER_* */
 } rlt_config;
 
 /* Parameters (device pointers, natural layout). Per-layer fields are HOST
@@ -107,6 +118,9 @@ typedef struct rlt_weights {
   const void* const* w_down;   /* [d][F]: FFN(h) = W_down(silu(W_gate h) (.) W_up h) */
   const float* out_norm;       /* [d]    gain of RMSNorm_o [eq. (2.6)] */
   const void* w_out;           /* [V][d] W_o */
+  const void* merge_ws_u;      /* [d][k] U of a rank-k W_s (merge_rank = k > 0) */
+  const void* merge_ws_v;      /* [k][d] V of a rank-k W_s; merge_ws is unused then.
+                                  A scalar gate uses merge_wg [1][2d], merge_bg [1]. */
 } rlt_weights;
 
 /* Decoder state of B_cap independent rows [RLT §2.1: H_t = (s_t, C_t^D)].
@@ -173,6 +187,8 @@ typedef struct rlt_step_io {
   float* sample_logmu;       /* [n] log mu(sample_tok) */
   float* z_trace;            /* [L_D][n][d] z after each block (debug), or NULL */
   int32_t flags;             /* RLT_STEP_* */
+  float top_p;               /* nucleus of the behaviour distribution applied after
+                                top-k (needs top_k >= 1); outside (0, 1): none */
 } rlt_step_io;
 
 /* Current-policy replay from H_0 [RLT App. A.4, eq. (2.7)]: for each
@@ -210,6 +226,7 @@ typedef struct rlt_score_io {
   float* logmu;              /* [n] log mu(token) under (tau, top_k), -inf off-support; or NULL */
   const float* logmu_behaviour; /* [n] recorded behaviour log-probs, or NULL */
   float* ratio;              /* [n] exp(logp - logmu_behaviour), or NULL */
+  float top_p;               /* nucleus after top-k as in rlt_step_io; outside (0, 1): none */
 } rlt_score_io;
 
 typedef struct rlt_ctx rlt_ctx;
@@ -248,6 +265,15 @@ int rlt_score_logprobs(rlt_ctx* ctx, const rlt_score_io* io, void* stream);
 
 /* Wait for `stream`, then return (and clear) any device-detected error. */
 int rlt_sync_error(rlt_ctx* ctx, void* stream);
+
+/* Log of the trajectory importance weight prod_i r_i [RLT §5.3, text after
+ * eq. (5.5)] of B sequences: out[b] = sum over t = split_host[b] ..
+ * len_host[b] - 1 of logp[b * logp_stride_b + t] - logmu[b * logmu_stride_b + t]
+ * (the positions a replay scores), summed in t order. HOST len/split arrays,
+ * device logp / logmu / out (float32). */
+int rlt_trajectory_log_ratio(rlt_ctx* ctx, int32_t B, const int32_t* len_host, const int32_t* split_host,
+                             const float* logp, int64_t logp_stride_b, const float* logmu,
+                             int64_t logmu_stride_b, float* out, void* stream);
 
 /* Exact prefix snapshot of decoder rows [RLT §6]: the complete decoder
  * state H_t = (s_t, C_t^D) of a row with its position metadata and the model

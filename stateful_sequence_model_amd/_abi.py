@@ -19,6 +19,8 @@ RLT_MERGE_GATED, RLT_MERGE_CONVEX = 0, 1
 RLT_POS_NONE, RLT_POS_ROPE = 0, 1
 RLT_STEP_GRAPH, RLT_STEP_DEFER = 1, 2
 RLT_INIT_POISON = 1
+RLT_GATE_VECTOR, RLT_GATE_SCALAR = 0, 1
+ORDERS = ("sxf", "sfx", "xsf", "xfs", "fsx", "fxs")   # RLT_ORDER_SXF .. RLT_ORDER_FXS
 
 STATUS_NAMES = {0: "RLT_OK", -1: "RLT_EINVAL", -2: "RLT_ESHAPE", -3: "RLT_EPREFIX", -4: "RLT_ESTALE",
                 -5: "RLT_EPENDING", -6: "RLT_EHIP", -7: "RLT_ENOMEM", -8: "RLT_EUNSUPPORTED"}
@@ -31,7 +33,7 @@ class rlt_config(C.Structure):
     _fields_ = [("n_layers", i32), ("d_model", i32), ("n_heads", i32), ("d_head", i32), ("window", i32),
                 ("n_groups", i32), ("d_ffn", i32), ("vocab", i32), ("merge_kind", i32), ("pos_kind", i32),
                 ("dtype", i32), ("alpha", f32), ("rms_eps", f32), ("rope_theta", f32),
-                ("weights_version", u64)]
+                ("weights_version", u64), ("merge_gate", i32), ("merge_rank", i32), ("block_order", i32)]
 
 
 class rlt_weights(C.Structure):
@@ -39,7 +41,7 @@ class rlt_weights(C.Structure):
                 ("norm_s", C.POINTER(P)), ("wq", C.POINTER(P)), ("wk", C.POINTER(P)), ("wv", C.POINTER(P)),
                 ("wo", C.POINTER(P)), ("norm_m", C.POINTER(P)), ("wqm", C.POINTER(P)), ("wom", C.POINTER(P)),
                 ("norm_d", C.POINTER(P)), ("w_gate", C.POINTER(P)), ("w_up", C.POINTER(P)),
-                ("w_down", C.POINTER(P)), ("out_norm", P), ("w_out", P)]
+                ("w_down", C.POINTER(P)), ("out_norm", P), ("w_out", P), ("merge_ws_u", P), ("merge_ws_v", P)]
 
 
 class rlt_state(C.Structure):
@@ -55,7 +57,7 @@ class rlt_step_io(C.Structure):
     _fields_ = [("n", i32), ("rows", P), ("e", P), ("mem", rlt_memory), ("consume_tok", P), ("s_out", P),
                 ("logits", P), ("argmax", P), ("score_tok", P), ("logp", P), ("uniform", P),
                 ("temperature", f32), ("top_k", i32), ("sample_tok", P), ("sample_logmu", P),
-                ("z_trace", P), ("flags", i32)]
+                ("z_trace", P), ("flags", i32), ("top_p", f32)]
 
 
 class rlt_replay_io(C.Structure):
@@ -67,7 +69,7 @@ class rlt_replay_io(C.Structure):
 
 class rlt_score_io(C.Structure):
     _fields_ = [("n", i32), ("s", P), ("tokens", P), ("logp", P), ("temperature", f32), ("top_k", i32),
-                ("logmu", P), ("logmu_behaviour", P), ("ratio", P)]
+                ("logmu", P), ("logmu_behaviour", P), ("ratio", P), ("top_p", f32)]
 
 
 class rlt_snapshot_header(C.Structure):
@@ -96,6 +98,7 @@ _SIGS = {
     "rlt_replay_sequence": (C.c_int, [P, C.POINTER(rlt_state), C.POINTER(rlt_replay_io), P]),
     "rlt_score_logprobs": (C.c_int, [P, C.POINTER(rlt_score_io), P]),
     "rlt_sync_error": (C.c_int, [P, P]),
+    "rlt_trajectory_log_ratio": (C.c_int, [P, i32, P, P, P, i64, P, i64, P, P]),
     "rlt_snapshot_bytes": (C.c_int, [C.POINTER(rlt_config), C.POINTER(C.c_size_t)]),
     "rlt_state_snapshot": (C.c_int, [P, C.POINTER(rlt_state), P, i32, P, P]),
     "rlt_state_restore": (C.c_int, [P, C.POINTER(rlt_state), P, i32, P, P]),
@@ -180,6 +183,11 @@ def rlt_score_logprobs(ctx: int, io: rlt_score_io, stream: int) -> int:
 
 def rlt_sync_error(ctx: int, stream: int) -> int:
     return lib().rlt_sync_error(ctx, stream)
+
+
+def rlt_trajectory_log_ratio(ctx: int, B: int, len_host, split_host, logp: int, logp_sb: int, logmu: int,
+                             logmu_sb: int, out: int, stream: int) -> int:
+    return lib().rlt_trajectory_log_ratio(ctx, B, len_host, split_host, logp, logp_sb, logmu, logmu_sb, out, stream)
 
 
 def rlt_snapshot_bytes(cfg: rlt_config) -> int:

@@ -117,6 +117,10 @@ struct Epi {
         z[cb] = zb;
         return produce(m, ca, za, cb, zb);
       }
+      case EPI_STORE_T:
+        ((T*)a.out_k)[(int64_t)m * a.ldo + ca] = from_f<T>(va * rs);
+        ((T*)a.out_k)[(int64_t)m * a.ldo + cb] = from_f<T>(vb * rs);
+        return 0.f;
       case EPI_MEMKV: {
         const int t = a.rows.t_row[m];
         if (t <= 0) return 0.f;

@@ -197,6 +197,22 @@ __global__ void k_mem_commit(const int* rows, int n, const int* t_row, int* mem_
   if (t_row[i] > 0) mem_len[rows[i]] = t_row[i];
 }
 
+// trajectory log-weight of sequence blockIdx.x: thread i takes positions
+// first + i, first + i + 256, ...; the 256 partial sums are added in a fixed
+// order
+__global__ __launch_bounds__(256) void k_traj_ratio(const int* first, const int* last, const float* logp,
+                                                    int64_t logp_sb, const float* logmu, int64_t logmu_sb,
+                                                    float* out) {
+  __shared__ float scratch[16];
+  const int b = blockIdx.x;
+  const float* lp = logp + (int64_t)b * logp_sb;
+  const float* lm = logmu + (int64_t)b * logmu_sb;
+  float acc = 0.f;
+  for (int t = first[b] + threadIdx.x; t <= last[b]; t += 256) acc += lp[t] - lm[t];
+  acc = block_sum(acc, scratch);
+  if (threadIdx.x == 0) out[b] = acc;
+}
+
 // ---------------------------------------------------------------------------
 // readout: log-sum-exp, argmax, top-k behaviour distribution, sampling
 // one workgroup of RB threads per slot; thread i owns logits
@@ -399,6 +415,22 @@ __global__ __launch_bounds__(RB) void k_readout(ReadoutArgs a) {
     const float top = c_val[c_ord[0]];
     float total = 0.f;
     for (int r = 0; r < K; ++r) total += __expf((c_val[c_ord[r]] - top) * inv_tau);
+    if (a.top_p > 0.f && a.top_p < 1.f) {
+      // nucleus: the shortest prefix of the order whose mass reaches top_p
+      const float need = a.top_p * total;
+      float cum = 0.f;
+      int kk = K;
+      for (int r = 0; r < K; ++r) {
+        cum += __expf((c_val[c_ord[r]] - top) * inv_tau);
+        if (cum >= need) {
+          kk = r + 1;
+          break;
+        }
+      }
+      K = kk;
+      total = 0.f;
+      for (int r = 0; r < K; ++r) total += __expf((c_val[c_ord[r]] - top) * inv_tau);
+    }
     const float ltot = logf(total);
     if (want_sample) {
       const float target = a.uniform[slot] * total;
@@ -505,6 +537,10 @@ void launch_mem_prep(int dtype, const Rows& rows, EIn e, int d, const float* gai
     hipLaunchKernelGGL(k_mem_prep<float>, dim3(rows.n), dim3(256), 0, s, rows, e, d, gain, (float*)A, ssq);
   else
     hipLaunchKernelGGL(k_mem_prep<uint16_t>, dim3(rows.n), dim3(256), 0, s, rows, e, d, gain, (uint16_t*)A, ssq);
+}
+void launch_traj_ratio(int B, const int* first, const int* last, const float* logp, int64_t logp_sb,
+                       const float* logmu, int64_t logmu_sb, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(k_traj_ratio, dim3(B), dim3(256), 0, s, first, last, logp, logp_sb, logmu, logmu_sb, out);
 }
 void launch_mem_setlen(const int* len, int B, int* mem_len, hipStream_t s) {
   hipLaunchKernelGGL(k_mem_setlen, dim3((B + 255) / 256), dim3(256), 0, s, len, B, mem_len);

@@ -24,6 +24,20 @@ __device__ __forceinline__ void merge_prep_body(const MiscArgs& a, int slot, flo
     ss = block_sum(ss, scratch);
     const float r = 1.0f / sqrtf(ss / (float)a.d + a.eps);
     for (int c = threadIdx.x; c < a.d; c += 256) X[a.d + c] = from_f<T>(s[c] * r * a.gain[c]);
+    if (a.wg) {
+      // scalar gate [text after eq. (2.11)]: g = sigmoid(w_g . [e; r] + b_g)
+      // over the product input as stored, one value for every channel
+      const T* wg = (const T*)a.wg;
+      float dot = 0.f;
+      for (int c = threadIdx.x; c < 2 * a.d; c += 256) {
+        const float x = c < a.d ? to_f<T>(e[c]) : to_f<T>(from_f<T>(s[c - a.d] * r * a.gain[c - a.d]));
+        dot = fmaf(to_f<T>(wg[c]), x, dot);
+      }
+      dot = block_sum(dot, scratch);
+      const float g = 1.0f / (1.0f + __expf(-(dot + a.bg[0])));
+      float* gb = a.gbuf + (int64_t)slot * a.d;
+      for (int c = threadIdx.x; c < a.d; c += 256) gb[c] = g;
+    }
   } else {
     for (int c = threadIdx.x; c < a.d; c += 256) X[a.d + c] = from_f<T>(s[c]);
   }

@@ -67,7 +67,7 @@ struct rlt_ctx {
   size_t es;       // element size
   // parameters (caller-owned device memory)
   const float *s_star, *merge_norm, *merge_bg, *out_norm;
-  const void *merge_wg, *merge_ws, *w_out;
+  const void *merge_wg, *merge_ws, *merge_ws_u, *merge_ws_v, *w_out;
   std::vector<const float*> norm_s, norm_m, norm_d;
   std::vector<const void*> wq, wk, wv, wo, wqm, wom, w_gate, w_up, w_down;
   // capacities and launch shapes
@@ -184,6 +184,13 @@ int check_config(const rlt_config* c) {
   if (c->n_groups != 1 && c->n_groups != c->n_layers)
     return fail(RLT_EUNSUPPORTED, "n_groups must be 1 or n_layers");
   if (!(c->rms_eps > 0.f) || !(c->rope_theta > 0.f)) return fail(RLT_EINVAL, "rms_eps, rope_theta");
+  if (c->merge_gate != RLT_GATE_VECTOR && c->merge_gate != RLT_GATE_SCALAR) return fail(RLT_EINVAL, "merge_gate");
+  if (c->merge_gate == RLT_GATE_SCALAR && c->merge_kind != RLT_MERGE_GATED)
+    return fail(RLT_EUNSUPPORTED, "the scalar gate is implemented for the gated merge");
+  if (c->merge_rank < 0 || c->merge_rank % 32 || c->merge_rank > c->d_ffn || c->merge_rank > c->d_model)
+    return fail(RLT_EUNSUPPORTED, "merge_rank must be 0 or a multiple of 32 up to min(d_model, d_ffn)");
+  if (c->merge_rank && c->merge_kind != RLT_MERGE_GATED) return fail(RLT_EINVAL, "merge_rank needs the gated merge");
+  if (c->block_order < RLT_ORDER_SXF || c->block_order > RLT_ORDER_FXS) return fail(RLT_EINVAL, "block_order");
   return RLT_OK;
 }
 
@@ -289,8 +296,9 @@ extern "C" int rlt_create(const rlt_config* cfg, const rlt_weights* w, int32_t m
   if (max_rows < 1 || max_rows > 65536 || max_ctx < 1) return fail(RLT_EINVAL, "max_rows/max_ctx");
   const int L = cfg->n_layers;
   const bool gated = cfg->merge_kind == RLT_MERGE_GATED;
+  const bool low_rank = cfg->merge_rank > 0;
   if (!w->s_star || !w->merge_wg || !w->merge_bg || !w->out_norm || !w->w_out ||
-      (gated && (!w->merge_norm || !w->merge_ws)))
+      (gated && (!w->merge_norm || (low_rank ? (!w->merge_ws_u || !w->merge_ws_v) : !w->merge_ws))))
     return fail(RLT_EINVAL, "missing global weight");
   const void* const* per[] = {(const void* const*)w->norm_s, w->wq, w->wk, w->wv, w->wo,
                               (const void* const*)w->norm_m, w->wqm, w->wom,
@@ -310,6 +318,8 @@ extern "C" int rlt_create(const rlt_config* cfg, const rlt_weights* w, int32_t m
   c->out_norm = w->out_norm;
   c->merge_wg = w->merge_wg;
   c->merge_ws = w->merge_ws;
+  c->merge_ws_u = w->merge_ws_u;
+  c->merge_ws_v = w->merge_ws_v;
   c->w_out = w->w_out;
   c->norm_s.assign(w->norm_s, w->norm_s + L);
   c->norm_m.assign(w->norm_m, w->norm_m + L);
@@ -559,38 +569,66 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
   m.e = P.e;
   m.merge_kind = cf.merge_kind;
 
+  // Sublayer order of every block [RLT §2.5, text after eq. (2.16)]: kinds
+  // 0 = SWA, 1 = cross-attention, 2 = FFN, each with its own pre-norm.
+  static const int kOrders[6][3] = {{0, 1, 2}, {0, 2, 1}, {1, 0, 2}, {1, 2, 0}, {2, 0, 1}, {2, 1, 0}};
+  const int* order = kOrders[cf.block_order];
+  auto gain_of = [&](int l, int kind) -> const float* {
+    if (l >= L) return c->out_norm;  // after the last block: RMSNorm_o of the readout [eq. (2.6)]
+    return kind == 0 ? c->norm_s[l] : kind == 1 ? c->norm_m[l] : c->norm_d[l];
+  };
+
   // ---- merge [eqs. (2.9)-(2.11)] ----
   // Every RMSNorm is folded into the matrix products: the producer of z
   // (merge or residual epilogue) writes z * gain_next into w.h and per-row
   // partial sums of squares into w.ssq; the consumer scales by rstd.
+  const bool scalar_gate = cf.merge_gate == RLT_GATE_SCALAR;
   m.gain = c->merge_norm;
   m.out = w.X;
   m.ld_out = 2 * d;
+  m.wg = scalar_gate ? c->merge_wg : nullptr;   // scalar gate: computed with the merge input
+  m.bg = c->merge_bg;
+  m.gbuf = w.gbuf;
   { Prof pf(c, RLT_PROF_NORM, s); launch_merge_prep(c->dt, m, s); }
   auto producer = [&](EpiArgs e, const float* gnext) {
     e.gnext = gnext;
     e.zb = w.h;
     return e;
   };
+  const float* g_first = gain_of(0, order[0]);
   if (cf.merge_kind == RLT_MERGE_GATED) {
     EpiArgs e = E0;
-    e.kind = EPI_MGATE;
-    e.out_f = w.gbuf;
-    e.ldo = d;
-    e.bias = c->merge_bg;
-    gm.run(w.X, 2 * d, {c->merge_wg}, d, 2 * d, PAIR_PLAIN, n, e);
+    if (!scalar_gate) {
+      e.kind = EPI_MGATE;
+      e.out_f = w.gbuf;
+      e.ldo = d;
+      e.bias = c->merge_bg;
+      gm.run(w.X, 2 * d, {c->merge_wg}, d, 2 * d, PAIR_PLAIN, n, e);
+    }
     e.kind = EPI_MOUT;
     e.out_f = w.z;
+    e.ldo = d;
     e.gbuf = w.gbuf;
-    gm.run((const char*)w.X + d * es, 2 * d, {c->merge_ws}, d, d, PAIR_PLAIN, n, producer(e, c->norm_s[0]),
-           nullptr, w.ssq);
+    const void* r_in = (const char*)w.X + d * es;  // RMSNorm_s(s_{t-1}), the second half of X
+    if (cf.merge_rank > 0) {
+      // low-rank W_s = U V: y = V r (stored in the dtype), then U y
+      const int k = cf.merge_rank;
+      EpiArgs ey = E0;
+      ey.kind = EPI_STORE_T;
+      ey.out_k = w.act;
+      ey.ldo = k;
+      gm.run(r_in, 2 * d, {c->merge_ws_v}, k, d, PAIR_PLAIN, n, ey);
+      gm.run(w.act, k, {c->merge_ws_u}, d, k, PAIR_PLAIN, n, producer(e, g_first), nullptr, w.ssq);
+    } else {
+      gm.run(r_in, 2 * d, {c->merge_ws}, d, d, PAIR_PLAIN, n, producer(e, g_first), nullptr, w.ssq);
+    }
   } else {
     EpiArgs e = E0;
     e.kind = EPI_CONVEX;
     e.out_f = w.z;
     e.ldo = d;
     e.bias = c->merge_bg;
-    gm.run(w.X, 2 * d, {c->merge_wg}, d, 2 * d, PAIR_PLAIN, n, producer(e, c->norm_s[0]), nullptr, w.ssq);
+    gm.run(w.X, 2 * d, {c->merge_wg}, d, 2 * d, PAIR_PLAIN, n, producer(e, g_first), nullptr, w.ssq);
   }
 
   AttnArgs at{};
@@ -607,8 +645,8 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
   at.st = P.mem.stride_t;
 
   const size_t ring_layer = (size_t)P.st->B_cap * (cf.window - 1) * d * es;
-  for (int l = 0; l < L; ++l) {
-    // ---- SWA sublayer [eqs. (2.12)-(2.14)]: RMSNorm_S folded into QKV ----
+  // ---- SWA sublayer [eqs. (2.12)-(2.14)]: RMSNorm_S folded into QKV ----
+  auto swa = [&](int l, const float* gnext) {
     {
       EpiArgs e = E0;
       e.kind = EPI_QKV;
@@ -625,14 +663,14 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
     at.out = w.o;
     at.hpw = c->hpw;
     { Prof pf(c, RLT_PROF_SWA, s); launch_swa(c->dt, at, s); }
-    {
-      EpiArgs e = E0;
-      e.kind = EPI_RESID;
-      e.out_f = w.z;
-      e.ldo = d;
-      gm.run(w.o, d, {c->wo[l]}, d, d, PAIR_PLAIN, n, producer(e, c->norm_m[l]), nullptr, w.ssq);
-    }
-    // ---- cross-attention sublayer [eq. (2.15)]: RMSNorm_M folded into the query ----
+    EpiArgs e = E0;
+    e.kind = EPI_RESID;
+    e.out_f = w.z;
+    e.ldo = d;
+    gm.run(w.o, d, {c->wo[l]}, d, d, PAIR_PLAIN, n, producer(e, gnext), nullptr, w.ssq);
+  };
+  // ---- cross-attention sublayer [eq. (2.15)]: RMSNorm_M folded into the query ----
+  auto cross = [&](int l, const float* gnext) {
     {
       EpiArgs e = E0;
       e.kind = EPI_QROT;
@@ -643,28 +681,36 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
     at.q = w.qm;
     at.mk = (const char*)P.mem.k + (size_t)g * P.mem.stride_g * es;
     at.mv = (const char*)P.mem.v + (size_t)g * P.mem.stride_g * es;
+    at.out = w.o;
     at.hpw = c->hpw_x;
     { Prof pf(c, RLT_PROF_XATTN, s); launch_xattn(c->dt, at, s); }
     { Prof pf(c, RLT_PROF_XCOMBINE, s); launch_xcombine(c->dt, at, s); }
-    {
-      EpiArgs e = E0;
-      e.kind = EPI_RESID;
-      e.out_f = w.z;
-      e.ldo = d;
-      gm.run(w.o, d, {c->wom[l]}, d, d, PAIR_PLAIN, n, producer(e, c->norm_d[l]), nullptr, w.ssq);
-    }
-    // ---- FFN sublayer [eq. (2.16)]: RMSNorm_D folded into gate/up ----
-    {
-      EpiArgs e = E0;
-      e.kind = EPI_SWIGLU;
-      e.out_k = w.act;
-      e.ldo = F;
-      gm.run(w.h, d, {c->w_gate[l], c->w_up[l]}, F, d, PAIR_DUAL, n, e, w.ssq);
-      e.kind = EPI_RESID;
-      e.out_f = w.z;
-      e.ldo = d;
-      const float* gnext = l + 1 < L ? c->norm_s[l + 1] : c->out_norm;  // next block, or RMSNorm_o
-      gm.run(w.act, F, {c->w_down[l]}, d, F, PAIR_PLAIN, n, producer(e, gnext), nullptr, w.ssq);
+    EpiArgs e = E0;
+    e.kind = EPI_RESID;
+    e.out_f = w.z;
+    e.ldo = d;
+    gm.run(w.o, d, {c->wom[l]}, d, d, PAIR_PLAIN, n, producer(e, gnext), nullptr, w.ssq);
+  };
+  // ---- FFN sublayer [eq. (2.16)]: RMSNorm_D folded into gate/up ----
+  auto ffn = [&](int l, const float* gnext) {
+    EpiArgs e = E0;
+    e.kind = EPI_SWIGLU;
+    e.out_k = w.act;
+    e.ldo = F;
+    gm.run(w.h, d, {c->w_gate[l], c->w_up[l]}, F, d, PAIR_DUAL, n, e, w.ssq);
+    e.kind = EPI_RESID;
+    e.out_f = w.z;
+    e.ldo = d;
+    gm.run(w.act, F, {c->w_down[l]}, d, F, PAIR_PLAIN, n, producer(e, gnext), nullptr, w.ssq);
+  };
+  for (int l = 0; l < L; ++l) {
+    for (int i = 0; i < 3; ++i) {
+      // the producer of this sublayer folds the gain of the next norm: the
+      // next sublayer's, the next block's first, or RMSNorm_o
+      const float* gnext = i + 1 < 3 ? gain_of(l, order[i + 1]) : gain_of(l + 1, order[0]);
+      if (order[i] == 0) swa(l, gnext);
+      else if (order[i] == 1) cross(l, gnext);
+      else ffn(l, gnext);
     }
     if (P.z_trace) launch_copy_f32(w.z, P.z_trace + (size_t)l * P.z_trace_ld * d, (int64_t)n * d, s);
   }
@@ -856,6 +902,7 @@ static int step_enqueue(rlt_ctx* c, rlt_state* st, const rlt_step_io* io, hipStr
   ro.uniform = io->uniform;
   ro.temperature = io->temperature;
   ro.top_k = io->top_k;
+  ro.top_p = io->top_p;
   ro.sample_tok = io->sample_tok;
   ro.sample_logmu = io->sample_logmu;
 
@@ -899,6 +946,7 @@ extern "C" int rlt_decoder_step(rlt_ctx* c, rlt_state* st, const rlt_step_io* io
       return fail(RLT_EUNSUPPORTED, "sampling needs 1 <= top_k <= min(1024, vocab)");
     if (!io->sample_tok && !io->sample_logmu) return fail(RLT_EINVAL, "sampling without outputs");
   }
+  if (!(io->top_p == io->top_p)) return fail(RLT_EINVAL, "top_p is NaN");
   if ((io->flags & RLT_STEP_DEFER) && !(io->uniform ? io->sample_tok : io->argmax))
     return fail(RLT_EINVAL, "RLT_STEP_DEFER needs sample_tok (sampling) or argmax");
   if ((rc = take_device_error(c))) return rc;
@@ -1030,6 +1078,8 @@ extern "C" int rlt_score_logprobs(rlt_ctx* c, const rlt_score_io* io, void* stre
   if (!io->s || !io->tokens || !io->logp) return fail(RLT_EINVAL, "null s, tokens or logp");
   if (io->logmu && !(io->temperature > 0.f)) return fail(RLT_EINVAL, "temperature must be > 0");
   if (io->logmu && (io->top_k < 0 || io->top_k > 1024)) return fail(RLT_EUNSUPPORTED, "top_k outside 0..1024");
+  if (io->logmu && io->top_p > 0.f && io->top_p < 1.f && io->top_k < 1)
+    return fail(RLT_EUNSUPPORTED, "a top-p nucleus is taken within the top-k set: needs top_k >= 1");
   if (io->ratio && !io->logmu_behaviour) return fail(RLT_EINVAL, "ratio needs logmu_behaviour");
   int rc = take_device_error(c);
   if (rc) return rc;
@@ -1065,6 +1115,7 @@ extern "C" int rlt_score_logprobs(rlt_ctx* c, const rlt_score_io* io, void* stre
   ro.logp = io->logp;
   ro.temperature = io->temperature;
   ro.top_k = io->top_k;
+  ro.top_p = io->top_p;
   ro.logmu = io->logmu;
   ro.logmu_beh = io->logmu_behaviour;
   ro.ratio = io->ratio;
@@ -1210,9 +1261,9 @@ int check_memory_weights(const rlt_ctx* c, const rlt_memory_weights* mw) {
   return RLT_OK;
 }
 
-// scratch for up to mem_rows entries per chunk and B prefill sequences
-int ensure_mem_ws(rlt_ctx* c, int B) {
-  if (!c->mem_A) {
+// scratch for up to mem_rows entries per chunk (when rows) and B prefill sequences
+int ensure_mem_ws(rlt_ctx* c, int B, bool rows = true) {
+  if (rows && !c->mem_A) {
     c->mem_rows = std::max(c->M_pad, 8192);
     const size_t R = c->mem_rows;
     int rc = 0;
@@ -1311,6 +1362,29 @@ extern "C" int rlt_memory_prefill(rlt_ctx* c, const rlt_memory_weights* mw, cons
     enqueue_mem_entries(c, mw, mem, R, EIn{e, e_stride_b, e_stride_t}, s);
   }
   launch_mem_setlen(c->mem_lens, B, const_cast<int*>(mem->mem_len), s);
+  HIP_TRY(hipGetLastError());
+  return RLT_OK;
+}
+
+extern "C" int rlt_trajectory_log_ratio(rlt_ctx* c, int32_t B, const int32_t* len_host, const int32_t* split_host,
+                                        const float* logp, int64_t logp_stride_b, const float* logmu,
+                                        int64_t logmu_stride_b, float* out, void* stream) {
+  if (!c || !len_host || !split_host || !logp || !logmu || !out) return fail(RLT_EINVAL, "null argument");
+  if (B < 1) return fail(RLT_ESHAPE, "B < 1");
+  if (logp_stride_b < 0 || logmu_stride_b < 0) return fail(RLT_EINVAL, "strides");
+  int rc = ensure_mem_ws(c, B, false);  // the prefill schedule buffers hold the first / last positions
+  if (rc) return rc;
+  std::vector<int> range(2 * (size_t)B);
+  for (int b = 0; b < B; ++b) {
+    if (split_host[b] < 1) return fail(RLT_EINVAL, "split[%d] < 1", b);
+    range[b] = split_host[b];
+    range[B + b] = len_host[b] - 1;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  HIP_TRY(hipStreamSynchronize(s));
+  HIP_TRY(hipMemcpy(c->mem_offs, range.data(), (size_t)B * 4, hipMemcpyHostToDevice));
+  HIP_TRY(hipMemcpy(c->mem_lens, range.data() + B, (size_t)B * 4, hipMemcpyHostToDevice));
+  launch_traj_ratio(B, c->mem_offs, c->mem_lens, logp, logp_stride_b, logmu, logmu_stride_b, out, s);
   HIP_TRY(hipGetLastError());
   return RLT_OK;
 }

@@ -183,7 +183,8 @@ enum EpiKind {
   EPI_MGATE = 5,   // g[m][c] = sigmoid(v + b_g[c])           eq (2.10)
   EPI_MOUT = 6,    // z[m][c] = e + alpha * g * v              eq (2.11)
   EPI_CONVEX = 7,  // g = sigmoid(v + b); z = g e + (1-g) s
-  EPI_MEMKV = 8    // memory entry: k (T, rotary at t) and v (T)   eq (2.2)
+  EPI_MEMKV = 8,   // memory entry: k (T, rotary at t) and v (T)   eq (2.2)
+  EPI_STORE_T = 9  // out_k[m][c] = v in the element type (low-rank W_s: V r)
 };
 
 struct EpiArgs {
@@ -260,6 +261,9 @@ struct MiscArgs {
   int64_t ld_out;
   EIn e;
   int merge_kind;
+  const void* wg;                 // scalar merge gate: w_g [2d] (T), or null (vector gate)
+  const float* bg;                // b_g [1] (scalar gate)
+  float* gbuf;                    // [n][d] gate values (scalar gate: broadcast)
   float* s_out;                   // optional [n][d]
   float* s_trace;                 // optional replay trace
   int64_t s_trace_sb;
@@ -283,6 +287,10 @@ void launch_mem_prep(int dtype, const Rows& rows, EIn e, int d, const float* gai
 void launch_mem_commit(const int* rows, int n, const int* t_row, int* mem_len, hipStream_t s);
 void launch_mem_setlen(const int* len, int B, int* mem_len, hipStream_t s);
 
+// out[b] = sum over t = first[b] .. last[b] of logp[b][t] - logmu[b][t] [RLT §5.3]
+void launch_traj_ratio(int B, const int* first, const int* last, const float* logp, int64_t logp_sb,
+                       const float* logmu, int64_t logmu_sb, float* out, hipStream_t s);
+
 struct ReadoutArgs {
   Rows rows;
   int n, V;
@@ -299,6 +307,7 @@ struct ReadoutArgs {
   const float* uniform;      // [n] or null
   float temperature;
   int top_k;
+  float top_p;               // nucleus after top-k; outside (0, 1): none
   int32_t* sample_tok;
   float* sample_logmu;
   float* logmu;              // behaviour log-prob of score_tok (score call)

@@ -64,13 +64,18 @@ class ModelConfig:
     rope_theta: float = 10000.0
     pos: str = "rope"
     version: int = 1
+    gate: str = "vector"     # merge gate: "vector" or "scalar"
+    ws_rank: int = 0         # 0: full W_s; k: W_s = U V (merge.ws_u [d, k], merge.ws_v [k, d])
+    order: str = "sxf"       # sublayer order of a block (permutation of s, x, f)
 
     def to_c(self) -> A.rlt_config:
         return A.rlt_config(self.L, self.d, self.H, self.dh, self.W, self.G, self.F, self.V,
                             A.RLT_MERGE_GATED if self.merge == "gated" else A.RLT_MERGE_CONVEX,
                             A.RLT_POS_ROPE if self.pos == "rope" else A.RLT_POS_NONE,
                             A.RLT_BF16 if self.dtype == "bf16" else A.RLT_F32,
-                            self.alpha, self.eps, self.rope_theta, self.version)
+                            self.alpha, self.eps, self.rope_theta, self.version,
+                            A.RLT_GATE_SCALAR if self.gate == "scalar" else A.RLT_GATE_VECTOR, self.ws_rank,
+                            A.ORDERS.index(self.order))
 
     @property
     def torch_dtype(self):
@@ -126,7 +131,9 @@ class Decoder:
         w.merge_norm = p["merge.norm"].data_ptr() if gated else None
         w.merge_wg = p["merge.wg"].data_ptr()
         w.merge_bg = p["merge.bg"].data_ptr()
-        w.merge_ws = p["merge.ws"].data_ptr() if gated else None
+        w.merge_ws = p["merge.ws"].data_ptr() if gated and not cfg.ws_rank else None
+        w.merge_ws_u = p["merge.ws_u"].data_ptr() if gated and cfg.ws_rank else None
+        w.merge_ws_v = p["merge.ws_v"].data_ptr() if gated and cfg.ws_rank else None
         for name, arr in self._arrays.items():
             setattr(w, name, C.cast(arr, C.POINTER(A.P)))
         w.out_norm = p["out.norm"].data_ptr()
@@ -162,7 +169,7 @@ class Decoder:
 
     def step(self, st: DecoderState, rows: torch.Tensor, e: torch.Tensor, mem: A.rlt_memory, *,
              consume_tok=None, s_out=None, logits=None, argmax=None, score_tok=None, logp=None,
-             uniform=None, temperature=1.0, top_k=0, sample_tok=None, sample_logmu=None,
+             uniform=None, temperature=1.0, top_k=0, top_p=1.0, sample_tok=None, sample_logmu=None,
              z_trace=None, graph=False, defer=False, stream=None) -> int:
         io = A.rlt_step_io()
         io.n = rows.numel()
@@ -182,6 +189,7 @@ class Decoder:
         io.sample_logmu = _ptr(sample_logmu)
         io.z_trace = _ptr(z_trace)
         io.flags = (A.RLT_STEP_GRAPH if graph else 0) | (A.RLT_STEP_DEFER if defer else 0)
+        io.top_p = top_p
         self._keep = (io, st.c())
         return A.rlt_decoder_step(self.ctx, self._keep[1], io, current_stream() if stream is None else stream)
 
@@ -212,10 +220,19 @@ class Decoder:
         return A.rlt_replay_sequence(self.ctx, stc, io, current_stream() if stream is None else stream)
 
     def score(self, s: torch.Tensor, tokens: torch.Tensor, logp: torch.Tensor, *, temperature=1.0, top_k=0,
-              logmu=None, logmu_behaviour=None, ratio=None, stream=None) -> int:
+              top_p=1.0, logmu=None, logmu_behaviour=None, ratio=None, stream=None) -> int:
         io = A.rlt_score_io(s.shape[0], s.data_ptr(), tokens.data_ptr(), logp.data_ptr(), temperature, top_k,
-                            _ptr(logmu), _ptr(logmu_behaviour), _ptr(ratio))
+                            _ptr(logmu), _ptr(logmu_behaviour), _ptr(ratio), top_p)
         return A.rlt_score_logprobs(self.ctx, io, current_stream() if stream is None else stream)
+
+    def trajectory_log_ratio(self, lens: np.ndarray, splits: np.ndarray, logp: torch.Tensor, logmu: torch.Tensor,
+                             out: torch.Tensor, stream=None) -> int:
+        """out[b] = sum over t = splits[b] .. lens[b]-1 of logp[b, t] - logmu[b, t]."""
+        lens = np.ascontiguousarray(lens, dtype=np.int32)
+        splits = np.ascontiguousarray(splits, dtype=np.int32)
+        return A.rlt_trajectory_log_ratio(self.ctx, len(lens), lens.ctypes.data, splits.ctypes.data, logp.data_ptr(),
+                                          logp.stride(0), logmu.data_ptr(), logmu.stride(0), out.data_ptr(),
+                                          current_stream() if stream is None else stream)
 
     def sync_error(self, stream=None) -> int:
         return A.rlt_sync_error(self.ctx, current_stream() if stream is None else stream)

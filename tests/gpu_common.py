@@ -25,7 +25,8 @@ def require_gpu():
 def model_config(wl: synth.Workload, **over):
     from stateful_sequence_model_amd import ModelConfig
     kw = dict(L=wl.L, d=wl.d, H=wl.H, dh=wl.dh, W=wl.W, G=wl.G, F=wl.F, V=wl.V, dtype=wl.dtype,
-              merge=wl.merge, alpha=wl.alpha, eps=wl.eps, rope_theta=wl.rope_theta, pos=wl.pos)
+              merge=wl.merge, alpha=wl.alpha, eps=wl.eps, rope_theta=wl.rope_theta, pos=wl.pos, gate=wl.gate,
+              ws_rank=wl.ws_rank, order=wl.order)
     kw.update(over)
     return ModelConfig(**kw)
 

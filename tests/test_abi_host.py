@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
     assert {"rlt_create", "rlt_destroy", "rlt_state_layout", "rlt_last_error", "rlt_init_state",
             "rlt_decoder_step", "rlt_replay_sequence", "rlt_score_logprobs", "rlt_sync_error",
             "rlt_memory_append", "rlt_memory_prefill", "rlt_snapshot_bytes", "rlt_state_snapshot",
-            "rlt_state_restore", "rlt_dbg_gemm"} <= decl
+            "rlt_state_restore", "rlt_trajectory_log_ratio", "rlt_dbg_gemm"} <= decl
     for name in decl:
         assert hasattr(L, name), name
     assert decl == set(_abi.exported_symbols())
@@ -82,6 +82,10 @@ def test_state_layout_sizes():
     (dict(G=2, L=3), -8),               # groups must be 1 or L_D
     (dict(W=0), -1),
     (dict(V=250), -8),                  # vocab multiple of 32
+    (dict(gate="scalar"), -8),          # scalar gate: gated merge only (_cfg is convex)
+    (dict(merge="gated", ws_rank=48), -8),   # rank not a multiple of 32
+    (dict(merge="gated", ws_rank=96), -8),   # rank above d
+    (dict(ws_rank=32), -1),             # low rank needs the gated merge
 ])
 def test_config_validation(kw, code):
     from stateful_sequence_model_amd import _abi
@@ -89,6 +93,15 @@ def test_config_validation(kw, code):
     cfg = _cfg(**kw)
     assert _abi.lib().rlt_state_layout(C.byref(cfg), 4, out) == code
     assert _abi.rlt_last_error()
+
+
+def test_config_rejects_bad_enums():
+    from stateful_sequence_model_amd import _abi
+    out = (C.c_size_t * 5)()
+    for field, value in (("merge_gate", 2), ("block_order", 6), ("block_order", -1)):
+        cfg = _cfg()
+        setattr(cfg, field, value)
+        assert _abi.lib().rlt_state_layout(C.byref(cfg), 4, out) == _abi.RLT_EINVAL, field
 
 
 def test_create_rejects_missing_weights_before_touching_the_device():
