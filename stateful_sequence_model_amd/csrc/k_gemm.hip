@@ -11,8 +11,10 @@
 //   one pair of 16-column blocks) and each streams a disjoint quarter of the
 //   workgroup's K range, so A and W are each read once per workgroup; the
 //   four partial tiles are summed in LDS in wave order. Optional split of K
-//   across S workgroups writes partial tiles that a second kernel sums in
-//   split order. Both orders are fixed, so results are deterministic.
+//   across S workgroups writes partial tiles; the last workgroup of a tile
+//   to finish (an arrival counter per tile) sums them in split order and
+//   runs the epilogue (the persistent step uses a phase of its own for this).
+//   Both orders are fixed, so results are deterministic.
 //   Accumulation is fp32; A (activations) arrive rounded to bf16.
 // fp32 path: one thread per output pair, sequential K loop (used by the
 //   float32 configuration, where precision rather than speed is the point).
@@ -55,6 +57,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, MB >= 8 
   __shared__ __attribute__((aligned(16))) uint16_t sa[2][MB * 2 * 64 * 8];
   __shared__ float s_rstd[R];
   __shared__ float s_part[256];
+  __shared__ int s_flag;
   // 1-D grid of T = groups * S * mtiles workgroups, XCD-aware: the hardware
   // deals consecutive workgroup ids to the 8 XCDs in turn, so id b runs on
   // XCD b % 8. Tile t = (b % 8) * (T / 8) + b / 8 gives each XCD a contiguous
@@ -78,7 +81,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, MB >= 8 
     const int q = c * 256 + tid, blk = q >> 6, L = q & 63;
     ap[c] = (const uint16_t*)g.A + (int64_t)(m0 + (blk >> 1) * 16 + (L & 15)) * g.lda + (blk & 1) * 32 + (L >> 4) * 8;
   }
-  const bool norm_here = g.S == 1 && g.ssq_in != nullptr;
+  const bool norm_here = (g.S == 1 || g.tile_cnt != nullptr) && g.ssq_in != nullptr;
   RowRstd<R> rr(g, norm_here ? m0 : 0);
   f32x4_t acc[MB][2];
 #pragma unroll
@@ -150,29 +153,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, MB >= 8 
       load_a(p & 1, min(i + p + 2, nst - 1));
     }
 
+  if (g.S > 1) {
+    // C layout: lane holds rows 4*(lane/16)+i of each 16-row block, column lane%16
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m = m0 + mb * 16 + (lane >> 4) * 4 + q;
+        if (m < g.M) {
+          float* Pp = g.partial + ((int64_t)split * g.M_pad + m) * g.Nv;
+          Pp[ba * 16 + r16] = acc[mb][0][q];
+          Pp[bb * 16 + r16] = acc[mb][1][q];
+        }
+      }
+    // K split reduced here: the tile's last workgroup sums the partials in
+    // split order into its accumulators (its own partial included)
+    if (!g.tile_cnt || !last_arrival(g.tile_cnt + grp * nmt + mt, g.S, &s_flag)) return;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m = m0 + mb * 16 + (lane >> 4) * 4 + q;
+        float va = 0.f, vb = 0.f;
+        if (m < g.M)
+          for (int sp = 0; sp < g.S; ++sp) {
+            const float* Pp = g.partial + ((int64_t)sp * g.M_pad + m) * g.Nv;
+            va += Pp[ba * 16 + r16];
+            vb += Pp[bb * 16 + r16];
+          }
+        acc[mb][0][q] = va;
+        acc[mb][1][q] = vb;
+      }
+  }
   if (norm_here) {  // uniform branch
     rr.finish(g, m0, s_part, s_rstd);
     __syncthreads();
   }
-  // C layout: lane holds rows 4*(lane/16)+i of each 16-row block, column lane%16
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int mr = mb * 16 + (lane >> 4) * 4 + q;
       const int m = m0 + mr;
-      const float va = acc[mb][0][q], vb = acc[mb][1][q];
-      if (g.S == 1) {
-        float sq = 0.f;
-        if (m < g.M) sq = epi(m, ba * 16 + r16, va, bb * 16 + r16, vb, norm_here ? s_rstd[mr] : 1.f);
-        if (g.ssq_out) {
-          sq = sum16(sq);
-          if (r16 == 0 && m < g.M) g.ssq_out[(int64_t)pair * g.M_pad + m] = sq;
-        }
-      } else if (m < g.M) {
-        float* Pp = g.partial + ((int64_t)split * g.M_pad + m) * g.Nv;
-        Pp[ba * 16 + r16] = va;
-        Pp[bb * 16 + r16] = vb;
+      float sq = 0.f;
+      if (m < g.M) sq = epi(m, ba * 16 + r16, acc[mb][0][q], bb * 16 + r16, acc[mb][1][q], norm_here ? s_rstd[mr] : 1.f);
+      if (g.ssq_out) {
+        sq = sum16(sq);
+        if (r16 == 0 && m < g.M) g.ssq_out[(int64_t)pair * g.M_pad + m] = sq;
       }
     }
 }
@@ -244,6 +271,7 @@ void launch_gemm(int dtype, const GemmArgs& g0, const EpiArgs& e, hipStream_t s)
     p.gy = g.S;
     p.gz = mt;
     p.u.gm.g = g;
+    p.u.gm.g.tile_cnt = nullptr;  // the persistent step sums the partials in a phase of its own
     p.u.gm.e = e;
     if (record_phase(p)) {
       if (g.S > 1) {
@@ -270,7 +298,7 @@ void launch_gemm(int dtype, const GemmArgs& g0, const EpiArgs& e, hipStream_t s)
       default: hipLaunchKernelGGL(k_gemm_bf16<4>, grid, dim3(256), 0, s, g, epi); break;
     }
   }
-  if (g.S > 1) {
+  if (g.S > 1 && !g.tile_cnt) {
     dim3 g2(g.npairs, (g.M + 15) / 16);
     hipLaunchKernelGGL(k_splitk_epi<uint16_t>, g2, dim3(256), 0, s, g, epi);
   }

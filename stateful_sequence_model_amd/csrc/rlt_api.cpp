@@ -57,7 +57,13 @@ struct Workspace {
   void *X, *kc, *vc, *o, *h, *act;
   float *gbuf, *z, *q, *qm, *part, *partial, *logits;
   float* ssq;  // [d/2][M_pad] partial sums of squares of z (folded RMSNorm)
+  unsigned* tile_cnt;  // [kTileCounters] arrival counters of K-split products (zero between calls)
 };
+
+// K-split products of the narrow tile with at most this many output tiles
+// reduce their partials in the product kernel itself (the split rule only
+// splits below 256 tiles)
+constexpr int kTileCounters = 1024;
 
 }  // namespace
 
@@ -78,7 +84,7 @@ struct rlt_ctx {
   int gemm_s_force;    // 0 or forced K split (tuning)
   int gemm_wide;       // wide-tile products for calls above 32 rows (1 = on)
   int split_min_rows;  // calls with at least this many rows run as two streams (0 = never)
-  int gemm_target;     // workgroups a matrix product aims to fill (K split heuristic)
+  int gemm_target;     // K split target of the persistent step's products (0: stand-alone kernels)
   size_t partial_cap;  // floats per workspace
   // persistent step for calls of at most fused_rows rows (bf16; 0 = off)
   int fused_rows;
@@ -245,7 +251,8 @@ extern "C" void rlt_destroy(rlt_ctx* c) {
   std::vector<void*> ptrs = {c->t_row, c->ident, c->ones, c->rows_buf, c->src_buf, c->split_buf, c->last_buf,
                              c->inv_freq};
   for (Workspace& w : c->ws) {
-    void* p[] = {w.X, w.kc, w.vc, w.o, w.h, w.act, w.gbuf, w.z, w.q, w.qm, w.part, w.partial, w.logits, w.ssq};
+    void* p[] = {w.X, w.kc, w.vc, w.o, w.h, w.act, w.gbuf, w.z, w.q, w.qm, w.part, w.partial, w.logits, w.ssq,
+                 w.tile_cnt};
     ptrs.insert(ptrs.end(), std::begin(p), std::end(p));
   }
   for (void* p : ptrs)
@@ -278,8 +285,9 @@ static int alloc_workspace(rlt_ctx* c, Workspace& w, bool full) {
       (rc = dev_alloc(&w.part, M * (size_t)c->nch * cf.n_heads * (cf.d_head + 2) * 4)) ||
       (rc = dev_alloc(&w.partial, c->partial_cap * 4)) ||
       (rc = dev_alloc(&w.logits, (full ? M : 16) * (size_t)cf.vocab * 4)) ||
-      (rc = dev_alloc(&w.ssq, M * (size_t)(d / 2) * 4)))
+      (rc = dev_alloc(&w.ssq, M * (size_t)(d / 2) * 4)) || (rc = dev_alloc(&w.tile_cnt, kTileCounters * 4)))
     return rc;
+  if (hipMemset(w.tile_cnt, 0, kTileCounters * 4) != hipSuccess) return fail(RLT_EHIP, "workspace initialisation failed");
   // rows beyond a call's n are read by the MFMA tiles and discarded: keep
   // them finite
   if (hipMemset(w.X, 0, M * 2 * d * es) != hipSuccess || hipMemset(w.o, 0, M * d * es) != hipSuccess ||
@@ -349,7 +357,7 @@ extern "C" int rlt_create(const rlt_config* cfg, const rlt_weights* w, int32_t m
   c->gemm_s_force = env_int("RLT_GEMM_S", 0);
   c->gemm_wide = env_int("RLT_GEMM_WIDE", 1);
   c->split_min_rows = env_int("RLT_SPLIT_MIN_ROWS", 0);
-  c->gemm_target = 512;
+  c->gemm_target = 0;
   // Off by default: on MI355X a device-scope grid barrier costs 3.5-8.7 us,
   // so ~15 phases per block make the persistent step slower than the
   // separate kernels at every batch size measured (1-16 rows).
@@ -494,7 +502,7 @@ struct Gemm {
       const int mt = (n + 16 * MB - 1) / (16 * MB);
       const int tiles = g.npairs / 4 * mt;
       const int kst = K / 64;
-      int S = std::max(1, (c->gemm_target / 2 + tiles - 1) / tiles);
+      int S = std::max(1, (256 + tiles - 1) / tiles);
       S = std::min(S, std::max(1, kst / 4));              // >= 4 stages per workgroup
       if (c->gemm_s_force > 0) S = std::min(c->gemm_s_force, kst);
       while (S > 1 && (size_t)S * g.M_pad * g.Nv > c->partial_cap) --S;
@@ -502,13 +510,20 @@ struct Gemm {
       g.mb = MB;
       g.S = S;
       g.kslice = (kst + S - 1) / S * 64;
+      // partials summed by a second kernel: the arrival protocol's acquire
+      // invalidates L2, which this tile relies on for its activation and
+      // weight re-reads (measured: the product time more than doubles)
     } else if (c->dt == 1) {
       int MB = gemm_row_blocks(n);
       const int mbf = c->gemm_mb_force;
       if (mbf == 1 || mbf == 2 || mbf == 4) MB = mbf;
       const int mt = (n + 16 * MB - 1) / (16 * MB);
       const int tiles = g.npairs * mt;
-      int S = std::max(1, (c->gemm_target + tiles - 1) / tiles);   // fill the chip
+      // K split: the persistent step fills its grid; a stand-alone kernel
+      // splits only while each split still adds a workgroup per compute unit
+      // (256 CUs): splitting further leaves workgroups queued behind others
+      // and adds partial traffic, which costs more than the latency it hides
+      int S = c->gemm_target ? std::max(1, (c->gemm_target + tiles - 1) / tiles) : std::max(1, 256 / tiles);
       S = std::min(S, std::max(1, K / 256));             // >= 64 K per wave
       S = std::min(S, std::max(1, K / (4 * n)));         // partial traffic <= the weights'
       if (c->gemm_s_force > 0) S = std::min(c->gemm_s_force, std::max(1, K / 128));
@@ -517,6 +532,7 @@ struct Gemm {
       g.mb = MB;
       const int per = (K + 4 * S - 1) / (4 * S);
       g.kslice = (per + 31) / 32 * 32;
+      if (S > 1 && tiles <= kTileCounters) g.tile_cnt = w->tile_cnt;
     }
     Prof pf(c, RLT_PROF_GEMM, s);
     launch_gemm(c->dt, g, e, s);
@@ -797,7 +813,7 @@ const Phase* fused_prepare(rlt_ctx* c, const StepPlan& P, hipStream_t s, int* np
   c->gemm_target = c->fused_target;
   enqueue_transition(c, c->ws[0], Q, s);
   t_rec = nullptr;
-  c->gemm_target = 512;
+  c->gemm_target = 0;
   *nphase = (int)rec.size();
   for (const Phase& p : rec)
     if (p.kind == PH_INVALID) return nullptr;
