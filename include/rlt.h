@@ -343,6 +343,74 @@ int rlt_memory_prefill(rlt_ctx* ctx, const rlt_memory_weights* mw, const rlt_mem
                        int32_t B, const int32_t* len_host, const void* e, int64_t e_stride_b, int64_t e_stride_t,
                        void* stream);
 
+/* Replay backward: full backpropagation through time of a replayed loss
+ * [RLT §5.4; App. B, eqs. (B.1)-(B.5)]. The loss is linear in the replayed
+ * log-probabilities,
+ *   L = sum_b sum_{t = split_b}^{len_b - 1} w[b][t] * log p(x_{t+1} | x_{1:t}),
+ * (w = -1: next-token likelihood; w = advantages: the score-function
+ * surrogate of eq. (5.4)), each sequence replayed from H_0 as in
+ * rlt_replay_sequence. Its gradient flows through s_t, through every decoder
+ * SWA key/value to the steps that read it (also after eviction) and through
+ * the encoder memory; nothing is detached.
+ *
+ * Gradients are float32 device buffers shaped as the matching rlt_weights
+ * fields, ACCUMULATED into (zero them first); per-layer fields are HOST
+ * arrays of n_layers device pointers. Any field (or per-layer array, or
+ * entry of one) may be NULL: that gradient is not formed.
+ *
+ * Arithmetic is float32 throughout, on the given parameter values (bf16
+ * parameters, e and memory are widened): the call differentiates the float32
+ * transition, which for a float32 configuration is the one the forward calls
+ * compute (up to summation order). Activations are checkpointed per step: a
+ * forward pass keeps s_t and the decoder keys/values of every step, and the
+ * backward pass recomputes each step's activations before differentiating
+ * it. Covers the vector merge gate, full-rank W_s and sublayer order SXF
+ * (others: RLT_EUNSUPPORTED); len - 1 <= 8192 - d_head. Work buffers are
+ * allocated for the call (RLT_ENOMEM if they do not fit). */
+typedef struct rlt_grads {
+  float* s_star;
+  float* merge_norm;
+  float* merge_wg;
+  float* merge_bg;
+  float* merge_ws;
+  float* const* norm_s;
+  float* const* wq;
+  float* const* wk;
+  float* const* wv;
+  float* const* wo;
+  float* const* norm_m;
+  float* const* wqm;
+  float* const* wom;
+  float* const* norm_d;
+  float* const* w_gate;
+  float* const* w_up;
+  float* const* w_down;
+  float* out_norm;
+  float* w_out;
+} rlt_grads;
+
+typedef struct rlt_backward_io {
+  int32_t B;                   /* sequences */
+  const int32_t* len_host;     /* HOST [B] tokens x_1..x_len, 2 <= len */
+  const int32_t* split_host;   /* HOST [B] first scored position, 1 <= split <= len - 1 */
+  const void* e;               /* e_t of sequence b at e[b*e_stride_b + (t-1)*e_stride_t] (config dtype) */
+  int64_t e_stride_b, e_stride_t;
+  rlt_memory mem;              /* memory of sequence b (config dtype), >= len_b - 1 positions; mem_len unused */
+  const int32_t* tokens;       /* x_t of sequence b at tokens[b*tok_stride_b + t-1] */
+  int64_t tok_stride_b;
+  const float* w;              /* w[b*w_stride_b + t]: weight of log p(x_{t+1} | x_{1:t}) */
+  int64_t w_stride_b;
+  float* logp;                 /* optional: logp[b*logp_stride_b + t] of the replay */
+  int64_t logp_stride_b;
+  float* de;                   /* optional: dL/de_t at de[b*de_stride_b + (t-1)*de_stride_t] (accumulated) */
+  int64_t de_stride_b, de_stride_t;
+  float* dmem_k;               /* optional (both or none): dL/dM at [g*stride_g + b*stride_b + (t-1)*stride_t] */
+  float* dmem_v;
+  int64_t dmem_stride_g, dmem_stride_b, dmem_stride_t;
+} rlt_backward_io;
+
+int rlt_replay_backward(rlt_ctx* ctx, const rlt_backward_io* io, const rlt_grads* grads, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

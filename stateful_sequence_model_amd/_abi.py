@@ -85,6 +85,22 @@ class rlt_memory_weights(C.Structure):
     _fields_ = [("norm_e", C.POINTER(P)), ("wk", C.POINTER(P)), ("wv", C.POINTER(P))]
 
 
+class rlt_grads(C.Structure):
+    _fields_ = [("s_star", P), ("merge_norm", P), ("merge_wg", P), ("merge_bg", P), ("merge_ws", P),
+                ("norm_s", C.POINTER(P)), ("wq", C.POINTER(P)), ("wk", C.POINTER(P)), ("wv", C.POINTER(P)),
+                ("wo", C.POINTER(P)), ("norm_m", C.POINTER(P)), ("wqm", C.POINTER(P)), ("wom", C.POINTER(P)),
+                ("norm_d", C.POINTER(P)), ("w_gate", C.POINTER(P)), ("w_up", C.POINTER(P)),
+                ("w_down", C.POINTER(P)), ("out_norm", P), ("w_out", P)]
+
+
+class rlt_backward_io(C.Structure):
+    _fields_ = [("B", i32), ("len_host", P), ("split_host", P), ("e", P), ("e_stride_b", i64),
+                ("e_stride_t", i64), ("mem", rlt_memory), ("tokens", P), ("tok_stride_b", i64), ("w", P),
+                ("w_stride_b", i64), ("logp", P), ("logp_stride_b", i64), ("de", P), ("de_stride_b", i64),
+                ("de_stride_t", i64), ("dmem_k", P), ("dmem_v", P), ("dmem_stride_g", i64),
+                ("dmem_stride_b", i64), ("dmem_stride_t", i64)]
+
+
 _lib = None
 
 # name -> (restype, argtypes)
@@ -105,6 +121,7 @@ _SIGS = {
     "rlt_memory_append": (C.c_int, [P, C.POINTER(rlt_memory_weights), C.POINTER(rlt_memory), i32, i32, P, i32, P, P]),
     "rlt_memory_prefill": (C.c_int, [P, C.POINTER(rlt_memory_weights), C.POINTER(rlt_memory), i32, i32, P, P, i64,
                                      i64, P]),
+    "rlt_replay_backward": (C.c_int, [P, C.POINTER(rlt_backward_io), C.POINTER(rlt_grads), P]),
     "rlt_dbg_gemm": (C.c_int, [P, P, P, i32, i32, i32, P, P]),
     "rlt_dbg_profile": (C.c_int, [P, i32]),
     "rlt_dbg_profile_read": (C.c_int, [P, i32, C.POINTER(C.c_double), C.POINTER(C.c_int64)]),
@@ -175,6 +192,10 @@ def rlt_decoder_step(ctx: int, st: rlt_state, io: rlt_step_io, stream: int) -> i
 
 def rlt_replay_sequence(ctx: int, st: rlt_state, io: rlt_replay_io, stream: int) -> int:
     return lib().rlt_replay_sequence(ctx, C.byref(st), C.byref(io), stream)
+
+
+def rlt_replay_backward(ctx: int, io: rlt_backward_io, grads: rlt_grads, stream: int) -> int:
+    return lib().rlt_replay_backward(ctx, C.byref(io), C.byref(grads), stream)
 
 
 def rlt_score_logprobs(ctx: int, io: rlt_score_io, stream: int) -> int:

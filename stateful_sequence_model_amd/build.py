@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "librlt.so")
-SOURCES = ["k_gemm.hip", "k_attn.hip", "k_misc.hip", "k_fused.hip", "rlt_api.cpp"]
+SOURCES = ["k_gemm.hip", "k_attn.hip", "k_misc.hip", "k_fused.hip", "k_bwd.hip", "rlt_api.cpp", "rlt_bwd.cpp"]
 ARCH = os.environ.get("RLT_OFFLOAD_ARCH", "gfx950")
 
 

@@ -1,0 +1,468 @@
+// Kernels of the replay backward: the float32 transition with its
+// activations kept, and the derivative of each of its operations
+// ("Recurrent Looped Transformer" §2.5 eqs. (2.9)-(2.16), §2.3 eq. (2.6);
+// full BPTT per §5.4 and App. B). Plain float32 arithmetic throughout; every
+// sum runs in a fixed order (deterministic results).
+#include <math.h>
+
+#include "bwd.h"
+#include "rlt_internal.h"
+
+namespace rlt {
+namespace bwd {
+namespace {
+
+template <typename T>
+__device__ __forceinline__ float ld_f(const void* p, int64_t i) {
+  return to_f<T>(((const T*)p)[i]);
+}
+
+__device__ __forceinline__ float ld_any(const void* p, int dt, int64_t i) {
+  return dt ? ld_f<uint16_t>(p, i) : ld_f<float>(p, i);
+}
+
+// fixed-order tree sum over a 256-thread block (every thread gets the sum)
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  red[threadIdx.x] = v;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  const float r = red[0];
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+  red[threadIdx.x] = v;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
+    __syncthreads();
+  }
+  const float r = red[0];
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ float sigm(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+// 16x16 output tile per 256-thread block; the unit-stride dimension of each
+// operand runs along threadIdx.x when its tile is loaded
+template <typename TB>
+__global__ __launch_bounds__(256) void k_mm(int M, int N, int K, const float* a, int64_t a_si, int64_t a_sk,
+                                           const TB* b, int64_t b_sk, int64_t b_sj, float* c, int64_t c_si,
+                                           int accumulate) {
+  __shared__ float As[16][17], Bs[16][17];
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int i0 = blockIdx.y * 16, j0 = blockIdx.x * 16;
+  const bool a_k_fast = a_sk == 1, b_j_fast = b_sj == 1;
+  float acc = 0.f;
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    {
+      const int ii = a_k_fast ? ty : tx, kk = a_k_fast ? tx : ty;
+      const int i = i0 + ii, k = k0 + kk;
+      As[ii][kk] = (i < M && k < K) ? a[(int64_t)i * a_si + (int64_t)k * a_sk] : 0.f;
+    }
+    {
+      const int kk = b_j_fast ? ty : tx, jj = b_j_fast ? tx : ty;
+      const int k = k0 + kk, j = j0 + jj;
+      Bs[kk][jj] = (k < K && j < N) ? to_f<TB>(b[(int64_t)k * b_sk + (int64_t)j * b_sj]) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) acc = fmaf(As[ty][kk], Bs[kk][tx], acc);
+    __syncthreads();
+  }
+  const int i = i0 + ty, j = j0 + tx;
+  if (i < M && j < N) {
+    float* p = c + (int64_t)i * c_si + j;
+    *p = accumulate ? *p + acc : acc;
+  }
+}
+
+// block per row
+__global__ __launch_bounds__(256) void k_rms_fwd(const float* x, int64_t ldx, const float* gain, float* y,
+                                                int64_t ldy, float* rstd, int d, float eps) {
+  __shared__ float red[256];
+  const int r = blockIdx.x;
+  const float* xr = x + (int64_t)r * ldx;
+  float ss = 0.f;
+  for (int c = threadIdx.x; c < d; c += 256) ss += xr[c] * xr[c];
+  const float rs = 1.0f / sqrtf(block_sum(ss, red) / (float)d + eps);
+  for (int c = threadIdx.x; c < d; c += 256) y[(int64_t)r * ldy + c] = xr[c] * rs * gain[c];
+  if (threadIdx.x == 0) rstd[r] = rs;
+}
+
+// y = x * rs * g: dx_c = rs g_c dy_c - x_c rs^3 (1/d) sum_j x_j g_j dy_j
+__global__ __launch_bounds__(256) void k_rms_bwd(const float* x, int64_t ldx, const float* gain, const float* rstd,
+                                                const float* dy, int64_t ldy, float* dx, int64_t lddx, int d,
+                                                int accumulate) {
+  __shared__ float red[256];
+  const int r = blockIdx.x;
+  const float* xr = x + (int64_t)r * ldx;
+  const float* dyr = dy + (int64_t)r * ldy;
+  float dot = 0.f;
+  for (int c = threadIdx.x; c < d; c += 256) dot += xr[c] * gain[c] * dyr[c];
+  dot = block_sum(dot, red);
+  const float rs = rstd[r];
+  const float k = rs * rs * rs * dot / (float)d;
+  for (int c = threadIdx.x; c < d; c += 256) {
+    const float v = rs * gain[c] * dyr[c] - xr[c] * k;
+    float* p = dx + (int64_t)r * lddx + c;
+    *p = accumulate ? *p + v : v;
+  }
+}
+
+// thread per column, rows in order
+__global__ __launch_bounds__(256) void k_colsum(float* dst, const float* a, int64_t lda, const float* b, int64_t ldb,
+                                               const float* rs, int n, int d) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= d) return;
+  float acc = 0.f;
+  for (int r = 0; r < n; ++r) {
+    float v = a[(int64_t)r * lda + c];
+    if (b) v *= b[(int64_t)r * ldb + c];
+    if (rs) v *= rs[r];
+    acc += v;
+  }
+  dst[c] += acc;
+}
+
+// thread per (row, head, i < dh/2): rotate (x_i, x_{i+dh/2}) by sign * t * w_i
+__global__ __launch_bounds__(256) void k_rope(float* x, int64_t ld, int n, int d, int dh, int t,
+                                             const double* inv_freq, int sign) {
+  const int half = dh / 2;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)n * (d / 2)) return;
+  const int r = (int)(idx / (d / 2)), q = (int)(idx % (d / 2));
+  const int h = q / half, i = q % half;
+  double sn, cs;
+  sincos((double)t * inv_freq[i], &sn, &cs);
+  const float c = (float)cs, s = (float)sn * (float)sign;
+  float* p = x + (int64_t)r * ld + h * dh;
+  const float a = p[i], b = p[i + half];
+  p[i] = a * c - b * s;
+  p[i + half] = b * c + a * s;
+}
+
+// block per (row, head); scores of all keys in dynamic LDS
+template <typename TK>
+__global__ __launch_bounds__(256) void k_attn_fwd(const float* q, int64_t ldq, KV kv, int lo, int hi, float* o,
+                                                 int64_t ldo, int H, int dh) {
+  extern __shared__ float sc[];  // [nk] scores, then [dh] query
+  __shared__ float red[256];
+  const int r = blockIdx.x / H, h = blockIdx.x % H;
+  const int nk = hi - lo + 1;
+  float* qs = sc + nk;
+  const float scale = 1.0f / sqrtf((float)dh);
+  for (int c = threadIdx.x; c < dh; c += 256) qs[c] = q[(int64_t)r * ldq + h * dh + c];
+  __syncthreads();
+  const int64_t row_off = (int64_t)(kv.map ? kv.map[r] : r) * kv.s_row + h * dh;
+  float mx = -INFINITY;
+  for (int j = threadIdx.x; j < nk; j += 256) {
+    const int64_t base = row_off + (int64_t)(lo + j - 1) * kv.s_pos;
+    float acc = 0.f;
+    for (int c = 0; c < dh; ++c) acc = fmaf(qs[c], ld_f<TK>(kv.k, base + c), acc);
+    sc[j] = acc * scale;
+    mx = fmaxf(mx, sc[j]);
+  }
+  mx = block_max(mx, red);
+  float sum = 0.f;
+  for (int j = threadIdx.x; j < nk; j += 256) {
+    sc[j] = expf(sc[j] - mx);
+    sum += sc[j];
+  }
+  sum = block_sum(sum, red);  // contains barriers: scores are visible below
+  const float inv = 1.0f / sum;
+  for (int c = threadIdx.x; c < dh; c += 256) {
+    float acc = 0.f;
+    for (int j = 0; j < nk; ++j) acc = fmaf(sc[j], ld_f<TK>(kv.v, row_off + (int64_t)(lo + j - 1) * kv.s_pos + c), acc);
+    o[(int64_t)r * ldo + h * dh + c] = acc * inv;
+  }
+}
+
+// p_j = softmax(s)_j; dv_j = p_j do; dp_j = do . v_j; ds_j = p_j (dp_j - sum_i p_i dp_i);
+// dq = scale sum_j ds_j k_j; dk_j = scale ds_j q
+template <typename TK>
+__global__ __launch_bounds__(256) void k_attn_bwd(const float* q, int64_t ldq, KV kv, int lo, int hi,
+                                                 const float* dout, int64_t lddo, float* dq, int64_t lddq, DKV dkv,
+                                                 int H, int dh) {
+  extern __shared__ float sc[];  // [nk] p, [nk] ds, [dh] q, [dh] do
+  __shared__ float red[256];
+  const int r = blockIdx.x / H, h = blockIdx.x % H;
+  const int nk = hi - lo + 1;
+  float* ds = sc + nk;
+  float* qs = ds + nk;
+  float* dos = qs + dh;
+  const float scale = 1.0f / sqrtf((float)dh);
+  for (int c = threadIdx.x; c < dh; c += 256) {
+    qs[c] = q[(int64_t)r * ldq + h * dh + c];
+    dos[c] = dout[(int64_t)r * lddo + h * dh + c];
+  }
+  __syncthreads();
+  const int64_t row_off = (int64_t)(kv.map ? kv.map[r] : r) * kv.s_row + h * dh;
+  float mx = -INFINITY;
+  for (int j = threadIdx.x; j < nk; j += 256) {
+    const int64_t base = row_off + (int64_t)(lo + j - 1) * kv.s_pos;
+    float acc = 0.f;
+    for (int c = 0; c < dh; ++c) acc = fmaf(qs[c], ld_f<TK>(kv.k, base + c), acc);
+    sc[j] = acc * scale;
+    mx = fmaxf(mx, sc[j]);
+  }
+  mx = block_max(mx, red);
+  float sum = 0.f;
+  for (int j = threadIdx.x; j < nk; j += 256) {
+    sc[j] = expf(sc[j] - mx);
+    sum += sc[j];
+  }
+  sum = block_sum(sum, red);
+  const float inv = 1.0f / sum;
+  float dsum = 0.f;
+  for (int j = threadIdx.x; j < nk; j += 256) {
+    const int64_t base = row_off + (int64_t)(lo + j - 1) * kv.s_pos;
+    sc[j] *= inv;
+    float dp = 0.f;
+    for (int c = 0; c < dh; ++c) dp = fmaf(dos[c], ld_f<TK>(kv.v, base + c), dp);
+    ds[j] = dp;
+    dsum += sc[j] * dp;
+  }
+  dsum = block_sum(dsum, red);
+  for (int j = threadIdx.x; j < nk; j += 256) ds[j] = sc[j] * (ds[j] - dsum);
+  __syncthreads();
+  for (int c = threadIdx.x; c < dh; c += 256) {
+    float acc = 0.f;
+    for (int j = 0; j < nk; ++j) acc = fmaf(ds[j], ld_f<TK>(kv.k, row_off + (int64_t)(lo + j - 1) * kv.s_pos + c), acc);
+    dq[(int64_t)r * lddq + h * dh + c] = acc * scale;
+  }
+  if (!dkv.k) return;
+  const int64_t drow = (int64_t)(dkv.map ? dkv.map[r] : r) * dkv.s_row + h * dh;
+  for (int64_t idx = threadIdx.x; idx < (int64_t)nk * dh; idx += 256) {
+    const int j = (int)(idx / dh), c = (int)(idx % dh);
+    const int64_t o = drow + (int64_t)(lo + j - 1) * dkv.s_pos + c;
+    dkv.k[o] += scale * ds[j] * qs[c];
+    dkv.v[o] += sc[j] * dos[c];
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_gather_e(float* x, int64_t ldx, const T* e, int64_t sb, int64_t st,
+                                                 const int* map, int t, int n, int d) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)n * d) return;
+  const int r = (int)(idx / d), c = (int)(idx % d);
+  x[(int64_t)r * ldx + c] = to_f<T>(e[(int64_t)map[r] * sb + (int64_t)(t - 1) * st + c]);
+}
+
+__global__ __launch_bounds__(256) void k_scatter_add_e(float* de, int64_t sb, int64_t st, const float* g, int64_t ldg,
+                                                      const int* map, int t, int n, int d) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)n * d) return;
+  const int r = (int)(idx / d), c = (int)(idx % d);
+  de[(int64_t)map[r] * sb + (int64_t)(t - 1) * st + c] += g[(int64_t)r * ldg + c];
+}
+
+__global__ __launch_bounds__(256) void k_sigmoid_bias(float* g, int64_t ld, const float* bias, int n, int d) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)n * d) return;
+  const int r = (int)(idx / d), c = (int)(idx % d);
+  float* p = g + (int64_t)r * ld + c;
+  *p = sigm(*p + bias[c]);
+}
+
+__global__ __launch_bounds__(256) void k_merge_fwd(int gated, float* u, const float* e, int64_t lde, const float* g,
+                                                  const float* w, int64_t ldw, float alpha, int n, int d) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)n * d) return;
+  const int r = (int)(idx / d), c = (int)(idx % d);
+  const float ev = e[(int64_t)r * lde + c], gv = g[idx], wv = w[(int64_t)r * ldw + c];
+  u[idx] = gated ? ev + alpha * gv * wv : gv * ev + (1.0f - gv) * wv;
+}
+
+__global__ __launch_bounds__(256) void k_merge_bwd(int gated, const float* du, const float* e, int64_t lde,
+                                                  const float* g, const float* w, int64_t ldw, float alpha, float* dpre,
+                                                  float* dw, float* de, int64_t ldde, int n, int d) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)n * d) return;
+  const int r = (int)(idx / d), c = (int)(idx % d);
+  const float duv = du[idx], ev = e[(int64_t)r * lde + c], gv = g[idx], wv = w[(int64_t)r * ldw + c];
+  const float gp = gv * (1.0f - gv);
+  if (gated) {
+    dpre[idx] = alpha * duv * wv * gp;
+    dw[idx] = alpha * gv * duv;
+    de[(int64_t)r * ldde + c] = duv;
+  } else {
+    dpre[idx] = duv * (ev - wv) * gp;
+    dw[idx] = duv * (1.0f - gv);
+    de[(int64_t)r * ldde + c] = duv * gv;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_swiglu_fwd(const float* a, const float* u, float* act, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  act[i] = a[i] * sigm(a[i]) * u[i];
+}
+
+__global__ __launch_bounds__(256) void k_swiglu_bwd(const float* a, const float* u, const float* dact, float* da,
+                                                   float* du, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const float s = sigm(a[i]);
+  da[i] = dact[i] * u[i] * s * (1.0f + a[i] * (1.0f - s));
+  du[i] = dact[i] * a[i] * s;
+}
+
+// block per row
+__global__ __launch_bounds__(256) void k_logsoftmax_bwd(const float* logits, int V, const int* tokens, int64_t tok_sb,
+                                                       const float* w, int64_t w_sb, const int* map, const int* split,
+                                                       int t, float* logp, int64_t logp_sb, float* dlogits) {
+  __shared__ float red[256];
+  const int r = blockIdx.x;
+  const int b = map[r];
+  const float* z = logits + (int64_t)r * V;
+  float* dz = dlogits + (int64_t)r * V;
+  if (t < split[r]) {
+    for (int c = threadIdx.x; c < V; c += 256) dz[c] = 0.f;
+    return;
+  }
+  float mx = -INFINITY;
+  for (int c = threadIdx.x; c < V; c += 256) mx = fmaxf(mx, z[c]);
+  mx = block_max(mx, red);
+  float s = 0.f;
+  for (int c = threadIdx.x; c < V; c += 256) s += expf(z[c] - mx);
+  s = block_sum(s, red);
+  const float lse = mx + logf(s);
+  const int tok = tokens[(int64_t)b * tok_sb + t];
+  const float wt = w[(int64_t)b * w_sb + t];
+  for (int c = threadIdx.x; c < V; c += 256) dz[c] = wt * ((c == tok ? 1.0f : 0.0f) - expf(z[c] - lse));
+  if (threadIdx.x == 0 && logp) logp[(int64_t)b * logp_sb + t] = z[tok] - lse;
+}
+
+__global__ __launch_bounds__(256) void k_add(float* y, int64_t ldy, const float* a, int64_t lda, const float* b,
+                                            int64_t ldb, int n, int d) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)n * d) return;
+  const int r = (int)(idx / d), c = (int)(idx % d);
+  y[(int64_t)r * ldy + c] = a[(int64_t)r * lda + c] + (b ? b[(int64_t)r * ldb + c] : 0.f);
+}
+
+inline unsigned nblk(int64_t n) { return (unsigned)((n + 255) / 256); }
+
+}  // namespace
+
+void mm(int M, int N, int K, const float* a, int64_t a_si, int64_t a_sk, const void* b, int bdt, int64_t b_sk,
+        int64_t b_sj, float* c, int64_t c_si, bool accumulate, hipStream_t s) {
+  if (M <= 0 || N <= 0) return;
+  dim3 grid((N + 15) / 16, (M + 15) / 16);
+  if (bdt)
+    hipLaunchKernelGGL(k_mm<uint16_t>, grid, dim3(256), 0, s, M, N, K, a, a_si, a_sk, (const uint16_t*)b, b_sk, b_sj, c,
+                       c_si, (int)accumulate);
+  else
+    hipLaunchKernelGGL(k_mm<float>, grid, dim3(256), 0, s, M, N, K, a, a_si, a_sk, (const float*)b, b_sk, b_sj, c,
+                       c_si, (int)accumulate);
+}
+
+void rms_fwd(const float* x, int64_t ldx, const float* gain, float* y, int64_t ldy, float* rstd, int n, int d,
+             float eps, hipStream_t s) {
+  if (n > 0) hipLaunchKernelGGL(k_rms_fwd, dim3(n), dim3(256), 0, s, x, ldx, gain, y, ldy, rstd, d, eps);
+}
+
+void rms_bwd(const float* x, int64_t ldx, const float* gain, const float* rstd, const float* dy, int64_t ldy,
+             float* dx, int64_t lddx, int n, int d, bool accumulate, hipStream_t s) {
+  if (n > 0)
+    hipLaunchKernelGGL(k_rms_bwd, dim3(n), dim3(256), 0, s, x, ldx, gain, rstd, dy, ldy, dx, lddx, d, (int)accumulate);
+}
+
+void colsum(float* dst, const float* a, int64_t lda, const float* b, int64_t ldb, const float* rs, int n, int d,
+            hipStream_t s) {
+  if (n > 0 && dst) hipLaunchKernelGGL(k_colsum, dim3(nblk(d)), dim3(256), 0, s, dst, a, lda, b, ldb, rs, n, d);
+}
+
+void rope(float* x, int64_t ld, int n, int d, int dh, int t, const double* inv_freq, int sign, hipStream_t s) {
+  if (n > 0) hipLaunchKernelGGL(k_rope, dim3(nblk((int64_t)n * (d / 2))), dim3(256), 0, s, x, ld, n, d, dh, t, inv_freq, sign);
+}
+
+void attn_fwd(const float* q, int64_t ldq, KV kv, int lo, int hi, float* o, int64_t ldo, int n, int H, int dh,
+              hipStream_t s) {
+  if (n <= 0) return;
+  const size_t lds = (size_t)(hi - lo + 1 + dh) * sizeof(float);
+  if (kv.dt)
+    hipLaunchKernelGGL(k_attn_fwd<uint16_t>, dim3(n * H), dim3(256), lds, s, q, ldq, kv, lo, hi, o, ldo, H, dh);
+  else
+    hipLaunchKernelGGL(k_attn_fwd<float>, dim3(n * H), dim3(256), lds, s, q, ldq, kv, lo, hi, o, ldo, H, dh);
+}
+
+void attn_bwd(const float* q, int64_t ldq, KV kv, int lo, int hi, const float* dout, int64_t lddo, float* dq,
+              int64_t lddq, DKV dkv, int n, int H, int dh, hipStream_t s) {
+  if (n <= 0) return;
+  const size_t lds = (size_t)(2 * (hi - lo + 1) + 2 * dh) * sizeof(float);
+  if (kv.dt)
+    hipLaunchKernelGGL(k_attn_bwd<uint16_t>, dim3(n * H), dim3(256), lds, s, q, ldq, kv, lo, hi, dout, lddo, dq, lddq,
+                       dkv, H, dh);
+  else
+    hipLaunchKernelGGL(k_attn_bwd<float>, dim3(n * H), dim3(256), lds, s, q, ldq, kv, lo, hi, dout, lddo, dq, lddq,
+                       dkv, H, dh);
+}
+
+void gather_e(float* x, int64_t ldx, const void* e, int dt, int64_t sb, int64_t st, const int* map, int t, int n,
+              int d, hipStream_t s) {
+  if (n <= 0) return;
+  if (dt)
+    hipLaunchKernelGGL(k_gather_e<uint16_t>, dim3(nblk((int64_t)n * d)), dim3(256), 0, s, x, ldx, (const uint16_t*)e,
+                       sb, st, map, t, n, d);
+  else
+    hipLaunchKernelGGL(k_gather_e<float>, dim3(nblk((int64_t)n * d)), dim3(256), 0, s, x, ldx, (const float*)e, sb,
+                       st, map, t, n, d);
+}
+
+void scatter_add_e(float* de, int64_t sb, int64_t st, const float* g, int64_t ldg, const int* map, int t, int n,
+                   int d, hipStream_t s) {
+  if (n > 0 && de)
+    hipLaunchKernelGGL(k_scatter_add_e, dim3(nblk((int64_t)n * d)), dim3(256), 0, s, de, sb, st, g, ldg, map, t, n, d);
+}
+
+void sigmoid_bias(float* g, int64_t ld, const float* bias, int n, int d, hipStream_t s) {
+  if (n > 0) hipLaunchKernelGGL(k_sigmoid_bias, dim3(nblk((int64_t)n * d)), dim3(256), 0, s, g, ld, bias, n, d);
+}
+
+void merge_fwd(int gated, float* u, const float* e, int64_t lde, const float* g, const float* w, int64_t ldw,
+               float alpha, int n, int d, hipStream_t s) {
+  if (n > 0)
+    hipLaunchKernelGGL(k_merge_fwd, dim3(nblk((int64_t)n * d)), dim3(256), 0, s, gated, u, e, lde, g, w, ldw, alpha, n, d);
+}
+
+void merge_bwd(int gated, const float* du, const float* e, int64_t lde, const float* g, const float* w, int64_t ldw,
+               float alpha, float* dpre, float* dw, float* de, int64_t ldde, int n, int d, hipStream_t s) {
+  if (n > 0)
+    hipLaunchKernelGGL(k_merge_bwd, dim3(nblk((int64_t)n * d)), dim3(256), 0, s, gated, du, e, lde, g, w, ldw, alpha,
+                       dpre, dw, de, ldde, n, d);
+}
+
+void swiglu_fwd(const float* a, const float* u, float* act, int n, int F, hipStream_t s) {
+  const int64_t m = (int64_t)n * F;
+  if (m > 0) hipLaunchKernelGGL(k_swiglu_fwd, dim3(nblk(m)), dim3(256), 0, s, a, u, act, m);
+}
+
+void swiglu_bwd(const float* a, const float* u, const float* dact, float* da, float* du, int n, int F,
+                hipStream_t s) {
+  const int64_t m = (int64_t)n * F;
+  if (m > 0) hipLaunchKernelGGL(k_swiglu_bwd, dim3(nblk(m)), dim3(256), 0, s, a, u, dact, da, du, m);
+}
+
+void logsoftmax_bwd(const float* logits, int V, const int* tokens, int64_t tok_sb, const float* w, int64_t w_sb,
+                    const int* map, const int* split, int t, float* logp, int64_t logp_sb, float* dlogits, int n,
+                    hipStream_t s) {
+  if (n > 0)
+    hipLaunchKernelGGL(k_logsoftmax_bwd, dim3(n), dim3(256), 0, s, logits, V, tokens, tok_sb, w, w_sb, map, split, t,
+                       logp, logp_sb, dlogits);
+}
+
+void add(float* y, int64_t ldy, const float* a, int64_t lda, const float* b, int64_t ldb, int n, int d,
+         hipStream_t s) {
+  if (n > 0) hipLaunchKernelGGL(k_add, dim3(nblk((int64_t)n * d)), dim3(256), 0, s, y, ldy, a, lda, b, ldb, n, d);
+}
+
+}  // namespace bwd
+}  // namespace rlt

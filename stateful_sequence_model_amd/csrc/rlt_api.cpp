@@ -23,6 +23,7 @@
 
 #include "../../include/rlt.h"
 #include "../../include/rlt_debug.h"
+#include "bwd.h"
 #include "rlt_internal.h"
 
 using namespace rlt;
@@ -1402,6 +1403,54 @@ extern "C" int rlt_trajectory_log_ratio(rlt_ctx* c, int32_t B, const int32_t* le
   HIP_TRY(hipMemcpy(c->mem_lens, range.data() + B, (size_t)B * 4, hipMemcpyHostToDevice));
   launch_traj_ratio(B, c->mem_offs, c->mem_lens, logp, logp_stride_b, logmu, logmu_stride_b, out, s);
   HIP_TRY(hipGetLastError());
+  return RLT_OK;
+}
+
+extern "C" int rlt_replay_backward(rlt_ctx* c, const rlt_backward_io* io, const rlt_grads* gr, void* stream) {
+  if (!c || !io || !gr) return fail(RLT_EINVAL, "null argument");
+  if (!io->len_host || !io->split_host || !io->e || !io->tokens || !io->w || !io->mem.k || !io->mem.v)
+    return fail(RLT_EINVAL, "null input array");
+  if ((io->dmem_k == nullptr) != (io->dmem_v == nullptr)) return fail(RLT_EINVAL, "dmem_k and dmem_v: both or none");
+  if (io->B < 1) return fail(RLT_ESHAPE, "B < 1");
+  if (io->e_stride_b < 0 || io->e_stride_t < 0 || io->tok_stride_b < 0 || io->w_stride_b < 0 ||
+      io->logp_stride_b < 0 || io->de_stride_b < 0 || io->de_stride_t < 0 || io->mem.stride_g < 0 ||
+      io->mem.stride_b < 0 || io->mem.stride_t < 0 || io->dmem_stride_g < 0 || io->dmem_stride_b < 0 ||
+      io->dmem_stride_t < 0)
+    return fail(RLT_EINVAL, "negative stride");
+  for (int b = 0; b < io->B; ++b) {
+    if (io->len_host[b] < 2) return fail(RLT_ESHAPE, "len[%d] < 2", b);
+    if (io->split_host[b] < 1 || io->split_host[b] > io->len_host[b] - 1)
+      return fail(RLT_EINVAL, "split[%d] outside 1 .. len - 1", b);
+  }
+  const rlt_config& cf = c->cfg;
+  if (cf.merge_gate != RLT_GATE_VECTOR || cf.merge_rank != 0 || cf.block_order != RLT_ORDER_SXF)
+    return fail(RLT_EUNSUPPORTED, "the replay backward covers the vector gate, full-rank W_s and order SXF");
+  bwd::Model m;
+  m.cfg = cf;
+  m.dt = c->dt;
+  m.s_star = c->s_star;
+  m.merge_norm = c->merge_norm;
+  m.merge_bg = c->merge_bg;
+  m.out_norm = c->out_norm;
+  m.merge_wg = c->merge_wg;
+  m.merge_ws = c->merge_ws;
+  m.w_out = c->w_out;
+  m.norm_s = c->norm_s;
+  m.norm_m = c->norm_m;
+  m.norm_d = c->norm_d;
+  m.wq = c->wq;
+  m.wk = c->wk;
+  m.wv = c->wv;
+  m.wo = c->wo;
+  m.wqm = c->wqm;
+  m.wom = c->wom;
+  m.w_gate = c->w_gate;
+  m.w_up = c->w_up;
+  m.w_down = c->w_down;
+  m.inv_freq = c->inv_freq;
+  std::string err;
+  const int rc = bwd::replay_backward(m, io, gr, (hipStream_t)stream, err);
+  if (rc) return fail(rc, "%s", err.c_str());
   return RLT_OK;
 }
 

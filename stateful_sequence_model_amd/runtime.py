@@ -219,6 +219,57 @@ class Decoder:
         stc = st.c()
         return A.rlt_replay_sequence(self.ctx, stc, io, current_stream() if stream is None else stream)
 
+    def grad_buffers(self) -> Dict[str, torch.Tensor]:
+        """Zeroed float32 gradient buffers, one per parameter of the default
+        variants (keys as the parameters)."""
+        names = ["s_star", "merge.wg", "merge.bg", "out.norm", "out.w"]
+        if self.cfg.merge == "gated":
+            names += ["merge.norm", "merge.ws"]
+        names += ["layer.%d.%s" % (l, n) for l in range(self.cfg.L) for n in _MATRICES + _LAYER_VECS]
+        return {n: torch.zeros(self.params[n].shape, dtype=torch.float32, device=self.device) for n in names}
+
+    def replay_backward(self, grads: Dict[str, torch.Tensor], lens: np.ndarray, splits: np.ndarray,
+                        e: torch.Tensor, mem: A.rlt_memory, tokens: torch.Tensor, w: torch.Tensor,
+                        logp: Optional[torch.Tensor] = None, de: Optional[torch.Tensor] = None,
+                        dmem_k: Optional[torch.Tensor] = None, dmem_v: Optional[torch.Tensor] = None,
+                        stream=None) -> int:
+        """Full-BPTT gradients of sum_b sum_t w[b, t] log p(x_{t+1} | x_{1:t}),
+        accumulated into ``grads`` (from ``grad_buffers``); e [B, T, d];
+        tokens int32 [B, T]; w, logp float32 [B, T]; de float32 [B, T, d];
+        dmem_k / dmem_v float32 [G, B, T, d]."""
+        lens = np.ascontiguousarray(lens, dtype=np.int32)
+        splits = np.ascontiguousarray(splits, dtype=np.int32)
+        io = A.rlt_backward_io()
+        io.B = len(lens)
+        io.len_host = lens.ctypes.data
+        io.split_host = splits.ctypes.data
+        io.e, io.e_stride_b, io.e_stride_t = e.data_ptr(), e.stride(0), e.stride(1)
+        io.mem = mem
+        io.tokens, io.tok_stride_b = tokens.data_ptr(), tokens.stride(0)
+        io.w, io.w_stride_b = w.data_ptr(), w.stride(0)
+        if logp is not None:
+            io.logp, io.logp_stride_b = logp.data_ptr(), logp.stride(0)
+        if de is not None:
+            io.de, io.de_stride_b, io.de_stride_t = de.data_ptr(), de.stride(0), de.stride(1)
+        if dmem_k is not None:
+            io.dmem_k, io.dmem_v = dmem_k.data_ptr(), dmem_v.data_ptr()
+            io.dmem_stride_g, io.dmem_stride_b, io.dmem_stride_t = dmem_k.stride(0), dmem_k.stride(1), dmem_k.stride(2)
+        L = self.cfg.L
+        gr = A.rlt_grads()
+        keep = []
+        for field, key in (("s_star", "s_star"), ("merge_norm", "merge.norm"), ("merge_wg", "merge.wg"),
+                           ("merge_bg", "merge.bg"), ("merge_ws", "merge.ws"), ("out_norm", "out.norm"),
+                           ("w_out", "out.w")):
+            if key in grads:
+                setattr(gr, field, grads[key].data_ptr())
+        for name in _MATRICES + _LAYER_VECS:
+            keys = ["layer.%d.%s" % (l, name) for l in range(L)]
+            if all(k in grads for k in keys):
+                arr = (A.P * L)(*[grads[k].data_ptr() for k in keys])
+                keep.append(arr)
+                setattr(gr, name, C.cast(arr, C.POINTER(A.P)))
+        return A.rlt_replay_backward(self.ctx, io, gr, current_stream() if stream is None else stream)
+
     def score(self, s: torch.Tensor, tokens: torch.Tensor, logp: torch.Tensor, *, temperature=1.0, top_k=0,
               top_p=1.0, logmu=None, logmu_behaviour=None, ratio=None, stream=None) -> int:
         io = A.rlt_score_io(s.shape[0], s.data_ptr(), tokens.data_ptr(), logp.data_ptr(), temperature, top_k,

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
     assert {"rlt_create", "rlt_destroy", "rlt_state_layout", "rlt_last_error", "rlt_init_state",
             "rlt_decoder_step", "rlt_replay_sequence", "rlt_score_logprobs", "rlt_sync_error",
             "rlt_memory_append", "rlt_memory_prefill", "rlt_snapshot_bytes", "rlt_state_snapshot",
-            "rlt_state_restore", "rlt_trajectory_log_ratio", "rlt_dbg_gemm"} <= decl
+            "rlt_state_restore", "rlt_trajectory_log_ratio", "rlt_replay_backward", "rlt_dbg_gemm"} <= decl
     for name in decl:
         assert hasattr(L, name), name
     assert decl == set(_abi.exported_symbols())
@@ -42,7 +42,8 @@ def test_ctypes_layout_matches_header(tmp_path):
     structs = {"rlt_config": _abi.rlt_config, "rlt_weights": _abi.rlt_weights, "rlt_state": _abi.rlt_state,
                "rlt_memory": _abi.rlt_memory, "rlt_step_io": _abi.rlt_step_io,
                "rlt_replay_io": _abi.rlt_replay_io, "rlt_score_io": _abi.rlt_score_io,
-               "rlt_memory_weights": _abi.rlt_memory_weights, "rlt_snapshot_header": _abi.rlt_snapshot_header}
+               "rlt_memory_weights": _abi.rlt_memory_weights, "rlt_snapshot_header": _abi.rlt_snapshot_header,
+               "rlt_grads": _abi.rlt_grads, "rlt_backward_io": _abi.rlt_backward_io}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "rlt.h"', "int main(void){"]
     for sname, cls in structs.items():
         lines.append('printf("%s %%zu\\n", sizeof(%s));' % (sname, sname))
@@ -125,6 +126,7 @@ def test_null_arguments_are_rejected():
     assert L.rlt_state_snapshot(None, None, None, 0, None, None) == _abi.RLT_EINVAL
     assert L.rlt_state_restore(None, None, None, 0, None, None) == _abi.RLT_EINVAL
     assert L.rlt_memory_prefill(None, None, None, 0, 0, None, None, 0, 0, None) == _abi.RLT_EINVAL
+    assert L.rlt_replay_backward(None, None, None, None) == _abi.RLT_EINVAL
 
 
 def test_snapshot_size_and_magic():
