@@ -135,7 +135,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="reference_depth")
+    ap.add_argument("--workload", default=None,
+                    help="preset (default: reference_depth; small_batched for --mode backward)")
     ap.add_argument("--batch", type=int, default=0, help="override B")
     ap.add_argument("--t-center", type=int, default=0, help="centre of the timed positions (default T/2)")
     ap.add_argument("--no-graph", action="store_true")
@@ -144,9 +145,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate", action="store_true",
                     help="also time a plain 4 GiB device copy and read-only sum (achievable HBM rates)")
-    ap.add_argument("--mode", choices=("step", "memory_prefill"), default="step",
+    ap.add_argument("--mode", choices=("step", "memory_prefill", "backward"), default="step",
                     help="step: the decoder transition (default); memory_prefill: token-parallel "
-                         "construction of the encoder memory of the whole batch")
+                         "construction of the encoder memory of the whole batch; backward: full-BPTT "
+                         "replay backward of the whole batch")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -159,11 +161,13 @@ def main():
     import synth
     from stateful_sequence_model_amd import Decoder, DecoderState, ModelConfig, _abi, to_device
 
-    wl = synth.PRESETS[args.workload]
+    wl = synth.PRESETS[args.workload or ("small_batched" if args.mode == "backward" else "reference_depth")]
     if args.batch:
         wl = wl.with_(B=args.batch)
     if args.mode == "memory_prefill":
         return bench_memory_prefill(args, wl)
+    if args.mode == "backward":
+        return bench_backward(args, wl)
     B, T = wl.B, wl.T
     es = 2 if wl.dtype == "bf16" else 4
     K, Wu = args.steps, args.warmup
@@ -358,6 +362,114 @@ def bench_memory_prefill(args, wl):
                      "frac": round(tflops / peak, 4), "traffic": None,
                      "algorithmic_flops_per_call": flops, "hbm_bytes_min_per_call": int(moved)},
     }), flush=True)
+
+
+def bench_backward(args, wl):
+    """Full-BPTT replay backward [RLT §5.4, App. B] of B sequences of T
+    tokens (every position scored, loss weights N(0,1)): one
+    rlt_replay_backward call per timed step, gradients of every parameter,
+    e_t and the memory. The kernels compute in float32 on the vector ALUs
+    (no matrix cores), so the call's algorithmic rate is reported against the
+    fp32 vector peak."""
+    import numpy as np
+    import torch
+    import synth
+    from stateful_sequence_model_amd import Decoder, ModelConfig, _abi
+
+    B, T, d, G, L = wl.B, wl.T, wl.d, wl.G, wl.L
+    steps = min(args.steps, 5)
+    torch.cuda.set_device(0)
+    raw = synth.make_weights(wl)
+    cfg = ModelConfig(L=L, d=d, H=wl.H, dh=wl.dh, W=wl.W, G=G, F=wl.F, V=wl.V, dtype=wl.dtype,
+                      merge=wl.merge, alpha=wl.alpha, eps=wl.eps, rope_theta=wl.rope_theta, pos=wl.pos)
+    dec = Decoder(cfg, raw, max_rows=B, max_ctx=T)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(wl.seed)
+    tdt = cfg.torch_dtype
+    e = torch.randn((B, T, d), generator=gen, device="cuda").to(tdt)
+    mk = torch.randn((G, B, T, d), generator=gen, device="cuda").to(tdt)
+    mv = torch.randn((G, B, T, d), generator=gen, device="cuda").to(tdt)
+    mem = Decoder.memory(mk, mv, torch.full((B,), T, dtype=torch.int32, device="cuda"))
+    tokens = torch.randint(0, wl.V, (B, T), generator=gen, device="cuda", dtype=torch.int32)
+    w = torch.randn((B, T), generator=gen, device="cuda")
+    de = torch.zeros((B, T, d), device="cuda")
+    dmk = torch.zeros((G, B, T, d), device="cuda")
+    dmv = torch.zeros((G, B, T, d), device="cuda")
+    grads = dec.grad_buffers()
+    lens = np.full(B, T, dtype=np.int32)
+    splits = np.ones(B, dtype=np.int32)
+
+    def call():
+        _abi.check(dec.replay_backward(grads, lens, splits, e, mem, tokens, w, de=de, dmem_k=dmk, dmem_v=dmv),
+                   "rlt_replay_backward")
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    trans = B * (T - 1)
+    # algorithmic flops: forward products 2P, backward 4P (inputs and weights)
+    # per transition, P = decoder matrices + readout; attention forward
+    # 4 d (window + prefix) per layer, backward twice that
+    P = matrix_params(wl) + wl.V * d
+    att = sum(min(t, wl.W) + t for t in range(1, T))
+    flops = 6.0 * P * trans + 12.0 * d * L * att * B
+    tflops = flops / (ms / 1e3) / 1e12
+    peak = 157.3
+    log("replay backward: %.1f ms per call (%d transitions), %.1f transitions/s, %.2f TFLOP/s" %
+        (ms, trans, trans / (ms / 1e3), tflops))
+    out = {
+        "metric": "replay-backward transitions/sec (full BPTT, seq*token)",
+        "value": round(trans / (ms / 1e3), 1), "unit": "transitions/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl.name + " replay backward", "L_D": L, "d": d, "batch": B, "T": T, "W": wl.W,
+                   "G": G, "params": wl.dtype},
+        "roofline": {"bound": "alu", "achieved": round(tflops, 3), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 5), "traffic": None, "scope": "whole call (fp32 vector ALU)",
+                     "algorithmic_flops_per_call": flops},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_backward(wl, raw, budget_s=args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_backward(wl, raw, budget_s: float) -> dict:
+    """The gradient oracle (float64 autograd twin) on one sequence, growing
+    its length until the budget is spent."""
+    import numpy as np
+    import torch
+    from oracle.rlt_oracle import Config
+    from oracle.rlt_grad import replay_grads
+
+    def widen(a):
+        if a.dtype == np.uint16:
+            return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        return a.astype(np.float64)
+
+    cfg = Config(L=wl.L, d=wl.d, H=wl.H, dh=wl.dh, W=wl.W, G=wl.G, F=wl.F, V=wl.V, merge=wl.merge,
+                 alpha=wl.alpha, eps=wl.eps, rope_theta=wl.rope_theta, pos=wl.pos)
+    w = {k: widen(v) for k, v in raw.items()}
+    rng = np.random.default_rng(1)
+    n, spent, done = 4, 0.0, 0
+    while spent < budget_s and n <= wl.T:
+        sq = dict(E=rng.standard_normal((n, wl.d)), mem_k=[rng.standard_normal((n, wl.d)) for _ in range(wl.G)],
+                  mem_v=[rng.standard_normal((n, wl.d)) for _ in range(wl.G)], tokens=rng.integers(0, wl.V, n),
+                  length=n, split=1, w=rng.standard_normal(n))
+        t0 = time.perf_counter()
+        replay_grads(cfg, w, [sq])
+        spent += time.perf_counter() - t0
+        done += n - 1
+        n *= 2
+    return {"value": round(done / spent, 2), "unit": "transitions/s", "cores": torch.get_num_threads(),
+            "kind": "oracle", "sample": "float64 autograd twin, single sequences of 4, 8, ... tokens "
+            "(%d transitions, %.1f s)" % (done, spent)}
 
 
 if __name__ == "__main__":
