@@ -6,7 +6,7 @@
 // call; the batch is the M dimension, so these products are HBM-bound for
 // the batch sizes of a decoder step.
 //
-// bf16 path (gfx950 MFMA v_mfma_f32_16x16x32_bf16):
+// bf16 path, calls of at most 32 rows (gfx950 MFMA v_mfma_f32_16x16x32_bf16):
 //   workgroup = 4 waves; all 4 waves own the same output tile (16*MB rows x
 //   one pair of 16-column blocks) and each streams a disjoint quarter of the
 //   workgroup's K range, so A and W are each read once per workgroup; the
@@ -34,174 +34,170 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs g, Epi<uint16_t> epi
   gemm_bf16_body<MB>(g, epi, blockIdx.x, blockIdx.y, blockIdx.z, lds);
 }
 
-// Wide tile for batches above 32 rows: 4 column pairs (128 columns) x 16*MB
-// rows per workgroup. Wave w owns pair 4*blockIdx.x + w over the whole K
-// range of the workgroup, so its accumulators are final (no cross-wave
-// reduction). The activation tile, which every column of the call needs, is
-// loaded from L2 once per workgroup and shared by the four waves through LDS;
-// the weights, each read by one wave only, go straight from HBM into
-// registers in MFMA operand layout. K advances in stages of 64 with P stages
-// of loads in flight (a register ring; the activation part of a stage is
-// written to one of two LDS buffers just before it is used).
-// LDS layout of a stage: block (mb, s) of 1 KB holds, at lane position L,
-// the 8 activations of row mb*16 + L%16 at k = 32 s + 8 (L/16): exactly the
-// MFMA A operand of lane L, so both the writes and the reads are contiguous.
-// grid: npairs / 4 * S * m-tiles (1-D, decoded below); block 256; K range
-// of a workgroup = kslice (a multiple of 64)
-template <int MB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, MB >= 8 ? 1 : 2))) void k_gemm_bf16_wide(
-    GemmArgs g, Epi<uint16_t> epi) {
-  constexpr int R = MB * 16;
-  constexpr int NA = MB / 2;  // 16-byte activation chunks per thread per stage
-  constexpr int PW = 4;       // weight stages in flight (even: a stage's LDS buffer is p & 1)
-  __shared__ __attribute__((aligned(16))) uint16_t sa[2][MB * 2 * 64 * 8];
-  __shared__ float s_rstd[R];
+// Tile for calls above 32 rows: 128 rows x BN virtual columns per
+// workgroup, K in stages of 64. Both operands are staged through LDS: a
+// stage is loaded with row-contiguous 16-byte loads (8 lanes read one
+// 128-byte row segment), PF stages ahead in registers, then written to one
+// of two LDS buffers whose rows are padded by 16 bytes so that the MFMA
+// operand reads (32 rows at one k offset) hit distinct banks. Four waves in
+// a 2 x 2 arrangement each multiply 64 rows by BN/2 columns with
+// v_mfma_f32_32x32x16_bf16, which issues close to its peak rate with four
+// accumulators per wave (the 16x16x32 form needs twice as many).
+// Virtual columns: the 32-column MFMA block j of a wave holds one column
+// pair, its first 16 columns being the pair's block ba and the last 16 its
+// block bb, so the epilogue of a pair combines lanes l and l ^ 16, which hold
+// the same rows (C layout: lane l holds column l % 32 of the block and rows
+// 8 g + 4 (l / 32) + q, g, q < 4).
+// grid: npairs / (BN / 32) * S * m-tiles (1-D, decoded as in the other
+// tiles); block 256; K range of a workgroup = kslice (a multiple of 64).
+template <int BN>
+__global__ __launch_bounds__(256) void k_gemm_bf16_tile(GemmArgs g, Epi<uint16_t> epi) {
+  constexpr int BM = 128, BK = 64, LDR = BK + 8, PF = 2;
+  constexpr int WN = BN / 2, NB = WN / 32;
+  constexpr int LA = BM * BK / 8 / 256, LW = BN * BK / 8 / 256;
+  constexpr int LDC = BN + 1;  // float row stride of the staged output tile
+  constexpr int STAGE_BYTES = 2 * (BM + BN) * LDR * 2, C_BYTES = BM * LDC * 4;
+  // the two operand buffers, reused for the output tile after the K loop
+  __shared__ __attribute__((aligned(16))) unsigned char smem[STAGE_BYTES > C_BYTES ? STAGE_BYTES : C_BYTES];
+  uint16_t(*sA)[BM * LDR] = reinterpret_cast<uint16_t(*)[BM * LDR]>(smem);
+  uint16_t(*sW)[BN * LDR] = reinterpret_cast<uint16_t(*)[BN * LDR]>(smem + 2 * BM * LDR * 2);
+  __shared__ float s_rstd[BM];
   __shared__ float s_part[256];
-  __shared__ int s_flag;
-  // 1-D grid of T = groups * S * mtiles workgroups, XCD-aware: the hardware
-  // deals consecutive workgroup ids to the 8 XCDs in turn, so id b runs on
-  // XCD b % 8. Tile t = (b % 8) * (T / 8) + b / 8 gives each XCD a contiguous
-  // run of tiles, ordered m-tile fastest, so the row tiles that read the same
-  // weight slice run together on one L2 (ids past 8 * (T / 8) map to themselves).
+  // XCD-aware order: consecutive workgroup ids run on the 8 XCDs in turn, so
+  // id b maps to tile (b % 8) * (T / 8) + b / 8 (ids past 8 * (T / 8) map to
+  // themselves), m-tile fastest: the row tiles of one weight slice share an L2
   const int T = gridDim.x, b = blockIdx.x, per = T >> 3;
   const int t = b < 8 * per ? (b & 7) * per + (b >> 3) : b;
-  const int nmt = (g.M + R - 1) / R;
+  const int nmt = (g.M + BM - 1) / BM;
   const int mt = t % nmt, split = (t / nmt) % g.S, grp = t / (nmt * g.S);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int pair = grp * 4 + wave;
-  int ba, bb;
-  pair_blocks(g, pair, ba, bb);
-  const int r16 = lane & 15, kq = (lane >> 4) * 8;
-  const uint16_t* wa = weight_row<uint16_t>(g, ba * 16 + r16) + kq;
-  const uint16_t* wb = weight_row<uint16_t>(g, bb * 16 + r16) + kq;
-  const int m0 = mt * R;
-  const uint16_t* ap[NA];
-#pragma unroll
-  for (int c = 0; c < NA; ++c) {
-    const int q = c * 256 + tid, blk = q >> 6, L = q & 63;
-    ap[c] = (const uint16_t*)g.A + (int64_t)(m0 + (blk >> 1) * 16 + (L & 15)) * g.lda + (blk & 1) * 32 + (L >> 4) * 8;
-  }
-  const bool norm_here = (g.S == 1 || g.tile_cnt != nullptr) && g.ssq_in != nullptr;
-  RowRstd<R> rr(g, norm_here ? m0 : 0);
-  f32x4_t acc[MB][2];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    acc[mb][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    acc[mb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = mt * BM, pair0 = grp * (BN / 32);
   const int kw0 = split * g.kslice;
   const int kw1 = min(kw0 + g.kslice, g.K);
-  const int nst = max(0, (kw1 - kw0) / 64);
-  // ring of register stages: weights PW stages ahead (HBM latency), the
-  // activations 2 stages ahead (L2 hits). Loads are issued in stage order
-  // and complete in order, so waiting for the activations of stage st also
-  // waits for the weights of stage st + 1 only.
-  bf16x8_t ra[2][NA];
-  bf16x8_t rw[PW][4];
-  auto load_a = [&](int pa, int st) {
-    const int k = kw0 + 64 * st;
+  const int nst = max(0, (kw1 - kw0) / BK);
+  // loads: thread covers rows lr + 32 i of the stage, 16-byte chunk lc
+  const int lr = tid >> 3, lc = (tid & 7) * 8;
+  const uint16_t* pa[LA];
 #pragma unroll
-    for (int c = 0; c < NA; ++c) ra[pa][c] = load8(ap[c] + k);
+  for (int i = 0; i < LA; ++i) pa[i] = (const uint16_t*)g.A + (int64_t)(m0 + lr + 32 * i) * g.lda + kw0 + lc;
+  const uint16_t* pw[LW];
+#pragma unroll
+  for (int i = 0; i < LW; ++i) {
+    const int v = lr + 32 * i;  // virtual column of the tile
+    int ba, bb;
+    pair_blocks(g, pair0 + v / 32, ba, bb);
+    pw[i] = weight_row<uint16_t>(g, ((v & 16) ? bb : ba) * 16 + (v & 15)) + kw0 + lc;
+  }
+  const bool norm_here = g.S == 1 && g.ssq_in != nullptr;
+  RowRstd<BM> rr(g, norm_here ? m0 : 0);
+  bf16x8_t ra[PF][LA], rw[PF][LW];
+  auto gload = [&](int p, int st) {
+#pragma unroll
+    for (int i = 0; i < LA; ++i) ra[p][i] = load8(pa[i] + BK * st);
+#pragma unroll
+    for (int i = 0; i < LW; ++i) rw[p][i] = load8(pw[i] + BK * st);
   };
-  auto load_w = [&](int pw, int st) {
-    const int k = kw0 + 64 * st;
-    rw[pw][0] = load8(wa + k);
-    rw[pw][1] = load8(wb + k);
-    rw[pw][2] = load8(wa + k + 32);
-    rw[pw][3] = load8(wb + k + 32);
+  auto lstore = [&](int p, int buf) {
+#pragma unroll
+    for (int i = 0; i < LA; ++i) *(bf16x8_t*)(sA[buf] + (lr + 32 * i) * LDR + lc) = ra[p][i];
+#pragma unroll
+    for (int i = 0; i < LW; ++i) *(bf16x8_t*)(sW[buf] + (lr + 32 * i) * LDR + lc) = rw[p][i];
   };
-  // The LDS buffer written at stage st is rewritten at st + 2: every wave has
-  // passed the barrier of st + 1, which follows its reads of stage st.
-  auto run_stage = [&](int p) {
-    uint16_t* buf = sa[p & 1];
+  f32x16_t acc[2][NB];
 #pragma unroll
-    for (int c = 0; c < NA; ++c) *(bf16x8_t*)(buf + (c * 256 + tid) * 8) = ra[p & 1][c];
-    __syncthreads();
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const bf16x8_t a = *(const bf16x8_t*)(buf + ((mb * 2 + s) * 64 + lane) * 8);
-        acc[mb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, rw[p][2 * s], acc[mb][0], 0, 0, 0);
-        acc[mb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, rw[p][2 * s + 1], acc[mb][1], 0, 0, 0);
-      }
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+  const int r32 = lane & 31, kh = (lane >> 5) * 8;
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8_t a[2], w[NB];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) a[i] = *(const bf16x8_t*)(sA[buf] + (wm * 64 + i * 32 + r32) * LDR + ks * 16 + kh);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) w[j] = *(const bf16x8_t*)(sW[buf] + (wn * WN + j * 32 + r32) * LDR + ks * 16 + kh);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], w[j], acc[i][j], 0, 0, 0);
+    }
   };
-  // branch-free steady state: refills are always issued, clamped to the last
-  // stage near the end (re-reads that hit in cache)
+  // Register slot s % PF holds stage s until it is written to LDS buffer
+  // s % 2, then takes stage s + PF. Stage st is multiplied from buffer st % 2
+  // while stages st + 1 .. st + PF are in flight; the barrier after it
+  // publishes stage st + 1 and frees buffer st % 2 for stage st + 2.
   if (nst > 0) {
-    load_a(0, 0);
-    load_a(1, min(1, nst - 1));
 #pragma unroll
-    for (int p = 0; p < PW; ++p) load_w(p, min(p, nst - 1));
-  }
-  int i = 0;
-  for (; i + PW <= nst; i += PW) {
-#pragma unroll
-    for (int p = 0; p < PW; ++p) {
-      run_stage(p);
-      load_a(p & 1, min(i + p + 2, nst - 1));
-      load_w(p, min(i + p + PW, nst - 1));
-    }
-  }
-  // tail (fewer than PW stages): the weights are all in flight already, the
-  // activations still need their 2-ahead refill; uniform conditions (the
-  // stage contains a barrier)
-#pragma unroll
-  for (int p = 0; p < PW; ++p)
-    if (i + p < nst) {
-      run_stage(p);
-      load_a(p & 1, min(i + p + 2, nst - 1));
-    }
-
-  if (g.S > 1) {
-    // C layout: lane holds rows 4*(lane/16)+i of each 16-row block, column lane%16
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int m = m0 + mb * 16 + (lane >> 4) * 4 + q;
-        if (m < g.M) {
-          float* Pp = g.partial + ((int64_t)split * g.M_pad + m) * g.Nv;
-          Pp[ba * 16 + r16] = acc[mb][0][q];
-          Pp[bb * 16 + r16] = acc[mb][1][q];
-        }
-      }
-    // K split reduced here: the tile's last workgroup sums the partials in
-    // split order into its accumulators (its own partial included)
-    if (!g.tile_cnt || !last_arrival(g.tile_cnt + grp * nmt + mt, g.S, &s_flag)) return;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int m = m0 + mb * 16 + (lane >> 4) * 4 + q;
-        float va = 0.f, vb = 0.f;
-        if (m < g.M)
-          for (int sp = 0; sp < g.S; ++sp) {
-            const float* Pp = g.partial + ((int64_t)sp * g.M_pad + m) * g.Nv;
-            va += Pp[ba * 16 + r16];
-            vb += Pp[bb * 16 + r16];
-          }
-        acc[mb][0][q] = va;
-        acc[mb][1][q] = vb;
-      }
-  }
-  if (norm_here) {  // uniform branch
-    rr.finish(g, m0, s_part, s_rstd);
+    for (int p = 0; p < PF; ++p) gload(p, min(p, nst - 1));
+    lstore(0, 0);
+    gload(0, min(PF, nst - 1));
     __syncthreads();
   }
+  int st = 0;
+  for (; st + PF <= nst; st += PF) {
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int mr = mb * 16 + (lane >> 4) * 4 + q;
-      const int m = m0 + mr;
-      float sq = 0.f;
-      if (m < g.M) sq = epi(m, ba * 16 + r16, acc[mb][0][q], bb * 16 + r16, acc[mb][1][q], norm_here ? s_rstd[mr] : 1.f);
-      if (g.ssq_out) {
-        sq = sum16(sq);
-        if (r16 == 0 && m < g.M) g.ssq_out[(int64_t)pair * g.M_pad + m] = sq;
+    for (int p = 0; p < PF; ++p) {
+      const int cur = st + p;
+      compute(cur & 1);
+      if (cur + 1 < nst) {  // uniform
+        lstore((p + 1) % PF, (cur + 1) & 1);
+        gload((p + 1) % PF, min(cur + 1 + PF, nst - 1));
       }
+      __syncthreads();
     }
+  }
+#pragma unroll
+  for (int p = 0; p < PF; ++p) {
+    const int cur = st + p;
+    if (cur < nst) {  // uniform
+      compute(cur & 1);
+      if (cur + 1 < nst) lstore((p + 1) % PF, (cur + 1) & 1);
+      __syncthreads();
+    }
+  }
+  // output tile to LDS (the operand buffers are free after the last barrier),
+  // C layout: lane l holds column l % 32 of a 32-column block and rows
+  // 8 g + 4 (l / 32) + q (g, q < 4)
+  float* Cs = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int gq = 0; gq < 16; ++gq)
+        Cs[(wm * 64 + i * 32 + 8 * (gq >> 2) + 4 * (lane >> 5) + (gq & 3)) * LDC + wn * WN + j * 32 + r32] =
+            acc[i][j][gq];
+  if (norm_here) rr.finish(g, m0, s_part, s_rstd);  // uniform branch: contains a barrier
+  __syncthreads();
+  // 16 consecutive threads take the 16 column positions of one (row, pair):
+  // virtual columns c16 (block ba) and 16 + c16 (block bb); every thread runs
+  // the same trip count, so the row sums of squares reduce over those 16
+  const int c16 = tid & 15;
+  for (int it = tid >> 4; it < BM * (BN / 32); it += 16) {
+    const int pl = it % (BN / 32), row = it / (BN / 32);
+    const int m = m0 + row, pair = pair0 + pl;
+    int ba, bb;
+    pair_blocks(g, pair, ba, bb);
+    const float va = Cs[row * LDC + pl * 32 + c16], vb = Cs[row * LDC + pl * 32 + 16 + c16];
+    if (g.S > 1) {
+      if (m < g.M) {
+        float* P = g.partial + ((int64_t)split * g.M_pad + m) * g.Nv;
+        P[ba * 16 + c16] = va;
+        P[bb * 16 + c16] = vb;
+      }
+      continue;
+    }
+    float sq = 0.f;
+    if (m < g.M) sq = epi(m, ba * 16 + c16, va, bb * 16 + c16, vb, norm_here ? s_rstd[row] : 1.f);
+    if (g.ssq_out) {
+      sq = sum16(sq);
+      if (c16 == 0 && m < g.M) g.ssq_out[(int64_t)pair * g.M_pad + m] = sq;
+    }
+  }
 }
 
 // grid: x = pair, y = ceil(M/16); block 256
@@ -285,11 +281,12 @@ void launch_gemm(int dtype, const GemmArgs& g0, const EpiArgs& e, hipStream_t s)
   }
   Epi<uint16_t> epi{e};
   if (g.wide) {
-    dim3 grid(g.npairs / 4 * g.S * mt);
-    if (MB == 8)
-      hipLaunchKernelGGL(k_gemm_bf16_wide<8>, grid, dim3(256), 0, s, g, epi);
+    const int tiles_m = (g.M + 127) / 128;
+    dim3 grid(g.npairs / (g.wide / 32) * g.S * tiles_m);
+    if (g.wide == 128)
+      hipLaunchKernelGGL(k_gemm_bf16_tile<128>, grid, dim3(256), 0, s, g, epi);
     else
-      hipLaunchKernelGGL(k_gemm_bf16_wide<4>, grid, dim3(256), 0, s, g, epi);
+      hipLaunchKernelGGL(k_gemm_bf16_tile<64>, grid, dim3(256), 0, s, g, epi);
   } else {
     dim3 grid(g.npairs, g.S, mt);
     switch (MB) {

@@ -496,24 +496,24 @@ struct Gemm {
     g.ssq_units = ssq_units ? ssq_units : c->cfg.d_model / (c->dt == 1 ? 32 : 2);  // producers' column units
     g.inv_d = 1.0f / (float)c->cfg.d_model;
     g.eps = c->cfg.rms_eps;
-    if (c->dt == 1 && c->gemm_wide && n > 32 && g.npairs % 4 == 0 && K % 64 == 0) {
-      // wide tile: 4 pairs x (64 or 128) rows per workgroup, K split so that
-      // about one workgroup per compute unit is resident
-      const int MB = c->gemm_mb_force == 8 ? 8 : 4;
-      const int mt = (n + 16 * MB - 1) / (16 * MB);
-      const int tiles = g.npairs / 4 * mt;
+    if (c->dt == 1 && c->gemm_wide && n > 32 && g.npairs % 2 == 0 && K % 64 == 0) {
+      // LDS tile of 128 rows x 64 columns (128 when that still leaves two
+      // workgroups per compute unit); K split while each split adds a
+      // workgroup per compute unit, at least two stages of 64 per split
+      const int mt = (n + 127) / 128;
+      const int BN = (g.npairs % 4 == 0 && g.npairs / 2 * mt >= 512) ? 128 : 64;
+      const int tiles = g.npairs / (BN / 32) * mt;
       const int kst = K / 64;
-      int S = std::max(1, (256 + tiles - 1) / tiles);
-      S = std::min(S, std::max(1, kst / 4));              // >= 4 stages per workgroup
+      int S = std::max(1, 256 / tiles);
+      S = std::min(S, std::max(1, kst / 2));
       if (c->gemm_s_force > 0) S = std::min(c->gemm_s_force, kst);
       while (S > 1 && (size_t)S * g.M_pad * g.Nv > c->partial_cap) --S;
-      g.wide = 1;
-      g.mb = MB;
+      g.wide = BN;
       g.S = S;
       g.kslice = (kst + S - 1) / S * 64;
-      // partials summed by a second kernel: the arrival protocol's acquire
-      // invalidates L2, which this tile relies on for its activation and
-      // weight re-reads (measured: the product time more than doubles)
+      // split partials are summed by a second kernel: the arrival protocol's
+      // acquire invalidates L2, which this tile relies on for its activation
+      // re-reads
     } else if (c->dt == 1) {
       int MB = gemm_row_blocks(n);
       const int mbf = c->gemm_mb_force;

@@ -84,10 +84,10 @@ struct GemmArgs {
   int dh;                 // head width for PAIR_ROPE
   int M, M_pad;           // valid rows / allocated rows of A
   int S;                  // splits of K across workgroups (bf16 path)
-  int mb;                 // 16-row blocks per tile (bf16 path): 1, 2 or 4; wide: 4 or 8
-  int wide;               // bf16 path: 1 = wide tile (4 pairs per workgroup, activations via LDS)
+  int mb;                 // 16-row blocks per tile of the narrow bf16 tile: 1, 2 or 4
+  int wide;               // bf16 path: 0 = narrow tile; 64 or 128 = LDS tile of 128 rows x this many columns
   int kslice;             // K elements per (split, wave) slice, multiple of 32;
-                          // wide: K elements per split, multiple of 64
+                          // LDS tile: K elements per split, multiple of 64
   float* partial;         // [S][M_pad][Nv] when S > 1
   unsigned* tile_cnt;     // S > 1: per-tile arrival counters (zero between calls); the
                           // last workgroup of a tile to finish sums the S partials in

@@ -53,11 +53,14 @@ def test_gemm_kernel_parity():
     wl = synth.SMALL
     run = GpuRun(wl, B=1, T=4, max_rows=200)
     rng = np.random.default_rng(0)
-    # above 32 rows with 4 | N/32 and 64 | K the wide-tile kernel runs: its K
-    # loop has a 4-stage body and a tail of 0-3 stages of 64 (K = 192, 448
-    # and 704 give tails of 3, 3 and 2/1 stages, the last with a K split)
+    # above 32 rows with N/32 even and 64 | K the LDS tile (128 rows x 64 or
+    # 128 columns) runs: its K loop has a 2-stage body and a tail of 0-1
+    # stages of 64 (K = 192, 448, 704: odd stage counts; the last with a K
+    # split whose final split is empty); N = 96 (odd pair count) falls back
+    # to the narrow tile; M = 200 spans two row tiles; N = 32768 takes the
+    # 128-column tile
     for M, N, K in [(1, 256, 512), (5, 64, 256), (16, 768, 256), (33, 96, 512), (70, 256, 384), (128, 512, 512),
-                    (200, 128, 256), (70, 256, 192), (128, 512, 448), (96, 1024, 704)]:
+                    (200, 128, 256), (70, 256, 192), (128, 512, 448), (96, 1024, 704), (40, 32768, 256)]:
         Abits = synth.normal(7, "dbgA%d" % M, (M, K), dtype="bf16")
         Wbits = synth.normal(7, "dbgW%d" % M, (N, K), sigma=0.05, dtype="bf16")
         Ad, Wd = to_device(Abits, "bf16"), to_device(Wbits, "bf16")

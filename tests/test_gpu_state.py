@@ -182,7 +182,8 @@ def test_pending_token_bookkeeping_and_errors():
     assert run.dec.sync_error() == _abi.RLT_EPENDING
     assert run.st.pos.tolist() == [2, 1, 2]
     assert torch.equal(run.st.s[1], s_before[1])
-    assert torch.equal(run.st.ring("k")[:, 1], ring_before)
+    # bitwise: slots not yet written hold arbitrary bits (possibly NaN patterns)
+    assert torch.equal(run.st.ring("k")[:, 1].view(torch.int16), ring_before.view(torch.int16))
     assert run.st.pending.tolist() == [-1, int(ok[1]), -1]
     # consuming the recorded token works and clears it
     assert run.step([1], 2, consume_tok=ok[1:2].contiguous()) == 0
