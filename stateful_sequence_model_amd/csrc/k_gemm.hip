@@ -171,6 +171,23 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_tile(GemmArgs g, Epi<uint16_t
       for (int gq = 0; gq < 16; ++gq)
         Cs[(wm * 64 + i * 32 + 8 * (gq >> 2) + 4 * (lane >> 5) + (gq & 3)) * LDC + wn * WN + j * 32 + r32] =
             acc[i][j][gq];
+  __syncthreads();
+  // output column of virtual column v of this tile
+  auto col_of = [&](int v) {
+    int ba, bb;
+    pair_blocks(g, pair0 + v / 32, ba, bb);
+    return ((v & 16) ? bb : ba) * 16 + (v & 15);
+  };
+  if (g.S > 1) {
+    for (int idx = tid; idx < BM * BN; idx += 256) {
+      const int row = idx / BN, v = idx % BN;
+      if (m0 + row < g.M) g.partial[((int64_t)split * g.M_pad + m0 + row) * g.Nv + col_of(v)] = Cs[row * LDC + v];
+    }
+    // summed in split order by k_splitk_epi: the in-kernel arrival protocol
+    // (release / acquire at device scope per workgroup) made this tile's
+    // products several times slower
+    return;
+  }
   if (norm_here) rr.finish(g, m0, s_part, s_rstd);  // uniform branch: contains a barrier
   __syncthreads();
   // 16 consecutive threads take the 16 column positions of one (row, pair):
@@ -183,14 +200,6 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_tile(GemmArgs g, Epi<uint16_t
     int ba, bb;
     pair_blocks(g, pair, ba, bb);
     const float va = Cs[row * LDC + pl * 32 + c16], vb = Cs[row * LDC + pl * 32 + 16 + c16];
-    if (g.S > 1) {
-      if (m < g.M) {
-        float* P = g.partial + ((int64_t)split * g.M_pad + m) * g.Nv;
-        P[ba * 16 + c16] = va;
-        P[bb * 16 + c16] = vb;
-      }
-      continue;
-    }
     float sq = 0.f;
     if (m < g.M) sq = epi(m, ba * 16 + c16, va, bb * 16 + c16, vb, norm_here ? s_rstd[row] : 1.f);
     if (g.ssq_out) {
