@@ -153,28 +153,8 @@ __device__ __forceinline__ bf16x8_t load8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8_t, u);
 }
 
-// Arrival of a workgroup whose partial tile is written: true in the last of
-// the S workgroups of the tile, which then reads every partial (the counter
-// is reset for the next call). Every thread of the workgroup calls it.
-__device__ __forceinline__ bool last_arrival(unsigned* cnt, int S, int* s_flag) {
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have reached the cache hierarchy
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    const unsigned old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int last = old == (unsigned)(S - 1);
-    if (last) {
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    *s_flag = last;
-  }
-  __syncthreads();
-  return *s_flag != 0;
-}
-
-// LDS floats used by gemm_bf16_body<MB> (the last one holds the arrival flag)
-constexpr int gemm_lds_floats(int MB) { return 4 * MB * 16 * 32 + MB * 16 + 256 + 1; }
+// LDS floats used by gemm_bf16_body<MB>
+constexpr int gemm_lds_floats(int MB) { return 4 * MB * 16 * 32 + MB * 16 + 256; }
 
 // One (pair, split, m-tile) tile of the product; block 256 (4 waves).
 template <int MB>
@@ -197,7 +177,7 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& g, const Epi<uint
     ap[mb] = (const uint16_t*)g.A + (int64_t)(m0 + mb * 16 + r16) * g.lda + kq;
 
   // folded RMSNorm: this tile's row sums of squares, loads in flight with the K loop
-  const bool norm_here = (g.S == 1 || g.tile_cnt != nullptr) && g.ssq_in != nullptr;
+  const bool norm_here = g.S == 1 && g.ssq_in != nullptr;
   RowRstd<MB * 16> rr(g, norm_here ? m0 : 0);
   f32x4_t acc[MB][2];
 #pragma unroll
@@ -266,7 +246,7 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& g, const Epi<uint
       red[wave][mb * 16 + (lane >> 4) * 4 + i][r16] = acc[mb][0][i];
       red[wave][mb * 16 + (lane >> 4) * 4 + i][16 + r16] = acc[mb][1][i];
     }
-  if (g.S == 1 && norm_here) rr.finish(g, m0, s_part, s_rstd);  // uniform branch: contains a barrier
+  if (norm_here) rr.finish(g, m0, s_part, s_rstd);  // uniform branch: contains a barrier
   __syncthreads();
   // every lane runs the same trip count (the 16 lanes of a row reduce together)
   for (int idx = threadIdx.x; idx < MB * 16 * 16; idx += 256) {
@@ -285,30 +265,6 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& g, const Epi<uint
       float* P = g.partial + ((int64_t)split * g.M_pad + slot) * g.Nv;
       P[ba * 16 + r] = va;
       P[bb * 16 + r] = vb;
-    }
-  }
-  // K split reduced here: the tile's last workgroup sums the partials in split order
-  if (g.S == 1 || !g.tile_cnt) return;
-  int* s_flag = reinterpret_cast<int*>(s_part + 256);
-  if (!last_arrival(g.tile_cnt + pair + (int64_t)g.npairs * mt, g.S, s_flag)) return;
-  if (norm_here) rr.finish(g, m0, s_part, s_rstd);  // uniform branch: contains a barrier
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < MB * 16 * 16; idx += 256) {
-    const int m = idx >> 4, r = idx & 15;
-    const int slot = m0 + m;
-    float sq = 0.f;
-    if (slot < g.M) {
-      float va = 0.f, vb = 0.f;
-      for (int s = 0; s < g.S; ++s) {
-        const float* P = g.partial + ((int64_t)s * g.M_pad + slot) * g.Nv;
-        va += P[ba * 16 + r];
-        vb += P[bb * 16 + r];
-      }
-      sq = epi(slot, ba * 16 + r, va, bb * 16 + r, vb, g.ssq_in ? s_rstd[m] : 1.f);
-    }
-    if (g.ssq_out) {
-      sq = sum16(sq);
-      if (r == 0 && slot < g.M) g.ssq_out[(int64_t)pair * g.M_pad + slot] = sq;
     }
   }
 }

@@ -11,10 +11,8 @@
 //   one pair of 16-column blocks) and each streams a disjoint quarter of the
 //   workgroup's K range, so A and W are each read once per workgroup; the
 //   four partial tiles are summed in LDS in wave order. Optional split of K
-//   across S workgroups writes partial tiles; the last workgroup of a tile
-//   to finish (an arrival counter per tile) sums them in split order and
-//   runs the epilogue (the persistent step uses a phase of its own for this).
-//   Both orders are fixed, so results are deterministic.
+//   across S workgroups writes partial tiles that a second kernel sums in
+//   split order. Both orders are fixed, so results are deterministic.
 //   Accumulation is fp32; A (activations) arrive rounded to bf16.
 // fp32 path: one thread per output pair, sequential K loop (used by the
 //   float32 configuration, where precision rather than speed is the point).
@@ -183,9 +181,9 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_tile(GemmArgs g, Epi<uint16_t
       const int row = idx / BN, v = idx % BN;
       if (m0 + row < g.M) g.partial[((int64_t)split * g.M_pad + m0 + row) * g.Nv + col_of(v)] = Cs[row * LDC + v];
     }
-    // summed in split order by k_splitk_epi: the in-kernel arrival protocol
-    // (release / acquire at device scope per workgroup) made this tile's
-    // products several times slower
+    // summed in split order by k_splitk_epi (an in-kernel reduction by the
+    // last workgroup of each tile, with release / acquire at device scope,
+    // measured several times slower)
     return;
   }
   if (norm_here) rr.finish(g, m0, s_part, s_rstd);  // uniform branch: contains a barrier
@@ -276,7 +274,6 @@ void launch_gemm(int dtype, const GemmArgs& g0, const EpiArgs& e, hipStream_t s)
     p.gy = g.S;
     p.gz = mt;
     p.u.gm.g = g;
-    p.u.gm.g.tile_cnt = nullptr;  // the persistent step sums the partials in a phase of its own
     p.u.gm.e = e;
     if (record_phase(p)) {
       if (g.S > 1) {
@@ -304,7 +301,7 @@ void launch_gemm(int dtype, const GemmArgs& g0, const EpiArgs& e, hipStream_t s)
       default: hipLaunchKernelGGL(k_gemm_bf16<4>, grid, dim3(256), 0, s, g, epi); break;
     }
   }
-  if (g.S > 1 && !g.tile_cnt) {
+  if (g.S > 1) {
     dim3 g2(g.npairs, (g.M + 15) / 16);
     hipLaunchKernelGGL(k_splitk_epi<uint16_t>, g2, dim3(256), 0, s, g, epi);
   }

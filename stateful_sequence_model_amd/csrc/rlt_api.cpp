@@ -58,13 +58,8 @@ struct Workspace {
   void *X, *kc, *vc, *o, *h, *act;
   float *gbuf, *z, *q, *qm, *part, *partial, *logits;
   float* ssq;  // [d/2][M_pad] partial sums of squares of z (folded RMSNorm)
-  unsigned* tile_cnt;  // [kTileCounters] arrival counters of K-split products (zero between calls)
 };
 
-// K-split products of the narrow tile with at most this many output tiles
-// reduce their partials in the product kernel itself (the split rule only
-// splits below 256 tiles)
-constexpr int kTileCounters = 1024;
 
 }  // namespace
 
@@ -252,8 +247,7 @@ extern "C" void rlt_destroy(rlt_ctx* c) {
   std::vector<void*> ptrs = {c->t_row, c->ident, c->ones, c->rows_buf, c->src_buf, c->split_buf, c->last_buf,
                              c->inv_freq};
   for (Workspace& w : c->ws) {
-    void* p[] = {w.X, w.kc, w.vc, w.o, w.h, w.act, w.gbuf, w.z, w.q, w.qm, w.part, w.partial, w.logits, w.ssq,
-                 w.tile_cnt};
+    void* p[] = {w.X, w.kc, w.vc, w.o, w.h, w.act, w.gbuf, w.z, w.q, w.qm, w.part, w.partial, w.logits, w.ssq};
     ptrs.insert(ptrs.end(), std::begin(p), std::end(p));
   }
   for (void* p : ptrs)
@@ -286,9 +280,8 @@ static int alloc_workspace(rlt_ctx* c, Workspace& w, bool full) {
       (rc = dev_alloc(&w.part, M * (size_t)c->nch * cf.n_heads * (cf.d_head + 2) * 4)) ||
       (rc = dev_alloc(&w.partial, c->partial_cap * 4)) ||
       (rc = dev_alloc(&w.logits, (full ? M : 16) * (size_t)cf.vocab * 4)) ||
-      (rc = dev_alloc(&w.ssq, M * (size_t)(d / 2) * 4)) || (rc = dev_alloc(&w.tile_cnt, kTileCounters * 4)))
+      (rc = dev_alloc(&w.ssq, M * (size_t)(d / 2) * 4)))
     return rc;
-  if (hipMemset(w.tile_cnt, 0, kTileCounters * 4) != hipSuccess) return fail(RLT_EHIP, "workspace initialisation failed");
   // rows beyond a call's n are read by the MFMA tiles and discarded: keep
   // them finite
   if (hipMemset(w.X, 0, M * 2 * d * es) != hipSuccess || hipMemset(w.o, 0, M * d * es) != hipSuccess ||
@@ -511,8 +504,6 @@ struct Gemm {
       g.wide = BN;
       g.S = S;
       g.kslice = (kst + S - 1) / S * 64;
-      // split partials summed by a second kernel (measured: the in-kernel
-      // arrival protocol's device-scope fences slow this tile's products 3x)
     } else if (c->dt == 1) {
       int MB = gemm_row_blocks(n);
       const int mbf = c->gemm_mb_force;
@@ -532,7 +523,6 @@ struct Gemm {
       g.mb = MB;
       const int per = (K + 4 * S - 1) / (4 * S);
       g.kslice = (per + 31) / 32 * 32;
-      if (S > 1 && tiles <= kTileCounters) g.tile_cnt = w->tile_cnt;
     }
     Prof pf(c, RLT_PROF_GEMM, s);
     launch_gemm(c->dt, g, e, s);

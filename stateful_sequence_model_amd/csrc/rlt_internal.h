@@ -89,9 +89,6 @@ struct GemmArgs {
   int kslice;             // K elements per (split, wave) slice, multiple of 32;
                           // LDS tile: K elements per split, multiple of 64
   float* partial;         // [S][M_pad][Nv] when S > 1
-  unsigned* tile_cnt;     // S > 1: per-tile arrival counters (zero between calls); the
-                          // last workgroup of a tile to finish sums the S partials in
-                          // split order and runs the epilogue. Null: a second kernel does.
   int Nv;                 // nseg * seg_rows
   // RMSNorm folded into the products (RMSNorm(z) W^T = rstd * ((z * gain) W^T)):
   // a consumer reads per-row partial sums of squares of z and scales its
