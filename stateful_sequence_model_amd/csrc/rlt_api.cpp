@@ -492,13 +492,14 @@ struct Gemm {
     if (c->dt == 1 && c->gemm_wide && n > 32 && g.npairs % 2 == 0 && K % 64 == 0) {
       // LDS tile of 128 rows x 64 columns (128 when that still leaves two
       // workgroups per compute unit); K split while each split adds a
-      // workgroup per compute unit, at least two stages of 64 per split
+      // workgroup per compute unit and keeps at least 8 stages of 64
+      // (measured best for every product shape at 64-256 rows)
       const int mt = (n + 127) / 128;
       const int BN = (g.npairs % 4 == 0 && g.npairs / 2 * mt >= 512) ? 128 : 64;
       const int tiles = g.npairs / (BN / 32) * mt;
       const int kst = K / 64;
       int S = std::max(1, 256 / tiles);
-      S = std::min(S, std::max(1, kst / 2));
+      S = std::min(S, std::max(1, kst / 8));
       if (c->gemm_s_force > 0) S = std::min(c->gemm_s_force, kst);
       while (S > 1 && (size_t)S * g.M_pad * g.Nv > c->partial_cap) --S;
       g.wide = BN;
