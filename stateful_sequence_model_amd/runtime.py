@@ -163,7 +163,9 @@ class Decoder:
 
     @staticmethod
     def memory(k: torch.Tensor, v: torch.Tensor, mem_len: torch.Tensor) -> A.rlt_memory:
-        """k, v shaped [G, B, T, d] (contiguous); mem_len int32 [B]."""
+        """k, v shaped [G, B, T, d] (contiguous); mem_len int32 [B]. The
+        returned struct holds raw device pointers: the caller keeps the three
+        tensors alive while it is in use."""
         G, B, T, d = k.shape
         return A.rlt_memory(k.data_ptr(), v.data_ptr(), B * T * d, T * d, d, mem_len.data_ptr())
 
