@@ -5,16 +5,31 @@
 
 namespace rlt {
 
-// 32 bytes of one head's keys or values held by one lane, unconverted
+// 32 bytes of one head's keys or values held by one lane, unconverted: two
+// 16-byte pieces, the second h elements after the first. A lane of a head
+// owns elements [jl·PE, jl·PE + PE) and the same range + DH/2, so that the
+// lanes of a head read one contiguous span per load instruction (128 bytes
+// for 128-wide bf16 heads: every cache line an instruction touches is used
+// whole).
 struct Raw {
   uint4 a, b;
 };
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// Streamed keys and values are read once per launch: non-temporal loads (a
+// read-only probe of the cross-attention access pattern measured 7.3 TB/s
+// with them against 6.4 TB/s with the default cache policy).
+__device__ __forceinline__ uint4 ld_stream(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 template <typename T> struct LaneVec;
 template <> struct LaneVec<uint16_t> {
-  static constexpr int E = 16;
-  __device__ static __forceinline__ Raw load(const uint16_t* p) {
-    return Raw{*(const uint4*)p, *(const uint4*)(p + 8)};
+  static constexpr int E = 16, PE = 8;
+  __device__ static __forceinline__ Raw load(const uint16_t* p, int h) {
+    return Raw{ld_stream(p), ld_stream(p + h)};
   }
   __device__ static __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
   __device__ static __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -36,22 +51,22 @@ template <> struct LaneVec<uint16_t> {
       o[2 * i + 1] = fmaf(p, hi(w[i]), o[2 * i + 1]);
     }
   }
-  __device__ static __forceinline__ void store(uint16_t* p, const float* f) {
+  __device__ static __forceinline__ void store(uint16_t* p, const float* f, int h) {
     uint32_t w[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) w[i] = (uint32_t)f2bf(f[2 * i]) | ((uint32_t)f2bf(f[2 * i + 1]) << 16);
     *(uint4*)p = make_uint4(w[0], w[1], w[2], w[3]);
-    *(uint4*)(p + 8) = make_uint4(w[4], w[5], w[6], w[7]);
+    *(uint4*)(p + h) = make_uint4(w[4], w[5], w[6], w[7]);
   }
-  __device__ static __forceinline__ void copy(uint16_t* d, const uint16_t* s) {
+  __device__ static __forceinline__ void copy(uint16_t* d, const uint16_t* s, int h) {
     *(uint4*)d = *(const uint4*)s;
-    *(uint4*)(d + 8) = *(const uint4*)(s + 8);
+    *(uint4*)(d + h) = *(const uint4*)(s + h);
   }
 };
 template <> struct LaneVec<float> {
-  static constexpr int E = 8;
-  __device__ static __forceinline__ Raw load(const float* p) {
-    return Raw{*(const uint4*)p, *(const uint4*)(p + 4)};
+  static constexpr int E = 8, PE = 4;
+  __device__ static __forceinline__ Raw load(const float* p, int h) {
+    return Raw{ld_stream(p), ld_stream(p + h)};
   }
   __device__ static __forceinline__ float dot(const float* q, const Raw& r) {
     const uint32_t w[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
@@ -65,13 +80,13 @@ template <> struct LaneVec<float> {
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] = fmaf(p, __uint_as_float(w[i]), o[i]);
   }
-  __device__ static __forceinline__ void store(float* p, const float* f) {
+  __device__ static __forceinline__ void store(float* p, const float* f, int h) {
     *(float4*)p = make_float4(f[0], f[1], f[2], f[3]);
-    *(float4*)(p + 4) = make_float4(f[4], f[5], f[6], f[7]);
+    *(float4*)(p + h) = make_float4(f[4], f[5], f[6], f[7]);
   }
-  __device__ static __forceinline__ void copy(float* d, const float* s) {
+  __device__ static __forceinline__ void copy(float* d, const float* s, int h) {
     *(float4*)d = *(const float4*)s;
-    *(float4*)(d + 4) = *(const float4*)(s + 4);
+    *(float4*)(d + h) = *(const float4*)(s + h);
   }
 };
 
@@ -117,6 +132,7 @@ struct Acc {
 // pointers), U at a time.
 template <typename T, int LPK, int U, class KV>
 __device__ __forceinline__ void walk(Acc<T>& acc, const float* q, int r0, int r1, int step, const KV& kv) {
+  constexpr int h = LPK * LaneVec<T>::PE;  // DH / 2
   using LV = LaneVec<T>;
   int r = r0;
   for (; r + (U - 1) * step < r1; r += U * step) {
@@ -125,8 +141,8 @@ __device__ __forceinline__ void walk(Acc<T>& acc, const float* q, int r0, int r1
     for (int u = 0; u < U; ++u) {
       const T *kp, *vp;
       kv(r + u * step, kp, vp);
-      kr[u] = LV::load(kp);
-      vr[u] = LV::load(vp);
+      kr[u] = LV::load(kp, h);
+      vr[u] = LV::load(vp, h);
     }
     float s[U];
 #pragma unroll
@@ -136,7 +152,7 @@ __device__ __forceinline__ void walk(Acc<T>& acc, const float* q, int r0, int r1
   for (; r < r1; r += step) {
     const T *kp, *vp;
     kv(r, kp, vp);
-    Raw kr[1] = {LV::load(kp)}, vr[1] = {LV::load(vp)};
+    Raw kr[1] = {LV::load(kp, h)}, vr[1] = {LV::load(vp, h)};
     float s[1] = {group_sum<LPK>(LV::dot(q, kr[0]))};
     acc.template fold<1>(s, vr);
   }
@@ -223,14 +239,18 @@ __device__ __forceinline__ void swa_body(const AttnArgs& a, int hg, int slot, fl
   const int kg = threadIdx.x / G;
   const int hh = (threadIdx.x % G) / LPK;
   const int jl = threadIdx.x % LPK;
-  const int col = (hg * a.hpw + hh) * DH + jl * E;
+  constexpr int PE = LV::PE, h = DH / 2;
+  const int col = (hg * a.hpw + hh) * DH + jl * PE;
   const int d = a.d;
 
   float q[E];
   {
     const float* qp = a.q + (int64_t)slot * d + col;
 #pragma unroll
-    for (int i = 0; i < E; ++i) q[i] = qp[i] * a.qscale;
+    for (int i = 0; i < PE; ++i) {
+      q[i] = qp[i] * a.qscale;
+      q[PE + i] = qp[h + i] * a.qscale;
+    }
   }
   const int W1 = a.W - 1;
   const int nh = min(t - 1, W1);
@@ -253,14 +273,14 @@ __device__ __forceinline__ void swa_body(const AttnArgs& a, int hg, int slot, fl
     float o[E];
 #pragma unroll
     for (int i = 0; i < E; ++i) o[i] = acc.o[i] * inv;
-    LV::store((T*)a.out + (int64_t)slot * d + col, o);
+    LV::store((T*)a.out + (int64_t)slot * d + col, o, h);
   }
   // cache insert after every read of this workgroup
   __syncthreads();
   if (W1 > 0 && kg == 0) {
     const int sl = (t - 1) % W1;
-    LV::copy((T*)a.ring_k + ((int64_t)row * W1 + sl) * d + col, kv.ck);
-    LV::copy((T*)a.ring_v + ((int64_t)row * W1 + sl) * d + col, kv.cv);
+    LV::copy((T*)a.ring_k + ((int64_t)row * W1 + sl) * d + col, kv.ck, h);
+    LV::copy((T*)a.ring_v + ((int64_t)row * W1 + sl) * d + col, kv.cv, h);
   }
 }
 
@@ -283,14 +303,18 @@ __device__ __forceinline__ void xattn_body(const AttnArgs& a, int hg, int ch, in
   const int hh = (threadIdx.x % G) / LPK;
   const int jl = threadIdx.x % LPK;
   const int head = hg * a.hpw + hh;
-  const int col = head * DH + jl * E;
+  constexpr int PE = LV::PE, h = DH / 2;
+  const int col = head * DH + jl * PE;
   const int d = a.d;
 
   float q[E];
   {
     const float* qp = a.q + (int64_t)slot * d + col;
 #pragma unroll
-    for (int i = 0; i < E; ++i) q[i] = qp[i] * a.qscale;
+    for (int i = 0; i < PE; ++i) {
+      q[i] = qp[i] * a.qscale;
+      q[PE + i] = qp[h + i] * a.qscale;
+    }
   }
   MemKV<T> kv{(const T*)a.mk + (int64_t)row * a.sb + col, (const T*)a.mv + (int64_t)row * a.sb + col, a.st};
   Acc<T> acc;
@@ -300,7 +324,10 @@ __device__ __forceinline__ void xattn_body(const AttnArgs& a, int hg, int ch, in
   if (lead) {
     float* P = a.part + (((int64_t)slot * a.nch + ch) * a.H + head) * (DH + 2);
 #pragma unroll
-    for (int i = 0; i < E; ++i) P[jl * E + i] = acc.o[i];
+    for (int i = 0; i < PE; ++i) {
+      P[jl * PE + i] = acc.o[i];
+      P[h + jl * PE + i] = acc.o[PE + i];
+    }
     if (jl == 0) {
       P[DH] = acc.m;
       P[DH + 1] = acc.l;
