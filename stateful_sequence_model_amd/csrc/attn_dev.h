@@ -90,10 +90,24 @@ template <> struct LaneVec<float> {
   }
 };
 
+// s + the value of lane (this lane with the DPP permutation CTRL applied)
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float s) {
+  return s + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over aligned groups of LPK (1..16) consecutive lanes, the result in
+// every lane of the group, through the data-parallel primitives of the
+// vector ALU (no LDS round trip): swap neighbours, swap pairs of a quad,
+// then mirror within 8 and 16 lanes (each mirror pairs a lane with one of
+// the half it has not summed yet, whose values are already uniform).
 template <int LPK>
 __device__ __forceinline__ float group_sum(float s) {
-#pragma unroll
-  for (int off = 1; off < LPK; off <<= 1) s += __shfl_xor(s, off);
+  static_assert(LPK >= 1 && LPK <= 16 && (LPK & (LPK - 1)) == 0, "group of 1-16 lanes");
+  if (LPK >= 2) s = dpp_add<0xb1>(s);   // quad_perm [1,0,3,2]
+  if (LPK >= 4) s = dpp_add<0x4e>(s);   // quad_perm [2,3,0,1]
+  if (LPK >= 8) s = dpp_add<0x141>(s);  // row_half_mirror
+  if (LPK >= 16) s = dpp_add<0x140>(s); // row_mirror
   return s;
 }
 

@@ -110,6 +110,27 @@ def test_small_batched(dtype):
     assert torch.equal(run.st.pos.cpu(), torch.full((wl.B,), wl.T, dtype=torch.int32))
 
 
+@pytest.mark.parametrize("dtype,dh", [("f32", 64), ("f32", 128), ("bf16", 64), ("bf16", 128)])
+def test_head_widths(dtype, dh):
+    """Head widths whose per-head lane groups (4, 8 or 16 lanes per head)
+    the other small cases do not reach: L_D=2, d=256, W=8, 3 sequences x 24
+    transitions against the oracle."""
+    require_gpu()
+    wl = synth.SMALL.with_(L=2, H=256 // dh, dh=dh, W=8, G=1, B=3, T=24, dtype=dtype)
+    run = GpuRun(wl)
+    run.init()
+    S, Z = run.run(wl.T)
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    agree = []
+    for b in range(wl.B):
+        So, Zo, _, _ = _oracle_run(run, b, wl.T)
+        ws, wz, top1 = _compare(S[:, b], Z[:, b], So, Zo, tol)
+        assert ws < tol and wz < tol, (b, ws, wz)
+        agree.append(top1)
+    if dtype == "bf16":
+        assert np.mean(agree) >= TOP1_BF16, agree
+
+
 def test_ring_slots_hold_retained_positions():
     """After t transitions every layer's ring holds the retained positions
     max(1, t-W+2)..t at slot (j-1) mod (W-1); compared with the oracle cache."""
