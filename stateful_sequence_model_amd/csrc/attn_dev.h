@@ -148,9 +148,11 @@ template <typename T, int LPK, int U, class KV>
 __device__ __forceinline__ void walk(Acc<T>& acc, const float* q, int r0, int r1, int step, const KV& kv) {
   constexpr int h = LPK * LaneVec<T>::PE;  // DH / 2
   using LV = LaneVec<T>;
-  int r = r0;
-  for (; r + (U - 1) * step < r1; r += U * step) {
-    Raw kr[U], vr[U];
+  // full batches: r0 + i·U·step for i < nb, each with its last key below r1
+  const int span = U * step;
+  const int last = r1 - 1 - (U - 1) * step;
+  const int nb = last >= r0 ? (last - r0) / span + 1 : 0;
+  auto issue = [&](Raw* kr, Raw* vr, int r) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const T *kp, *vp;
@@ -158,12 +160,26 @@ __device__ __forceinline__ void walk(Acc<T>& acc, const float* q, int r0, int r1
       kr[u] = LV::load(kp, h);
       vr[u] = LV::load(vp, h);
     }
+  };
+  auto consume = [&](const Raw* kr, const Raw* vr) {
     float s[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) s[u] = group_sum<LPK>(LV::dot(q, kr[u]));
     acc.template fold<U>(s, vr);
+  };
+  // two register sets: the next batch's loads are in flight while the
+  // current batch is folded (same batches, same fold order as one set)
+  Raw ka[U], va[U], kb[U], vb[U];
+  if (nb > 0) issue(ka, va, r0);
+  for (int i = 0; i < nb; i += 2) {
+    if (i + 1 < nb) issue(kb, vb, r0 + (i + 1) * span);
+    consume(ka, va);
+    if (i + 1 < nb) {
+      if (i + 2 < nb) issue(ka, va, r0 + (i + 2) * span);
+      consume(kb, vb);
+    }
   }
-  for (; r < r1; r += step) {
+  for (int r = r0 + nb * span; r < r1; r += step) {
     const T *kp, *vp;
     kv(r, kp, vp);
     Raw kr[1] = {LV::load(kp, h)}, vr[1] = {LV::load(vp, h)};
