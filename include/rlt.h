@@ -13,7 +13,8 @@
  *  - Pointers are DEVICE pointers unless a field says HOST.
  *  - The caller owns every buffer it passes; the library keeps the weight
  *    pointers given to rlt_create (they must outlive the context) and owns
- *    only its internal workspace.
+ *    only its internal workspace (for bf16 contexts with max_rows > 32 this
+ *    includes a copy of the decoder's matrix weights, see rlt_create).
  *  - Calls enqueue work on `stream` (a hipStream_t passed as void*; NULL is
  *    the default stream) and return without waiting for it, except where
  *    a call says otherwise.
@@ -233,7 +234,14 @@ typedef struct rlt_ctx rlt_ctx;
 
 /* Create a context on the current HIP device. Validates the config,
  * precomputes position tables and allocates workspace for up to max_rows
- * rows per call and memory prefixes up to max_ctx positions. */
+ * rows per call and memory prefixes up to max_ctx positions.
+ * bf16 with max_rows > 32 (and d_model, d_ffn multiples of 64, weights
+ * 16-byte aligned): the context also holds a copy of the decoder's matrix
+ * weights (wq/wk/wv, wo, wqm, wom, w_gate/w_up, w_down, w_out; as much device
+ * memory again as those) in the operand order of the gfx950 32x32x16 bf16
+ * matrix instruction, read by calls of more than 32 rows. The copy is made
+ * here: after changing those weights in place, call rlt_refresh_weights
+ * before the next call. Returns RLT_ENOMEM if it does not fit. */
 int rlt_create(const rlt_config* cfg, const rlt_weights* w, int32_t max_rows, int32_t max_ctx,
                rlt_ctx** out);
 void rlt_destroy(rlt_ctx* ctx);
@@ -265,6 +273,13 @@ int rlt_score_logprobs(rlt_ctx* ctx, const rlt_score_io* io, void* stream);
 
 /* Wait for `stream`, then return (and clear) any device-detected error. */
 int rlt_sync_error(rlt_ctx* ctx, void* stream);
+
+/* Rebuild the context's operand-order copy of the matrix weights (see
+ * rlt_create) from the caller's weights, on `stream`; a no-op for contexts
+ * without the copy. Needed after the caller changes weight values in place
+ * (an optimiser step on the gradients of rlt_replay_backward); the pointers
+ * themselves are fixed at rlt_create. */
+int rlt_refresh_weights(rlt_ctx* ctx, void* stream);
 
 /* Log of the trajectory importance weight prod_i r_i [RLT §5.3, text after
  * eq. (5.5)] of B sequences: out[b] = sum over t = split_host[b] ..

@@ -114,6 +114,7 @@ _SIGS = {
     "rlt_replay_sequence": (C.c_int, [P, C.POINTER(rlt_state), C.POINTER(rlt_replay_io), P]),
     "rlt_score_logprobs": (C.c_int, [P, C.POINTER(rlt_score_io), P]),
     "rlt_sync_error": (C.c_int, [P, P]),
+    "rlt_refresh_weights": (C.c_int, [P, P]),
     "rlt_trajectory_log_ratio": (C.c_int, [P, i32, P, P, P, i64, P, i64, P, P]),
     "rlt_snapshot_bytes": (C.c_int, [C.POINTER(rlt_config), C.POINTER(C.c_size_t)]),
     "rlt_state_snapshot": (C.c_int, [P, C.POINTER(rlt_state), P, i32, P, P]),
@@ -123,6 +124,7 @@ _SIGS = {
                                      i64, P]),
     "rlt_replay_backward": (C.c_int, [P, C.POINTER(rlt_backward_io), C.POINTER(rlt_grads), P]),
     "rlt_dbg_gemm": (C.c_int, [P, P, P, i32, i32, i32, P, P]),
+    "rlt_dbg_gemm_packed": (C.c_int, [P, P, P, i32, i32, i32, P, P]),
     "rlt_dbg_profile": (C.c_int, [P, i32]),
     "rlt_dbg_profile_read": (C.c_int, [P, i32, C.POINTER(C.c_double), C.POINTER(C.c_int64)]),
 }
@@ -206,6 +208,10 @@ def rlt_sync_error(ctx: int, stream: int) -> int:
     return lib().rlt_sync_error(ctx, stream)
 
 
+def rlt_refresh_weights(ctx: int, stream: int) -> int:
+    return lib().rlt_refresh_weights(ctx, stream)
+
+
 def rlt_trajectory_log_ratio(ctx: int, B: int, len_host, split_host, logp: int, logp_sb: int, logmu: int,
                              logmu_sb: int, out: int, stream: int) -> int:
     return lib().rlt_trajectory_log_ratio(ctx, B, len_host, split_host, logp, logp_sb, logmu, logmu_sb, out, stream)
@@ -238,6 +244,10 @@ def rlt_memory_prefill(ctx: int, mw: rlt_memory_weights, mem: rlt_memory, T_cap:
 
 def rlt_dbg_gemm(ctx: int, A: int, W: int, M: int, N: int, K: int, out: int, stream: int) -> int:
     return lib().rlt_dbg_gemm(ctx, A, W, M, N, K, out, stream)
+
+
+def rlt_dbg_gemm_packed(ctx: int, A: int, W: int, M: int, N: int, K: int, out: int, stream: int) -> int:
+    return lib().rlt_dbg_gemm_packed(ctx, A, W, M, N, K, out, stream)
 
 
 def rlt_dbg_profile(ctx: int, enable: int) -> int:

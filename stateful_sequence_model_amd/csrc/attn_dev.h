@@ -51,12 +51,13 @@ template <> struct LaneVec<uint16_t> {
       o[2 * i + 1] = fmaf(p, hi(w[i]), o[2 * i + 1]);
     }
   }
-  __device__ static __forceinline__ void store(uint16_t* p, const float* f, int h) {
+  // the lane's two pieces to p0 and p1
+  __device__ static __forceinline__ void store(uint16_t* p0, uint16_t* p1, const float* f) {
     uint32_t w[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) w[i] = (uint32_t)f2bf(f[2 * i]) | ((uint32_t)f2bf(f[2 * i + 1]) << 16);
-    *(uint4*)p = make_uint4(w[0], w[1], w[2], w[3]);
-    *(uint4*)(p + h) = make_uint4(w[4], w[5], w[6], w[7]);
+    *(uint4*)p0 = make_uint4(w[0], w[1], w[2], w[3]);
+    *(uint4*)p1 = make_uint4(w[4], w[5], w[6], w[7]);
   }
   __device__ static __forceinline__ void copy(uint16_t* d, const uint16_t* s, int h) {
     *(uint4*)d = *(const uint4*)s;
@@ -80,9 +81,9 @@ template <> struct LaneVec<float> {
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] = fmaf(p, __uint_as_float(w[i]), o[i]);
   }
-  __device__ static __forceinline__ void store(float* p, const float* f, int h) {
-    *(float4*)p = make_float4(f[0], f[1], f[2], f[3]);
-    *(float4*)(p + h) = make_float4(f[4], f[5], f[6], f[7]);
+  __device__ static __forceinline__ void store(float* p0, float* p1, const float* f) {
+    *(float4*)p0 = make_float4(f[0], f[1], f[2], f[3]);
+    *(float4*)p1 = make_float4(f[4], f[5], f[6], f[7]);
   }
   __device__ static __forceinline__ void copy(float* d, const float* s, int h) {
     *(float4*)d = *(const float4*)s;
@@ -303,7 +304,11 @@ __device__ __forceinline__ void swa_body(const AttnArgs& a, int hg, int slot, fl
     float o[E];
 #pragma unroll
     for (int i = 0; i < E; ++i) o[i] = acc.o[i] * inv;
-    LV::store((T*)a.out + (int64_t)slot * d + col, o, h);
+    T* out = (T*)a.out;
+    if (a.out_pk)  // the 8-element pieces are 8-aligned: contiguous in fragment order
+      LV::store(out + pk_off(slot, col, d >> 6), out + pk_off(slot, col + h, d >> 6), o);
+    else
+      LV::store(out + (int64_t)slot * d + col, out + (int64_t)slot * d + col + h, o);
   }
   // cache insert after every read of this workgroup
   __syncthreads();
@@ -378,11 +383,12 @@ __device__ __forceinline__ void xcombine_body(const AttnArgs& a, int head, int s
   float L = 0.f;
   for (int c = 0; c < nc; ++c) L += P[c * cs + DH + 1] * exp2f(P[c * cs + DH] - M);
   const float inv = 1.f / L;
-  T* out = (T*)a.out + (int64_t)slot * a.d + head * DH;
+  T* out = (T*)a.out;
   for (int e = tid; e < DH; e += nt) {
     float o = 0.f;
     for (int c = 0; c < nc; ++c) o = fmaf(P[c * cs + e], exp2f(P[c * cs + DH] - M), o);
-    out[e] = from_f<T>(o * inv);
+    const int col = head * DH + e;
+    out[a.out_pk ? pk_off(slot, col, a.d >> 6) : (int64_t)slot * a.d + col] = from_f<T>(o * inv);
   }
 }
 

@@ -35,9 +35,11 @@ struct Epi {
 
   // next RMSNorm's input: zb = z * gain (the rstd is applied by the consumer)
   __device__ __forceinline__ float produce(int m, int ca, float za, int cb, float zb) const {
-    T* o = (T*)a.zb + (int64_t)m * a.d;
-    o[ca] = from_f<T>(za * a.gnext[ca]);
-    o[cb] = from_f<T>(zb * a.gnext[cb]);
+    T* o = (T*)a.zb;
+    const int64_t ia = a.pk ? pk_off(m, ca, a.d >> 6) : (int64_t)m * a.d + ca;
+    const int64_t ib = a.pk ? pk_off(m, cb, a.d >> 6) : (int64_t)m * a.d + cb;
+    o[ia] = from_f<T>(za * a.gnext[ca]);
+    o[ib] = from_f<T>(zb * a.gnext[cb]);
     return za * za + zb * zb;
   }
 
@@ -86,7 +88,7 @@ struct Epi {
         va *= rs;
         vb *= rs;
         const float act = va * sigmoidf_(va) * vb;
-        ((T*)a.out_k)[(int64_t)m * a.ldo + ca] = from_f<T>(act);
+        ((T*)a.out_k)[a.pk ? pk_off(m, ca, (int)(a.ldo >> 6)) : (int64_t)m * a.ldo + ca] = from_f<T>(act);
         return 0.f;
       }
       case EPI_MGATE: {

@@ -207,6 +207,136 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_tile(GemmArgs g, Epi<uint16_t
   }
 }
 
+// Product for calls above 32 rows with both operands in fragment order (see
+// pk_off): a workgroup owns 32 RB rows x CB column pairs over the whole K, so
+// there is no K split and no partial traffic; its four waves take the 64-wide
+// K chunks round-robin (wave w: chunks w, w + 4, ...) and load each chunk's
+// fragments straight into registers, every load instruction reading 1 KB of
+// consecutive bytes, PF chunks ahead. No LDS staging and no barrier inside the
+// K loop. The four wave partials are summed in LDS in wave order by the
+// epilogue threads (16 consecutive threads per row and column pair, as in the
+// other tiles). Tile order: workgroup b runs on XCD b % 8 and takes column
+// tile 8 (q / mtiles) + b % 8 and row tile q % mtiles (q = b / 8), so the row
+// tiles of one column tile share its weights in one L2.
+// grid: 8 * mtiles * ceil(ntiles / 8); block 256.
+template <int RB, int CB>
+__global__ __launch_bounds__(256) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16_t> epi) {
+  constexpr int R = 32 * RB, PF = 2;
+  constexpr int TILE = RB * CB * 16 * 64;  // floats of one wave's partial tile
+  __shared__ float red[4 * TILE];
+  __shared__ float s_rstd[R];
+  __shared__ float s_part[256];
+  const int mtiles = (g.M + R - 1) / R, ntiles = g.npairs / CB;
+  const int b = blockIdx.x, q = b >> 3;
+  const int mt = q % mtiles, nt = 8 * (q / mtiles) + (b & 7);
+  if (nt >= ntiles) return;  // whole workgroup, before any barrier
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int m0 = mt * R;
+  const int nchunk = g.K >> 6;
+  const uint16_t* ap[RB];
+  const uint16_t* wp[CB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) ap[r] = (const uint16_t*)g.A + ((int64_t)(mt * RB + r) * nchunk * 256 + lane) * 8;
+#pragma unroll
+  for (int c = 0; c < CB; ++c) wp[c] = (const uint16_t*)g.Wp + ((int64_t)(nt * CB + c) * nchunk * 256 + lane) * 8;
+  const bool norm_here = g.ssq_in != nullptr;
+  RowRstd<R> rr(g, norm_here ? m0 : 0);
+  const int n = (nchunk - wave + 3) >> 2;  // chunks of this wave
+  bf16x8_t ra[PF][RB][4], rw[PF][CB][4];
+  f32x16_t acc[RB][CB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r)
+#pragma unroll
+    for (int c = 0; c < CB; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[r][c][e] = 0.f;
+  auto load = [&](int slot, int i) {
+    const int64_t off = (int64_t)(wave + 4 * i) * 256 * 8;
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+      for (int st = 0; st < 4; ++st) ra[slot][r][st] = load8(ap[r] + off + st * 512);
+#pragma unroll
+    for (int c = 0; c < CB; ++c)
+#pragma unroll
+      for (int st = 0; st < 4; ++st) rw[slot][c][st] = load8(wp[c] + off + st * 512);
+  };
+  auto compute = [&](int slot) {
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int c = 0; c < CB; ++c)
+          acc[r][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[slot][r][st], rw[slot][c][st], acc[r][c], 0, 0, 0);
+  };
+#pragma unroll
+  for (int p = 0; p < PF; ++p)
+    if (p < n) load(p, p);
+  int i = 0;
+  for (; i + PF <= n; i += PF) {
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      compute(p);
+      if (i + p + PF < n) load(p, i + p + PF);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < PF; ++p)
+    if (i + p < n) compute(p);
+  // wave partials to LDS; C layout of a 32x32 block: acc[4 gg + qq] of lane l
+  // is row 8 gg + 4 (l / 32) + qq, column l % 32
+#pragma unroll
+  for (int r = 0; r < RB; ++r)
+#pragma unroll
+    for (int c = 0; c < CB; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) red[wave * TILE + ((r * CB + c) * 16 + e) * 64 + lane] = acc[r][c][e];
+  if (norm_here) rr.finish(g, m0, s_part, s_rstd);  // uniform branch: contains a barrier
+  __syncthreads();
+  const int c16 = tid & 15;
+  for (int it = tid >> 4; it < R * CB; it += 16) {  // same trip count on every thread
+    const int row = it / CB, pc = it - row * CB;
+    const int m = m0 + row, pair = nt * CB + pc;
+    const int r32 = row & 31;
+    const int ia = (((row >> 5) * CB + pc) * 16 + 4 * (r32 >> 3) + (r32 & 3)) * 64 + ((r32 >> 2) & 1) * 32 + c16;
+    const int ib = ia + 16;
+    const float va = ((red[ia] + red[TILE + ia]) + red[2 * TILE + ia]) + red[3 * TILE + ia];
+    const float vb = ((red[ib] + red[TILE + ib]) + red[2 * TILE + ib]) + red[3 * TILE + ib];
+    int ba, bb;
+    pair_blocks(g, pair, ba, bb);
+    float sq = 0.f;
+    if (m < g.M) sq = epi(m, ba * 16 + c16, va, bb * 16 + c16, vb, norm_here ? s_rstd[row] : 1.f);
+    if (g.ssq_out) {
+      sq = sum16(sq);
+      if (c16 == 0 && m < g.M) g.ssq_out[(int64_t)pair * g.M_pad + m] = sq;
+    }
+  }
+}
+
+// Weights in fragment order: one thread per 16-byte fragment (pair p = block
+// p of the packed rows: its virtual columns 0-15 are block ba, 16-31 block bb).
+__global__ __launch_bounds__(256) void k_pack_weights(GemmArgs g, uint16_t* dst) {
+  const int nchunk = g.K >> 6;
+  const int64_t total = (int64_t)g.npairs * nchunk * 256;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int l = (int)(i & 63), st = (int)((i >> 6) & 3);
+  const int64_t pc = i >> 8;
+  const int c = (int)(pc % nchunk), p = (int)(pc / nchunk);
+  int ba, bb;
+  pair_blocks(g, p, ba, bb);
+  const int v = l & 31;
+  const int k = 64 * c + 32 * (l >> 5) + 8 * st;
+  const uint16_t* src = weight_row<uint16_t>(g, ((v & 16) ? bb : ba) * 16 + (v & 15)) + k;
+  *(uint4*)(dst + i * 8) = *(const uint4*)src;
+}
+
+void launch_pack_weights(const GemmArgs& g, void* Wp, hipStream_t s) {
+  const int64_t total = (int64_t)g.npairs * (g.K >> 6) * 256;
+  hipLaunchKernelGGL(k_pack_weights, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, g, (uint16_t*)Wp);
+}
+
 // grid: x = pair, y = ceil(M/16); block 256
 template <typename T>
 __global__ __launch_bounds__(256) void k_splitk_epi(GemmArgs g, Epi<T> epi) {
@@ -259,6 +389,21 @@ void launch_gemm(int dtype, const GemmArgs& g0, const EpiArgs& e, hipStream_t s)
   if (dtype == 0) {
     dim3 grid((g.Nv / 2 + 63) / 64, g.M);
     hipLaunchKernelGGL(k_gemm_f32, grid, dim3(64), 0, s, g, Epi<float>{e});
+    return;
+  }
+  if (g.Wp) {
+    Phase bad{};
+    bad.kind = PH_INVALID;  // not runnable by the persistent kernel: the recording is dropped
+    if (record_phase(bad)) return;
+    Epi<uint16_t> epi{e};
+    const int mtiles = (g.M + 32 * g.rb - 1) / (32 * g.rb), ntiles = g.npairs / g.cb;
+    dim3 grid(8 * mtiles * ((ntiles + 7) / 8));
+    if (g.rb == 2 && g.cb == 2)
+      hipLaunchKernelGGL((k_gemm_bf16_pk<2, 2>), grid, dim3(256), 0, s, g, epi);
+    else if (g.rb == 2)
+      hipLaunchKernelGGL((k_gemm_bf16_pk<2, 1>), grid, dim3(256), 0, s, g, epi);
+    else
+      hipLaunchKernelGGL((k_gemm_bf16_pk<1, 1>), grid, dim3(256), 0, s, g, epi);
     return;
   }
   const int MB = g.mb;

@@ -82,6 +82,14 @@ struct rlt_ctx {
   int split_min_rows;  // calls with at least this many rows run as two streams (0 = never)
   int gemm_target;     // K split target of the persistent step's products (0: stand-alone kernels)
   size_t partial_cap;  // floats per workspace
+  // bf16 calls above 32 rows: the decoder's weights in fragment order (a
+  // library-owned copy, rebuilt by rlt_refresh_weights) and the products
+  // that read them; the activations they multiply are then written in
+  // fragment order by their producers
+  bool pk_ready;
+  std::vector<void*> pk_qkv, pk_wo, pk_wqm, pk_wom, pk_gu, pk_down;
+  void* pk_out;
+  std::vector<std::pair<GemmArgs, void*>> pk_all;
   // persistent step for calls of at most fused_rows rows (bf16; 0 = off)
   int fused_rows;
   int fused_grid;      // workgroups = compute units
@@ -253,6 +261,7 @@ extern "C" void rlt_destroy(rlt_ctx* c) {
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   if (c->fused_sync) (void)hipFree(c->fused_sync);
+  for (auto& e : c->pk_all) (void)hipFree(e.second);
   for (void* p : {c->mem_A, (void*)c->mem_ssq, (void*)c->mem_src, (void*)c->mem_t, (void*)c->mem_offs,
                   (void*)c->mem_lens})
     if (p) (void)hipFree(p);
@@ -287,6 +296,61 @@ static int alloc_workspace(rlt_ctx* c, Workspace& w, bool full) {
   if (hipMemset(w.X, 0, M * 2 * d * es) != hipSuccess || hipMemset(w.o, 0, M * d * es) != hipSuccess ||
       hipMemset(w.h, 0, M * d * es) != hipSuccess || hipMemset(w.act, 0, M * F * es) != hipSuccess)
     return fail(RLT_EHIP, "workspace initialisation failed");
+  return RLT_OK;
+}
+
+// Fragment-order copies of the decoder's product weights (bf16 contexts that
+// take calls above 32 rows): one per product as the transition calls it
+// (Q/K/V together, gate/up together). Weights not 16-byte aligned leave the
+// copies unbuilt and those calls on the LDS tile.
+static int build_packed(rlt_ctx* c) {
+  const rlt_config& cf = c->cfg;
+  const int d = cf.d_model, F = cf.d_ffn, L = cf.n_layers;
+  std::vector<const void*> all = {c->w_out};
+  for (auto* v : {&c->wq, &c->wk, &c->wv, &c->wo, &c->wqm, &c->wom, &c->w_gate, &c->w_up, &c->w_down})
+    all.insert(all.end(), v->begin(), v->end());
+  for (const void* p : all)
+    if ((uintptr_t)p % 16) return RLT_OK;
+  auto pack = [&](std::initializer_list<const void*> W, int seg_rows, int K, int pairing, void** out) -> int {
+    GemmArgs g{};
+    int i = 0;
+    for (const void* p : W) g.W[i++] = p;
+    g.nseg = i;
+    g.seg_rows = seg_rows;
+    g.K = K;
+    g.pairing = pairing;
+    g.dh = cf.d_head;
+    g.Nv = g.nseg * seg_rows;
+    g.npairs = g.Nv / 32;
+    int rc = dev_alloc(out, (size_t)g.Nv * K * 2);
+    if (rc) return rc;
+    c->pk_all.push_back({g, *out});
+    launch_pack_weights(g, *out, nullptr);
+    return RLT_OK;
+  };
+  for (auto* v : {&c->pk_qkv, &c->pk_wo, &c->pk_wqm, &c->pk_wom, &c->pk_gu, &c->pk_down}) v->assign(L, nullptr);
+  int rc = 0;
+  for (int l = 0; l < L && !rc; ++l) {
+    if ((rc = pack({c->wq[l], c->wk[l], c->wv[l]}, d, d, PAIR_ROPE, &c->pk_qkv[l])) ||
+        (rc = pack({c->wo[l]}, d, d, PAIR_PLAIN, &c->pk_wo[l])) ||
+        (rc = pack({c->wqm[l]}, d, d, PAIR_ROPE, &c->pk_wqm[l])) ||
+        (rc = pack({c->wom[l]}, d, d, PAIR_PLAIN, &c->pk_wom[l])) ||
+        (rc = pack({c->w_gate[l], c->w_up[l]}, F, d, PAIR_DUAL, &c->pk_gu[l])) ||
+        (rc = pack({c->w_down[l]}, d, F, PAIR_PLAIN, &c->pk_down[l])))
+      break;
+  }
+  if (!rc) rc = pack({c->w_out}, cf.vocab, d, PAIR_PLAIN, &c->pk_out);
+  if (rc) return rc;
+  HIP_TRY(hipGetLastError());
+  HIP_TRY(hipDeviceSynchronize());
+  c->pk_ready = true;
+  return RLT_OK;
+}
+
+extern "C" int rlt_refresh_weights(rlt_ctx* c, void* stream) {
+  if (!c) return fail(RLT_EINVAL, "null context");
+  for (auto& e : c->pk_all) launch_pack_weights(e.first, e.second, (hipStream_t)stream);
+  HIP_TRY(hipGetLastError());
   return RLT_OK;
 }
 
@@ -424,6 +488,12 @@ extern "C" int rlt_create(const rlt_config* cfg, const rlt_weights* w, int32_t m
     rlt_destroy(c);
     return fail(RLT_EHIP, "pinned staging allocation failed");
   }
+  if (c->dt == 1 && max_rows > 32 && d % 64 == 0 && F % 64 == 0 && env_int("RLT_GEMM_PK", 1)) {
+    if ((rc = build_packed(c))) {
+      rlt_destroy(c);
+      return rc;
+    }
+  }
   *out = c;
   return RLT_OK;
 }
@@ -464,8 +534,9 @@ struct Gemm {
   int m_pad = 0;       // rows allocated in A (default: the context's M_pad)
   int ssq_units = 0;   // units of ssq_in (default: the decoder producers' units)
 
+  // Wp: the weights in fragment order; A is then in fragment order too
   void run(const void* A, int64_t lda, std::initializer_list<const void*> W, int seg_rows, int K, int pairing,
-           int n, EpiArgs e, const float* ssq_in = nullptr, float* ssq_out = nullptr) {
+           int n, EpiArgs e, const float* ssq_in = nullptr, float* ssq_out = nullptr, const void* Wp = nullptr) {
     GemmArgs g{};
     g.A = A;
     g.lda = lda;
@@ -489,7 +560,15 @@ struct Gemm {
     g.ssq_units = ssq_units ? ssq_units : c->cfg.d_model / (c->dt == 1 ? 32 : 2);  // producers' column units
     g.inv_d = 1.0f / (float)c->cfg.d_model;
     g.eps = c->cfg.rms_eps;
-    if (c->dt == 1 && c->gemm_wide && n > 32 && g.npairs % 2 == 0 && K % 64 == 0) {
+    if (Wp) {
+      // tile shape: the largest of 64 x 2 pairs, 64 x 1, 32 x 1 that still
+      // gives 160 workgroups (measured per product shape at 64-128 rows)
+      g.Wp = Wp;
+      auto wgs = [&](int rb, int cb) { return (g.npairs % cb ? 0 : g.npairs / cb) * ((n + 32 * rb - 1) / (32 * rb)); };
+      if (wgs(2, 2) >= 160) g.rb = 2, g.cb = 2;
+      else if (wgs(2, 1) >= 160) g.rb = 2, g.cb = 1;
+      else g.rb = 1, g.cb = 1;
+    } else if (c->dt == 1 && c->gemm_wide && n > 32 && g.npairs % 2 == 0 && K % 64 == 0) {
       // LDS tile of 128 rows x 64 columns (128 when that still leaves two
       // workgroups per compute unit); K split while each split adds a
       // workgroup per compute unit and keeps at least 8 stages of 64
@@ -556,7 +635,14 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
   const size_t es = c->es;
   Gemm gm{c, &w, s};
 
+  // bf16 calls above 32 rows run the fragment-order products: every producer
+  // of their activations (residual / merge epilogues, SwiGLU, attention
+  // outputs) writes in fragment order
+  const bool pk = c->pk_ready && n > 32;
+  auto pw = [&](const std::vector<void*>& v, int l) -> const void* { return pk ? v[l] : nullptr; };
+
   EpiArgs E0{};
+  E0.pk = pk ? 1 : 0;
   E0.rows = P.R;
   E0.d = d;
   E0.dh = dh;
@@ -648,6 +734,7 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
   at.chunk = c->chunk;
   at.nch = c->nch;
   at.part = w.part;
+  at.out_pk = pk ? 1 : 0;
   at.sb = P.mem.stride_b;
   at.st = P.mem.stride_t;
 
@@ -660,7 +747,7 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
       e.out_f = w.q;
       e.out_k = w.kc;
       e.out_v = w.vc;
-      gm.run(w.h, d, {c->wq[l], c->wk[l], c->wv[l]}, d, d, PAIR_ROPE, n, e, w.ssq);
+      gm.run(w.h, d, {c->wq[l], c->wk[l], c->wv[l]}, d, d, PAIR_ROPE, n, e, w.ssq, nullptr, pw(c->pk_qkv, l));
     }
     at.q = w.q;
     at.kc = w.kc;
@@ -674,7 +761,7 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
     e.kind = EPI_RESID;
     e.out_f = w.z;
     e.ldo = d;
-    gm.run(w.o, d, {c->wo[l]}, d, d, PAIR_PLAIN, n, producer(e, gnext), nullptr, w.ssq);
+    gm.run(w.o, d, {c->wo[l]}, d, d, PAIR_PLAIN, n, producer(e, gnext), nullptr, w.ssq, pw(c->pk_wo, l));
   };
   // ---- cross-attention sublayer [eq. (2.15)]: RMSNorm_M folded into the query ----
   auto cross = [&](int l, const float* gnext) {
@@ -682,7 +769,7 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
       EpiArgs e = E0;
       e.kind = EPI_QROT;
       e.out_f = w.qm;
-      gm.run(w.h, d, {c->wqm[l]}, d, d, PAIR_ROPE, n, e, w.ssq);
+      gm.run(w.h, d, {c->wqm[l]}, d, d, PAIR_ROPE, n, e, w.ssq, nullptr, pw(c->pk_wqm, l));
     }
     const int g = (l * cf.n_groups) / L;
     at.q = w.qm;
@@ -696,7 +783,7 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
     e.kind = EPI_RESID;
     e.out_f = w.z;
     e.ldo = d;
-    gm.run(w.o, d, {c->wom[l]}, d, d, PAIR_PLAIN, n, producer(e, gnext), nullptr, w.ssq);
+    gm.run(w.o, d, {c->wom[l]}, d, d, PAIR_PLAIN, n, producer(e, gnext), nullptr, w.ssq, pw(c->pk_wom, l));
   };
   // ---- FFN sublayer [eq. (2.16)]: RMSNorm_D folded into gate/up ----
   auto ffn = [&](int l, const float* gnext) {
@@ -704,11 +791,11 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
     e.kind = EPI_SWIGLU;
     e.out_k = w.act;
     e.ldo = F;
-    gm.run(w.h, d, {c->w_gate[l], c->w_up[l]}, F, d, PAIR_DUAL, n, e, w.ssq);
+    gm.run(w.h, d, {c->w_gate[l], c->w_up[l]}, F, d, PAIR_DUAL, n, e, w.ssq, nullptr, pw(c->pk_gu, l));
     e.kind = EPI_RESID;
     e.out_f = w.z;
     e.ldo = d;
-    gm.run(w.act, F, {c->w_down[l]}, d, F, PAIR_PLAIN, n, producer(e, gnext), nullptr, w.ssq);
+    gm.run(w.act, F, {c->w_down[l]}, d, F, PAIR_PLAIN, n, producer(e, gnext), nullptr, w.ssq, pw(c->pk_down, l));
   };
   for (int l = 0; l < L; ++l) {
     for (int i = 0; i < 3; ++i) {
@@ -733,7 +820,8 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
     e.kind = EPI_STORE;
     e.out_f = logits;
     e.ldo = cf.vocab;
-    gm.run(w.h, d, {c->w_out}, cf.vocab, d, PAIR_PLAIN, n, e, w.ssq);  // RMSNorm_o folded in [eq. (2.6)]
+    gm.run(w.h, d, {c->w_out}, cf.vocab, d, PAIR_PLAIN, n, e, w.ssq, nullptr,
+           pk ? c->pk_out : nullptr);  // RMSNorm_o folded in [eq. (2.6)]
   }
   if (P.do_readout) {
     ReadoutArgs ro = P.ro;
@@ -1465,6 +1553,59 @@ extern "C" int rlt_dbg_gemm(rlt_ctx* c, const void* A, const void* W, int32_t M,
   gm.run(stage, K, {W}, N, K, PAIR_PLAIN, M, e);
   HIP_TRY(hipGetLastError());
   return RLT_OK;
+}
+
+extern "C" int rlt_dbg_gemm_packed(rlt_ctx* c, const void* A, const void* W, int32_t M, int32_t N, int32_t K,
+                                   float* out, void* stream) {
+  if (!c || !A || !W || !out) return fail(RLT_EINVAL, "null argument");
+  if (c->dt != 1) return fail(RLT_EUNSUPPORTED, "the operand-order path is bf16 only");
+  const int kmax = std::max(2 * c->cfg.d_model, c->cfg.d_ffn);
+  if (M <= 32 || M > c->max_rows || N < 32 || N % 32 || K < 64 || K % 64 || K > kmax)
+    return fail(RLT_ESHAPE, "need 33 <= M <= max_rows, N a multiple of 32, K a multiple of 64 <= max(2*d_model, d_ffn)");
+  hipStream_t s = (hipStream_t)stream;
+  const Workspace& w = c->ws[0];
+  const int Mr = (M + 63) / 64 * 64;  // whole row tiles of the 64-row shapes (<= M_pad)
+  void *Ap = nullptr, *Wp = nullptr;
+  int rc = dev_alloc(&Ap, (size_t)Mr * K * 2);
+  if (!rc) rc = dev_alloc(&Wp, (size_t)N * K * 2);
+  if (!rc) {
+    // rows of A past M (up to the 64-row tile) are zero
+    GemmArgs ga{}, gw{};
+    ga.W[0] = A;
+    ga.nseg = 1;
+    ga.seg_rows = Mr;
+    ga.K = K;
+    ga.pairing = PAIR_PLAIN;
+    ga.Nv = Mr;
+    ga.npairs = Mr / 32;
+    gw = ga;
+    gw.W[0] = W;
+    gw.seg_rows = gw.Nv = N;
+    gw.npairs = N / 32;
+    void* stage = w.act;  // [M_pad][d_ffn] >= Mr x K when K <= d_ffn; else X (2 d_model wide)
+    if (K > c->cfg.d_ffn) stage = w.X;
+    if (hipMemsetAsync(stage, 0, (size_t)Mr * K * 2, s) != hipSuccess ||
+        hipMemcpyAsync(stage, A, (size_t)M * K * 2, hipMemcpyDeviceToDevice, s) != hipSuccess) {
+      rc = fail(RLT_EHIP, "staging copy failed");
+    } else {
+      ga.W[0] = stage;
+      launch_pack_weights(ga, Ap, s);
+      launch_pack_weights(gw, Wp, s);
+      Rows R{c->ident, c->ident, c->ones, M};
+      EpiArgs e{};
+      e.kind = EPI_STORE;
+      e.rows = R;
+      e.out_f = out;
+      e.ldo = N;
+      Gemm gm{c, &w, s};
+      gm.run(Ap, K, {W}, N, K, PAIR_PLAIN, M, e, nullptr, nullptr, Wp);
+      if (hipGetLastError() != hipSuccess || hipStreamSynchronize(s) != hipSuccess)
+        rc = fail(RLT_EHIP, "operand-order product failed");
+    }
+  }
+  if (Ap) (void)hipFree(Ap);
+  if (Wp) (void)hipFree(Wp);
+  return rc;
 }
 
 extern "C" int rlt_dbg_profile(rlt_ctx* c, int32_t enable) {

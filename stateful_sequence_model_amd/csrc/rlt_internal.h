@@ -73,10 +73,25 @@ struct EIn {
 
 enum Pairing { PAIR_PLAIN = 0, PAIR_ROPE = 1, PAIR_DUAL = 2 };
 
+// Fragment order of a bf16 operand [R][K] (R a multiple of 32, K of 64) of
+// v_mfma_f32_32x32x16_bf16: for 32-row block b, 64-wide K chunk c and step
+// s < 4, the 64 lanes' 16-byte fragments are contiguous; lane l holds row
+// 32 b + l % 32 and k in [64 c + 32 (l / 32) + 8 s, + 8). The k order inside
+// a chunk is a permutation of the plain one, applied alike to both operands
+// of a product, so the sums are unchanged. One wave load instruction then
+// reads 1 KB of consecutive bytes.
+__host__ __device__ inline int64_t pk_off(int m, int k, int nchunk) {
+  return ((((int64_t)(m >> 5) * nchunk + (k >> 6)) * 4 + ((k & 31) >> 3)) * 64 + ((k >> 5) & 1) * 32 + (m & 31)) * 8 +
+         (k & 7);
+}
+
 struct GemmArgs {
-  const void* A;          // [M_pad][lda] activations (T)
+  const void* A;          // [M_pad][lda] activations (T); fragment order when Wp is set
   int64_t lda;
   const void* W[3];       // weight segments, each [seg_rows][K] (T), natural layout
+  const void* Wp;         // bf16: the same weights in fragment order, virtual column
+                          // pairs as 32-row blocks (pair p = block p), or null
+  int rb, cb;             // fragment-order tile: 32 rb rows x cb column pairs
   int nseg, seg_rows;
   int K;
   int npairs;             // output handled as pairs of 16-column blocks
@@ -206,6 +221,7 @@ struct EpiArgs {
   // the [M][d] (T) buffer receiving z * gain, the next product's input
   const float* gnext;
   void* zb;
+  int pk;                   // bf16: zb and the SwiGLU output are written in fragment order
   // memory entries (EPI_MEMKV): one group's K / V buffers; the entry of slot
   // m is at rows[m] * msb + (t_row[m] - 1) * mst elements
   void* mk;
@@ -237,9 +253,12 @@ struct AttnArgs {
   int nch;                  // chunk slots per row in `part`
   float* part;              // [n][nch][H][dh + 2]
   void* out;                // [n][d] (T) attention output
+  int out_pk;               // bf16: out in fragment order (the next product's operand)
 };
 
 void launch_gemm(int dtype, const GemmArgs& g, const EpiArgs& e, hipStream_t s);
+// Wp <- g's weights (bf16) in fragment order (K % 64 == 0, Nv % 32 == 0)
+void launch_pack_weights(const GemmArgs& g, void* Wp, hipStream_t s);
 void launch_swa(int dtype, const AttnArgs& a, hipStream_t s);
 void launch_xattn(int dtype, const AttnArgs& a, hipStream_t s);
 void launch_xcombine(int dtype, const AttnArgs& a, hipStream_t s);

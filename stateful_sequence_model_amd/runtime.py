@@ -290,6 +290,11 @@ class Decoder:
     def sync_error(self, stream=None) -> int:
         return A.rlt_sync_error(self.ctx, current_stream() if stream is None else stream)
 
+    def refresh_weights(self, stream=None) -> int:
+        """Rebuild the context's operand-order weight copy after the weight
+        tensors were changed in place (rlt_refresh_weights)."""
+        return A.rlt_refresh_weights(self.ctx, current_stream() if stream is None else stream)
+
     # -- exact prefix snapshots ---------------------------------------------------
     def snapshot(self, st: DecoderState, rows, stream=None) -> np.ndarray:
         """Snapshots of the listed rows: a uint8 array [n, bytes per row]
@@ -327,11 +332,13 @@ class Decoder:
         return A.rlt_memory_prefill(self.ctx, mw.c, mem, T_cap, len(lens), lens.ctypes.data, e.data_ptr(),
                                     e.stride(0), e.stride(1), current_stream() if stream is None else stream)
 
-    def dbg_gemm(self, Amat: torch.Tensor, W: torch.Tensor, out: torch.Tensor, stream=None) -> int:
+    def dbg_gemm(self, Amat: torch.Tensor, W: torch.Tensor, out: torch.Tensor, stream=None,
+                 packed: bool = False) -> int:
         M, K = Amat.shape
         N = W.shape[0]
-        return A.rlt_dbg_gemm(self.ctx, Amat.data_ptr(), W.data_ptr(), M, N, K, out.data_ptr(),
-                              current_stream() if stream is None else stream)
+        fn = A.rlt_dbg_gemm_packed if packed else A.rlt_dbg_gemm
+        return fn(self.ctx, Amat.data_ptr(), W.data_ptr(), M, N, K, out.data_ptr(),
+                  current_stream() if stream is None else stream)
 
 
 class MemoryWeights:
