@@ -25,11 +25,11 @@ int rlt_dbg_gemm(rlt_ctx* ctx, const void* A, const void* W, int32_t M, int32_t 
                  void* stream);
 
 /* The same product through the operand-order path that bf16 decoder calls
- * above 32 rows take: W and A are first rearranged into the order of the
- * 32x32x16 matrix instruction (into buffers this call allocates and frees;
- * it waits for `stream`), then multiplied with the tile shape an M-row call
- * would use. Requires a bf16 context, 33 <= M <= max_rows, N a multiple of
- * 32, K a multiple of 64, K <= max(2 * d_model, d_ffn). */
+ * take: W and A are first rearranged into the order of the 32x32x16 matrix
+ * instruction (into buffers this call allocates and frees; it waits for
+ * `stream`), then multiplied with the tile shape an M-row call would use.
+ * Requires a bf16 context, 1 <= M <= max_rows, N a multiple of 32, K a
+ * multiple of 64, K <= max(2 * d_model, d_ffn). */
 int rlt_dbg_gemm_packed(rlt_ctx* ctx, const void* A, const void* W, int32_t M, int32_t N, int32_t K, float* out,
                         void* stream);
 

@@ -207,13 +207,15 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_tile(GemmArgs g, Epi<uint16_t
   }
 }
 
-// Product for calls above 32 rows with both operands in fragment order (see
-// pk_off): a workgroup owns 32 RB rows x CB column pairs over the whole K, so
+// Product with both operands in fragment order (see pk_off): a workgroup owns
+// 32 RB rows x CB column pairs over the whole K, so
 // there is no K split and no partial traffic; its four waves take the 64-wide
 // K chunks round-robin (wave w: chunks w, w + 4, ...) and load each chunk's
 // fragments straight into registers, every load instruction reading 1 KB of
 // consecutive bytes, PF chunks ahead. No LDS staging and no barrier inside the
-// K loop. The four wave partials are summed in LDS in wave order by the
+// K loop. Lanes of rows at or past M load no activations (zeros), so a call
+// of a few rows reads little more than the weights. The four wave partials
+// are summed in LDS in wave order by the
 // epilogue threads (16 consecutive threads per row and column pair, as in the
 // other tiles). Tile order: workgroup b runs on XCD b % 8 and takes column
 // tile 8 (q / mtiles) + b % 8 and row tile q % mtiles (q = b / 8), so the row
@@ -250,12 +252,15 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16_t> 
     for (int c = 0; c < CB; ++c)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[r][c][e] = 0.f;
+  bool live[RB];  // this lane's activation row exists
+#pragma unroll
+  for (int r = 0; r < RB; ++r) live[r] = m0 + 32 * r + (lane & 31) < g.M;
   auto load = [&](int slot, int i) {
     const int64_t off = (int64_t)(wave + 4 * i) * 256 * 8;
 #pragma unroll
     for (int r = 0; r < RB; ++r)
 #pragma unroll
-      for (int st = 0; st < 4; ++st) ra[slot][r][st] = load8(ap[r] + off + st * 512);
+      for (int st = 0; st < 4; ++st) ra[slot][r][st] = live[r] ? load8(ap[r] + off + st * 512) : bf16x8_t{};
 #pragma unroll
     for (int c = 0; c < CB; ++c)
 #pragma unroll

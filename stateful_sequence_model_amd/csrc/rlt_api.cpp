@@ -82,7 +82,7 @@ struct rlt_ctx {
   int split_min_rows;  // calls with at least this many rows run as two streams (0 = never)
   int gemm_target;     // K split target of the persistent step's products (0: stand-alone kernels)
   size_t partial_cap;  // floats per workspace
-  // bf16 calls above 32 rows: the decoder's weights in fragment order (a
+  // bf16: the decoder's weights in fragment order (a
   // library-owned copy, rebuilt by rlt_refresh_weights) and the products
   // that read them; the activations they multiply are then written in
   // fragment order by their producers
@@ -299,8 +299,8 @@ static int alloc_workspace(rlt_ctx* c, Workspace& w, bool full) {
   return RLT_OK;
 }
 
-// Fragment-order copies of the decoder's product weights (bf16 contexts that
-// take calls above 32 rows): one per product as the transition calls it
+// Fragment-order copies of the decoder's product weights (bf16 contexts): one
+// per product as the transition calls it
 // (Q/K/V together, gate/up together). Weights not 16-byte aligned leave the
 // copies unbuilt and those calls on the LDS tile.
 static int build_packed(rlt_ctx* c) {
@@ -488,7 +488,7 @@ extern "C" int rlt_create(const rlt_config* cfg, const rlt_weights* w, int32_t m
     rlt_destroy(c);
     return fail(RLT_EHIP, "pinned staging allocation failed");
   }
-  if (c->dt == 1 && max_rows > 32 && d % 64 == 0 && F % 64 == 0 && env_int("RLT_GEMM_PK", 1)) {
+  if (c->dt == 1 && d % 64 == 0 && F % 64 == 0 && env_int("RLT_GEMM_PK", 1)) {
     if ((rc = build_packed(c))) {
       rlt_destroy(c);
       return rc;
@@ -562,10 +562,12 @@ struct Gemm {
     g.eps = c->cfg.rms_eps;
     if (Wp) {
       // tile shape: the largest of 64 x 2 pairs, 64 x 1, 32 x 1 that still
-      // gives 160 workgroups (measured per product shape at 64-128 rows)
+      // gives 160 workgroups (measured per product shape at 32-128 rows);
+      // 32 rows at most for calls of at most 32 rows
       g.Wp = Wp;
       auto wgs = [&](int rb, int cb) { return (g.npairs % cb ? 0 : g.npairs / cb) * ((n + 32 * rb - 1) / (32 * rb)); };
-      if (wgs(2, 2) >= 160) g.rb = 2, g.cb = 2;
+      if (n <= 32) g.rb = 1, g.cb = 1;
+      else if (wgs(2, 2) >= 160) g.rb = 2, g.cb = 2;
       else if (wgs(2, 1) >= 160) g.rb = 2, g.cb = 1;
       else g.rb = 1, g.cb = 1;
     } else if (c->dt == 1 && c->gemm_wide && n > 32 && g.npairs % 2 == 0 && K % 64 == 0) {
@@ -635,10 +637,11 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
   const size_t es = c->es;
   Gemm gm{c, &w, s};
 
-  // bf16 calls above 32 rows run the fragment-order products: every producer
-  // of their activations (residual / merge epilogues, SwiGLU, attention
-  // outputs) writes in fragment order
-  const bool pk = c->pk_ready && n > 32;
+  // bf16 calls run the fragment-order products (except calls taken by the
+  // opt-in persistent step, which runs the narrow tile): every producer of
+  // their activations (residual / merge epilogues, SwiGLU, attention outputs)
+  // then writes in fragment order
+  const bool pk = c->pk_ready && !(c->fused_rows > 0 && n <= c->fused_rows);
   auto pw = [&](const std::vector<void*>& v, int l) -> const void* { return pk ? v[l] : nullptr; };
 
   EpiArgs E0{};
@@ -1560,8 +1563,8 @@ extern "C" int rlt_dbg_gemm_packed(rlt_ctx* c, const void* A, const void* W, int
   if (!c || !A || !W || !out) return fail(RLT_EINVAL, "null argument");
   if (c->dt != 1) return fail(RLT_EUNSUPPORTED, "the operand-order path is bf16 only");
   const int kmax = std::max(2 * c->cfg.d_model, c->cfg.d_ffn);
-  if (M <= 32 || M > c->max_rows || N < 32 || N % 32 || K < 64 || K % 64 || K > kmax)
-    return fail(RLT_ESHAPE, "need 33 <= M <= max_rows, N a multiple of 32, K a multiple of 64 <= max(2*d_model, d_ffn)");
+  if (M < 1 || M > c->max_rows || N < 32 || N % 32 || K < 64 || K % 64 || K > kmax)
+    return fail(RLT_ESHAPE, "need 1 <= M <= max_rows, N a multiple of 32, K a multiple of 64 <= max(2*d_model, d_ffn)");
   hipStream_t s = (hipStream_t)stream;
   const Workspace& w = c->ws[0];
   const int Mr = (M + 63) / 64 * 64;  // whole row tiles of the 64-row shapes (<= M_pad)

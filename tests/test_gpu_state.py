@@ -275,21 +275,28 @@ def test_argmax_sampling_and_scoring_against_oracle_on_gpu_logits():
 def test_persistent_step_equals_separate_kernels():
     """The persistent step (one kernel, grid barriers between the recorded
     phases; enabled per context with RLT_FUSED_ROWS) reproduces the separate
-    kernels bit for bit: same bodies, launch shapes and reduction orders.
+    kernels bit for bit: same bodies, launch shapes and reduction orders
+    (the reference context runs the same narrow-tile products, RLT_GEMM_PK=0,
+    since the persistent step does not take the operand-order products).
     Covers plain steps, hipGraph-captured steps and a replay from H_0."""
     require_gpu()
     import os
+
+    def with_env(env, fn):
+        old = {k: os.environ.get(k) for k in env}
+        os.environ.update(env)
+        try:
+            return fn()
+        finally:
+            for k, v in old.items():
+                if v is None:
+                    del os.environ[k]
+                else:
+                    os.environ[k] = v
+
     wl = SMALL.with_(B=8, T=40)
-    ref = GpuRun(wl)
-    old = os.environ.get("RLT_FUSED_ROWS")
-    os.environ["RLT_FUSED_ROWS"] = "16"
-    try:
-        fz = GpuRun(wl, raw=ref.raw)
-    finally:
-        if old is None:
-            del os.environ["RLT_FUSED_ROWS"]
-        else:
-            os.environ["RLT_FUSED_ROWS"] = old
+    ref = with_env({"RLT_GEMM_PK": "0"}, lambda: GpuRun(wl))
+    fz = with_env({"RLT_FUSED_ROWS": "16"}, lambda: GpuRun(wl, raw=ref.raw))
     for run in (ref, fz):
         run.init()
     S0, Z0 = ref.run(10)
