@@ -21,16 +21,83 @@ struct Epi {
     return to_f<T>(p[c]);
   }
 
-  // rotary transform of the pair (x_i, x_{i+dh/2}) of one head at position t
-  __device__ __forceinline__ void rotate(int m, int c_in_head, float& x, float& y) const {
-    const int t = a.rows.t_row[m];
+  // (cos, sin) of the rotary angle of pair index i (< dh/2) at position t:
+  // computed (no memory round trip inside an epilogue), or from the table,
+  // which holds the same values, when loaded ahead of the product
+  __device__ __forceinline__ float2 rope_cs(int t, int i, bool tab = false) const {
+    if (tab && a.rope_tab && t <= a.rope_tmax) return a.rope_tab[(int64_t)t * (a.dh >> 1) + i];
     double sn, cs;
-    sincos((double)t * a.inv_freq[c_in_head], &sn, &cs);
-    const float c = (float)cs, s = (float)sn;
-    const float xr = x * c - y * s;
-    const float yr = y * c + x * s;
+    sincos((double)t * a.inv_freq[i], &sn, &cs);
+    return make_float2((float)cs, (float)sn);
+  }
+  __device__ __forceinline__ static void rot(float2 r, float& x, float& y) {
+    const float xr = x * r.x - y * r.y;
+    const float yr = y * r.x + x * r.y;
     x = xr;
     y = yr;
+  }
+  // rotary transform of the pair (x_i, x_{i+dh/2}) of one head at position t
+  __device__ __forceinline__ void rotate(int m, int c_in_head, float& x, float& y) const {
+    rot(rope_cs(a.rows.t_row[m], c_in_head), x, y);
+  }
+
+  // Values an epilogue reads from memory for (row m, columns ca, cb), loaded
+  // ahead of the product by tiles that know their outputs in advance: the
+  // residual and the next norm's gains (EPI_RESID), the rotary (cos, sin)
+  // (EPI_QKV on q and k, EPI_QROT). apply() with them equals operator().
+  struct Pre {
+    float2 u, v;
+  };
+  __device__ __forceinline__ Pre pre(int m, int ca, int cb) const {
+    Pre p{};
+    if (a.kind == EPI_RESID) {
+      const float* z = a.out_f + (int64_t)m * a.ldo;
+      p.u = make_float2(z[ca], z[cb]);
+      p.v = make_float2(a.gnext[ca], a.gnext[cb]);
+    } else if (a.rope && (a.kind == EPI_QROT || (a.kind == EPI_QKV && ca / a.d < 2))) {
+      p.u = rope_cs(a.rows.t_row[m], (ca % a.d) % a.dh, true);
+    }
+    return p;
+  }
+  __device__ __forceinline__ float apply(int m, int ca, float va, int cb, float vb, float rs, const Pre& p) const {
+    if (a.kind == EPI_RESID) {
+      float* z = a.out_f + (int64_t)m * a.ldo;
+      const float za = p.u.x + va, zb = p.u.y + vb;
+      z[ca] = za;
+      z[cb] = zb;
+      T* o = (T*)a.zb;
+      const int64_t ia = a.pk ? pk_off(m, ca, a.d >> 6) : (int64_t)m * a.d + ca;
+      const int64_t ib = a.pk ? pk_off(m, cb, a.d >> 6) : (int64_t)m * a.d + cb;
+      o[ia] = from_f<T>(za * p.v.x);
+      o[ib] = from_f<T>(zb * p.v.y);
+      return za * za + zb * zb;
+    }
+    if (a.kind == EPI_QROT) {
+      va *= rs;
+      vb *= rs;
+      if (a.rope) rot(p.u, va, vb);
+      a.out_f[(int64_t)m * a.d + ca] = va;
+      a.out_f[(int64_t)m * a.d + cb] = vb;
+      return 0.f;
+    }
+    if (a.kind == EPI_QKV) {
+      va *= rs;
+      vb *= rs;
+      const int seg = ca / a.d;
+      const int xa = ca - seg * a.d, xb = cb - seg * a.d;
+      if (seg < 2 && a.rope) rot(p.u, va, vb);
+      const int64_t o = (int64_t)m * a.d;
+      if (seg == 0) {
+        a.out_f[o + xa] = va;
+        a.out_f[o + xb] = vb;
+      } else {
+        T* dst = (T*)(seg == 1 ? a.out_k : a.out_v);
+        dst[o + xa] = from_f<T>(va);
+        dst[o + xb] = from_f<T>(vb);
+      }
+      return 0.f;
+    }
+    return (*this)(m, ca, va, cb, vb, rs);
   }
 
   // next RMSNorm's input: zb = z * gain (the rstd is applied by the consumer)

@@ -220,8 +220,11 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_tile(GemmArgs g, Epi<uint16_t
 // other tiles). Tile order: workgroup b runs on XCD b % 8 and takes column
 // tile 8 (q / mtiles) + b % 8 and row tile q % mtiles (q = b / 8), so the row
 // tiles of one column tile share its weights in one L2.
+// PRE: the epilogue reads memory (residual, gains, rotary table) and loads it
+// before the K loop (registers that would otherwise halve the occupancy of
+// the larger tiles).
 // grid: 8 * mtiles * ceil(ntiles / 8); block 256.
-template <int RB, int CB>
+template <int RB, int CB, bool PRE>
 __global__ __launch_bounds__(256) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16_t> epi) {
   constexpr int R = 32 * RB, PF = 2;
   constexpr int TILE = RB * CB * 16 * 64;  // floats of one wave's partial tile
@@ -243,6 +246,19 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16_t> 
   for (int c = 0; c < CB; ++c) wp[c] = (const uint16_t*)g.Wp + ((int64_t)(nt * CB + c) * nchunk * 256 + lane) * 8;
   const bool norm_here = g.ssq_in != nullptr;
   RowRstd<R> rr(g, norm_here ? m0 : 0);
+  // this thread's epilogue items (16 consecutive threads per row and pair)
+  // and the values their epilogue reads, loaded now, in flight with the K loop
+  constexpr int NI = R * CB / 16;
+  const int c16 = tid & 15;
+  typename Epi<uint16_t>::Pre pre[PRE ? NI : 1];
+#pragma unroll
+  for (int j = 0; j < (PRE ? NI : 0); ++j) {
+    const int it = (tid >> 4) + 16 * j;
+    const int row = it / CB, pc = it - row * CB;
+    int ba, bb;
+    pair_blocks(g, nt * CB + pc, ba, bb);
+    pre[j] = m0 + row < g.M ? epi.pre(m0 + row, ba * 16 + c16, bb * 16 + c16) : typename Epi<uint16_t>::Pre{};
+  }
   const int n = (nchunk - wave + 3) >> 2;  // chunks of this wave
   bf16x8_t ra[PF][RB][4], rw[PF][CB][4];
   f32x16_t acc[RB][CB];
@@ -299,8 +315,11 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16_t> 
       for (int e = 0; e < 16; ++e) red[wave * TILE + ((r * CB + c) * 16 + e) * 64 + lane] = acc[r][c][e];
   if (norm_here) rr.finish(g, m0, s_part, s_rstd);  // uniform branch: contains a barrier
   __syncthreads();
-  const int c16 = tid & 15;
-  for (int it = tid >> 4; it < R * CB; it += 16) {  // same trip count on every thread
+  // same trip count on every thread; unrolled only where the prefetched
+  // values need static indices (the unrolled Q/K/V epilogue measured slower)
+#pragma unroll(PRE ? NI : 1)
+  for (int j = 0; j < NI; ++j) {
+    const int it = (tid >> 4) + 16 * j;
     const int row = it / CB, pc = it - row * CB;
     const int m = m0 + row, pair = nt * CB + pc;
     const int r32 = row & 31;
@@ -311,12 +330,31 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16_t> 
     int ba, bb;
     pair_blocks(g, pair, ba, bb);
     float sq = 0.f;
-    if (m < g.M) sq = epi(m, ba * 16 + c16, va, bb * 16 + c16, vb, norm_here ? s_rstd[row] : 1.f);
+    if (m < g.M) {
+      const float rs = norm_here ? s_rstd[row] : 1.f;
+      sq = PRE ? epi.apply(m, ba * 16 + c16, va, bb * 16 + c16, vb, rs, pre[PRE ? j : 0])
+               : epi(m, ba * 16 + c16, va, bb * 16 + c16, vb, rs);
+    }
     if (g.ssq_out) {
       sq = sum16(sq);
       if (c16 == 0 && m < g.M) g.ssq_out[(int64_t)pair * g.M_pad + m] = sq;
     }
   }
+}
+
+// rotary table: one thread per (t, i)
+__global__ __launch_bounds__(256) void k_rope_table(const double* inv_freq, int half, int tmax, float2* tab) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)(tmax + 1) * half) return;
+  const int t = (int)(i / half), f = (int)(i % half);
+  double sn, cs;
+  sincos((double)t * inv_freq[f], &sn, &cs);
+  tab[i] = make_float2((float)cs, (float)sn);
+}
+
+void launch_rope_table(const double* inv_freq, int dh, int tmax, float2* tab, hipStream_t s) {
+  const int64_t n = (int64_t)(tmax + 1) * (dh / 2);
+  hipLaunchKernelGGL(k_rope_table, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, inv_freq, dh / 2, tmax, tab);
 }
 
 // Weights in fragment order: one thread per 16-byte fragment (pair p = block
@@ -403,12 +441,18 @@ void launch_gemm(int dtype, const GemmArgs& g0, const EpiArgs& e, hipStream_t s)
     Epi<uint16_t> epi{e};
     const int mtiles = (g.M + 32 * g.rb - 1) / (32 * g.rb), ntiles = g.npairs / g.cb;
     dim3 grid(8 * mtiles * ((ntiles + 7) / 8));
-    if (g.rb == 2 && g.cb == 2)
-      hipLaunchKernelGGL((k_gemm_bf16_pk<2, 2>), grid, dim3(256), 0, s, g, epi);
-    else if (g.rb == 2)
-      hipLaunchKernelGGL((k_gemm_bf16_pk<2, 1>), grid, dim3(256), 0, s, g, epi);
-    else
-      hipLaunchKernelGGL((k_gemm_bf16_pk<1, 1>), grid, dim3(256), 0, s, g, epi);
+    // (the Q/K/V product's 64 x 2 tile measured slower with it, 26.4 vs 19.9
+    // us at 128 rows, and slower again with table lookups in its epilogue)
+    const bool pre = e.kind == EPI_RESID || e.kind == EPI_QROT;
+#define RLT_PK(RB_, CB_)                                                                        \
+  do {                                                                                          \
+    if (pre) hipLaunchKernelGGL((k_gemm_bf16_pk<RB_, CB_, true>), grid, dim3(256), 0, s, g, epi);  \
+    else hipLaunchKernelGGL((k_gemm_bf16_pk<RB_, CB_, false>), grid, dim3(256), 0, s, g, epi);     \
+  } while (0)
+    if (g.rb == 2 && g.cb == 2) RLT_PK(2, 2);
+    else if (g.rb == 2) RLT_PK(2, 1);
+    else RLT_PK(1, 1);
+#undef RLT_PK
     return;
   }
   const int MB = g.mb;

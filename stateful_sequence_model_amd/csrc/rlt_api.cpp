@@ -112,6 +112,8 @@ struct rlt_ctx {
   // shared device buffers
   int *t_row, *ident, *ones, *rows_buf, *src_buf, *split_buf, *last_buf;
   double* inv_freq;
+  float2* rope_tab;  // [rope_tmax + 1][d_head / 2] rotary (cos, sin)
+  int rope_tmax;
   Workspace ws[2];
   hipStream_t aux;
   hipEvent_t ev_fork, ev_join;
@@ -253,7 +255,7 @@ extern "C" int rlt_state_layout(const rlt_config* cfg, int32_t B_cap, size_t byt
 extern "C" void rlt_destroy(rlt_ctx* c) {
   if (!c) return;
   std::vector<void*> ptrs = {c->t_row, c->ident, c->ones, c->rows_buf, c->src_buf, c->split_buf, c->last_buf,
-                             c->inv_freq};
+                             c->inv_freq, c->rope_tab};
   for (Workspace& w : c->ws) {
     void* p[] = {w.X, w.kc, w.vc, w.o, w.h, w.act, w.gbuf, w.z, w.q, w.qm, w.part, w.partial, w.logits, w.ssq};
     ptrs.insert(ptrs.end(), std::begin(p), std::end(p));
@@ -437,6 +439,8 @@ extern "C" int rlt_create(const rlt_config* cfg, const rlt_weights* w, int32_t m
   ALLOC(c->split_buf, M * 4);
   ALLOC(c->last_buf, M * 4);
   ALLOC(c->inv_freq, (size_t)(dh / 2) * sizeof(double));
+  c->rope_tmax = std::min(max_ctx, 65536);  // positions past it compute their angles
+  ALLOC(c->rope_tab, (size_t)(c->rope_tmax + 1) * (dh / 2) * sizeof(float2));
 #undef ALLOC
   for (int i = 0; i < 2; ++i) {
     if (i == 1 && c->split_min_rows <= 0) break;
@@ -454,6 +458,11 @@ extern "C" int rlt_create(const rlt_config* cfg, const rlt_weights* w, int32_t m
       hipMemcpy(c->inv_freq, fr.data(), fr.size() * sizeof(double), hipMemcpyHostToDevice) != hipSuccess) {
     rlt_destroy(c);
     return fail(RLT_EHIP, "workspace initialisation failed");
+  }
+  launch_rope_table(c->inv_freq, dh, c->rope_tmax, c->rope_tab, nullptr);
+  if (hipGetLastError() != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    rlt_destroy(c);
+    return fail(RLT_EHIP, "rotary table initialisation failed");
   }
   if (c->split_min_rows > 0 &&
       (hipStreamCreateWithFlags(&c->aux, hipStreamNonBlocking) != hipSuccess ||
@@ -652,6 +661,8 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
   E0.H = H;
   E0.rope = cf.pos_kind == RLT_POS_ROPE;
   E0.inv_freq = c->inv_freq;
+  E0.rope_tab = c->rope_tab;
+  E0.rope_tmax = c->rope_tmax;
   E0.alpha = cf.alpha;
   E0.e = P.e;
   E0.s_state = P.st->s;
@@ -1398,6 +1409,8 @@ void enqueue_mem_entries(rlt_ctx* c, const rlt_memory_weights* mw, const rlt_mem
     ep.H = cf.n_heads;
     ep.rope = cf.pos_kind == RLT_POS_ROPE;
     ep.inv_freq = c->inv_freq;
+    ep.rope_tab = c->rope_tab;
+    ep.rope_tmax = c->rope_tmax;
     ep.mk = (char*)mem->k + (size_t)g * mem->stride_g * c->es;
     ep.mv = (char*)mem->v + (size_t)g * mem->stride_g * c->es;
     ep.msb = mem->stride_b;

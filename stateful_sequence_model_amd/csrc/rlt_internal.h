@@ -208,6 +208,8 @@ struct EpiArgs {
   int d, dh, H;
   int rope;                 // apply rotary transform
   const double* inv_freq;   // [dh/2] theta^(-2i/dh)
+  const float2* rope_tab;   // [rope_tmax + 1][dh/2] (cos, sin) of t * inv_freq[i], or null
+  int rope_tmax;
   float* out_f;             // f32 output (q, logits, z, g)
   int64_t ldo;
   void* out_k;              // T outputs (k, act)
@@ -257,6 +259,9 @@ struct AttnArgs {
 };
 
 void launch_gemm(int dtype, const GemmArgs& g, const EpiArgs& e, hipStream_t s);
+// tab[t][i] = (cos, sin)(t * inv_freq[i]) for t <= tmax, i < dh/2: the values
+// the epilogues' rotary transform computes (double precision, rounded)
+void launch_rope_table(const double* inv_freq, int dh, int tmax, float2* tab, hipStream_t s);
 // Wp <- g's weights (bf16) in fragment order (K % 64 == 0, Nv % 32 == 0)
 void launch_pack_weights(const GemmArgs& g, void* Wp, hipStream_t s);
 void launch_swa(int dtype, const AttnArgs& a, hipStream_t s);
