@@ -39,11 +39,13 @@ __global__ __launch_bounds__(256) void k_swa(AttnArgs a) {
   swa_body<T, DH>(a, blockIdx.x, blockIdx.y, lds);
 }
 
-// grid: x = head group, y = chunk, z = slot; block 256
+// grid: x = head group, y = slot, z = chunk (chunk outermost: with rows at
+// similar positions the workgroups of chunks past t, which exit at once, come
+// last instead of interleaved with the active ones); block 256
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void k_xattn(AttnArgs a) {
   __shared__ float lds[attn_lds_floats<T>()];
-  xattn_body<T, DH>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds);
+  xattn_body<T, DH>(a, blockIdx.x, blockIdx.z, blockIdx.y, lds);
 }
 
 // grid: x = head, y = slot; block 64
@@ -59,7 +61,7 @@ static void swa_t(const AttnArgs& a, hipStream_t s) {
 }
 template <typename T, int DH>
 static void xattn_t(const AttnArgs& a, hipStream_t s) {
-  dim3 grid(a.H / a.hpw, a.nch, a.rows.n);
+  dim3 grid(a.H / a.hpw, a.rows.n, a.nch);
   hipLaunchKernelGGL((k_xattn<T, DH>), grid, dim3(256), 0, s, a);
 }
 template <typename T, int DH>
@@ -94,8 +96,8 @@ void launch_xattn(int dtype, const AttnArgs& a, hipStream_t s) {
     Phase p{};
     p.kind = PH_XATTN;
     p.gx = a.H / a.hpw;
-    p.gy = a.nch;
-    p.gz = a.rows.n;
+    p.gy = a.rows.n;
+    p.gz = a.nch;
     p.u.at = a;
     if (record_phase(p)) return;
   }

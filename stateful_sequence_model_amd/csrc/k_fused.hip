@@ -69,7 +69,7 @@ __device__ __forceinline__ void attn_phase(int kind, const AttnArgs& a, int bx, 
   if (kind == PH_SWA)
     swa_body<uint16_t, DH>(a, bx, by, lds);
   else if (kind == PH_XATTN)
-    xattn_body<uint16_t, DH>(a, bx, by, bz, lds);
+    xattn_body<uint16_t, DH>(a, bx, bz, by, lds);  // (head group, slot, chunk) grid
   else
     xcombine_body<uint16_t, DH>(a, bx, by, threadIdx.x, 256);
 }
