@@ -145,10 +145,16 @@ struct Acc {
 
 // Walk keys r = r0, r0 + step, ... < r1 (addressed by kv(r) -> (k, v)
 // pointers), U at a time.
+// qp: this lane's query elements (pieces at qp and qp + DH/2), unscaled;
+// scores are scaled by qscale. The query is loaded after the first batch of
+// keys is issued, so no workgroup waits for it before its key loads start.
 template <typename T, int LPK, int U, class KV>
-__device__ __forceinline__ void walk(Acc<T>& acc, const float* q, int r0, int r1, int step, const KV& kv) {
+__device__ __forceinline__ void walk(Acc<T>& acc, const float* qp, float qscale, int r0, int r1, int step,
+                                     const KV& kv) {
   constexpr int h = LPK * LaneVec<T>::PE;  // DH / 2
+  constexpr int E = LaneVec<T>::E, PE = LaneVec<T>::PE;
   using LV = LaneVec<T>;
+  float q[E];
   // full batches: r0 + i·U·step for i < nb, each with its last key below r1
   const int span = U * step;
   const int last = r1 - 1 - (U - 1) * step;
@@ -165,13 +171,18 @@ __device__ __forceinline__ void walk(Acc<T>& acc, const float* q, int r0, int r1
   auto consume = [&](const Raw* kr, const Raw* vr) {
     float s[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) s[u] = group_sum<LPK>(LV::dot(q, kr[u]));
+    for (int u = 0; u < U; ++u) s[u] = group_sum<LPK>(LV::dot(q, kr[u])) * qscale;
     acc.template fold<U>(s, vr);
   };
   // two register sets: the next batch's loads are in flight while the
   // current batch is folded (same batches, same fold order as one set)
   Raw ka[U], va[U], kb[U], vb[U];
   if (nb > 0) issue(ka, va, r0);
+#pragma unroll
+  for (int i = 0; i < PE; ++i) {
+    q[i] = qp[i];
+    q[PE + i] = qp[h + i];
+  }
   for (int i = 0; i < nb; i += 2) {
     if (i + 1 < nb) issue(kb, vb, r0 + (i + 1) * span);
     consume(ka, va);
@@ -184,7 +195,7 @@ __device__ __forceinline__ void walk(Acc<T>& acc, const float* q, int r0, int r1
     const T *kp, *vp;
     kv(r, kp, vp);
     Raw kr[1] = {LV::load(kp, h)}, vr[1] = {LV::load(vp, h)};
-    float s[1] = {group_sum<LPK>(LV::dot(q, kr[0]))};
+    float s[1] = {group_sum<LPK>(LV::dot(q, kr[0])) * qscale};
     acc.template fold<1>(s, vr);
   }
 }
@@ -273,16 +284,6 @@ __device__ __forceinline__ void swa_body(const AttnArgs& a, int hg, int slot, fl
   constexpr int PE = LV::PE, h = DH / 2;
   const int col = (hg * a.hpw + hh) * DH + jl * PE;
   const int d = a.d;
-
-  float q[E];
-  {
-    const float* qp = a.q + (int64_t)slot * d + col;
-#pragma unroll
-    for (int i = 0; i < PE; ++i) {
-      q[i] = qp[i] * a.qscale;
-      q[PE + i] = qp[h + i] * a.qscale;
-    }
-  }
   const int W1 = a.W - 1;
   const int nh = min(t - 1, W1);
   RingKV<T> kv;
@@ -297,7 +298,7 @@ __device__ __forceinline__ void swa_body(const AttnArgs& a, int hg, int slot, fl
 
   Acc<T> acc;
   acc.init();
-  walk<T, LPK, UNROLL>(acc, q, kg, nh + 1, KPW, kv);
+  walk<T, LPK, UNROLL>(acc, a.q + (int64_t)slot * d + col, a.qscale, kg, nh + 1, KPW, kv);
   const bool lead = merge_groups<T>(acc, kg, G, KPW, s_o, s_ml);
   if (lead) {
     const float inv = 1.f / acc.l;
@@ -341,20 +342,10 @@ __device__ __forceinline__ void xattn_body(const AttnArgs& a, int hg, int ch, in
   constexpr int PE = LV::PE, h = DH / 2;
   const int col = head * DH + jl * PE;
   const int d = a.d;
-
-  float q[E];
-  {
-    const float* qp = a.q + (int64_t)slot * d + col;
-#pragma unroll
-    for (int i = 0; i < PE; ++i) {
-      q[i] = qp[i] * a.qscale;
-      q[PE + i] = qp[h + i] * a.qscale;
-    }
-  }
   MemKV<T> kv{(const T*)a.mk + (int64_t)row * a.sb + col, (const T*)a.mv + (int64_t)row * a.sb + col, a.st};
   Acc<T> acc;
   acc.init();
-  walk<T, LPK, UNROLL>(acc, q, j0 + kg, j1, KPW, kv);
+  walk<T, LPK, UNROLL>(acc, a.q + (int64_t)slot * d + col, a.qscale, j0 + kg, j1, KPW, kv);
   const bool lead = merge_groups<T>(acc, kg, G, KPW, s_o, s_ml);
   if (lead) {
     float* P = a.part + (((int64_t)slot * a.nch + ch) * a.H + head) * (DH + 2);
