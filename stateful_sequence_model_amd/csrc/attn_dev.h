@@ -200,36 +200,34 @@ __device__ __forceinline__ void walk(Acc<T>& acc, const float* qp, float qscale,
   }
 }
 
-// Merge the key groups' partials of the workgroup (fixed group order).
-// Returns true on the lanes of key group 0, which then hold the merged
-// (m, l, o) of their (head, element range).
-template <typename T>
-__device__ __forceinline__ bool merge_groups(Acc<T>& acc, int kg, int G, int KPW, float* s_o, float* s_ml) {
+// Merge the key groups' partials of the workgroup (fixed group order), all
+// 256 threads at once: thread idx takes (lane li of a key group, element e)
+// for idx = threadIdx.x, + 256, ... < G * E, sums that element over the
+// groups in group order (the same operations, in the same order, as one
+// lane per element would do) and hands emit(li, e, o, M, L) the merged
+// unnormalised output element, running max and sum. Contains one barrier.
+template <typename T, class Emit>
+__device__ __forceinline__ void merge_groups(const Acc<T>& acc, int G, int KPW, float* s_o, float* s_ml,
+                                             const Emit& emit) {
   constexpr int E = Acc<T>::E;
-  const int li = threadIdx.x - kg * G;  // lane index within the key group
 #pragma unroll
   for (int i = 0; i < E; ++i) s_o[threadIdx.x * E + i] = acc.o[i];
   s_ml[2 * threadIdx.x] = acc.m;
   s_ml[2 * threadIdx.x + 1] = acc.l;
   __syncthreads();
-  if (kg != 0) return false;
-  float M = -INFINITY;
-  for (int g = 0; g < KPW; ++g) M = fmaxf(M, s_ml[2 * (g * G + li)]);
-  float L = 0.f, o[E];
-#pragma unroll
-  for (int i = 0; i < E; ++i) o[i] = 0.f;
-  for (int g = 0; g < KPW; ++g) {
-    const int th = g * G + li;
-    const float w = exp2f(s_ml[2 * th] - M);
-    L += s_ml[2 * th + 1] * w;
-#pragma unroll
-    for (int i = 0; i < E; ++i) o[i] = fmaf(s_o[th * E + i], w, o[i]);
+  for (int idx = threadIdx.x; idx < G * E; idx += 256) {
+    const int li = idx / E, e = idx - li * E;
+    float M = -INFINITY;
+    for (int g = 0; g < KPW; ++g) M = fmaxf(M, s_ml[2 * (g * G + li)]);
+    float L = 0.f, o = 0.f;
+    for (int g = 0; g < KPW; ++g) {
+      const int th = g * G + li;
+      const float w = exp2f(s_ml[2 * th] - M);
+      L += s_ml[2 * th + 1] * w;
+      o = fmaf(s_o[th * E + e], w, o);
+    }
+    emit(li, e, o, M, L);
   }
-  acc.m = M;
-  acc.l = L;
-#pragma unroll
-  for (int i = 0; i < E; ++i) acc.o[i] = o[i];
-  return true;
 }
 
 template <typename T>
@@ -299,18 +297,13 @@ __device__ __forceinline__ void swa_body(const AttnArgs& a, int hg, int slot, fl
   Acc<T> acc;
   acc.init();
   walk<T, LPK, UNROLL>(acc, a.q + (int64_t)slot * d + col, a.qscale, kg, nh + 1, KPW, kv);
-  const bool lead = merge_groups<T>(acc, kg, G, KPW, s_o, s_ml);
-  if (lead) {
-    const float inv = 1.f / acc.l;
-    float o[E];
-#pragma unroll
-    for (int i = 0; i < E; ++i) o[i] = acc.o[i] * inv;
-    T* out = (T*)a.out;
-    if (a.out_pk)  // the 8-element pieces are 8-aligned: contiguous in fragment order
-      LV::store(out + pk_off(slot, col, d >> 6), out + pk_off(slot, col + h, d >> 6), o);
-    else
-      LV::store(out + (int64_t)slot * d + col, out + (int64_t)slot * d + col + h, o);
-  }
+  T* out = (T*)a.out;
+  const int c0 = hg * a.hpw * DH;
+  merge_groups<T>(acc, G, KPW, s_o, s_ml, [&](int li, int e, float o, float, float L) {
+    // element e of lane li: piece e / PE of that lane's two
+    const int c = c0 + (li / LPK) * DH + (li % LPK) * PE + (e < PE ? e : h + e - PE);
+    out[a.out_pk ? pk_off(slot, c, d >> 6) : (int64_t)slot * d + c] = from_f<T>(o * (1.f / L));
+  });
   // cache insert after every read of this workgroup
   __syncthreads();
   if (W1 > 0 && kg == 0) {
@@ -346,19 +339,15 @@ __device__ __forceinline__ void xattn_body(const AttnArgs& a, int hg, int ch, in
   Acc<T> acc;
   acc.init();
   walk<T, LPK, UNROLL>(acc, a.q + (int64_t)slot * d + col, a.qscale, j0 + kg, j1, KPW, kv);
-  const bool lead = merge_groups<T>(acc, kg, G, KPW, s_o, s_ml);
-  if (lead) {
-    float* P = a.part + (((int64_t)slot * a.nch + ch) * a.H + head) * (DH + 2);
-#pragma unroll
-    for (int i = 0; i < PE; ++i) {
-      P[jl * PE + i] = acc.o[i];
-      P[h + jl * PE + i] = acc.o[PE + i];
+  merge_groups<T>(acc, G, KPW, s_o, s_ml, [&](int li, int e, float o, float M, float L) {
+    const int ljl = li % LPK;
+    float* P = a.part + (((int64_t)slot * a.nch + ch) * a.H + hg * a.hpw + li / LPK) * (DH + 2);
+    P[ljl * PE + (e < PE ? e : h + e - PE)] = o;
+    if (ljl == 0 && e == 0) {
+      P[DH] = M;
+      P[DH + 1] = L;
     }
-    if (jl == 0) {
-      P[DH] = acc.m;
-      P[DH + 1] = acc.l;
-    }
-  }
+  });
 }
 
 // chunk combine of (head, slot) by `nt` threads with index `tid`
