@@ -231,15 +231,20 @@ __device__ __forceinline__ void merge_groups(const Acc<T>& acc, int G, int KPW, 
 }
 
 template <typename T>
+// Keys r < nh are ring slots in memory order: position j sits at slot
+// (j - 1) mod (W - 1), so the nh retained positions t - nh .. t - 1 occupy
+// exactly slots 0 .. nh - 1, before the ring wraps (nh = t - 1 < W - 1) and
+// after (nh = W - 1: every slot). Visiting slots in order (not positions)
+// reads the window front to back with no modulo; the softmax is
+// order-free up to rounding. Key nh is the current (k, v).
 struct RingKV {
   const T *rk, *rv, *ck, *cv;
-  int t, nh, W1;
+  int nh;
   int64_t d;
   __device__ __forceinline__ void operator()(int r, const T*& kp, const T*& vp) const {
     if (r < nh) {
-      const int sl = (t - nh + r - 1) % W1;  // slot of absolute position t - nh + r
-      kp = rk + sl * d;
-      vp = rv + sl * d;
+      kp = rk + r * d;
+      vp = rv + r * d;
     } else {
       kp = ck;
       vp = cv;
@@ -289,9 +294,7 @@ __device__ __forceinline__ void swa_body(const AttnArgs& a, int hg, int slot, fl
   kv.rv = (const T*)a.ring_v + (int64_t)row * W1 * d + col;
   kv.ck = (const T*)a.kc + (int64_t)slot * d + col;
   kv.cv = (const T*)a.vc + (int64_t)slot * d + col;
-  kv.t = t;
   kv.nh = nh;
-  kv.W1 = W1;
   kv.d = d;
 
   Acc<T> acc;
