@@ -41,6 +41,19 @@ struct Epi {
     rot(rope_cs(a.rows.t_row[m], c_in_head), x, y);
   }
 
+  // EPI_MEMKV for a row whose position t (> 0) and destination offset
+  // (row * msb + (t - 1) * mst elements) the tile loaded ahead
+  __device__ __forceinline__ void memkv_at(int t, int64_t off, int ca, float va, int cb, float vb, float rs) const {
+    va *= rs;
+    vb *= rs;
+    const int seg = ca / a.d;
+    const int xa = ca - seg * a.d, xb = cb - seg * a.d;
+    if (seg == 0 && a.rope) rot(rope_cs(t, xa % a.dh, true), va, vb);
+    T* dst = (T*)(seg == 0 ? a.mk : a.mv) + off;
+    dst[xa] = from_f<T>(va);
+    dst[xb] = from_f<T>(vb);
+  }
+
   // Values an epilogue reads from memory for (row m, columns ca, cb), loaded
   // ahead of the product by tiles that know their outputs in advance: the
   // residual and the next norm's gains (EPI_RESID), the rotary (cos, sin)
@@ -198,7 +211,9 @@ struct Epi {
         vb *= rs;
         const int seg = ca / a.d;
         const int xa = ca - seg * a.d, xb = cb - seg * a.d;
-        if (seg == 0 && a.rope) rotate(m, xa % a.dh, va, vb);
+        // (cos, sin) from the table: the token-parallel prefill rotates
+        // millions of keys per call, where the angles dominated the epilogue
+        if (seg == 0 && a.rope) rot(rope_cs(t, xa % a.dh, true), va, vb);
         T* dst = (T*)(seg == 0 ? a.mk : a.mv) + (int64_t)a.rows.rows[m] * a.msb + (int64_t)(t - 1) * a.mst;
         dst[xa] = from_f<T>(va);
         dst[xb] = from_f<T>(vb);

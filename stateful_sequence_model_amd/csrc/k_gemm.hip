@@ -89,6 +89,17 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_tile(GemmArgs g, Epi<uint16_t
   }
   const bool norm_here = g.S == 1 && g.ssq_in != nullptr;
   RowRstd<BM> rr(g, norm_here ? m0 : 0);
+  // memory entries (the token-parallel prefill): each row's position and
+  // destination, loaded now and staged for the epilogue (no dependent loads
+  // inside it)
+  const bool memkv = g.S == 1 && epi.a.kind == EPI_MEMKV;
+  __shared__ int s_t[BM];
+  __shared__ int64_t s_off[BM];
+  int my_t = 0, my_row = 0;
+  if (memkv && tid < BM && m0 + tid < g.M) {
+    my_t = epi.a.rows.t_row[m0 + tid];
+    my_row = epi.a.rows.rows[m0 + tid];
+  }
   bf16x8_t ra[PF][LA], rw[PF][LW];
   auto gload = [&](int p, int st) {
 #pragma unroll
@@ -186,6 +197,10 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_tile(GemmArgs g, Epi<uint16_t
     // measured several times slower)
     return;
   }
+  if (memkv && tid < BM) {
+    s_t[tid] = my_t;
+    s_off[tid] = (int64_t)my_row * epi.a.msb + (int64_t)(my_t - 1) * epi.a.mst;
+  }
   if (norm_here) rr.finish(g, m0, s_part, s_rstd);  // uniform branch: contains a barrier
   __syncthreads();
   // 16 consecutive threads take the 16 column positions of one (row, pair):
@@ -199,7 +214,12 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_tile(GemmArgs g, Epi<uint16_t
     pair_blocks(g, pair, ba, bb);
     const float va = Cs[row * LDC + pl * 32 + c16], vb = Cs[row * LDC + pl * 32 + 16 + c16];
     float sq = 0.f;
-    if (m < g.M) sq = epi(m, ba * 16 + c16, va, bb * 16 + c16, vb, norm_here ? s_rstd[row] : 1.f);
+    if (memkv) {
+      if (m < g.M && s_t[row] > 0)
+        epi.memkv_at(s_t[row], s_off[row], ba * 16 + c16, va, bb * 16 + c16, vb, norm_here ? s_rstd[row] : 1.f);
+    } else if (m < g.M) {
+      sq = epi(m, ba * 16 + c16, va, bb * 16 + c16, vb, norm_here ? s_rstd[row] : 1.f);
+    }
     if (g.ssq_out) {
       sq = sum16(sq);
       if (c16 == 0 && m < g.M) g.ssq_out[(int64_t)pair * g.M_pad + m] = sq;

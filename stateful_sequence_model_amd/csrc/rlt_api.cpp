@@ -1429,6 +1429,7 @@ void enqueue_mem_entries(rlt_ctx* c, const rlt_memory_weights* mw, const rlt_mem
     ep.mv = (char*)mem->v + (size_t)g * mem->stride_g * c->es;
     ep.msb = mem->stride_b;
     ep.mst = mem->stride_t;
+
     Gemm gm{c, &c->ws[0], s};
     gm.m_pad = c->mem_rows;
     gm.ssq_units = 1;
