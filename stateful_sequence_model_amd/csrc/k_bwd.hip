@@ -49,7 +49,8 @@ __device__ __forceinline__ float block_max(float v, float* red) {
 __device__ __forceinline__ float sigm(float x) { return 1.0f / (1.0f + expf(-x)); }
 
 // 16x16 output tile per 256-thread block; the unit-stride dimension of each
-// operand runs along threadIdx.x when its tile is loaded
+// operand runs along threadIdx.x when its tile is loaded; the next K step's
+// elements are loaded into registers while the current step is multiplied
 template <typename TB>
 __global__ __launch_bounds__(256) void k_mm(int M, int N, int K, const float* a, int64_t a_si, int64_t a_sk,
                                            const TB* b, int64_t b_sk, int64_t b_sj, float* c, int64_t c_si,
@@ -58,19 +59,26 @@ __global__ __launch_bounds__(256) void k_mm(int M, int N, int K, const float* a,
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   const int i0 = blockIdx.y * 16, j0 = blockIdx.x * 16;
   const bool a_k_fast = a_sk == 1, b_j_fast = b_sj == 1;
+  const int aii = a_k_fast ? ty : tx, akk = a_k_fast ? tx : ty;
+  const int bkk = b_j_fast ? ty : tx, bjj = b_j_fast ? tx : ty;
+  auto lda = [&](int k0) {
+    const int i = i0 + aii, k = k0 + akk;
+    return (i < M && k < K) ? a[(int64_t)i * a_si + (int64_t)k * a_sk] : 0.f;
+  };
+  auto ldb = [&](int k0) {
+    const int k = k0 + bkk, j = j0 + bjj;
+    return (k < K && j < N) ? to_f<TB>(b[(int64_t)k * b_sk + (int64_t)j * b_sj]) : 0.f;
+  };
   float acc = 0.f;
+  float an = lda(0), bn = ldb(0);
   for (int k0 = 0; k0 < K; k0 += 16) {
-    {
-      const int ii = a_k_fast ? ty : tx, kk = a_k_fast ? tx : ty;
-      const int i = i0 + ii, k = k0 + kk;
-      As[ii][kk] = (i < M && k < K) ? a[(int64_t)i * a_si + (int64_t)k * a_sk] : 0.f;
-    }
-    {
-      const int kk = b_j_fast ? ty : tx, jj = b_j_fast ? tx : ty;
-      const int k = k0 + kk, j = j0 + jj;
-      Bs[kk][jj] = (k < K && j < N) ? to_f<TB>(b[(int64_t)k * b_sk + (int64_t)j * b_sj]) : 0.f;
-    }
+    As[aii][akk] = an;
+    Bs[bkk][bjj] = bn;
     __syncthreads();
+    if (k0 + 16 < K) {
+      an = lda(k0 + 16);
+      bn = ldb(k0 + 16);
+    }
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) acc = fmaf(As[ty][kk], Bs[kk][tx], acc);
     __syncthreads();
