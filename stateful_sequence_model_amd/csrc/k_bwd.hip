@@ -48,15 +48,21 @@ __device__ __forceinline__ float block_max(float v, float* red) {
 
 __device__ __forceinline__ float sigm(float x) { return 1.0f / (1.0f + expf(-x)); }
 
-// 16x16 output tile per 256-thread block; the unit-stride dimension of each
-// operand runs along threadIdx.x when its tile is loaded; the next K step's
-// elements are loaded into registers while the current step is multiplied
+// 16x16 output tile per 1024-thread block: 4 groups of 256 threads take the
+// 16-wide K steps round-robin (group q: steps q, q + 4, ...), each summing
+// its steps in k order; the 4 partial sums are then added in group order.
+// The unit-stride dimension of each operand runs along threadIdx.x when its
+// tile is loaded; the next step's elements are loaded into registers while
+// the current step is multiplied.
 template <typename TB>
-__global__ __launch_bounds__(256) void k_mm(int M, int N, int K, const float* a, int64_t a_si, int64_t a_sk,
-                                           const TB* b, int64_t b_sk, int64_t b_sj, float* c, int64_t c_si,
-                                           int accumulate) {
-  __shared__ float As[16][17], Bs[16][17];
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+__global__ __launch_bounds__(1024) void k_mm(int M, int N, int K, const float* a, int64_t a_si, int64_t a_sk,
+                                            const TB* b, int64_t b_sk, int64_t b_sj, float* c, int64_t c_si,
+                                            int accumulate) {
+  constexpr int KG = 4;
+  __shared__ float As[KG][16][17], Bs[KG][16][17];
+  __shared__ float red[KG - 1][256];
+  const int q = threadIdx.x >> 8, t = threadIdx.x & 255;
+  const int tx = t & 15, ty = t >> 4;
   const int i0 = blockIdx.y * 16, j0 = blockIdx.x * 16;
   const bool a_k_fast = a_sk == 1, b_j_fast = b_sj == 1;
   const int aii = a_k_fast ? ty : tx, akk = a_k_fast ? tx : ty;
@@ -69,24 +75,35 @@ __global__ __launch_bounds__(256) void k_mm(int M, int N, int K, const float* a,
     const int k = k0 + bkk, j = j0 + bjj;
     return (k < K && j < N) ? to_f<TB>(b[(int64_t)k * b_sk + (int64_t)j * b_sj]) : 0.f;
   };
+  const int nst = (K + 15) / 16;
+  const int steps = (nst + KG - 1) / KG;  // the same trip count in every group (barriers)
   float acc = 0.f;
-  float an = lda(0), bn = ldb(0);
-  for (int k0 = 0; k0 < K; k0 += 16) {
-    As[aii][akk] = an;
-    Bs[bkk][bjj] = bn;
+  float an = lda(16 * q), bn = ldb(16 * q);
+  for (int s = 0; s < steps; ++s) {
+    const int k0 = 16 * (q + KG * s);
+    As[q][aii][akk] = an;
+    Bs[q][bkk][bjj] = bn;
     __syncthreads();
-    if (k0 + 16 < K) {
-      an = lda(k0 + 16);
-      bn = ldb(k0 + 16);
+    if (s + 1 < steps) {
+      an = lda(k0 + 16 * KG);
+      bn = ldb(k0 + 16 * KG);
     }
+    if (k0 < K) {
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) acc = fmaf(As[ty][kk], Bs[kk][tx], acc);
+      for (int kk = 0; kk < 16; ++kk) acc = fmaf(As[q][ty][kk], Bs[q][kk][tx], acc);
+    }
     __syncthreads();
   }
-  const int i = i0 + ty, j = j0 + tx;
-  if (i < M && j < N) {
-    float* p = c + (int64_t)i * c_si + j;
-    *p = accumulate ? *p + acc : acc;
+  if (q > 0) red[q - 1][t] = acc;
+  __syncthreads();
+  if (q == 0) {
+#pragma unroll
+    for (int g = 0; g < KG - 1; ++g) acc += red[g][t];
+    const int i = i0 + ty, j = j0 + tx;
+    if (i < M && j < N) {
+      float* p = c + (int64_t)i * c_si + j;
+      *p = accumulate ? *p + acc : acc;
+    }
   }
 }
 
@@ -365,10 +382,10 @@ void mm(int M, int N, int K, const float* a, int64_t a_si, int64_t a_sk, const v
   if (M <= 0 || N <= 0) return;
   dim3 grid((N + 15) / 16, (M + 15) / 16);
   if (bdt)
-    hipLaunchKernelGGL(k_mm<uint16_t>, grid, dim3(256), 0, s, M, N, K, a, a_si, a_sk, (const uint16_t*)b, b_sk, b_sj, c,
+    hipLaunchKernelGGL(k_mm<uint16_t>, grid, dim3(1024), 0, s, M, N, K, a, a_si, a_sk, (const uint16_t*)b, b_sk, b_sj, c,
                        c_si, (int)accumulate);
   else
-    hipLaunchKernelGGL(k_mm<float>, grid, dim3(256), 0, s, M, N, K, a, a_si, a_sk, (const float*)b, b_sk, b_sj, c,
+    hipLaunchKernelGGL(k_mm<float>, grid, dim3(1024), 0, s, M, N, K, a, a_si, a_sk, (const float*)b, b_sk, b_sj, c,
                        c_si, (int)accumulate);
 }
 
