@@ -48,61 +48,88 @@ __device__ __forceinline__ float block_max(float v, float* red) {
 
 __device__ __forceinline__ float sigm(float x) { return 1.0f / (1.0f + expf(-x)); }
 
-// 16x16 output tile per 1024-thread block: 4 groups of 256 threads take the
-// 16-wide K steps round-robin (group q: steps q, q + 4, ...), each summing
-// its steps in k order; the 4 partial sums are then added in group order.
-// The unit-stride dimension of each operand runs along threadIdx.x when its
-// tile is loaded; the next step's elements are loaded into registers while
-// the current step is multiplied.
+// 16x16 output tile per 1024-thread block: 8 groups of 128 threads take the
+// 16-wide K steps round-robin (group q: steps q, q + 8, ...), each thread
+// summing two outputs over its group's steps in k order; the 8 partial sums
+// are then added in group order. The unit-stride dimension of each operand
+// runs along the fastest thread index when its tile is loaded; the next
+// step's elements are loaded into registers while the current step is
+// multiplied.
 template <typename TB>
 __global__ __launch_bounds__(1024) void k_mm(int M, int N, int K, const float* a, int64_t a_si, int64_t a_sk,
                                             const TB* b, int64_t b_sk, int64_t b_sj, float* c, int64_t c_si,
                                             int accumulate) {
-  constexpr int KG = 4;
+  constexpr int KG = 8;
   __shared__ float As[KG][16][17], Bs[KG][16][17];
   __shared__ float red[KG - 1][256];
-  const int q = threadIdx.x >> 8, t = threadIdx.x & 255;
-  const int tx = t & 15, ty = t >> 4;
+  const int q = threadIdx.x >> 7, t = threadIdx.x & 127;
+  const int tx = t & 7, ty = t >> 3;  // outputs (ty, 2 tx) and (ty, 2 tx + 1)
   const int i0 = blockIdx.y * 16, j0 = blockIdx.x * 16;
   const bool a_k_fast = a_sk == 1, b_j_fast = b_sj == 1;
-  const int aii = a_k_fast ? ty : tx, akk = a_k_fast ? tx : ty;
-  const int bkk = b_j_fast ? ty : tx, bjj = b_j_fast ? tx : ty;
-  auto lda = [&](int k0) {
-    const int i = i0 + aii, k = k0 + akk;
+  // tile loads: element e = t + 128 h (h < 2) of a 16 x 16 tile, fastest index e % 16
+  auto lda = [&](int k0, int h) {
+    const int e = t + 128 * h, f = e & 15, o = e >> 4;
+    const int i = i0 + (a_k_fast ? o : f), k = k0 + (a_k_fast ? f : o);
     return (i < M && k < K) ? a[(int64_t)i * a_si + (int64_t)k * a_sk] : 0.f;
   };
-  auto ldb = [&](int k0) {
-    const int k = k0 + bkk, j = j0 + bjj;
+  auto ldb = [&](int k0, int h) {
+    const int e = t + 128 * h, f = e & 15, o = e >> 4;
+    const int k = k0 + (b_j_fast ? o : f), j = j0 + (b_j_fast ? f : o);
     return (k < K && j < N) ? to_f<TB>(b[(int64_t)k * b_sk + (int64_t)j * b_sj]) : 0.f;
+  };
+  auto sta = [&](int h, float v) {
+    const int e = t + 128 * h, f = e & 15, o = e >> 4;
+    if (a_k_fast) As[q][o][f] = v;
+    else As[q][f][o] = v;
+  };
+  auto stb = [&](int h, float v) {
+    const int e = t + 128 * h, f = e & 15, o = e >> 4;
+    if (b_j_fast) Bs[q][o][f] = v;
+    else Bs[q][f][o] = v;
   };
   const int nst = (K + 15) / 16;
   const int steps = (nst + KG - 1) / KG;  // the same trip count in every group (barriers)
-  float acc = 0.f;
-  float an = lda(16 * q), bn = ldb(16 * q);
+  float acc0 = 0.f, acc1 = 0.f;
+  float an0 = lda(16 * q, 0), an1 = lda(16 * q, 1), bn0 = ldb(16 * q, 0), bn1 = ldb(16 * q, 1);
   for (int s = 0; s < steps; ++s) {
     const int k0 = 16 * (q + KG * s);
-    As[q][aii][akk] = an;
-    Bs[q][bkk][bjj] = bn;
+    sta(0, an0);
+    sta(1, an1);
+    stb(0, bn0);
+    stb(1, bn1);
     __syncthreads();
     if (s + 1 < steps) {
-      an = lda(k0 + 16 * KG);
-      bn = ldb(k0 + 16 * KG);
+      an0 = lda(k0 + 16 * KG, 0);
+      an1 = lda(k0 + 16 * KG, 1);
+      bn0 = ldb(k0 + 16 * KG, 0);
+      bn1 = ldb(k0 + 16 * KG, 1);
     }
     if (k0 < K) {
 #pragma unroll
-      for (int kk = 0; kk < 16; ++kk) acc = fmaf(As[q][ty][kk], Bs[q][kk][tx], acc);
+      for (int kk = 0; kk < 16; ++kk) {
+        const float av = As[q][ty][kk];
+        acc0 = fmaf(av, Bs[q][kk][2 * tx], acc0);
+        acc1 = fmaf(av, Bs[q][kk][2 * tx + 1], acc1);
+      }
     }
     __syncthreads();
   }
-  if (q > 0) red[q - 1][t] = acc;
+  if (q > 0) {
+    red[q - 1][2 * t] = acc0;
+    red[q - 1][2 * t + 1] = acc1;
+  }
   __syncthreads();
   if (q == 0) {
 #pragma unroll
-    for (int g = 0; g < KG - 1; ++g) acc += red[g][t];
-    const int i = i0 + ty, j = j0 + tx;
-    if (i < M && j < N) {
+    for (int g = 0; g < KG - 1; ++g) {
+      acc0 += red[g][2 * t];
+      acc1 += red[g][2 * t + 1];
+    }
+    const int i = i0 + ty, j = j0 + 2 * tx;
+    if (i < M) {
       float* p = c + (int64_t)i * c_si + j;
-      *p = accumulate ? *p + acc : acc;
+      if (j < N) p[0] = accumulate ? p[0] + acc0 : acc0;
+      if (j + 1 < N) p[1] = accumulate ? p[1] + acc1 : acc1;
     }
   }
 }
