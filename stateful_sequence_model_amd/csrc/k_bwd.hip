@@ -200,6 +200,24 @@ __global__ __launch_bounds__(256) void k_rope(float* x, int64_t ld, int n, int d
 }
 
 // block per (row, head); scores of all keys in dynamic LDS
+// sum over keys j < nk of w[j] * x_j[c] for c < dh (dh divides 256), by all
+// 256 threads: 256 / dh groups take keys round-robin, the group partials are
+// then added in group order; the result is returned on threads c < dh.
+// Contains one barrier (part: 256 floats of LDS).
+template <typename TK>
+__device__ __forceinline__ float key_wsum(const float* w, const void* x, int64_t row_off, int lo, int nk, int64_t s_pos,
+                                          int dh, float* part) {
+  const int G = 256 / dh, c = threadIdx.x % dh, g = threadIdx.x / dh;
+  float acc = 0.f;
+  for (int j = g; j < nk; j += G) acc = fmaf(w[j], ld_f<TK>(x, row_off + (int64_t)(lo + j - 1) * s_pos + c), acc);
+  part[threadIdx.x] = acc;
+  __syncthreads();
+  float sum = 0.f;
+  if (threadIdx.x < dh)
+    for (int q = 0; q < G; ++q) sum += part[q * dh + c];
+  return sum;
+}
+
 template <typename TK>
 __global__ __launch_bounds__(256) void k_attn_fwd(const float* q, int64_t ldq, KV kv, int lo, int hi, float* o,
                                                  int64_t ldo, int H, int dh) {
@@ -228,11 +246,9 @@ __global__ __launch_bounds__(256) void k_attn_fwd(const float* q, int64_t ldq, K
   }
   sum = block_sum(sum, red);  // contains barriers: scores are visible below
   const float inv = 1.0f / sum;
-  for (int c = threadIdx.x; c < dh; c += 256) {
-    float acc = 0.f;
-    for (int j = 0; j < nk; ++j) acc = fmaf(sc[j], ld_f<TK>(kv.v, row_off + (int64_t)(lo + j - 1) * kv.s_pos + c), acc);
-    o[(int64_t)r * ldo + h * dh + c] = acc * inv;
-  }
+  __shared__ float part[256];
+  const float acc = key_wsum<TK>(sc, kv.v, row_off, lo, nk, kv.s_pos, dh, part);
+  if (threadIdx.x < dh) o[(int64_t)r * ldo + h * dh + threadIdx.x] = acc * inv;
 }
 
 // p_j = softmax(s)_j; dv_j = p_j do; dp_j = do . v_j; ds_j = p_j (dp_j - sum_i p_i dp_i);
@@ -283,11 +299,9 @@ __global__ __launch_bounds__(256) void k_attn_bwd(const float* q, int64_t ldq, K
   dsum = block_sum(dsum, red);
   for (int j = threadIdx.x; j < nk; j += 256) ds[j] = sc[j] * (ds[j] - dsum);
   __syncthreads();
-  for (int c = threadIdx.x; c < dh; c += 256) {
-    float acc = 0.f;
-    for (int j = 0; j < nk; ++j) acc = fmaf(ds[j], ld_f<TK>(kv.k, row_off + (int64_t)(lo + j - 1) * kv.s_pos + c), acc);
-    dq[(int64_t)r * lddq + h * dh + c] = acc * scale;
-  }
+  __shared__ float part[256];
+  const float acc = key_wsum<TK>(ds, kv.k, row_off, lo, nk, kv.s_pos, dh, part);
+  if (threadIdx.x < dh) dq[(int64_t)r * lddq + h * dh + threadIdx.x] = acc * scale;
   if (!dkv.k) return;
   const int64_t drow = (int64_t)(dkv.map ? dkv.map[r] : r) * dkv.s_row + h * dh;
   for (int64_t idx = threadIdx.x; idx < (int64_t)nk * dh; idx += 256) {
