@@ -358,3 +358,33 @@ def test_snapshot_restore_resumes_bit_exact():
         setattr(h, field, value)
         assert b.dec.restore(b.st, rows, bad) == code, field
     assert np.array_equal(b.dec.snapshot(b.st, rows), before)
+
+
+def test_refresh_weights_after_in_place_update():
+    """bf16 contexts multiply an operand-order copy of the decoder's matrix
+    weights made at creation: weights changed in place are not seen until
+    rlt_refresh_weights, after which the transitions equal those of a
+    context created with the new weights, bit for bit."""
+    require_gpu()
+    wl = SMALL.with_(B=4, T=16)
+    a = GpuRun(wl)
+    a.init()
+    S0, Z0 = a.run(3)
+    # exact bf16 rescalings of matrices that only the operand-order products read
+    a.dec.params["layer.0.wq"].mul_(2)
+    a.dec.params["layer.1.w_down"].mul_(0.5)
+    a.dec.params["out.w"].mul_(2)
+    a.init()
+    S1, Z1 = a.run(3)
+    assert np.array_equal(S1, S0) and np.array_equal(Z1, Z0)  # the copy made at creation
+    assert a.dec.refresh_weights() == 0
+    a.init()
+    S2, Z2 = a.run(3)
+    raw = dict(a.raw)
+    for k in ("layer.0.wq", "layer.1.w_down", "out.w"):
+        raw[k] = a.dec.params[k].clone()
+    b = GpuRun(wl, raw=raw)
+    b.init()
+    S3, Z3 = b.run(3)
+    assert np.array_equal(S2, S3) and np.array_equal(Z2, Z3)
+    assert not np.array_equal(S2, S0)
