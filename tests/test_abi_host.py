@@ -125,6 +125,9 @@ def test_null_arguments_are_rejected():
     assert L.rlt_memory_append(None, None, None, 0, 0, None, 0, None, None) == _abi.RLT_EINVAL
     assert L.rlt_state_snapshot(None, None, None, 0, None, None) == _abi.RLT_EINVAL
     assert L.rlt_state_restore(None, None, None, 0, None, None) == _abi.RLT_EINVAL
+    assert L.rlt_refresh_weights(None, None) == _abi.RLT_EINVAL
+    assert L.rlt_dbg_gemm(None, None, None, 1, 32, 32, None, None) == _abi.RLT_EINVAL
+    assert L.rlt_dbg_gemm_packed(None, None, None, 1, 32, 64, None, None) == _abi.RLT_EINVAL
     assert L.rlt_memory_prefill(None, None, None, 0, 0, None, None, 0, 0, None) == _abi.RLT_EINVAL
     assert L.rlt_replay_backward(None, None, None, None) == _abi.RLT_EINVAL
 
