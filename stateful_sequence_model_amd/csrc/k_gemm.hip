@@ -229,12 +229,12 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_tile(GemmArgs g, Epi<uint16_t
 
 // Product with both operands in fragment order (see pk_off): a workgroup owns
 // 32 RB rows x CB column pairs over the whole K, so
-// there is no K split and no partial traffic; its four waves take the 64-wide
-// K chunks round-robin (wave w: chunks w, w + 4, ...) and load each chunk's
+// there is no K split and no partial traffic; its NW waves take the 64-wide
+// K chunks round-robin (wave w: chunks w, w + NW, ...) and load each chunk's
 // fragments straight into registers, every load instruction reading 1 KB of
 // consecutive bytes, PF chunks ahead. No LDS staging and no barrier inside the
 // K loop. Lanes of rows at or past M load no activations (zeros), so a call
-// of a few rows reads little more than the weights. The four wave partials
+// of a few rows reads little more than the weights. The NW wave partials
 // are summed in LDS in wave order by the
 // epilogue threads (16 consecutive threads per row and column pair, as in the
 // other tiles). Tile order: workgroup b runs on XCD b % 8 and takes column
@@ -243,14 +243,20 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_tile(GemmArgs g, Epi<uint16_t
 // PRE: the epilogue reads memory (residual, gains, rotary table) and loads it
 // before the K loop (registers that would otherwise halve the occupancy of
 // the larger tiles).
-// grid: 8 * mtiles * ceil(ntiles / 8); block 256.
-template <int RB, int CB, bool PRE>
-__global__ __launch_bounds__(256) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16_t> epi) {
-  constexpr int R = 32 * RB, PF = 2;
+// NW = 8 (with 4 chunks in flight per wave) serves the smallest tile when it
+// needs at most one workgroup per compute unit: a compute unit holds only so
+// many loads in flight, and with few column tiles (64 workgroups for a
+// 2048-wide product at one row) the weights stream faster with twice the
+// waves per workgroup.
+// grid: 8 * mtiles * ceil(ntiles / 8); block 64 NW.
+template <int RB, int CB, bool PRE, int NW>
+__global__ __launch_bounds__(64 * NW) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16_t> epi) {
+  constexpr int R = 32 * RB, PF = NW == 8 ? 4 : 2, NT = 64 * NW;
   constexpr int TILE = RB * CB * 16 * 64;  // floats of one wave's partial tile
-  __shared__ float red[4 * TILE];
+  static_assert((R * CB * 16) % NT == 0, "epilogue items per thread");
+  __shared__ float red[NW * TILE];
   __shared__ float s_rstd[R];
-  __shared__ float s_part[256];
+  __shared__ float s_part[NT];  // RowRstd uses the first 256; the rest keeps stray writes in bounds
   const int mtiles = (g.M + R - 1) / R, ntiles = g.npairs / CB;
   const int b = blockIdx.x, q = b >> 3;
   const int mt = q % mtiles, nt = 8 * (q / mtiles) + (b & 7);
@@ -268,18 +274,18 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16_t> 
   RowRstd<R> rr(g, norm_here ? m0 : 0);
   // this thread's epilogue items (16 consecutive threads per row and pair)
   // and the values their epilogue reads, loaded now, in flight with the K loop
-  constexpr int NI = R * CB / 16;
+  constexpr int NI = R * CB * 16 / NT;
   const int c16 = tid & 15;
   typename Epi<uint16_t>::Pre pre[PRE ? NI : 1];
 #pragma unroll
   for (int j = 0; j < (PRE ? NI : 0); ++j) {
-    const int it = (tid >> 4) + 16 * j;
+    const int it = (tid >> 4) + (NT / 16) * j;
     const int row = it / CB, pc = it - row * CB;
     int ba, bb;
     pair_blocks(g, nt * CB + pc, ba, bb);
     pre[j] = m0 + row < g.M ? epi.pre(m0 + row, ba * 16 + c16, bb * 16 + c16) : typename Epi<uint16_t>::Pre{};
   }
-  const int n = (nchunk - wave + 3) >> 2;  // chunks of this wave
+  const int n = (nchunk - wave + NW - 1) / NW;  // chunks of this wave
   bf16x8_t ra[PF][RB][4], rw[PF][CB][4];
   f32x16_t acc[RB][CB];
 #pragma unroll
@@ -292,7 +298,7 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16_t> 
 #pragma unroll
   for (int r = 0; r < RB; ++r) live[r] = m0 + 32 * r + (lane & 31) < g.M;
   auto load = [&](int slot, int i) {
-    const int64_t off = (int64_t)(wave + 4 * i) * 256 * 8;
+    const int64_t off = (int64_t)(wave + NW * i) * 256 * 8;
 #pragma unroll
     for (int r = 0; r < RB; ++r)
 #pragma unroll
@@ -339,14 +345,18 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16_t> 
   // values need static indices (the unrolled Q/K/V epilogue measured slower)
 #pragma unroll(PRE ? NI : 1)
   for (int j = 0; j < NI; ++j) {
-    const int it = (tid >> 4) + 16 * j;
+    const int it = (tid >> 4) + (NT / 16) * j;
     const int row = it / CB, pc = it - row * CB;
     const int m = m0 + row, pair = nt * CB + pc;
     const int r32 = row & 31;
     const int ia = (((row >> 5) * CB + pc) * 16 + 4 * (r32 >> 3) + (r32 & 3)) * 64 + ((r32 >> 2) & 1) * 32 + c16;
     const int ib = ia + 16;
-    const float va = ((red[ia] + red[TILE + ia]) + red[2 * TILE + ia]) + red[3 * TILE + ia];
-    const float vb = ((red[ib] + red[TILE + ib]) + red[2 * TILE + ib]) + red[3 * TILE + ib];
+    float va = red[ia], vb = red[ib];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      va += red[w * TILE + ia];
+      vb += red[w * TILE + ib];
+    }
     int ba, bb;
     pair_blocks(g, pair, ba, bb);
     float sq = 0.f;
@@ -464,14 +474,15 @@ void launch_gemm(int dtype, const GemmArgs& g0, const EpiArgs& e, hipStream_t s)
     // (the Q/K/V product's 64 x 2 tile measured slower with it, 26.4 vs 19.9
     // us at 128 rows, and slower again with table lookups in its epilogue)
     const bool pre = e.kind == EPI_RESID || e.kind == EPI_QROT;
-#define RLT_PK(RB_, CB_)                                                                        \
-  do {                                                                                          \
-    if (pre) hipLaunchKernelGGL((k_gemm_bf16_pk<RB_, CB_, true>), grid, dim3(256), 0, s, g, epi);  \
-    else hipLaunchKernelGGL((k_gemm_bf16_pk<RB_, CB_, false>), grid, dim3(256), 0, s, g, epi);     \
+#define RLT_PK(RB_, CB_, NW_)                                                                          \
+  do {                                                                                                 \
+    if (pre) hipLaunchKernelGGL((k_gemm_bf16_pk<RB_, CB_, true, NW_>), grid, dim3(64 * NW_), 0, s, g, epi); \
+    else hipLaunchKernelGGL((k_gemm_bf16_pk<RB_, CB_, false, NW_>), grid, dim3(64 * NW_), 0, s, g, epi);    \
   } while (0)
-    if (g.rb == 2 && g.cb == 2) RLT_PK(2, 2);
-    else if (g.rb == 2) RLT_PK(2, 1);
-    else RLT_PK(1, 1);
+    if (g.rb == 2 && g.cb == 2) RLT_PK(2, 2, 4);
+    else if (g.rb == 2) RLT_PK(2, 1, 4);
+    else if (grid.x <= 256) RLT_PK(1, 1, 8);  // one workgroup per compute unit at most
+    else RLT_PK(1, 1, 4);                      // (8 waves at 344 workgroups: 15.6 vs 13.3 us)
 #undef RLT_PK
     return;
   }

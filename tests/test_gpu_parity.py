@@ -78,13 +78,18 @@ def test_gemm_operand_order_parity():
     products: the three tile shapes (32 rows x 1 pair: M=70 N=256; 64 x 1:
     M=64 N=6144; 64 x 2: M=200 N=8192), K of 1, 3, 7 and 11 chunks of 64
     (waves with 0-3 chunks, the 2-deep register ring's tail), a ragged last
-    row tile, and calls of 1-32 rows (lanes of absent rows load nothing)."""
+    row tile, and calls of 1-32 rows (lanes of absent rows load nothing):
+    eight waves per workgroup with a 4-deep ring up to 256 workgroups (waves
+    with 0-2 chunks here; full turns of that ring run in the model-level
+    tests, K = 2816 and 5504), four waves beyond (M=3 N=9216: 288
+    workgroups)."""
     require_gpu()
     from stateful_sequence_model_amd import to_device
     wl = synth.SMALL
     run = GpuRun(wl, B=1, T=4, max_rows=200)
     for M, N, K in [(70, 256, 64), (33, 96, 192), (64, 6144, 448), (200, 8192, 704), (128, 512, 704),
-                    (40, 32768, 256), (1, 256, 64), (5, 2048, 704), (16, 96, 192), (32, 4096, 256)]:
+                    (40, 32768, 256), (1, 256, 64), (5, 2048, 704), (16, 96, 192), (32, 4096, 256),
+                    (3, 9216, 448)]:
         Abits = synth.normal(8, "pkA%d" % M, (M, K), dtype="bf16")
         Wbits = synth.normal(8, "pkW%d" % N, (N, K), sigma=0.05, dtype="bf16")
         Ad, Wd = to_device(Abits, "bf16"), to_device(Wbits, "bf16")
