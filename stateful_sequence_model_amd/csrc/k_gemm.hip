@@ -251,7 +251,7 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_tile(GemmArgs g, Epi<uint16_t
 // grid: 8 * mtiles * ceil(ntiles / 8); block 64 NW.
 template <int RB, int CB, bool PRE, int NW>
 __global__ __launch_bounds__(64 * NW) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16_t> epi) {
-  constexpr int R = 32 * RB, PF = NW == 8 ? 4 : 2, NT = 64 * NW;
+  constexpr int R = 32 * RB, PF = NW == 8 && RB * CB == 1 ? 4 : 2, NT = 64 * NW;
   constexpr int TILE = RB * CB * 16 * 64;  // floats of one wave's partial tile
   static_assert((R * CB * 16) % NT == 0, "epilogue items per thread");
   __shared__ float red[NW * TILE];
@@ -479,10 +479,19 @@ void launch_gemm(int dtype, const GemmArgs& g0, const EpiArgs& e, hipStream_t s)
     if (pre) hipLaunchKernelGGL((k_gemm_bf16_pk<RB_, CB_, true, NW_>), grid, dim3(64 * NW_), 0, s, g, epi); \
     else hipLaunchKernelGGL((k_gemm_bf16_pk<RB_, CB_, false, NW_>), grid, dim3(64 * NW_), 0, s, g, epi);    \
   } while (0)
-    if (g.rb == 2 && g.cb == 2) RLT_PK(2, 2, 4);
-    else if (g.rb == 2) RLT_PK(2, 1, 4);
-    else if (grid.x <= 256) RLT_PK(1, 1, 8);  // one workgroup per compute unit at most
-    else RLT_PK(1, 1, 4);                      // (8 waves at 344 workgroups: 15.6 vs 13.3 us)
+    // eight waves where the call needs at most one workgroup per compute
+    // unit (8 waves at 344 workgroups of 32 x 1: 15.6 vs 13.0 us)
+    const bool w8 = grid.x <= 256;
+    if (g.rb == 2 && g.cb == 2) {
+      if (w8 && !pre) RLT_PK(2, 2, 8);  // (with the prefetched epilogue values it would spill)
+      else RLT_PK(2, 2, 4);
+    } else if (g.rb == 2) {
+      if (w8) RLT_PK(2, 1, 8);
+      else RLT_PK(2, 1, 4);
+    } else {
+      if (w8) RLT_PK(1, 1, 8);
+      else RLT_PK(1, 1, 4);
+    }
 #undef RLT_PK
     return;
   }

@@ -82,14 +82,16 @@ def test_gemm_operand_order_parity():
     eight waves per workgroup with a 4-deep ring up to 256 workgroups (waves
     with 0-2 chunks here; full turns of that ring run in the model-level
     tests, K = 2816 and 5504), four waves beyond (M=3 N=9216: 288
-    workgroups)."""
+    workgroups); the 64 x 2 tile with eight waves (M=100 N=6144: 192
+    workgroups, ragged second row tile) and 64 x 1 with four (M=64 N=9600:
+    304)."""
     require_gpu()
     from stateful_sequence_model_amd import to_device
     wl = synth.SMALL
     run = GpuRun(wl, B=1, T=4, max_rows=200)
     for M, N, K in [(70, 256, 64), (33, 96, 192), (64, 6144, 448), (200, 8192, 704), (128, 512, 704),
                     (40, 32768, 256), (1, 256, 64), (5, 2048, 704), (16, 96, 192), (32, 4096, 256),
-                    (3, 9216, 448)]:
+                    (3, 9216, 448), (100, 6144, 448), (64, 9600, 256)]:
         Abits = synth.normal(8, "pkA%d" % M, (M, K), dtype="bf16")
         Wbits = synth.normal(8, "pkW%d" % N, (N, K), sigma=0.05, dtype="bf16")
         Ad, Wd = to_device(Abits, "bf16"), to_device(Wbits, "bf16")
