@@ -68,6 +68,46 @@ def test_mid_from_h0_sampled_rows():
     assert decided >= 0.99
 
 
+@pytest.mark.timeout(900)
+def test_mid_many_rows_tile_shapes():
+    """L_D=12, d=1024 at 320 and 640 rows from H_0 (6 steps), three rows of
+    each checked: the product tiles of large calls, 64 rows x 1 pair with
+    eight waves and prefetched epilogue values (the 1024-wide products at
+    320 rows), 64 x 2 with eight waves (Q/K/V at 320 rows) and 64 x 2 with
+    four waves and prefetched values (1024-wide at 640 rows)."""
+    require_gpu()
+    wl = synth.MID.with_(T=8)
+    raw = synth.make_weights(wl)
+    orc = Oracle(oracle_config(wl), oracle_weights(raw))
+    nsteps = 6
+    for B in (320, 640):
+        run = GpuRun(wl, raw=raw, B=B, T=wl.T)
+        run.init()
+        check = (0, B // 2 + 1, B - 1)
+        s_out = torch.empty((B, wl.d), device="cuda")
+        logits = torch.empty((B, wl.V), device="cuda")
+        S = {b: [] for b in check}
+        Z = {b: [] for b in check}
+        for t in range(1, nsteps + 1):
+            assert run.step(range(B), t, s_out=s_out, logits=logits) == 0
+            torch.cuda.synchronize()
+            for b in check:
+                S[b].append(s_out[b].double().cpu().numpy())
+                Z[b].append(logits[b].double().cpu().numpy())
+        assert run.dec.sync_error() == 0
+        for b in check:
+            mem = Memory([widen(run.mk[g, b]) for g in range(wl.G)], [widen(run.mv[g, b]) for g in range(wl.G)])
+            st = orc.initial_state()
+            So, Zo = [], []
+            for t in range(1, nsteps + 1):
+                st = orc.transition(st, widen(run.E[b, t - 1]), mem)
+                So.append(st.s)
+                Zo.append(orc.logits(st.s))
+            outs = _check(S[b], Z[b], So, Zo, "mid B=%d b=%d" % (B, b))
+            assert 0 not in outs, ("top-1 differs outside a near-tie", B, b, outs)
+        run.dec.close()
+
+
 def _prefilled(wl, B, t0, check_rows, graph=False, nsteps=3, seed=0):
     """GPU run of nsteps from a pre-filled state at pos t0-1 (ring full,
     memory of length T); rows in check_rows get synth values (the oracle
