@@ -343,7 +343,8 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16
   __syncthreads();
   // same trip count on every thread; unrolled only where the prefetched
   // values need static indices (the unrolled Q/K/V epilogue measured slower)
-#pragma unroll(PRE ? NI : 1)
+  constexpr int EU = PRE ? NI : 1;
+#pragma unroll EU
   for (int j = 0; j < NI; ++j) {
     const int it = (tid >> 4) + (NT / 16) * j;
     const int row = it / CB, pc = it - row * CB;
@@ -483,7 +484,8 @@ void launch_gemm(int dtype, const GemmArgs& g0, const EpiArgs& e, hipStream_t s)
     // unit (8 waves at 344 workgroups of 32 x 1: 15.6 vs 13.0 us)
     const bool w8 = grid.x <= 256;
     if (g.rb == 2 && g.cb == 2) {
-      if (w8 && !pre) RLT_PK(2, 2, 8);  // (with the prefetched epilogue values it would spill)
+      // (eight waves with the prefetched epilogue values would spill)
+      if (w8 && !pre) hipLaunchKernelGGL((k_gemm_bf16_pk<2, 2, false, 8>), grid, dim3(512), 0, s, g, epi);
       else RLT_PK(2, 2, 4);
     } else if (g.rb == 2) {
       if (w8) RLT_PK(2, 1, 8);
