@@ -138,6 +138,7 @@ __device__ __forceinline__ float row_rstd(const GemmArgs& g, int m) {
 // into registers when constructed (before the main loop, so the loads are in
 // flight with it), and finish() sums them in a fixed order through LDS.
 // Units beyond P*RU (only for very wide d) are summed in finish() directly.
+// Rows at or past M load nothing (their rstd is never used).
 template <int R>
 struct RowRstd {
   static constexpr int P = 256 / R;
@@ -145,10 +146,11 @@ struct RowRstd {
   float v[RU];
   __device__ __forceinline__ RowRstd(const GemmArgs& g, int m0) {
     const int row = threadIdx.x % R, part = threadIdx.x / R;
+    const bool live = g.ssq_in && m0 + row < g.M;
 #pragma unroll
     for (int j = 0; j < RU; ++j) {
       const int u = part + j * P;
-      v[j] = (g.ssq_in && u < g.ssq_units) ? g.ssq_in[(int64_t)u * g.M_pad + m0 + row] : 0.f;
+      v[j] = (live && u < g.ssq_units) ? g.ssq_in[(int64_t)u * g.M_pad + m0 + row] : 0.f;
     }
   }
   // s_part: LDS [P][R]; s_rstd: LDS [R]; contains one __syncthreads
@@ -157,7 +159,8 @@ struct RowRstd {
     float a = 0.f;
 #pragma unroll
     for (int j = 0; j < RU; ++j) a += v[j];
-    for (int u = part + RU * P; u < g.ssq_units; u += P) a += g.ssq_in[(int64_t)u * g.M_pad + m0 + row];
+    if (m0 + row < g.M)
+      for (int u = part + RU * P; u < g.ssq_units; u += P) a += g.ssq_in[(int64_t)u * g.M_pad + m0 + row];
     s_part[part * R + row] = a;
     __syncthreads();
     if (threadIdx.x < R) {
