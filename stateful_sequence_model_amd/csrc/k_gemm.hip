@@ -484,8 +484,9 @@ void launch_gemm(int dtype, const GemmArgs& g0, const EpiArgs& e, hipStream_t s)
     // unit (8 waves at 344 workgroups of 32 x 1: 15.6 vs 13.0 us)
     const bool w8 = grid.x <= 256;
     if (g.rb == 2 && g.cb == 2) {
-      // (eight waves with the prefetched epilogue values would spill)
-      if (w8 && !pre) hipLaunchKernelGGL((k_gemm_bf16_pk<2, 2, false, 8>), grid, dim3(512), 0, s, g, epi);
+      // eight waves load the epilogue's values after the K loop (prefetched
+      // they would spill)
+      if (w8) hipLaunchKernelGGL((k_gemm_bf16_pk<2, 2, false, 8>), grid, dim3(512), 0, s, g, epi);
       else RLT_PK(2, 2, 4);
     } else if (g.rb == 2) {
       if (w8) RLT_PK(2, 1, 8);

@@ -70,17 +70,19 @@ def test_mid_from_h0_sampled_rows():
 
 @pytest.mark.timeout(900)
 def test_mid_many_rows_tile_shapes():
-    """L_D=12, d=1024 at 320 and 640 rows from H_0 (6 steps), three rows of
-    each checked: the product tiles of large calls, 64 rows x 1 pair with
-    eight waves and prefetched epilogue values (the 1024-wide products at
-    320 rows), 64 x 2 with eight waves (Q/K/V at 320 rows) and 64 x 2 with
-    four waves and prefetched values (1024-wide at 640 rows)."""
+    """L_D=12, d=1024 at 320, 640 and 1088 rows from H_0 (6 steps), three
+    rows of each checked: the product tiles of large calls, 64 rows x 1 pair
+    with eight waves and prefetched epilogue values (the 1024-wide products
+    at 320 rows), 64 x 2 with eight waves (Q/K/V at 320 rows; the 1024-wide
+    products at 640 rows, whose residual epilogue then loads its values after
+    the K loop) and 64 x 2 with four waves and prefetched values (1024-wide
+    at 1088 rows: 272 workgroups)."""
     require_gpu()
     wl = synth.MID.with_(T=8)
     raw = synth.make_weights(wl)
     orc = Oracle(oracle_config(wl), oracle_weights(raw))
     nsteps = 6
-    for B in (320, 640):
+    for B in (320, 640, 1088):
         run = GpuRun(wl, raw=raw, B=B, T=wl.T)
         run.init()
         check = (0, B // 2 + 1, B - 1)
