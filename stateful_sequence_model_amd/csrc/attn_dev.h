@@ -353,25 +353,64 @@ __device__ __forceinline__ void xattn_body(const AttnArgs& a, int hg, int ch, in
   });
 }
 
-// chunk combine of (head, slot) by `nt` threads with index `tid`
+// chunk combine of (head, slot) by `nt` (>= 64) threads with index `tid`:
+// M = max of the chunk maxima, L = sum over chunks in chunk order of
+// l_c 2^(m_c - M), o = the same weights applied to the chunk outputs in chunk
+// order. Up to CU chunks all partials are loaded at once (one memory round
+// trip); more chunks take the same arithmetic in a plain loop.
 template <typename T, int DH>
 __device__ __forceinline__ void xcombine_body(const AttnArgs& a, int head, int slot, int tid, int nt) {
+  constexpr int CU = 16, EPT = (DH + 63) / 64;  // chunks loaded at once, elements per thread
   const int t = a.rows.t_row[slot];
   if (t <= 0) return;
   const int nc = (t + a.chunk - 1) / a.chunk;
   const float* P = a.part + ((int64_t)slot * a.nch * a.H + head) * (DH + 2);
   const int64_t cs = (int64_t)a.H * (DH + 2);  // chunk stride
-  float M = -INFINITY;
-  for (int c = 0; c < nc; ++c) M = fmaxf(M, P[c * cs + DH]);
-  float L = 0.f;
-  for (int c = 0; c < nc; ++c) L += P[c * cs + DH + 1] * exp2f(P[c * cs + DH] - M);
+  float M = -INFINITY, L = 0.f;
+  float o[EPT];
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) o[k] = 0.f;
+  if (nc <= CU) {
+    float m[CU], l[CU], p[CU][EPT];
+#pragma unroll
+    for (int c = 0; c < CU; ++c) {
+      if (c < nc) {
+        m[c] = P[c * cs + DH];
+        l[c] = P[c * cs + DH + 1];
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) p[c][k] = tid + k * nt < DH ? P[c * cs + tid + k * nt] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < CU; ++c)
+      if (c < nc) M = fmaxf(M, m[c]);
+#pragma unroll
+    for (int c = 0; c < CU; ++c)
+      if (c < nc) {
+        const float w = exp2f(m[c] - M);
+        L += l[c] * w;
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) o[k] = fmaf(p[c][k], w, o[k]);
+      }
+  } else {
+    for (int c = 0; c < nc; ++c) M = fmaxf(M, P[c * cs + DH]);
+    for (int c = 0; c < nc; ++c) {
+      const float w = exp2f(P[c * cs + DH] - M);
+      L += P[c * cs + DH + 1] * w;
+#pragma unroll
+      for (int k = 0; k < EPT; ++k)
+        if (tid + k * nt < DH) o[k] = fmaf(P[c * cs + tid + k * nt], w, o[k]);
+    }
+  }
   const float inv = 1.f / L;
   T* out = (T*)a.out;
-  for (int e = tid; e < DH; e += nt) {
-    float o = 0.f;
-    for (int c = 0; c < nc; ++c) o = fmaf(P[c * cs + e], exp2f(P[c * cs + DH] - M), o);
-    const int col = head * DH + e;
-    out[a.out_pk ? pk_off(slot, col, a.d >> 6) : (int64_t)slot * a.d + col] = from_f<T>(o * inv);
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    const int e = tid + k * nt;
+    if (e < DH) {
+      const int col = head * DH + e;
+      out[a.out_pk ? pk_off(slot, col, a.d >> 6) : (int64_t)slot * a.d + col] = from_f<T>(o[k] * inv);
+    }
   }
 }
 
