@@ -75,7 +75,8 @@ struct rlt_ctx {
   // capacities and launch shapes
   int max_rows, max_ctx, M_pad;
   int chunk, nch;      // cross-attention chunk forced for every call (0: per call), partial slots
-  int hpw, hpw_x;      // heads per workgroup: SWA, cross-attention
+  int hpw, hpw_x;      // heads per workgroup: SWA (the most a call uses), cross-attention
+  bool hpw_forced, hpw_x_forced;  // hpw / hpw_x for every call (tuning sweeps)
   int gemm_mb_force;   // 0 or 1/2/4 (tuning)
   int gemm_s_force;    // 0 or forced K split (tuning)
   int gemm_wide;       // wide-tile products for calls above 32 rows (1 = on)
@@ -211,13 +212,16 @@ int elems_per_lane(int dt) { return dt == 1 ? 16 : 8; }
 // heads per attention workgroup: hpw * (dh / E) lanes per key group, which
 // must divide 256; default: the widest group of at most 32 lanes. A
 // requested value (tuning) is used when valid.
-int choose_hpw(const rlt_config& c, int dt, int requested) {
+bool hpw_ok(const rlt_config& c, int dt, int h) {
   const int lpk = c.d_head / elems_per_lane(dt);
-  auto ok = [&](int h) { return h >= 1 && h <= c.n_heads && c.n_heads % h == 0 && 256 % (h * lpk) == 0; };
-  if (requested > 0 && ok(requested)) return requested;
+  return h >= 1 && h <= c.n_heads && c.n_heads % h == 0 && 256 % (h * lpk) == 0;
+}
+int choose_hpw(const rlt_config& c, int dt, int requested) {
+  if (requested > 0 && hpw_ok(c, dt, requested)) return requested;
+  const int lpk = c.d_head / elems_per_lane(dt);
   int best = 1;
   for (int h = 1; h <= c.n_heads; ++h)
-    if (ok(h) && h * lpk <= 32) best = h;
+    if (hpw_ok(c, dt, h) && h * lpk <= 32) best = h;
   return best;
 }
 
@@ -412,7 +416,9 @@ extern "C" int rlt_create(const rlt_config* cfg, const rlt_weights* w, int32_t m
   c->chunk = env_int("RLT_XATTN_CHUNK", 0);  // > 0: every call (tuning sweeps)
   if (c->chunk != 0 && (c->chunk < 16 || c->chunk > 4096)) c->chunk = 0;
   c->nch = (max_ctx + (c->chunk ? c->chunk : 256) - 1) / (c->chunk ? c->chunk : 256);
+  c->hpw_forced = env_int("RLT_SWA_HPW", 0) > 0;
   c->hpw = choose_hpw(*cfg, c->dt, env_int("RLT_SWA_HPW", 0));
+  c->hpw_x_forced = env_int("RLT_XATTN_HPW", 0) > 0;
   c->hpw_x = choose_hpw(*cfg, c->dt, env_int("RLT_XATTN_HPW", 2));
   c->gemm_mb_force = env_int("RLT_GEMM_MB", 0);
   c->gemm_s_force = env_int("RLT_GEMM_S", 0);
@@ -628,9 +634,24 @@ struct Gemm {
 // 128 rows 14.7 ms per step with 2048 against 15.4 with 512; 64 rows best
 // at 1024, 16 at 512, 1 at 256). Chunk boundaries depend only on t and the
 // call's row count.
+// Attention heads per workgroup of an n-row call: the context's width h,
+// narrowed (down to one head) while the call would have fewer than `want`
+// workgroups per key range, so that small calls spread their keys over more
+// compute units. SWA: 256 (batch 1 at t ~ 2048: 4.43 -> 4.09 ms per step,
+// batch 16: 6.25 -> 5.91); cross-attention, whose chunks multiply its
+// workgroups: 128 (narrower measured slower at 16 rows, 6.05 vs 5.92 ms, and
+// faster at one row, 4.02 vs 4.09)
+int narrow_hpw(const rlt_ctx* c, int h, int n, int want) {
+  for (int k = h - 1; k >= 1 && (int64_t)n * (c->cfg.n_heads / h) < want; --k)
+    if (hpw_ok(c->cfg, c->dt, k)) h = k;
+  return h;
+}
+int swa_hpw(const rlt_ctx* c, int n) { return c->hpw_forced ? c->hpw : narrow_hpw(c, c->hpw, n, 256); }
+int xattn_hpw(const rlt_ctx* c, int n) { return c->hpw_x_forced ? c->hpw_x : narrow_hpw(c, c->hpw_x, n, 128); }
+
 int xattn_chunk(const rlt_ctx* c, int n) {
   if (c->chunk > 0) return c->chunk;
-  const int wg = n * (c->cfg.n_heads / c->hpw_x);  // workgroups per chunk index
+  const int wg = n * (c->cfg.n_heads / xattn_hpw(c, n));  // workgroups per chunk index
   return wg >= 1024 ? 2048 : wg >= 512 ? 1024 : wg >= 128 ? 512 : 256;
 }
 
@@ -783,7 +804,7 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
     at.ring_k = (char*)P.st->ring_k + l * ring_layer;
     at.ring_v = (char*)P.st->ring_v + l * ring_layer;
     at.out = w.o;
-    at.hpw = c->hpw;
+    at.hpw = swa_hpw(c, n);
     { Prof pf(c, RLT_PROF_SWA, s); launch_swa(c->dt, at, s); }
     EpiArgs e = E0;
     e.kind = EPI_RESID;
@@ -804,7 +825,7 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
     at.mk = (const char*)P.mem.k + (size_t)g * P.mem.stride_g * es;
     at.mv = (const char*)P.mem.v + (size_t)g * P.mem.stride_g * es;
     at.out = w.o;
-    at.hpw = c->hpw_x;
+    at.hpw = xattn_hpw(c, n);
     { Prof pf(c, RLT_PROF_XATTN, s); launch_xattn(c->dt, at, s); }
     { Prof pf(c, RLT_PROF_XCOMBINE, s); launch_xcombine(c->dt, at, s); }
     EpiArgs e = E0;
