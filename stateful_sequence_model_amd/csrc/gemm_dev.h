@@ -62,6 +62,35 @@ struct Epi {
     dst[xb] = from_f<T>(vb);
   }
 
+  // memkv_at for 8 consecutive columns from ca and from cb (one 16-byte
+  // store each; same arithmetic per element); needs a.mem_vec
+  __device__ __forceinline__ void memkv_at8(int t, int64_t off, int ca, const float* va, int cb, const float* vb,
+                                            float rs) const {
+    static_assert(sizeof(T) == 2, "16-byte runs of 8 two-byte elements");
+    const int seg = ca / a.d;
+    const int xa = ca - seg * a.d, xb = cb - seg * a.d;
+    float x[8], y[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      x[k] = va[k] * rs;
+      y[k] = vb[k] * rs;
+    }
+    if (seg == 0 && a.rope) {
+      const int i0 = xa % a.dh;  // the 8 columns stay in the first half of the head
+#pragma unroll
+      for (int k = 0; k < 8; ++k) rot(rope_cs(t, i0 + k, true), x[k], y[k]);
+    }
+    T* dst = (T*)(seg == 0 ? a.mk : a.mv) + off;
+    uint16_t px[8], py[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      px[k] = from_f<T>(x[k]);
+      py[k] = from_f<T>(y[k]);
+    }
+    *(uint4*)(dst + xa) = *(const uint4*)px;
+    *(uint4*)(dst + xb) = *(const uint4*)py;
+  }
+
   // Values an epilogue reads from memory for (row m, columns ca, cb), loaded
   // ahead of the product by tiles that know their outputs in advance: the
   // residual and the next norm's gains (EPI_RESID), the rotary (cos, sin)

@@ -203,6 +203,26 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_tile(GemmArgs g, Epi<uint16_t
   }
   if (norm_here) rr.finish(g, m0, s_part, s_rstd);  // uniform branch: contains a barrier
   __syncthreads();
+  if (memkv && epi.a.mem_vec) {
+    // two threads per (row, pair), each 8 consecutive columns of block ba and
+    // the same 8 of bb: 16-byte stores (2 bytes per lane and store measured
+    // as most of the prefill's epilogue)
+    for (int it = tid; it < BM * (BN / 32) * 2; it += 256) {
+      const int hh = it & 1, rp = it >> 1;
+      const int pl = rp % (BN / 32), row = rp / (BN / 32);
+      if (m0 + row >= g.M || s_t[row] <= 0) continue;
+      int ba, bb;
+      pair_blocks(g, pair0 + pl, ba, bb);
+      float va[8], vb[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        va[k] = Cs[row * LDC + pl * 32 + 8 * hh + k];
+        vb[k] = Cs[row * LDC + pl * 32 + 16 + 8 * hh + k];
+      }
+      epi.memkv_at8(s_t[row], s_off[row], ba * 16 + 8 * hh, va, bb * 16 + 8 * hh, vb, norm_here ? s_rstd[row] : 1.f);
+    }
+    return;
+  }
   // 16 consecutive threads take the 16 column positions of one (row, pair):
   // virtual columns c16 (block ba) and 16 + c16 (block bb); every thread runs
   // the same trip count, so the row sums of squares reduce over those 16

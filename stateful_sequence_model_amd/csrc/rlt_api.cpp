@@ -1450,6 +1450,8 @@ void enqueue_mem_entries(rlt_ctx* c, const rlt_memory_weights* mw, const rlt_mem
     ep.mv = (char*)mem->v + (size_t)g * mem->stride_g * c->es;
     ep.msb = mem->stride_b;
     ep.mst = mem->stride_t;
+    ep.mem_vec = c->dt == 1 && (uintptr_t)ep.mk % 16 == 0 && (uintptr_t)ep.mv % 16 == 0 && mem->stride_b % 8 == 0 &&
+                 mem->stride_t % 8 == 0 && d % 8 == 0;
 
     Gemm gm{c, &c->ws[0], s};
     gm.m_pad = c->mem_rows;

@@ -232,6 +232,7 @@ struct EpiArgs {
   void* mk;
   void* mv;
   int64_t msb, mst;
+  int mem_vec;  // bf16 and every 8-column run of a destination entry 16-byte aligned
 };
 
 // ----------------------------------------------------------------------------
