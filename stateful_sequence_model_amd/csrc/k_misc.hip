@@ -186,6 +186,39 @@ __global__ __launch_bounds__(256) void k_mem_prep(Rows rows, EIn e, int d, const
   if (threadIdx.x == 0) ssq[slot] = ss;
 }
 
+// bf16 with every row of e and of A in 16-byte runs: thread i takes the 8
+// consecutive elements 8 i, 8 i + 2048, ... (one 16-byte load and store each)
+__global__ __launch_bounds__(256) void k_mem_prep_v8(Rows rows, EIn e, int d, const float* gain, uint16_t* A,
+                                                     float* ssq) {
+  __shared__ float scratch[16];
+  const int slot = blockIdx.x;
+  const int t = rows.t_row[slot];
+  uint16_t* out = A + (int64_t)slot * d;
+  if (t <= 0) {
+    for (int c = threadIdx.x * 8; c < d; c += 2048) *(uint4*)(out + c) = make_uint4(0, 0, 0, 0);
+    if (threadIdx.x == 0) ssq[slot] = (float)d;
+    return;
+  }
+  const uint16_t* x = (const uint16_t*)e.p + (int64_t)rows.src[slot] * e.sb + (int64_t)(t - 1) * e.st;
+  float ss = 0.f;
+  for (int c = threadIdx.x * 8; c < d; c += 2048) {
+    const uint4 xv = *(const uint4*)(x + c);
+    const float4 g0 = *(const float4*)(gain + c), g1 = *(const float4*)(gain + c + 4);
+    const uint16_t* xs = (const uint16_t*)&xv;
+    const float gs[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    uint16_t o[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float v = bf2f(xs[k]);
+      ss = fmaf(v, v, ss);
+      o[k] = f2bf(v * gs[k]);
+    }
+    *(uint4*)(out + c) = *(const uint4*)o;
+  }
+  ss = block_sum(ss, scratch);
+  if (threadIdx.x == 0) ssq[slot] = ss;
+}
+
 __global__ void k_mem_setlen(const int* len, int B, int* mem_len) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b < B) mem_len[b] = len[b];
@@ -533,8 +566,12 @@ void launch_mem_rows(const int* offs, int B, int64_t r0, int n, int* src_out, in
 }
 void launch_mem_prep(int dtype, const Rows& rows, EIn e, int d, const float* gain, void* A, float* ssq,
                      hipStream_t s) {
+  const bool v8 = dtype == 1 && d % 8 == 0 && (uintptr_t)e.p % 16 == 0 && e.sb % 8 == 0 && e.st % 8 == 0 &&
+                  (uintptr_t)A % 16 == 0 && (uintptr_t)gain % 16 == 0;
   if (dtype == 0)
     hipLaunchKernelGGL(k_mem_prep<float>, dim3(rows.n), dim3(256), 0, s, rows, e, d, gain, (float*)A, ssq);
+  else if (v8)
+    hipLaunchKernelGGL(k_mem_prep_v8, dim3(rows.n), dim3(256), 0, s, rows, e, d, gain, (uint16_t*)A, ssq);
   else
     hipLaunchKernelGGL(k_mem_prep<uint16_t>, dim3(rows.n), dim3(256), 0, s, rows, e, d, gain, (uint16_t*)A, ssq);
 }
