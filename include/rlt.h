@@ -151,7 +151,11 @@ typedef struct rlt_state {
  * and holds d contiguous elements of the config dtype. Only positions
  * j <= t are read at step t [RLT §4.2]; mem_len[r] (device) is the number
  * of valid positions of row r; a step needing t > mem_len[r] is a
- * device-detected RLT_EPREFIX. Strides are in elements. */
+ * device-detected RLT_EPREFIX. Strides are in elements. The decoder calls
+ * (rlt_decoder_step, rlt_replay_sequence) read entries in 16-byte runs: k and
+ * v must be 16-byte aligned and the strides multiples of 16 bytes' worth of
+ * elements (8 bf16, 4 fp32), else RLT_EINVAL; the memory writers accept any
+ * element-aligned layout (16-byte stores where it allows them). */
 typedef struct rlt_memory {
   const void* k;
   const void* v;

@@ -999,6 +999,17 @@ int check_memory(const rlt_memory& m) {
   return RLT_OK;
 }
 
+// the attention kernels read memory entries in 16-byte runs
+int check_memory_read(const rlt_ctx* c, const rlt_memory& m) {
+  int rc = check_memory(m);
+  if (rc) return rc;
+  const int64_t run = 16 / c->es;  // elements per 16 bytes
+  if ((uintptr_t)m.k % 16 || (uintptr_t)m.v % 16 || m.stride_t % run || m.stride_b % run || m.stride_g % run)
+    return fail(RLT_EINVAL, "memory k/v must be 16-byte aligned with strides in multiples of %lld elements",
+                (long long)run);
+  return RLT_OK;
+}
+
 }  // namespace
 
 // ----------------------------------------------------------------------------
@@ -1082,7 +1093,7 @@ extern "C" int rlt_decoder_step(rlt_ctx* c, rlt_state* st, const rlt_step_io* io
   if (io->n < 1 || io->n > c->max_rows) return fail(RLT_ESHAPE, "n=%d outside 1..max_rows=%d", io->n, c->max_rows);
   if (io->n > st->B_cap) return fail(RLT_ESHAPE, "n > B_cap");
   if (!io->rows || !io->e) return fail(RLT_EINVAL, "null rows or e");
-  if ((rc = check_memory(io->mem))) return rc;
+  if ((rc = check_memory_read(c, io->mem))) return rc;
   if (io->logp && !io->score_tok) return fail(RLT_EINVAL, "logp needs score_tok");
   if (io->uniform) {
     if (!(io->temperature > 0.f)) return fail(RLT_EINVAL, "temperature must be > 0");
@@ -1141,7 +1152,7 @@ extern "C" int rlt_replay_sequence(rlt_ctx* c, rlt_state* st, const rlt_replay_i
   if (B < 1 || B > c->max_rows || B > st->B_cap) return fail(RLT_ESHAPE, "B outside 1..max_rows/B_cap");
   if (!io->len_host || !io->split_host || !io->e || !io->tokens || !io->logp)
     return fail(RLT_EINVAL, "null replay input");
-  if ((rc = check_memory(io->mem))) return rc;
+  if ((rc = check_memory_read(c, io->mem))) return rc;
   int maxlen = 0;
   std::vector<int> rows(B);
   for (int b = 0; b < B; ++b) {

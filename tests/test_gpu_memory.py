@@ -51,6 +51,43 @@ def _check_entries(wl, K, V, mw_raw, E, entries, tol):
     return worst
 
 
+def test_prefill_unaligned_buffers_and_decoder_alignment_check():
+    """bf16 small workload with e and the memory buffers starting 2 bytes past
+    a 16-byte boundary: the prefill takes its element-wise gather and
+    epilogue (the 16-byte ones need aligned runs), every entry against the
+    oracle; a decoder step on that memory is refused on the host (RLT_EINVAL:
+    the attention kernels read 16-byte runs)."""
+    require_gpu()
+    from stateful_sequence_model_amd import Decoder, DecoderState
+    from stateful_sequence_model_amd._abi import RLT_EINVAL
+    wl = synth.SMALL
+    B, T_cap = 4, 40
+    dec, mw, mw_raw, K0, V0, mem_len, _, _ = _setup(wl, B, T_cap)
+    n = K0.numel()
+    kbuf = torch.zeros(n + 8, dtype=K0.dtype, device="cuda")
+    vbuf = torch.zeros_like(kbuf)
+    K, V = kbuf[1:n + 1].view(K0.shape), vbuf[1:n + 1].view(V0.shape)
+    assert K.data_ptr() % 16 and V.data_ptr() % 16
+    mem = Decoder.memory(K, V, mem_len)
+    E = synth.make_e(wl, 0, B, T_cap)
+    flat = torch.from_numpy(E.view(np.int16)).cuda().view(torch.bfloat16).reshape(-1)
+    ebuf = torch.zeros(flat.numel() + 8, dtype=torch.bfloat16, device="cuda")
+    ebuf[1:flat.numel() + 1] = flat
+    Ed = ebuf[1:flat.numel() + 1].view(B, T_cap, wl.d)
+    assert Ed.data_ptr() % 16
+    lens = np.array([40, 17, 1, 33], dtype=np.int32)
+    assert dec.memory_prefill(mw, mem, T_cap, lens, Ed) == 0
+    torch.cuda.synchronize()
+    assert dec.sync_error() == 0
+    assert mem_len.cpu().tolist() == lens.tolist()
+    worst = _check_entries(wl, K, V, mw_raw, E, [(b, t) for b in range(B) for t in range(1, lens[b] + 1)], 1e-2)
+    print("unaligned prefill: worst entry rel L2 %.2e" % worst)
+    st = DecoderState(dec.cfg, B)
+    rows = torch.arange(B, dtype=torch.int32, device="cuda")
+    dec.init_state(st, rows)
+    assert dec.step(st, rows, Ed[:, 0].contiguous(), mem) == RLT_EINVAL
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_prefill_matches_oracle(dtype):
     """Small workload (G = 4 groups, d = 256): ragged lengths; every entry
