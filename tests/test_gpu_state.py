@@ -160,6 +160,27 @@ def test_batch_composition_independence():
         assert np.array_equal(S3[:, j], S[:, b])
 
 
+def test_memory_strides_other_layout_bit_exact():
+    """The memory ABI takes explicit strides: the same entries laid out
+    [B][G][T][d] (stride_b = G T d, stride_g = T d) instead of [G][B][T][d]
+    give bit-identical states and logits (only the addressing differs)."""
+    require_gpu()
+    from stateful_sequence_model_amd import _abi as A
+    wl = SMALL.with_(B=4, T=24)
+    ref = GpuRun(wl)
+    ref.init()
+    S, Z = ref.run(12)
+    alt = GpuRun(wl)
+    alt.init()
+    G, B, T, d = alt.mkd.shape
+    mk = alt.mkd.permute(1, 0, 2, 3).contiguous()  # [B][G][T][d]
+    mv = alt.mvd.permute(1, 0, 2, 3).contiguous()
+    alt.mem = A.rlt_memory(mk.data_ptr(), mv.data_ptr(), T * d, G * T * d, d, alt.mem_len.data_ptr())
+    S2, Z2 = alt.run(12)
+    assert np.array_equal(S2, S) and np.array_equal(Z2, Z)
+    del mk, mv
+
+
 def test_pending_token_bookkeeping_and_errors():
     """App. A.2: a deferred token is recorded as pending; consuming it clears
     it; consuming a different token is RLT_EPENDING and leaves that row's
