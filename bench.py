@@ -152,8 +152,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        log("bench.py measures one GPU only: this build has no multi-GPU path "
-            "(sequences shard across GPUs with no per-step exchange; see DESIGN.md). Use --gpus 1.")
+        log("bench.py measures one GPU only: the library has no multi-GPU path "
+            "(sequences would shard across GPUs with no per-step exchange). Use --gpus 1.")
         sys.exit(2)
 
     import numpy as np
