@@ -344,8 +344,15 @@ __device__ __forceinline__ void xattn_body(const AttnArgs& a, int hg, int ch, in
   walk<T, LPK, UNROLL>(acc, a.q + (int64_t)slot * d + col, a.qscale, j0 + kg, j1, KPW, kv);
   merge_groups<T>(acc, G, KPW, s_o, s_ml, [&](int li, int e, float o, float M, float L) {
     const int ljl = li % LPK;
+    const int eo = ljl * PE + (e < PE ? e : h + e - PE);  // element of the head
+    if (a.direct) {
+      // the only chunk: what the combine would write for it (weight 2^0 = 1)
+      const int c = (hg * a.hpw + li / LPK) * DH + eo;
+      ((T*)a.out)[a.out_pk ? pk_off(slot, c, d >> 6) : (int64_t)slot * d + c] = from_f<T>(o * (1.f / L));
+      return;
+    }
     float* P = a.part + (((int64_t)slot * a.nch + ch) * a.H + hg * a.hpw + li / LPK) * (DH + 2);
-    P[ljl * PE + (e < PE ? e : h + e - PE)] = o;
+    P[eo] = o;
     if (ljl == 0 && e == 0) {
       P[DH] = M;
       P[DH + 1] = L;

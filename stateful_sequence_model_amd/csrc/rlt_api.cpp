@@ -652,7 +652,10 @@ int xattn_hpw(const rlt_ctx* c, int n) { return c->hpw_x_forced ? c->hpw_x : nar
 int xattn_chunk(const rlt_ctx* c, int n) {
   if (c->chunk > 0) return c->chunk;
   const int wg = n * (c->cfg.n_heads / xattn_hpw(c, n));  // workgroups per chunk index
-  return wg >= 1024 ? 2048 : wg >= 512 ? 1024 : wg >= 128 ? 512 : 256;
+  // (one chunk of the whole context up to 4096 positions when there are
+  // enough workgroups: no combine launch)
+  if (wg >= 1024) return c->max_ctx <= 4096 ? 4096 : 2048;
+  return wg >= 512 ? 1024 : wg >= 128 ? 512 : 256;
 }
 
 struct StepPlan {
@@ -782,6 +785,7 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
   at.W = cf.window;
   at.chunk = xattn_chunk(c, n);
   at.nch = (c->max_ctx + at.chunk - 1) / at.chunk;
+  at.direct = at.nch == 1 ? 1 : 0;
   at.part = w.part;
   at.out_pk = pk ? 1 : 0;
   at.sb = P.mem.stride_b;
@@ -827,7 +831,10 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
     at.out = w.o;
     at.hpw = xattn_hpw(c, n);
     { Prof pf(c, RLT_PROF_XATTN, s); launch_xattn(c->dt, at, s); }
-    { Prof pf(c, RLT_PROF_XCOMBINE, s); launch_xcombine(c->dt, at, s); }
+    if (!at.direct) {
+      Prof pf(c, RLT_PROF_XCOMBINE, s);
+      launch_xcombine(c->dt, at, s);
+    }
     EpiArgs e = E0;
     e.kind = EPI_RESID;
     e.out_f = w.z;

@@ -260,6 +260,7 @@ struct AttnArgs {
   float* part;              // [n][nch][H][dh + 2]
   void* out;                // [n][d] (T) attention output
   int out_pk;               // bf16: out in fragment order (the next product's operand)
+  int direct;               // cross-attention with one chunk: the normalised output, no combine
 };
 
 void launch_gemm(int dtype, const GemmArgs& g, const EpiArgs& e, hipStream_t s);
