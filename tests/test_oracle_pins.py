@@ -14,7 +14,7 @@ import torch
 import torch.nn.functional as Fn
 
 import synth
-from oracle import (Config, Memory, Oracle, attend, behaviour_logprobs, importance_ratio,
+from oracle import (Config, Memory, Oracle, attend, behaviour_logprobs, importance_ratio, replay,
                     retained_positions, ring_slot, rms_norm, rope, sample, state_from_ring,
                     state_to_ring, topk_order, window_positions)
 from tests.helpers import e_of, make_oracle, memory_of, oracle_config, rel_l2
@@ -694,3 +694,61 @@ def test_trajectory_log_ratio_is_log_of_product():
         prod *= importance_ratio(a, b)
     assert math.isclose(math.exp(trajectory_log_ratio(lp, lm)), prod, rel_tol=1e-12)
     assert trajectory_log_ratio([], []) == 0.0
+
+
+# ---------------------------------------------------------------------------
+# replay scoring index ("Recurrent Looped Transformer" App. A.4 and App. A.2)
+# ---------------------------------------------------------------------------
+
+# A hand-written token table: x_1 .. x_5 (1-based as in the report). The
+# literals below are the ids each scored position must use, written out
+# rather than indexed from the table, so that an off-by-one in the replay's
+# token index (scoring x_t instead of x_{t+1}) changes every expected value.
+REPLAY_X = [7, 11, 22, 33, 44]
+REPLAY_EXPECT = {2: 22, 3: 33, 4: 44}   # split = 2, length = 5: t -> x_{t+1}
+
+
+def _replay_fixture():
+    wl = _tiny(T=8)
+    orc = make_oracle(wl)
+    mem, E = memory_of(wl, 0), e_of(wl, 0)
+    return wl, orc, mem, E
+
+
+def test_replay_scores_next_token_before_consuming_it():
+    """App. A.4: after consuming x_t (t >= split) the replay reads
+    log p(x_{t+1} | x_{1:t}) from s_t, before x_{t+1} is consumed; x_len is
+    never consumed (App. A.2, pending). The states come from explicit
+    transitions, the scored ids from the literal table above."""
+    wl, orc, mem, E = _replay_fixture()
+    final, logp, ss = replay(orc, E, mem, np.array(REPLAY_X), 5, 2)
+    assert sorted(logp) == [2, 3, 4]
+    st = orc.initial_state()
+    states = {}
+    for t in (1, 2, 3, 4):
+        st = orc.transition(st, E[t - 1], mem)
+        states[t] = st.s
+    for t, tok in REPLAY_EXPECT.items():
+        assert logp[t] == orc.log_prob(states[t], tok), t
+        # a neighbouring id scores differently (the pin can see an index slip)
+        assert logp[t] != orc.log_prob(states[t], REPLAY_X[t - 1])
+    assert final.pos == 4 and np.array_equal(final.s, states[4])
+    assert len(ss) == 4 and np.array_equal(ss[1], states[2])
+
+
+def test_gradient_twin_scores_next_token():
+    """The autograd twin of the replay scores the same literal ids."""
+    from oracle.rlt_grad import replay_loss
+    import torch as _t
+    wl, orc, mem, E = _replay_fixture()
+    cfg = orc.cfg
+    w = {k: _t.tensor(np.asarray(v, dtype=np.float64)) for k, v in orc.w.items()}
+    seq = dict(E=_t.tensor(E), mem_k=[_t.tensor(m) for m in mem.k], mem_v=[_t.tensor(m) for m in mem.v],
+               tokens=np.array(REPLAY_X), length=5, split=2, w=np.ones(5))
+    _, lps = replay_loss(cfg, w, [seq])
+    st = orc.initial_state()
+    for t in (1, 2, 3, 4):
+        st = orc.transition(st, E[t - 1], mem)
+        if t in REPLAY_EXPECT:
+            assert abs(float(lps[0][t]) - orc.log_prob(st.s, REPLAY_EXPECT[t])) < 1e-10, t
+    assert sorted(lps[0]) == [2, 3, 4]
