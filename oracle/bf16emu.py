@@ -7,22 +7,25 @@ no code with the GPU path.
 The plain oracle (``rlt_oracle.Oracle``) is the definition of the transition
 ("Recurrent Looped Transformer" §2.3 eqs. (2.4)-(2.6), §2.5 eqs.
 (2.9)-(2.16)) in float64 on the given (bf16-valued) weights and inputs. The
-bf16 mode of the GPU library additionally rounds to bfloat16 at fixed points
-of the computation (the rounding contract, a convention of this
-implementation that the report leaves open):
+bf16 mode of the GPU library additionally rounds at fixed points of the
+computation (the rounding contract, a convention of this implementation
+that the report leaves open):
 
-  * every matrix-product input: the merge input [e; r] with
-    r = RMSNorm_s(s_{t-1}) rounded (convex merge: [e; s] with s rounded), the
-    low-rank intermediate V r, the attention outputs before their output
-    projections, the SwiGLU product silu(W_gate h) * (W_up h);
+  * every matrix-product input ("act"): the merge input [e; r] with
+    r = RMSNorm_s(s_{t-1}) (convex merge: [e; s]), the low-rank intermediate
+    V r, the attention outputs before their output projections, the SwiGLU
+    product silu(W_gate h) * (W_up h). The bf16 products of the operand-order
+    path take it as two bf16 terms, x rounded and then the remainder rounded
+    (``two_term``); the other bf16 tiles as one rounded term (``bf16_round``);
   * the normalised inputs of the products that follow an RMSNorm are carried
-    as round(z * gain) and the factor 1 / sqrt(mean(z^2) + eps) multiplies the
+    as act(z * gain) and the factor 1 / sqrt(mean(z^2) + eps) multiplies the
     product's result (RMSNorm(z) W^T = rstd * ((z * gain) W^T));
-  * the SWA key and value of the current token when they are produced.
+  * the SWA key and value of the current token when they are stored ("kv"),
+    always one bf16 rounding (the cache is bf16).
 
 Everything else (accumulation, softmax, residual stream, the state s_t)
 stays unrounded, here in float64. ``RoundingOracle`` applies exactly those
-roundings; with ``rnd`` the identity it is the plain oracle rearranged
+roundings; with identities for act and kv it is the plain oracle rearranged
 (pinned in the tests to 1e-12). Comparing the GPU with it separates what the
 rounding contract itself does (for example an argmax flipped by a near-tie)
 from what the kernels add.
@@ -48,14 +51,25 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
     return r.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
+def two_term(x: np.ndarray) -> np.ndarray:
+    """The value two bf16 terms carry: hi = x rounded, lo = (x - hi) rounded,
+    hi + lo (about 16 significant bits of x)."""
+    x = np.asarray(x, dtype=np.float64)
+    hi = bf16_round(x)
+    return hi + bf16_round(x - hi)
+
+
 class RoundingOracle(Oracle):
     """The transition with the bf16 rounding contract applied (float64
-    elsewhere). ``rnd`` maps an array to its rounded value."""
+    elsewhere). ``act`` maps a matrix-product input to the value the product
+    sees, ``kv`` a produced SWA key or value to its stored value."""
 
     def __init__(self, cfg: Config, weights: Dict[str, np.ndarray],
-                 rnd: Callable[[np.ndarray], np.ndarray] = bf16_round):
+                 act: Callable[[np.ndarray], np.ndarray] = two_term,
+                 kv: Callable[[np.ndarray], np.ndarray] = bf16_round):
         super().__init__(cfg, weights, dtype=np.float64)
-        self.rnd = rnd
+        self.rnd = act
+        self.kv = kv
 
     # rstd * (W @ rnd(x * gain)) == W @ RMSNorm(x) before rounding
     def _rstd(self, x: np.ndarray) -> float:
@@ -95,8 +109,8 @@ class RoundingOracle(Oracle):
         p = "layer.%d." % l
         gain = w[p + "norm_s"]
         q = self._pos(self._normed(w[p + "wq"], z, gain), t)
-        k = self.rnd(self._pos(self._normed(w[p + "wk"], z, gain), t))
-        v = self.rnd(self._normed(w[p + "wv"], z, gain))
+        k = self.kv(self._pos(self._normed(w[p + "wk"], z, gain), t))
+        v = self.kv(self._normed(w[p + "wv"], z, gain))
         win = window_positions(t, c.W)
         o = attend(q, np.stack([hist[j][0] for j in win[:-1]] + [k]),
                    np.stack([hist[j][1] for j in win[:-1]] + [v]), c.H, c.dh)

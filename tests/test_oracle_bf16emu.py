@@ -18,7 +18,7 @@ import torch
 
 import synth
 from oracle import Oracle
-from oracle.bf16emu import RoundingOracle, bf16_round
+from oracle.bf16emu import RoundingOracle, bf16_round, two_term
 from tests.helpers import e_of, memory_of, oracle_config, oracle_weights, rel_l2
 
 
@@ -37,8 +37,9 @@ def _emu_vs_plain(wl, n=6, rows=(0, 1)):
     raw = synth.make_weights(wl)
     w = oracle_weights(raw)
     plain = Oracle(oracle_config(wl), w)
-    ident = RoundingOracle(oracle_config(wl), w, rnd=lambda a: np.asarray(a, dtype=np.float64))
-    rounded = RoundingOracle(oracle_config(wl), w)
+    idf = lambda a: np.asarray(a, dtype=np.float64)
+    ident = RoundingOracle(oracle_config(wl), w, act=idf, kv=idf)
+    rounded = RoundingOracle(oracle_config(wl), w, act=bf16_round)
     worst_id, worst_rnd = 0.0, 0.0
     for b in rows:
         mem, E = memory_of(wl, b), e_of(wl, b)
@@ -60,3 +61,15 @@ def test_identity_rounding_equals_plain_oracle(over):
     assert worst_id < 1e-12, worst_id
     # the rounding contract moves the results by bf16 noise, no more
     assert 1e-6 < worst_rnd < 2e-2, worst_rnd
+
+
+def test_two_term_carries_sixteen_bits():
+    """hi + lo with hi = bf16(x), lo = bf16(x - hi): relative error below
+    2^-16 (each term keeps 8 significant bits; the remainder is at most half
+    an ulp of hi), exact for bf16-valued x (lo = 0)."""
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal(100000) * 10.0 ** rng.integers(-8, 8, 100000)
+    err = np.abs(two_term(x) - x) / np.abs(x)
+    assert err.max() < 2.0 ** -16
+    b = bf16_round(x)
+    assert np.array_equal(two_term(b), b)
