@@ -51,44 +51,61 @@ def step_bytes(wl, B: int, t: int, es: int) -> dict:
                 total=weights + ring + memory + small)
 
 
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, t0: int, budget_s: float, raw) -> dict:
-    """The float64 oracle timed on this host on a bounded sample: one
-    sequence, consecutive transitions from a pre-filled state at t0."""
+    """The float32 oracle timed on this host on a bounded sample: one
+    sequence, consecutive transitions (with the readout) from a pre-filled
+    state at t0, first with the BLAS thread pool at its default size (all
+    cores), then with one thread; each leg gets half the budget."""
     import numpy as np
     import synth
     from oracle import Config, Memory, Oracle, state_from_ring
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        cores = os.cpu_count() or 1
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     def widen(a):
-        return synth.bf16_bits_to_f32(a).astype(np.float64) if a.dtype == np.uint16 else a.astype(np.float64)
+        return synth.bf16_bits_to_f32(a) if a.dtype == np.uint16 else a.astype(np.float32)
 
     cfg = Config(L=wl.L, d=wl.d, H=wl.H, dh=wl.dh, W=wl.W, G=wl.G, F=wl.F, V=wl.V, merge=wl.merge,
                  alpha=wl.alpha, eps=wl.eps, rope_theta=wl.rope_theta, pos=wl.pos)
-    orc = Oracle(cfg, {k: widen(v) for k, v in raw.items()})
+    orc = Oracle(cfg, {k: widen(v) for k, v in raw.items()}, dtype=np.float32)
     nT = t0 + 64
     mem = Memory([widen(synth.make_memory(wl, "k", g, 0, 1, nT)[0]) for g in range(wl.G)],
                  [widen(synth.make_memory(wl, "v", g, 0, 1, nT)[0]) for g in range(wl.G)])
     rk = np.stack([widen(synth.make_ring_prefill(wl, "k", l, 0, 1)[0]) for l in range(wl.L)])
     rv = np.stack([widen(synth.make_ring_prefill(wl, "v", l, 0, 1)[0]) for l in range(wl.L)])
     s0 = widen(synth.normal(wl.seed, "s_prefill", (wl.d,)))
-    st = state_from_ring(cfg, s0, t0 - 1, rk, rv)
     E = widen(synth.make_e(wl, 0, 1, nT)[0])
-    n = 0
-    t_start = time.perf_counter()
-    while True:
-        st = orc.transition(st, E[st.pos], mem)
-        orc.logits(st.s)
-        n += 1
-        el = time.perf_counter() - t_start
-        if el >= budget_s or n >= 60:
-            break
-    return {"value": n / el, "unit": "transitions/s", "cores": int(cores), "kind": "oracle",
-            "sample": "float64 oracle, 1 sequence x %d transitions (incl. readout) at t=%d..%d from a "
-                      "pre-filled state, %.1f s" % (n, t0, t0 + n - 1, el)}
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+
+    def leg(budget):
+        st = state_from_ring(cfg, s0, t0 - 1, rk, rv, dtype=np.float32)
+        n = 0
+        t_start = time.perf_counter()
+        while True:
+            st = orc.transition(st, E[st.pos], mem)
+            orc.logits(st.s)
+            n += 1
+            el = time.perf_counter() - t_start
+            if el >= budget or n >= 60:
+                return n, el
+
+    n_all, el_all = leg(budget_s / 2)
+    with threadpool_limits(limits=1):
+        n_one, el_one = leg(budget_s / 2)
+    return {"value": n_all / el_all, "unit": "transitions/s", "cores": int(threads), "kind": "oracle",
+            "value_1_thread": n_one / el_one, "cpu_model": _cpu_model(), "host_cpus": os.cpu_count(),
+            "sample": "float32 oracle, 1 sequence, transitions (incl. readout) from a pre-filled state at "
+                      "t=%d: %d in %.1f s on %d BLAS threads, %d in %.1f s on 1 thread"
+                      % (t0, n_all, el_all, threads, n_one, el_one)}
 
 
 def measured_traffic(x_bytes: float):
@@ -145,6 +162,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate", action="store_true",
                     help="also time a plain 4 GiB device copy and read-only sum (achievable HBM rates)")
+    ap.add_argument("--launch", action="append", default=[], metavar="FIELD=VALUE",
+                    help="launch option of the context (rlt_dbg_launch field, for tuning sweeps)")
     ap.add_argument("--mode", choices=("step", "memory_prefill", "backward"), default="step",
                     help="step: the decoder transition (default); memory_prefill: token-parallel "
                          "construction of the encoder memory of the whole batch; backward: full-BPTT "
@@ -182,7 +201,8 @@ def main():
     log("weights generated in %.1fs" % (time.perf_counter() - tg))
     cfg = ModelConfig(L=wl.L, d=wl.d, H=wl.H, dh=wl.dh, W=wl.W, G=wl.G, F=wl.F, V=wl.V, dtype=wl.dtype,
                       merge=wl.merge, alpha=wl.alpha, eps=wl.eps, rope_theta=wl.rope_theta, pos=wl.pos)
-    dec = Decoder(cfg, raw, max_rows=B, max_ctx=T)
+    launch = {k: int(v) for k, v in (a.split("=", 1) for a in args.launch)}
+    dec = Decoder(cfg, raw, max_rows=B, max_ctx=T, launch=launch or None)
     st = DecoderState(cfg, B)
     gen = torch.Generator(device=dev)
     gen.manual_seed(wl.seed)
@@ -288,7 +308,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "L_D": wl.L, "d": wl.d, "heads": "%dx%d" % (wl.H, wl.dh), "W": wl.W,
                    "G": wl.G, "ffn": wl.F, "vocab": wl.V, "batch": B, "T": T,
-                   "timed_positions": [t_first, t_first + K - 1], "hipgraph": graph},
+                   "timed_positions": [t_first, t_first + K - 1], "hipgraph": graph,
+                   **({"launch": launch} if launch else {})},
         "roofline": roof,
         "step_roofline": {"algorithmic_bytes": int(sb["total"]),
                           "achieved_GBs": round(sb["total"] / (ms_step / 1e3) / 1e9, 1),

@@ -171,7 +171,9 @@ enum { RLT_STEP_GRAPH = 1,  /* capture the step in a hipGraph on the first
                                row's pending token [RLT App. A.2] */ };
 typedef struct rlt_step_io {
   int32_t n;                 /* rows in this call, 0 < n <= max_rows */
-  const int32_t* rows;       /* [n] distinct state rows */
+  const int32_t* rows;       /* [n] distinct state rows; a row outside 0..B_cap-1 or
+                                named by more than one slot is a device-detected
+                                RLT_EINVAL and those slots are skipped */
   const void* e;             /* [n][d] e_t of the token each row consumes */
   rlt_memory mem;
   const int32_t* consume_tok;  /* [n] id of the consumed token, or NULL; must
@@ -266,7 +268,12 @@ int rlt_init_state(rlt_ctx* ctx, rlt_state* st, const int32_t* rows, int32_t n, 
                    void* stream);
 
 /* One transition F_t for each listed row, t = pos[row] + 1, then the
- * readout and optional scoring/sampling from s_t. Advances pos[row]. */
+ * readout and optional scoring/sampling from s_t. Advances pos[row].
+ * A row's results do not depend on the other rows of the call or their
+ * order (bit for bit within one context: every reduction order is fixed by
+ * the config and the context's capacities, not by n) [RLT §3.1 Prop. 3.1,
+ * §4.1]. For bf16 contexts without the operand-order weight copy this holds
+ * among calls of at most 32 rows and among calls of more than 32 rows. */
 int rlt_decoder_step(rlt_ctx* ctx, rlt_state* st, const rlt_step_io* io, void* stream);
 
 /* See rlt_replay_io. Synchronises the stream once at the start (upload of
@@ -278,12 +285,17 @@ int rlt_score_logprobs(rlt_ctx* ctx, const rlt_score_io* io, void* stream);
 /* Wait for `stream`, then return (and clear) any device-detected error. */
 int rlt_sync_error(rlt_ctx* ctx, void* stream);
 
-/* Rebuild the context's operand-order copy of the matrix weights (see
- * rlt_create) from the caller's weights, on `stream`; a no-op for contexts
- * without the copy. Needed after the caller changes weight values in place
- * (an optimiser step on the gradients of rlt_replay_backward); the pointers
- * themselves are fixed at rlt_create. */
-int rlt_refresh_weights(rlt_ctx* ctx, void* stream);
+/* The caller changed weight values in place (an optimiser step on the
+ * gradients of rlt_replay_backward): states computed under the old values no
+ * longer hold the model's state [RLT §5.4; App. A.4 replays under the current
+ * parameters]. This rebuilds the context's operand-order copy of the matrix
+ * weights (see rlt_create) from the caller's weights, on `stream` (nothing to
+ * rebuild for contexts without the copy), and makes weights_version the
+ * context's version: states and snapshots carrying any other version are then
+ * refused with RLT_ESTALE until re-initialised under the new version. The
+ * pointers themselves are fixed at rlt_create. weights_version must differ
+ * from the context's current version (else RLT_EINVAL, nothing done). */
+int rlt_refresh_weights(rlt_ctx* ctx, uint64_t weights_version, void* stream);
 
 /* Log of the trajectory importance weight prod_i r_i [RLT §5.3, text after
  * eq. (5.5)] of B sequences: out[b] = sum over t = split_host[b] ..

@@ -1,8 +1,9 @@
 /*
- * rlt_debug.h -- test-only entry point for kernel-level parity checks of the
+ * rlt_debug.h -- test and benchmark hooks: kernel-level parity checks of the
  * library's matrix-product kernel (the kernel behind every projection of
  * "Recurrent Looped Transformer" §2.5 eqs. (2.9)-(2.16) and the readout of
- * §2.3 eq. (2.6)). Not part of the method's interface.
+ * §2.3 eq. (2.6)), launch options, per-class timing. Not part of the
+ * method's interface.
  */
 #ifndef RLT_DEBUG_H
 #define RLT_DEBUG_H
@@ -32,6 +33,27 @@ int rlt_dbg_gemm(rlt_ctx* ctx, const void* A, const void* W, int32_t M, int32_t 
  * multiple of 64, K <= max(2 * d_model, d_ffn). */
 int rlt_dbg_gemm_packed(rlt_ctx* ctx, const void* A, const void* W, int32_t M, int32_t N, int32_t K, float* out,
                         void* stream);
+
+/* Launch options of a context, for tests and tuning sweeps. A field left 0
+ * keeps the library's choice, which depends on the config and the context's
+ * capacities (max_rows, max_ctx) only. Fields that change a reduction order
+ * (the attention fields) change the low bits of results. */
+typedef struct rlt_dbg_launch {
+  int32_t xattn_chunk;  /* memory positions per cross-attention partial, 16 .. 4096
+                           (more than one chunk per row: partials merged by a combine kernel) */
+  int32_t swa_hpw;      /* attention heads per SWA workgroup (ignored if invalid) */
+  int32_t xattn_hpw;    /* attention heads per cross-attention workgroup (ignored if invalid) */
+  int32_t fused_rows;   /* bf16: calls of at most this many rows (<= 32) run the persistent
+                           step kernel (one launch, grid barriers between phases) */
+  int32_t no_packed;    /* 1: no operand-order weight copy (bf16 products on the other tiles) */
+  int32_t one_term;     /* 1: the operand-order products take their activations as one bf16
+                           term (the other tiles always do) instead of two (value rounded,
+                           then its rounding remainder): lower precision, for comparisons */
+} rlt_dbg_launch;
+
+/* rlt_create with launch options (opt must not be NULL). */
+int rlt_dbg_create(const rlt_config* cfg, const rlt_weights* w, int32_t max_rows, int32_t max_ctx,
+                   const rlt_dbg_launch* opt, rlt_ctx** out);
 
 /* Kernel classes for the timing hook below. */
 enum {

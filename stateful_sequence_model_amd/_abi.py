@@ -101,6 +101,11 @@ class rlt_backward_io(C.Structure):
                 ("dmem_stride_b", i64), ("dmem_stride_t", i64)]
 
 
+class rlt_dbg_launch(C.Structure):
+    _fields_ = [("xattn_chunk", i32), ("swa_hpw", i32), ("xattn_hpw", i32), ("fused_rows", i32),
+                ("no_packed", i32), ("one_term", i32)]
+
+
 _lib = None
 
 # name -> (restype, argtypes)
@@ -114,7 +119,7 @@ _SIGS = {
     "rlt_replay_sequence": (C.c_int, [P, C.POINTER(rlt_state), C.POINTER(rlt_replay_io), P]),
     "rlt_score_logprobs": (C.c_int, [P, C.POINTER(rlt_score_io), P]),
     "rlt_sync_error": (C.c_int, [P, P]),
-    "rlt_refresh_weights": (C.c_int, [P, P]),
+    "rlt_refresh_weights": (C.c_int, [P, u64, P]),
     "rlt_trajectory_log_ratio": (C.c_int, [P, i32, P, P, P, i64, P, i64, P, P]),
     "rlt_snapshot_bytes": (C.c_int, [C.POINTER(rlt_config), C.POINTER(C.c_size_t)]),
     "rlt_state_snapshot": (C.c_int, [P, C.POINTER(rlt_state), P, i32, P, P]),
@@ -123,6 +128,8 @@ _SIGS = {
     "rlt_memory_prefill": (C.c_int, [P, C.POINTER(rlt_memory_weights), C.POINTER(rlt_memory), i32, i32, P, P, i64,
                                      i64, P]),
     "rlt_replay_backward": (C.c_int, [P, C.POINTER(rlt_backward_io), C.POINTER(rlt_grads), P]),
+    "rlt_dbg_create": (C.c_int, [C.POINTER(rlt_config), C.POINTER(rlt_weights), i32, i32,
+                                 C.POINTER(rlt_dbg_launch), C.POINTER(P)]),
     "rlt_dbg_gemm": (C.c_int, [P, P, P, i32, i32, i32, P, P]),
     "rlt_dbg_gemm_packed": (C.c_int, [P, P, P, i32, i32, i32, P, P]),
     "rlt_dbg_profile": (C.c_int, [P, i32]),
@@ -170,6 +177,13 @@ def rlt_create(cfg: rlt_config, w: rlt_weights, max_rows: int, max_ctx: int) -> 
     return h.value
 
 
+def rlt_dbg_create(cfg: rlt_config, w: rlt_weights, max_rows: int, max_ctx: int, opt: rlt_dbg_launch) -> int:
+    h = P()
+    check(lib().rlt_dbg_create(C.byref(cfg), C.byref(w), max_rows, max_ctx, C.byref(opt), C.byref(h)),
+          "rlt_dbg_create")
+    return h.value
+
+
 def rlt_destroy(ctx: int) -> None:
     lib().rlt_destroy(ctx)
 
@@ -208,8 +222,8 @@ def rlt_sync_error(ctx: int, stream: int) -> int:
     return lib().rlt_sync_error(ctx, stream)
 
 
-def rlt_refresh_weights(ctx: int, stream: int) -> int:
-    return lib().rlt_refresh_weights(ctx, stream)
+def rlt_refresh_weights(ctx: int, version: int, stream: int) -> int:
+    return lib().rlt_refresh_weights(ctx, version, stream)
 
 
 def rlt_trajectory_log_ratio(ctx: int, B: int, len_host, split_host, logp: int, logp_sb: int, logmu: int,

@@ -305,7 +305,7 @@ __device__ __forceinline__ void swa_body(const AttnArgs& a, int hg, int slot, fl
   merge_groups<T>(acc, G, KPW, s_o, s_ml, [&](int li, int e, float o, float, float L) {
     // element e of lane li: piece e / PE of that lane's two
     const int c = c0 + (li / LPK) * DH + (li % LPK) * PE + (e < PE ? e : h + e - PE);
-    out[a.out_pk ? pk_off(slot, c, d >> 6) : (int64_t)slot * d + c] = from_f<T>(o * (1.f / L));
+    store_op(out, a.out_pk ? pk_off(slot, c, d >> 6) : (int64_t)slot * d + c, a.out_lo, o * (1.f / L));
   });
   // cache insert after every read of this workgroup
   __syncthreads();
@@ -348,7 +348,7 @@ __device__ __forceinline__ void xattn_body(const AttnArgs& a, int hg, int ch, in
     if (a.direct) {
       // the only chunk: what the combine would write for it (weight 2^0 = 1)
       const int c = (hg * a.hpw + li / LPK) * DH + eo;
-      ((T*)a.out)[a.out_pk ? pk_off(slot, c, d >> 6) : (int64_t)slot * d + c] = from_f<T>(o * (1.f / L));
+      store_op((T*)a.out, a.out_pk ? pk_off(slot, c, d >> 6) : (int64_t)slot * d + c, a.out_lo, o * (1.f / L));
       return;
     }
     float* P = a.part + (((int64_t)slot * a.nch + ch) * a.H + hg * a.hpw + li / LPK) * (DH + 2);
@@ -416,7 +416,7 @@ __device__ __forceinline__ void xcombine_body(const AttnArgs& a, int head, int s
     const int e = tid + k * nt;
     if (e < DH) {
       const int col = head * DH + e;
-      out[a.out_pk ? pk_off(slot, col, a.d >> 6) : (int64_t)slot * a.d + col] = from_f<T>(o[k] * inv);
+      store_op(out, a.out_pk ? pk_off(slot, col, a.d >> 6) : (int64_t)slot * a.d + col, a.out_lo, o[k] * inv);
     }
   }
 }

@@ -118,8 +118,8 @@ struct Epi {
       T* o = (T*)a.zb;
       const int64_t ia = a.pk ? pk_off(m, ca, a.d >> 6) : (int64_t)m * a.d + ca;
       const int64_t ib = a.pk ? pk_off(m, cb, a.d >> 6) : (int64_t)m * a.d + cb;
-      o[ia] = from_f<T>(za * p.v.x);
-      o[ib] = from_f<T>(zb * p.v.y);
+      store_op(o, ia, a.lo, za * p.v.x);
+      store_op(o, ib, a.lo, zb * p.v.y);
       return za * za + zb * zb;
     }
     if (a.kind == EPI_QROT) {
@@ -155,8 +155,8 @@ struct Epi {
     T* o = (T*)a.zb;
     const int64_t ia = a.pk ? pk_off(m, ca, a.d >> 6) : (int64_t)m * a.d + ca;
     const int64_t ib = a.pk ? pk_off(m, cb, a.d >> 6) : (int64_t)m * a.d + cb;
-    o[ia] = from_f<T>(za * a.gnext[ca]);
-    o[ib] = from_f<T>(zb * a.gnext[cb]);
+    store_op(o, ia, a.lo, za * a.gnext[ca]);
+    store_op(o, ib, a.lo, zb * a.gnext[cb]);
     return za * za + zb * zb;
   }
 
@@ -205,7 +205,7 @@ struct Epi {
         va *= rs;
         vb *= rs;
         const float act = va * sigmoidf_(va) * vb;
-        ((T*)a.out_k)[a.pk ? pk_off(m, ca, (int)(a.ldo >> 6)) : (int64_t)m * a.ldo + ca] = from_f<T>(act);
+        store_op((T*)a.out_k, a.pk ? pk_off(m, ca, (int)(a.ldo >> 6)) : (int64_t)m * a.ldo + ca, a.lo, act);
         return 0.f;
       }
       case EPI_MGATE: {
@@ -237,10 +237,14 @@ struct Epi {
         z[cb] = zb;
         return produce(m, ca, za, cb, zb);
       }
-      case EPI_STORE_T:
-        ((T*)a.out_k)[(int64_t)m * a.ldo + ca] = from_f<T>(va * rs);
-        ((T*)a.out_k)[(int64_t)m * a.ldo + cb] = from_f<T>(vb * rs);
+      case EPI_STORE_T: {
+        // fragment order ([M][ldo], ldo % 64 == 0) when a.pk: the next product's operand
+        const int64_t ia = a.pk ? pk_off(m, ca, (int)(a.ldo >> 6)) : (int64_t)m * a.ldo + ca;
+        const int64_t ib = a.pk ? pk_off(m, cb, (int)(a.ldo >> 6)) : (int64_t)m * a.ldo + cb;
+        store_op((T*)a.out_k, ia, a.lo, va * rs);
+        store_op((T*)a.out_k, ib, a.lo, vb * rs);
         return 0.f;
+      }
       case EPI_MEMKV: {
         const int t = a.rows.t_row[m];
         if (t <= 0) return 0.f;

@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_tile(GemmArgs g, Epi<uint16_t
   uint16_t(*sA)[BM * LDR] = reinterpret_cast<uint16_t(*)[BM * LDR]>(smem);
   uint16_t(*sW)[BN * LDR] = reinterpret_cast<uint16_t(*)[BN * LDR]>(smem + 2 * BM * LDR * 2);
   __shared__ float s_rstd[BM];
-  __shared__ float s_part[256];
+  __shared__ float s_part[4 * BM];
   // XCD-aware order: consecutive workgroup ids run on the 8 XCDs in turn, so
   // id b maps to tile (b % 8) * (T / 8) + b / 8 (ids past 8 * (T / 8) map to
   // themselves), m-tile fastest: the row tiles of one weight slice share an L2
@@ -263,20 +263,27 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_tile(GemmArgs g, Epi<uint16_t
 // PRE: the epilogue reads memory (residual, gains, rotary table) and loads it
 // before the K loop (registers that would otherwise halve the occupancy of
 // the larger tiles).
-// NW = 8 (with 4 chunks in flight per wave) serves the smallest tile when it
-// needs at most one workgroup per compute unit: a compute unit holds only so
-// many loads in flight, and with few column tiles (64 workgroups for a
-// 2048-wide product at one row) the weights stream faster with twice the
-// waves per workgroup.
+// NW = 8 (with 4 chunks in flight per wave for the smallest tile) serves the
+// products of at most 256 column pairs: a compute unit holds only so many
+// loads in flight, and with few column tiles (64 workgroups for a 2048-wide
+// product at one row) the weights stream faster with twice the waves per
+// workgroup. NW is a function of the product's width only: it fixes the
+// order in which the K chunks are summed.
+// TWO: the activations carry a second bf16 term at A + a_lo (the rounding
+// remainder of the first): each step multiplies the first term, then the
+// second, into the same accumulator, so the product sees its float32 input to
+// about 16 significant bits while the weights stay bf16.
 // grid: 8 * mtiles * ceil(ntiles / 8); block 64 NW.
-template <int RB, int CB, bool PRE, int NW>
+template <int RB, int CB, bool PRE, int NW, bool TWO>
 __global__ __launch_bounds__(64 * NW) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16_t> epi) {
-  constexpr int R = 32 * RB, PF = NW == 8 && RB * CB == 1 ? 4 : 2, NT = 64 * NW;
+  // chunks in flight per wave (the two-term 1 x 1 tile keeps three: four
+  // would spill)
+  constexpr int R = 32 * RB, PF = NW == 8 && RB * CB == 1 ? (TWO ? 3 : 4) : 2, NT = 64 * NW;
   constexpr int TILE = RB * CB * 16 * 64;  // floats of one wave's partial tile
   static_assert((R * CB * 16) % NT == 0, "epilogue items per thread");
   __shared__ float red[NW * TILE];
   __shared__ float s_rstd[R];
-  __shared__ float s_part[NT];  // RowRstd uses the first 256; the rest keeps stray writes in bounds
+  __shared__ float s_part[4 * R];
   const int mtiles = (g.M + R - 1) / R, ntiles = g.npairs / CB;
   const int b = blockIdx.x, q = b >> 3;
   const int mt = q % mtiles, nt = 8 * (q / mtiles) + (b & 7);
@@ -291,7 +298,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16
 #pragma unroll
   for (int c = 0; c < CB; ++c) wp[c] = (const uint16_t*)g.Wp + ((int64_t)(nt * CB + c) * nchunk * 256 + lane) * 8;
   const bool norm_here = g.ssq_in != nullptr;
-  RowRstd<R> rr(g, norm_here ? m0 : 0);
+  RowRstd<R, NT> rr(g, norm_here ? m0 : 0);
   // this thread's epilogue items (16 consecutive threads per row and pair)
   // and the values their epilogue reads, loaded now, in flight with the K loop
   constexpr int NI = R * CB * 16 / NT;
@@ -306,7 +313,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16
     pre[j] = m0 + row < g.M ? epi.pre(m0 + row, ba * 16 + c16, bb * 16 + c16) : typename Epi<uint16_t>::Pre{};
   }
   const int n = (nchunk - wave + NW - 1) / NW;  // chunks of this wave
-  bf16x8_t ra[PF][RB][4], rw[PF][CB][4];
+  bf16x8_t ra[PF][RB][4], rw[PF][CB][4], rl[TWO ? PF : 1][RB][4];
   f32x16_t acc[RB][CB];
 #pragma unroll
   for (int r = 0; r < RB; ++r)
@@ -323,6 +330,13 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16
     for (int r = 0; r < RB; ++r)
 #pragma unroll
       for (int st = 0; st < 4; ++st) ra[slot][r][st] = live[r] ? load8(ap[r] + off + st * 512) : bf16x8_t{};
+    if (TWO) {
+#pragma unroll
+      for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+          rl[TWO ? slot : 0][r][st] = live[r] ? load8(ap[r] + g.a_lo + off + st * 512) : bf16x8_t{};
+    }
 #pragma unroll
     for (int c = 0; c < CB; ++c)
 #pragma unroll
@@ -334,8 +348,12 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16
 #pragma unroll
       for (int r = 0; r < RB; ++r)
 #pragma unroll
-        for (int c = 0; c < CB; ++c)
+        for (int c = 0; c < CB; ++c) {
           acc[r][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[slot][r][st], rw[slot][c][st], acc[r][c], 0, 0, 0);
+          if (TWO)
+            acc[r][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rl[TWO ? slot : 0][r][st], rw[slot][c][st], acc[r][c],
+                                                               0, 0, 0);
+        }
   };
 #pragma unroll
   for (int p = 0; p < PF; ++p)
@@ -490,23 +508,38 @@ void launch_gemm(int dtype, const GemmArgs& g0, const EpiArgs& e, hipStream_t s)
     bad.kind = PH_INVALID;  // not runnable by the persistent kernel: the recording is dropped
     if (record_phase(bad)) return;
     Epi<uint16_t> epi{e};
+    const bool two = g.a_lo != 0;
+    // The waves split the K loop (wave w sums chunks w, w + NW, ...; the
+    // partials are added in wave order), so NW fixes the summation order and
+    // is chosen from the product's width alone, never from the call's rows:
+    // eight waves for products of at most 256 column pairs (8192 columns),
+    // which at the decoder's batch sizes need about one workgroup per compute
+    // unit (the 2048-wide products at 1-512 rows, Q/K/V at 1-128), four for
+    // wider ones (gate/up at 5504: 8 waves measured 15.6 vs 13.0 us at 344
+    // workgroups; the vocabulary).
+    const bool w8 = g.npairs <= 256;
+    // the 64 x 2 tile would spill registers with eight waves and two terms:
+    // 64 x 1 then (the tile shape leaves every output's arithmetic unchanged)
+    if (two && w8) g.cb = 1;
     const int mtiles = (g.M + 32 * g.rb - 1) / (32 * g.rb), ntiles = g.npairs / g.cb;
     dim3 grid(8 * mtiles * ((ntiles + 7) / 8));
     // (the Q/K/V product's 64 x 2 tile measured slower with it, 26.4 vs 19.9
     // us at 128 rows, and slower again with table lookups in its epilogue)
     const bool pre = e.kind == EPI_RESID || e.kind == EPI_QROT;
-#define RLT_PK(RB_, CB_, NW_)                                                                          \
-  do {                                                                                                 \
-    if (pre) hipLaunchKernelGGL((k_gemm_bf16_pk<RB_, CB_, true, NW_>), grid, dim3(64 * NW_), 0, s, g, epi); \
-    else hipLaunchKernelGGL((k_gemm_bf16_pk<RB_, CB_, false, NW_>), grid, dim3(64 * NW_), 0, s, g, epi);    \
+#define RLT_PK2(RB_, CB_, PRE_, NW_)                                                                    \
+  do {                                                                                                  \
+    if (two) hipLaunchKernelGGL((k_gemm_bf16_pk<RB_, CB_, PRE_, NW_, true>), grid, dim3(64 * NW_), 0, s, g, epi); \
+    else hipLaunchKernelGGL((k_gemm_bf16_pk<RB_, CB_, PRE_, NW_, false>), grid, dim3(64 * NW_), 0, s, g, epi);    \
   } while (0)
-    // eight waves where the call needs at most one workgroup per compute
-    // unit (8 waves at 344 workgroups of 32 x 1: 15.6 vs 13.0 us)
-    const bool w8 = grid.x <= 256;
+#define RLT_PK(RB_, CB_, NW_)              \
+  do {                                     \
+    if (pre) RLT_PK2(RB_, CB_, true, NW_); \
+    else RLT_PK2(RB_, CB_, false, NW_);    \
+  } while (0)
     if (g.rb == 2 && g.cb == 2) {
-      // eight waves load the epilogue's values after the K loop (prefetched
-      // they would spill)
-      if (w8) hipLaunchKernelGGL((k_gemm_bf16_pk<2, 2, false, 8>), grid, dim3(512), 0, s, g, epi);
+      // eight waves (one term only) load the epilogue's values after the K
+      // loop (prefetched they would spill)
+      if (w8) hipLaunchKernelGGL((k_gemm_bf16_pk<2, 2, false, 8, false>), grid, dim3(512), 0, s, g, epi);
       else RLT_PK(2, 2, 4);
     } else if (g.rb == 2) {
       if (w8) RLT_PK(2, 1, 8);
@@ -516,6 +549,7 @@ void launch_gemm(int dtype, const GemmArgs& g0, const EpiArgs& e, hipStream_t s)
       else RLT_PK(1, 1, 4);
     }
 #undef RLT_PK
+#undef RLT_PK2
     return;
   }
   const int MB = g.mb;

@@ -15,7 +15,8 @@ static constexpr int ERR_INVAL = -1;    // RLT_EINVAL
 
 // t = pos + 1 per slot; rows whose memory is shorter than t, or whose
 // consumed token differs from a recorded pending token, get t = 0 (skipped)
-// and raise the error word.
+// and raise the error word. Each slot also counts its row in a.claim (zero
+// between calls): the merge preparation skips rows counted more than once.
 __global__ void k_prestep(MiscArgs a) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= a.n) return;
@@ -25,6 +26,7 @@ __global__ void k_prestep(MiscArgs a) {
     *(volatile int*)a.err = ERR_INVAL;
     return;
   }
+  if (a.claim) atomicAdd(a.claim + row, 1);
   const int t = a.pos[row] + 1;
   int code = 0;
   if (t > a.max_t || (a.mem_len && t > a.mem_len[row])) code = ERR_PREFIX;
@@ -49,9 +51,10 @@ __global__ void k_replay_rows(const int* rows, int n, int tick, int* t_row, cons
 __global__ void k_poststep(PostArgs a) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= a.n) return;
+  const int row = a.rows.rows[i];
+  if (a.claim && row >= 0 && row < a.B_cap) a.claim[row] = 0;  // ready for the next call
   const int t = a.rows.t_row[i];
   if (t <= 0) return;
-  const int row = a.rows.rows[i];
   a.pos[row] = t;
   a.pending[row] = a.next_tok ? a.next_tok[i] : -1;
 }

@@ -3,12 +3,15 @@
 // captured-graph cache. No arithmetic of the method happens here; every
 // step runs in the HIP kernels.
 //
-// Concurrency: rows of one call are independent sequences ("Recurrent
-// Looped Transformer" §4.1), so a call with enough rows is split into two
-// row ranges whose transitions run on two streams (the caller's and one
-// the context owns), each with its own workspace, joined with events before
-// the bookkeeping kernel. The bandwidth-bound attention of one range then
-// overlaps the short matrix-product and normalisation kernels of the other.
+// Batch invariance: rows of one call are independent sequences ("Recurrent
+// Looped Transformer" §4.1) and the report's exact-replay arguments (§3.1
+// Prop. 3.1, App. A.4) assume deterministic operations. Every launch shape
+// that fixes a reduction order (attention heads per workgroup and chunk
+// length, the waves that split a product's K loop, K splits) is chosen from
+// the configuration and the context's capacities (max_rows, max_ctx) only,
+// never from the number of rows in a call, so a row's results do not depend
+// on which other rows share its call. Shapes that leave the arithmetic of
+// each output unchanged (row and column tiling) still follow the call.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -48,12 +51,7 @@ int fail(int code, const char* fmt, ...) {
 
 size_t elt_size(int dtype) { return dtype == RLT_BF16 ? 2 : 4; }
 
-int env_int(const char* name, int dflt) {
-  const char* v = std::getenv(name);
-  return (v && *v) ? std::atoi(v) : dflt;
-}
-
-// Per-stream scratch of one transition pipeline (rows indexed by slot).
+// Scratch of one transition pipeline (rows indexed by slot).
 struct Workspace {
   void *X, *kc, *vc, *o, *h, *act;
   float *gbuf, *z, *q, *qm, *part, *partial, *logits;
@@ -72,15 +70,12 @@ struct rlt_ctx {
   const void *merge_wg, *merge_ws, *merge_ws_u, *merge_ws_v, *w_out;
   std::vector<const float*> norm_s, norm_m, norm_d;
   std::vector<const void*> wq, wk, wv, wo, wqm, wom, w_gate, w_up, w_down;
-  // capacities and launch shapes
+  // capacities and the launch shapes that fix reduction orders (chosen at
+  // create from the config and the capacities; see the note at the top)
   int max_rows, max_ctx, M_pad;
-  int chunk, nch;      // cross-attention chunk forced for every call (0: per call), partial slots
-  int hpw, hpw_x;      // heads per workgroup: SWA (the most a call uses), cross-attention
-  bool hpw_forced, hpw_x_forced;  // hpw / hpw_x for every call (tuning sweeps)
-  int gemm_mb_force;   // 0 or 1/2/4 (tuning)
-  int gemm_s_force;    // 0 or forced K split (tuning)
-  int gemm_wide;       // wide-tile products for calls above 32 rows (1 = on)
-  int split_min_rows;  // calls with at least this many rows run as two streams (0 = never)
+  int chunk, nch;      // cross-attention positions per partial, partial slots per row
+  int hpw, hpw_x;      // attention heads per workgroup: SWA, cross-attention
+  int narrow_rows;     // row count whose K splits the narrow product tile uses
   int gemm_target;     // K split target of the persistent step's products (0: stand-alone kernels)
   size_t partial_cap;  // floats per workspace
   // bf16: the decoder's weights in fragment order (a
@@ -90,6 +85,16 @@ struct rlt_ctx {
   bool pk_ready;
   std::vector<void*> pk_qkv, pk_wo, pk_wqm, pk_wom, pk_gu, pk_down;
   void* pk_out;
+  void *pk_mwg, *pk_mws, *pk_mws_u, *pk_mws_v;  // merge products (null: not packed)
+  // the operand-order products' activations carry two bf16 terms (x rounded,
+  // then the rounding remainder) unless one_term; the second term of each
+  // fragment-order buffer lies this many elements after the first
+  bool one_term;
+  int64_t lo_X, lo_o, lo_h, lo_act;
+  // duplicate-row detection of rlt_decoder_step: per state row, the number
+  // of slots of the current call naming it (zero between calls)
+  int* claim;
+  int claim_cap;
   std::vector<std::pair<GemmArgs, void*>> pk_all;
   // persistent step for calls of at most fused_rows rows (bf16; 0 = off)
   int fused_rows;
@@ -115,9 +120,7 @@ struct rlt_ctx {
   double* inv_freq;
   float2* rope_tab;  // [rope_tmax + 1][d_head / 2] rotary (cos, sin)
   int rope_tmax;
-  Workspace ws[2];
-  hipStream_t aux;
-  hipEvent_t ev_fork, ev_join;
+  Workspace ws[1];
   // pinned host staging for replay schedules
   int* host_stage;
   // error word: host-mapped pinned memory written by kernels
@@ -274,9 +277,7 @@ extern "C" void rlt_destroy(rlt_ctx* c) {
   for (auto& e : c->fused_cache) (void)hipFree(e.dev);
   if (c->graph_exec) (void)hipGraphExecDestroy(c->graph_exec);
   if (c->graph) (void)hipGraphDestroy(c->graph);
-  if (c->aux) (void)hipStreamDestroy(c->aux);
-  if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
-  if (c->ev_join) (void)hipEventDestroy(c->ev_join);
+  if (c->claim) (void)hipFree(c->claim);
   if (c->err_host) (void)hipHostFree(c->err_host);
   if (c->host_stage) (void)hipHostFree(c->host_stage);
   for (hipEvent_t e : c->prof_ev) (void)hipEventDestroy(e);
@@ -286,10 +287,11 @@ extern "C" void rlt_destroy(rlt_ctx* c) {
 static int alloc_workspace(rlt_ctx* c, Workspace& w, bool full) {
   const rlt_config& cf = c->cfg;
   const size_t M = c->M_pad, es = c->es, d = cf.d_model, F = cf.d_ffn;
+  const size_t nt = c->dt == 1 ? 2 : 1;  // bf16 product operands: room for a second term
   int rc = 0;
-  if ((rc = dev_alloc(&w.X, M * 2 * d * es)) || (rc = dev_alloc(&w.kc, M * d * es)) ||
-      (rc = dev_alloc(&w.vc, M * d * es)) || (rc = dev_alloc(&w.o, M * d * es)) ||
-      (rc = dev_alloc(&w.h, M * d * es)) || (rc = dev_alloc(&w.act, M * F * es)) ||
+  if ((rc = dev_alloc(&w.X, nt * M * 2 * d * es)) || (rc = dev_alloc(&w.kc, M * d * es)) ||
+      (rc = dev_alloc(&w.vc, M * d * es)) || (rc = dev_alloc(&w.o, nt * M * d * es)) ||
+      (rc = dev_alloc(&w.h, nt * M * d * es)) || (rc = dev_alloc(&w.act, nt * M * F * es)) ||
       (rc = dev_alloc(&w.gbuf, M * d * 4)) || (rc = dev_alloc(&w.z, M * d * 4)) ||
       (rc = dev_alloc(&w.q, M * d * 4)) || (rc = dev_alloc(&w.qm, M * d * 4)) ||
       (rc = dev_alloc(&w.part, M * (size_t)c->nch * cf.n_heads * (cf.d_head + 2) * 4)) ||
@@ -299,22 +301,33 @@ static int alloc_workspace(rlt_ctx* c, Workspace& w, bool full) {
     return rc;
   // rows beyond a call's n are read by the MFMA tiles and discarded: keep
   // them finite
-  if (hipMemset(w.X, 0, M * 2 * d * es) != hipSuccess || hipMemset(w.o, 0, M * d * es) != hipSuccess ||
-      hipMemset(w.h, 0, M * d * es) != hipSuccess || hipMemset(w.act, 0, M * F * es) != hipSuccess)
+  if (hipMemset(w.X, 0, nt * M * 2 * d * es) != hipSuccess || hipMemset(w.o, 0, nt * M * d * es) != hipSuccess ||
+      hipMemset(w.h, 0, nt * M * d * es) != hipSuccess || hipMemset(w.act, 0, nt * M * F * es) != hipSuccess)
     return fail(RLT_EHIP, "workspace initialisation failed");
   return RLT_OK;
 }
 
-// Fragment-order copies of the decoder's product weights (bf16 contexts): one
-// per product as the transition calls it
-// (Q/K/V together, gate/up together). Weights not 16-byte aligned leave the
-// copies unbuilt and those calls on the LDS tile.
+// Fragment-order copies of the transition's product weights (bf16 contexts):
+// one per product as the transition calls it (Q/K/V together, gate/up
+// together), the merge's included. Weights not 16-byte aligned leave the
+// copies unbuilt and those calls on the other tiles.
 static int build_packed(rlt_ctx* c) {
   const rlt_config& cf = c->cfg;
-  const int d = cf.d_model, F = cf.d_ffn, L = cf.n_layers;
+  const int d = cf.d_model, F = cf.d_ffn, L = cf.n_layers, k = cf.merge_rank;
+  const bool gated = cf.merge_kind == RLT_MERGE_GATED;
+  const bool vec_gate = !gated || cf.merge_gate == RLT_GATE_VECTOR;
   std::vector<const void*> all = {c->w_out};
   for (auto* v : {&c->wq, &c->wk, &c->wv, &c->wo, &c->wqm, &c->wom, &c->w_gate, &c->w_up, &c->w_down})
     all.insert(all.end(), v->begin(), v->end());
+  if (vec_gate) all.push_back(c->merge_wg);
+  if (gated) {
+    if (k > 0) {
+      all.push_back(c->merge_ws_u);
+      all.push_back(c->merge_ws_v);
+    } else {
+      all.push_back(c->merge_ws);
+    }
+  }
   for (const void* p : all)
     if ((uintptr_t)p % 16) return RLT_OK;
   auto pack = [&](std::initializer_list<const void*> W, int seg_rows, int K, int pairing, void** out) -> int {
@@ -346,6 +359,12 @@ static int build_packed(rlt_ctx* c) {
       break;
   }
   if (!rc) rc = pack({c->w_out}, cf.vocab, d, PAIR_PLAIN, &c->pk_out);
+  // merge [eqs. (2.9)-(2.11)]: W_g over [e; r] (or [e; s]), W_s (or V then
+  // U of a low-rank W_s; U needs a rank that is a multiple of 64)
+  if (!rc && vec_gate) rc = pack({c->merge_wg}, d, 2 * d, PAIR_PLAIN, &c->pk_mwg);
+  if (!rc && gated && k == 0) rc = pack({c->merge_ws}, d, d, PAIR_PLAIN, &c->pk_mws);
+  if (!rc && gated && k > 0) rc = pack({c->merge_ws_v}, k, d, PAIR_PLAIN, &c->pk_mws_v);
+  if (!rc && gated && k > 0 && k % 64 == 0) rc = pack({c->merge_ws_u}, d, k, PAIR_PLAIN, &c->pk_mws_u);
   if (rc) return rc;
   HIP_TRY(hipGetLastError());
   HIP_TRY(hipDeviceSynchronize());
@@ -353,15 +372,44 @@ static int build_packed(rlt_ctx* c) {
   return RLT_OK;
 }
 
-extern "C" int rlt_refresh_weights(rlt_ctx* c, void* stream) {
+extern "C" int rlt_refresh_weights(rlt_ctx* c, uint64_t weights_version, void* stream) {
   if (!c) return fail(RLT_EINVAL, "null context");
+  if (weights_version == c->cfg.weights_version)
+    return fail(RLT_EINVAL, "changed weights need a new weights_version (the context has %llu)",
+                (unsigned long long)weights_version);
   for (auto& e : c->pk_all) launch_pack_weights(e.first, e.second, (hipStream_t)stream);
   HIP_TRY(hipGetLastError());
+  c->cfg.weights_version = weights_version;
   return RLT_OK;
 }
 
-extern "C" int rlt_create(const rlt_config* cfg, const rlt_weights* w, int32_t max_rows, int32_t max_ctx,
-                          rlt_ctx** out) {
+// Attention heads per workgroup for calls of up to `rows` rows: the widest
+// valid group h, narrowed (down to one head) while such a call would have
+// fewer than `want` workgroups per key range, so that contexts for small
+// calls spread their keys over more compute units. SWA: 256 (batch 1 at
+// t ~ 2048: 4.43 -> 4.09 ms per step, batch 16: 6.25 -> 5.91); cross-
+// attention, whose chunks multiply its workgroups: 128 (narrower measured
+// slower at 16 rows, 6.05 vs 5.92 ms, and faster at one row, 4.02 vs 4.09).
+static int narrow_hpw(const rlt_config& cf, int dt, int h, int rows, int want) {
+  for (int k = h - 1; k >= 1 && (int64_t)rows * (cf.n_heads / h) < want; --k)
+    if (hpw_ok(cf, dt, k)) h = k;
+  return h;
+}
+
+// Memory positions per cross-attention partial for calls of up to `rows`
+// rows: few long workgroups stream faster than many short ones (each pays a
+// start-up latency and a merge), so the chunk grows with the rows while the
+// grid still fills the chip at mid context (reference depth, t = 2048: 128
+// rows 14.7 ms per step with 2048 against 15.4 with 512; 64 rows best at
+// 1024, 16 at 512, 1 at 256). One chunk of the whole context up to 4096
+// positions when there are enough workgroups: no combine launch.
+static int pick_chunk(int wg_per_chunk, int max_ctx) {
+  if (wg_per_chunk >= 1024) return max_ctx <= 4096 ? 4096 : 2048;
+  return wg_per_chunk >= 512 ? 1024 : wg_per_chunk >= 128 ? 512 : 256;
+}
+
+static int create_ctx(const rlt_config* cfg, const rlt_weights* w, int32_t max_rows, int32_t max_ctx,
+                      const rlt_dbg_launch* opt, rlt_ctx** out) {
   int rc = check_config(cfg);
   if (rc) return rc;
   if (!w || !out) return fail(RLT_EINVAL, "null weights or output");
@@ -410,25 +458,22 @@ extern "C" int rlt_create(const rlt_config* cfg, const rlt_weights* w, int32_t m
   c->max_rows = max_rows;
   c->max_ctx = max_ctx;
   c->M_pad = (max_rows + 127) / 128 * 128;
-  // launch shapes (environment overrides exist for tuning sweeps only)
-  // cross-attention chunk: chosen per call (xattn_chunk); the partials buffer
-  // holds the chunk count of the smallest one
-  c->chunk = env_int("RLT_XATTN_CHUNK", 0);  // > 0: every call (tuning sweeps)
-  if (c->chunk != 0 && (c->chunk < 16 || c->chunk > 4096)) c->chunk = 0;
-  c->nch = (max_ctx + (c->chunk ? c->chunk : 256) - 1) / (c->chunk ? c->chunk : 256);
-  c->hpw_forced = env_int("RLT_SWA_HPW", 0) > 0;
-  c->hpw = choose_hpw(*cfg, c->dt, env_int("RLT_SWA_HPW", 0));
-  c->hpw_x_forced = env_int("RLT_XATTN_HPW", 0) > 0;
-  c->hpw_x = choose_hpw(*cfg, c->dt, env_int("RLT_XATTN_HPW", 2));
-  c->gemm_mb_force = env_int("RLT_GEMM_MB", 0);
-  c->gemm_s_force = env_int("RLT_GEMM_S", 0);
-  c->gemm_wide = env_int("RLT_GEMM_WIDE", 1);
-  c->split_min_rows = env_int("RLT_SPLIT_MIN_ROWS", 0);
+  // launch shapes that fix reduction orders: from the config and the
+  // capacities only (batch invariance); `opt` overrides them for tests
+  const rlt_dbg_launch o = opt ? *opt : rlt_dbg_launch{};
+  c->hpw = hpw_ok(*cfg, c->dt, o.swa_hpw) ? o.swa_hpw
+                                           : narrow_hpw(*cfg, c->dt, choose_hpw(*cfg, c->dt, 0), max_rows, 256);
+  c->hpw_x = hpw_ok(*cfg, c->dt, o.xattn_hpw) ? o.xattn_hpw
+                                                : narrow_hpw(*cfg, c->dt, choose_hpw(*cfg, c->dt, 2), max_rows, 128);
+  c->chunk = (o.xattn_chunk >= 16 && o.xattn_chunk <= 4096) ? o.xattn_chunk
+                                                            : pick_chunk(max_rows * (cfg->n_heads / c->hpw_x), max_ctx);
+  c->nch = (max_ctx + c->chunk - 1) / c->chunk;
+  c->narrow_rows = std::min(max_rows, 32);
   c->gemm_target = 0;
-  // Off by default: on MI355X a device-scope grid barrier costs 3.5-8.7 us,
+  // Opt-in only: on MI355X a device-scope grid barrier costs 3.5-8.7 us,
   // so ~15 phases per block make the persistent step slower than the
   // separate kernels at every batch size measured (1-16 rows).
-  c->fused_rows = c->dt == 1 ? std::min(32, std::max(0, env_int("RLT_FUSED_ROWS", 0))) : 0;
+  c->fused_rows = c->dt == 1 ? std::min(32, std::max(0, (int)o.fused_rows)) : 0;
   c->fused_spin = (int64_t)200000000;  // 2 s of the 100 MHz real-time counter
   c->partial_cap = (size_t)8 * c->M_pad * std::max(3 * d, 2 * F);
   const size_t M = c->M_pad;
@@ -449,12 +494,9 @@ extern "C" int rlt_create(const rlt_config* cfg, const rlt_weights* w, int32_t m
   c->rope_tmax = std::min(max_ctx, 65536);  // positions past it compute their angles
   ALLOC(c->rope_tab, (size_t)(c->rope_tmax + 1) * (dh / 2) * sizeof(float2));
 #undef ALLOC
-  for (int i = 0; i < 2; ++i) {
-    if (i == 1 && c->split_min_rows <= 0) break;
-    if ((rc = alloc_workspace(c, c->ws[i], true))) {
-      rlt_destroy(c);
-      return rc;
-    }
+  if ((rc = alloc_workspace(c, c->ws[0], true))) {
+    rlt_destroy(c);
+    return rc;
   }
   std::vector<int> iv(M), ov(M, 1);
   std::iota(iv.begin(), iv.end(), 0);
@@ -471,13 +513,6 @@ extern "C" int rlt_create(const rlt_config* cfg, const rlt_weights* w, int32_t m
     rlt_destroy(c);
     return fail(RLT_EHIP, "rotary table initialisation failed");
   }
-  if (c->split_min_rows > 0 &&
-      (hipStreamCreateWithFlags(&c->aux, hipStreamNonBlocking) != hipSuccess ||
-       hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming) != hipSuccess ||
-       hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming) != hipSuccess)) {
-    rlt_destroy(c);
-    return fail(RLT_EHIP, "auxiliary stream creation failed");
-  }
   if (hipHostMalloc((void**)&c->err_host, sizeof(int), hipHostMallocMapped) != hipSuccess ||
       hipHostGetDevicePointer((void**)&c->err_dev, c->err_host, 0) != hipSuccess) {
     rlt_destroy(c);
@@ -491,9 +526,7 @@ extern "C" int rlt_create(const rlt_config* cfg, const rlt_weights* w, int32_t m
         fused_blocks_per_cu() < 1)
       c->fused_rows = 0;  // no persistent path on this device: separate kernels only
     c->fused_grid = ncu;
-    const int gf = env_int("RLT_FUSED_GRID", 0);
-    if (gf > 0 && gf < ncu) c->fused_grid = gf;
-    c->fused_target = env_int("RLT_FUSED_TARGET", c->fused_grid);
+    c->fused_target = c->fused_grid;
   }
   if (c->fused_rows > 0 && (dev_alloc(&c->fused_sync, 2 * sizeof(unsigned)) != RLT_OK ||
                             hipMemset(c->fused_sync, 0, 2 * sizeof(unsigned)) != hipSuccess)) {
@@ -504,14 +537,31 @@ extern "C" int rlt_create(const rlt_config* cfg, const rlt_weights* w, int32_t m
     rlt_destroy(c);
     return fail(RLT_EHIP, "pinned staging allocation failed");
   }
-  if (c->dt == 1 && d % 64 == 0 && F % 64 == 0 && env_int("RLT_GEMM_PK", 1)) {
+  if (c->dt == 1 && d % 64 == 0 && F % 64 == 0 && !o.no_packed) {
     if ((rc = build_packed(c))) {
       rlt_destroy(c);
       return rc;
     }
   }
+  c->one_term = o.one_term != 0;
+  if (c->pk_ready && !c->one_term) {
+    c->lo_X = (int64_t)M * 2 * d;
+    c->lo_o = c->lo_h = (int64_t)M * d;
+    c->lo_act = (int64_t)M * F;
+  }
   *out = c;
   return RLT_OK;
+}
+
+extern "C" int rlt_create(const rlt_config* cfg, const rlt_weights* w, int32_t max_rows, int32_t max_ctx,
+                          rlt_ctx** out) {
+  return create_ctx(cfg, w, max_rows, max_ctx, nullptr, out);
+}
+
+extern "C" int rlt_dbg_create(const rlt_config* cfg, const rlt_weights* w, int32_t max_rows, int32_t max_ctx,
+                              const rlt_dbg_launch* opt, rlt_ctx** out) {
+  if (!opt) return fail(RLT_EINVAL, "null launch options");
+  return create_ctx(cfg, w, max_rows, max_ctx, opt, out);
 }
 
 // a device-detected error from earlier work, if any (cleared when returned)
@@ -552,10 +602,12 @@ struct Gemm {
 
   // Wp: the weights in fragment order; A is then in fragment order too
   void run(const void* A, int64_t lda, std::initializer_list<const void*> W, int seg_rows, int K, int pairing,
-           int n, EpiArgs e, const float* ssq_in = nullptr, float* ssq_out = nullptr, const void* Wp = nullptr) {
+           int n, EpiArgs e, const float* ssq_in = nullptr, float* ssq_out = nullptr, const void* Wp = nullptr,
+           int64_t a_lo = 0) {
     GemmArgs g{};
     g.A = A;
     g.lda = lda;
+    g.a_lo = Wp ? a_lo : 0;
     int i = 0;
     for (const void* p : W) g.W[i++] = p;
     g.nseg = i;
@@ -586,36 +638,37 @@ struct Gemm {
       else if (wgs(2, 2) >= 160) g.rb = 2, g.cb = 2;
       else if (wgs(2, 1) >= 160) g.rb = 2, g.cb = 1;
       else g.rb = 1, g.cb = 1;
-    } else if (c->dt == 1 && c->gemm_wide && n > 32 && g.npairs % 2 == 0 && K % 64 == 0) {
+    } else if (c->dt == 1 && n > 32 && g.npairs % 2 == 0 && K % 64 == 0) {
       // LDS tile of 128 rows x 64 columns (128 when that still leaves two
       // workgroups per compute unit); K split while each split adds a
       // workgroup per compute unit and keeps at least 8 stages of 64
-      // (measured best for every product shape at 64-256 rows)
-      const int mt = (n + 127) / 128;
+      // (measured best for every product shape at 64-256 rows). The split,
+      // which fixes the summation order, is taken for a call of the
+      // context's capacity (mt_cap row tiles); the column tile follows the call.
+      const int mt = (n + 127) / 128, mt_cap = (std::max(c->max_rows, 33) + 127) / 128;
       const int BN = (g.npairs % 4 == 0 && g.npairs / 2 * mt >= 512) ? 128 : 64;
-      const int tiles = g.npairs / (BN / 32) * mt;
+      const int BN_cap = (g.npairs % 4 == 0 && g.npairs / 2 * mt_cap >= 512) ? 128 : 64;
+      const int tiles = g.npairs / (BN_cap / 32) * mt_cap;
       const int kst = K / 64;
       int S = std::max(1, 256 / tiles);
       S = std::min(S, std::max(1, kst / 8));
-      if (c->gemm_s_force > 0) S = std::min(c->gemm_s_force, kst);
       while (S > 1 && (size_t)S * g.M_pad * g.Nv > c->partial_cap) --S;
       g.wide = BN;
       g.S = S;
       g.kslice = (kst + S - 1) / S * 64;
     } else if (c->dt == 1) {
-      int MB = gemm_row_blocks(n);
-      const int mbf = c->gemm_mb_force;
-      if (mbf == 1 || mbf == 2 || mbf == 4) MB = mbf;
-      const int mt = (n + 16 * MB - 1) / (16 * MB);
-      const int tiles = g.npairs * mt;
+      const int MB = gemm_row_blocks(n);
       // K split: the persistent step fills its grid; a stand-alone kernel
       // splits only while each split still adds a workgroup per compute unit
       // (256 CUs): splitting further leaves workgroups queued behind others
-      // and adds partial traffic, which costs more than the latency it hides
+      // and adds partial traffic, which costs more than the latency it hides.
+      // The split fixes the summation order, so it is taken for a call of
+      // nr = min(max_rows, 32) rows whatever the call's own row count.
+      const int nr = c->narrow_rows, MBr = gemm_row_blocks(nr);
+      const int tiles = g.npairs * ((nr + 16 * MBr - 1) / (16 * MBr));
       int S = c->gemm_target ? std::max(1, (c->gemm_target + tiles - 1) / tiles) : std::max(1, 256 / tiles);
       S = std::min(S, std::max(1, K / 256));             // >= 64 K per wave
-      S = std::min(S, std::max(1, K / (4 * n)));         // partial traffic <= the weights'
-      if (c->gemm_s_force > 0) S = std::min(c->gemm_s_force, std::max(1, K / 128));
+      S = std::min(S, std::max(1, K / (4 * nr)));        // partial traffic <= the weights'
       while (S > 1 && (size_t)S * g.M_pad * g.Nv > c->partial_cap) --S;
       g.S = S;
       g.mb = MB;
@@ -627,40 +680,10 @@ struct Gemm {
   }
 };
 
-// Positions per cross-attention partial for an n-row call: few long
-// workgroups stream faster than many short ones (each pays a start-up
-// latency and a merge), so the chunk grows with the rows while the grid
-// still fills the chip at mid context (measured at reference depth, t = 2048:
-// 128 rows 14.7 ms per step with 2048 against 15.4 with 512; 64 rows best
-// at 1024, 16 at 512, 1 at 256). Chunk boundaries depend only on t and the
-// call's row count.
-// Attention heads per workgroup of an n-row call: the context's width h,
-// narrowed (down to one head) while the call would have fewer than `want`
-// workgroups per key range, so that small calls spread their keys over more
-// compute units. SWA: 256 (batch 1 at t ~ 2048: 4.43 -> 4.09 ms per step,
-// batch 16: 6.25 -> 5.91); cross-attention, whose chunks multiply its
-// workgroups: 128 (narrower measured slower at 16 rows, 6.05 vs 5.92 ms, and
-// faster at one row, 4.02 vs 4.09)
-int narrow_hpw(const rlt_ctx* c, int h, int n, int want) {
-  for (int k = h - 1; k >= 1 && (int64_t)n * (c->cfg.n_heads / h) < want; --k)
-    if (hpw_ok(c->cfg, c->dt, k)) h = k;
-  return h;
-}
-int swa_hpw(const rlt_ctx* c, int n) { return c->hpw_forced ? c->hpw : narrow_hpw(c, c->hpw, n, 256); }
-int xattn_hpw(const rlt_ctx* c, int n) { return c->hpw_x_forced ? c->hpw_x : narrow_hpw(c, c->hpw_x, n, 128); }
-
-int xattn_chunk(const rlt_ctx* c, int n) {
-  if (c->chunk > 0) return c->chunk;
-  const int wg = n * (c->cfg.n_heads / xattn_hpw(c, n));  // workgroups per chunk index
-  // (one chunk of the whole context up to 4096 positions when there are
-  // enough workgroups: no combine launch)
-  if (wg >= 1024) return c->max_ctx <= 4096 ? 4096 : 2048;
-  return wg >= 512 ? 1024 : wg >= 128 ? 512 : 256;
-}
-
 struct StepPlan {
   Rows R;                 // rows / src / t_row (t_row filled by the pre-step)
   int n;
+  int* claim;             // decoder step: per-row slot counts (duplicate rows), else null
   EIn e;
   rlt_memory mem;
   rlt_state* st;
@@ -691,8 +714,12 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
   const bool pk = c->pk_ready && !(c->fused_rows > 0 && n <= c->fused_rows);
   auto pw = [&](const std::vector<void*>& v, int l) -> const void* { return pk ? v[l] : nullptr; };
 
+  // second terms of the fragment-order operands (none off the operand-order path)
+  const int64_t lo_X = pk ? c->lo_X : 0, lo_o = pk ? c->lo_o : 0, lo_h = pk ? c->lo_h : 0,
+                lo_act = pk ? c->lo_act : 0;
   EpiArgs E0{};
   E0.pk = pk ? 1 : 0;
+  E0.lo = lo_h;  // the producers' output, the next norm's input w.h
   E0.rows = P.R;
   E0.d = d;
   E0.dh = dh;
@@ -713,6 +740,7 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
   m.s_state = P.st->s;
   m.e = P.e;
   m.merge_kind = cf.merge_kind;
+  m.err = c->err_dev;
 
   // Sublayer order of every block [RLT §2.5, text after eq. (2.16)]: kinds
   // 0 = SWA, 1 = cross-attention, 2 = FFN, each with its own pre-norm.
@@ -734,7 +762,16 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
   m.wg = scalar_gate ? c->merge_wg : nullptr;   // scalar gate: computed with the merge input
   m.bg = c->merge_bg;
   m.gbuf = w.gbuf;
+  // operand-order merge products: X = [e; r] (or [e; s]) and r alone are
+  // written in fragment order ([n][2d] and [n][d]); r alone goes to w.o,
+  // which the blocks use only later
+  m.pk = pk ? 1 : 0;
+  m.out2 = w.o;
+  m.lo = lo_X;
+  m.lo2 = lo_o;
+  m.claim = P.claim;
   { Prof pf(c, RLT_PROF_NORM, s); launch_merge_prep(c->dt, m, s); }
+  auto mw = [&](void* p) -> const void* { return pk ? p : nullptr; };
   auto producer = [&](EpiArgs e, const float* gnext) {
     e.gnext = gnext;
     e.zb = w.h;
@@ -748,24 +785,32 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
       e.out_f = w.gbuf;
       e.ldo = d;
       e.bias = c->merge_bg;
-      gm.run(w.X, 2 * d, {c->merge_wg}, d, 2 * d, PAIR_PLAIN, n, e);
+      gm.run(w.X, 2 * d, {c->merge_wg}, d, 2 * d, PAIR_PLAIN, n, e, nullptr, nullptr, mw(c->pk_mwg), lo_X);
     }
     e.kind = EPI_MOUT;
     e.out_f = w.z;
     e.ldo = d;
     e.gbuf = w.gbuf;
-    const void* r_in = (const char*)w.X + d * es;  // RMSNorm_s(s_{t-1}), the second half of X
+    // RMSNorm_s(s_{t-1}): the fragment-order copy, or the second half of X
+    const void* r_in = pk ? w.o : (const char*)w.X + d * es;
+    const int64_t ld_r = pk ? d : 2 * d;
     if (cf.merge_rank > 0) {
-      // low-rank W_s = U V: y = V r (stored in the dtype), then U y
+      // low-rank W_s = U V: y = V r (stored in the dtype), then U y; y is in
+      // fragment order when U has an operand-order copy (rank % 64 == 0)
       const int k = cf.merge_rank;
+      const bool pk_u = pk && c->pk_mws_u;
       EpiArgs ey = E0;
       ey.kind = EPI_STORE_T;
       ey.out_k = w.act;
       ey.ldo = k;
-      gm.run(r_in, 2 * d, {c->merge_ws_v}, k, d, PAIR_PLAIN, n, ey);
-      gm.run(w.act, k, {c->merge_ws_u}, d, k, PAIR_PLAIN, n, producer(e, g_first), nullptr, w.ssq);
+      ey.pk = pk_u ? 1 : 0;
+      ey.lo = pk_u ? lo_act : 0;
+      gm.run(r_in, ld_r, {c->merge_ws_v}, k, d, PAIR_PLAIN, n, ey, nullptr, nullptr, mw(c->pk_mws_v), lo_o);
+      gm.run(w.act, k, {c->merge_ws_u}, d, k, PAIR_PLAIN, n, producer(e, g_first), nullptr, w.ssq,
+             pk_u ? c->pk_mws_u : nullptr, lo_act);
     } else {
-      gm.run(r_in, 2 * d, {c->merge_ws}, d, d, PAIR_PLAIN, n, producer(e, g_first), nullptr, w.ssq);
+      gm.run(r_in, ld_r, {c->merge_ws}, d, d, PAIR_PLAIN, n, producer(e, g_first), nullptr, w.ssq, mw(c->pk_mws),
+             lo_o);
     }
   } else {
     EpiArgs e = E0;
@@ -773,7 +818,8 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
     e.out_f = w.z;
     e.ldo = d;
     e.bias = c->merge_bg;
-    gm.run(w.X, 2 * d, {c->merge_wg}, d, 2 * d, PAIR_PLAIN, n, producer(e, g_first), nullptr, w.ssq);
+    gm.run(w.X, 2 * d, {c->merge_wg}, d, 2 * d, PAIR_PLAIN, n, producer(e, g_first), nullptr, w.ssq,
+           mw(c->pk_mwg), lo_X);
   }
 
   AttnArgs at{};
@@ -783,11 +829,12 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
   at.dh = dh;
   at.qscale = (float)(1.4426950408889634 / std::sqrt((double)dh));
   at.W = cf.window;
-  at.chunk = xattn_chunk(c, n);
-  at.nch = (c->max_ctx + at.chunk - 1) / at.chunk;
+  at.chunk = c->chunk;
+  at.nch = c->nch;
   at.direct = at.nch == 1 ? 1 : 0;
   at.part = w.part;
   at.out_pk = pk ? 1 : 0;
+  at.out_lo = lo_o;
   at.sb = P.mem.stride_b;
   at.st = P.mem.stride_t;
 
@@ -800,7 +847,7 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
       e.out_f = w.q;
       e.out_k = w.kc;
       e.out_v = w.vc;
-      gm.run(w.h, d, {c->wq[l], c->wk[l], c->wv[l]}, d, d, PAIR_ROPE, n, e, w.ssq, nullptr, pw(c->pk_qkv, l));
+      gm.run(w.h, d, {c->wq[l], c->wk[l], c->wv[l]}, d, d, PAIR_ROPE, n, e, w.ssq, nullptr, pw(c->pk_qkv, l), lo_h);
     }
     at.q = w.q;
     at.kc = w.kc;
@@ -808,13 +855,13 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
     at.ring_k = (char*)P.st->ring_k + l * ring_layer;
     at.ring_v = (char*)P.st->ring_v + l * ring_layer;
     at.out = w.o;
-    at.hpw = swa_hpw(c, n);
+    at.hpw = c->hpw;
     { Prof pf(c, RLT_PROF_SWA, s); launch_swa(c->dt, at, s); }
     EpiArgs e = E0;
     e.kind = EPI_RESID;
     e.out_f = w.z;
     e.ldo = d;
-    gm.run(w.o, d, {c->wo[l]}, d, d, PAIR_PLAIN, n, producer(e, gnext), nullptr, w.ssq, pw(c->pk_wo, l));
+    gm.run(w.o, d, {c->wo[l]}, d, d, PAIR_PLAIN, n, producer(e, gnext), nullptr, w.ssq, pw(c->pk_wo, l), lo_o);
   };
   // ---- cross-attention sublayer [eq. (2.15)]: RMSNorm_M folded into the query ----
   auto cross = [&](int l, const float* gnext) {
@@ -822,14 +869,14 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
       EpiArgs e = E0;
       e.kind = EPI_QROT;
       e.out_f = w.qm;
-      gm.run(w.h, d, {c->wqm[l]}, d, d, PAIR_ROPE, n, e, w.ssq, nullptr, pw(c->pk_wqm, l));
+      gm.run(w.h, d, {c->wqm[l]}, d, d, PAIR_ROPE, n, e, w.ssq, nullptr, pw(c->pk_wqm, l), lo_h);
     }
     const int g = (l * cf.n_groups) / L;
     at.q = w.qm;
     at.mk = (const char*)P.mem.k + (size_t)g * P.mem.stride_g * es;
     at.mv = (const char*)P.mem.v + (size_t)g * P.mem.stride_g * es;
     at.out = w.o;
-    at.hpw = xattn_hpw(c, n);
+    at.hpw = c->hpw_x;
     { Prof pf(c, RLT_PROF_XATTN, s); launch_xattn(c->dt, at, s); }
     if (!at.direct) {
       Prof pf(c, RLT_PROF_XCOMBINE, s);
@@ -839,7 +886,7 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
     e.kind = EPI_RESID;
     e.out_f = w.z;
     e.ldo = d;
-    gm.run(w.o, d, {c->wom[l]}, d, d, PAIR_PLAIN, n, producer(e, gnext), nullptr, w.ssq, pw(c->pk_wom, l));
+    gm.run(w.o, d, {c->wom[l]}, d, d, PAIR_PLAIN, n, producer(e, gnext), nullptr, w.ssq, pw(c->pk_wom, l), lo_o);
   };
   // ---- FFN sublayer [eq. (2.16)]: RMSNorm_D folded into gate/up ----
   auto ffn = [&](int l, const float* gnext) {
@@ -847,11 +894,14 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
     e.kind = EPI_SWIGLU;
     e.out_k = w.act;
     e.ldo = F;
-    gm.run(w.h, d, {c->w_gate[l], c->w_up[l]}, F, d, PAIR_DUAL, n, e, w.ssq, nullptr, pw(c->pk_gu, l));
+    e.lo = lo_act;
+    gm.run(w.h, d, {c->w_gate[l], c->w_up[l]}, F, d, PAIR_DUAL, n, e, w.ssq, nullptr, pw(c->pk_gu, l), lo_h);
     e.kind = EPI_RESID;
     e.out_f = w.z;
     e.ldo = d;
-    gm.run(w.act, F, {c->w_down[l]}, d, F, PAIR_PLAIN, n, producer(e, gnext), nullptr, w.ssq, pw(c->pk_down, l));
+    e.lo = lo_h;
+    gm.run(w.act, F, {c->w_down[l]}, d, F, PAIR_PLAIN, n, producer(e, gnext), nullptr, w.ssq, pw(c->pk_down, l),
+           lo_act);
   };
   for (int l = 0; l < L; ++l) {
     for (int i = 0; i < 3; ++i) {
@@ -877,7 +927,7 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
     e.out_f = logits;
     e.ldo = cf.vocab;
     gm.run(w.h, d, {c->w_out}, cf.vocab, d, PAIR_PLAIN, n, e, w.ssq, nullptr,
-           pk ? c->pk_out : nullptr);  // RMSNorm_o folded in [eq. (2.6)]
+           pk ? c->pk_out : nullptr, lo_h);  // RMSNorm_o folded in [eq. (2.6)]
   }
   if (P.do_readout) {
     ReadoutArgs ro = P.ro;
@@ -885,33 +935,6 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
     Prof pf(c, RLT_PROF_READOUT, s);
     launch_readout(ro, s);
   }
-}
-
-template <typename T>
-T* off_ptr(T* p, int64_t off) {
-  return p ? p + off : p;
-}
-
-// The plan restricted to slots [off, off + cnt).
-StepPlan slice(const StepPlan& P, int off, int cnt, int d, int V) {
-  StepPlan Q = P;
-  Q.R = Rows{P.R.rows + off, P.R.src + off, P.R.t_row + off, cnt};
-  Q.n = cnt;
-  Q.s_out = off_ptr(P.s_out, (int64_t)off * d);
-  Q.z_trace = off_ptr(P.z_trace, (int64_t)off * d);
-  Q.logits = off_ptr(P.logits, (int64_t)off * V);
-  ReadoutArgs& ro = Q.ro;
-  ro.rows = Q.R;
-  ro.n = cnt;
-  ro.argmax = off_ptr(P.ro.argmax, off);
-  if (P.ro.mode == 0) {
-    ro.score_tok = off_ptr(P.ro.score_tok, off);
-    ro.logp = off_ptr(P.ro.logp, off);
-  }
-  ro.uniform = off_ptr(P.ro.uniform, off);
-  ro.sample_tok = off_ptr(P.ro.sample_tok, off);
-  ro.sample_logmu = off_ptr(P.ro.sample_logmu, off);
-  return Q;
 }
 
 // The device copy of a recorded phase list: found in the cache, or
@@ -955,8 +978,8 @@ const Phase* fused_prepare(rlt_ctx* c, const StepPlan& P, hipStream_t s, int* np
   return fused_phases(c, rec, s);
 }
 
-// Run the plan: one persistent kernel for small calls, otherwise the
-// separate kernels, as two concurrent row ranges when it has enough rows.
+// Run the plan: one persistent kernel for small calls (opt-in), otherwise
+// the separate kernels.
 void enqueue_rows(rlt_ctx* c, const StepPlan& P, hipStream_t s) {
   const int n = P.n;
   if (c->fused_rows > 0 && n <= c->fused_rows) {
@@ -976,18 +999,7 @@ void enqueue_rows(rlt_ctx* c, const StepPlan& P, hipStream_t s) {
       return;
     }
   }
-  if (c->split_min_rows <= 0 || n < c->split_min_rows || !c->aux) {
-    enqueue_transition(c, c->ws[0], P, s);
-    return;
-  }
-  const int d = c->cfg.d_model, V = c->cfg.vocab;
-  const int n0 = ((n + 1) / 2 + 15) / 16 * 16 < n ? ((n + 1) / 2 + 15) / 16 * 16 : (n + 1) / 2;
-  (void)hipEventRecord(c->ev_fork, s);
-  (void)hipStreamWaitEvent(c->aux, c->ev_fork, 0);
-  enqueue_transition(c, c->ws[0], slice(P, 0, n0, d, V), s);
-  enqueue_transition(c, c->ws[1], slice(P, n0, n - n0, d, V), c->aux);
-  (void)hipEventRecord(c->ev_join, c->aux);
-  (void)hipStreamWaitEvent(s, c->ev_join, 0);
+  enqueue_transition(c, c->ws[0], P, s);
 }
 
 int check_state(rlt_ctx* c, const rlt_state* st) {
@@ -1036,13 +1048,34 @@ extern "C" int rlt_init_state(rlt_ctx* c, rlt_state* st, const int32_t* rows, in
   return RLT_OK;
 }
 
-// dry: only record and upload the persistent step's phases (before a graph
-// capture, which cannot upload them)
+// The duplicate-row counters for states of up to B_cap rows (zero-filled;
+// grown outside any capture, waiting for earlier work that may use them).
+static int ensure_claim(rlt_ctx* c, int B_cap, hipStream_t s) {
+  if (c->claim_cap >= B_cap) return RLT_OK;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  HIP_TRY(hipStreamIsCapturing(s, &cs));
+  if (cs != hipStreamCaptureStatusNone) return fail(RLT_EINVAL, "state rows grew during a graph capture");
+  HIP_TRY(hipDeviceSynchronize());
+  if (c->claim) (void)hipFree(c->claim);
+  c->claim = nullptr;
+  c->claim_cap = 0;
+  int rc = dev_alloc(&c->claim, (size_t)B_cap * 4);
+  if (rc) return rc;
+  HIP_TRY(hipMemset(c->claim, 0, (size_t)B_cap * 4));
+  c->claim_cap = B_cap;
+  return RLT_OK;
+}
+
+// dry: only prepare what a capture cannot (the persistent step's phase list
+// upload, the duplicate-row counters), before a graph capture
 static int step_enqueue(rlt_ctx* c, rlt_state* st, const rlt_step_io* io, hipStream_t s, bool dry = false) {
   const int n = io->n;
+  int rc = ensure_claim(c, st->B_cap, s);
+  if (rc) return rc;
   StepPlan P{};
   P.R = Rows{io->rows, c->ident, c->t_row, n};
   P.n = n;
+  P.claim = c->claim;
   P.e = EIn{io->e, (int64_t)c->cfg.d_model, 0};
   P.mem = io->mem;
   P.st = st;
@@ -1079,6 +1112,7 @@ static int step_enqueue(rlt_ctx* c, rlt_state* st, const rlt_step_io* io, hipStr
   m.err = c->err_dev;
   m.max_t = c->max_ctx;
   m.B_cap = st->B_cap;
+  m.claim = c->claim;
   if (dry) {
     int nph = 0;
     if (c->fused_rows > 0 && n <= c->fused_rows) (void)fused_prepare(c, P, s, &nph);
@@ -1086,7 +1120,7 @@ static int step_enqueue(rlt_ctx* c, rlt_state* st, const rlt_step_io* io, hipStr
   }
   launch_prestep(m, s);
   enqueue_rows(c, P, s);
-  PostArgs pa{P.R, n, st->pos, st->pending, nullptr};
+  PostArgs pa{P.R, n, st->pos, st->pending, nullptr, c->claim, st->B_cap};
   if (io->flags & RLT_STEP_DEFER) pa.next_tok = sampling ? io->sample_tok : io->argmax;
   launch_poststep(pa, s);
   HIP_TRY(hipGetLastError());
@@ -1226,7 +1260,7 @@ extern "C" int rlt_replay_sequence(rlt_ctx* c, rlt_state* st, const rlt_replay_i
     ro.split = c->split_buf;
     launch_replay_rows(c->rows_buf, c->src_buf, nt, t, c->t_row, st->pos, io->mem.mem_len, c->err_dev, s);
     enqueue_rows(c, P, s);
-    PostArgs pa{P.R, nt, st->pos, st->pending, nullptr};
+    PostArgs pa{P.R, nt, st->pos, st->pending, nullptr, nullptr, st->B_cap};
     launch_poststep(pa, s);
   }
   launch_set_pending(c->rows_buf, c->src_buf, B, io->tokens, io->tok_stride_b, c->last_buf, st->pending, s);

@@ -31,6 +31,17 @@ template <typename T> __device__ __forceinline__ T from_f(float x);
 template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
 template <> __device__ __forceinline__ uint16_t from_f<uint16_t>(float x) { return f2bf(x); }
 
+// Store x as a matrix-product operand: p[i] = x in the element type and,
+// when lo != 0 (bf16 operands carried as two terms), p[i + lo] = the rounding
+// remainder x - p[i] in the element type, so that p[i] + p[i + lo] holds x to
+// about 16 significant bits.
+template <typename T>
+__device__ __forceinline__ void store_op(T* p, int64_t i, int64_t lo, float x) {
+  const T h = from_f<T>(x);
+  p[i] = h;
+  if (lo) p[i + lo] = from_f<T>(x - to_f<T>(h));
+}
+
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
 
 // Block-wide sum of one float per thread, fixed reduction order (wave
@@ -88,6 +99,7 @@ __host__ __device__ inline int64_t pk_off(int m, int k, int nchunk) {
 struct GemmArgs {
   const void* A;          // [M_pad][lda] activations (T); fragment order when Wp is set
   int64_t lda;
+  int64_t a_lo;           // fragment order: elements from A to its second term (0: one term)
   const void* W[3];       // weight segments, each [seg_rows][K] (T), natural layout
   const void* Wp;         // bf16: the same weights in fragment order, virtual column
                           // pairs as 32-row blocks (pair p = block p), or null
@@ -133,39 +145,56 @@ __device__ __forceinline__ float row_rstd(const GemmArgs& g, int m) {
   return 1.0f / sqrtf(a * g.inv_d + g.eps);
 }
 
-// Per-row rstd for R rows starting at m0, computed by all 256 threads of a
-// workgroup: thread (part, row) loads units part, part + P, ... (P = 256/R)
-// into registers when constructed (before the main loop, so the loads are in
-// flight with it), and finish() sums them in a fixed order through LDS.
-// Units beyond P*RU (only for very wide d) are summed in finish() directly.
-// Rows at or past M load nothing (their rstd is never used).
-template <int R>
+// Per-row rstd for R rows starting at m0, computed by the NT threads of a
+// workgroup. The partial sums of squares of a row are added in one fixed
+// order whatever R and NT are (so that a row's rstd, like every other
+// reduction of a product, does not depend on the tile it lands in): unit u
+// goes to part u % 4, each part adds its units in increasing u, and the row's
+// sum is ((p0 + p1) + p2) + p3. Thread (part slot, row) loads the first RU
+// units of its part(s) into registers when constructed (before the main
+// loop, so the loads are in flight with it); finish() adds the rest and
+// combines the parts through LDS. Rows at or past M load nothing (their rstd
+// is never used).
+template <int R, int NT = 256>
 struct RowRstd {
-  static constexpr int P = 256 / R;
-  static constexpr int RU = 16;
-  float v[RU];
+  static constexpr int CP = 4;                      // parts of the fixed order
+  static constexpr int PA = NT / R;                 // part slots per row
+  static_assert(PA >= 1 && (PA >= CP ? PA % CP == 0 : CP % PA == 0), "part slots");
+  static constexpr int CPT = PA >= CP ? 1 : CP / PA;  // parts per thread
+  static constexpr int RU = 16 / CPT;               // units per part in registers
+  float v[CPT][RU];
   __device__ __forceinline__ RowRstd(const GemmArgs& g, int m0) {
-    const int row = threadIdx.x % R, part = threadIdx.x / R;
+    const int row = threadIdx.x % R, slot = threadIdx.x / R;
     const bool live = g.ssq_in && m0 + row < g.M;
 #pragma unroll
-    for (int j = 0; j < RU; ++j) {
-      const int u = part + j * P;
-      v[j] = (live && u < g.ssq_units) ? g.ssq_in[(int64_t)u * g.M_pad + m0 + row] : 0.f;
+    for (int c = 0; c < CPT; ++c) {
+      const int cp = slot + c * PA;
+#pragma unroll
+      for (int j = 0; j < RU; ++j) {
+        const int u = cp + CP * j;
+        v[c][j] = (live && cp < CP && u < g.ssq_units) ? g.ssq_in[(int64_t)u * g.M_pad + m0 + row] : 0.f;
+      }
     }
   }
-  // s_part: LDS [P][R]; s_rstd: LDS [R]; contains one __syncthreads
+  // s_part: LDS [CP][R]; s_rstd: LDS [R]; contains one __syncthreads
   __device__ __forceinline__ void finish(const GemmArgs& g, int m0, float* s_part, float* s_rstd) {
-    const int row = threadIdx.x % R, part = threadIdx.x / R;
-    float a = 0.f;
+    const int row = threadIdx.x % R, slot = threadIdx.x / R;
 #pragma unroll
-    for (int j = 0; j < RU; ++j) a += v[j];
-    if (m0 + row < g.M)
-      for (int u = part + RU * P; u < g.ssq_units; u += P) a += g.ssq_in[(int64_t)u * g.M_pad + m0 + row];
-    s_part[part * R + row] = a;
+    for (int c = 0; c < CPT; ++c) {
+      const int cp = slot + c * PA;
+      if (cp < CP) {
+        float a = 0.f;
+#pragma unroll
+        for (int j = 0; j < RU; ++j) a += v[c][j];
+        if (m0 + row < g.M)
+          for (int u = cp + CP * RU; u < g.ssq_units; u += CP) a += g.ssq_in[(int64_t)u * g.M_pad + m0 + row];
+        s_part[cp * R + row] = a;
+      }
+    }
     __syncthreads();
     if (threadIdx.x < R) {
-      float s = 0.f;
-      for (int p = 0; p < P; ++p) s += s_part[p * R + threadIdx.x];
+      const float s = ((s_part[threadIdx.x] + s_part[R + threadIdx.x]) + s_part[2 * R + threadIdx.x]) +
+                      s_part[3 * R + threadIdx.x];
       s_rstd[threadIdx.x] = 1.0f / sqrtf(s * g.inv_d + g.eps);
     }
   }
@@ -227,6 +256,7 @@ struct EpiArgs {
   const float* gnext;
   void* zb;
   int pk;                   // bf16: zb and the SwiGLU output are written in fragment order
+  int64_t lo;               // fragment-order outputs: elements to their second term (0: one term)
   // memory entries (EPI_MEMKV): one group's K / V buffers; the entry of slot
   // m is at rows[m] * msb + (t_row[m] - 1) * mst elements
   void* mk;
@@ -260,6 +290,7 @@ struct AttnArgs {
   float* part;              // [n][nch][H][dh + 2]
   void* out;                // [n][d] (T) attention output
   int out_pk;               // bf16: out in fragment order (the next product's operand)
+  int64_t out_lo;           // fragment-order out: elements to its second term (0: one term)
   int direct;               // cross-attention with one chunk: the normalised output, no combine
 };
 
@@ -298,6 +329,10 @@ struct MiscArgs {
   int64_t s_trace_sb;
   int max_t;                      // largest position the workspace supports
   int B_cap;                      // rows in the state buffers
+  int pk;                         // merge preparation: X (and out2) in fragment order
+  void* out2;                     // merge preparation: RMSNorm_s(s_{t-1}) alone (pk, gated)
+  int64_t lo, lo2;                // fragment order: elements from out / out2 to their second terms
+  int* claim;                     // [B_cap] slots per state row in this call (decoder step), or null
 };
 
 void launch_prestep(const MiscArgs& a, hipStream_t s);
@@ -351,6 +386,8 @@ struct PostArgs {
   int* pos;
   int* pending;
   const int32_t* next_tok;   // token to record as pending (DEFER) or null
+  int* claim;                // [B_cap] slot counts to clear (decoder step), or null
+  int B_cap;
 };
 void launch_poststep(const PostArgs& a, hipStream_t s);
 

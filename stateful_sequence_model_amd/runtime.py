@@ -113,7 +113,8 @@ class Decoder:
     """A context (``rlt_create``) over device copies of the parameters."""
 
     def __init__(self, cfg: ModelConfig, params: Dict[str, object], max_rows: int, max_ctx: int,
-                 device="cuda"):
+                 device="cuda", launch: Optional[Dict[str, int]] = None):
+        """launch: optional ``rlt_dbg_launch`` fields (tests and tuning sweeps)."""
         self.cfg = cfg
         self.device = device
         self.params = {}
@@ -141,7 +142,10 @@ class Decoder:
         self._w = w
         self._cfg_c = cfg.to_c()
         self.max_rows, self.max_ctx = max_rows, max_ctx
-        self.ctx = A.rlt_create(self._cfg_c, w, max_rows, max_ctx)
+        if launch:
+            self.ctx = A.rlt_dbg_create(self._cfg_c, w, max_rows, max_ctx, A.rlt_dbg_launch(**launch))
+        else:
+            self.ctx = A.rlt_create(self._cfg_c, w, max_rows, max_ctx)
 
     def close(self):
         if getattr(self, "ctx", None):
@@ -290,10 +294,15 @@ class Decoder:
     def sync_error(self, stream=None) -> int:
         return A.rlt_sync_error(self.ctx, current_stream() if stream is None else stream)
 
-    def refresh_weights(self, stream=None) -> int:
-        """Rebuild the context's operand-order weight copy after the weight
-        tensors were changed in place (rlt_refresh_weights)."""
-        return A.rlt_refresh_weights(self.ctx, current_stream() if stream is None else stream)
+    def refresh_weights(self, version: int, stream=None) -> int:
+        """The weight tensors were changed in place: rebuild the context's
+        operand-order weight copy and adopt ``version`` (rlt_refresh_weights);
+        states must then carry the new version (re-initialise them)."""
+        rc = A.rlt_refresh_weights(self.ctx, version, current_stream() if stream is None else stream)
+        if rc == A.RLT_OK:
+            self.cfg.version = version
+            self._cfg_c = self.cfg.to_c()
+        return rc
 
     # -- exact prefix snapshots ---------------------------------------------------
     def snapshot(self, st: DecoderState, rows, stream=None) -> np.ndarray:

@@ -35,14 +35,15 @@ class GpuRun:
     """A context, a state of B rows and device copies of e / memory."""
 
     def __init__(self, wl: synth.Workload, raw: Optional[Dict[str, np.ndarray]] = None, B: Optional[int] = None,
-                 T: Optional[int] = None, max_rows: Optional[int] = None, b0: int = 0, **over):
+                 T: Optional[int] = None, max_rows: Optional[int] = None, b0: int = 0,
+                 launch: Optional[Dict[str, int]] = None, **over):
         from stateful_sequence_model_amd import Decoder, DecoderState, to_device
         self.wl = wl
         self.B = wl.B if B is None else B
         self.T = wl.T if T is None else T
         self.raw = synth.make_weights(wl) if raw is None else raw
         self.cfg = model_config(wl, **over)
-        self.dec = Decoder(self.cfg, self.raw, max_rows=max_rows or max(self.B, 1), max_ctx=self.T)
+        self.dec = Decoder(self.cfg, self.raw, max_rows=max_rows or max(self.B, 1), max_ctx=self.T, launch=launch)
         self.st = DecoderState(self.cfg, self.B)
         self.E = synth.make_e(wl, b0, self.B, self.T)
         self.mk = np.stack([synth.make_memory(wl, "k", g, b0, self.B, self.T) for g in range(wl.G)])

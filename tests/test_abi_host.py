@@ -112,6 +112,10 @@ def test_create_rejects_missing_weights_before_touching_the_device():
     h = C.c_void_p()
     assert _abi.lib().rlt_create(C.byref(cfg), C.byref(w), 4, 32, C.byref(h)) == _abi.RLT_EINVAL
     assert h.value is None
+    opt = _abi.rlt_dbg_launch()
+    assert _abi.lib().rlt_dbg_create(C.byref(cfg), C.byref(w), 4, 32, C.byref(opt), C.byref(h)) == _abi.RLT_EINVAL
+    assert _abi.lib().rlt_dbg_create(C.byref(cfg), C.byref(w), 4, 32, None, C.byref(h)) == _abi.RLT_EINVAL
+    assert h.value is None
 
 
 def test_null_arguments_are_rejected():
@@ -125,7 +129,7 @@ def test_null_arguments_are_rejected():
     assert L.rlt_memory_append(None, None, None, 0, 0, None, 0, None, None) == _abi.RLT_EINVAL
     assert L.rlt_state_snapshot(None, None, None, 0, None, None) == _abi.RLT_EINVAL
     assert L.rlt_state_restore(None, None, None, 0, None, None) == _abi.RLT_EINVAL
-    assert L.rlt_refresh_weights(None, None) == _abi.RLT_EINVAL
+    assert L.rlt_refresh_weights(None, 2, None) == _abi.RLT_EINVAL
     assert L.rlt_dbg_gemm(None, None, None, 1, 32, 32, None, None) == _abi.RLT_EINVAL
     assert L.rlt_dbg_gemm_packed(None, None, None, 1, 32, 64, None, None) == _abi.RLT_EINVAL
     assert L.rlt_memory_prefill(None, None, None, 0, 0, None, None, 0, 0, None) == _abi.RLT_EINVAL

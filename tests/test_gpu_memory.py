@@ -222,3 +222,58 @@ def test_decoder_on_gpu_built_memory():
             assert rel_l2(S[t - 1][b], ost.s) < 2e-2, (b, t)
             zo = orc.logits(ost.s)
             assert rel_l2(Z[t - 1][b], zo) < 2e-2, (b, t)
+
+
+@pytest.mark.timeout(900)
+def test_prefill_reference_width_and_decoder_on_it():
+    """Reference width (d = 2048, 16 x 128 heads, the width the memory
+    prefill benchmark times): 10,861 entries over two chunks of the prefill
+    schedule, with the 16-byte rotary/scatter epilogue (aligned bf16
+    buffers); sampled entries against the oracle (incl. both sides of the
+    chunk edge and each sequence's first and last position), mem_len exact;
+    then four decoder steps from H_0 of two rows reading that memory,
+    against the oracle on its own memory built from the same weights
+    [RLT §2.2 eq. (2.2), §2.5 eq. (2.15)]."""
+    require_gpu()
+    from stateful_sequence_model_amd import DecoderState
+    wl = synth.REF
+    B, T_cap = 5, 4096
+    dec, mw, mw_raw, K, V, mem_len, mem, raw = _setup(wl, B, T_cap)
+    E = synth.make_e(wl, 0, B, T_cap)
+    Ed = torch.from_numpy(E.view(np.int16)).cuda().view(torch.bfloat16)
+    lens = np.array([4096, 3000, 1200, 2048, 517], dtype=np.int32)
+    assert dec.memory_prefill(mw, mem, T_cap, lens, Ed) == 0
+    torch.cuda.synchronize()
+    assert dec.sync_error() == 0
+    assert mem_len.cpu().tolist() == lens.tolist()
+    offs = np.concatenate([[0], np.cumsum(lens)])
+    b_edge = int(np.searchsorted(offs, 8192, side="right") - 1)
+    t_edge = 8192 - int(offs[b_edge]) + 1
+    assert (b_edge, t_edge) == (2, 1097)  # the second chunk starts inside sequence 2
+    sample = [(0, 1), (0, 4096), (0, 2049), (1, 1), (1, 3000), (2, 600), (2, 1200), (3, 1), (3, 2048),
+              (b_edge, t_edge - 1), (b_edge, t_edge), (4, 1), (4, 517)]
+    worst = _check_entries(wl, K, V, mw_raw, E, sample, 1e-2)
+    print("reference-width prefill: worst sampled entry rel L2 %.2e" % worst)
+    # decoder steps on the GPU-built memory
+    st = DecoderState(dec.cfg, B)
+    rows = torch.tensor([0, 4], dtype=torch.int32, device="cuda")
+    dec.init_state(st, rows)
+    s_out = torch.empty((2, wl.d), device="cuda")
+    logits = torch.empty((2, wl.V), device="cuda")
+    S, Z = [], []
+    for t in range(1, 5):
+        assert dec.step(st, rows, Ed[rows.long(), t - 1].contiguous(), mem, s_out=s_out, logits=logits) == 0
+        S.append(s_out.double().cpu().numpy())
+        Z.append(logits.double().cpu().numpy())
+    assert dec.sync_error() == 0
+    del K, V
+    cfg = oracle_config(wl)
+    orc = Oracle(cfg, oracle_weights(raw))
+    omw = oracle_weights(mw_raw)
+    for j, b in enumerate((0, 4)):
+        omem = build_memory(cfg, widen(E[b]), omw, n=4)
+        ost = orc.initial_state()
+        for t in range(1, 5):
+            ost = orc.transition(ost, widen(E[b, t - 1]), omem)
+            assert rel_l2(S[t - 1][j], ost.s) < 2e-2, (b, t)
+            assert rel_l2(Z[t - 1][j], orc.logits(ost.s)) < 2e-2, (b, t)

@@ -13,7 +13,7 @@ import pytest
 import synth
 from oracle import Memory, Oracle, behaviour_logprobs, replay as oracle_replay
 from tests.gpu_common import GpuRun, require_gpu, torch
-from tests.helpers import oracle_config, oracle_weights, rel_l2, widen
+from tests.helpers import memory_of, oracle_config, oracle_weights, rel_l2, widen
 
 pytestmark = pytest.mark.gpu
 
@@ -137,27 +137,78 @@ def test_causality_with_poisoned_unread_data():
 
 def test_batch_composition_independence():
     """A sequence's results do not depend on which other sequences share the
-    call, or their order (tolerance: only fp32 accumulation order may differ
-    between launch shapes; identical shapes are bit-exact)."""
+    call, or their order [RLT §3.1 Prop. 3.1, §4.1]: bit for bit within one
+    context, since every reduction order is fixed by the config and the
+    context's capacities, not by the call's row count."""
     require_gpu()
     wl = SMALL.with_(B=8, T=40)
     full = GpuRun(wl)
     full.init()
     S, Z = full.run(20)
-    part = GpuRun(wl)
+    part = GpuRun(wl, raw=full.raw)
     part.init([5, 2])
     S2, Z2 = part.run(20, [5, 2])
+    one = GpuRun(wl, raw=full.raw)
+    one.init([6])
+    S4, Z4 = one.run(20, [6])
     for j, b in enumerate((5, 2)):
-        for i in range(20):
-            assert rel_l2(S2[i, j], S[i, b]) < 1e-5
-            assert rel_l2(Z2[i, j], Z[i, b]) < 1e-5
-    # same launch shape, permuted rows: bit-exact
-    perm = GpuRun(wl)
+        assert np.array_equal(S2[:, j], S[:, b]) and np.array_equal(Z2[:, j], Z[:, b]), b
+    assert np.array_equal(S4[:, 0], S[:, 6]) and np.array_equal(Z4[:, 0], Z[:, 6])
+    # same call size, permuted rows
+    perm = GpuRun(wl, raw=full.raw)
     perm.init()
     order = [7, 3, 0, 1, 6, 2, 5, 4]
     S3, Z3 = perm.run(20, order)
     for j, b in enumerate(order):
-        assert np.array_equal(S3[:, j], S[:, b])
+        assert np.array_equal(S3[:, j], S[:, b]) and np.array_equal(Z3[:, j], Z[:, b])
+
+
+@pytest.mark.timeout(600)
+def test_batch_invariance_across_product_tiles():
+    """Mid width (d=1024, 16x64 heads, W=128) in a 96-row context: calls of
+    96, 40, 7 and 1 rows take different product tiles (64 x 2 pairs, 64 x 1,
+    32 x 1), yet every row's states and logits are bit-identical to its
+    results in the full call."""
+    require_gpu()
+    wl = synth.MID.with_(T=24, L=3)
+    B, n = 96, 6
+    full = GpuRun(wl, B=B, T=wl.T)
+    full.init()
+    S, Z = full.run(n)
+    for sub in ([3, 50] + list(range(58, 96)), [10, 20, 30, 40, 50, 60, 70], [41]):
+        part = GpuRun(wl, raw=full.raw, B=B, T=wl.T)
+        part.init(sub)
+        S2, Z2 = part.run(n, sub)
+        for j, b in enumerate(sub):
+            assert np.array_equal(S2[:, j], S[:, b]) and np.array_equal(Z2[:, j], Z[:, b]), (len(sub), b)
+        part.dec.close()
+
+
+def test_duplicate_rows_are_refused_on_device():
+    """A decoder call naming one state row in two slots would let two
+    workgroups update the same row: the library detects it on the device,
+    skips those slots (their rows stay unchanged), processes the others and
+    reports RLT_EINVAL on the next call; the detection leaves nothing behind
+    (the following call is clean)."""
+    require_gpu()
+    from stateful_sequence_model_amd import _abi as A
+    wl = SMALL.with_(B=4, T=16)
+    run = GpuRun(wl)
+    run.init()
+    run.run(2)
+    before_s = run.st.s.clone()
+    before_pos = run.st.pos.clone()
+    rows = torch.tensor([1, 3, 1], dtype=torch.int32, device="cuda")
+    e = run.Ed[[1, 3, 1], 2].contiguous()
+    assert run.dec.step(run.st, rows, e, run.mem) == 0
+    assert run.dec.sync_error() == A.RLT_EINVAL
+    assert torch.equal(run.st.s[1], before_s[1]) and int(run.st.pos[1]) == int(before_pos[1])
+    assert int(run.st.pos[3]) == int(before_pos[3]) + 1 and not torch.equal(run.st.s[3], before_s[3])
+    # the counters were cleared: a proper call of the same rows succeeds
+    ok = run.rows([1, 0])
+    assert run.dec.step(run.st, ok, run.Ed[[1, 0], 2].contiguous(), run.mem) == 0
+    assert run.dec.sync_error() == 0
+    assert int(run.st.pos[1]) == int(before_pos[1]) + 1
 
 
 def test_memory_strides_other_layout_bit_exact():
@@ -334,33 +385,24 @@ def test_argmax_sampling_and_scoring_against_oracle_on_gpu_logits():
 
 def test_persistent_step_equals_separate_kernels():
     """The persistent step (one kernel, grid barriers between the recorded
-    phases; enabled per context with RLT_FUSED_ROWS) reproduces the separate
-    kernels bit for bit: same bodies, launch shapes and reduction orders
-    (the reference context runs the same narrow-tile products, RLT_GEMM_PK=0,
-    since the persistent step does not take the operand-order products).
-    Covers plain steps, hipGraph-captured steps and a replay from H_0."""
+    phases; enabled per context by the fused_rows launch option) reproduces
+    the separate kernels bit for bit: same bodies, launch shapes and
+    reduction orders (the reference context runs the same narrow-tile
+    products, no_packed, since the persistent step does not take the
+    operand-order products). Covers plain steps, hipGraph-captured steps
+    and a replay from H_0."""
     require_gpu()
-    import os
-
-    def with_env(env, fn):
-        old = {k: os.environ.get(k) for k in env}
-        os.environ.update(env)
-        try:
-            return fn()
-        finally:
-            for k, v in old.items():
-                if v is None:
-                    del os.environ[k]
-                else:
-                    os.environ[k] = v
-
     wl = SMALL.with_(B=8, T=40)
-    ref = with_env({"RLT_GEMM_PK": "0"}, lambda: GpuRun(wl))
-    fz = with_env({"RLT_FUSED_ROWS": "16"}, lambda: GpuRun(wl, raw=ref.raw))
+    ref = GpuRun(wl, launch=dict(no_packed=1))
+    fz = GpuRun(wl, raw=ref.raw, launch=dict(no_packed=1, fused_rows=16))
+    _persistent_vs_separate(wl, ref, fz)
+
+
+def _persistent_vs_separate(wl, ref, fz, nsteps=10):
     for run in (ref, fz):
         run.init()
-    S0, Z0 = ref.run(10)
-    S1, Z1 = fz.run(10)
+    S0, Z0 = ref.run(nsteps)
+    S1, Z1 = fz.run(nsteps)
     assert np.array_equal(S0, S1) and np.array_equal(Z0, Z1)
     # captured steps
     stream = torch.cuda.Stream()
@@ -374,7 +416,7 @@ def test_persistent_step_equals_separate_kernels():
             stream.synchronize()
             assert torch.equal(ref.st.s, fz.st.s) and torch.equal(am[0], am[1]), i
     # replay from H_0 with an active set that shrinks over the ticks
-    lens = np.array([12, 9, 5, 12, 3, 7, 2, 10], dtype=np.int32)
+    lens = np.array([12, 9, 5, 12, 3, 7, 2, 10], dtype=np.int32)[:wl.B]
     splits = np.ones(wl.B, dtype=np.int32)
     tokens = torch.from_numpy(synth.make_tokens(wl, 0, wl.B, wl.T)).cuda()
     lp = [torch.full((wl.B, wl.T), float("nan"), device="cuda") for _ in range(2)]
@@ -384,6 +426,41 @@ def test_persistent_step_equals_separate_kernels():
     assert torch.equal(lp[0].isnan(), lp[1].isnan())
     assert torch.equal(torch.nan_to_num(lp[0]), torch.nan_to_num(lp[1]))
     assert torch.equal(ref.st.s, fz.st.s)
+    return S0, Z0
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_cross_attention_many_chunks(dtype):
+    """Cross-attention split into 16-position chunks up to t = 300 (up to 19
+    chunks per row: the combine's all-at-once path for <= 16 chunks and its
+    plain loop beyond), through the separate kernels against the oracle,
+    and (bf16) the persistent step's combine phase against the separate
+    kernels bit for bit [RLT §2.5 eq. (2.15), §4.2]."""
+    require_gpu()
+    T = 300
+    wl = synth.SMALL.with_(B=2, T=T, L=2, G=2, dtype=dtype)
+    sep = GpuRun(wl, launch=dict(xattn_chunk=16, no_packed=1))
+    sep.init()
+    S, Z = sep.run(T)
+    orc = Oracle(oracle_config(wl), oracle_weights(sep.raw))
+    tol = 2e-2 if dtype == "bf16" else 1e-4
+    worst = 0.0
+    for b in range(wl.B):
+        mem = memory_of(wl, b, T=T)
+        st = orc.initial_state()
+        for t in range(1, T + 1):
+            st = orc.transition(st, widen(sep.E[b, t - 1]), mem)
+            if t % 7 == 0 or t > T - 20 or t in (16, 17, 256, 257, 272, 273):
+                es, ez = rel_l2(S[t - 1, b], st.s), rel_l2(Z[t - 1, b], orc.logits(st.s))
+                worst = max(worst, es, ez)
+                assert es < tol and ez < tol, (dtype, b, t, es, ez)
+    print("many chunks %s: worst rel L2 %.2e" % (dtype, worst))
+    if dtype == "bf16":
+        f = GpuRun(wl, raw=sep.raw, launch=dict(xattn_chunk=16, no_packed=1, fused_rows=16))
+        f.init()
+        Sf, Zf = f.run(T)
+        assert np.array_equal(Sf, S) and np.array_equal(Zf, Z)
 
 
 def test_snapshot_restore_resumes_bit_exact():
@@ -421,27 +498,36 @@ def test_snapshot_restore_resumes_bit_exact():
 
 
 def test_refresh_weights_after_in_place_update():
-    """bf16 contexts multiply an operand-order copy of the decoder's matrix
-    weights made at creation: weights changed in place are not seen until
-    rlt_refresh_weights, after which the transitions equal those of a
-    context created with the new weights, bit for bit."""
+    """bf16 contexts multiply an operand-order copy of the matrix weights
+    made at creation: weights changed in place are not seen until
+    rlt_refresh_weights, which rebuilds the copy and adopts a new weights
+    version [RLT §5.4, App. A.4]: states of the old version are then refused
+    (RLT_ESTALE) and, re-initialised under the new version, transition
+    exactly like those of a context created with the new weights."""
     require_gpu()
+    from stateful_sequence_model_amd import DecoderState, _abi as A
     wl = SMALL.with_(B=4, T=16)
     a = GpuRun(wl)
     a.init()
     S0, Z0 = a.run(3)
-    # exact bf16 rescalings of matrices that only the operand-order products read
+    # exact bf16 rescalings of matrices of the decoder, the readout and the merge
     a.dec.params["layer.0.wq"].mul_(2)
     a.dec.params["layer.1.w_down"].mul_(0.5)
     a.dec.params["out.w"].mul_(2)
+    a.dec.params["merge.ws"].mul_(2)
     a.init()
     S1, Z1 = a.run(3)
     assert np.array_equal(S1, S0) and np.array_equal(Z1, Z0)  # the copy made at creation
-    assert a.dec.refresh_weights() == 0
+    assert a.dec.refresh_weights(a.cfg.version) == A.RLT_EINVAL  # a refresh needs a new version
+    old_version = a.st.version
+    assert a.dec.refresh_weights(old_version + 1) == 0
+    assert a.step(range(4), 4) == A.RLT_ESTALE                  # old states are stale
+    a.st = DecoderState(a.cfg, wl.B)
+    assert a.st.version == old_version + 1
     a.init()
     S2, Z2 = a.run(3)
     raw = dict(a.raw)
-    for k in ("layer.0.wq", "layer.1.w_down", "out.w"):
+    for k in ("layer.0.wq", "layer.1.w_down", "out.w", "merge.ws"):
         raw[k] = a.dec.params[k].clone()
     b = GpuRun(wl, raw=raw)
     b.init()
