@@ -276,6 +276,22 @@ int rlt_init_state(rlt_ctx* ctx, rlt_state* st, const int32_t* rows, int32_t n, 
  * among calls of at most 32 rows and among calls of more than 32 rows. */
 int rlt_decoder_step(rlt_ctx* ctx, rlt_state* st, const rlt_step_io* io, void* stream);
 
+/* rlt_decoder_step for callers that cannot allocate device memory (code
+ * under their own HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same transition, kernels and results bit for bit,
+ * but the call allocates nothing. The duplicate-row counters, which
+ * rlt_decoder_step allocates on its first call for a state, live here in a
+ * fixed device array of the library (RLT_NOALLOC_MAX_ROWS int32 per device,
+ * held until the process ends); everything else is the context's workspace
+ * from rlt_create. Limits: st->B_cap <= RLT_NOALLOC_MAX_ROWS (else
+ * RLT_ESHAPE); RLT_STEP_GRAPH is refused (RLT_EINVAL: instantiating a graph
+ * allocates) and the opt-in persistent step is not used. The counters are
+ * shared by every such call on one device and cleared by each call for its
+ * own rows: calls of this entry point that overlap on one device (other
+ * streams, other contexts) race and must be ordered by the caller. */
+#define RLT_NOALLOC_MAX_ROWS 65536
+int rlt_decoder_step_noalloc(rlt_ctx* ctx, rlt_state* st, const rlt_step_io* io, void* stream);
+
 /* See rlt_replay_io. Synchronises the stream once at the start (upload of
  * the schedule). */
 int rlt_replay_sequence(rlt_ctx* ctx, rlt_state* st, const rlt_replay_io* io, void* stream);

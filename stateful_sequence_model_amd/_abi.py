@@ -79,6 +79,7 @@ class rlt_snapshot_header(C.Structure):
 
 
 RLT_SNAPSHOT_MAGIC = 0x53544C52
+RLT_NOALLOC_MAX_ROWS = 65536
 
 
 class rlt_memory_weights(C.Structure):
@@ -116,6 +117,7 @@ _SIGS = {
     "rlt_last_error": (C.c_char_p, []),
     "rlt_init_state": (C.c_int, [P, C.POINTER(rlt_state), P, i32, i32, P]),
     "rlt_decoder_step": (C.c_int, [P, C.POINTER(rlt_state), C.POINTER(rlt_step_io), P]),
+    "rlt_decoder_step_noalloc": (C.c_int, [P, C.POINTER(rlt_state), C.POINTER(rlt_step_io), P]),
     "rlt_replay_sequence": (C.c_int, [P, C.POINTER(rlt_state), C.POINTER(rlt_replay_io), P]),
     "rlt_score_logprobs": (C.c_int, [P, C.POINTER(rlt_score_io), P]),
     "rlt_sync_error": (C.c_int, [P, P]),
@@ -204,6 +206,10 @@ def rlt_init_state(ctx: int, st: rlt_state, rows: int, n: int, flags: int, strea
 
 def rlt_decoder_step(ctx: int, st: rlt_state, io: rlt_step_io, stream: int) -> int:
     return lib().rlt_decoder_step(ctx, C.byref(st), C.byref(io), stream)
+
+
+def rlt_decoder_step_noalloc(ctx: int, st: rlt_state, io: rlt_step_io, stream: int) -> int:
+    return lib().rlt_decoder_step_noalloc(ctx, C.byref(st), C.byref(io), stream)
 
 
 def rlt_replay_sequence(ctx: int, st: rlt_state, io: rlt_replay_io, stream: int) -> int:

@@ -506,6 +506,19 @@ void launch_replay_rows(const int* rows, const int* src, int n, int tick, int* t
 void launch_poststep(const PostArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_poststep, dim3((a.n + 255) / 256), dim3(256), 0, s, a);
 }
+
+// counts[rows[i]] = 0 for the rows of a call (rows outside 0..B_cap-1 left
+// to the pre-step's own check)
+__global__ void k_zero_rows(int* counts, const int* rows, int n, int B_cap) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int row = rows[i];
+  if (row >= 0 && row < B_cap) counts[row] = 0;
+}
+
+void launch_zero_rows(int* counts, const int* rows, int n, int B_cap, hipStream_t s) {
+  hipLaunchKernelGGL(k_zero_rows, dim3((n + 255) / 256), dim3(256), 0, s, counts, rows, n, B_cap);
+}
 void launch_init(int dtype, const int* rows, int n, const float* s_star, float* st, int* pos, int* pending,
                  void* ring_k, void* ring_v, int L, int B_cap, int W, int d, int poison, hipStream_t s) {
   if (dtype == 0)

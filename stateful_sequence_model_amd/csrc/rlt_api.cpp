@@ -20,6 +20,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <numeric>
 #include <string>
 #include <vector>
@@ -31,9 +32,21 @@
 
 using namespace rlt;
 
+// Duplicate-row counters of rlt_decoder_step_noalloc: a fixed device array
+// (each device holds its own copy until the process ends). In host code this
+// name is not a device address: host code uses the per-device address from
+// hipGetSymbolAddress (g_scratch_ptr below), never the name itself.
+static __device__ __align__(256) int scratch[RLT_NOALLOC_MAX_ROWS];
+
 namespace {
 
 thread_local char g_msg[512] = "";
+
+// device address of `scratch` per device, resolved once per device (with the
+// device current) by rlt_create
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int* g_scratch_ptr[kMaxDevices] = {};
 
 int fail(int code, const char* fmt, ...) {
   va_list ap;
@@ -63,6 +76,7 @@ struct Workspace {
 
 struct rlt_ctx {
   rlt_config cfg;
+  int device;      // the HIP device the context was created on
   int dt;          // 0 = f32, 1 = bf16
   size_t es;       // element size
   // parameters (caller-owned device memory)
@@ -408,6 +422,19 @@ static int pick_chunk(int wg_per_chunk, int max_ctx) {
   return wg_per_chunk >= 512 ? 1024 : wg_per_chunk >= 128 ? 512 : 256;
 }
 
+// The device address of the allocation-free step's counters on `dev` (the
+// current device), resolved on the first context created there.
+static int resolve_scratch(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(RLT_EUNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev]) return RLT_OK;
+  void* p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !p) return fail(RLT_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+  g_scratch_ptr[dev] = (int*)p;
+  return RLT_OK;
+}
+
 static int create_ctx(const rlt_config* cfg, const rlt_weights* w, int32_t max_rows, int32_t max_ctx,
                       const rlt_dbg_launch* opt, rlt_ctx** out) {
   int rc = check_config(cfg);
@@ -428,8 +455,12 @@ static int create_ctx(const rlt_config* cfg, const rlt_weights* w, int32_t max_r
     for (int l = 0; l < L; ++l)
       if (!arr[l]) return fail(RLT_EINVAL, "missing per-layer weight of layer %d", l);
   }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(RLT_EHIP, "hipGetDevice failed");
+  if ((rc = resolve_scratch(dev))) return rc;
   rlt_ctx* c = new rlt_ctx();  // value-initialised: every pointer starts null
   c->cfg = *cfg;
+  c->device = dev;
   c->dt = cfg->dtype == RLT_BF16 ? 1 : 0;
   c->es = elt_size(cfg->dtype);
   c->s_star = w->s_star;
@@ -980,9 +1011,9 @@ const Phase* fused_prepare(rlt_ctx* c, const StepPlan& P, hipStream_t s, int* np
 
 // Run the plan: one persistent kernel for small calls (opt-in), otherwise
 // the separate kernels.
-void enqueue_rows(rlt_ctx* c, const StepPlan& P, hipStream_t s) {
+void enqueue_rows(rlt_ctx* c, const StepPlan& P, hipStream_t s, bool allow_fused = true) {
   const int n = P.n;
-  if (c->fused_rows > 0 && n <= c->fused_rows) {
+  if (allow_fused && c->fused_rows > 0 && n <= c->fused_rows) {
     int nph = 0;
     const Phase* ph = fused_prepare(c, P, s, &nph);
     if (ph) {
@@ -1067,15 +1098,22 @@ static int ensure_claim(rlt_ctx* c, int B_cap, hipStream_t s) {
 }
 
 // dry: only prepare what a capture cannot (the persistent step's phase list
-// upload, the duplicate-row counters), before a graph capture
-static int step_enqueue(rlt_ctx* c, rlt_state* st, const rlt_step_io* io, hipStream_t s, bool dry = false) {
+// upload, the duplicate-row counters), before a graph capture.
+// fixed_claim: the allocation-free step's counters (cleared here for the
+// call's rows; no allocation, no persistent step), else the context's own.
+static int step_enqueue(rlt_ctx* c, rlt_state* st, const rlt_step_io* io, hipStream_t s, bool dry = false,
+                        int* fixed_claim = nullptr) {
   const int n = io->n;
-  int rc = ensure_claim(c, st->B_cap, s);
-  if (rc) return rc;
+  int* claim = fixed_claim;
+  if (!claim) {
+    int rc = ensure_claim(c, st->B_cap, s);
+    if (rc) return rc;
+    claim = c->claim;
+  }
   StepPlan P{};
   P.R = Rows{io->rows, c->ident, c->t_row, n};
   P.n = n;
-  P.claim = c->claim;
+  P.claim = claim;
   P.e = EIn{io->e, (int64_t)c->cfg.d_model, 0};
   P.mem = io->mem;
   P.st = st;
@@ -1112,22 +1150,44 @@ static int step_enqueue(rlt_ctx* c, rlt_state* st, const rlt_step_io* io, hipStr
   m.err = c->err_dev;
   m.max_t = c->max_ctx;
   m.B_cap = st->B_cap;
-  m.claim = c->claim;
+  m.claim = claim;
   if (dry) {
     int nph = 0;
     if (c->fused_rows > 0 && n <= c->fused_rows) (void)fused_prepare(c, P, s, &nph);
     return RLT_OK;
   }
+  if (fixed_claim) launch_zero_rows(fixed_claim, io->rows, n, st->B_cap, s);
   launch_prestep(m, s);
-  enqueue_rows(c, P, s);
-  PostArgs pa{P.R, n, st->pos, st->pending, nullptr, c->claim, st->B_cap};
+  enqueue_rows(c, P, s, fixed_claim == nullptr);
+  PostArgs pa{P.R, n, st->pos, st->pending, nullptr, claim, st->B_cap};
   if (io->flags & RLT_STEP_DEFER) pa.next_tok = sampling ? io->sample_tok : io->argmax;
   launch_poststep(pa, s);
   HIP_TRY(hipGetLastError());
   return RLT_OK;
 }
 
-extern "C" int rlt_decoder_step(rlt_ctx* c, rlt_state* st, const rlt_step_io* io, void* stream) {
+static int check_step(rlt_ctx* c, rlt_state* st, const rlt_step_io* io);
+
+extern "C" int rlt_decoder_step_noalloc(rlt_ctx* c, rlt_state* st, const rlt_step_io* io, void* stream) {
+  int rc = check_step(c, st, io);
+  if (rc) return rc;
+  if (st->B_cap > RLT_NOALLOC_MAX_ROWS)
+    return fail(RLT_ESHAPE, "B_cap %d exceeds the allocation-free step's maximum of %d rows", st->B_cap,
+                RLT_NOALLOC_MAX_ROWS);
+  if (io->flags & RLT_STEP_GRAPH)
+    return fail(RLT_EINVAL, "RLT_STEP_GRAPH allocates a graph: capture the allocation-free step yourself");
+  int* claim = g_scratch_ptr[c->device];
+  if (!claim) return fail(RLT_EHIP, "the fixed counter array of device %d is not resolved", c->device);
+  if ((rc = take_device_error(c))) return rc;
+  const bool prof = c->prof_on;  // the timing hook creates events: off for this call
+  c->prof_on = false;
+  rc = step_enqueue(c, st, io, (hipStream_t)stream, false, claim);
+  c->prof_on = prof;
+  return rc;
+}
+
+// argument checks shared by the decoder step entry points
+static int check_step(rlt_ctx* c, rlt_state* st, const rlt_step_io* io) {
   if (!c || !io) return fail(RLT_EINVAL, "null context or io");
   int rc = check_state(c, st);
   if (rc) return rc;
@@ -1145,6 +1205,12 @@ extern "C" int rlt_decoder_step(rlt_ctx* c, rlt_state* st, const rlt_step_io* io
   if (!(io->top_p == io->top_p)) return fail(RLT_EINVAL, "top_p is NaN");
   if ((io->flags & RLT_STEP_DEFER) && !(io->uniform ? io->sample_tok : io->argmax))
     return fail(RLT_EINVAL, "RLT_STEP_DEFER needs sample_tok (sampling) or argmax");
+  return RLT_OK;
+}
+
+extern "C" int rlt_decoder_step(rlt_ctx* c, rlt_state* st, const rlt_step_io* io, void* stream) {
+  int rc = check_step(c, st, io);
+  if (rc) return rc;
   if ((rc = take_device_error(c))) return rc;
   hipStream_t s = (hipStream_t)stream;
   if (!(io->flags & RLT_STEP_GRAPH)) return step_enqueue(c, st, io, s);

@@ -390,6 +390,8 @@ struct PostArgs {
   int B_cap;
 };
 void launch_poststep(const PostArgs& a, hipStream_t s);
+// counts[rows[i]] = 0 for i < n (a fill kernel: capturable)
+void launch_zero_rows(int* counts, const int* rows, int n, int B_cap, hipStream_t s);
 
 // ----------------------------------------------------------------------------
 // persistent step: the launches of a transition are recorded as phases and

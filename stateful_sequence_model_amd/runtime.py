@@ -176,7 +176,9 @@ class Decoder:
     def step(self, st: DecoderState, rows: torch.Tensor, e: torch.Tensor, mem: A.rlt_memory, *,
              consume_tok=None, s_out=None, logits=None, argmax=None, score_tok=None, logp=None,
              uniform=None, temperature=1.0, top_k=0, top_p=1.0, sample_tok=None, sample_logmu=None,
-             z_trace=None, graph=False, defer=False, stream=None) -> int:
+             z_trace=None, graph=False, defer=False, noalloc=False, stream=None) -> int:
+        """One transition of the listed rows (rlt_decoder_step, or with
+        noalloc=True rlt_decoder_step_noalloc, which allocates nothing)."""
         io = A.rlt_step_io()
         io.n = rows.numel()
         io.rows = rows.data_ptr()
@@ -197,7 +199,8 @@ class Decoder:
         io.flags = (A.RLT_STEP_GRAPH if graph else 0) | (A.RLT_STEP_DEFER if defer else 0)
         io.top_p = top_p
         self._keep = (io, st.c())
-        return A.rlt_decoder_step(self.ctx, self._keep[1], io, current_stream() if stream is None else stream)
+        fn = A.rlt_decoder_step_noalloc if noalloc else A.rlt_decoder_step
+        return fn(self.ctx, self._keep[1], io, current_stream() if stream is None else stream)
 
     def replay(self, st: DecoderState, lens: np.ndarray, splits: np.ndarray, e: torch.Tensor,
                mem: A.rlt_memory, tokens: torch.Tensor, logp: torch.Tensor, rows: Optional[np.ndarray] = None,
