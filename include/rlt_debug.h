@@ -55,6 +55,14 @@ typedef struct rlt_dbg_launch {
 int rlt_dbg_create(const rlt_config* cfg, const rlt_weights* w, int32_t max_rows, int32_t max_ctx,
                    const rlt_dbg_launch* opt, rlt_ctx** out);
 
+/* Tuning sweeps: force the shape of the operand-order products of later
+ * calls (rows per tile 32 * rb, waves nw, chunks in flight per wave pf,
+ * epilogue values loaded before (1) or after (0) the K loop, or -1 for the
+ * library's choice); rb = 0 restores the library's choice. Shapes change
+ * timing only, never results. Shapes without a compiled kernel fall back to
+ * the default. */
+int rlt_dbg_product_shape(rlt_ctx* ctx, int32_t rb, int32_t nw, int32_t pf, int32_t pre);
+
 /* Kernel classes for the timing hook below. */
 enum {
   RLT_PROF_XATTN = 0,     /* prefix cross-attention partials (eq. 2.15) */

@@ -279,7 +279,7 @@ __device__ __forceinline__ bf16x8_t load8(const uint16_t* p) {
 }
 
 // LDS floats used by gemm_bf16_body<MB>
-constexpr int gemm_lds_floats(int MB) { return 4 * MB * 16 * 32 + MB * 16 + 256; }
+constexpr int gemm_lds_floats(int MB) { return 4 * MB * 16 * 32 + MB * 16 + rowrstd_lds<16, 256>() * MB; }
 
 // One (pair, split, m-tile) tile of the product; block 256 (4 waves).
 template <int MB>
@@ -394,7 +394,7 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& g, const Epi<uint
   }
 }
 
-constexpr int SPLITK_LDS_FLOATS = 16 + 256;
+constexpr int SPLITK_LDS_FLOATS = 16 + rowrstd_lds<16, 256>();
 
 // Sum of the S split partials of (pair, 16-row block mt) in split order, then
 // the epilogue; block 256.

@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_tile(GemmArgs g, Epi<uint16_t
   uint16_t(*sA)[BM * LDR] = reinterpret_cast<uint16_t(*)[BM * LDR]>(smem);
   uint16_t(*sW)[BN * LDR] = reinterpret_cast<uint16_t(*)[BN * LDR]>(smem + 2 * BM * LDR * 2);
   __shared__ float s_rstd[BM];
-  __shared__ float s_part[4 * BM];
+  __shared__ float s_part[rowrstd_lds<BM, 256>()];
   // XCD-aware order: consecutive workgroup ids run on the 8 XCDs in turn, so
   // id b maps to tile (b % 8) * (T / 8) + b / 8 (ids past 8 * (T / 8) map to
   // themselves), m-tile fastest: the row tiles of one weight slice share an L2
@@ -248,42 +248,47 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_tile(GemmArgs g, Epi<uint16_t
 }
 
 // Product with both operands in fragment order (see pk_off): a workgroup owns
-// 32 RB rows x CB column pairs over the whole K, so
-// there is no K split and no partial traffic; its NW waves take the 64-wide
-// K chunks round-robin (wave w: chunks w, w + NW, ...) and load each chunk's
-// fragments straight into registers, every load instruction reading 1 KB of
-// consecutive bytes, PF chunks ahead. No LDS staging and no barrier inside the
-// K loop. Lanes of rows at or past M load no activations (zeros), so a call
-// of a few rows reads little more than the weights. The NW wave partials
-// are summed in LDS in wave order by the
-// epilogue threads (16 consecutive threads per row and column pair, as in the
-// other tiles). Tile order: workgroup b runs on XCD b % 8 and takes column
-// tile 8 (q / mtiles) + b % 8 and row tile q % mtiles (q = b / 8), so the row
-// tiles of one column tile share its weights in one L2.
-// PRE: the epilogue reads memory (residual, gains, rotary table) and loads it
-// before the K loop (registers that would otherwise halve the occupancy of
-// the larger tiles).
-// NW = 8 (with 4 chunks in flight per wave for the smallest tile) serves the
-// products of at most 256 column pairs: a compute unit holds only so many
-// loads in flight, and with few column tiles (64 workgroups for a 2048-wide
-// product at one row) the weights stream faster with twice the waves per
-// workgroup. NW is a function of the product's width only: it fixes the
-// order in which the K chunks are summed.
+// 32 RB rows x CB column pairs over the whole K (no K split, no partial
+// traffic) and loads each 64-wide K chunk's fragments straight into
+// registers, one load instruction reading 1 KB of consecutive bytes; no LDS
+// staging and no barrier in the K loop. The K loop is branch-free, so that
+// each chunk waits only for its own loads: lanes of rows at or past M load
+// the last row below M (the same addresses for all of them, so a call of a
+// few rows reads little more than the weights; those outputs are discarded),
+// and refills past a wave's last chunk re-read that chunk (never used).
+//
+// Summation order (the same for every launch shape, so that a row's result
+// does not depend on the call it is in): chunk c belongs to stream c % 8;
+// each stream accumulates its chunks in increasing c, each chunk as four
+// 16-wide MFMA steps (with TWO, the activations' first term, then their
+// second, per step); the 8 stream sums are combined by a fixed tree that adds
+// streams 4 apart, then 2 and 1 apart:
+//   ((s0 + s4) + (s2 + s6)) + ((s1 + s5) + (s3 + s7)).
+// NW waves (NW | 8) split the streams: wave w owns streams w + NW j
+// (SPW = 8 / NW of them, one accumulator set each) and takes chunks
+// w, w + NW, w + 2 NW, ... (chunk w + NW i feeds accumulator i % SPW); it adds
+// its own streams over the tree's wide strides (4 .. NW) in registers, and
+// the epilogue threads finish the narrow strides (NW / 2 .. 1) across waves
+// from LDS. NW, the tile and the prefetch depth PF are therefore free per
+// call: more waves keep more chunks in flight, fewer waves leave more
+// registers for larger tiles.
 // TWO: the activations carry a second bf16 term at A + a_lo (the rounding
-// remainder of the first): each step multiplies the first term, then the
-// second, into the same accumulator, so the product sees its float32 input to
-// about 16 significant bits while the weights stay bf16.
+// remainder of the first), so the product sees its float32 input to about 16
+// significant bits while the weights stay bf16.
+// Tile order: workgroup b runs on XCD b % 8 and takes column tile
+// 8 (q / mtiles) + b % 8 and row tile q % mtiles (q = b / 8), so the row
+// tiles of one column tile share its weights in one L2.
+// PRE: the epilogue's memory reads (residual, gains, rotary table) are issued
+// before the K loop.
 // grid: 8 * mtiles * ceil(ntiles / 8); block 64 NW.
-template <int RB, int CB, bool PRE, int NW, bool TWO>
+template <int RB, int CB, int NW, int PF, bool PRE, bool TWO>
 __global__ __launch_bounds__(64 * NW) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16_t> epi) {
-  // chunks in flight per wave (the two-term 1 x 1 tile keeps three: four
-  // would spill)
-  constexpr int R = 32 * RB, PF = NW == 8 && RB * CB == 1 ? (TWO ? 3 : 4) : 2, NT = 64 * NW;
+  constexpr int R = 32 * RB, NT = 64 * NW, SPW = 8 / NW;
+  static_assert(8 % NW == 0, "waves divide the 8 streams");
   constexpr int TILE = RB * CB * 16 * 64;  // floats of one wave's partial tile
-  static_assert((R * CB * 16) % NT == 0, "epilogue items per thread");
   __shared__ float red[NW * TILE];
   __shared__ float s_rstd[R];
-  __shared__ float s_part[4 * R];
+  __shared__ float s_part[rowrstd_lds<R, NT>()];
   const int mtiles = (g.M + R - 1) / R, ntiles = g.npairs / CB;
   const int b = blockIdx.x, q = b >> 3;
   const int mt = q % mtiles, nt = 8 * (q / mtiles) + (b & 7);
@@ -294,81 +299,113 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16
   const uint16_t* ap[RB];
   const uint16_t* wp[CB];
 #pragma unroll
-  for (int r = 0; r < RB; ++r) ap[r] = (const uint16_t*)g.A + ((int64_t)(mt * RB + r) * nchunk * 256 + lane) * 8;
+  for (int r = 0; r < RB; ++r) {
+    // this lane's row of block r, clamped below M (lane l holds row l % 32)
+    const int last = g.M - 1 - (m0 + 32 * r);
+    const int rl = last < 0 ? 0 : ((lane & 31) < last ? (lane & 31) : last);
+    ap[r] = (const uint16_t*)g.A + ((int64_t)(mt * RB + r) * nchunk * 256 + (lane & 32) + rl) * 8;
+  }
 #pragma unroll
   for (int c = 0; c < CB; ++c) wp[c] = (const uint16_t*)g.Wp + ((int64_t)(nt * CB + c) * nchunk * 256 + lane) * 8;
   const bool norm_here = g.ssq_in != nullptr;
   RowRstd<R, NT> rr(g, norm_here ? m0 : 0);
-  // this thread's epilogue items (16 consecutive threads per row and pair)
-  // and the values their epilogue reads, loaded now, in flight with the K loop
-  constexpr int NI = R * CB * 16 / NT;
-  const int c16 = tid & 15;
+  // epilogue items: (row, column pair) units of 16 consecutive threads
+  constexpr int NU = R * CB, NG = NT / 16, NI = (NU + NG - 1) / NG;
+  const int c16 = tid & 15, grp = tid >> 4;
   typename Epi<uint16_t>::Pre pre[PRE ? NI : 1];
 #pragma unroll
   for (int j = 0; j < (PRE ? NI : 0); ++j) {
-    const int it = (tid >> 4) + (NT / 16) * j;
+    // (rows clamped below M: loads without branches; rows at or past M are
+    // not stored)
+    const int it = grp + NG * j < NU ? grp + NG * j : NU - 1;
     const int row = it / CB, pc = it - row * CB;
     int ba, bb;
     pair_blocks(g, nt * CB + pc, ba, bb);
-    pre[j] = m0 + row < g.M ? epi.pre(m0 + row, ba * 16 + c16, bb * 16 + c16) : typename Epi<uint16_t>::Pre{};
+    pre[j] = epi.pre(m0 + row < g.M ? m0 + row : g.M - 1, ba * 16 + c16, bb * 16 + c16);
   }
   const int n = (nchunk - wave + NW - 1) / NW;  // chunks of this wave
   bf16x8_t ra[PF][RB][4], rw[PF][CB][4], rl[TWO ? PF : 1][RB][4];
-  f32x16_t acc[RB][CB];
+  f32x16_t acc[SPW][RB][CB];
 #pragma unroll
-  for (int r = 0; r < RB; ++r)
-#pragma unroll
-    for (int c = 0; c < CB; ++c)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[r][c][e] = 0.f;
-  bool live[RB];  // this lane's activation row exists
-#pragma unroll
-  for (int r = 0; r < RB; ++r) live[r] = m0 + 32 * r + (lane & 31) < g.M;
-  auto load = [&](int slot, int i) {
-    const int64_t off = (int64_t)(wave + NW * i) * 256 * 8;
+  for (int j = 0; j < SPW; ++j)
 #pragma unroll
     for (int r = 0; r < RB; ++r)
 #pragma unroll
-      for (int st = 0; st < 4; ++st) ra[slot][r][st] = live[r] ? load8(ap[r] + off + st * 512) : bf16x8_t{};
+      for (int c = 0; c < CB; ++c)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[j][r][c][e] = 0.f;
+  // chunk i of this wave into register slot `slot` (past the wave's last
+  // chunk: that chunk again, never computed)
+  const int clast = nchunk - 1;
+  auto load = [&](int slot, int i) {
+    const int cidx = wave + NW * i;
+    const int64_t off = (int64_t)(cidx < clast ? cidx : clast) * 256 * 8;
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+      for (int st = 0; st < 4; ++st) ra[slot][r][st] = load8(ap[r] + off + st * 512);
     if (TWO) {
 #pragma unroll
       for (int r = 0; r < RB; ++r)
 #pragma unroll
-        for (int st = 0; st < 4; ++st)
-          rl[TWO ? slot : 0][r][st] = live[r] ? load8(ap[r] + g.a_lo + off + st * 512) : bf16x8_t{};
+        for (int st = 0; st < 4; ++st) rl[TWO ? slot : 0][r][st] = load8(ap[r] + g.a_lo + off + st * 512);
     }
 #pragma unroll
     for (int c = 0; c < CB; ++c)
 #pragma unroll
       for (int st = 0; st < 4; ++st) rw[slot][c][st] = load8(wp[c] + off + st * 512);
   };
-  auto compute = [&](int slot) {
+  // chunk i of this wave (register slot `slot`) into accumulator set j
+  auto compute = [&](int slot, int j) {
 #pragma unroll
     for (int st = 0; st < 4; ++st)
 #pragma unroll
       for (int r = 0; r < RB; ++r)
 #pragma unroll
         for (int c = 0; c < CB; ++c) {
-          acc[r][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[slot][r][st], rw[slot][c][st], acc[r][c], 0, 0, 0);
+          acc[j][r][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[slot][r][st], rw[slot][c][st], acc[j][r][c], 0, 0, 0);
           if (TWO)
-            acc[r][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rl[TWO ? slot : 0][r][st], rw[slot][c][st], acc[r][c],
-                                                               0, 0, 0);
+            acc[j][r][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rl[TWO ? slot : 0][r][st], rw[slot][c][st],
+                                                                  acc[j][r][c], 0, 0, 0);
         }
   };
+  // Register slot p holds chunks i = p, p + PF, ...; chunk i feeds
+  // accumulator set i % SPW. The steady state is unrolled over a period of
+  // LCM(PF, SPW) chunks so that both indices are static.
+  constexpr int PER = (PF % SPW == 0) ? PF : (SPW % PF == 0 ? SPW : PF * SPW);
 #pragma unroll
-  for (int p = 0; p < PF; ++p)
-    if (p < n) load(p, p);
+  for (int p = 0; p < PF; ++p) load(p, p);
+  // steady state, branch-free: every refill is a chunk still to come
   int i = 0;
-  for (; i + PF <= n; i += PF) {
+  for (; i + PER + PF <= n; i += PER) {
 #pragma unroll
-    for (int p = 0; p < PF; ++p) {
-      compute(p);
-      if (i + p + PF < n) load(p, i + p + PF);
+    for (int u = 0; u < PER; ++u) {
+      compute(u % PF, u % SPW);
+      load(u % PF, i + u + PF);
     }
   }
+  // the rest (fewer than PER + PF chunks); i stays a multiple of PER (and
+  // of PF, SPW), so slot and accumulator indices continue as above
+  for (; i < n; i += PER) {
 #pragma unroll
-  for (int p = 0; p < PF; ++p)
-    if (i + p < n) compute(p);
+    for (int u = 0; u < PER; ++u)
+      if (i + u < n) {
+        compute(u % PF, u % SPW);
+        if (i + u + PF < n) load(u % PF, i + u + PF);
+      }
+  }
+  // this wave's streams over the tree's strides 4 .. NW (accumulator set j
+  // holds stream wave + NW j)
+#pragma unroll
+  for (int h = SPW / 2; h >= 1; h >>= 1)
+#pragma unroll
+    for (int j = 0; j < h; ++j)
+#pragma unroll
+      for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int c = 0; c < CB; ++c)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[j][r][c][e] += acc[j + h][r][c][e];
   // wave partials to LDS; C layout of a 32x32 block: acc[4 gg + qq] of lane l
   // is row 8 gg + 4 (l / 32) + qq, column l % 32
 #pragma unroll
@@ -376,33 +413,42 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16
 #pragma unroll
     for (int c = 0; c < CB; ++c)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) red[wave * TILE + ((r * CB + c) * 16 + e) * 64 + lane] = acc[r][c][e];
+      for (int e = 0; e < 16; ++e) red[wave * TILE + ((r * CB + c) * 16 + e) * 64 + lane] = acc[0][r][c][e];
   if (norm_here) rr.finish(g, m0, s_part, s_rstd);  // uniform branch: contains a barrier
   __syncthreads();
-  // same trip count on every thread; unrolled only where the prefetched
-  // values need static indices (the unrolled Q/K/V epilogue measured slower)
-  constexpr int EU = PRE ? NI : 1;
-#pragma unroll EU
+  // every 16-thread group runs the same trip count (the row sums of squares
+  // reduce over its 16 lanes); unrolled where the prefetched values need
+  // static indices
+#pragma unroll
   for (int j = 0; j < NI; ++j) {
-    const int it = (tid >> 4) + (NT / 16) * j;
+    const int it = grp + NG * j;
+    if (it >= NU) break;  // uniform within the 16-thread group
     const int row = it / CB, pc = it - row * CB;
     const int m = m0 + row, pair = nt * CB + pc;
     const int r32 = row & 31;
     const int ia = (((row >> 5) * CB + pc) * 16 + 4 * (r32 >> 3) + (r32 & 3)) * 64 + ((r32 >> 2) & 1) * 32 + c16;
     const int ib = ia + 16;
-    float va = red[ia], vb = red[ib];
+    // the tree's strides NW / 2 .. 1 across the waves
+    float va[NW], vb[NW];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) {
-      va += red[w * TILE + ia];
-      vb += red[w * TILE + ib];
+    for (int w = 0; w < NW; ++w) {
+      va[w] = red[w * TILE + ia];
+      vb[w] = red[w * TILE + ib];
     }
+#pragma unroll
+    for (int h = NW / 2; h >= 1; h >>= 1)
+#pragma unroll
+      for (int w = 0; w < h; ++w) {
+        va[w] += va[w + h];
+        vb[w] += vb[w + h];
+      }
     int ba, bb;
     pair_blocks(g, pair, ba, bb);
     float sq = 0.f;
     if (m < g.M) {
       const float rs = norm_here ? s_rstd[row] : 1.f;
-      sq = PRE ? epi.apply(m, ba * 16 + c16, va, bb * 16 + c16, vb, rs, pre[PRE ? j : 0])
-               : epi(m, ba * 16 + c16, va, bb * 16 + c16, vb, rs);
+      sq = PRE ? epi.apply(m, ba * 16 + c16, va[0], bb * 16 + c16, vb[0], rs, pre[PRE ? j : 0])
+               : epi(m, ba * 16 + c16, va[0], bb * 16 + c16, vb[0], rs);
     }
     if (g.ssq_out) {
       sq = sum16(sq);
@@ -509,45 +555,29 @@ void launch_gemm(int dtype, const GemmArgs& g0, const EpiArgs& e, hipStream_t s)
     if (record_phase(bad)) return;
     Epi<uint16_t> epi{e};
     const bool two = g.a_lo != 0;
-    // The waves split the K loop (wave w sums chunks w, w + NW, ...; the
-    // partials are added in wave order), so NW fixes the summation order and
-    // is chosen from the product's width alone, never from the call's rows:
-    // eight waves for products of at most 256 column pairs (8192 columns),
-    // which at the decoder's batch sizes need about one workgroup per compute
-    // unit (the 2048-wide products at 1-512 rows, Q/K/V at 1-128), four for
-    // wider ones (gate/up at 5504: 8 waves measured 15.6 vs 13.0 us at 344
-    // workgroups; the vocabulary).
-    const bool w8 = g.npairs <= 256;
-    // the 64 x 2 tile would spill registers with eight waves and two terms:
-    // 64 x 1 then (the tile shape leaves every output's arithmetic unchanged)
-    if (two && w8) g.cb = 1;
     const int mtiles = (g.M + 32 * g.rb - 1) / (32 * g.rb), ntiles = g.npairs / g.cb;
     dim3 grid(8 * mtiles * ((ntiles + 7) / 8));
-    // (the Q/K/V product's 64 x 2 tile measured slower with it, 26.4 vs 19.9
-    // us at 128 rows, and slower again with table lookups in its epilogue)
-    const bool pre = e.kind == EPI_RESID || e.kind == EPI_QROT;
-#define RLT_PK2(RB_, CB_, PRE_, NW_)                                                                    \
-  do {                                                                                                  \
-    if (two) hipLaunchKernelGGL((k_gemm_bf16_pk<RB_, CB_, PRE_, NW_, true>), grid, dim3(64 * NW_), 0, s, g, epi); \
-    else hipLaunchKernelGGL((k_gemm_bf16_pk<RB_, CB_, PRE_, NW_, false>), grid, dim3(64 * NW_), 0, s, g, epi);    \
+    // the Q/K/V product's epilogue computes its rotary angles (prefetching a
+    // table lookup measured slower)
+    const bool pre = g.pre >= 0 ? g.pre != 0 : (e.kind == EPI_RESID || e.kind == EPI_QROT);
+#define RLT_PK2(RB_, CB_, NW_, PF_, PRE_)                                                                     \
+  do {                                                                                                     \
+    if (two) hipLaunchKernelGGL((k_gemm_bf16_pk<RB_, CB_, NW_, PF_, PRE_, true>), grid, dim3(64 * NW_), 0, s, g, epi); \
+    else hipLaunchKernelGGL((k_gemm_bf16_pk<RB_, CB_, NW_, PF_, PRE_, false>), grid, dim3(64 * NW_), 0, s, g, epi);    \
   } while (0)
-#define RLT_PK(RB_, CB_, NW_)              \
-  do {                                     \
-    if (pre) RLT_PK2(RB_, CB_, true, NW_); \
-    else RLT_PK2(RB_, CB_, false, NW_);    \
+#define RLT_PK(RB_, CB_, NW_, PF_)              \
+  do {                                          \
+    if (pre) RLT_PK2(RB_, CB_, NW_, PF_, true); \
+    else RLT_PK2(RB_, CB_, NW_, PF_, false);    \
   } while (0)
-    if (g.rb == 2 && g.cb == 2) {
-      // eight waves (one term only) load the epilogue's values after the K
-      // loop (prefetched they would spill)
-      if (w8) hipLaunchKernelGGL((k_gemm_bf16_pk<2, 2, false, 8, false>), grid, dim3(512), 0, s, g, epi);
-      else RLT_PK(2, 2, 4);
-    } else if (g.rb == 2) {
-      if (w8) RLT_PK(2, 1, 8);
-      else RLT_PK(2, 1, 4);
-    } else {
-      if (w8) RLT_PK(1, 1, 8);
-      else RLT_PK(1, 1, 4);
+#define RLT_SHAPE(RB_, NW_, PF_) if (g.rb == RB_ && g.nw == NW_ && g.pf == PF_) RLT_PK(RB_, 1, NW_, PF_); else
+    // shapes the host may pick (none changes the arithmetic, see the kernel)
+    RLT_SHAPE(1, 8, 2) RLT_SHAPE(1, 8, 3) RLT_SHAPE(1, 8, 4) RLT_SHAPE(1, 4, 4) RLT_SHAPE(1, 4, 8)
+    RLT_SHAPE(2, 8, 1) RLT_SHAPE(2, 8, 2) RLT_SHAPE(2, 4, 2) RLT_SHAPE(2, 4, 4) {
+      if (g.rb == 2) RLT_PK(2, 1, 8, 2);
+      else RLT_PK(1, 1, 8, 4);
     }
+#undef RLT_SHAPE
 #undef RLT_PK
 #undef RLT_PK2
     return;

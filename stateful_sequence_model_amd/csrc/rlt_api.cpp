@@ -105,6 +105,9 @@ struct rlt_ctx {
   // fragment-order buffer lies this many elements after the first
   bool one_term;
   int64_t lo_X, lo_o, lo_h, lo_act;
+  // forced operand-order product shape (tuning sweeps): rows 32 * rb, waves,
+  // chunks in flight, epilogue prefetch (-1: the library's choice); 0 = none
+  int shape_rb, shape_nw, shape_pf, shape_pre;
   // duplicate-row detection of rlt_decoder_step: per state row, the number
   // of slots of the current call naming it (zero between calls)
   int* claim;
@@ -660,15 +663,32 @@ struct Gemm {
     g.inv_d = 1.0f / (float)c->cfg.d_model;
     g.eps = c->cfg.rms_eps;
     if (Wp) {
-      // tile shape: the largest of 64 x 2 pairs, 64 x 1, 32 x 1 that still
-      // gives 160 workgroups (measured per product shape at 32-128 rows);
-      // 32 rows at most for calls of at most 32 rows
+      // tile shape (none of these choices changes the arithmetic: fixed
+      // stream order, see the kernel), measured per product at 1 and 128
+      // rows, reference depth, over 4/8 waves, 1-8 chunks in flight and
+      // 32/64-row tiles: products of 128 or more column pairs (Q/K/V,
+      // gate/up, vocabulary) take four waves with four chunks in flight
+      // each and the epilogue's reads after the K loop (register budget);
+      // the 2048-wide ones eight waves, two chunks in flight (three past 32
+      // rows). 64-row tiles were slower at every size measured.
       g.Wp = Wp;
-      auto wgs = [&](int rb, int cb) { return (g.npairs % cb ? 0 : g.npairs / cb) * ((n + 32 * rb - 1) / (32 * rb)); };
-      if (n <= 32) g.rb = 1, g.cb = 1;
-      else if (wgs(2, 2) >= 160) g.rb = 2, g.cb = 2;
-      else if (wgs(2, 1) >= 160) g.rb = 2, g.cb = 1;
-      else g.rb = 1, g.cb = 1;
+      g.cb = 1;
+      g.rb = 1;
+      if (g.npairs >= 128) {
+        g.nw = 4;
+        g.pf = 4;
+        g.pre = 0;
+      } else {
+        g.nw = 8;
+        g.pf = n > 32 ? 3 : 2;
+        g.pre = -1;
+      }
+      if (c->shape_rb > 0) {
+        g.rb = c->shape_rb;
+        g.nw = c->shape_nw;
+        g.pf = c->shape_pf;
+        g.pre = c->shape_pre;
+      }
     } else if (c->dt == 1 && n > 32 && g.npairs % 2 == 0 && K % 64 == 0) {
       // LDS tile of 128 rows x 64 columns (128 when that still leaves two
       // workgroups per compute unit); K split while each split adds a
@@ -1778,6 +1798,17 @@ extern "C" int rlt_dbg_gemm_packed(rlt_ctx* c, const void* A, const void* W, int
   if (Ap) (void)hipFree(Ap);
   if (Wp) (void)hipFree(Wp);
   return rc;
+}
+
+extern "C" int rlt_dbg_product_shape(rlt_ctx* c, int32_t rb, int32_t nw, int32_t pf, int32_t pre) {
+  if (!c) return fail(RLT_EINVAL, "null context");
+  if (rb != 0 && (rb < 1 || rb > 2 || (nw != 4 && nw != 8) || pf < 1 || pf > 8 || pre < -1 || pre > 1))
+    return fail(RLT_EINVAL, "product shape");
+  c->shape_rb = rb;
+  c->shape_nw = nw;
+  c->shape_pf = pf;
+  c->shape_pre = pre;
+  return RLT_OK;
 }
 
 extern "C" int rlt_dbg_profile(rlt_ctx* c, int32_t enable) {

@@ -104,6 +104,8 @@ struct GemmArgs {
   const void* Wp;         // bf16: the same weights in fragment order, virtual column
                           // pairs as 32-row blocks (pair p = block p), or null
   int rb, cb;             // fragment-order tile: 32 rb rows x cb column pairs
+  int nw, pf;             // fragment-order tile: waves per workgroup, chunks in flight per wave
+  int pre;                // fragment-order tile: -1 = by epilogue kind, 0/1 = epilogue values after / before the K loop
   int nseg, seg_rows;
   int K;
   int npairs;             // output handled as pairs of 16-column blocks
@@ -150,47 +152,61 @@ __device__ __forceinline__ float row_rstd(const GemmArgs& g, int m) {
 // order whatever R and NT are (so that a row's rstd, like every other
 // reduction of a product, does not depend on the tile it lands in): unit u
 // goes to part u % 4, each part adds its units in increasing u, and the row's
-// sum is ((p0 + p1) + p2) + p3. Thread (part slot, row) loads the first RU
-// units of its part(s) into registers when constructed (before the main
-// loop, so the loads are in flight with it); finish() adds the rest and
-// combines the parts through LDS. Rows at or past M load nothing (their rstd
-// is never used).
+// sum is ((p0 + p1) + p2) + p3.
+// Loads: the PA = NT / R threads of a row take the row's first PA * RU
+// units round-robin (thread slot sl: units sl, sl + PA, ...) into registers
+// when constructed (before the main loop, so the loads are in flight with
+// it); finish() stages them in LDS and the four part sums are then formed by
+// one thread each, reading units in increasing order (units past PA * RU,
+// only for very wide rows, straight from memory). Rows at or past M load
+// nothing (their rstd is never used).
 template <int R, int NT = 256>
 struct RowRstd {
-  static constexpr int CP = 4;                      // parts of the fixed order
-  static constexpr int PA = NT / R;                 // part slots per row
-  static_assert(PA >= 1 && (PA >= CP ? PA % CP == 0 : CP % PA == 0), "part slots");
-  static constexpr int CPT = PA >= CP ? 1 : CP / PA;  // parts per thread
-  static constexpr int RU = 16 / CPT;               // units per part in registers
-  float v[CPT][RU];
+  static constexpr int PA = NT / R;                 // threads per row
+  static constexpr int RU = PA >= 16 ? 4 : (PA >= 4 ? 64 / PA : 16);  // units per thread in registers
+  static constexpr int NU = PA * RU;                // units staged
+  static_assert(PA >= 2 && (PA & (PA - 1)) == 0, "threads per row");
+  float v[RU];
   __device__ __forceinline__ RowRstd(const GemmArgs& g, int m0) {
-    const int row = threadIdx.x % R, slot = threadIdx.x / R;
-    const bool live = g.ssq_in && m0 + row < g.M;
+    const int row = threadIdx.x % R, sl = threadIdx.x / R;
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int cp = slot + c * PA;
+    for (int j = 0; j < RU; ++j) v[j] = 0.f;
+    if (!g.ssq_in) return;  // uniform
+    // no branches around the loads (rows clamped below M: those rows' rstd
+    // is never used; units clamped, then zeroed past the last)
+    const int m = m0 + row < g.M ? m0 + row : g.M - 1;
 #pragma unroll
-      for (int j = 0; j < RU; ++j) {
-        const int u = cp + CP * j;
-        v[c][j] = (live && cp < CP && u < g.ssq_units) ? g.ssq_in[(int64_t)u * g.M_pad + m0 + row] : 0.f;
-      }
+    for (int j = 0; j < RU; ++j) {
+      const int u = sl + PA * j;
+      const float x = g.ssq_in[(int64_t)(u < g.ssq_units ? u : g.ssq_units - 1) * g.M_pad + m];
+      v[j] = u < g.ssq_units ? x : 0.f;
     }
   }
-  // s_part: LDS [CP][R]; s_rstd: LDS [R]; contains one __syncthreads
+  // s_part: LDS [NU][R] floats (the staged units; its first 4 R floats then
+  // hold the part sums); s_rstd: LDS [R]; contains two __syncthreads
   __device__ __forceinline__ void finish(const GemmArgs& g, int m0, float* s_part, float* s_rstd) {
-    const int row = threadIdx.x % R, slot = threadIdx.x / R;
+    const int row = threadIdx.x % R, sl = threadIdx.x / R;
+#pragma unroll
+    for (int j = 0; j < RU; ++j) s_part[(sl + PA * j) * R + row] = v[j];
+    __syncthreads();
+    // the threads of slots 0 .. 3 form the part sums (slot sl: parts sl, sl + PA, ...)
+    constexpr int CPT = PA >= 4 ? 1 : 4 / PA;
+    float a[CPT];
+    const int nst = g.ssq_units < NU ? g.ssq_units : NU;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const int cp = slot + c * PA;
-      if (cp < CP) {
-        float a = 0.f;
-#pragma unroll
-        for (int j = 0; j < RU; ++j) a += v[c][j];
+      const int cp = sl + PA * c;
+      a[c] = 0.f;
+      if (cp < 4) {
+        for (int u = cp; u < nst; u += 4) a[c] += s_part[u * R + row];
         if (m0 + row < g.M)
-          for (int u = cp + CP * RU; u < g.ssq_units; u += CP) a += g.ssq_in[(int64_t)u * g.M_pad + m0 + row];
-        s_part[cp * R + row] = a;
+          for (int u = NU + cp; u < g.ssq_units; u += 4) a[c] += g.ssq_in[(int64_t)u * g.M_pad + m0 + row];
       }
     }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < CPT; ++c)
+      if (sl + PA * c < 4) s_part[(sl + PA * c) * R + row] = a[c];
     __syncthreads();
     if (threadIdx.x < R) {
       const float s = ((s_part[threadIdx.x] + s_part[R + threadIdx.x]) + s_part[2 * R + threadIdx.x]) +
@@ -199,6 +215,10 @@ struct RowRstd {
     }
   }
 };
+
+// LDS floats RowRstd<R, NT>::finish needs for s_part
+template <int R, int NT>
+constexpr int rowrstd_lds() { return RowRstd<R, NT>::NU * R; }
 
 // 16-row blocks per matrix-product tile for an M-row call (tile <= 64 rows;
 // larger M runs several row tiles)
