@@ -56,12 +56,14 @@ int rlt_dbg_create(const rlt_config* cfg, const rlt_weights* w, int32_t max_rows
                    const rlt_dbg_launch* opt, rlt_ctx** out);
 
 /* Tuning sweeps: force the shape of the operand-order products of later
- * calls (rows per tile 32 * rb, waves nw, chunks in flight per wave pf,
- * epilogue values loaded before (1) or after (0) the K loop, or -1 for the
- * library's choice); rb = 0 restores the library's choice. Shapes change
- * timing only, never results. Shapes without a compiled kernel fall back to
- * the default. */
-int rlt_dbg_product_shape(rlt_ctx* ctx, int32_t rb, int32_t nw, int32_t pf, int32_t pre);
+ * calls. lt > 0: the staged 128-row tile split over lt workgroups per tile
+ * (1, 2, 4 or 8; rb, cb, pf, pre ignored). lt = 0: the register tile of
+ * 32 * rb rows and cb column pairs with pf chunks in flight per wave, the
+ * epilogue's values loaded before (pre = 1) or after (0) the K loop, or by
+ * epilogue kind (-1). rb = 0 restores the library's choice. Shapes change
+ * timing only, never results; shapes without a compiled kernel fall back to
+ * the default register tile. */
+int rlt_dbg_product_shape(rlt_ctx* ctx, int32_t rb, int32_t cb, int32_t lt, int32_t pf, int32_t pre);
 
 /* Kernel classes for the timing hook below. */
 enum {

@@ -134,7 +134,7 @@ _SIGS = {
                                  C.POINTER(rlt_dbg_launch), C.POINTER(P)]),
     "rlt_dbg_gemm": (C.c_int, [P, P, P, i32, i32, i32, P, P]),
     "rlt_dbg_gemm_packed": (C.c_int, [P, P, P, i32, i32, i32, P, P]),
-    "rlt_dbg_product_shape": (C.c_int, [P, i32, i32, i32, i32]),
+    "rlt_dbg_product_shape": (C.c_int, [P, i32, i32, i32, i32, i32]),
     "rlt_dbg_profile": (C.c_int, [P, i32]),
     "rlt_dbg_profile_read": (C.c_int, [P, i32, C.POINTER(C.c_double), C.POINTER(C.c_int64)]),
 }
@@ -271,8 +271,8 @@ def rlt_dbg_gemm_packed(ctx: int, A: int, W: int, M: int, N: int, K: int, out: i
     return lib().rlt_dbg_gemm_packed(ctx, A, W, M, N, K, out, stream)
 
 
-def rlt_dbg_product_shape(ctx: int, rb: int, nw: int, pf: int, pre: int) -> int:
-    return lib().rlt_dbg_product_shape(ctx, rb, nw, pf, pre)
+def rlt_dbg_product_shape(ctx: int, rb: int, cb: int, lt: int, pf: int, pre: int) -> int:
+    return lib().rlt_dbg_product_shape(ctx, rb, cb, lt, pf, pre)
 
 
 def rlt_dbg_profile(ctx: int, enable: int) -> int:

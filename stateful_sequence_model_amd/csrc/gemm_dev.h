@@ -4,6 +4,13 @@
 #pragma once
 #include "rlt_internal.h"
 
+// No contraction of multiplies and adds into fused multiply-adds below: the
+// epilogues are inlined into several kernels (and into different points of
+// one kernel), and the compiler's choice to fuse depends on the context, so
+// the same expression could round differently from one launch shape to
+// another.
+#pragma clang fp contract(off)
+
 namespace rlt {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
@@ -45,8 +52,10 @@ struct Epi {
     y = yr;
   }
   // rotary transform of the pair (x_i, x_{i+dh/2}) of one head at position t
+  // (the table when it covers t, like the prefetching epilogue: the same
+  // angle values on every path)
   __device__ __forceinline__ void rotate(int m, int c_in_head, float& x, float& y) const {
-    rot(rope_cs(a.rows.t_row[m], c_in_head), x, y);
+    rot(rope_cs(a.rows.t_row[m], c_in_head, true), x, y);
   }
 
   // EPI_MEMKV for a row whose position t (> 0) and destination offset

@@ -247,31 +247,65 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_tile(GemmArgs g, Epi<uint16_t
   }
 }
 
-// Product with both operands in fragment order (see pk_off): a workgroup owns
-// 32 RB rows x CB column pairs over the whole K (no K split, no partial
-// traffic) and loads each 64-wide K chunk's fragments straight into
-// registers, one load instruction reading 1 KB of consecutive bytes; no LDS
-// staging and no barrier in the K loop. The K loop is branch-free, so that
-// each chunk waits only for its own loads: lanes of rows at or past M load
-// the last row below M (the same addresses for all of them, so a call of a
-// few rows reads little more than the weights; those outputs are discarded),
-// and refills past a wave's last chunk re-read that chunk (never used).
-//
-// Summation order (the same for every launch shape, so that a row's result
-// does not depend on the call it is in): chunk c belongs to stream c % 8;
-// each stream accumulates its chunks in increasing c, each chunk as four
-// 16-wide MFMA steps (with TWO, the activations' first term, then their
-// second, per step); the 8 stream sums are combined by a fixed tree that adds
-// streams 4 apart, then 2 and 1 apart:
-//   ((s0 + s4) + (s2 + s6)) + ((s1 + s5) + (s3 + s7)).
-// NW waves (NW | 8) split the streams: wave w owns streams w + NW j
-// (SPW = 8 / NW of them, one accumulator set each) and takes chunks
-// w, w + NW, w + 2 NW, ... (chunk w + NW i feeds accumulator i % SPW); it adds
-// its own streams over the tree's wide strides (4 .. NW) in registers, and
-// the epilogue threads finish the narrow strides (NW / 2 .. 1) across waves
-// from LDS. NW, the tile and the prefetch depth PF are therefore free per
-// call: more waves keep more chunks in flight, fewer waves leave more
-// registers for larger tiles.
+// Summation order of the products with both operands in fragment order (the
+// same for every kernel and launch shape below, so that a row's result does
+// not depend on the call it is in, nor on how the call is tiled):
+//   * the K range is n = K / 64 chunks of 64, cut into 8 streams; stream s
+//     holds the contiguous chunks [s n / 8, (s + 1) n / 8) (floor; empty
+//     streams are zero);
+//   * a stream accumulates its chunks in increasing order, each chunk as four
+//     16-wide v_mfma_f32_32x32x16_bf16 steps starting from zero (with two
+//     activation terms: per step the first term, then the second);
+//   * the 8 stream sums combine by a balanced tree of neighbours:
+//       ((s0 + s1) + (s2 + s3)) + ((s4 + s5) + (s6 + s7)).
+// A group of 2^j consecutive streams is a subtree, so the work can be split
+// over waves, over workgroups (partials combined by k_pk_combine), or run in
+// sequence by one wave that keeps finished subtrees on a small stack.
+__device__ __forceinline__ int stream_begin(int nchunk, int s) { return (s * nchunk) >> 3; }
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// Fold the running sum r of stream j (of a group of Q) into the stack of
+// finished subtrees (st[l] holds a subtree of 2^l streams; log2 Q levels);
+// after the last stream r holds the group's sum. r restarts at zero
+// otherwise.
+template <int Q>
+constexpr int fold_levels() { return Q >= 8 ? 3 : (Q >= 4 ? 2 : 1); }
+template <int Q>
+__device__ __forceinline__ void stream_fold(int j, f32x16_t& r, f32x16_t (&st)[fold_levels<Q>()]) {
+  f32x16_t v = r;
+  int t = j + 1, l = 0;
+#pragma unroll
+  for (int h = 0; h < 3; ++h)
+    if ((t & 1) == 0 && (1 << h) < Q) {
+      v = st[h] + v;
+      t >>= 1;
+      l = h + 1;
+    } else {
+      break;
+    }
+  if (j == Q - 1) {
+    r = v;
+  } else {
+#pragma unroll
+    for (int h = 0; h < fold_levels<Q>(); ++h)
+      if (h == l) st[h] = v;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) r[e] = 0.f;
+  }
+}
+
+// Product for calls of up to 64 rows, both operands in fragment order (see
+// pk_off): a workgroup owns 32 RB rows x CB column pairs over the whole K;
+// its 8 waves are the 8 streams, each loading its chunks' fragments straight
+// into registers (one load instruction reads 1 KB of consecutive bytes; no
+// LDS staging and no barrier in the K loop). The K loop is branch-free, so
+// that each chunk waits only for its own loads: lanes of rows at or past M
+// load the last row below M (the same addresses for all of them, so a call
+// of a few rows reads little more than the weights; those outputs are
+// discarded), and loads past a wave's last chunk re-read that chunk (never
+// used). The epilogue threads add the waves' sums by the stream tree, from
+// LDS.
 // TWO: the activations carry a second bf16 term at A + a_lo (the rounding
 // remainder of the first), so the product sees its float32 input to about 16
 // significant bits while the weights stay bf16.
@@ -280,11 +314,10 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_tile(GemmArgs g, Epi<uint16_t
 // tiles of one column tile share its weights in one L2.
 // PRE: the epilogue's memory reads (residual, gains, rotary table) are issued
 // before the K loop.
-// grid: 8 * mtiles * ceil(ntiles / 8); block 64 NW.
-template <int RB, int CB, int NW, int PF, bool PRE, bool TWO>
-__global__ __launch_bounds__(64 * NW) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16_t> epi) {
-  constexpr int R = 32 * RB, NT = 64 * NW, SPW = 8 / NW;
-  static_assert(8 % NW == 0, "waves divide the 8 streams");
+// grid: 8 * mtiles * ceil(ntiles / 8); block 512.
+template <int RB, int CB, int PF, bool PRE, bool TWO>
+__global__ __launch_bounds__(512) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16_t> epi) {
+  constexpr int NW = 8, R = 32 * RB, NT = 64 * NW;
   constexpr int TILE = RB * CB * 16 * 64;  // floats of one wave's partial tile
   __shared__ float red[NW * TILE];
   __shared__ float s_rstd[R];
@@ -323,22 +356,21 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16
     pair_blocks(g, nt * CB + pc, ba, bb);
     pre[j] = epi.pre(m0 + row < g.M ? m0 + row : g.M - 1, ba * 16 + c16, bb * 16 + c16);
   }
-  const int n = (nchunk - wave + NW - 1) / NW;  // chunks of this wave
+  // this wave's stream: chunks [c0, c0 + n); c0 < nchunk also when n = 0
+  const int c0 = stream_begin(nchunk, wave), n = stream_begin(nchunk, wave + 1) - c0;
+  const int clast = n > 0 ? c0 + n - 1 : c0;
   bf16x8_t ra[PF][RB][4], rw[PF][CB][4], rl[TWO ? PF : 1][RB][4];
-  f32x16_t acc[SPW][RB][CB];
+  f32x16_t acc[RB][CB];
 #pragma unroll
-  for (int j = 0; j < SPW; ++j)
+  for (int r = 0; r < RB; ++r)
 #pragma unroll
-    for (int r = 0; r < RB; ++r)
+    for (int c = 0; c < CB; ++c)
 #pragma unroll
-      for (int c = 0; c < CB; ++c)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[j][r][c][e] = 0.f;
-  // chunk i of this wave into register slot `slot` (past the wave's last
-  // chunk: that chunk again, never computed)
-  const int clast = nchunk - 1;
+      for (int e = 0; e < 16; ++e) acc[r][c][e] = 0.f;
+  // chunk i of the stream into register slot `slot` (past the last chunk:
+  // that chunk again, never computed)
   auto load = [&](int slot, int i) {
-    const int cidx = wave + NW * i;
+    const int cidx = c0 + i;
     const int64_t off = (int64_t)(cidx < clast ? cidx : clast) * 256 * 8;
 #pragma unroll
     for (int r = 0; r < RB; ++r)
@@ -355,65 +387,47 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16
 #pragma unroll
       for (int st = 0; st < 4; ++st) rw[slot][c][st] = load8(wp[c] + off + st * 512);
   };
-  // chunk i of this wave (register slot `slot`) into accumulator set j
-  auto compute = [&](int slot, int j) {
+  auto compute = [&](int slot) {
 #pragma unroll
     for (int st = 0; st < 4; ++st)
 #pragma unroll
       for (int r = 0; r < RB; ++r)
 #pragma unroll
         for (int c = 0; c < CB; ++c) {
-          acc[j][r][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[slot][r][st], rw[slot][c][st], acc[j][r][c], 0, 0, 0);
+          acc[r][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[slot][r][st], rw[slot][c][st], acc[r][c], 0, 0, 0);
           if (TWO)
-            acc[j][r][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rl[TWO ? slot : 0][r][st], rw[slot][c][st],
-                                                                  acc[j][r][c], 0, 0, 0);
+            acc[r][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rl[TWO ? slot : 0][r][st], rw[slot][c][st], acc[r][c],
+                                                               0, 0, 0);
         }
   };
-  // Register slot p holds chunks i = p, p + PF, ...; chunk i feeds
-  // accumulator set i % SPW. The steady state is unrolled over a period of
-  // LCM(PF, SPW) chunks so that both indices are static.
-  constexpr int PER = (PF % SPW == 0) ? PF : (SPW % PF == 0 ? SPW : PF * SPW);
 #pragma unroll
   for (int p = 0; p < PF; ++p) load(p, p);
   // steady state, branch-free: every refill is a chunk still to come
   int i = 0;
-  for (; i + PER + PF <= n; i += PER) {
+  for (; i + 2 * PF <= n; i += PF) {
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      compute(u % PF, u % SPW);
-      load(u % PF, i + u + PF);
+    for (int u = 0; u < PF; ++u) {
+      compute(u);
+      load(u, i + u + PF);
     }
   }
-  // the rest (fewer than PER + PF chunks); i stays a multiple of PER (and
-  // of PF, SPW), so slot and accumulator indices continue as above
-  for (; i < n; i += PER) {
+  // the rest (fewer than 2 PF chunks); i stays a multiple of PF
+  for (; i < n; i += PF) {
 #pragma unroll
-    for (int u = 0; u < PER; ++u)
+    for (int u = 0; u < PF; ++u)
       if (i + u < n) {
-        compute(u % PF, u % SPW);
-        if (i + u + PF < n) load(u % PF, i + u + PF);
+        compute(u);
+        if (i + u + PF < n) load(u, i + u + PF);
       }
   }
-  // this wave's streams over the tree's strides 4 .. NW (accumulator set j
-  // holds stream wave + NW j)
-#pragma unroll
-  for (int h = SPW / 2; h >= 1; h >>= 1)
-#pragma unroll
-    for (int j = 0; j < h; ++j)
-#pragma unroll
-      for (int r = 0; r < RB; ++r)
-#pragma unroll
-        for (int c = 0; c < CB; ++c)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc[j][r][c][e] += acc[j + h][r][c][e];
-  // wave partials to LDS; C layout of a 32x32 block: acc[4 gg + qq] of lane l
+  // stream sums to LDS; C layout of a 32x32 block: acc[4 gg + qq] of lane l
   // is row 8 gg + 4 (l / 32) + qq, column l % 32
 #pragma unroll
   for (int r = 0; r < RB; ++r)
 #pragma unroll
     for (int c = 0; c < CB; ++c)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) red[wave * TILE + ((r * CB + c) * 16 + e) * 64 + lane] = acc[0][r][c][e];
+      for (int e = 0; e < 16; ++e) red[wave * TILE + ((r * CB + c) * 16 + e) * 64 + lane] = acc[r][c][e];
   if (norm_here) rr.finish(g, m0, s_part, s_rstd);  // uniform branch: contains a barrier
   __syncthreads();
   // every 16-thread group runs the same trip count (the row sums of squares
@@ -428,7 +442,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16
     const int r32 = row & 31;
     const int ia = (((row >> 5) * CB + pc) * 16 + 4 * (r32 >> 3) + (r32 & 3)) * 64 + ((r32 >> 2) & 1) * 32 + c16;
     const int ib = ia + 16;
-    // the tree's strides NW / 2 .. 1 across the waves
+    // the stream tree: neighbours, then pairs 2 apart, then 4 apart
     float va[NW], vb[NW];
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
@@ -436,9 +450,9 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16
       vb[w] = red[w * TILE + ib];
     }
 #pragma unroll
-    for (int h = NW / 2; h >= 1; h >>= 1)
+    for (int h = 1; h < NW; h <<= 1)
 #pragma unroll
-      for (int w = 0; w < h; ++w) {
+      for (int w = 0; w < NW; w += 2 * h) {
         va[w] += va[w + h];
         vb[w] += vb[w + h];
       }
@@ -454,6 +468,223 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16
       sq = sum16(sq);
       if (c16 == 0 && m < g.M) g.ssq_out[(int64_t)pair * g.M_pad + m] = sq;
     }
+  }
+}
+
+// Product for calls of more than 64 rows, both operands in fragment order:
+// a workgroup owns 128 rows (4 row blocks) x 2 column pairs and a group of Q
+// consecutive streams (8 / Q workgroups per tile split the K range). Each
+// 64-wide chunk of both operands (128 x 64 activations, one or two terms, and
+// 64 x 64 weights: 40 KB with two terms) is staged once into LDS by all 512
+// threads (16-byte pieces; one wave load reads 1 KB of consecutive bytes and
+// writes it to consecutive LDS), so the weights are read once per 128 rows
+// and the activations once per 64 columns. Wave w computes block (w / 2,
+// w % 2) from LDS, running through its group's streams in order and folding
+// each finished stream into a stack of subtrees (stream_fold), which gives
+// the stream tree's order exactly. Three LDS buffers: while a chunk is
+// multiplied, each wave reads the next chunk's fragments into registers and
+// the workgroup writes the one after into the third buffer (from registers
+// loaded two chunks ahead); one barrier per chunk.
+// Q = 8 (one group): the epilogue runs here; otherwise each workgroup writes
+// its group sum (rows below M) to g.partial[group] and k_pk_combine finishes.
+// Rows past the last 32-row block below M load that block (discarded).
+// grid: 8 * (mtiles * G) * ceil(ntiles / 8), G = 8 / Q; block 512.
+template <int Q, bool TWO>
+__global__ __launch_bounds__(512) void k_gemm_bf16_lt(GemmArgs g, Epi<uint16_t> epi) {
+  constexpr int NT = 512, R = 128, RBK = 4, NCB = 2, G = 8 / Q, TERMS = TWO ? 2 : 1, NF = 4 * (TERMS + 1);
+  constexpr int A_PIECES = RBK * TERMS * 256, PIECES = A_PIECES + NCB * 256, PPT = PIECES / NT;
+  static_assert(PIECES % NT == 0, "16-byte pieces per thread");
+  constexpr int TILE = RBK * NCB * 16 * 64;  // floats of the workgroup's tile, C layout
+  static_assert(TILE * 4 <= 3 * PIECES * 16, "the epilogue reuses the stage buffers");
+  __shared__ u32x4_t stage[3][PIECES];
+  __shared__ float s_rstd[R];
+  __shared__ float s_part[rowrstd_lds<R, NT>()];
+  const int mtiles = (g.M + R - 1) / R, ntiles = g.npairs / NCB;
+  const int b = blockIdx.x, q = b >> 3, per = mtiles * G;
+  const int sub = q % per, nt = 8 * (q / per) + (b & 7);
+  if (nt >= ntiles) return;  // whole workgroup, before any barrier
+  const int mt = sub / G, grp = sub - mt * G;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int m0 = mt * R, nchunk = g.K >> 6;
+  const int lastblk = (g.M - 1) >> 5;
+  // this thread's pieces: global element offsets at chunk 0 (a chunk adds 4 KB)
+  const uint16_t* gp[PPT];
+#pragma unroll
+  for (int k = 0; k < PPT; ++k) {
+    const int pc = tid + NT * k;
+    if (pc < A_PIECES) {
+      const int rbk = pc / (TERMS * 256), rem = pc - rbk * TERMS * 256, term = rem >> 8, sl = rem & 255;
+      const int blk = mt * RBK + rbk < lastblk ? mt * RBK + rbk : lastblk;
+      gp[k] = (const uint16_t*)g.A + (term ? g.a_lo : 0) + ((int64_t)blk * nchunk * 256 + sl) * 8;
+    } else {
+      const int pw = pc - A_PIECES, cbk = pw >> 8, sl = pw & 255;
+      gp[k] = (const uint16_t*)g.Wp + ((int64_t)(nt * NCB + cbk) * nchunk * 256 + sl) * 8;
+    }
+  }
+  const bool norm_here = (Q == 8) && g.ssq_in != nullptr;
+  // the group's chunks [cb, ce)
+  const int cb = stream_begin(nchunk, grp * Q), ce = stream_begin(nchunk, grp * Q + Q), n = ce - cb;
+  const int clast = n > 0 ? ce - 1 : cb;
+  u32x4_t rg[2][PPT];  // staging: global -> registers -> LDS
+  u32x4_t fr[2][NF];   // one chunk's fragments of this wave, from LDS
+  auto load = [&](int set, int i) __attribute__((always_inline)) {  // chunk cb + i (clamped) into set `set`
+    const int c = cb + i < clast ? cb + i : clast;
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+      const u32x4_t* src = (const u32x4_t*)(gp[k] + (int64_t)c * 2048);
+      // weights are read once per call: streamed past the caches
+      rg[set][k] = k * NT >= A_PIECES ? __builtin_nontemporal_load(src) : *src;
+    }
+  };
+  auto put = [&](int set, int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) stage[buf][tid + NT * k] = rg[set][k];
+  };
+  const int rw = wave >> 1, cw = wave & 1;
+  auto frag = [&](int f, int buf) __attribute__((always_inline)) {
+    const u32x4_t* sa = &stage[buf][rw * TERMS * 256 + lane];
+    const u32x4_t* sw = &stage[buf][A_PIECES + cw * 256 + lane];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      fr[f][s * (TERMS + 1)] = sa[s * 64];
+      if (TWO) fr[f][s * (TERMS + 1) + 1] = sa[256 + s * 64];
+      fr[f][s * (TERMS + 1) + TERMS] = sw[s * 64];
+    }
+  };
+  f32x16_t r, st[fold_levels<Q>()];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) r[e] = 0.f;
+  auto mma = [&](int f) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const bf16x8_t w = __builtin_bit_cast(bf16x8_t, fr[f][s * (TERMS + 1) + TERMS]);
+      r = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fr[f][s * (TERMS + 1)]), w, r, 0, 0, 0);
+      if (TWO)
+        r = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fr[f][s * (TERMS + 1) + 1]), w, r, 0, 0,
+                                                    0);
+    }
+  };
+  // streams of the group that end at or before chunk c are folded
+  int j = 0, nb = stream_begin(nchunk, grp * Q + 1);
+  auto fold_until = [&](int c) __attribute__((always_inline)) {
+    while (j < Q && nb <= c) {
+      stream_fold<Q>(j, r, st);
+      ++j;
+      nb = stream_begin(nchunk, grp * Q + j + 1);
+    }
+  };
+  // Chunk i: LDS buffer i % 3, fragment set i % 2; register set i % 2 holds
+  // chunk i + 2 until it is written to LDS (then chunk i + 4). While chunk i
+  // is multiplied, the wave reads chunk i + 1's fragments and the workgroup
+  // writes chunk i + 2 into the third buffer.
+  load(0, 0);
+  load(1, 1);
+  put(0, 0);
+  put(1, 1);
+  load(0, 2);
+  load(1, 3);
+  __syncthreads();
+  frag(0, 0);
+  auto chunk = [&](int u, int i, bool refill) __attribute__((always_inline)) {  // chunk i, u = i % 6
+    fold_until(cb + i);
+    frag((u + 1) & 1, (u + 1) % 3);
+    mma(u & 1);
+    put(u & 1, (u + 2) % 3);
+    if (refill) load(u & 1, i + 4);
+    __syncthreads();
+  };
+  int i = 0;
+  for (; i + 10 <= n; i += 6) {  // every refill is a chunk still to come
+#pragma unroll
+    for (int u = 0; u < 6; ++u) chunk(u, i + u, true);
+  }
+  for (; i < n; i += 6) {
+#pragma unroll
+    for (int u = 0; u < 6; ++u)
+      if (i + u < n) chunk(u, i + u, i + u + 4 < n);
+  }
+  fold_until(ce + 1);  // the group's remaining streams (empty ones included)
+  if (Q < 8) {
+    // group sum of block (rw, cw), rows below M, to the partial buffer
+    int ba, bbk;
+    pair_blocks(g, nt * NCB + cw, ba, bbk);
+    const int col = (lane & 16) ? bbk * 16 + (lane & 15) : ba * 16 + (lane & 15);
+    float* P = g.partial + (int64_t)grp * g.M_pad * g.Nv + col;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int m = m0 + rw * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+      if (m < g.M) P[(int64_t)m * g.Nv] = r[e];
+    }
+    return;
+  }
+  // block sums to LDS in C layout (in the stage buffers: their last reads and
+  // writes were before the loop's final barrier)
+  float* red = (float*)&stage[0][0];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) red[((rw * NCB + cw) * 16 + e) * 64 + lane] = r[e];
+  if (norm_here) {  // uniform branch: contains a barrier (the row statistics are
+                    // loaded after the K loop, where their registers are free)
+    RowRstd<R, NT> rr(g, m0);
+    rr.finish(g, m0, s_part, s_rstd);
+  }
+  __syncthreads();
+  constexpr int NU = R * NCB, NG = NT / 16, NI = NU / NG;
+  const int c16 = tid & 15, grp16 = tid >> 4;
+  for (int jj = 0; jj < NI; ++jj) {
+    const int it = grp16 + NG * jj;
+    const int row = it / NCB, pc = it - row * NCB;
+    const int m = m0 + row, pair = nt * NCB + pc;
+    const int r32 = row & 31;
+    const int ia = (((row >> 5) * NCB + pc) * 16 + 4 * (r32 >> 3) + (r32 & 3)) * 64 + ((r32 >> 2) & 1) * 32 + c16;
+    int ba, bbk;
+    pair_blocks(g, pair, ba, bbk);
+    float sq = 0.f;
+    if (m < g.M) sq = epi(m, ba * 16 + c16, red[ia], bbk * 16 + c16, red[ia + 16], norm_here ? s_rstd[row] : 1.f);
+    if (g.ssq_out) {
+      sq = sum16(sq);
+      if (c16 == 0 && m < g.M) g.ssq_out[(int64_t)pair * g.M_pad + m] = sq;
+    }
+  }
+}
+
+// Combine the G group sums of k_gemm_bf16_lt by the stream tree's top levels
+// (neighbours, then pairs 2 apart, then 4 apart) and apply the epilogue.
+// grid: (pairs, 16-row tiles); block 256 (16 rows x 16 columns of a pair).
+template <int G>
+__global__ __launch_bounds__(256) void k_pk_combine(GemmArgs g, Epi<uint16_t> epi) {
+  __shared__ float lds[SPLITK_LDS_FLOATS];
+  float* s_rstd = lds;
+  float* s_part = lds + 16;
+  const int pair = blockIdx.x, mt = blockIdx.y;
+  int ba, bb;
+  pair_blocks(g, pair, ba, bb);
+  const int m = mt * 16 + (threadIdx.x >> 4), r = threadIdx.x & 15;
+  if (g.ssq_in) {
+    RowRstd<16> rr(g, mt * 16);
+    rr.finish(g, mt * 16, s_part, s_rstd);
+  }
+  __syncthreads();
+  float sq = 0.f;
+  if (m < g.M) {
+    float va[G], vb[G];
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      const float* P = g.partial + ((int64_t)k * g.M_pad + m) * g.Nv;
+      va[k] = P[ba * 16 + r];
+      vb[k] = P[bb * 16 + r];
+    }
+#pragma unroll
+    for (int h = 1; h < G; h <<= 1)
+#pragma unroll
+      for (int k = 0; k < G; k += 2 * h) {
+        va[k] += va[k + h];
+        vb[k] += vb[k + h];
+      }
+    sq = epi(m, ba * 16 + r, va[0], bb * 16 + r, vb[0], g.ssq_in ? s_rstd[threadIdx.x >> 4] : 1.f);
+  }
+  if (g.ssq_out) {
+    sq = sum16(sq);
+    if (r == 0 && m < g.M) g.ssq_out[(int64_t)pair * g.M_pad + m] = sq;
   }
 }
 
@@ -555,27 +786,54 @@ void launch_gemm(int dtype, const GemmArgs& g0, const EpiArgs& e, hipStream_t s)
     if (record_phase(bad)) return;
     Epi<uint16_t> epi{e};
     const bool two = g.a_lo != 0;
+    if (g.lt_groups > 0) {
+      // staged tile: 128 rows x 2 column pairs per workgroup, G workgroups
+      // per tile over the stream groups
+      const int G = g.lt_groups, mtiles = (g.M + 127) / 128, ntiles = g.npairs / 2;
+      dim3 grid(8 * mtiles * G * ((ntiles + 7) / 8));
+#define RLT_LT(Q_)                                                                              \
+  do {                                                                                          \
+    if (two) hipLaunchKernelGGL((k_gemm_bf16_lt<Q_, true>), grid, dim3(512), 0, s, g, epi);   \
+    else hipLaunchKernelGGL((k_gemm_bf16_lt<Q_, false>), grid, dim3(512), 0, s, g, epi);      \
+  } while (0)
+      switch (G) {
+        case 1: RLT_LT(8); break;
+        case 2: RLT_LT(4); break;
+        case 4: RLT_LT(2); break;
+        default: RLT_LT(1); break;
+      }
+#undef RLT_LT
+      if (G > 1) {
+        dim3 g2(g.npairs, (g.M + 15) / 16);
+        switch (G) {
+          case 2: hipLaunchKernelGGL(k_pk_combine<2>, g2, dim3(256), 0, s, g, epi); break;
+          case 4: hipLaunchKernelGGL(k_pk_combine<4>, g2, dim3(256), 0, s, g, epi); break;
+          default: hipLaunchKernelGGL(k_pk_combine<8>, g2, dim3(256), 0, s, g, epi); break;
+        }
+      }
+      return;
+    }
     const int mtiles = (g.M + 32 * g.rb - 1) / (32 * g.rb), ntiles = g.npairs / g.cb;
     dim3 grid(8 * mtiles * ((ntiles + 7) / 8));
     // the Q/K/V product's epilogue computes its rotary angles (prefetching a
     // table lookup measured slower)
     const bool pre = g.pre >= 0 ? g.pre != 0 : (e.kind == EPI_RESID || e.kind == EPI_QROT);
-#define RLT_PK2(RB_, CB_, NW_, PF_, PRE_)                                                                     \
-  do {                                                                                                     \
-    if (two) hipLaunchKernelGGL((k_gemm_bf16_pk<RB_, CB_, NW_, PF_, PRE_, true>), grid, dim3(64 * NW_), 0, s, g, epi); \
-    else hipLaunchKernelGGL((k_gemm_bf16_pk<RB_, CB_, NW_, PF_, PRE_, false>), grid, dim3(64 * NW_), 0, s, g, epi);    \
+#define RLT_PK2(RB_, CB_, PF_, PRE_)                                                                   \
+  do {                                                                                                 \
+    if (two) hipLaunchKernelGGL((k_gemm_bf16_pk<RB_, CB_, PF_, PRE_, true>), grid, dim3(512), 0, s, g, epi); \
+    else hipLaunchKernelGGL((k_gemm_bf16_pk<RB_, CB_, PF_, PRE_, false>), grid, dim3(512), 0, s, g, epi);    \
   } while (0)
-#define RLT_PK(RB_, CB_, NW_, PF_)              \
-  do {                                          \
-    if (pre) RLT_PK2(RB_, CB_, NW_, PF_, true); \
-    else RLT_PK2(RB_, CB_, NW_, PF_, false);    \
+#define RLT_PK(RB_, CB_, PF_)              \
+  do {                                     \
+    if (pre) RLT_PK2(RB_, CB_, PF_, true); \
+    else RLT_PK2(RB_, CB_, PF_, false);    \
   } while (0)
-#define RLT_SHAPE(RB_, NW_, PF_) if (g.rb == RB_ && g.nw == NW_ && g.pf == PF_) RLT_PK(RB_, 1, NW_, PF_); else
+#define RLT_SHAPE(RB_, CB_, PF_) \
+  if (g.rb == RB_ && g.cb == CB_ && g.pf == PF_) RLT_PK(RB_, CB_, PF_); else
     // shapes the host may pick (none changes the arithmetic, see the kernel)
-    RLT_SHAPE(1, 8, 2) RLT_SHAPE(1, 8, 3) RLT_SHAPE(1, 8, 4) RLT_SHAPE(1, 4, 4) RLT_SHAPE(1, 4, 8)
-    RLT_SHAPE(2, 8, 1) RLT_SHAPE(2, 8, 2) RLT_SHAPE(2, 4, 2) RLT_SHAPE(2, 4, 4) {
-      if (g.rb == 2) RLT_PK(2, 1, 8, 2);
-      else RLT_PK(1, 1, 8, 4);
+    RLT_SHAPE(1, 1, 2) RLT_SHAPE(1, 1, 3) RLT_SHAPE(1, 1, 4) RLT_SHAPE(2, 1, 1) RLT_SHAPE(2, 1, 2)
+    RLT_SHAPE(1, 2, 1) RLT_SHAPE(1, 2, 2) {
+      RLT_PK(1, 1, 2);
     }
 #undef RLT_SHAPE
 #undef RLT_PK

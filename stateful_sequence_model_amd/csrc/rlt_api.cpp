@@ -107,7 +107,7 @@ struct rlt_ctx {
   int64_t lo_X, lo_o, lo_h, lo_act;
   // forced operand-order product shape (tuning sweeps): rows 32 * rb, waves,
   // chunks in flight, epilogue prefetch (-1: the library's choice); 0 = none
-  int shape_rb, shape_nw, shape_pf, shape_pre;
+  int shape_rb, shape_cb, shape_lt, shape_pf, shape_pre;
   // duplicate-row detection of rlt_decoder_step: per state row, the number
   // of slots of the current call naming it (zero between calls)
   int* claim;
@@ -664,30 +664,34 @@ struct Gemm {
     g.eps = c->cfg.rms_eps;
     if (Wp) {
       // tile shape (none of these choices changes the arithmetic: fixed
-      // stream order, see the kernel), measured per product at 1 and 128
-      // rows, reference depth, over 4/8 waves, 1-8 chunks in flight and
-      // 32/64-row tiles: products of 128 or more column pairs (Q/K/V,
-      // gate/up, vocabulary) take four waves with four chunks in flight
-      // each and the epilogue's reads after the K loop (register budget);
-      // the 2048-wide ones eight waves, two chunks in flight (three past 32
-      // rows). 64-row tiles were slower at every size measured.
+      // stream order, see the kernels), measured per product at 1 and 128
+      // rows, reference depth: calls of more than 64 rows whose products
+      // have at least 64 staged tiles of 128 rows x 64 columns (Q/K/V,
+      // gate/up, vocabulary) take the staged tile, in one workgroup per tile
+      // from 150 tiles, else split over two stream groups; the others the
+      // register tile of 32 rows, two chunks in flight per wave (three past
+      // 32 rows)
       g.Wp = Wp;
-      g.cb = 1;
       g.rb = 1;
-      if (g.npairs >= 128) {
-        g.nw = 4;
-        g.pf = 4;
-        g.pre = 0;
-      } else {
-        g.nw = 8;
-        g.pf = n > 32 ? 3 : 2;
-        g.pre = -1;
+      g.cb = 1;
+      g.pre = -1;
+      g.pf = n > 32 ? 3 : 2;
+      g.lt_groups = 0;
+      if (n > 64 && g.npairs % 2 == 0) {
+        const int tiles = g.npairs / 2 * ((n + 127) / 128);
+        if (tiles >= 64) g.lt_groups = tiles >= 150 ? 1 : 2;
+        while (g.lt_groups > 1 && (size_t)g.lt_groups * g.M_pad * g.Nv > c->partial_cap) g.lt_groups /= 2;
       }
       if (c->shape_rb > 0) {
-        g.rb = c->shape_rb;
-        g.nw = c->shape_nw;
-        g.pf = c->shape_pf;
-        g.pre = c->shape_pre;
+        if (c->shape_lt > 0) {
+          if (g.npairs % 2 == 0 && (size_t)c->shape_lt * g.M_pad * g.Nv <= c->partial_cap) g.lt_groups = c->shape_lt;
+        } else if (g.npairs % c->shape_cb == 0) {
+          g.lt_groups = 0;
+          g.rb = c->shape_rb;
+          g.cb = c->shape_cb;
+          g.pf = c->shape_pf;
+          g.pre = c->shape_pre;
+        }
       }
     } else if (c->dt == 1 && n > 32 && g.npairs % 2 == 0 && K % 64 == 0) {
       // LDS tile of 128 rows x 64 columns (128 when that still leaves two
@@ -1800,12 +1804,14 @@ extern "C" int rlt_dbg_gemm_packed(rlt_ctx* c, const void* A, const void* W, int
   return rc;
 }
 
-extern "C" int rlt_dbg_product_shape(rlt_ctx* c, int32_t rb, int32_t nw, int32_t pf, int32_t pre) {
+extern "C" int rlt_dbg_product_shape(rlt_ctx* c, int32_t rb, int32_t cb, int32_t lt, int32_t pf, int32_t pre) {
   if (!c) return fail(RLT_EINVAL, "null context");
-  if (rb != 0 && (rb < 1 || rb > 2 || (nw != 4 && nw != 8) || pf < 1 || pf > 8 || pre < -1 || pre > 1))
+  if (rb != 0 && (rb < 1 || rb > 2 || (cb != 1 && cb != 2) || (lt != 0 && lt != 1 && lt != 2 && lt != 4 && lt != 8) ||
+                  pf < 1 || pf > 4 || pre < -1 || pre > 1))
     return fail(RLT_EINVAL, "product shape");
   c->shape_rb = rb;
-  c->shape_nw = nw;
+  c->shape_cb = cb;
+  c->shape_lt = lt;
   c->shape_pf = pf;
   c->shape_pre = pre;
   return RLT_OK;

@@ -104,7 +104,9 @@ struct GemmArgs {
   const void* Wp;         // bf16: the same weights in fragment order, virtual column
                           // pairs as 32-row blocks (pair p = block p), or null
   int rb, cb;             // fragment-order tile: 32 rb rows x cb column pairs
-  int nw, pf;             // fragment-order tile: waves per workgroup, chunks in flight per wave
+  int pf;                 // fragment-order tile: chunks in flight per wave
+  int lt_groups;          // fragment order, > 0: staged 128-row tile, this many workgroups
+                          // per tile over the stream groups (1, 2, 4 or 8); 0: register tile
   int pre;                // fragment-order tile: -1 = by epilogue kind, 0/1 = epilogue values after / before the K loop
   int nseg, seg_rows;
   int K;
