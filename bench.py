@@ -164,10 +164,14 @@ def main():
                     help="also time a plain 4 GiB device copy and read-only sum (achievable HBM rates)")
     ap.add_argument("--launch", action="append", default=[], metavar="FIELD=VALUE",
                     help="launch option of the context (rlt_dbg_launch field, for tuning sweeps)")
-    ap.add_argument("--mode", choices=("step", "memory_prefill", "backward"), default="step",
+    ap.add_argument("--mode", choices=("step", "memory_prefill", "backward", "replay"), default="step",
                     help="step: the decoder transition (default); memory_prefill: token-parallel "
                          "construction of the encoder memory of the whole batch; backward: full-BPTT "
-                         "replay backward of the whole batch")
+                         "replay backward of the whole batch; replay: current-policy replay from H_0 of "
+                         "ragged sequences (default preset ragged_rl_replay, lengths capped by "
+                         "--replay-max-len)")
+    ap.add_argument("--replay-max-len", type=int, default=1024,
+                    help="replay mode: upper end of the uniform length draw (the preset's lower end kept)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -180,13 +184,16 @@ def main():
     import synth
     from stateful_sequence_model_amd import Decoder, DecoderState, ModelConfig, _abi, to_device
 
-    wl = synth.PRESETS[args.workload or ("small_batched" if args.mode == "backward" else "reference_depth")]
+    default = {"backward": "small_batched", "replay": "ragged_rl_replay"}.get(args.mode, "reference_depth")
+    wl = synth.PRESETS[args.workload or default]
     if args.batch:
         wl = wl.with_(B=args.batch)
     if args.mode == "memory_prefill":
         return bench_memory_prefill(args, wl)
     if args.mode == "backward":
         return bench_backward(args, wl)
+    if args.mode == "replay":
+        return bench_replay(args, wl)
     B, T = wl.B, wl.T
     es = 2 if wl.dtype == "bf16" else 4
     K, Wu = args.steps, args.warmup
@@ -387,6 +394,74 @@ def bench_memory_prefill(args, wl):
                      "frac": round(tflops / peak, 4), "traffic": None,
                      "algorithmic_flops_per_call": flops, "hbm_bytes_min_per_call": int(moved)},
     }), flush=True)
+
+
+def bench_replay(args, wl):
+    """Current-policy replay from H_0 ("Recurrent Looped Transformer" App. A.4,
+    §4.1: ready transitions of uneven length batched tick by tick) of B ragged
+    sequences: one rlt_replay_sequence call per timed step, every position from
+    the split scored. The preset's length draw U[len_lo, len_hi] is capped at
+    --replay-max-len (the prefix cross-attention makes a sequence's cost grow
+    with the square of its length: the uncapped draw is hours of GPU time per
+    call); value = transitions (sum of len - 1) per second. Timed twice: with
+    the runs of ticks of one active set captured as graphs (the default on a
+    stream) and with every tick launched directly."""
+    import numpy as np
+    import torch
+    import synth
+    from stateful_sequence_model_amd import Decoder, DecoderState, ModelConfig, _abi
+
+    wl = wl.with_(len_hi=min(wl.len_hi, args.replay_max_len)) if wl.ragged else wl
+    lens, splits = synth.make_lengths(wl)
+    B, T, d, G = wl.B, int(lens.max()), wl.d, wl.G
+    steps = max(1, min(args.steps, 3))
+    torch.cuda.set_device(0)
+    raw = synth.make_weights(wl)
+    cfg = ModelConfig(L=wl.L, d=d, H=wl.H, dh=wl.dh, W=wl.W, G=G, F=wl.F, V=wl.V, dtype=wl.dtype,
+                      merge=wl.merge, alpha=wl.alpha, eps=wl.eps, rope_theta=wl.rope_theta, pos=wl.pos)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(wl.seed)
+    tdt = cfg.torch_dtype
+    e = torch.empty((B, T, d), device="cuda", dtype=tdt).normal_(generator=gen)
+    mk = torch.empty((G, B, T, d), device="cuda", dtype=tdt).normal_(generator=gen)
+    mv = torch.empty((G, B, T, d), device="cuda", dtype=tdt).normal_(generator=gen)
+    mem_len = torch.from_numpy(lens).cuda()  # kept alive: the memory struct holds its pointer
+    mem = Decoder.memory(mk, mv, mem_len)
+    tokens = torch.randint(0, wl.V, (B, T), generator=gen, device="cuda", dtype=torch.int32)
+    logp = torch.empty((B, T), device="cuda")
+    trans = int((lens - 1).sum())
+    stream = torch.cuda.Stream()
+    res = {}
+    for label, gmin in (("graphs", 0), ("direct", -1)):
+        dec = Decoder(cfg, raw, max_rows=B, max_ctx=T, launch={"replay_graph_min": gmin})
+        st = DecoderState(cfg, B)
+        with torch.cuda.stream(stream):
+            for _ in range(max(1, args.warmup if args.warmup < 2 else 1)):
+                _abi.check(dec.replay(st, lens, splits, e, mem, tokens, logp, stream=stream.cuda_stream), "replay")
+            stream.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                _abi.check(dec.replay(st, lens, splits, e, mem, tokens, logp, stream=stream.cuda_stream), "replay")
+            stream.synchronize()
+            ms = (time.perf_counter() - t0) * 1e3 / steps
+        _abi.check(dec.sync_error(), "device error")
+        res[label] = ms
+        log("replay (%s): %.1f ms per call, %d transitions, %.1f transitions/s" % (label, ms, trans, trans / (ms / 1e3)))
+        dec.close()
+        del st
+    ms = res["graphs"]
+    out = {
+        "metric": "replay transitions/sec (ragged, from H_0, seq*token)",
+        "value": round(trans / (ms / 1e3), 1), "unit": "transitions/s", "n_gpus": 1, "steps": steps,
+        "warmup": 1, "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name + " replay", "L_D": wl.L, "d": d, "heads": "%dx%d" % (wl.H, wl.dh),
+                   "W": wl.W, "G": G, "batch": B, "lengths": "U[%d, %d]" % (wl.len_lo, wl.len_hi),
+                   "max_len": T, "transitions": trans},
+        "direct_launch_ms_per_call": round(res["direct"], 3),
+        "graph_speedup": round(res["direct"] / ms, 3),
+    }
+    print(json.dumps(out), flush=True)
 
 
 def bench_backward(args, wl):

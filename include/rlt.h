@@ -293,7 +293,12 @@ int rlt_decoder_step(rlt_ctx* ctx, rlt_state* st, const rlt_step_io* io, void* s
 int rlt_decoder_step_noalloc(rlt_ctx* ctx, rlt_state* st, const rlt_step_io* io, void* stream);
 
 /* See rlt_replay_io. Synchronises the stream once at the start (upload of
- * the schedule). */
+ * the schedule). On a non-default stream that is not being captured, each
+ * run of ticks with the same active set (the sequences still running) is
+ * captured once as a graph and replayed for the run's ticks (the launches
+ * of a tick depend on the set's size only; the position is kept on the
+ * device); the call then also waits for the stream at its end, when it
+ * releases those graphs. Results are the same either way. */
 int rlt_replay_sequence(rlt_ctx* ctx, rlt_state* st, const rlt_replay_io* io, void* stream);
 
 int rlt_score_logprobs(rlt_ctx* ctx, const rlt_score_io* io, void* stream);

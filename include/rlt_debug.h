@@ -49,6 +49,8 @@ typedef struct rlt_dbg_launch {
   int32_t one_term;     /* 1: the operand-order products take their activations as one bf16
                            term (the other tiles always do) instead of two (value rounded,
                            then its rounding remainder): lower precision, for comparisons */
+  int32_t replay_graph_min; /* rlt_replay_sequence: runs of at least this many ticks with one
+                           active set are captured as a graph and replayed (0: 4; -1: never) */
 } rlt_dbg_launch;
 
 /* rlt_create with launch options (opt must not be NULL). */

@@ -36,10 +36,13 @@ __global__ void k_prestep(MiscArgs a) {
 }
 
 // replay tick: every active slot is at position `tick`
-__global__ void k_replay_rows(const int* rows, int n, int tick, int* t_row, const int* pos,
+// tick: the replay's current position, on the device (advanced by the
+// post-step of each tick), so that the launches of a tick do not depend on it
+__global__ void k_replay_rows(const int* rows, int n, const int* tick_dev, int* t_row, const int* pos,
                               const int* mem_len, int* err) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
+  const int tick = *tick_dev;
   const int row = rows[i];
   int code = 0;
   if (pos[row] + 1 != tick) code = ERR_PENDING;
@@ -50,6 +53,7 @@ __global__ void k_replay_rows(const int* rows, int n, int tick, int* t_row, cons
 
 __global__ void k_poststep(PostArgs a) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (a.tick && i == 0) *a.tick += 1;  // replay: the next tick (read by the next tick's kernels only)
   if (i >= a.n) return;
   const int row = a.rows.rows[i];
   if (a.claim && row >= 0 && row < a.B_cap) a.claim[row] = 0;  // ready for the next call
@@ -497,10 +501,9 @@ __global__ __launch_bounds__(RB) void k_readout(ReadoutArgs a) {
 void launch_prestep(const MiscArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_prestep, dim3((a.n + 255) / 256), dim3(256), 0, s, a);
 }
-void launch_replay_rows(const int* rows, const int* src, int n, int tick, int* t_row, int* pos,
-                        const int* mem_len, int* err, hipStream_t s) {
-  (void)src;
-  hipLaunchKernelGGL(k_replay_rows, dim3((n + 255) / 256), dim3(256), 0, s, rows, n, tick, t_row,
+void launch_replay_rows(const int* rows, int n, const int* tick_dev, int* t_row, int* pos, const int* mem_len,
+                        int* err, hipStream_t s) {
+  hipLaunchKernelGGL(k_replay_rows, dim3((n + 255) / 256), dim3(256), 0, s, rows, n, tick_dev, t_row,
                      (const int*)pos, mem_len, err);
 }
 void launch_poststep(const PostArgs& a, hipStream_t s) {

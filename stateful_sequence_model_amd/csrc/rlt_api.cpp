@@ -134,6 +134,8 @@ struct rlt_ctx {
   int mem_B;
   // shared device buffers
   int *t_row, *ident, *ones, *rows_buf, *src_buf, *split_buf, *last_buf;
+  int* tick_dev;        // replay: the current tick, advanced on the device
+  int replay_graph_min;  // replay: runs of at least this many ticks of one active set are captured (0: never)
   double* inv_freq;
   float2* rope_tab;  // [rope_tmax + 1][d_head / 2] rotary (cos, sin)
   int rope_tmax;
@@ -279,7 +281,7 @@ extern "C" int rlt_state_layout(const rlt_config* cfg, int32_t B_cap, size_t byt
 extern "C" void rlt_destroy(rlt_ctx* c) {
   if (!c) return;
   std::vector<void*> ptrs = {c->t_row, c->ident, c->ones, c->rows_buf, c->src_buf, c->split_buf, c->last_buf,
-                             c->inv_freq, c->rope_tab};
+                             c->tick_dev, c->inv_freq, c->rope_tab};
   for (Workspace& w : c->ws) {
     void* p[] = {w.X, w.kc, w.vc, w.o, w.h, w.act, w.gbuf, w.z, w.q, w.qm, w.part, w.partial, w.logits, w.ssq};
     ptrs.insert(ptrs.end(), std::begin(p), std::end(p));
@@ -524,6 +526,7 @@ static int create_ctx(const rlt_config* cfg, const rlt_weights* w, int32_t max_r
   ALLOC(c->src_buf, M * 4);
   ALLOC(c->split_buf, M * 4);
   ALLOC(c->last_buf, M * 4);
+  ALLOC(c->tick_dev, 4);
   ALLOC(c->inv_freq, (size_t)(dh / 2) * sizeof(double));
   c->rope_tmax = std::min(max_ctx, 65536);  // positions past it compute their angles
   ALLOC(c->rope_tab, (size_t)(c->rope_tmax + 1) * (dh / 2) * sizeof(float2));
@@ -567,7 +570,7 @@ static int create_ctx(const rlt_config* cfg, const rlt_weights* w, int32_t max_r
     rlt_destroy(c);
     return fail(RLT_EHIP, "barrier word allocation failed");
   }
-  if (hipHostMalloc((void**)&c->host_stage, M * 4 * 4, hipHostMallocDefault) != hipSuccess) {
+  if (hipHostMalloc((void**)&c->host_stage, (M * 4 + 16) * 4, hipHostMallocDefault) != hipSuccess) {
     rlt_destroy(c);
     return fail(RLT_EHIP, "pinned staging allocation failed");
   }
@@ -578,6 +581,7 @@ static int create_ctx(const rlt_config* cfg, const rlt_weights* w, int32_t max_r
     }
   }
   c->one_term = o.one_term != 0;
+  c->replay_graph_min = o.replay_graph_min < 0 ? 0 : (o.replay_graph_min > 0 ? o.replay_graph_min : 4);
   if (c->pk_ready && !c->one_term) {
     c->lo_X = (int64_t)M * 2 * d;
     c->lo_o = c->lo_h = (int64_t)M * d;
@@ -1325,9 +1329,32 @@ extern "C" int rlt_replay_sequence(rlt_ctx* c, rlt_state* st, const rlt_replay_i
               c->cfg.n_layers, st->B_cap, c->cfg.window, c->cfg.d_model, 0, s);
   std::vector<int> lens_sorted(B);
   for (int i = 0; i < B; ++i) lens_sorted[i] = io->len_host[order[i]];
-  for (int t = 1; t <= maxlen - 1; ++t) {
+  auto active = [&](int t) {
     int nt = 0;
     while (nt < B && lens_sorted[nt] - 1 >= t) ++nt;
+    return nt;
+  };
+  // The launches of a tick depend on the size of the active set only (the
+  // tick itself lives on the device): a run of ticks with one active set
+  // is captured once and replayed, on a caller's stream that is not itself
+  // capturing and with the timing hook off.
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (stream) HIP_TRY(hipStreamIsCapturing(s, &cap));
+  const bool graphs = stream && cap == hipStreamCaptureStatusNone && !c->prof_on && c->replay_graph_min > 0 &&
+                      c->fused_rows == 0;  // (the persistent path builds its phase tables on first use)
+  stg[4 * M] = 1;
+  HIP_TRY(hipMemcpyAsync(c->tick_dev, stg + 4 * M, 4, hipMemcpyHostToDevice, s));
+  std::vector<hipGraphExec_t> execs;
+  std::vector<hipGraph_t> graphs_made;
+  auto release = [&]() {
+    for (hipGraphExec_t e : execs) (void)hipGraphExecDestroy(e);
+    for (hipGraph_t g : graphs_made) (void)hipGraphDestroy(g);
+  };
+  int t = 1;
+  while (t <= maxlen - 1) {
+    const int nt = active(t);
+    int run = 1;
+    while (t + run <= maxlen - 1 && active(t + run) == nt) ++run;
     StepPlan P{};
     P.R = Rows{c->rows_buf, c->src_buf, c->t_row, nt};
     P.n = nt;
@@ -1348,10 +1375,44 @@ extern "C" int rlt_replay_sequence(rlt_ctx* c, rlt_state* st, const rlt_replay_i
     ro.logp = io->logp;
     ro.logp_sb = io->logp_stride_b;
     ro.split = c->split_buf;
-    launch_replay_rows(c->rows_buf, c->src_buf, nt, t, c->t_row, st->pos, io->mem.mem_len, c->err_dev, s);
-    enqueue_rows(c, P, s);
-    PostArgs pa{P.R, nt, st->pos, st->pending, nullptr, nullptr, st->B_cap};
-    launch_poststep(pa, s);
+    PostArgs pa{P.R, nt, st->pos, st->pending, nullptr, nullptr, st->B_cap, c->tick_dev};
+    auto tick = [&]() {
+      launch_replay_rows(c->rows_buf, nt, c->tick_dev, c->t_row, st->pos, io->mem.mem_len, c->err_dev, s);
+      enqueue_rows(c, P, s);
+      launch_poststep(pa, s);
+    };
+    if (graphs && run >= c->replay_graph_min) {
+      hipGraph_t g = nullptr;
+      hipGraphExec_t ge = nullptr;
+      if (hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+        release();
+        return fail(RLT_EHIP, "replay capture failed to start");
+      }
+      tick();
+      const hipError_t ec = hipStreamEndCapture(s, &g);
+      if (g) graphs_made.push_back(g);
+      if (ec != hipSuccess || hipGraphInstantiate(&ge, g, nullptr, nullptr, 0) != hipSuccess) {
+        (void)hipStreamSynchronize(s);
+        release();
+        return fail(RLT_EHIP, "replay capture failed");
+      }
+      execs.push_back(ge);
+      for (int r = 0; r < run; ++r)
+        if (hipGraphLaunch(ge, s) != hipSuccess) {
+          (void)hipStreamSynchronize(s);
+          release();
+          return fail(RLT_EHIP, "replay graph launch failed");
+        }
+    } else {
+      for (int r = 0; r < run; ++r) tick();
+    }
+    t += run;
+  }
+  if (!execs.empty()) {
+    // the graphs are released once their launches have run
+    const hipError_t es = hipStreamSynchronize(s);
+    release();
+    if (es != hipSuccess) return fail(RLT_EHIP, "replay: %s", hipGetErrorString(es));
   }
   launch_set_pending(c->rows_buf, c->src_buf, B, io->tokens, io->tok_stride_b, c->last_buf, st->pending, s);
   HIP_TRY(hipGetLastError());

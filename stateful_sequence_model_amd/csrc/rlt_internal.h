@@ -410,6 +410,7 @@ struct PostArgs {
   const int32_t* next_tok;   // token to record as pending (DEFER) or null
   int* claim;                // [B_cap] slot counts to clear (decoder step), or null
   int B_cap;
+  int* tick;                 // replay: position counter to advance by one, or null
 };
 void launch_poststep(const PostArgs& a, hipStream_t s);
 // counts[rows[i]] = 0 for i < n (a fill kernel: capturable)
@@ -473,7 +474,7 @@ void launch_init(int dtype, const int* rows, int n, const float* s_star, float* 
                  int poison, hipStream_t s);
 void launch_set_pending(const int* rows, const int* src, int n, const int* tokens, int64_t tok_sb,
                         const int* last_index, int* pending, hipStream_t s);
-void launch_replay_rows(const int* rows, const int* src, int n, int tick, int* t_row, int* pos,
-                        const int* mem_len, int* err, hipStream_t s);
+void launch_replay_rows(const int* rows, int n, const int* tick_dev, int* t_row, int* pos, const int* mem_len,
+                        int* err, hipStream_t s);
 
 }  // namespace rlt

@@ -57,6 +57,46 @@ def test_replay_equals_incremental_steps_bitexact():
     assert torch.isnan(logp[:, 0]).all()                            # t = 0 never scored
 
 
+def test_replay_graph_runs_equal_direct_launches():
+    """Replay on a side stream captures each run of ticks with one active set
+    as a graph (the position advances on the device) and replays it; with
+    capture off (every tick launched directly) or on for every run, the
+    log-probs, the state trace and the final state are bit-identical. Ragged
+    lengths give runs shorter and longer than the capture threshold."""
+    require_gpu()
+    wl = SMALL.with_(B=6, T=40)
+    lens = np.array([40, 33, 33, 20, 9, 3], dtype=np.int32)
+    splits = np.array([1, 5, 2, 1, 3, 1], dtype=np.int32)
+    out = {}
+    raw = None
+    for name, gmin in (("direct", -1), ("default", 0), ("every", 1)):
+        run = GpuRun(wl, raw=raw, launch={"replay_graph_min": gmin})
+        raw = run.raw
+        B, T = run.B, run.T
+        tokens = torch.from_numpy(synth.make_tokens(wl, 0, B, T)).cuda()
+        logp = torch.full((B, T), float("nan"), device="cuda")
+        s_trace = torch.zeros((B, T, wl.d), device="cuda")
+        run.st.ring_k.zero_()  # slots the short sequences never write: equal in every run
+        run.st.ring_v.zero_()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            assert run.dec.replay(run.st, lens, splits, run.Ed, run.mem, tokens, logp, s_trace=s_trace,
+                                  stream=side.cuda_stream) == 0
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        assert run.dec.sync_error() == 0
+        out[name] = (logp.cpu(), s_trace.cpu(), run.st.pos.cpu(), run.st.pending.cpu(), run.st.ring("k").cpu(),
+                     run.st.s.cpu())
+        run.dec.close()
+    ref = out["direct"]
+    for name in ("default", "every"):
+        for a, b in zip(out[name], ref):
+            assert torch.equal(a.view(torch.int32) if a.is_floating_point() else a,
+                               b.view(torch.int32) if b.is_floating_point() else b), name
+    assert torch.equal(ref[2], torch.from_numpy(lens - 1))
+
+
 def test_split_invariance_prop_3_1_bitexact():
     """Prop. 3.1: replaying a prefix then stepping equals replaying the
     whole history, for several split points."""
