@@ -126,13 +126,25 @@ def measured_traffic(x_bytes: float):
 
 
 def calibrate(torch, nbytes: int = 4 << 30, reps: int = 10) -> dict:
-    """Achievable HBM rates on this device: a plain copy (read + write) and
-    a read-only reduction over nbytes of bf16."""
+    """Achievable HBM rates on this device, and known-size launches for the
+    counter calibration: a plain copy (read + write), a read-only reduction
+    over nbytes of bf16, and the library's streaming read of the same nbytes
+    with non-temporal 16-byte loads (the load of the attention kernels) and
+    with plain ones."""
+    from stateful_sequence_model_amd import _abi
     src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").normal_()
     dst = torch.empty_like(src)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def stream_read(nt):
+        _abi.check(_abi.lib().rlt_dbg_stream_read(src.data_ptr(), nbytes, nt, sink.data_ptr(), stream),
+                   "rlt_dbg_stream_read")
     res = {}
     for name, fn, moved in (("copy", lambda: dst.copy_(src), 2 * nbytes),
-                            ("read_sum", lambda: src.sum(dtype=torch.float32), nbytes)):
+                            ("read_sum", lambda: src.sum(dtype=torch.float32), nbytes),
+                            ("stream_read_nt", lambda: stream_read(1), nbytes),
+                            ("stream_read", lambda: stream_read(0), nbytes)):
         fn()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

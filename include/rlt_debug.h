@@ -67,6 +67,38 @@ int rlt_dbg_create(const rlt_config* cfg, const rlt_weights* w, int32_t max_rows
  * the default register tile. */
 int rlt_dbg_product_shape(rlt_ctx* ctx, int32_t rb, int32_t cb, int32_t lt, int32_t pf, int32_t pre);
 
+/* Host-side walk of the narrow product tile's index math (the functions the
+ * kernel itself uses) over every workgroup and lane of an n-row product with
+ * npairs column pairs, K inputs, a weight of nseg segments of seg_rows rows
+ * (pairing: 0 plain, 1 rotary halves of dh-wide heads, 2 two segments side
+ * by side), activations of M_pad rows, and the launcher's own choice of K
+ * split, row blocks and K slice (narrow_rows = min(max_rows, 32), target: 0
+ * for a stand-alone launch, else the persistent step's workgroup count,
+ * partial_cap: partial-buffer floats). Runs on the CPU: no device needed.
+ * Fills *out with the plan and the largest index of each access. */
+typedef struct rlt_narrow_report {
+  int32_t S, mb, kslice;      /* the plan: K splits, 16-row blocks per tile, K per (split, wave) */
+  int32_t w_seg_max, w_row_max; /* largest weight segment and row read */
+  int32_t pad_;
+  int64_t a_row_max;          /* largest activation row read (must be < M_pad) */
+  int64_t a_col_end;          /* largest activation / weight column read + 8 (must be <= K) */
+  int64_t partial_end;        /* largest partial index written + 1 (0: no split) */
+  int64_t ssq_end;            /* largest row-statistics index written + 1 */
+  int64_t steps_missing;      /* 32-wide K steps of a tile no wave multiplies */
+  int64_t steps_repeated;     /* 32-wide K steps multiplied more than once */
+} rlt_narrow_report;
+int rlt_dbg_narrow_bounds(int32_t n, int32_t npairs, int32_t K, int32_t pairing, int32_t dh, int32_t nseg,
+                          int32_t seg_rows, int32_t M_pad, int32_t narrow_rows, int32_t target, int64_t partial_cap,
+                          rlt_narrow_report* out);
+
+/* Counter calibration: read `bytes` (a multiple of 16) at device pointer
+ * src once, in 16-byte pieces, with non-temporal loads (the load instruction
+ * of the attention kernels' key and value streams; nontemporal = 1) or plain
+ * ones, on `stream`; sink is a device word written only if the xor of all
+ * data equals a fixed value (it keeps the loads). A rocprofv3 counter of
+ * this launch against `bytes` gives the counter's bytes-per-unit factor. */
+int rlt_dbg_stream_read(const void* src, int64_t bytes, int32_t nontemporal, uint32_t* sink, void* stream);
+
 /* Kernel classes for the timing hook below. */
 enum {
   RLT_PROF_XATTN = 0,     /* prefix cross-attention partials (eq. 2.15) */

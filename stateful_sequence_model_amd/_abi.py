@@ -102,6 +102,12 @@ class rlt_backward_io(C.Structure):
                 ("dmem_stride_b", i64), ("dmem_stride_t", i64)]
 
 
+class rlt_narrow_report(C.Structure):
+    _fields_ = [("S", i32), ("mb", i32), ("kslice", i32), ("w_seg_max", i32), ("w_row_max", i32), ("pad_", i32),
+                ("a_row_max", i64), ("a_col_end", i64), ("partial_end", i64), ("ssq_end", i64),
+                ("steps_missing", i64), ("steps_repeated", i64)]
+
+
 class rlt_dbg_launch(C.Structure):
     _fields_ = [("xattn_chunk", i32), ("swa_hpw", i32), ("xattn_hpw", i32), ("fused_rows", i32),
                 ("no_packed", i32), ("one_term", i32), ("replay_graph_min", i32)]
@@ -135,6 +141,9 @@ _SIGS = {
     "rlt_dbg_gemm": (C.c_int, [P, P, P, i32, i32, i32, P, P]),
     "rlt_dbg_gemm_packed": (C.c_int, [P, P, P, i32, i32, i32, P, P]),
     "rlt_dbg_product_shape": (C.c_int, [P, i32, i32, i32, i32, i32]),
+    "rlt_dbg_stream_read": (C.c_int, [P, i64, i32, P, P]),
+    "rlt_dbg_narrow_bounds": (C.c_int, [i32, i32, i32, i32, i32, i32, i32, i32, i32, i32, i64,
+                                        C.POINTER(rlt_narrow_report)]),
     "rlt_dbg_profile": (C.c_int, [P, i32]),
     "rlt_dbg_profile_read": (C.c_int, [P, i32, C.POINTER(C.c_double), C.POINTER(C.c_int64)]),
 }

@@ -277,8 +277,8 @@ struct Epi {
 
 template <typename T>
 __device__ __forceinline__ const T* weight_row(const GemmArgs& g, int vc) {
-  const int seg = vc / g.seg_rows;
-  const int r = vc - seg * g.seg_rows;
+  int seg, r;
+  weight_pos(g, vc, seg, r);
   return (const T*)g.W[seg] + (int64_t)r * g.K;
 }
 
@@ -300,8 +300,8 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& g, const Epi<uint
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int ba, bb;
   pair_blocks(g, pair, ba, bb);
-  const int r16 = lane & 15;
-  const int kq = (lane >> 4) * 8;
+  const int r16 = narrow_lane_row(lane);
+  const int kq = narrow_lane_k(lane);
   const uint16_t* wa = weight_row<uint16_t>(g, ba * 16 + r16) + kq;
   const uint16_t* wb = weight_row<uint16_t>(g, bb * 16 + r16) + kq;
   const int m0 = mt * MB * 16;
@@ -319,26 +319,23 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& g, const Epi<uint
     acc[mb][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     acc[mb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  // The workgroup's K range [kw0, kw1) is cut in 32-wide steps dealt to the
-  // four waves round-robin (wave w takes steps w, w+4, ...): at any moment
-  // the waves read adjacent 64-byte pieces of each weight row, so rows are
-  // streamed in long contiguous runs.
-  const int kw0 = split * 4 * g.kslice;
-  const int kw1 = min(kw0 + 4 * g.kslice, g.K);
-  const int all_steps = max(0, (kw1 - kw0) / 32);
-  const int k0 = kw0 + 32 * wave;  // step j of this wave is at k0 + 128 j
+  // The workgroup's K range is cut in 32-wide steps dealt to the four waves
+  // round-robin (wave w takes steps w, w+4, ...): at any moment the waves
+  // read adjacent 64-byte pieces of each weight row, so rows are streamed in
+  // long contiguous runs.
+  int k0, nsteps;  // step j of this wave is at k0 + 128 j
+  narrow_wave_steps(g, split, wave, k0, nsteps);
   // PF K-steps of loads in flight: step i is multiplied while steps
   // i+1 .. i+PF-1 are still arriving (a register ring, statically indexed).
   // The steady-state loop is branch-free so that each step waits only for
   // its own loads: the refill of step i+PF is always issued, its address
   // clamped to the last step (a harmless re-read) near the end.
   constexpr int PF = MB >= 4 ? 4 : 6;
-  const int nsteps = (all_steps - wave + 3) / 4;
   bf16x8_t bufa[PF][MB], bufb[PF][2];
   if (nsteps > 0) {
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
-      const int k = k0 + 128 * min(p, nsteps - 1);
+      const int k = narrow_step_k(k0, p, nsteps);
       bufb[p][0] = load8(wa + k);
       bufb[p][1] = load8(wb + k);
 #pragma unroll
@@ -354,7 +351,7 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& g, const Epi<uint
         acc[mb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bufa[p][mb], bufb[p][0], acc[mb][0], 0, 0, 0);
         acc[mb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bufa[p][mb], bufb[p][1], acc[mb][1], 0, 0, 0);
       }
-      const int kn = k0 + 128 * min(i + p + PF, nsteps - 1);
+      const int kn = narrow_step_k(k0, i + p + PF, nsteps);
       bufb[p][0] = load8(wa + kn);
       bufb[p][1] = load8(wb + kn);
 #pragma unroll

@@ -519,6 +519,29 @@ __global__ void k_zero_rows(int* counts, const int* rows, int n, int B_cap) {
   if (row >= 0 && row < B_cap) counts[row] = 0;
 }
 
+// Calibration read: n16 16-byte pieces, each read once, with the load
+// instruction of the attention kernels' key and value streams (non-temporal
+// 16-byte loads) or a plain one; the xor of everything goes to sink only in
+// the unlikely case it equals a magic value (so the loads are kept).
+typedef unsigned int cal_u32x4 __attribute__((ext_vector_type(4)));
+template <bool NT>
+__global__ __launch_bounds__(256) void k_stream_read(const cal_u32x4* __restrict__ p, int64_t n16, unsigned* sink) {
+  const int64_t nth = (int64_t)gridDim.x * blockDim.x;
+  unsigned acc = 0;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += nth) {
+    const cal_u32x4 v = NT ? __builtin_nontemporal_load(p + i) : p[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == 0x9e3779b9u) *sink = acc;
+}
+
+void launch_stream_read(const void* p, int64_t n16, bool nontemporal, unsigned* sink, hipStream_t s) {
+  if (nontemporal)
+    hipLaunchKernelGGL(k_stream_read<true>, dim3(4096), dim3(256), 0, s, (const cal_u32x4*)p, n16, sink);
+  else
+    hipLaunchKernelGGL(k_stream_read<false>, dim3(4096), dim3(256), 0, s, (const cal_u32x4*)p, n16, sink);
+}
+
 void launch_zero_rows(int* counts, const int* rows, int n, int B_cap, hipStream_t s) {
   hipLaunchKernelGGL(k_zero_rows, dim3((n + 255) / 256), dim3(256), 0, s, counts, rows, n, B_cap);
 }

@@ -716,23 +716,8 @@ struct Gemm {
       g.S = S;
       g.kslice = (kst + S - 1) / S * 64;
     } else if (c->dt == 1) {
-      const int MB = gemm_row_blocks(n);
-      // K split: the persistent step fills its grid; a stand-alone kernel
-      // splits only while each split still adds a workgroup per compute unit
-      // (256 CUs): splitting further leaves workgroups queued behind others
-      // and adds partial traffic, which costs more than the latency it hides.
-      // The split fixes the summation order, so it is taken for a call of
-      // nr = min(max_rows, 32) rows whatever the call's own row count.
-      const int nr = c->narrow_rows, MBr = gemm_row_blocks(nr);
-      const int tiles = g.npairs * ((nr + 16 * MBr - 1) / (16 * MBr));
-      int S = c->gemm_target ? std::max(1, (c->gemm_target + tiles - 1) / tiles) : std::max(1, 256 / tiles);
-      S = std::min(S, std::max(1, K / 256));             // >= 64 K per wave
-      S = std::min(S, std::max(1, K / (4 * nr)));        // partial traffic <= the weights'
-      while (S > 1 && (size_t)S * g.M_pad * g.Nv > c->partial_cap) --S;
-      g.S = S;
-      g.mb = MB;
-      const int per = (K + 4 * S - 1) / (4 * S);
-      g.kslice = (per + 31) / 32 * 32;
+      narrow_plan(n, g.npairs, K, c->narrow_rows, c->gemm_target, g.M_pad, g.Nv, c->partial_cap, g.S, g.mb,
+                  g.kslice);
     }
     Prof pf(c, RLT_PROF_GEMM, s);
     launch_gemm(c->dt, g, e, s);
@@ -1863,6 +1848,92 @@ extern "C" int rlt_dbg_gemm_packed(rlt_ctx* c, const void* A, const void* W, int
   if (Ap) (void)hipFree(Ap);
   if (Wp) (void)hipFree(Wp);
   return rc;
+}
+
+extern "C" int rlt_dbg_narrow_bounds(int32_t n, int32_t npairs, int32_t K, int32_t pairing, int32_t dh,
+                                     int32_t nseg, int32_t seg_rows, int32_t M_pad, int32_t narrow_rows,
+                                     int32_t target, int64_t partial_cap, rlt_narrow_report* out) {
+  if (!out) return fail(RLT_EINVAL, "null report");
+  if (n < 1 || n > M_pad || npairs < 1 || K < 32 || nseg < 1 || nseg > 3 || seg_rows < 16 || narrow_rows < 1 ||
+      partial_cap < 0 || (pairing == PAIR_ROPE && (dh < 32 || dh % 32)))
+    return fail(RLT_EINVAL, "narrow bounds: arguments");
+  GemmArgs g{};
+  g.K = K;
+  g.pairing = pairing;
+  g.dh = dh;
+  g.nseg = nseg;
+  g.seg_rows = seg_rows;
+  g.M = n;
+  g.M_pad = M_pad;
+  g.npairs = npairs;
+  g.Nv = nseg * seg_rows;
+  narrow_plan(n, npairs, K, narrow_rows, target, M_pad, g.Nv, (size_t)partial_cap, g.S, g.mb, g.kslice);
+  rlt_narrow_report r{};
+  r.S = g.S;
+  r.mb = g.mb;
+  r.kslice = g.kslice;
+  r.a_row_max = -1;
+  r.a_col_end = 0;
+  r.w_seg_max = r.w_row_max = -1;
+  const int MB = g.mb, mtiles = (n + 16 * MB - 1) / (16 * MB);
+  // K coverage of one tile (the same for every tile): each 32-wide step once
+  std::vector<int> cover(K / 32 + 1, 0);
+  int64_t kend = 0;
+  for (int split = 0; split < g.S; ++split)
+    for (int wave = 0; wave < 4; ++wave) {
+      int k0, ns;
+      narrow_wave_steps(g, split, wave, k0, ns);
+      for (int j = 0; j < ns; ++j) {
+        const int k = narrow_step_k(k0, j, ns);
+        if (k / 32 < (int)cover.size()) ++cover[k / 32];
+      }
+      if (ns > 0)
+        for (int lane = 0; lane < 64; ++lane)
+          kend = std::max<int64_t>(kend, narrow_step_k(k0, ns - 1, ns) + narrow_lane_k(lane) + 8);
+    }
+  for (int st = 0; st < K / 32; ++st) {
+    if (cover[st] == 0) ++r.steps_missing;
+    if (cover[st] > 1) r.steps_repeated += cover[st] - 1;
+  }
+  for (size_t st = K / 32; st < cover.size(); ++st) r.steps_repeated += cover[st];  // steps past K
+  r.a_col_end = kend;
+  for (int pair = 0; pair < npairs; ++pair) {
+    int ba, bb;
+    pair_blocks(g, pair, ba, bb);
+    for (int lane = 0; lane < 64; ++lane)
+      for (int vc : {ba * 16 + narrow_lane_row(lane), bb * 16 + narrow_lane_row(lane)}) {
+        int seg, row;
+        weight_pos(g, vc, seg, row);
+        r.w_seg_max = std::max(r.w_seg_max, seg);
+        r.w_row_max = std::max(r.w_row_max, row);
+      }
+    for (int mt = 0; mt < mtiles; ++mt) {
+      const int m0 = mt * MB * 16;
+      for (int lane = 0; lane < 64; ++lane)
+        for (int mb = 0; mb < MB; ++mb) r.a_row_max = std::max<int64_t>(r.a_row_max, m0 + mb * 16 + narrow_lane_row(lane));
+      // epilogue: item idx of MB * 16 * 16 (row m, column r of the pair's halves); stores only rows < M
+      for (int idx = 0; idx < MB * 16 * 16; ++idx) {
+        const int slot = m0 + (idx >> 4), c = idx & 15;
+        if (slot >= n) continue;
+        if (g.S > 1)
+          for (int split = 0; split < g.S; ++split)
+            r.partial_end = std::max<int64_t>(
+                r.partial_end, ((int64_t)split * M_pad + slot) * g.Nv + std::max(ba, bb) * 16 + c + 1);
+        else
+          r.ssq_end = std::max<int64_t>(r.ssq_end, (int64_t)pair * M_pad + slot + 1);
+      }
+    }
+  }
+  *out = r;
+  return RLT_OK;
+}
+
+extern "C" int rlt_dbg_stream_read(const void* src, int64_t bytes, int32_t nontemporal, uint32_t* sink, void* stream) {
+  if (!src || !sink) return fail(RLT_EINVAL, "null argument");
+  if (bytes < 16 || bytes % 16 || (uintptr_t)src % 16) return fail(RLT_ESHAPE, "bytes and src must be 16-byte multiples");
+  launch_stream_read(src, bytes / 16, nontemporal != 0, sink, (hipStream_t)stream);
+  HIP_TRY(hipGetLastError());
+  return RLT_OK;
 }
 
 extern "C" int rlt_dbg_product_shape(rlt_ctx* c, int32_t rb, int32_t cb, int32_t lt, int32_t pf, int32_t pre) {

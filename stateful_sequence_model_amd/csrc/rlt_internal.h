@@ -3,6 +3,7 @@
 // bit patterns (RLT_BF16); the same T is used for weights, SWA cache,
 // encoder memory, e and the activations fed to matrix products.
 #pragma once
+#include <algorithm>
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -227,7 +228,7 @@ constexpr int rowrstd_lds() { return RowRstd<R, NT>::NU * R; }
 __host__ __device__ inline int gemm_row_blocks(int M) { return M <= 16 ? 1 : M <= 32 ? 2 : 4; }
 
 // virtual column blocks (16 columns each) of pair p
-__device__ __forceinline__ void pair_blocks(const GemmArgs& g, int p, int& ba, int& bb) {
+__host__ __device__ inline void pair_blocks(const GemmArgs& g, int p, int& ba, int& bb) {
   if (g.pairing == PAIR_PLAIN) {
     ba = 2 * p;
     bb = 2 * p + 1;
@@ -240,6 +241,51 @@ __device__ __forceinline__ void pair_blocks(const GemmArgs& g, int p, int& ba, i
     ba = p;
     bb = p + g.seg_rows / 16;
   }
+}
+
+// Index math of the narrow tile (gemm_bf16_body), shared with the host-side
+// bounds walk (rlt_dbg_narrow_bounds):
+// virtual column vc of a weight = row r of segment seg
+__host__ __device__ inline void weight_pos(const GemmArgs& g, int vc, int& seg, int& r) {
+  seg = vc / g.seg_rows;
+  r = vc - seg * g.seg_rows;
+}
+// the workgroup's K range [kw0, kw1) = split's 4 kslice, cut in 32-wide steps
+// dealt to the four waves round-robin: wave `wave` takes steps at k0 + 128 j,
+// j < nsteps
+__host__ __device__ inline void narrow_wave_steps(const GemmArgs& g, int split, int wave, int& k0, int& nsteps) {
+  const int kw0 = split * 4 * g.kslice;
+  const int kw1 = kw0 + 4 * g.kslice < g.K ? kw0 + 4 * g.kslice : g.K;
+  const int all = kw1 > kw0 ? (kw1 - kw0) / 32 : 0;
+  k0 = kw0 + 32 * wave;
+  nsteps = (all - wave + 3) / 4;
+}
+// K offset of the wave's step j, clamped to its last step (the refills past
+// the last step re-read it)
+__host__ __device__ inline int narrow_step_k(int k0, int j, int nsteps) { return k0 + 128 * (j < nsteps - 1 ? j : nsteps - 1); }
+// lane's row within a 16-row block and its 8-element K offset within a step
+__host__ __device__ inline int narrow_lane_row(int lane) { return lane & 15; }
+__host__ __device__ inline int narrow_lane_k(int lane) { return (lane >> 4) * 8; }
+// The host's choice of K split, row blocks per tile and per-wave K slice of
+// the narrow tile for an n-row call (nr = min(max_rows, 32) rows fix the
+// split, whatever the call's own row count; target: workgroups the
+// persistent step fills, 0 for a stand-alone kernel with 256 compute units).
+// The split fixes the summation order. It only splits while each split still
+// adds a workgroup per compute unit (splitting further leaves workgroups
+// queued behind others and adds partial traffic, which costs more than the
+// latency it hides), keeps >= 64 K per wave, partial traffic below the
+// weights', and the partials within the workspace.
+inline void narrow_plan(int n, int npairs, int K, int nr, int target, int M_pad, int Nv, size_t partial_cap, int& S,
+                        int& mb, int& kslice) {
+  mb = gemm_row_blocks(n);
+  const int MBr = gemm_row_blocks(nr);
+  const int tiles = npairs * ((nr + 16 * MBr - 1) / (16 * MBr));
+  S = target ? std::max(1, (target + tiles - 1) / tiles) : std::max(1, 256 / tiles);
+  S = std::min(S, std::max(1, K / 256));
+  S = std::min(S, std::max(1, K / (4 * nr)));
+  while (S > 1 && (size_t)S * M_pad * Nv > partial_cap) --S;
+  const int per = (K + 4 * S - 1) / (4 * S);
+  kslice = (per + 31) / 32 * 32;
 }
 
 // Epilogue kinds (functors live in the GEMM translation unit).
@@ -413,6 +459,8 @@ struct PostArgs {
   int* tick;                 // replay: position counter to advance by one, or null
 };
 void launch_poststep(const PostArgs& a, hipStream_t s);
+// read n16 16-byte pieces once (counter calibration)
+void launch_stream_read(const void* p, int64_t n16, bool nontemporal, unsigned* sink, hipStream_t s);
 // counts[rows[i]] = 0 for i < n (a fill kernel: capturable)
 void launch_zero_rows(int* counts, const int* rows, int n, int B_cap, hipStream_t s);
 

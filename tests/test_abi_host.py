@@ -43,8 +43,10 @@ def test_ctypes_layout_matches_header(tmp_path):
                "rlt_memory": _abi.rlt_memory, "rlt_step_io": _abi.rlt_step_io,
                "rlt_replay_io": _abi.rlt_replay_io, "rlt_score_io": _abi.rlt_score_io,
                "rlt_memory_weights": _abi.rlt_memory_weights, "rlt_snapshot_header": _abi.rlt_snapshot_header,
-               "rlt_grads": _abi.rlt_grads, "rlt_backward_io": _abi.rlt_backward_io}
-    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "rlt.h"', "int main(void){"]
+               "rlt_grads": _abi.rlt_grads, "rlt_backward_io": _abi.rlt_backward_io,
+               "rlt_dbg_launch": _abi.rlt_dbg_launch, "rlt_narrow_report": _abi.rlt_narrow_report}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "rlt.h"', '#include "rlt_debug.h"',
+             "int main(void){"]
     for sname, cls in structs.items():
         lines.append('printf("%s %%zu\\n", sizeof(%s));' % (sname, sname))
         for fname, _ in cls._fields_:
