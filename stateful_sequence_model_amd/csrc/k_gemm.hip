@@ -301,9 +301,9 @@ __device__ __forceinline__ void stream_fold(int j, f32x16_t& r, f32x16_t (&st)[f
 // into registers (one load instruction reads 1 KB of consecutive bytes; no
 // LDS staging and no barrier in the K loop). The K loop is branch-free, so
 // that each chunk waits only for its own loads: lanes of rows at or past M
-// load the last row below M (the same addresses for all of them, so a call
-// of a few rows reads little more than the weights; those outputs are
-// discarded), and loads past a wave's last chunk re-read that chunk (never
+// issue no activation loads (their registers stay zero, those outputs are
+// discarded; a call of a few rows then issues little more than its weight
+// loads), and loads past a wave's last chunk re-read that chunk (never
 // used). The epilogue threads add the waves' sums by the stream tree, from
 // LDS.
 // TWO: the activations carry a second bf16 term at A + a_lo (the rounding
@@ -331,12 +331,11 @@ __global__ __launch_bounds__(512) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16_t> 
   const int nchunk = g.K >> 6;
   const uint16_t* ap[RB];
   const uint16_t* wp[CB];
+  bool arow[RB];  // this lane's row of block r is below M (lane l holds row l % 32)
 #pragma unroll
   for (int r = 0; r < RB; ++r) {
-    // this lane's row of block r, clamped below M (lane l holds row l % 32)
-    const int last = g.M - 1 - (m0 + 32 * r);
-    const int rl = last < 0 ? 0 : ((lane & 31) < last ? (lane & 31) : last);
-    ap[r] = (const uint16_t*)g.A + ((int64_t)(mt * RB + r) * nchunk * 256 + (lane & 32) + rl) * 8;
+    arow[r] = m0 + 32 * r + (lane & 31) < g.M;
+    ap[r] = (const uint16_t*)g.A + ((int64_t)(mt * RB + r) * nchunk * 256 + lane) * 8;
   }
 #pragma unroll
   for (int c = 0; c < CB; ++c) wp[c] = (const uint16_t*)g.Wp + ((int64_t)(nt * CB + c) * nchunk * 256 + lane) * 8;
@@ -360,6 +359,15 @@ __global__ __launch_bounds__(512) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16_t> 
   const int c0 = stream_begin(nchunk, wave), n = stream_begin(nchunk, wave + 1) - c0;
   const int clast = n > 0 ? c0 + n - 1 : c0;
   bf16x8_t ra[PF][RB][4], rw[PF][CB][4], rl[TWO ? PF : 1][RB][4];
+#pragma unroll
+  for (int p = 0; p < PF; ++p)
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        ra[p][r][st] = bf16x8_t{};
+        rl[TWO ? p : 0][r][st] = bf16x8_t{};
+      }
   f32x16_t acc[RB][CB];
 #pragma unroll
   for (int r = 0; r < RB; ++r)
@@ -374,14 +382,14 @@ __global__ __launch_bounds__(512) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16_t> 
     const int64_t off = (int64_t)(cidx < clast ? cidx : clast) * 256 * 8;
 #pragma unroll
     for (int r = 0; r < RB; ++r)
+      if (arow[r]) {
 #pragma unroll
-      for (int st = 0; st < 4; ++st) ra[slot][r][st] = load8(ap[r] + off + st * 512);
-    if (TWO) {
+        for (int st = 0; st < 4; ++st) ra[slot][r][st] = load8(ap[r] + off + st * 512);
+        if (TWO) {
 #pragma unroll
-      for (int r = 0; r < RB; ++r)
-#pragma unroll
-        for (int st = 0; st < 4; ++st) rl[TWO ? slot : 0][r][st] = load8(ap[r] + g.a_lo + off + st * 512);
-    }
+          for (int st = 0; st < 4; ++st) rl[TWO ? slot : 0][r][st] = load8(ap[r] + g.a_lo + off + st * 512);
+        }
+      }
 #pragma unroll
     for (int c = 0; c < CB; ++c)
 #pragma unroll
@@ -585,13 +593,29 @@ __global__ __launch_bounds__(512) void k_gemm_bf16_lt(GemmArgs g, Epi<uint16_t> 
   load(1, 3);
   __syncthreads();
   frag(0, 0);
+  // Per chunk, in this order: the LDS writes of chunk i + 2 and the refill
+  // loads, then the next chunk's fragment reads interleaved with chunk i's
+  // MFMA chain. The barrier that ends a chunk waits only for this wave's
+  // writes (LDS operations complete in order: all but the NF fragment reads
+  // just issued), so those reads proceed across it; they target the buffer
+  // of chunk i + 1, which no wave writes before the next barrier. A plain
+  // barrier would wait for them and serialise the chain behind the reads.
   auto chunk = [&](int u, int i, bool refill) __attribute__((always_inline)) {  // chunk i, u = i % 6
     fold_until(cb + i);
-    frag((u + 1) & 1, (u + 1) % 3);
-    mma(u & 1);
     put(u & 1, (u + 2) % 3);
     if (refill) load(u & 1, i + 4);
-    __syncthreads();
+    frag((u + 1) & 1, (u + 1) % 3);
+    mma(u & 1);
+    __builtin_amdgcn_sched_group_barrier(0x200, PPT, 0);  // LDS writes first
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, TERMS + 1, 0);    // fragment reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);            // refill loads
+    }
+    static_assert(NF <= 15, "lgkmcnt field");
+    asm volatile("s_waitcnt lgkmcnt(%0)\n\ts_barrier" ::"n"(NF) : "memory");
   };
   int i = 0;
   for (; i + 10 <= n; i += 6) {  // every refill is a chunk still to come
@@ -603,6 +627,7 @@ __global__ __launch_bounds__(512) void k_gemm_bf16_lt(GemmArgs g, Epi<uint16_t> 
     for (int u = 0; u < 6; ++u)
       if (i + u < n) chunk(u, i + u, i + u + 4 < n);
   }
+  __syncthreads();      // every wave's fragment reads done before the stage buffers are reused
   fold_until(ce + 1);  // the group's remaining streams (empty ones included)
   if (Q < 8) {
     // group sum of block (rw, cw), rows below M, to the partial buffer
