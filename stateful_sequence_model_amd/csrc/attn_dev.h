@@ -59,10 +59,6 @@ template <> struct LaneVec<uint16_t> {
     *(uint4*)p0 = make_uint4(w[0], w[1], w[2], w[3]);
     *(uint4*)p1 = make_uint4(w[4], w[5], w[6], w[7]);
   }
-  __device__ static __forceinline__ void copy(uint16_t* d, const uint16_t* s, int h) {
-    *(uint4*)d = *(const uint4*)s;
-    *(uint4*)(d + h) = *(const uint4*)(s + h);
-  }
 };
 template <> struct LaneVec<float> {
   static constexpr int E = 8, PE = 4;
@@ -84,10 +80,6 @@ template <> struct LaneVec<float> {
   __device__ static __forceinline__ void store(float* p0, float* p1, const float* f) {
     *(float4*)p0 = make_float4(f[0], f[1], f[2], f[3]);
     *(float4*)p1 = make_float4(f[4], f[5], f[6], f[7]);
-  }
-  __device__ static __forceinline__ void copy(float* d, const float* s, int h) {
-    *(float4*)d = *(const float4*)s;
-    *(float4*)(d + h) = *(const float4*)(s + h);
   }
 };
 
@@ -297,6 +289,16 @@ __device__ __forceinline__ void swa_body(const AttnArgs& a, int hg, int slot, fl
   kv.nh = nh;
   kv.d = d;
 
+  // the cache insert's data (this lane's pieces of the current k and v),
+  // loaded before the walk so that the insert at the end is stores only
+  const bool ins = W1 > 0 && kg == 0;
+  uint4 ik0{}, ik1{}, iv0{}, iv1{};
+  if (ins) {
+    ik0 = *(const uint4*)kv.ck;
+    ik1 = *(const uint4*)(kv.ck + h);
+    iv0 = *(const uint4*)kv.cv;
+    iv1 = *(const uint4*)(kv.cv + h);
+  }
   Acc<T> acc;
   acc.init();
   walk<T, LPK, UNROLL>(acc, a.q + (int64_t)slot * d + col, a.qscale, kg, nh + 1, KPW, kv);
@@ -307,12 +309,16 @@ __device__ __forceinline__ void swa_body(const AttnArgs& a, int hg, int slot, fl
     const int c = c0 + (li / LPK) * DH + (li % LPK) * PE + (e < PE ? e : h + e - PE);
     store_op(out, a.out_pk ? pk_off(slot, c, d >> 6) : (int64_t)slot * d + c, a.out_lo, o * (1.f / L));
   });
-  // cache insert after every read of this workgroup
-  __syncthreads();
-  if (W1 > 0 && kg == 0) {
+  // cache insert: every read of this workgroup is complete (the barrier in
+  // merge_groups follows every thread's walk)
+  if (ins) {
     const int sl = (t - 1) % W1;
-    LV::copy((T*)a.ring_k + ((int64_t)row * W1 + sl) * d + col, kv.ck, h);
-    LV::copy((T*)a.ring_v + ((int64_t)row * W1 + sl) * d + col, kv.cv, h);
+    T* dk = (T*)a.ring_k + ((int64_t)row * W1 + sl) * d + col;
+    T* dv = (T*)a.ring_v + ((int64_t)row * W1 + sl) * d + col;
+    *(uint4*)dk = ik0;
+    *(uint4*)(dk + h) = ik1;
+    *(uint4*)dv = iv0;
+    *(uint4*)(dv + h) = iv1;
   }
 }
 

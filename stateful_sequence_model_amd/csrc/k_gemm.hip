@@ -585,8 +585,17 @@ __global__ __launch_bounds__(512) void k_gemm_bf16_lt(GemmArgs g, Epi<uint16_t> 
   // chunk i + 2 until it is written to LDS (then chunk i + 4). While chunk i
   // is multiplied, the wave reads chunk i + 1's fragments and the workgroup
   // writes chunk i + 2 into the third buffer.
-  load(0, 0);
-  load(1, 1);
+  // The row statistics are loaded first and staged in LDS before the loop
+  // (their registers are needed by the loop; the epilogue then reads LDS only).
+  if (norm_here) {  // uniform
+    RowRstd<R, NT> rr(g, m0);
+    load(0, 0);
+    load(1, 1);
+    rr.stage(s_part);
+  } else {
+    load(0, 0);
+    load(1, 1);
+  }
   put(0, 0);
   put(1, 1);
   load(0, 2);
@@ -647,10 +656,8 @@ __global__ __launch_bounds__(512) void k_gemm_bf16_lt(GemmArgs g, Epi<uint16_t> 
   float* red = (float*)&stage[0][0];
 #pragma unroll
   for (int e = 0; e < 16; ++e) red[((rw * NCB + cw) * 16 + e) * 64 + lane] = r[e];
-  if (norm_here) {  // uniform branch: contains a barrier (the row statistics are
-                    // loaded after the K loop, where their registers are free)
-    RowRstd<R, NT> rr(g, m0);
-    rr.finish(g, m0, s_part, s_rstd);
+  if (norm_here) {  // uniform branch: contains barriers
+    RowRstd<R, NT>::reduce(g, m0, s_part, s_rstd);
   }
   __syncthreads();
   constexpr int NU = R * NCB, NG = NT / 16, NI = NU / NG;

@@ -159,10 +159,11 @@ __device__ __forceinline__ float row_rstd(const GemmArgs& g, int m) {
 // Loads: the PA = NT / R threads of a row take the row's first PA * RU
 // units round-robin (thread slot sl: units sl, sl + PA, ...) into registers
 // when constructed (before the main loop, so the loads are in flight with
-// it); finish() stages them in LDS and the four part sums are then formed by
-// one thread each, reading units in increasing order (units past PA * RU,
-// only for very wide rows, straight from memory). Rows at or past M load
-// nothing (their rstd is never used).
+// it); finish() stages them in LDS (or stage() does, early, where the main
+// loop needs the registers) and the four part sums are then formed by one
+// thread each, reading units in increasing order (units past PA * RU, only
+// for very wide rows, straight from memory). Rows at or past M load nothing
+// (their rstd is never used).
 template <int R, int NT = 256>
 struct RowRstd {
   static constexpr int PA = NT / R;                 // threads per row
@@ -185,12 +186,21 @@ struct RowRstd {
       v[j] = u < g.ssq_units ? x : 0.f;
     }
   }
-  // s_part: LDS [NU][R] floats (the staged units; its first 4 R floats then
-  // hold the part sums); s_rstd: LDS [R]; contains two __syncthreads
-  __device__ __forceinline__ void finish(const GemmArgs& g, int m0, float* s_part, float* s_rstd) {
+  // the loaded units to s_part (LDS [NU][R] floats)
+  __device__ __forceinline__ void stage(float* s_part) const {
     const int row = threadIdx.x % R, sl = threadIdx.x / R;
 #pragma unroll
     for (int j = 0; j < RU; ++j) s_part[(sl + PA * j) * R + row] = v[j];
+  }
+  // s_part: LDS [NU][R] floats (the staged units; its first 4 R floats then
+  // hold the part sums); s_rstd: LDS [R]; contains three __syncthreads
+  __device__ __forceinline__ void finish(const GemmArgs& g, int m0, float* s_part, float* s_rstd) const {
+    stage(s_part);
+    reduce(g, m0, s_part, s_rstd);
+  }
+  // finish() after stage(s_part) ran (in every thread of the workgroup)
+  __device__ static __forceinline__ void reduce(const GemmArgs& g, int m0, float* s_part, float* s_rstd) {
+    const int row = threadIdx.x % R, sl = threadIdx.x / R;
     __syncthreads();
     // the threads of slots 0 .. 3 form the part sums (slot sl: parts sl, sl + PA, ...)
     constexpr int CPT = PA >= 4 ? 1 : 4 / PA;
