@@ -301,9 +301,9 @@ __device__ __forceinline__ void stream_fold(int j, f32x16_t& r, f32x16_t (&st)[f
 // into registers (one load instruction reads 1 KB of consecutive bytes; no
 // LDS staging and no barrier in the K loop). The K loop is branch-free, so
 // that each chunk waits only for its own loads: lanes of rows at or past M
-// issue no activation loads (their registers stay zero, those outputs are
-// discarded; a call of a few rows then issues little more than its weight
-// loads), and loads past a wave's last chunk re-read that chunk (never
+// load the last row below M (the same addresses for all of them, so a call
+// of a few rows reads little more than the weights; those outputs are
+// discarded), and loads past a wave's last chunk re-read that chunk (never
 // used). The epilogue threads add the waves' sums by the stream tree, from
 // LDS.
 // TWO: the activations carry a second bf16 term at A + a_lo (the rounding
@@ -331,11 +331,11 @@ __global__ __launch_bounds__(512) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16_t> 
   const int nchunk = g.K >> 6;
   const uint16_t* ap[RB];
   const uint16_t* wp[CB];
-  bool arow[RB];  // this lane's row of block r is below M (lane l holds row l % 32)
-#pragma unroll
   for (int r = 0; r < RB; ++r) {
-    arow[r] = m0 + 32 * r + (lane & 31) < g.M;
-    ap[r] = (const uint16_t*)g.A + ((int64_t)(mt * RB + r) * nchunk * 256 + lane) * 8;
+    // this lane's row of block r, clamped below M (lane l holds row l % 32)
+    const int last = g.M - 1 - (m0 + 32 * r);
+    const int rl = last < 0 ? 0 : ((lane & 31) < last ? (lane & 31) : last);
+    ap[r] = (const uint16_t*)g.A + ((int64_t)(mt * RB + r) * nchunk * 256 + (lane & 32) + rl) * 8;
   }
 #pragma unroll
   for (int c = 0; c < CB; ++c) wp[c] = (const uint16_t*)g.Wp + ((int64_t)(nt * CB + c) * nchunk * 256 + lane) * 8;
@@ -359,15 +359,6 @@ __global__ __launch_bounds__(512) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16_t> 
   const int c0 = stream_begin(nchunk, wave), n = stream_begin(nchunk, wave + 1) - c0;
   const int clast = n > 0 ? c0 + n - 1 : c0;
   bf16x8_t ra[PF][RB][4], rw[PF][CB][4], rl[TWO ? PF : 1][RB][4];
-#pragma unroll
-  for (int p = 0; p < PF; ++p)
-#pragma unroll
-    for (int r = 0; r < RB; ++r)
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        ra[p][r][st] = bf16x8_t{};
-        rl[TWO ? p : 0][r][st] = bf16x8_t{};
-      }
   f32x16_t acc[RB][CB];
 #pragma unroll
   for (int r = 0; r < RB; ++r)
@@ -382,14 +373,14 @@ __global__ __launch_bounds__(512) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16_t> 
     const int64_t off = (int64_t)(cidx < clast ? cidx : clast) * 256 * 8;
 #pragma unroll
     for (int r = 0; r < RB; ++r)
-      if (arow[r]) {
 #pragma unroll
-        for (int st = 0; st < 4; ++st) ra[slot][r][st] = load8(ap[r] + off + st * 512);
-        if (TWO) {
+      for (int st = 0; st < 4; ++st) ra[slot][r][st] = load8(ap[r] + off + st * 512);
+    if (TWO) {
 #pragma unroll
-          for (int st = 0; st < 4; ++st) rl[TWO ? slot : 0][r][st] = load8(ap[r] + g.a_lo + off + st * 512);
-        }
-      }
+      for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int st = 0; st < 4; ++st) rl[TWO ? slot : 0][r][st] = load8(ap[r] + g.a_lo + off + st * 512);
+    }
 #pragma unroll
     for (int c = 0; c < CB; ++c)
 #pragma unroll
