@@ -682,6 +682,18 @@ __global__ __launch_bounds__(256) void k_pk_combine(GemmArgs g, Epi<uint16_t> ep
   int ba, bb;
   pair_blocks(g, pair, ba, bb);
   const int m = mt * 16 + (threadIdx.x >> 4), r = threadIdx.x & 15;
+  // the group sums and the epilogue's own inputs are loaded first, so that
+  // their round trips overlap the row statistics' (rows at or past M load
+  // row M - 1, never used)
+  const int mc = m < g.M ? m : g.M - 1;
+  float va[G], vb[G];
+#pragma unroll
+  for (int k = 0; k < G; ++k) {
+    const float* P = g.partial + ((int64_t)k * g.M_pad + mc) * g.Nv;
+    va[k] = P[ba * 16 + r];
+    vb[k] = P[bb * 16 + r];
+  }
+  const typename Epi<uint16_t>::Pre pv = epi.pre(mc, ba * 16 + r, bb * 16 + r);
   if (g.ssq_in) {
     RowRstd<16> rr(g, mt * 16);
     rr.finish(g, mt * 16, s_part, s_rstd);
@@ -689,13 +701,6 @@ __global__ __launch_bounds__(256) void k_pk_combine(GemmArgs g, Epi<uint16_t> ep
   __syncthreads();
   float sq = 0.f;
   if (m < g.M) {
-    float va[G], vb[G];
-#pragma unroll
-    for (int k = 0; k < G; ++k) {
-      const float* P = g.partial + ((int64_t)k * g.M_pad + m) * g.Nv;
-      va[k] = P[ba * 16 + r];
-      vb[k] = P[bb * 16 + r];
-    }
 #pragma unroll
     for (int h = 1; h < G; h <<= 1)
 #pragma unroll
@@ -703,7 +708,7 @@ __global__ __launch_bounds__(256) void k_pk_combine(GemmArgs g, Epi<uint16_t> ep
         va[k] += va[k + h];
         vb[k] += vb[k + h];
       }
-    sq = epi(m, ba * 16 + r, va[0], bb * 16 + r, vb[0], g.ssq_in ? s_rstd[threadIdx.x >> 4] : 1.f);
+    sq = epi.apply(m, ba * 16 + r, va[0], bb * 16 + r, vb[0], g.ssq_in ? s_rstd[threadIdx.x >> 4] : 1.f, pv);
   }
   if (g.ssq_out) {
     sq = sum16(sq);
