@@ -12,8 +12,12 @@ reads t memory entries per row and layer), so the mean cost over a full run
 t = 1..T equals the cost at t = T/2: the timed steps are centred on T/2,
 starting from a synthetically pre-filled state (full SWA ring, pos set).
 
-Printed: one JSON line with the metric, the dominant kernel's roofline
-(algorithmic bytes / live HIP-event duration) and the CPU oracle baseline.
+The K timed steps are run --repeats times (3) at the same positions and the
+median is reported. Printed: one JSON line with the metric, the dominant
+kernel's roofline (algorithmic bytes / live HIP-event duration), the CPU
+oracle baseline and, for the default reference-depth run, the step at
+batches 1, 8 and 16 (t ~ 40 and t ~ T/2) against the step's algorithmic
+bytes at 8 TB/s.
 """
 from __future__ import annotations
 
@@ -125,6 +129,57 @@ def measured_traffic(x_bytes: float):
     return int(rec["traffic_over_algorithmic"] * x_bytes)
 
 
+def small_batches(wl, raw, cfg, mk, mv, es: int, graph: bool, batches=(1, 8, 16), K: int = 20, Wu: int = 3) -> list:
+    """The step at small batches (a context of exactly that many rows each),
+    timed at t ~ 40 and t ~ T/2 from a pre-filled state, against the step's
+    algorithmic bytes at 8 TB/s (the small-batch HBM target); rows use the
+    first rows of the main run's memory."""
+    import torch
+    from stateful_sequence_model_amd import Decoder, DecoderState, _abi
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(wl.seed + 1)
+    res = []
+    for B in batches:
+        dec = Decoder(cfg, raw, max_rows=B, max_ctx=wl.T)
+        st = DecoderState(cfg, B)
+        for l in range(wl.L):
+            st.ring("k")[l].normal_(generator=gen)
+            st.ring("v")[l].normal_(generator=gen)
+        mem_len = torch.full((B,), wl.T, dtype=torch.int32, device="cuda")
+        mem = Decoder.memory(mk[:, :B], mv[:, :B], mem_len)
+        e = torch.empty((B, wl.d), device="cuda", dtype=cfg.torch_dtype).normal_(generator=gen)
+        rows = torch.arange(B, dtype=torch.int32, device="cuda")
+        argmax = torch.empty(B, dtype=torch.int32, device="cuda")
+        stream = torch.cuda.Stream()
+        with torch.cuda.stream(stream):
+            for t_c in (40, wl.T // 2):
+                st.s.normal_(generator=gen)
+                st.pos.fill_(t_c - K // 2 - Wu)
+                st.pending.fill_(-1)
+                for _ in range(Wu):
+                    _abi.check(dec.step(st, rows, e, mem, argmax=argmax, graph=graph), "rlt_decoder_step")
+                ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                ev0.record(stream)
+                for _ in range(K):
+                    _abi.check(dec.step(st, rows, e, mem, argmax=argmax, graph=graph), "rlt_decoder_step")
+                ev1.record(stream)
+                torch.cuda.synchronize()
+                _abi.check(dec.sync_error(), "device error")
+                ms = ev0.elapsed_time(ev1) / K
+                t_mid = t_c - K // 2 + (K - 1) / 2.0
+                sb = step_bytes(wl, B, int(round(t_mid)), es)["total"]
+                gbs = sb / (ms / 1e3) / 1e9
+                res.append({"batch": B, "t_mid": t_mid, "ms_per_step": round(ms, 4),
+                            "transitions_per_s": round(B / (ms / 1e3), 1), "step_algorithmic_GBs": round(gbs, 1),
+                            "frac_of_8TBs": round(gbs / HBM_PEAK_GBS, 4)})
+                log("small batch B=%d t~%d: %.3f ms/step, %.1f GB/s (%.1f%% of 8 TB/s)"
+                    % (B, t_mid, ms, gbs, 100 * gbs / HBM_PEAK_GBS))
+        dec.close()
+        del dec, st
+        torch.cuda.empty_cache()
+    return res
+
+
 def calibrate(torch, nbytes: int = 4 << 30, reps: int = 10) -> dict:
     """Achievable HBM rates on this device, and known-size launches for the
     counter calibration: a plain copy (read + write), a read-only reduction
@@ -156,6 +211,21 @@ def calibrate(torch, nbytes: int = 4 << 30, reps: int = 10) -> dict:
         res[name + "_GBs"] = round(moved * reps / (e0.elapsed_time(e1) / 1e3) / 1e9, 1)
     del src, dst
     torch.cuda.empty_cache()
+    # matrix cores: independent chains of the bf16 32x32x16 instruction
+    blocks, iters = 1024, 20000
+    flops = 4 * 4 * 32768 * iters * blocks
+
+    def mfma():
+        _abi.check(_abi.lib().rlt_dbg_mfma_loop(blocks, iters, sink.data_ptr(), stream), "rlt_dbg_mfma_loop")
+    mfma()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        mfma()
+    e1.record()
+    torch.cuda.synchronize()
+    res["mfma_bf16_TFLOPs"] = round(flops * 5 / (e0.elapsed_time(e1) / 1e3) / 1e12, 1)
     return res
 
 
@@ -172,6 +242,11 @@ def main():
     ap.add_argument("--profile-steps", type=int, default=8)
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--repeats", type=int, default=3,
+                    help="timed runs of --steps steps each (same positions); the median is reported")
+    ap.add_argument("--no-small-batch", action="store_true",
+                    help="skip the small-batch lines (batches 1, 8, 16 at t ~ 40 and t ~ T/2) that the "
+                         "default reference-depth run adds")
     ap.add_argument("--calibrate", action="store_true",
                     help="also time a plain 4 GiB device copy and read-only sum (achievable HBM rates)")
     ap.add_argument("--launch", action="append", default=[], metavar="FIELD=VALUE",
@@ -258,14 +333,20 @@ def main():
         t_first = int(st.pos[0].item()) + 1
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
-        ev0.record(stream)
-        for _ in range(K):
-            _abi.check(dec.step(st, rows, e, mem, argmax=argmax, graph=graph), "rlt_decoder_step")
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        ms = ev0.elapsed_time(ev1)
-        _abi.check(dec.sync_error(), "device error")
-        assert int(st.pos[0].item()) == t_first + K - 1
+        runs = []
+        for r in range(max(1, args.repeats)):
+            if r:  # the same positions again
+                reset(t_first - 1)
+                torch.cuda.synchronize()
+            ev0.record(stream)
+            for _ in range(K):
+                _abi.check(dec.step(st, rows, e, mem, argmax=argmax, graph=graph), "rlt_decoder_step")
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            runs.append(ev0.elapsed_time(ev1))
+            _abi.check(dec.sync_error(), "device error")
+            assert int(st.pos[0].item()) == t_first + K - 1
+        ms = sorted(runs)[len(runs) // 2]
         # live per-kernel timing (direct launches, same positions as the timed steps)
         P = max(1, min(args.profile_steps, K))
         reset(t_first - 1)
@@ -335,7 +416,11 @@ def main():
                           "frac": round(sb["total"] / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                           "bytes_split": {k: int(v) for k, v in sb.items() if k != "total"}},
         "kernel_ms_per_step": breakdown,
+        "timing": {"repeats": len(runs), "statistic": "median",
+                   "ms_per_step_runs": [round(x / K, 4) for x in runs]},
     }
+    if wl.name == "reference_depth" and not args.batch and not args.t_center and not args.no_small_batch:
+        out["small_batch"] = small_batches(wl, raw, cfg, mk, mv, es, graph)
     if args.calibrate:
         out["calibration"] = calibrate(torch)
     if not args.no_cpu_baseline:

@@ -99,6 +99,15 @@ int rlt_dbg_narrow_bounds(int32_t n, int32_t npairs, int32_t K, int32_t pairing,
  * this launch against `bytes` gives the counter's bytes-per-unit factor. */
 int rlt_dbg_stream_read(const void* src, int64_t bytes, int32_t nontemporal, uint32_t* sink, void* stream);
 
+/* Peak calibration of the matrix cores: `blocks` workgroups of 256 threads,
+ * each wave running 4 independent chains of the bf16 32x32x16 matrix
+ * instruction (32768 flops each) for `iters` steps on register operands, on
+ * `stream`: 4 * 4 * 32768 * iters * blocks flops per launch, timed by the
+ * caller. sink: a device word written only if the results' xor equals a
+ * fixed value (it keeps the work). Errors: RLT_EINVAL (null sink),
+ * RLT_ESHAPE (blocks outside 1..2^20 or iters < 1). */
+int rlt_dbg_mfma_loop(int32_t blocks, int32_t iters, uint32_t* sink, void* stream);
+
 /* Kernel classes for the timing hook below. */
 enum {
   RLT_PROF_XATTN = 0,     /* prefix cross-attention partials (eq. 2.15) */

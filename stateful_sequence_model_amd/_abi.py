@@ -142,6 +142,7 @@ _SIGS = {
     "rlt_dbg_gemm_packed": (C.c_int, [P, P, P, i32, i32, i32, P, P]),
     "rlt_dbg_product_shape": (C.c_int, [P, i32, i32, i32, i32, i32]),
     "rlt_dbg_stream_read": (C.c_int, [P, i64, i32, P, P]),
+    "rlt_dbg_mfma_loop": (C.c_int, [i32, i32, P, P]),
     "rlt_dbg_narrow_bounds": (C.c_int, [i32, i32, i32, i32, i32, i32, i32, i32, i32, i32, i64,
                                         C.POINTER(rlt_narrow_report)]),
     "rlt_dbg_profile": (C.c_int, [P, i32]),

@@ -542,6 +542,38 @@ void launch_stream_read(const void* p, int64_t n16, bool nontemporal, unsigned* 
     hipLaunchKernelGGL(k_stream_read<false>, dim3(4096), dim3(256), 0, s, (const cal_u32x4*)p, n16, sink);
 }
 
+// Peak calibration of the matrix cores: every wave runs 4 independent
+// chains of v_mfma_f32_32x32x16_bf16 (enough to cover the instruction's
+// latency) for `iters` steps on register operands; sink is written only if
+// the results' xor equals a fixed value (it keeps the chains). 32768 flops
+// per instruction.
+typedef __bf16 cal_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float cal_f32x16 __attribute__((ext_vector_type(16)));
+__global__ __launch_bounds__(256) void k_mfma_loop(int iters, unsigned* sink) {
+  cal_bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(float)((threadIdx.x + i) & 7);
+    b[i] = (__bf16)(float)((threadIdx.x * 3 + i) & 7);
+  }
+  cal_f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int k = 0; k < iters; ++k) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, a, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, b, c3, 0, 0, 0);
+  }
+  unsigned acc = 0;
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+    acc ^= __float_as_uint(c0[e]) ^ __float_as_uint(c1[e]) ^ __float_as_uint(c2[e]) ^ __float_as_uint(c3[e]);
+  if (acc == 0x9e3779b9u) *sink = acc;
+}
+
+void launch_mfma_loop(int blocks, int iters, unsigned* sink, hipStream_t s) {
+  hipLaunchKernelGGL(k_mfma_loop, dim3(blocks), dim3(256), 0, s, iters, sink);
+}
+
 void launch_zero_rows(int* counts, const int* rows, int n, int B_cap, hipStream_t s) {
   hipLaunchKernelGGL(k_zero_rows, dim3((n + 255) / 256), dim3(256), 0, s, counts, rows, n, B_cap);
 }

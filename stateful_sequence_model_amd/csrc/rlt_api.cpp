@@ -1936,6 +1936,14 @@ extern "C" int rlt_dbg_stream_read(const void* src, int64_t bytes, int32_t nonte
   return RLT_OK;
 }
 
+extern "C" int rlt_dbg_mfma_loop(int32_t blocks, int32_t iters, uint32_t* sink, void* stream) {
+  if (!sink) return fail(RLT_EINVAL, "null argument");
+  if (blocks < 1 || blocks > (1 << 20) || iters < 1) return fail(RLT_ESHAPE, "blocks in 1..2^20, iters >= 1");
+  launch_mfma_loop(blocks, iters, sink, (hipStream_t)stream);
+  HIP_TRY(hipGetLastError());
+  return RLT_OK;
+}
+
 extern "C" int rlt_dbg_product_shape(rlt_ctx* c, int32_t rb, int32_t cb, int32_t lt, int32_t pf, int32_t pre) {
   if (!c) return fail(RLT_EINVAL, "null context");
   if (rb != 0 && (rb < 1 || rb > 2 || (cb != 1 && cb != 2) || (lt != 0 && lt != 1 && lt != 2 && lt != 4 && lt != 8) ||

@@ -471,6 +471,7 @@ struct PostArgs {
 void launch_poststep(const PostArgs& a, hipStream_t s);
 // read n16 16-byte pieces once (counter calibration)
 void launch_stream_read(const void* p, int64_t n16, bool nontemporal, unsigned* sink, hipStream_t s);
+void launch_mfma_loop(int blocks, int iters, unsigned* sink, hipStream_t s);
 // counts[rows[i]] = 0 for i < n (a fill kernel: capturable)
 void launch_zero_rows(int* counts, const int* rows, int n, int B_cap, hipStream_t s);
 
