@@ -136,6 +136,11 @@ def test_null_arguments_are_rejected():
     assert L.rlt_dbg_gemm_packed(None, None, None, 1, 32, 64, None, None) == _abi.RLT_EINVAL
     assert L.rlt_memory_prefill(None, None, None, 0, 0, None, None, 0, 0, None) == _abi.RLT_EINVAL
     assert L.rlt_replay_backward(None, None, None, None) == _abi.RLT_EINVAL
+    assert L.rlt_dbg_stream_read(None, 16, 1, None, None) == _abi.RLT_EINVAL
+    assert L.rlt_dbg_mfma_loop(1, 1, None, None) == _abi.RLT_EINVAL
+    # sizes are checked before any launch (the sink pointer is never touched)
+    assert L.rlt_dbg_mfma_loop(0, 1, 16, None) == _abi.RLT_ESHAPE
+    assert L.rlt_dbg_mfma_loop(1, 0, 16, None) == _abi.RLT_ESHAPE
 
 
 def test_snapshot_size_and_magic():
