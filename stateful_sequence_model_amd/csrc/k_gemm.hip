@@ -314,14 +314,24 @@ __device__ __forceinline__ void stream_fold(int j, f32x16_t& r, f32x16_t (&st)[f
 // tiles of one column tile share its weights in one L2.
 // PRE: the epilogue's memory reads (residual, gains, rotary table) are issued
 // before the K loop.
+// MS > 0 (calls of at most MS rows, K at most 64 PK_LDS_CHUNKS): the
+// activations' fragments of the call's rows (the only lanes whose outputs are
+// kept) are staged once in LDS for the whole K, and each chunk reads them
+// from there; the K loop then issues weight loads only. (At one row the
+// activation loads, at one address per half-wave but one instruction each,
+// otherwise take two of every three load slots of the compute unit.) Same
+// operand values for the kept rows, same instructions in the same order.
 // grid: 8 * mtiles * ceil(ntiles / 8); block 512.
-template <int RB, int CB, int PF, bool PRE, bool TWO>
+template <int RB, int CB, int PF, bool PRE, bool TWO, int MS>
 __global__ __launch_bounds__(512) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16_t> epi) {
-  constexpr int NW = 8, R = 32 * RB, NT = 64 * NW;
+  constexpr int NW = 8, R = 32 * RB, NT = 64 * NW, TERMS = TWO ? 2 : 1;
   constexpr int TILE = RB * CB * 16 * 64;  // floats of one wave's partial tile
+  static_assert(MS == 0 || (RB == 1 && MS <= 32), "staged activations: one row block");
   __shared__ float red[NW * TILE];
   __shared__ float s_rstd[R];
   __shared__ float s_part[rowrstd_lds<R, NT>()];
+  // staged activations: piece ((term * nchunk + c) * 4 + st) * 2 MS + half * MS + row
+  __shared__ bf16x8_t s_a[MS > 0 ? TERMS * PK_LDS_CHUNKS * 8 * MS : 1];
   const int mtiles = (g.M + R - 1) / R, ntiles = g.npairs / CB;
   const int b = blockIdx.x, q = b >> 3;
   const int mt = q % mtiles, nt = 8 * (q / mtiles) + (b & 7);
@@ -358,7 +368,11 @@ __global__ __launch_bounds__(512) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16_t> 
   // this wave's stream: chunks [c0, c0 + n); c0 < nchunk also when n = 0
   const int c0 = stream_begin(nchunk, wave), n = stream_begin(nchunk, wave + 1) - c0;
   const int clast = n > 0 ? c0 + n - 1 : c0;
-  bf16x8_t ra[PF][RB][4], rw[PF][CB][4], rl[TWO ? PF : 1][RB][4];
+  constexpr int AS = MS > 0 ? 1 : PF;  // activation register slots
+  bf16x8_t ra[AS][RB][4], rw[PF][CB][4], rl[TWO ? AS : 1][RB][4];
+  // staged activations: this lane's row (rows at or past M read row M - 1)
+  // and half of the 16-wide step
+  const int s_row = (lane & 31) < g.M ? (lane & 31) : g.M - 1, s_half = lane >> 5;
   f32x16_t acc[RB][CB];
 #pragma unroll
   for (int r = 0; r < RB; ++r)
@@ -371,42 +385,66 @@ __global__ __launch_bounds__(512) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16_t> 
   auto load = [&](int slot, int i) {
     const int cidx = c0 + i;
     const int64_t off = (int64_t)(cidx < clast ? cidx : clast) * 256 * 8;
-#pragma unroll
-    for (int r = 0; r < RB; ++r)
-#pragma unroll
-      for (int st = 0; st < 4; ++st) ra[slot][r][st] = load8(ap[r] + off + st * 512);
-    if (TWO) {
+    if (MS == 0) {
 #pragma unroll
       for (int r = 0; r < RB; ++r)
 #pragma unroll
-        for (int st = 0; st < 4; ++st) rl[TWO ? slot : 0][r][st] = load8(ap[r] + g.a_lo + off + st * 512);
+        for (int st = 0; st < 4; ++st) ra[MS ? 0 : slot][r][st] = load8(ap[r] + off + st * 512);
+      if (TWO) {
+#pragma unroll
+        for (int r = 0; r < RB; ++r)
+#pragma unroll
+          for (int st = 0; st < 4; ++st) rl[TWO && !MS ? slot : 0][r][st] = load8(ap[r] + g.a_lo + off + st * 512);
+      }
     }
 #pragma unroll
     for (int c = 0; c < CB; ++c)
 #pragma unroll
       for (int st = 0; st < 4; ++st) rw[slot][c][st] = load8(wp[c] + off + st * 512);
   };
-  auto compute = [&](int slot) {
+  // chunk i of the stream from register slot `slot` (and the staged activations)
+  auto compute = [&](int slot, int i) {
+    const int as = MS > 0 ? 0 : slot;
+    if (MS > 0) {
+      const int c = c0 + i;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        ra[0][0][st] = s_a[(c * 4 + st) * 2 * MS + s_half * MS + s_row];
+        if (TWO) rl[0][0][st] = s_a[((nchunk + c) * 4 + st) * 2 * MS + s_half * MS + s_row];
+      }
+    }
 #pragma unroll
     for (int st = 0; st < 4; ++st)
 #pragma unroll
       for (int r = 0; r < RB; ++r)
 #pragma unroll
         for (int c = 0; c < CB; ++c) {
-          acc[r][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[slot][r][st], rw[slot][c][st], acc[r][c], 0, 0, 0);
+          acc[r][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[as][r][st], rw[slot][c][st], acc[r][c], 0, 0, 0);
           if (TWO)
-            acc[r][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rl[TWO ? slot : 0][r][st], rw[slot][c][st], acc[r][c],
+            acc[r][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rl[TWO ? as : 0][r][st], rw[slot][c][st], acc[r][c],
                                                                0, 0, 0);
         }
   };
 #pragma unroll
   for (int p = 0; p < PF; ++p) load(p, p);
+  if (MS > 0) {
+    // the call's rows of every chunk, both terms (the first weight chunks are
+    // already in flight); rows past M: row M - 1 (never used)
+    const int npc = TERMS * nchunk * 8 * MS;
+    for (int p = tid; p < npc; p += NT) {
+      const int row = p % MS, rest = p / MS, half = rest & 1, tcs = rest >> 1, st = tcs & 3, tc = tcs >> 2;
+      const int term = tc >= nchunk ? 1 : 0, c = tc - term * nchunk;
+      const int rc = row < g.M ? row : g.M - 1;
+      s_a[p] = load8((const uint16_t*)g.A + (term ? g.a_lo : 0) + ((int64_t)c * 256 + st * 64 + half * 32 + rc) * 8);
+    }
+    __syncthreads();
+  }
   // steady state, branch-free: every refill is a chunk still to come
   int i = 0;
   for (; i + 2 * PF <= n; i += PF) {
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
-      compute(u);
+      compute(u, i + u);
       load(u, i + u + PF);
     }
   }
@@ -415,7 +453,7 @@ __global__ __launch_bounds__(512) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16_t> 
 #pragma unroll
     for (int u = 0; u < PF; ++u)
       if (i + u < n) {
-        compute(u);
+        compute(u, i + u);
         if (i + u + PF < n) load(u, i + u + PF);
       }
   }
@@ -846,11 +884,22 @@ void launch_gemm(int dtype, const GemmArgs& g0, const EpiArgs& e, hipStream_t s)
     // the Q/K/V product's epilogue computes its rotary angles (prefetching a
     // table lookup measured slower)
     const bool pre = g.pre >= 0 ? g.pre != 0 : (e.kind == EPI_RESID || e.kind == EPI_QROT);
-#define RLT_PK2(RB_, CB_, PF_, PRE_)                                                                   \
-  do {                                                                                                 \
-    if (two) hipLaunchKernelGGL((k_gemm_bf16_pk<RB_, CB_, PF_, PRE_, true>), grid, dim3(512), 0, s, g, epi); \
-    else hipLaunchKernelGGL((k_gemm_bf16_pk<RB_, CB_, PF_, PRE_, false>), grid, dim3(512), 0, s, g, epi);    \
+#define RLT_PK3(RB_, CB_, PF_, PRE_, MS_)                                                                   \
+  do {                                                                                                      \
+    if (two) hipLaunchKernelGGL((k_gemm_bf16_pk<RB_, CB_, PF_, PRE_, true, MS_>), grid, dim3(512), 0, s, g, epi); \
+    else hipLaunchKernelGGL((k_gemm_bf16_pk<RB_, CB_, PF_, PRE_, false, MS_>), grid, dim3(512), 0, s, g, epi);    \
   } while (0)
+#define RLT_PK2(RB_, CB_, PF_, PRE_) RLT_PK3(RB_, CB_, PF_, PRE_, 0)
+    if (g.a_lds > 0 && g.M <= g.a_lds && (g.K >> 6) <= PK_LDS_CHUNKS) {  // a few rows: activations in LDS
+      if (g.a_lds == 1) {
+        if (pre) RLT_PK3(1, 1, 2, true, 1);
+        else RLT_PK3(1, 1, 2, false, 1);
+      } else {
+        if (pre) RLT_PK3(1, 1, 2, true, 4);
+        else RLT_PK3(1, 1, 2, false, 4);
+      }
+      return;
+    }
 #define RLT_PK(RB_, CB_, PF_)              \
   do {                                     \
     if (pre) RLT_PK2(RB_, CB_, PF_, true); \
@@ -866,6 +915,7 @@ void launch_gemm(int dtype, const GemmArgs& g0, const EpiArgs& e, hipStream_t s)
 #undef RLT_SHAPE
 #undef RLT_PK
 #undef RLT_PK2
+#undef RLT_PK3
     return;
   }
   const int MB = g.mb;

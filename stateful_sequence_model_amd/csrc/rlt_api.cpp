@@ -681,6 +681,9 @@ struct Gemm {
       g.pre = -1;
       g.pf = n > 32 ? 3 : 2;
       g.lt_groups = 0;
+      // calls of at most 4 rows: activations staged in LDS (the K loop then
+      // issues weight loads only)
+      g.a_lds = (n <= 4 && K / 64 <= PK_LDS_CHUNKS) ? (n == 1 ? 1 : 4) : 0;
       if (n > 64 && g.npairs % 2 == 0) {
         const int tiles = g.npairs / 2 * ((n + 127) / 128);
         if (tiles >= 64) g.lt_groups = tiles >= 150 ? 1 : 2;
@@ -688,9 +691,13 @@ struct Gemm {
       }
       if (c->shape_rb > 0) {
         if (c->shape_lt > 0) {
-          if (g.npairs % 2 == 0 && (size_t)c->shape_lt * g.M_pad * g.Nv <= c->partial_cap) g.lt_groups = c->shape_lt;
+          if (g.npairs % 2 == 0 && (size_t)c->shape_lt * g.M_pad * g.Nv <= c->partial_cap) {
+            g.lt_groups = c->shape_lt;
+            g.a_lds = 0;
+          }
         } else if (g.npairs % c->shape_cb == 0) {
           g.lt_groups = 0;
+          g.a_lds = 0;
           g.rb = c->shape_rb;
           g.cb = c->shape_cb;
           g.pf = c->shape_pf;
