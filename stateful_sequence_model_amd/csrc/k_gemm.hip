@@ -314,13 +314,15 @@ __device__ __forceinline__ void stream_fold(int j, f32x16_t& r, f32x16_t (&st)[f
 // tiles of one column tile share its weights in one L2.
 // PRE: the epilogue's memory reads (residual, gains, rotary table) are issued
 // before the K loop.
-// MS > 0 (calls of at most MS rows, K at most 64 PK_LDS_CHUNKS): the
-// activations' fragments of the call's rows (the only lanes whose outputs are
-// kept) are staged once in LDS for the whole K, and each chunk reads them
-// from there; the K loop then issues weight loads only. (At one row the
-// activation loads, at one address per half-wave but one instruction each,
-// otherwise take two of every three load slots of the compute unit.) Same
-// operand values for the kept rows, same instructions in the same order.
+// MS > 0 (calls of at most MS rows, K at most 64 PK_LDS_CHUNKS; taken for
+// one-row calls): the activations' fragments of the call's rows (the only
+// lanes whose outputs are kept) are staged once in LDS for the whole K, and
+// each chunk reads them from there; the K loop then issues weight loads only.
+// (At one row the activation loads, at one address per half-wave but one
+// instruction each, otherwise take two of every three load slots of the
+// compute unit; the smaller register and LDS footprint also fits two
+// workgroups per compute unit.) Same operand values for the kept rows, same
+// instructions in the same order.
 // grid: 8 * mtiles * ceil(ntiles / 8); block 512.
 template <int RB, int CB, int PF, bool PRE, bool TWO, int MS>
 __global__ __launch_bounds__(512) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16_t> epi) {
@@ -890,14 +892,9 @@ void launch_gemm(int dtype, const GemmArgs& g0, const EpiArgs& e, hipStream_t s)
     else hipLaunchKernelGGL((k_gemm_bf16_pk<RB_, CB_, PF_, PRE_, false, MS_>), grid, dim3(512), 0, s, g, epi);    \
   } while (0)
 #define RLT_PK2(RB_, CB_, PF_, PRE_) RLT_PK3(RB_, CB_, PF_, PRE_, 0)
-    if (g.a_lds > 0 && g.M <= g.a_lds && (g.K >> 6) <= PK_LDS_CHUNKS) {  // a few rows: activations in LDS
-      if (g.a_lds == 1) {
-        if (pre) RLT_PK3(1, 1, 2, true, 1);
-        else RLT_PK3(1, 1, 2, false, 1);
-      } else {
-        if (pre) RLT_PK3(1, 1, 2, true, 4);
-        else RLT_PK3(1, 1, 2, false, 4);
-      }
+    if (g.a_lds == 1 && g.M == 1 && (g.K >> 6) <= PK_LDS_CHUNKS) {  // one row: activations in LDS
+      if (pre) RLT_PK3(1, 1, 2, true, 1);
+      else RLT_PK3(1, 1, 2, false, 1);
       return;
     }
 #define RLT_PK(RB_, CB_, PF_)              \

@@ -681,9 +681,9 @@ struct Gemm {
       g.pre = -1;
       g.pf = n > 32 ? 3 : 2;
       g.lt_groups = 0;
-      // calls of at most 4 rows: activations staged in LDS (the K loop then
-      // issues weight loads only)
-      g.a_lds = (n <= 4 && K / 64 <= PK_LDS_CHUNKS) ? (n == 1 ? 1 : 4) : 0;
+      // one-row calls: activations staged in LDS (the K loop then issues
+      // weight loads only; at 4 and 8 rows measured slower)
+      g.a_lds = (n == 1 && K / 64 <= PK_LDS_CHUNKS) ? 1 : 0;
       if (n > 64 && g.npairs % 2 == 0) {
         const int tiles = g.npairs / 2 * ((n + 127) / 128);
         if (tiles >= 64) g.lt_groups = tiles >= 150 ? 1 : 2;

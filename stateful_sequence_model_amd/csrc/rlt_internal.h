@@ -97,7 +97,7 @@ __host__ __device__ inline int64_t pk_off(int m, int k, int nchunk) {
          (k & 7);
 }
 
-// 64-wide chunks of K the register tile can stage in LDS for calls of a few rows
+// 64-wide chunks of K the register tile can stage in LDS for one-row calls
 constexpr int PK_LDS_CHUNKS = 96;
 
 struct GemmArgs {
@@ -111,8 +111,8 @@ struct GemmArgs {
   int pf;                 // fragment-order tile: chunks in flight per wave
   int lt_groups;          // fragment order, > 0: staged 128-row tile, this many workgroups
                           // per tile over the stream groups (1, 2, 4 or 8); 0: register tile
-  int a_lds;              // register tile: > 0 (1 or 4, at least M; K <= 64 PK_LDS_CHUNKS):
-                          // the activations staged in LDS for the whole K
+  int a_lds;              // register tile: 1 (M = 1, K <= 64 PK_LDS_CHUNKS): the
+                          // activations staged in LDS for the whole K
   int pre;                // fragment-order tile: -1 = by epilogue kind, 0/1 = epilogue values after / before the K loop
   int nseg, seg_rows;
   int K;

@@ -227,13 +227,13 @@ def test_batch_invariance_across_product_tiles():
 def test_every_product_shape_bit_identical():
     """Mid width (K = 1024 and 2816: 16 and 44 chunks of 64, so stream groups
     of 2 to 44 chunks and every tail of the staged tile's unrolled loop) at 1,
-    3, 40 and 128 rows: each operand-order product shape the launcher can be
+    3, 8, 40 and 128 rows: each operand-order product shape the launcher can be
     told to take -- register tile of 32 or 64 rows x 1 or 2 column pairs with
     1-4 chunks in flight and the epilogue values loaded before or after the K
     loop; staged 128-row tile over 1, 2, 4 or 8 stream groups (with the
     combine kernel below 8 streams per group) -- gives states and logits
-    bit-identical to the default shapes (at 1 and 3 rows: the register tile
-    with the activations staged in LDS): the stream tree fixes the summation
+    bit-identical to the default shapes (at 1 row: the register tile with
+    the activations staged in LDS): the stream tree fixes the summation
     order, the tile does not."""
     require_gpu()
     from stateful_sequence_model_amd import _abi
@@ -242,7 +242,7 @@ def test_every_product_shape_bit_identical():
     shapes = [(1, 1, 0, 2, 0), (1, 1, 0, 2, 1), (1, 1, 0, 3, 0), (1, 1, 0, 3, 1), (1, 1, 0, 4, 0), (2, 1, 0, 1, 1),
               (2, 1, 0, 2, 0), (1, 2, 0, 1, 1), (1, 2, 0, 2, 0), (1, 1, 1, 1, 0), (1, 1, 2, 1, 0), (1, 1, 4, 1, 0),
               (1, 1, 8, 1, 0)]
-    for B in (1, 3, 40, 128):
+    for B in (1, 3, 8, 40, 128):
         base = GpuRun(wl, raw=raw, B=B, T=wl.T)
         base.init()
         S, Z = base.run(3)
