@@ -58,8 +58,9 @@ int rlt_dbg_create(const rlt_config* cfg, const rlt_weights* w, int32_t max_rows
                    const rlt_dbg_launch* opt, rlt_ctx** out);
 
 /* Tuning sweeps: force the shape of the operand-order products of later
- * calls. lt > 0: the staged 128-row tile split over lt workgroups per tile
- * (1, 2, 4 or 8; rb, cb, pf, pre ignored). lt = 0: the register tile of
+ * calls. lt > 0: the staged tile split over lt workgroups per tile
+ * (1, 2, 4 or 8), of 128 rows x 2 column pairs, or of 64 rows x 4 column
+ * pairs when cb = 4 (rb, pf, pre ignored). lt = 0: the register tile of
  * 32 * rb rows and cb column pairs with pf chunks in flight per wave, the
  * epilogue's values loaded before (pre = 1) or after (0) the K loop, or by
  * epilogue kind (-1). rb = 0 restores the library's choice. Shapes change

@@ -511,14 +511,15 @@ __global__ __launch_bounds__(512) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16_t> 
 }
 
 // Product for calls of more than 64 rows, both operands in fragment order:
-// a workgroup owns 128 rows (4 row blocks) x 2 column pairs and a group of Q
-// consecutive streams (8 / Q workgroups per tile split the K range). Each
-// 64-wide chunk of both operands (128 x 64 activations, one or two terms, and
-// 64 x 64 weights: 40 KB with two terms) is staged once into LDS by all 512
+// a workgroup owns 32 RBK rows (RBK = 4 or 2 row blocks) x 8 / RBK column
+// pairs and a group of Q consecutive streams (8 / Q workgroups per tile split
+// the K range). Each 64-wide chunk of both operands (RBK = 4: 128 x 64
+// activations, one or two terms, and 64 x 64 weights, 40 KB with two terms;
+// RBK = 2: 64 x 64 and 128 x 64, 32 KB) is staged once into LDS by all 512
 // threads (16-byte pieces; one wave load reads 1 KB of consecutive bytes and
-// writes it to consecutive LDS), so the weights are read once per 128 rows
-// and the activations once per 64 columns. Wave w computes block (w / 2,
-// w % 2) from LDS, running through its group's streams in order and folding
+// writes it to consecutive LDS), so the weights are read once per tile's
+// rows and the activations once per tile's columns. Wave w computes block
+// (w / NCB, w % NCB) from LDS, running through its group's streams in order and folding
 // each finished stream into a stack of subtrees (stream_fold), which gives
 // the stream tree's order exactly. Three LDS buffers: while a chunk is
 // multiplied, each wave reads the next chunk's fragments into registers and
@@ -528,9 +529,10 @@ __global__ __launch_bounds__(512) void k_gemm_bf16_pk(GemmArgs g, Epi<uint16_t> 
 // its group sum (rows below M) to g.partial[group] and k_pk_combine finishes.
 // Rows past the last 32-row block below M load that block (discarded).
 // grid: 8 * (mtiles * G) * ceil(ntiles / 8), G = 8 / Q; block 512.
-template <int Q, bool TWO>
+template <int Q, bool TWO, int RBK>
 __global__ __launch_bounds__(512) void k_gemm_bf16_lt(GemmArgs g, Epi<uint16_t> epi) {
-  constexpr int NT = 512, R = 128, RBK = 4, NCB = 2, G = 8 / Q, TERMS = TWO ? 2 : 1, NF = 4 * (TERMS + 1);
+  constexpr int NT = 512, R = 32 * RBK, NCB = 8 / RBK, G = 8 / Q, TERMS = TWO ? 2 : 1, NF = 4 * (TERMS + 1);
+  static_assert(RBK == 4 || RBK == 2, "128 x 64 or 64 x 128 tiles");
   constexpr int A_PIECES = RBK * TERMS * 256, PIECES = A_PIECES + NCB * 256, PPT = PIECES / NT;
   static_assert(PIECES % NT == 0, "16-byte pieces per thread");
   constexpr int TILE = RBK * NCB * 16 * 64;  // floats of the workgroup's tile, C layout
@@ -579,7 +581,7 @@ __global__ __launch_bounds__(512) void k_gemm_bf16_lt(GemmArgs g, Epi<uint16_t> 
 #pragma unroll
     for (int k = 0; k < PPT; ++k) stage[buf][tid + NT * k] = rg[set][k];
   };
-  const int rw = wave >> 1, cw = wave & 1;
+  const int rw = wave / NCB, cw = wave % NCB;
   auto frag = [&](int f, int buf) __attribute__((always_inline)) {
     const u32x4_t* sa = &stage[buf][rw * TERMS * 256 + lane];
     const u32x4_t* sw = &stage[buf][A_PIECES + cw * 256 + lane];
@@ -855,14 +857,20 @@ void launch_gemm(int dtype, const GemmArgs& g0, const EpiArgs& e, hipStream_t s)
     Epi<uint16_t> epi{e};
     const bool two = g.a_lo != 0;
     if (g.lt_groups > 0) {
-      // staged tile: 128 rows x 2 column pairs per workgroup, G workgroups
-      // per tile over the stream groups
-      const int G = g.lt_groups, mtiles = (g.M + 127) / 128, ntiles = g.npairs / 2;
+      // staged tile: 32 rbk rows x 8 / rbk column pairs per workgroup, G
+      // workgroups per tile over the stream groups
+      const int rbk = g.lt_rbk == 2 ? 2 : 4;
+      const int G = g.lt_groups, mtiles = (g.M + 32 * rbk - 1) / (32 * rbk), ntiles = g.npairs / (8 / rbk);
       dim3 grid(8 * mtiles * G * ((ntiles + 7) / 8));
-#define RLT_LT(Q_)                                                                              \
-  do {                                                                                          \
-    if (two) hipLaunchKernelGGL((k_gemm_bf16_lt<Q_, true>), grid, dim3(512), 0, s, g, epi);   \
-    else hipLaunchKernelGGL((k_gemm_bf16_lt<Q_, false>), grid, dim3(512), 0, s, g, epi);      \
+#define RLT_LT2(Q_, RBK_)                                                                              \
+  do {                                                                                                 \
+    if (two) hipLaunchKernelGGL((k_gemm_bf16_lt<Q_, true, RBK_>), grid, dim3(512), 0, s, g, epi);     \
+    else hipLaunchKernelGGL((k_gemm_bf16_lt<Q_, false, RBK_>), grid, dim3(512), 0, s, g, epi);        \
+  } while (0)
+#define RLT_LT(Q_)                       \
+  do {                                   \
+    if (rbk == 2) RLT_LT2(Q_, 2);         \
+    else RLT_LT2(Q_, 4);                  \
   } while (0)
       switch (G) {
         case 1: RLT_LT(8); break;
@@ -871,6 +879,7 @@ void launch_gemm(int dtype, const GemmArgs& g0, const EpiArgs& e, hipStream_t s)
         default: RLT_LT(1); break;
       }
 #undef RLT_LT
+#undef RLT_LT2
       if (G > 1) {
         dim3 g2(g.npairs, (g.M + 15) / 16);
         switch (G) {

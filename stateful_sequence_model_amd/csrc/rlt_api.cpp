@@ -671,28 +671,35 @@ struct Gemm {
       // stream order, see the kernels), measured per product at 1 and 128
       // rows, reference depth: calls of more than 64 rows whose products
       // have at least 64 staged tiles of 128 rows x 64 columns (Q/K/V,
-      // gate/up, vocabulary) take the staged tile, in one workgroup per tile
-      // from 150 tiles, else split over two stream groups; the others the
-      // register tile of 32 rows, two chunks in flight per wave (three past
-      // 32 rows)
+      // gate/up, vocabulary) take the staged tile (64 x 128 where the
+      // columns allow), in one workgroup per tile from 150 tiles, else
+      // split over two stream groups; the others the register tile of 32
+      // rows, two chunks in flight per wave (three past 32 rows)
       g.Wp = Wp;
       g.rb = 1;
       g.cb = 1;
       g.pre = -1;
       g.pf = n > 32 ? 3 : 2;
       g.lt_groups = 0;
+      g.lt_rbk = 4;
       // one-row calls: activations staged in LDS (the K loop then issues
       // weight loads only; at 4 and 8 rows measured slower)
       g.a_lds = (n == 1 && K / 64 <= PK_LDS_CHUNKS) ? 1 : 0;
       if (n > 64 && g.npairs % 2 == 0) {
-        const int tiles = g.npairs / 2 * ((n + 127) / 128);
+        const int tiles = g.npairs / 2 * ((n + 127) / 128);  // counted in 128 x 64 tiles
         if (tiles >= 64) g.lt_groups = tiles >= 150 ? 1 : 2;
         while (g.lt_groups > 1 && (size_t)g.lt_groups * g.M_pad * g.Nv > c->partial_cap) g.lt_groups /= 2;
+        // tiles of 64 rows x 4 column pairs where the columns allow: the same
+        // workgroups move a fifth less through LDS per chunk (measured faster
+        // for Q/K/V, gate/up and the vocabulary at 128 rows)
+        if (g.lt_groups > 0 && g.npairs % 4 == 0) g.lt_rbk = 2;
       }
       if (c->shape_rb > 0) {
         if (c->shape_lt > 0) {
-          if (g.npairs % 2 == 0 && (size_t)c->shape_lt * g.M_pad * g.Nv <= c->partial_cap) {
+          const int lcb = c->shape_cb == 4 ? 4 : 2;  // column pairs per staged tile
+          if (g.npairs % lcb == 0 && (size_t)c->shape_lt * g.M_pad * g.Nv <= c->partial_cap) {
             g.lt_groups = c->shape_lt;
+            g.lt_rbk = 8 / lcb;
             g.a_lds = 0;
           }
         } else if (g.npairs % c->shape_cb == 0) {
@@ -1953,8 +1960,8 @@ extern "C" int rlt_dbg_mfma_loop(int32_t blocks, int32_t iters, uint32_t* sink, 
 
 extern "C" int rlt_dbg_product_shape(rlt_ctx* c, int32_t rb, int32_t cb, int32_t lt, int32_t pf, int32_t pre) {
   if (!c) return fail(RLT_EINVAL, "null context");
-  if (rb != 0 && (rb < 1 || rb > 2 || (cb != 1 && cb != 2) || (lt != 0 && lt != 1 && lt != 2 && lt != 4 && lt != 8) ||
-                  pf < 1 || pf > 4 || pre < -1 || pre > 1))
+  if (rb != 0 && (rb < 1 || rb > 2 || (cb != 1 && cb != 2 && !(cb == 4 && lt > 0)) ||
+                  (lt != 0 && lt != 1 && lt != 2 && lt != 4 && lt != 8) || pf < 1 || pf > 4 || pre < -1 || pre > 1))
     return fail(RLT_EINVAL, "product shape");
   c->shape_rb = rb;
   c->shape_cb = cb;

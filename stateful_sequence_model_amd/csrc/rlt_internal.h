@@ -109,8 +109,9 @@ struct GemmArgs {
                           // pairs as 32-row blocks (pair p = block p), or null
   int rb, cb;             // fragment-order tile: 32 rb rows x cb column pairs
   int pf;                 // fragment-order tile: chunks in flight per wave
-  int lt_groups;          // fragment order, > 0: staged 128-row tile, this many workgroups
+  int lt_groups;          // fragment order, > 0: staged tile, this many workgroups
                           // per tile over the stream groups (1, 2, 4 or 8); 0: register tile
+  int lt_rbk;             // staged tile: 32-row blocks per tile, 4 (128 x 64) or 2 (64 x 128)
   int a_lds;              // register tile: 1 (M = 1, K <= 64 PK_LDS_CHUNKS): the
                           // activations staged in LDS for the whole K
   int pre;                // fragment-order tile: -1 = by epilogue kind, 0/1 = epilogue values after / before the K loop

@@ -230,8 +230,9 @@ def test_every_product_shape_bit_identical():
     3, 8, 40 and 128 rows: each operand-order product shape the launcher can be
     told to take -- register tile of 32 or 64 rows x 1 or 2 column pairs with
     1-4 chunks in flight and the epilogue values loaded before or after the K
-    loop; staged 128-row tile over 1, 2, 4 or 8 stream groups (with the
-    combine kernel below 8 streams per group) -- gives states and logits
+    loop; staged tile of 128 x 64 or 64 x 128 over 1, 2, 4 or 8 stream
+    groups (with the combine kernel below 8 streams per group) -- gives
+    states and logits
     bit-identical to the default shapes (at 1 row: the register tile with
     the activations staged in LDS): the stream tree fixes the summation
     order, the tile does not."""
@@ -241,7 +242,7 @@ def test_every_product_shape_bit_identical():
     raw = synth.make_weights(wl)
     shapes = [(1, 1, 0, 2, 0), (1, 1, 0, 2, 1), (1, 1, 0, 3, 0), (1, 1, 0, 3, 1), (1, 1, 0, 4, 0), (2, 1, 0, 1, 1),
               (2, 1, 0, 2, 0), (1, 2, 0, 1, 1), (1, 2, 0, 2, 0), (1, 1, 1, 1, 0), (1, 1, 2, 1, 0), (1, 1, 4, 1, 0),
-              (1, 1, 8, 1, 0)]
+              (1, 1, 8, 1, 0), (1, 4, 1, 1, 0), (1, 4, 2, 1, 0), (1, 4, 4, 1, 0), (1, 4, 8, 1, 0)]
     for B in (1, 3, 8, 40, 128):
         base = GpuRun(wl, raw=raw, B=B, T=wl.T)
         base.init()

@@ -106,7 +106,7 @@ def _min_reads_after_last_write(blocks, preds, k, pos, nf):
 
 def test_staged_tile_barrier_waits_cover_the_lds_writes(gemm_asm):
     seen = 0
-    for name, body in _kernels(gemm_asm, r"_ZN3rlt14k_gemm_bf16_ltILi\dELb\dEEEvNS_8GemmArgsENS_3EpiItEE"):
+    for name, body in _kernels(gemm_asm, r"_ZN3rlt14k_gemm_bf16_ltILi\dELb\dELi\dEEEvNS_8GemmArgsENS_3EpiItEE"):
         two = re.search(r"ILi\dELb(\d)", name).group(1) == "1"
         nf = 4 * (3 if two else 2)
         blocks, preds = _blocks(body)
@@ -119,7 +119,7 @@ def test_staged_tile_barrier_waits_cover_the_lds_writes(gemm_asm):
                     assert r >= nf, (name, "a path with only %d LDS reads after the last write" % r)
         assert relaxed >= 2, (name, "relaxed chunk barriers not found")
         seen += 1
-    assert seen == 8  # Q in 1, 2, 4, 8 with one and two activation terms
+    assert seen == 16  # Q in 1, 2, 4, 8 with one and two activation terms, 128 x 64 and 64 x 128 tiles
 
 
 def test_checker_finds_a_short_path():
