@@ -69,7 +69,10 @@ def cpu_baseline(wl, t0: int, budget_s: float, raw) -> dict:
     """The float32 oracle timed on this host on a bounded sample: one
     sequence, consecutive transitions (with the readout) from a pre-filled
     state at t0, first with the BLAS thread pool at its default size (all
-    cores), then with one thread; each leg gets half the budget."""
+    cores), then with one thread; each leg gets half the budget. As a
+    cross-check of the affine cost model, one transition (all threads) at
+    t = 1, W, T/4, T/2, 3T/4 and T: cost fitted as a + b t and averaged over a
+    full run t = 1..T."""
     import numpy as np
     import synth
     from oracle import Config, Memory, Oracle, state_from_ring
@@ -81,7 +84,7 @@ def cpu_baseline(wl, t0: int, budget_s: float, raw) -> dict:
     cfg = Config(L=wl.L, d=wl.d, H=wl.H, dh=wl.dh, W=wl.W, G=wl.G, F=wl.F, V=wl.V, merge=wl.merge,
                  alpha=wl.alpha, eps=wl.eps, rope_theta=wl.rope_theta, pos=wl.pos)
     orc = Oracle(cfg, {k: widen(v) for k, v in raw.items()}, dtype=np.float32)
-    nT = t0 + 64
+    nT = max(t0 + 64, wl.T + 1)
     mem = Memory([widen(synth.make_memory(wl, "k", g, 0, 1, nT)[0]) for g in range(wl.G)],
                  [widen(synth.make_memory(wl, "v", g, 0, 1, nT)[0]) for g in range(wl.G)])
     rk = np.stack([widen(synth.make_ring_prefill(wl, "k", l, 0, 1)[0]) for l in range(wl.L)])
@@ -105,11 +108,24 @@ def cpu_baseline(wl, t0: int, budget_s: float, raw) -> dict:
     n_all, el_all = leg(budget_s / 2)
     with threadpool_limits(limits=1):
         n_one, el_one = leg(budget_s / 2)
+    prof = {}
+    for t in sorted({1, wl.W, wl.T // 4, wl.T // 2, 3 * wl.T // 4, wl.T}):
+        st = state_from_ring(cfg, s0, t - 1, rk, rv, dtype=np.float32)
+        t_start = time.perf_counter()
+        st = orc.transition(st, E[st.pos], mem)
+        orc.logits(st.s)
+        prof[t] = time.perf_counter() - t_start
+    ts = np.array(sorted(prof), dtype=np.float64)
+    b, a = np.polyfit(ts, np.array([prof[t] for t in sorted(prof)]), 1)
+    mean_cost = a + b * (wl.T + 1) / 2.0
     return {"value": n_all / el_all, "unit": "transitions/s", "cores": int(threads), "kind": "oracle",
             "value_1_thread": n_one / el_one, "cpu_model": _cpu_model(), "host_cpus": os.cpu_count(),
+            "t_profile_s": {int(t): round(v, 4) for t, v in prof.items()},
+            "affine_fit_full_run_value": round(float(1.0 / mean_cost), 3),
             "sample": "float32 oracle, 1 sequence, transitions (incl. readout) from a pre-filled state at "
-                      "t=%d: %d in %.1f s on %d BLAS threads, %d in %.1f s on 1 thread"
-                      % (t0, n_all, el_all, threads, n_one, el_one)}
+                      "t=%d: %d in %.1f s on %d BLAS threads, %d in %.1f s on 1 thread; plus one transition "
+                      "at each of t=%s (all threads), fitted as a + b t over t = 1..%d"
+                      % (t0, n_all, el_all, threads, n_one, el_one, ",".join(str(int(t)) for t in ts), wl.T)}
 
 
 def measured_traffic(x_bytes: float):
