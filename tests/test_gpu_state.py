@@ -258,6 +258,38 @@ def test_every_product_shape_bit_identical():
             run.dec.close()
 
 
+def test_one_term_activations_shapes_and_closeness():
+    """The one-term activation mode (launch option one_term: the products'
+    activations as one bf16 value, the kernels' single-term instantiations)
+    at 1, 40 and 128 rows: bit-identical across product shapes, and close to
+    the two-term results (relative L2 of the states and logits within 2e-2
+    after 3 steps: only the activations' rounding differs)."""
+    require_gpu()
+    from stateful_sequence_model_amd import _abi
+    wl = synth.MID.with_(T=24, L=2)
+    raw = synth.make_weights(wl)
+    shapes = [(1, 1, 0, 2, 0), (1, 1, 0, 3, 1), (1, 1, 2, 1, 0), (1, 1, 8, 1, 0), (1, 4, 1, 1, 0), (1, 4, 4, 1, 0)]
+    for B in (1, 40, 128):
+        two = GpuRun(wl, raw=raw, B=B, T=wl.T)
+        two.init()
+        S2, Z2 = two.run(3)
+        two.dec.close()
+        base = GpuRun(wl, raw=raw, B=B, T=wl.T, launch={"one_term": 1})
+        base.init()
+        S, Z = base.run(3)
+        base.dec.close()
+        assert rel_l2(S, S2) < 2e-2 and rel_l2(Z, Z2) < 2e-2, (B, rel_l2(S, S2), rel_l2(Z, Z2))
+        assert not np.array_equal(S, S2)  # the mode is in effect
+        for sh in shapes:
+            run = GpuRun(wl, raw=raw, B=B, T=wl.T, launch={"one_term": 1})
+            _abi.check(_abi.rlt_dbg_product_shape(run.dec.ctx, *sh), "product shape")
+            run.init()
+            S3, Z3 = run.run(3)
+            assert run.dec.sync_error() == 0
+            assert np.array_equal(S3, S) and np.array_equal(Z3, Z), (B, sh)
+            run.dec.close()
+
+
 def test_duplicate_rows_are_refused_on_device():
     """A decoder call naming one state row in two slots would let two
     workgroups update the same row: the library detects it on the device,
