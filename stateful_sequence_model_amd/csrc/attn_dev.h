@@ -351,8 +351,10 @@ __device__ __forceinline__ void xattn_body(const AttnArgs& a, int hg, int ch, in
   merge_groups<T>(acc, G, KPW, s_o, s_ml, [&](int li, int e, float o, float M, float L) {
     const int ljl = li % LPK;
     const int eo = ljl * PE + (e < PE ? e : h + e - PE);  // element of the head
-    if (a.direct) {
-      // the only chunk: what the combine would write for it (weight 2^0 = 1)
+    if (a.direct || t <= a.chunk) {
+      // the row's only chunk (one chunk per launch, or a row whose position
+      // fits the first chunk): what the combine would write for it (weight
+      // 2^0 = 1, the same division); the combine skips such rows
       const int c = (hg * a.hpw + li / LPK) * DH + eo;
       store_op((T*)a.out, a.out_pk ? pk_off(slot, c, d >> 6) : (int64_t)slot * d + c, a.out_lo, o * (1.f / L));
       return;
@@ -370,12 +372,13 @@ __device__ __forceinline__ void xattn_body(const AttnArgs& a, int hg, int ch, in
 // M = max of the chunk maxima, L = sum over chunks in chunk order of
 // l_c 2^(m_c - M), o = the same weights applied to the chunk outputs in chunk
 // order. Up to CU chunks all partials are loaded at once (one memory round
-// trip); more chunks take the same arithmetic in a plain loop.
+// trip); more chunks take the same arithmetic in a plain loop. Rows with a
+// single chunk (t <= chunk) were written by the cross-attention itself.
 template <typename T, int DH>
 __device__ __forceinline__ void xcombine_body(const AttnArgs& a, int head, int slot, int tid, int nt) {
   constexpr int CU = 16, EPT = (DH + 63) / 64;  // chunks loaded at once, elements per thread
   const int t = a.rows.t_row[slot];
-  if (t <= 0) return;
+  if (t <= a.chunk) return;  // no position, or one chunk: written by the cross-attention itself
   const int nc = (t + a.chunk - 1) / a.chunk;
   const float* P = a.part + ((int64_t)slot * a.nch * a.H + head) * (DH + 2);
   const int64_t cs = (int64_t)a.H * (DH + 2);  // chunk stride

@@ -27,7 +27,9 @@
 // Cross-attention (eq. 2.15): keys are memory positions 1..t only; the
 // range is split into chunks of `chunk` positions (boundaries depend on t
 // only), each chunk writes an unnormalised (o, max, sum) partial, and a
-// combine kernel merges the chunks in chunk order.
+// combine kernel merges the chunks in chunk order. A row whose t fits the
+// first chunk gets its normalised output from that chunk directly (what the
+// combine would write); the combine skips it.
 #include "attn_dev.h"
 
 namespace rlt {
