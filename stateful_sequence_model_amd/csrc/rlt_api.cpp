@@ -668,13 +668,14 @@ struct Gemm {
     g.eps = c->cfg.rms_eps;
     if (Wp) {
       // tile shape (none of these choices changes the arithmetic: fixed
-      // stream order, see the kernels), measured per product at 1 and 128
-      // rows, reference depth: calls of more than 64 rows whose products
-      // have at least 64 staged tiles of 128 rows x 64 columns (Q/K/V,
-      // gate/up, vocabulary) take the staged tile (64 x 128 where the
-      // columns allow), in one workgroup per tile from 150 tiles, else
-      // split over two stream groups; the others the register tile of 32
-      // rows, two chunks in flight per wave (three past 32 rows)
+      // stream order, see the kernels), measured per product at 1, 128, 256
+      // and 512 rows, reference depth: calls of more than 64 rows whose
+      // products have at least 96 staged tiles of 128 rows x 64 columns
+      // (64 with K of 4096 or more) take the staged tile (64 x 128 where the
+      // columns allow), in one workgroup per tile from 150 tiles, else split
+      // over two stream groups (four below 96 tiles); the others the
+      // register tile of 32 rows, two chunks in flight per wave (three past
+      // 32 rows)
       g.Wp = Wp;
       g.rb = 1;
       g.cb = 1;
@@ -687,7 +688,7 @@ struct Gemm {
       g.a_lds = (n == 1 && K / 64 <= PK_LDS_CHUNKS) ? 1 : 0;
       if (n > 64 && g.npairs % 2 == 0) {
         const int tiles = g.npairs / 2 * ((n + 127) / 128);  // counted in 128 x 64 tiles
-        if (tiles >= 64) g.lt_groups = tiles >= 150 ? 1 : 2;
+        if (tiles >= 96 || (tiles >= 64 && K >= 4096)) g.lt_groups = tiles >= 150 ? 1 : tiles >= 96 ? 2 : 4;
         while (g.lt_groups > 1 && (size_t)g.lt_groups * g.M_pad * g.Nv > c->partial_cap) g.lt_groups /= 2;
         // tiles of 64 rows x 4 column pairs where the columns allow: the same
         // workgroups move a fifth less through LDS per chunk (measured faster
