@@ -267,12 +267,13 @@ def main():
                     help="also time a plain 4 GiB device copy and read-only sum (achievable HBM rates)")
     ap.add_argument("--launch", action="append", default=[], metavar="FIELD=VALUE",
                     help="launch option of the context (rlt_dbg_launch field, for tuning sweeps)")
-    ap.add_argument("--mode", choices=("step", "memory_prefill", "backward", "replay"), default="step",
+    ap.add_argument("--mode", choices=("step", "memory_prefill", "backward", "replay", "shapes"), default="step",
                     help="step: the decoder transition (default); memory_prefill: token-parallel "
                          "construction of the encoder memory of the whole batch; backward: full-BPTT "
                          "replay backward of the whole batch; replay: current-policy replay from H_0 of "
                          "ragged sequences (default preset ragged_rl_replay, lengths capped by "
-                         "--replay-max-len)")
+                         "--replay-max-len); shapes: the step with each product tile shape forced "
+                         "in turn (rlt_dbg_product_shape), against the library's own choice")
     ap.add_argument("--replay-max-len", type=int, default=1024,
                     help="replay mode: upper end of the uniform length draw (the preset's lower end kept)")
     args = ap.parse_args()
@@ -297,6 +298,8 @@ def main():
         return bench_backward(args, wl)
     if args.mode == "replay":
         return bench_replay(args, wl)
+    if args.mode == "shapes":
+        return bench_shapes(args, wl)
     B, T = wl.B, wl.T
     es = 2 if wl.dtype == "bf16" else 4
     K, Wu = args.steps, args.warmup
@@ -507,6 +510,71 @@ def bench_memory_prefill(args, wl):
                      "frac": round(tflops / peak, 4), "traffic": None,
                      "algorithmic_flops_per_call": flops, "hbm_bytes_min_per_call": int(moved)},
     }), flush=True)
+
+
+# product tile shapes of the sweep: (rb, cb, lt, pf, pre) as rlt_dbg_product_shape
+# takes them; rb = 0 is the library's own choice
+SWEEP_SHAPES = [(0, 1, 0, 2, -1), (1, 1, 0, 2, -1), (1, 1, 0, 3, -1), (1, 2, 0, 2, -1), (2, 1, 0, 2, -1),
+                (1, 2, 1, 1, 0), (1, 2, 2, 1, 0), (1, 2, 4, 1, 0), (1, 2, 8, 1, 0),
+                (1, 4, 1, 1, 0), (1, 4, 2, 1, 0), (1, 4, 4, 1, 0), (1, 4, 8, 1, 0)]
+
+
+def bench_shapes(args, wl):
+    """The decoder step (direct launches, --steps steps after --warmup) with
+    each operand-order product shape forced in turn: ms per step and the
+    products' share (HIP events per launch, rlt_dbg_profile). Run under
+    rocprofv3 --kernel-trace for the per-product durations; the shapes run in
+    the order of SWEEP_SHAPES."""
+    import torch
+    import synth
+    from stateful_sequence_model_amd import Decoder, DecoderState, ModelConfig, _abi
+    B, T = wl.B, wl.T
+    t0 = args.t_center or T // 2
+    K, Wu = args.steps, args.warmup
+    raw = synth.make_weights(wl)
+    cfg = ModelConfig(L=wl.L, d=wl.d, H=wl.H, dh=wl.dh, W=wl.W, G=wl.G, F=wl.F, V=wl.V, dtype=wl.dtype,
+                      merge=wl.merge, alpha=wl.alpha, eps=wl.eps, rope_theta=wl.rope_theta, pos=wl.pos)
+    dec = Decoder(cfg, raw, max_rows=B, max_ctx=T)
+    st = DecoderState(cfg, B)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(wl.seed)
+    tdt = cfg.torch_dtype
+    mk = torch.empty((wl.G, B, T, wl.d), device="cuda", dtype=tdt).normal_(generator=gen)
+    mv = torch.empty_like(mk).normal_(generator=gen)
+    for l in range(wl.L):
+        st.ring("k")[l].normal_(generator=gen)
+        st.ring("v")[l].normal_(generator=gen)
+    e = torch.empty((B, wl.d), device="cuda", dtype=tdt).normal_(generator=gen)
+    mem_len = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    mem = Decoder.memory(mk, mv, mem_len)
+    rows = torch.arange(B, dtype=torch.int32, device="cuda")
+    argmax = torch.empty(B, dtype=torch.int32, device="cuda")
+    res = []
+    for sh in SWEEP_SHAPES:
+        _abi.check(_abi.lib().rlt_dbg_product_shape(dec.ctx, *sh), "rlt_dbg_product_shape")
+        st.s.normal_(generator=gen)
+        st.pos.fill_(max(0, t0 - K // 2 - Wu))
+        st.pending.fill_(-1)
+        for _ in range(Wu):
+            _abi.check(dec.step(st, rows, e, mem, argmax=argmax), "rlt_decoder_step")
+        torch.cuda.synchronize()
+        _abi.check(_abi.rlt_dbg_profile(dec.ctx, 1), "profile")
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(K):
+            _abi.check(dec.step(st, rows, e, mem, argmax=argmax), "rlt_decoder_step")
+        ev1.record()
+        torch.cuda.synchronize()
+        g_ms, g_n = _abi.rlt_dbg_profile_read(dec.ctx, _abi.PROF_NAMES.index("gemm"))
+        _abi.check(_abi.rlt_dbg_profile(dec.ctx, 0), "profile")
+        ms = ev0.elapsed_time(ev1) / K
+        res.append({"rb": sh[0], "cb": sh[1], "lt": sh[2], "pf": sh[3], "pre": sh[4],
+                    "ms_per_step": round(ms, 4), "products_ms_per_step": round(g_ms / K, 4)})
+        log("shape rb=%d cb=%d lt=%d pf=%d pre=%d: %.3f ms/step, products %.3f ms (direct launches)"
+            % (sh + (ms, g_ms / K)))
+    _abi.check(dec.sync_error(), "device error")
+    print(json.dumps({"mode": "shapes", "workload": wl.name, "batch": B, "t": t0, "steps": K,
+                      "warmup": Wu, "shapes": res}), flush=True)
 
 
 def bench_replay(args, wl):
