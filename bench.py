@@ -469,7 +469,8 @@ def bench_memory_prefill(args, wl):
     # group a one-layer context of the same widths suffices
     ctx_wl = wl.with_(L=1) if G == 1 else wl
     ctx_cfg = ModelConfig(**{**cfg.__dict__, "L": ctx_wl.L})
-    dec = Decoder(ctx_cfg, synth.make_weights(ctx_wl), max_rows=128, max_ctx=T)
+    launch = {k: int(v) for k, v in (a.split("=", 1) for a in args.launch)}
+    dec = Decoder(ctx_cfg, synth.make_weights(ctx_wl), max_rows=128, max_ctx=T, launch=launch or None)
     mw = dec.memory_weights(synth.make_memory_weights(wl))
     gen = torch.Generator(device="cuda")
     gen.manual_seed(wl.seed)

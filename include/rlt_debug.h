@@ -51,6 +51,8 @@ typedef struct rlt_dbg_launch {
                            then its rounding remainder): lower precision, for comparisons */
   int32_t replay_graph_min; /* rlt_replay_sequence: runs of at least this many ticks with one
                            active set are captured as a graph and replayed (0: 4; -1: never) */
+  int32_t no_big_tile;  /* 1: the memory construction's K/V product on the 128 x 128 LDS tile
+                           instead of the 256 x 256 one (same summation order, same results) */
 } rlt_dbg_launch;
 
 /* rlt_create with launch options (opt must not be NULL). */

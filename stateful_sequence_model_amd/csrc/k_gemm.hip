@@ -295,6 +295,167 @@ __device__ __forceinline__ void stream_fold(int j, f32x16_t& r, f32x16_t (&st)[f
   }
 }
 
+// Tile for the token-parallel memory construction (calls of at least 256
+// rows whose K/V epilogue stores 16-byte runs, no K split): 256 rows x 256
+// virtual columns per workgroup of 8 waves, K in stages of 64. The operands
+// are staged through two padded LDS buffers as in k_gemm_bf16_tile (register
+// prefetch PF stages ahead); the waves form 2 x 4, each multiplying 128 rows
+// by 64 columns (4 x 2 accumulators of v_mfma_f32_32x32x16_bf16), so a wave
+// reads 6 KB of LDS per 8 MFMAs of a 16-wide step instead of 4 KB per 4 with
+// 64 x 64 wave tiles. The row statistics are loaded after the K loop (their
+// registers are taken by the accumulators) and the output is staged in LDS
+// 128 rows at a time for the epilogue (virtual columns and C layout as in
+// k_gemm_bf16_tile).
+// grid: npairs / 8 * m-tiles (1-D, m-tile fastest within an XCD); block 512.
+__global__ __launch_bounds__(512) void k_gemm_bf16_big(GemmArgs g, Epi<uint16_t> epi) {
+  constexpr int BM = 256, BN = 256, BK = 64, LDR = BK + 8, NT = 512, PF = 2;
+  constexpr int LA = BM * BK / 8 / NT, LW = BN * BK / 8 / NT;  // 16-byte pieces per thread and stage
+  constexpr int HM = BM / 2, LDC = BN + 1;                     // output staged HM rows at a time
+  constexpr int STAGE_BYTES = 2 * (BM + BN) * LDR * 2;
+  static_assert(HM * LDC * 4 <= STAGE_BYTES && rowrstd_lds<BM, NT>() * 4 <= STAGE_BYTES,
+                "the epilogue reuses the operand buffers");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[STAGE_BYTES];
+  uint16_t(*sA)[BM * LDR] = reinterpret_cast<uint16_t(*)[BM * LDR]>(smem);
+  uint16_t(*sW)[BN * LDR] = reinterpret_cast<uint16_t(*)[BN * LDR]>(smem + 2 * BM * LDR * 2);
+  __shared__ float s_rstd[BM];
+  __shared__ int s_t[BM];
+  __shared__ int64_t s_off[BM];
+  const int T = gridDim.x, b = blockIdx.x, per = T >> 3;
+  const int t = b < 8 * per ? (b & 7) * per + (b >> 3) : b;
+  const int nmt = (g.M + BM - 1) / BM;
+  const int mt = t % nmt, grp = t / nmt;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int m0 = mt * BM, pair0 = grp * (BN / 32);
+  const int nst = g.K / BK;
+  // loads: thread covers rows lr + 64 i of the stage (clamped below M, never
+  // stored), 16-byte chunk lc
+  const int lr = tid >> 3, lc = (tid & 7) * 8;
+  const uint16_t* pa[LA];
+#pragma unroll
+  for (int i = 0; i < LA; ++i) {
+    const int m = m0 + lr + 64 * i < g.M ? m0 + lr + 64 * i : g.M - 1;
+    pa[i] = (const uint16_t*)g.A + (int64_t)m * g.lda + lc;
+  }
+  const uint16_t* pw[LW];
+#pragma unroll
+  for (int i = 0; i < LW; ++i) {
+    const int v = lr + 64 * i;  // virtual column of the tile
+    int ba, bb;
+    pair_blocks(g, pair0 + v / 32, ba, bb);
+    pw[i] = weight_row<uint16_t>(g, ((v & 16) ? bb : ba) * 16 + (v & 15)) + lc;
+  }
+  if (tid < BM) {
+    const int m = m0 + tid;
+    s_t[tid] = m < g.M ? epi.a.rows.t_row[m] : 0;
+    s_off[tid] = m < g.M ? (int64_t)epi.a.rows.rows[m] * epi.a.msb + (int64_t)(s_t[tid] - 1) * epi.a.mst : 0;
+  }
+  bf16x8_t ra[PF][LA], rw[PF][LW];
+  auto gload = [&](int p, int st) {
+#pragma unroll
+    for (int i = 0; i < LA; ++i) ra[p][i] = load8(pa[i] + BK * st);
+#pragma unroll
+    for (int i = 0; i < LW; ++i) rw[p][i] = load8(pw[i] + BK * st);
+  };
+  auto lstore = [&](int p, int buf) {
+#pragma unroll
+    for (int i = 0; i < LA; ++i) *(bf16x8_t*)(sA[buf] + (lr + 64 * i) * LDR + lc) = ra[p][i];
+#pragma unroll
+    for (int i = 0; i < LW; ++i) *(bf16x8_t*)(sW[buf] + (lr + 64 * i) * LDR + lc) = rw[p][i];
+  };
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+  const int r32 = lane & 31, kh = (lane >> 5) * 8;
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8_t a[4], w[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = *(const bf16x8_t*)(sA[buf] + (wm * 128 + i * 32 + r32) * LDR + ks * 16 + kh);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) w[j] = *(const bf16x8_t*)(sW[buf] + (wn * 64 + j * 32 + r32) * LDR + ks * 16 + kh);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], w[j], acc[i][j], 0, 0, 0);
+    }
+  };
+  // the schedule of k_gemm_bf16_tile: register slot s % PF holds stage s
+  // until it is written to LDS buffer s % 2; one barrier per stage
+  if (nst > 0) {
+#pragma unroll
+    for (int p = 0; p < PF; ++p) gload(p, min(p, nst - 1));
+    lstore(0, 0);
+    gload(0, min(PF, nst - 1));
+    __syncthreads();
+  }
+  int st = 0;
+  for (; st + PF <= nst; st += PF) {
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      const int cur = st + p;
+      compute(cur & 1);
+      if (cur + 1 < nst) {  // uniform
+        lstore((p + 1) % PF, (cur + 1) & 1);
+        gload((p + 1) % PF, min(cur + 1 + PF, nst - 1));
+      }
+      __syncthreads();
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < PF; ++p) {
+    const int cur = st + p;
+    if (cur < nst) {  // uniform
+      compute(cur & 1);
+      if (cur + 1 < nst) lstore((p + 1) % PF, (cur + 1) & 1);
+      __syncthreads();
+    }
+  }
+  // row statistics (into the free operand buffers), then the output in two
+  // halves of 128 rows: the waves of half h stage their tile, all threads
+  // run the epilogue, 16-byte runs of 8 columns of a pair's two blocks
+  const bool norm_here = g.ssq_in != nullptr;
+  if (norm_here) {  // uniform branch: contains barriers
+    RowRstd<BM, NT> rr(g, m0);
+    rr.finish(g, m0, reinterpret_cast<float*>(smem), s_rstd);
+  }
+  __syncthreads();
+  float* Cs = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (wm == h) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int gq = 0; gq < 16; ++gq)
+            Cs[(i * 32 + 8 * (gq >> 2) + 4 * (lane >> 5) + (gq & 3)) * LDC + wn * 64 + j * 32 + r32] = acc[i][j][gq];
+    }
+    __syncthreads();
+    for (int it = tid; it < HM * (BN / 32) * 2; it += NT) {
+      const int hh = it & 1, rp = it >> 1;
+      const int pl = rp % (BN / 32), rh = rp / (BN / 32), row = h * HM + rh;
+      if (m0 + row >= g.M || s_t[row] <= 0) continue;
+      int ba, bb;
+      pair_blocks(g, pair0 + pl, ba, bb);
+      float va[8], vb[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        va[k] = Cs[rh * LDC + pl * 32 + 8 * hh + k];
+        vb[k] = Cs[rh * LDC + pl * 32 + 16 + 8 * hh + k];
+      }
+      epi.memkv_at8(s_t[row], s_off[row], ba * 16 + 8 * hh, va, bb * 16 + 8 * hh, vb, norm_here ? s_rstd[row] : 1.f);
+    }
+    __syncthreads();
+  }
+}
+
 // Product for calls of up to 64 rows, both operands in fragment order (see
 // pk_off): a workgroup owns 32 RB rows x CB column pairs over the whole K;
 // its 8 waves are the 8 streams, each loading its chunks' fragments straight
@@ -949,6 +1110,11 @@ void launch_gemm(int dtype, const GemmArgs& g0, const EpiArgs& e, hipStream_t s)
     }
   }
   Epi<uint16_t> epi{e};
+  if (g.wide == 256) {  // host checked: M >= 256, K % 64 == 0, no split, K/V epilogue with 16-byte runs
+    dim3 grid(g.npairs / 8 * ((g.M + 255) / 256));
+    hipLaunchKernelGGL(k_gemm_bf16_big, grid, dim3(512), 0, s, g, epi);
+    return;
+  }
   if (g.wide) {
     const int tiles_m = (g.M + 127) / 128;
     dim3 grid(g.npairs / (g.wide / 32) * g.S * tiles_m);

@@ -136,6 +136,7 @@ struct rlt_ctx {
   int *t_row, *ident, *ones, *rows_buf, *src_buf, *split_buf, *last_buf;
   int* tick_dev;        // replay: the current tick, advanced on the device
   int replay_graph_min;  // replay: runs of at least this many ticks of one active set are captured (0: never)
+  bool big_tile;         // the memory construction's K/V product on the 256 x 256 tile
   double* inv_freq;
   float2* rope_tab;  // [rope_tmax + 1][d_head / 2] rotary (cos, sin)
   int rope_tmax;
@@ -582,6 +583,7 @@ static int create_ctx(const rlt_config* cfg, const rlt_weights* w, int32_t max_r
   }
   c->one_term = o.one_term != 0;
   c->replay_graph_min = o.replay_graph_min < 0 ? 0 : (o.replay_graph_min > 0 ? o.replay_graph_min : 4);
+  c->big_tile = o.no_big_tile == 0;
   if (c->pk_ready && !c->one_term) {
     c->lo_X = (int64_t)M * 2 * d;
     c->lo_o = c->lo_h = (int64_t)M * d;
@@ -738,6 +740,11 @@ struct Gemm {
       g.wide = BN;
       g.S = S;
       g.kslice = (kst + S - 1) / S * 64;
+      // the memory construction's K/V product (16-byte runs, no split, at
+      // least 256 rows): tiles of 256 x 256 with 128 x 64 per wave
+      if (BN == 128 && S == 1 && e.kind == EPI_MEMKV && e.mem_vec && g.npairs % 8 == 0 && n >= 256 &&
+          c->big_tile)
+        g.wide = 256;
     } else if (c->dt == 1) {
       narrow_plan(n, g.npairs, K, c->narrow_rows, c->gemm_target, g.M_pad, g.Nv, c->partial_cap, g.S, g.mb,
                   g.kslice);

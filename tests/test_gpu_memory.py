@@ -19,11 +19,11 @@ from tests.helpers import oracle_config, oracle_weights, rel_l2, widen
 pytestmark = pytest.mark.gpu
 
 
-def _setup(wl, B, T_cap):
+def _setup(wl, B, T_cap, launch=None):
     from stateful_sequence_model_amd import Decoder
     raw = synth.make_weights(wl)
     cfg = model_config(wl)
-    dec = Decoder(cfg, raw, max_rows=max(B, 1), max_ctx=T_cap)
+    dec = Decoder(cfg, raw, max_rows=max(B, 1), max_ctx=T_cap, launch=launch)
     mw_raw = synth.make_memory_weights(wl)
     mw = dec.memory_weights(mw_raw)
     tdt = cfg.torch_dtype
@@ -277,3 +277,30 @@ def test_prefill_reference_width_and_decoder_on_it():
             ost = orc.transition(ost, widen(E[b, t - 1]), omem)
             assert rel_l2(S[t - 1][j], ost.s) < 2e-2, (b, t)
             assert rel_l2(Z[t - 1][j], orc.logits(ost.s)) < 2e-2, (b, t)
+
+
+def test_prefill_big_tile_equals_lds_tile():
+    """Reference width (d = 2048, 16 x 128 heads), 2,333 entries (nine full
+    256-row tiles and a ragged tenth): the K/V product on the 256 x 256 tile
+    writes exactly the entries of the 128 x 128 tile (launch option
+    no_big_tile): both add every entry's products in the same order (K in
+    stages of 64, 16-wide MFMA steps in order, one accumulator per 32 x 32
+    block), and a few of them match the oracle."""
+    require_gpu()
+    wl = synth.REF.with_(L=2)
+    B, T_cap = 3, 1500
+    lens = np.array([1500, 700, 133], dtype=np.int32)
+    out = []
+    for launch in (None, {"no_big_tile": 1}):
+        dec, mw, mw_raw, K, V, mem_len, mem, _ = _setup(wl, B, T_cap, launch=launch)
+        E = synth.make_e(wl, 0, B, T_cap)
+        Ed = torch.from_numpy(E.view(np.int16)).cuda().view(torch.bfloat16)
+        assert dec.memory_prefill(mw, mem, T_cap, lens, Ed) == 0
+        torch.cuda.synchronize()
+        assert dec.sync_error() == 0
+        assert mem_len.cpu().tolist() == lens.tolist()
+        out.append((K.clone(), V.clone()))
+        if launch is None:
+            _check_entries(wl, K, V, mw_raw, E, [(0, 1), (0, 1500), (1, 700), (2, 1), (2, 133)], 1e-2)
+        dec.close()
+    assert torch.equal(out[0][0], out[1][0]) and torch.equal(out[0][1], out[1][1])
