@@ -298,8 +298,9 @@ __device__ __forceinline__ void stream_fold(int j, f32x16_t& r, f32x16_t (&st)[f
 // Tile for the token-parallel memory construction (calls of at least 256
 // rows whose K/V epilogue stores 16-byte runs, no K split): 256 rows x 256
 // virtual columns per workgroup of 8 waves, K in stages of 64. The operands
-// are staged through two padded LDS buffers as in k_gemm_bf16_tile (register
-// prefetch PF stages ahead); the waves form 2 x 4, each multiplying 128 rows
+// are staged through two padded LDS buffers as in k_gemm_bf16_tile (each
+// stage's loads issued one stage ahead, its LDS writes before the MFMAs of
+// the stage before it); the waves form 2 x 4, each multiplying 128 rows
 // by 64 columns (4 x 2 accumulators of v_mfma_f32_32x32x16_bf16), so a wave
 // reads 6 KB of LDS per 8 MFMAs of a 16-wide step instead of 4 KB per 4 with
 // 64 x 64 wave tiles. The row statistics are loaded after the K loop (their
@@ -308,7 +309,7 @@ __device__ __forceinline__ void stream_fold(int j, f32x16_t& r, f32x16_t (&st)[f
 // k_gemm_bf16_tile).
 // grid: npairs / 8 * m-tiles (1-D, m-tile fastest within an XCD); block 512.
 __global__ __launch_bounds__(512) void k_gemm_bf16_big(GemmArgs g, Epi<uint16_t> epi) {
-  constexpr int BM = 256, BN = 256, BK = 64, LDR = BK + 8, NT = 512, PF = 2;
+  constexpr int BM = 256, BN = 256, BK = 64, LDR = BK + 8, NT = 512, PF = 1;
   constexpr int LA = BM * BK / 8 / NT, LW = BN * BK / 8 / NT;  // 16-byte pieces per thread and stage
   constexpr int HM = BM / 2, LDC = BN + 1;                     // output staged HM rows at a time
   constexpr int STAGE_BYTES = 2 * (BM + BN) * LDR * 2;
@@ -394,16 +395,20 @@ __global__ __launch_bounds__(512) void k_gemm_bf16_big(GemmArgs g, Epi<uint16_t>
     gload(0, min(PF, nst - 1));
     __syncthreads();
   }
+  // The next stage's LDS writes and the refill loads are issued before the
+  // current stage's MFMAs (buffer (cur + 1) % 2 was last read before the
+  // previous barrier; the refill's register slot was just written out), so
+  // that they proceed under the MFMA chain.
   int st = 0;
   for (; st + PF <= nst; st += PF) {
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
       const int cur = st + p;
-      compute(cur & 1);
       if (cur + 1 < nst) {  // uniform
         lstore((p + 1) % PF, (cur + 1) & 1);
         gload((p + 1) % PF, min(cur + 1 + PF, nst - 1));
       }
+      compute(cur & 1);
       __syncthreads();
     }
   }
@@ -411,8 +416,8 @@ __global__ __launch_bounds__(512) void k_gemm_bf16_big(GemmArgs g, Epi<uint16_t>
   for (int p = 0; p < PF; ++p) {
     const int cur = st + p;
     if (cur < nst) {  // uniform
-      compute(cur & 1);
       if (cur + 1 < nst) lstore((p + 1) % PF, (cur + 1) & 1);
+      compute(cur & 1);
       __syncthreads();
     }
   }
