@@ -53,10 +53,6 @@ typedef struct rlt_dbg_launch {
                            active set are captured as a graph and replayed (0: 4; -1: never) */
   int32_t no_big_tile;  /* 1: the memory construction's K/V product on the 128 x 128 LDS tile
                            instead of the 256 x 256 one (same summation order, same results) */
-  int32_t split_rows;   /* bf16 with operand-order weights: decoder-step and replay calls of at
-                           least this many rows (>= 2) run their transition as two halves of the
-                           rows, the second on a stream of the context's own, joined before the
-                           call's last kernel (0 or less: never; results unchanged) */
 } rlt_dbg_launch;
 
 /* rlt_create with launch options (opt must not be NULL). */

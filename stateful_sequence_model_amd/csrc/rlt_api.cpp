@@ -140,14 +140,7 @@ struct rlt_ctx {
   double* inv_freq;
   float2* rope_tab;  // [rope_tmax + 1][d_head / 2] rotary (cos, sin)
   int rope_tmax;
-  // calls of at least split_rows rows run their transition as two halves of
-  // rows, the second on stream s2 with workspace ws[1] (0: never); the
-  // halves' kernels overlap, and every row's result is the one it gets in
-  // any other call (fixed summation orders per row)
-  int split_rows;
-  hipStream_t s2;
-  hipEvent_t ev_fork, ev_join;
-  Workspace ws[2];
+  Workspace ws[1];
   // pinned host staging for replay schedules
   int* host_stage;
   // error word: host-mapped pinned memory written by kernels
@@ -304,9 +297,6 @@ extern "C" void rlt_destroy(rlt_ctx* c) {
   for (auto& e : c->fused_cache) (void)hipFree(e.dev);
   if (c->graph_exec) (void)hipGraphExecDestroy(c->graph_exec);
   if (c->graph) (void)hipGraphDestroy(c->graph);
-  if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
-  if (c->ev_join) (void)hipEventDestroy(c->ev_join);
-  if (c->s2) (void)hipStreamDestroy(c->s2);
   if (c->claim) (void)hipFree(c->claim);
   if (c->err_host) (void)hipHostFree(c->err_host);
   if (c->host_stage) (void)hipHostFree(c->host_stage);
@@ -594,22 +584,6 @@ static int create_ctx(const rlt_config* cfg, const rlt_weights* w, int32_t max_r
   c->one_term = o.one_term != 0;
   c->replay_graph_min = o.replay_graph_min < 0 ? 0 : (o.replay_graph_min > 0 ? o.replay_graph_min : 4);
   c->big_tile = o.no_big_tile == 0;
-  // two row halves on two streams (operand-order products only; the
-  // persistent step's calls are not split)
-  c->split_rows = o.split_rows > 0 ? std::max(2, (int)o.split_rows) : 0;
-  if (c->split_rows > 0 && (!c->pk_ready || c->split_rows > max_rows)) c->split_rows = 0;
-  if (c->split_rows > 0) {
-    if ((rc = alloc_workspace(c, c->ws[1], true))) {
-      rlt_destroy(c);
-      return rc;
-    }
-    if (hipStreamCreateWithFlags(&c->s2, hipStreamNonBlocking) != hipSuccess ||
-        hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming) != hipSuccess) {
-      rlt_destroy(c);
-      return fail(RLT_EHIP, "second stream creation failed");
-    }
-  }
   if (c->pk_ready && !c->one_term) {
     c->lo_X = (int64_t)M * 2 * d;
     c->lo_o = c->lo_h = (int64_t)M * d;
@@ -799,22 +773,8 @@ struct StepPlan {
   bool do_readout;
 };
 
-// Launch units of a transition: 0 = merge; per block l, 5 units from
-// 1 + 5 l in the block's sublayer order (SWA and FFN one unit each, the
-// cross-attention three: query product, attention (+ combine), output
-// product); 1 + 5 L = final norm, logits and readout.
-int xattn_unit(const rlt_config& cf, int l) {
-  static const int kOrders[6][3] = {{0, 1, 2}, {0, 2, 1}, {1, 0, 2}, {1, 2, 0}, {2, 0, 1}, {2, 1, 0}};
-  const int* order = kOrders[cf.block_order];
-  int u = 1 + 5 * l;
-  for (int i = 0; order[i] != 1; ++i) u += 1;
-  return u + 1;
-}
-
-// the transition for the plan's slots: merge, L_D blocks, final norm,
-// readout; only units u0 .. u1 - 1 are launched
-void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipStream_t s, int u0 = 0,
-                        int u1 = 1 << 30) {
+// the transition for the plan's slots: merge, L_D blocks, final norm, readout
+void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipStream_t s) {
   const rlt_config& cf = c->cfg;
   const int d = cf.d_model, F = cf.d_ffn, H = cf.n_heads, dh = cf.d_head, L = cf.n_layers;
   const int n = P.n;
@@ -884,7 +844,7 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
   m.lo = lo_X;
   m.lo2 = lo_o;
   m.claim = P.claim;
-  auto in = [&](int u) { return u >= u0 && u < u1; };
+  { Prof pf(c, RLT_PROF_NORM, s); launch_merge_prep(c->dt, m, s); }
   auto mw = [&](void* p) -> const void* { return pk ? p : nullptr; };
   auto producer = [&](EpiArgs e, const float* gnext) {
     e.gnext = gnext;
@@ -892,8 +852,6 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
     return e;
   };
   const float* g_first = gain_of(0, order[0]);
-  if (in(0)) {
-  { Prof pf(c, RLT_PROF_NORM, s); launch_merge_prep(c->dt, m, s); }
   if (cf.merge_kind == RLT_MERGE_GATED) {
     EpiArgs e = E0;
     if (!scalar_gate) {
@@ -937,7 +895,6 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
     gm.run(w.X, 2 * d, {c->merge_wg}, d, 2 * d, PAIR_PLAIN, n, producer(e, g_first), nullptr, w.ssq,
            mw(c->pk_mwg), lo_X);
   }
-  }  // unit 0
 
   AttnArgs at{};
   at.rows = P.R;
@@ -981,8 +938,8 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
     gm.run(w.o, d, {c->wo[l]}, d, d, PAIR_PLAIN, n, producer(e, gnext), nullptr, w.ssq, pw(c->pk_wo, l), lo_o);
   };
   // ---- cross-attention sublayer [eq. (2.15)]: RMSNorm_M folded into the query ----
-  auto cross = [&](int l, const float* gnext, int u) {
-    if (in(u)) {
+  auto cross = [&](int l, const float* gnext) {
+    {
       EpiArgs e = E0;
       e.kind = EPI_QROT;
       e.out_f = w.qm;
@@ -994,14 +951,11 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
     at.mv = (const char*)P.mem.v + (size_t)g * P.mem.stride_g * es;
     at.out = w.o;
     at.hpw = c->hpw_x;
-    if (in(u + 1)) {
-      { Prof pf(c, RLT_PROF_XATTN, s); launch_xattn(c->dt, at, s); }
-      if (!at.direct) {
-        Prof pf(c, RLT_PROF_XCOMBINE, s);
-        launch_xcombine(c->dt, at, s);
-      }
+    { Prof pf(c, RLT_PROF_XATTN, s); launch_xattn(c->dt, at, s); }
+    if (!at.direct) {
+      Prof pf(c, RLT_PROF_XCOMBINE, s);
+      launch_xcombine(c->dt, at, s);
     }
-    if (!in(u + 2)) return;
     EpiArgs e = E0;
     e.kind = EPI_RESID;
     e.out_f = w.z;
@@ -1023,26 +977,17 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
     gm.run(w.act, F, {c->w_down[l]}, d, F, PAIR_PLAIN, n, producer(e, gnext), nullptr, w.ssq, pw(c->pk_down, l),
            lo_act);
   };
-  for (int l = 0, u = 1; l < L; ++l) {
+  for (int l = 0; l < L; ++l) {
     for (int i = 0; i < 3; ++i) {
       // the producer of this sublayer folds the gain of the next norm: the
       // next sublayer's, the next block's first, or RMSNorm_o
       const float* gnext = i + 1 < 3 ? gain_of(l, order[i + 1]) : gain_of(l + 1, order[0]);
-      if (order[i] == 0) {
-        if (in(u)) swa(l, gnext);
-        u += 1;
-      } else if (order[i] == 1) {
-        cross(l, gnext, u);
-        u += 3;
-      } else {
-        if (in(u)) ffn(l, gnext);
-        u += 1;
-      }
+      if (order[i] == 0) swa(l, gnext);
+      else if (order[i] == 1) cross(l, gnext);
+      else ffn(l, gnext);
     }
-    if (P.z_trace && in(u - 1))
-      launch_copy_f32(w.z, P.z_trace + (size_t)l * P.z_trace_ld * d, (int64_t)n * d, s);
+    if (P.z_trace) launch_copy_f32(w.z, P.z_trace + (size_t)l * P.z_trace_ld * d, (int64_t)n * d, s);
   }
-  if (!in(1 + 5 * L)) return;
   // ---- s_t write-back [eq. (2.5)] ----
   m.z = w.z;
   m.s_out = P.s_out;
@@ -1127,55 +1072,6 @@ void enqueue_rows(rlt_ctx* c, const StepPlan& P, hipStream_t s, bool allow_fused
       }
       return;
     }
-  }
-  if (c->split_rows > 0 && n >= c->split_rows && !(c->fused_rows > 0 && n <= c->fused_rows)) {
-    // first half: whole 32-row tiles where possible
-    const int na = std::min(n - 1, std::max(1, (n / 2 + 31) / 32 * 32));
-    StepPlan A = P, B = P;
-    A.n = A.R.n = A.ro.n = A.ro.rows.n = na;
-    const int nb = n - na;
-    B.n = nb;
-    B.R = Rows{P.R.rows + na, P.R.src + na, P.R.t_row + na, nb};
-    B.ro.rows = B.R;
-    B.ro.n = nb;
-    // outputs located by slot move with the half (by sequence: unchanged)
-    const int d = c->cfg.d_model, V = c->cfg.vocab;
-    if (B.s_out) B.s_out += (size_t)na * d;
-    if (B.z_trace) B.z_trace += (size_t)na * d;
-    if (B.logits) B.logits += (size_t)na * V;
-    if (B.ro.argmax) B.ro.argmax += na;
-    if (B.ro.uniform) B.ro.uniform += na;
-    if (B.ro.sample_tok) B.ro.sample_tok += na;
-    if (B.ro.sample_logmu) B.ro.sample_logmu += na;
-    if (B.ro.mode == 0) {
-      if (B.ro.score_tok) B.ro.score_tok += na;
-      if (B.ro.logp) B.ro.logp += na;
-    }
-    // The halves' cross-attention launches alternate (A's of block l, then
-    // B's, then A's of block l + 1, ...), so that each half's products and
-    // SWA run under the other half's cross-attention stream instead of
-    // beside it. (Errors of the event calls surface through the launches'
-    // own checks.)
-    hipStream_t s2 = c->s2;
-    const int L = c->cfg.n_layers;
-    (void)hipEventRecord(c->ev_fork, s);
-    (void)hipStreamWaitEvent(s2, c->ev_fork, 0);
-    enqueue_transition(c, c->ws[0], A, s, 0, xattn_unit(c->cfg, 0));
-    enqueue_transition(c, c->ws[1], B, s2, 0, xattn_unit(c->cfg, 0));
-    for (int l = 0; l < L; ++l) {
-      const int ux = xattn_unit(c->cfg, l), next = l + 1 < L ? xattn_unit(c->cfg, l + 1) : 2 + 5 * L;
-      if (l > 0) (void)hipStreamWaitEvent(s, c->ev_join, 0);
-      enqueue_transition(c, c->ws[0], A, s, ux, ux + 1);
-      (void)hipEventRecord(c->ev_fork, s);
-      (void)hipStreamWaitEvent(s2, c->ev_fork, 0);
-      enqueue_transition(c, c->ws[1], B, s2, ux, ux + 1);
-      (void)hipEventRecord(c->ev_join, s2);
-      enqueue_transition(c, c->ws[0], A, s, ux + 1, next);
-      enqueue_transition(c, c->ws[1], B, s2, ux + 1, next);
-    }
-    (void)hipEventRecord(c->ev_join, s2);
-    (void)hipStreamWaitEvent(s, c->ev_join, 0);
-    return;
   }
   enqueue_transition(c, c->ws[0], P, s);
 }

@@ -258,76 +258,6 @@ def test_every_product_shape_bit_identical():
             run.dec.close()
 
 
-def _all_outputs(run, idx, t, graph=False, stream=None):
-    """One step of rows idx at position t with every per-slot output
-    requested; returns them as CPU tensors (floats viewed as int32)."""
-    n, d, V = len(idx), run.wl.d, run.wl.V
-    o = dict(s_out=torch.empty((n, d), device="cuda"), logits=torch.empty((n, V), device="cuda"),
-             argmax=torch.empty(n, dtype=torch.int32, device="cuda"),
-             sample_tok=torch.empty(n, dtype=torch.int32, device="cuda"),
-             sample_logmu=torch.empty(n, device="cuda"), logp=torch.empty(n, device="cuda"),
-             z_trace=torch.empty((run.wl.L, n, d), device="cuda"))
-    u = torch.from_numpy(synth.uniform01(run.wl.seed, "u", n, start=t * n)).cuda()
-    score = torch.from_numpy(synth.uniform_int(run.wl.seed, "score", n, 0, V - 1, start=t * n)).cuda()
-    assert run.step(idx, t, uniform=u, temperature=0.7, top_k=50, score_tok=score, graph=graph, stream=stream,
-                    **o) == 0
-    torch.cuda.synchronize()
-    return {k: (v.view(torch.int32) if v.is_floating_point() else v).cpu() for k, v in o.items()}
-
-
-def test_two_stream_row_halves_bit_identical():
-    """Calls split into two halves of their rows, the second half on a
-    stream of the context's own (launch option split_rows), give states,
-    logits, argmax, samples, behaviour and scoring log-probs, layer traces
-    and replay results bit-identical to the unsplit calls (each row's
-    arithmetic does not depend on the call it is in), for direct launches
-    and the captured step, at 7, 40 and 128 rows (halves 6+1, 32+8, 64+64)."""
-    require_gpu()
-    wl = synth.MID.with_(T=24, L=2)
-    raw = synth.make_weights(wl)
-    for B in (7, 40, 128):
-        runs = [GpuRun(wl, raw=raw, B=B, T=wl.T, launch=lc) for lc in (None, {"split_rows": 2})]
-        for r in runs:
-            r.init()
-        idx = list(range(B))
-        stream = torch.cuda.Stream()
-        with torch.cuda.stream(stream):
-            for t in range(1, 5):
-                outs = [_all_outputs(r, idx, t, graph=(t >= 3), stream=stream.cuda_stream) for r in runs]
-                for k in outs[0]:
-                    assert torch.equal(outs[0][k], outs[1][k]), (B, t, k)
-        assert torch.equal(runs[0].st.s, runs[1].st.s) and torch.equal(runs[0].st.pos, runs[1].st.pos)
-        for r in runs:
-            assert r.dec.sync_error() == 0
-            r.dec.close()
-    # ragged replay (active sets of 40 down to 1 rows: split and unsplit ticks)
-    B, T = 40, 24
-    lens = np.array([24 - (i % 23) for i in range(B)], dtype=np.int32)
-    splits = np.ones(B, dtype=np.int32)
-    res = []
-    for lc in ({"replay_graph_min": -1}, {"replay_graph_min": -1, "split_rows": 2}, {"split_rows": 2}):
-        run = GpuRun(wl, raw=raw, B=B, T=T, launch=lc)
-        tokens = torch.from_numpy(synth.make_tokens(wl, 0, B, T)).cuda()
-        logp = torch.full((B, T), float("nan"), device="cuda")
-        s_trace = torch.zeros((B, T, wl.d), device="cuda")
-        run.st.ring_k.zero_()
-        run.st.ring_v.zero_()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            assert run.dec.replay(run.st, lens, splits, run.Ed, run.mem, tokens, logp, s_trace=s_trace,
-                                  stream=side.cuda_stream) == 0
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        assert run.dec.sync_error() == 0
-        res.append([logp.cpu().view(torch.int32), s_trace.cpu().view(torch.int32), run.st.s.cpu().view(torch.int32),
-                    run.st.ring("k").cpu()])
-        run.dec.close()
-    for other in res[1:]:
-        for a, b in zip(res[0], other):
-            assert torch.equal(a, b)
-
-
 def test_one_term_activations_shapes_and_closeness():
     """The one-term activation mode (launch option one_term: the products'
     activations as one bf16 value, the kernels' single-term instantiations)
