@@ -53,6 +53,13 @@ typedef struct rlt_dbg_launch {
                            active set are captured as a graph and replayed (0: 4; -1: never) */
   int32_t no_big_tile;  /* 1: the memory construction's K/V product on the 128 x 128 LDS tile
                            instead of the 256 x 256 one (same summation order, same results) */
+  int32_t xattn_combine_kernel; /* where several cross-attention chunks of a row are merged
+                           (same results): 0 by call size (inside the cross-attention launch, by
+                           the last of the row's chunk workgroups, for calls of at most 256
+                           workgroups; else a separate combine kernel), 1 always the combine
+                           kernel, 2 always inside the launch */
+  int32_t one_row_pf;   /* weight chunks in flight per wave in one-row products, 2 .. 4
+                           (other values: the default; timing only, same results) */
 } rlt_dbg_launch;
 
 /* rlt_create with launch options (opt must not be NULL). */

@@ -322,7 +322,15 @@ __device__ __forceinline__ void swa_body(const AttnArgs& a, int hg, int slot, fl
   }
 }
 
-// cross-attention partial of (head group hg, chunk ch, slot); block 256
+template <typename T, int DH>
+__device__ __forceinline__ void xcombine_body(const AttnArgs& a, int head, int slot, int tid, int nt);
+
+// cross-attention partial of (head group hg, chunk ch, slot); block 256.
+// With a.cnt set, the chunks of a (row, head group) are also combined in
+// this launch: each workgroup publishes its partial and counts itself in
+// a.cnt[slot][hg]; the one that arrives last resets the counter and merges
+// every chunk's partial (the combine kernel's arithmetic, in chunk order, so
+// the result does not depend on which workgroup is last).
 template <typename T, int DH>
 __device__ __forceinline__ void xattn_body(const AttnArgs& a, int hg, int ch, int slot, float* lds) {
   using LV = LaneVec<T>;
@@ -366,6 +374,29 @@ __device__ __forceinline__ void xattn_body(const AttnArgs& a, int hg, int ch, in
       P[DH + 1] = L;
     }
   });
+  if (a.cnt == nullptr || a.direct || t <= a.chunk) return;  // uniform in the workgroup
+  __shared__ int s_last;
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have reached the cache hierarchy
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // publish the workgroup's partial
+    int* cp = a.cnt + (int64_t)slot * (a.H / a.hpw) + hg;
+    const int nc = (t + a.chunk - 1) / a.chunk;
+    const int last = __hip_atomic_fetch_add(cp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nc - 1;
+    if (last) {
+      __hip_atomic_store(cp, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next launch
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every chunk's partial is visible
+    }
+    s_last = last;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  const int ntp = 256 / a.hpw;
+  if (ntp >= 64) {
+    xcombine_body<T, DH>(a, hg * a.hpw + (int)threadIdx.x / ntp, slot, (int)threadIdx.x % ntp, ntp);
+  } else {
+    for (int hh = 0; hh < a.hpw; ++hh) xcombine_body<T, DH>(a, hg * a.hpw + hh, slot, threadIdx.x, 256);
+  }
 }
 
 // chunk combine of (head, slot) by `nt` (>= 64) threads with index `tid`:

@@ -26,8 +26,10 @@
 // those columns of this row).
 // Cross-attention (eq. 2.15): keys are memory positions 1..t only; the
 // range is split into chunks of `chunk` positions (boundaries depend on t
-// only), each chunk writes an unnormalised (o, max, sum) partial, and a
-// combine kernel merges the chunks in chunk order. A row whose t fits the
+// only), each chunk writes an unnormalised (o, max, sum) partial, and the
+// chunks are merged in chunk order, by the last of a row's chunk workgroups
+// to finish (arrival counter per row and head group) or by a combine kernel
+// (the persistent step's phase list, or on request). A row whose t fits the
 // first chunk gets its normalised output from that chunk directly (what the
 // combine would write); the combine skips it.
 #include "attn_dev.h"
@@ -101,6 +103,7 @@ void launch_xattn(int dtype, const AttnArgs& a, hipStream_t s) {
     p.gy = a.rows.n;
     p.gz = a.nch;
     p.u.at = a;
+    p.u.at.cnt = nullptr;  // the persistent step runs the combine as a phase of its own
     if (record_phase(p)) return;
   }
   if (dtype == 0) { RLT_DISPATCH_DH(xattn_t, float, a, s); }
@@ -116,6 +119,7 @@ void launch_xcombine(int dtype, const AttnArgs& a, hipStream_t s) {
     p.u.at = a;
     if (record_phase(p)) return;
   }
+  if (a.cnt) return;  // merged by the cross-attention launch
   if (dtype == 0) { RLT_DISPATCH_DH(xcomb_t, float, a, s); }
   else { RLT_DISPATCH_DH(xcomb_t, uint16_t, a, s); }
 }

@@ -1068,8 +1068,16 @@ void launch_gemm(int dtype, const GemmArgs& g0, const EpiArgs& e, hipStream_t s)
   } while (0)
 #define RLT_PK2(RB_, CB_, PF_, PRE_) RLT_PK3(RB_, CB_, PF_, PRE_, 0)
     if (g.a_lds == 1 && g.M == 1 && (g.K >> 6) <= PK_LDS_CHUNKS) {  // one row: activations in LDS
-      if (pre) RLT_PK3(1, 1, 2, true, 1);
-      else RLT_PK3(1, 1, 2, false, 1);
+      if (g.pf == 4) {
+        if (pre) RLT_PK3(1, 1, 4, true, 1);
+        else RLT_PK3(1, 1, 4, false, 1);
+      } else if (g.pf == 3) {
+        if (pre) RLT_PK3(1, 1, 3, true, 1);
+        else RLT_PK3(1, 1, 3, false, 1);
+      } else {
+        if (pre) RLT_PK3(1, 1, 2, true, 1);
+        else RLT_PK3(1, 1, 2, false, 1);
+      }
       return;
     }
 #define RLT_PK(RB_, CB_, PF_)              \

@@ -69,6 +69,7 @@ struct Workspace {
   void *X, *kc, *vc, *o, *h, *act;
   float *gbuf, *z, *q, *qm, *part, *partial, *logits;
   float* ssq;  // [d/2][M_pad] partial sums of squares of z (folded RMSNorm)
+  int* xcnt;   // [M_pad][n_heads] cross-attention chunk arrival counters (zero between launches)
 };
 
 
@@ -88,6 +89,8 @@ struct rlt_ctx {
   // create from the config and the capacities; see the note at the top)
   int max_rows, max_ctx, M_pad;
   int chunk, nch;      // cross-attention positions per partial, partial slots per row
+  int xcomb_mode;      // cross-attention chunks merged: 0 by call size, 1 combine kernel, 2 in the launch
+  int one_row_pf;      // weight chunks in flight per wave of one-row products
   int hpw, hpw_x;      // attention heads per workgroup: SWA, cross-attention
   int narrow_rows;     // row count whose K splits the narrow product tile uses
   int gemm_target;     // K split target of the persistent step's products (0: stand-alone kernels)
@@ -284,7 +287,8 @@ extern "C" void rlt_destroy(rlt_ctx* c) {
   std::vector<void*> ptrs = {c->t_row, c->ident, c->ones, c->rows_buf, c->src_buf, c->split_buf, c->last_buf,
                              c->tick_dev, c->inv_freq, c->rope_tab};
   for (Workspace& w : c->ws) {
-    void* p[] = {w.X, w.kc, w.vc, w.o, w.h, w.act, w.gbuf, w.z, w.q, w.qm, w.part, w.partial, w.logits, w.ssq};
+    void* p[] = {w.X, w.kc, w.vc, w.o, w.h, w.act, w.gbuf, w.z, w.q, w.qm, w.part, w.partial, w.logits, w.ssq,
+                 w.xcnt};
     ptrs.insert(ptrs.end(), std::begin(p), std::end(p));
   }
   for (void* p : ptrs)
@@ -317,12 +321,14 @@ static int alloc_workspace(rlt_ctx* c, Workspace& w, bool full) {
       (rc = dev_alloc(&w.part, M * (size_t)c->nch * cf.n_heads * (cf.d_head + 2) * 4)) ||
       (rc = dev_alloc(&w.partial, c->partial_cap * 4)) ||
       (rc = dev_alloc(&w.logits, (full ? M : 16) * (size_t)cf.vocab * 4)) ||
-      (rc = dev_alloc(&w.ssq, M * (size_t)(d / 2) * 4)))
+      (rc = dev_alloc(&w.ssq, M * (size_t)(d / 2) * 4)) ||
+      (rc = dev_alloc(&w.xcnt, M * (size_t)cf.n_heads * 4)))
     return rc;
   // rows beyond a call's n are read by the MFMA tiles and discarded: keep
   // them finite
   if (hipMemset(w.X, 0, nt * M * 2 * d * es) != hipSuccess || hipMemset(w.o, 0, nt * M * d * es) != hipSuccess ||
-      hipMemset(w.h, 0, nt * M * d * es) != hipSuccess || hipMemset(w.act, 0, nt * M * F * es) != hipSuccess)
+      hipMemset(w.h, 0, nt * M * d * es) != hipSuccess || hipMemset(w.act, 0, nt * M * F * es) != hipSuccess ||
+      hipMemset(w.xcnt, 0, M * (size_t)cf.n_heads * 4) != hipSuccess)
     return fail(RLT_EHIP, "workspace initialisation failed");
   return RLT_OK;
 }
@@ -584,6 +590,8 @@ static int create_ctx(const rlt_config* cfg, const rlt_weights* w, int32_t max_r
   c->one_term = o.one_term != 0;
   c->replay_graph_min = o.replay_graph_min < 0 ? 0 : (o.replay_graph_min > 0 ? o.replay_graph_min : 4);
   c->big_tile = o.no_big_tile == 0;
+  c->xcomb_mode = (o.xattn_combine_kernel >= 0 && o.xattn_combine_kernel <= 2) ? o.xattn_combine_kernel : 0;
+  c->one_row_pf = (o.one_row_pf >= 2 && o.one_row_pf <= 4) ? o.one_row_pf : 2;
   if (c->pk_ready && !c->one_term) {
     c->lo_X = (int64_t)M * 2 * d;
     c->lo_o = c->lo_h = (int64_t)M * d;
@@ -688,6 +696,7 @@ struct Gemm {
       // one-row calls: activations staged in LDS (the K loop then issues
       // weight loads only; at 4 and 8 rows measured slower)
       g.a_lds = (n == 1 && K / 64 <= PK_LDS_CHUNKS) ? 1 : 0;
+      if (g.a_lds) g.pf = c->one_row_pf;
       if (n > 64 && g.npairs % 2 == 0) {
         const int tiles = g.npairs / 2 * ((n + 127) / 128);  // counted in 128 x 64 tiles
         if (tiles >= 96 || (tiles >= 64 && K >= 4096)) g.lt_groups = tiles >= 150 ? 1 : tiles >= 96 ? 2 : 4;
@@ -907,6 +916,15 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
   at.nch = c->nch;
   at.direct = at.nch == 1 ? 1 : 0;
   at.part = w.part;
+  // chunks merged inside the cross-attention launch (no combine launch) for
+  // calls of at most 256 workgroups: each workgroup that writes a partial
+  // then pays a device-scope release (an L2 write-back), which costs more
+  // than the combine launch it saves once many workgroups write partials
+  // (reference depth, batch 1: t ~ 40 3.74 -> 3.66 ms per step, t ~ 2048
+  // 4.19 -> 4.13; 8 rows: t ~ 40 4.03 -> 3.97, but t ~ 2048 5.30 -> 6.07)
+  const bool in_launch = c->xcomb_mode == 2 ||
+                         (c->xcomb_mode == 0 && (int64_t)n * (H / c->hpw_x) * c->nch <= 256);
+  at.cnt = in_launch ? w.xcnt : nullptr;
   at.out_pk = pk ? 1 : 0;
   at.out_lo = lo_o;
   at.sb = P.mem.stride_b;

@@ -376,6 +376,8 @@ struct AttnArgs {
   int out_pk;               // bf16: out in fragment order (the next product's operand)
   int64_t out_lo;           // fragment-order out: elements to its second term (0: one term)
   int direct;               // cross-attention with one chunk: the normalised output, no combine
+  int* cnt;                 // [n][H / hpw] arrival counters, zero between launches: chunks combined
+                            // by the cross-attention launch itself (null: by the combine kernel)
 };
 
 void launch_gemm(int dtype, const GemmArgs& g, const EpiArgs& e, hipStream_t s);

@@ -256,6 +256,14 @@ def test_every_product_shape_bit_identical():
             assert run.dec.sync_error() == 0
             assert np.array_equal(S2, S) and np.array_equal(Z2, Z), (B, sh)
             run.dec.close()
+        if B == 1:  # the one-row tile with 3 and 4 weight chunks in flight
+            for pf in (3, 4):
+                run = GpuRun(wl, raw=raw, B=B, T=wl.T, launch={"one_row_pf": pf})
+                run.init()
+                S2, Z2 = run.run(3)
+                assert run.dec.sync_error() == 0
+                assert np.array_equal(S2, S) and np.array_equal(Z2, Z), (B, "one_row_pf", pf)
+                run.dec.close()
 
 
 def test_one_term_activations_shapes_and_closeness():
@@ -540,13 +548,16 @@ def _persistent_vs_separate(wl, ref, fz, nsteps=10):
 def test_cross_attention_many_chunks(dtype):
     """Cross-attention split into 16-position chunks up to t = 300 (up to 19
     chunks per row: the combine's all-at-once path for <= 16 chunks and its
-    plain loop beyond), through the separate kernels against the oracle,
-    and (bf16) the persistent step's combine phase against the separate
-    kernels bit for bit [RLT §2.5 eq. (2.15), §4.2]."""
+    plain loop beyond), chunks merged inside the cross-attention launch
+    (forced: the call has more workgroups than the in-launch merge is
+    chosen for),
+    against the oracle; the separate combine kernel and (bf16) the
+    persistent step's combine phase against it bit for bit [RLT §2.5
+    eq. (2.15), §4.2]."""
     require_gpu()
     T = 300
     wl = synth.SMALL.with_(B=2, T=T, L=2, G=2, dtype=dtype)
-    sep = GpuRun(wl, launch=dict(xattn_chunk=16, no_packed=1))
+    sep = GpuRun(wl, launch=dict(xattn_chunk=16, no_packed=1, xattn_combine_kernel=2))
     sep.init()
     S, Z = sep.run(T)
     orc = Oracle(oracle_config(wl), oracle_weights(sep.raw))
@@ -562,6 +573,10 @@ def test_cross_attention_many_chunks(dtype):
                 worst = max(worst, es, ez)
                 assert es < tol and ez < tol, (dtype, b, t, es, ez)
     print("many chunks %s: worst rel L2 %.2e" % (dtype, worst))
+    k = GpuRun(wl, raw=sep.raw, launch=dict(xattn_chunk=16, no_packed=1, xattn_combine_kernel=1))
+    k.init()
+    Sk, Zk = k.run(T)
+    assert np.array_equal(Sk, S) and np.array_equal(Zk, Z)
     if dtype == "bf16":
         f = GpuRun(wl, raw=sep.raw, launch=dict(xattn_chunk=16, no_packed=1, fused_rows=16))
         f.init()
