@@ -664,7 +664,8 @@ def bench_backward(args, wl):
     raw = synth.make_weights(wl)
     cfg = ModelConfig(L=L, d=d, H=wl.H, dh=wl.dh, W=wl.W, G=G, F=wl.F, V=wl.V, dtype=wl.dtype,
                       merge=wl.merge, alpha=wl.alpha, eps=wl.eps, rope_theta=wl.rope_theta, pos=wl.pos)
-    dec = Decoder(cfg, raw, max_rows=B, max_ctx=T)
+    launch = {k: int(v) for k, v in (a.split("=", 1) for a in args.launch)}
+    dec = Decoder(cfg, raw, max_rows=B, max_ctx=T, launch=launch or None)
     gen = torch.Generator(device="cuda")
     gen.manual_seed(wl.seed)
     tdt = cfg.torch_dtype
@@ -712,7 +713,7 @@ def bench_backward(args, wl):
         "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": wl.name + " replay backward", "L_D": L, "d": d, "batch": B, "T": T, "W": wl.W,
-                   "G": G, "params": wl.dtype},
+                   "G": G, "params": wl.dtype, **({"launch": launch} if launch else {})},
         "roofline": {"bound": "alu", "achieved": round(tflops, 3), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 5), "traffic": None, "scope": "whole call (fp32 vector ALU)",
                      "algorithmic_flops_per_call": flops},

@@ -413,10 +413,11 @@ int rlt_memory_prefill(rlt_ctx* ctx, const rlt_memory_weights* mw, const rlt_mem
  * Arithmetic is float32 throughout, on the given parameter values (bf16
  * parameters, e and memory are widened): the call differentiates the float32
  * transition, which for a float32 configuration is the one the forward calls
- * compute (up to summation order). Activations are checkpointed per step: a
- * forward pass keeps s_t and the decoder keys/values of every step, and the
- * backward pass recomputes each step's activations before differentiating
- * it. Covers the vector merge gate, full-rank W_s and sublayer order SXF
+ * compute (up to summation order). A forward pass keeps s_t and the decoder
+ * keys/values of every step; it also keeps every step's activations when they
+ * fit in a quarter of the device memory free at the call, and otherwise
+ * (per-step checkpointing) the backward pass recomputes each step's
+ * activations before differentiating it, with the same results. Covers the vector merge gate, full-rank W_s and sublayer order SXF
  * (others: RLT_EUNSUPPORTED); len - 1 <= 8192 - d_head. Work buffers are
  * allocated for the call (RLT_ENOMEM if they do not fit). */
 typedef struct rlt_grads {

@@ -93,6 +93,8 @@ struct Model {
   std::vector<const float*> norm_s, norm_m, norm_d;
   std::vector<const void*> wq, wk, wv, wo, wqm, wom, w_gate, w_up, w_down;
   const double* inv_freq;  // [d_head / 2] rotary frequencies
+  int keep_acts;  // 0: keep every step's activations when they fit a quarter of the free device
+                  // memory, else recompute them per step; 1: always recompute; 2: always keep
 };
 
 // The replay backward of rlt_replay_backward (validated arguments); returns

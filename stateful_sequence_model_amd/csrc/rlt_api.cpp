@@ -91,6 +91,7 @@ struct rlt_ctx {
   int chunk, nch;      // cross-attention positions per partial, partial slots per row
   int xcomb_mode;      // cross-attention chunks merged: 0 by call size, 1 combine kernel, 2 in the launch
   int one_row_pf;      // weight chunks in flight per wave of one-row products
+  int bwd_keep;        // replay backward activations: 0 by size, 1 recomputed, 2 kept
   int hpw, hpw_x;      // attention heads per workgroup: SWA, cross-attention
   int narrow_rows;     // row count whose K splits the narrow product tile uses
   int gemm_target;     // K split target of the persistent step's products (0: stand-alone kernels)
@@ -592,6 +593,7 @@ static int create_ctx(const rlt_config* cfg, const rlt_weights* w, int32_t max_r
   c->big_tile = o.no_big_tile == 0;
   c->xcomb_mode = (o.xattn_combine_kernel >= 0 && o.xattn_combine_kernel <= 2) ? o.xattn_combine_kernel : 0;
   c->one_row_pf = (o.one_row_pf >= 2 && o.one_row_pf <= 4) ? o.one_row_pf : 2;
+  c->bwd_keep = (o.bwd_activations >= 0 && o.bwd_activations <= 2) ? o.bwd_activations : 0;
   if (c->pk_ready && !c->one_term) {
     c->lo_X = (int64_t)M * 2 * d;
     c->lo_o = c->lo_h = (int64_t)M * d;
@@ -1816,6 +1818,7 @@ extern "C" int rlt_replay_backward(rlt_ctx* c, const rlt_backward_io* io, const 
   m.w_up = c->w_up;
   m.w_down = c->w_down;
   m.inv_freq = c->inv_freq;
+  m.keep_acts = c->bwd_keep;
   std::string err;
   const int rc = bwd::replay_backward(m, io, gr, (hipStream_t)stream, err);
   if (rc) return fail(rc, "%s", err.c_str());

@@ -3,9 +3,10 @@
 // replayed log-probabilities. The sequences advance in lockstep as in the
 // forward replay (sorted by length, longest first, so the rows active at
 // step t are a prefix). A forward pass keeps s_t and every decoder key/value
-// (the per-step checkpoint); the backward pass walks t from the last step to
-// the first, recomputes the step's activations from s_{t-1} and the kept
-// keys/values, and differentiates it:
+// (the per-step checkpoint), and every step's activations too when they fit
+// the memory budget; the backward pass walks t from the last step to the
+// first, recomputes the step's activations from s_{t-1} and the kept
+// keys/values unless they were kept, and differentiates it:
 //   readout -> blocks L-1..0 (FFN, cross-attention, SWA) -> merge -> s_{t-1}.
 // Gradients of a step's current key/value collect the contributions of every
 // later step whose window read them (their steps are processed first), so
@@ -81,25 +82,39 @@ int replay_backward(const Model& m, const rlt_backward_io* io, const rlt_grads* 
   float* VT = buf.f((size_t)L * Tm * Bd);                   // decoder values
   float* dKT = buf.f((size_t)L * Tm * Bd);                  // their gradients
   float* dVT = buf.f((size_t)L * Tm * Bd);
-  // activations of one step (all layers)
-  float* cat = buf.f(2 * Bd);  // [e_t; r] or [e_t; s_{t-1}]
-  float* rr = buf.f(B);
-  float* g = buf.f(Bd);
-  float* wsr = buf.f(Bd);
-  float* zin = buf.f((size_t)(L + 1) * Bd);  // layer inputs; zin[L] = s_t
-  float* hs = buf.f((size_t)L * Bd);
-  float* q = buf.f((size_t)L * Bd);
-  float* o = buf.f((size_t)L * Bd);
-  float* zb = buf.f((size_t)L * Bd);
-  float* hm = buf.f((size_t)L * Bd);
-  float* qm = buf.f((size_t)L * Bd);
-  float* om = buf.f((size_t)L * Bd);
-  float* za = buf.f((size_t)L * Bd);
-  float* hd = buf.f((size_t)L * Bd);
-  float* rs = buf.f((size_t)4 * L * B + B);  // rstd of RMSNorm_S, _M, _D per layer, then _o
-  float* ga = buf.f((size_t)L * BF);
-  float* gu = buf.f((size_t)L * BF);
-  float* act = buf.f((size_t)L * BF);
+  // activations of a step (all layers), in one slot per step when they fit
+  // the budget (the backward pass then reads the forward pass's values), else
+  // in one slot that every step overwrites (recomputed in the backward pass,
+  // by the same kernels, so the values are the same bits either way)
+  auto pad = [](size_t n) { return (n + 63) / 64 * 64; };  // 256-byte sub-buffers
+  const size_t sz[] = {2 * Bd, (size_t)B, Bd, Bd, (size_t)(L + 1) * Bd, (size_t)L * Bd, (size_t)L * Bd,
+                       (size_t)L * Bd, (size_t)L * Bd, (size_t)L * Bd, (size_t)L * Bd, (size_t)L * Bd,
+                       (size_t)L * Bd, (size_t)L * Bd, (size_t)4 * L * B + B, (size_t)L * BF, (size_t)L * BF,
+                       (size_t)L * BF};
+  size_t per_step = 0;
+  for (size_t n : sz) per_step += pad(n);
+  bool keep = m.keep_acts == 2;
+  if (m.keep_acts == 0) {
+    size_t free_b = 0, total_b = 0;
+    keep = hipMemGetInfo(&free_b, &total_b) == hipSuccess && (size_t)Tm * per_step * sizeof(float) <= free_b / 4;
+  }
+  float* acts = buf.f((keep ? (size_t)Tm : 1) * per_step);
+  struct Act {
+    float *cat, *rr, *g, *wsr, *zin, *hs, *q, *o, *zb, *hm, *qm, *om, *za, *hd, *rs, *ga, *gu, *act;
+  };
+  // cat: [e_t; r] or [e_t; s_{t-1}]; zin: layer inputs, zin[L] = s_t; rs: rstd
+  // of RMSNorm_S, _M, _D per layer, then _o
+  auto act_at = [&](int t) {
+    float* p = acts + (keep ? (size_t)(t - 1) * per_step : 0);
+    Act a;
+    float** dst[] = {&a.cat, &a.rr, &a.g, &a.wsr, &a.zin, &a.hs, &a.q, &a.o, &a.zb, &a.hm, &a.qm, &a.om,
+                     &a.za, &a.hd, &a.rs, &a.ga, &a.gu, &a.act};
+    for (size_t i = 0; i < sizeof(sz) / sizeof(sz[0]); ++i) {
+      *dst[i] = p;
+      p += pad(sz[i]);
+    }
+    return a;
+  };
   float* no = buf.f(Bd);
   float* logits = buf.f((size_t)B * V);
   // gradient temporaries
@@ -129,10 +144,6 @@ int replay_backward(const Model& m, const rlt_backward_io* io, const rlt_grads* 
     err = "upload of the schedule failed";
     return RLT_EHIP;
   }
-  float* rs_s = rs;
-  float* rs_m = rs + (size_t)L * B;
-  float* rs_d = rs + (size_t)2 * L * B;
-  float* rs_o = rs + (size_t)4 * L * B;
   const size_t LT = (size_t)Tm * Bd;  // per-layer extent of the key/value trace
   auto kt_at = [&](float* base, int l, int t) { return base + (size_t)l * LT + (size_t)(t - 1) * Bd; };
   auto mem_kv = [&](int l) {
@@ -169,8 +180,12 @@ int replay_backward(const Model& m, const rlt_backward_io* io, const rlt_grads* 
     if (dW) mm(N, K, n, dY, 1, ldy, X, 0, ldx, 1, dW, K, true, s);
   };
 
-  // one transition of the n active rows at step t, keeping its activations
-  auto step_forward = [&](int t, int n) {
+  // one transition of the n active rows at step t, keeping its activations in a
+  auto step_forward = [&](int t, int n, const Act& a) {
+    float *cat = a.cat, *rr = a.rr, *g = a.g, *wsr = a.wsr, *zin = a.zin, *hs = a.hs, *q = a.q, *o = a.o;
+    float *zb = a.zb, *hm = a.hm, *qm = a.qm, *om = a.om, *za = a.za, *hd = a.hd, *ga = a.ga, *gu = a.gu;
+    float* act = a.act;
+    float *rs_s = a.rs, *rs_m = a.rs + (size_t)L * B, *rs_d = a.rs + (size_t)2 * L * B;
     const float* sp = S + (size_t)(t - 1) * Bd;
     gather_e(cat, 2 * d, io->e, dt, io->e_stride_b, io->e_stride_t, map, t, n, d, s);
     if (gated)
@@ -219,9 +234,9 @@ int replay_backward(const Model& m, const rlt_backward_io* io, const rlt_grads* 
     }
   };
   // readout [eq. (2.6)]: log p and its gradient w (onehot - softmax)
-  auto readout = [&](int t, int n, float* logp_out) {
-    const float* st = zin + (size_t)L * Bd;
-    rms_fwd(st, d, m.out_norm, no, d, rs_o, n, d, c.rms_eps, s);
+  auto readout = [&](int t, int n, float* logp_out, const Act& a) {
+    const float* st = a.zin + (size_t)L * Bd;
+    rms_fwd(st, d, m.out_norm, no, d, a.rs + (size_t)4 * L * B, n, d, c.rms_eps, s);
     lin(n, V, d, no, d, m.w_out, logits, V, false);
     logsoftmax_bwd(logits, V, io->tokens, io->tok_stride_b, io->w, io->w_stride_b, map, split, t, logp_out,
                    io->logp_stride_b, dlog, n, s);
@@ -231,18 +246,25 @@ int replay_backward(const Model& m, const rlt_backward_io* io, const rlt_grads* 
   add(S, d, m.s_star, 0, nullptr, 0, B, d, s);
   for (int t = 1; t <= Tm; ++t) {
     const int n = n_at[t];
-    step_forward(t, n);
-    add(S + (size_t)t * Bd, d, zin + (size_t)L * Bd, d, nullptr, 0, n, d, s);
-    if (io->logp) readout(t, n, io->logp);
+    const Act a = act_at(t);
+    step_forward(t, n, a);
+    add(S + (size_t)t * Bd, d, a.zin + (size_t)L * Bd, d, nullptr, 0, n, d, s);
+    if (io->logp) readout(t, n, io->logp, a);
   }
 
   // backward pass
   for (int t = Tm; t >= 1; --t) {
     const int n = n_at[t];
-    step_forward(t, n);
+    const Act a = act_at(t);
+    if (!keep) step_forward(t, n, a);
+    float *cat = a.cat, *rr = a.rr, *g = a.g, *wsr = a.wsr, *zin = a.zin, *hs = a.hs, *q = a.q, *o = a.o;
+    float *zb = a.zb, *hm = a.hm, *qm = a.qm, *om = a.om, *za = a.za, *hd = a.hd, *ga = a.ga, *gu = a.gu;
+    float* act = a.act;
+    float *rs_s = a.rs, *rs_m = a.rs + (size_t)L * B, *rs_d = a.rs + (size_t)2 * L * B;
+    float* rs_o = a.rs + (size_t)4 * L * B;
     add(dz, d, ds, d, nullptr, 0, n, d, s);  // dL/ds_t from step t+1 (zero rows past n_{t+1})
     const float* st = zin + (size_t)L * Bd;
-    readout(t, n, nullptr);
+    readout(t, n, nullptr, a);
     lin_dw(n, V, d, dlog, V, no, d, gr->w_out);
     lin_dx(n, V, d, dlog, V, m.w_out, t1, d, false);
     colsum(gr->out_norm, t1, d, st, d, rs_o, n, d, s);

@@ -21,8 +21,8 @@ pytestmark = pytest.mark.gpu
 TOL = 1e-4
 
 
-def _case(wl, lens, splits, seed=7):
-    run = GpuRun(wl, B=len(lens), T=max(lens))
+def _case(wl, lens, splits, seed=7, launch=None, raw=None):
+    run = GpuRun(wl, B=len(lens), T=max(lens), launch=launch, raw=raw)
     rng = np.random.default_rng(seed)
     B, T = len(lens), max(lens)
     tokens = rng.integers(0, wl.V, (B, T)).astype(np.int32)
@@ -144,6 +144,28 @@ def test_backward_logp_matches_replay_sequence():
     ref = ref.double().cpu().numpy()
     for b, (n, sp) in enumerate(zip(lens, splits)):
         assert np.allclose(logp[b, sp:n], ref[b, sp:n], atol=2e-5, rtol=0), b
+
+
+def test_backward_kept_and_recomputed_activations_bit_identical():
+    """Activations kept from the forward pass (the choice when they fit) and
+    recomputed per step (per-step checkpointing) give the same gradients,
+    log-probabilities, e and memory gradients bit for bit: the recompute runs
+    the same kernels on the same inputs [RLT §5.4, App. C]."""
+    require_gpu()
+    wl = synth.SMALL
+    lens, splits = [12, 7, 10, 3], [3, 1, 9, 2]
+    outs = []
+    raw = None
+    for mode in (1, 2):
+        run, tokens, w = _case(wl, lens, splits, seed=11, launch={"bwd_activations": mode}, raw=raw)
+        raw = run.raw
+        outs.append(_gpu_backward(run, lens, splits, tokens, w))
+        run.dec.close()
+    (g1, *r1), (g2, *r2) = outs
+    for k in g1:
+        assert np.array_equal(g1[k], g2[k]), k
+    for a, b in zip(r1, r2):
+        assert np.array_equal(a, b)
 
 
 def test_backward_rejects_unsupported_variants():
