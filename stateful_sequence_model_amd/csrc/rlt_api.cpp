@@ -973,8 +973,12 @@ void enqueue_transition(rlt_ctx* c, const Workspace& w, const StepPlan& P, hipSt
     at.hpw = c->hpw_x;
     { Prof pf(c, RLT_PROF_XATTN, s); launch_xattn(c->dt, at, s); }
     if (!at.direct) {
-      Prof pf(c, RLT_PROF_XCOMBINE, s);
-      launch_xcombine(c->dt, at, s);
+      if (at.cnt) {
+        launch_xcombine(c->dt, at, s);  // merged in the launch: only records the persistent step's phase
+      } else {
+        Prof pf(c, RLT_PROF_XCOMBINE, s);
+        launch_xcombine(c->dt, at, s);
+      }
     }
     EpiArgs e = E0;
     e.kind = EPI_RESID;
