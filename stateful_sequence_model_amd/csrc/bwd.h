@@ -24,12 +24,16 @@ void mm(int M, int N, int K, const float* a, int64_t a_si, int64_t a_sk, const v
 // y = RMSNorm(x) * gain (rows of width d, leading dimensions ld), rstd[r] saved
 void rms_fwd(const float* x, int64_t ldx, const float* gain, float* y, int64_t ldy, float* rstd, int n, int d,
              float eps, hipStream_t s);
-// dx (+)= d RMSNorm(x)*gain / dx applied to dy
+// dx (+)= d RMSNorm(x)*gain / dx applied to dy; with base: dx = base + that
 void rms_bwd(const float* x, int64_t ldx, const float* gain, const float* rstd, const float* dy, int64_t ldy,
-             float* dx, int64_t lddx, int n, int d, bool accumulate, hipStream_t s);
+             float* dx, int64_t lddx, int n, int d, bool accumulate, hipStream_t s, const float* base = nullptr,
+             int64_t ldb = 0);
 // dst[c] += sum_r a[r][c] * (b ? b[r][c] : 1) * (rs ? rs[r] : 1), rows in order
 void colsum(float* dst, const float* a, int64_t lda, const float* b, int64_t ldb, const float* rs, int n, int d,
             hipStream_t s);
+// the same sums over many rows (16 row lanes per column, lanes added in order)
+void colsum_rows(float* dst, const float* a, int64_t lda, const float* b, int64_t ldb, const float* rs, int64_t n,
+                 int d, hipStream_t s);
 // rotary transform of every head of n rows at position t (sign -1: inverse)
 void rope(float* x, int64_t ld, int n, int d, int dh, int t, const double* inv_freq, int sign, hipStream_t s);
 

@@ -147,10 +147,11 @@ __global__ __launch_bounds__(256) void k_rms_fwd(const float* x, int64_t ldx, co
   if (threadIdx.x == 0) rstd[r] = rs;
 }
 
-// y = x * rs * g: dx_c = rs g_c dy_c - x_c rs^3 (1/d) sum_j x_j g_j dy_j
+// y = x * rs * g: dx_c = rs g_c dy_c - x_c rs^3 (1/d) sum_j x_j g_j dy_j,
+// stored as v, dx + v (accumulate) or base + v (base given)
 __global__ __launch_bounds__(256) void k_rms_bwd(const float* x, int64_t ldx, const float* gain, const float* rstd,
                                                 const float* dy, int64_t ldy, float* dx, int64_t lddx, int d,
-                                                int accumulate) {
+                                                int accumulate, const float* base, int64_t ldb) {
   __shared__ float red[256];
   const int r = blockIdx.x;
   const float* xr = x + (int64_t)r * ldx;
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(256) void k_rms_bwd(const float* x, int64_t ldx, co
   for (int c = threadIdx.x; c < d; c += 256) {
     const float v = rs * gain[c] * dyr[c] - xr[c] * k;
     float* p = dx + (int64_t)r * lddx + c;
-    *p = accumulate ? *p + v : v;
+    *p = base ? base[(int64_t)r * ldb + c] + v : accumulate ? *p + v : v;
   }
 }
 
@@ -414,6 +415,32 @@ __global__ __launch_bounds__(256) void k_add(float* y, int64_t ldy, const float*
   y[(int64_t)r * ldy + c] = a[(int64_t)r * lda + c] + (b ? b[(int64_t)r * ldb + c] : 0.f);
 }
 
+// the column sums of k_colsum over many rows: 16 columns per block, row lane
+// q (of 16) sums rows q, q + 16, ... in order, then the lanes' sums are
+// added in lane order
+__global__ __launch_bounds__(256) void k_colsum_rows(float* dst, const float* a, int64_t lda, const float* b,
+                                                    int64_t ldb, const float* rs, int64_t n, int d) {
+  __shared__ float part[16][17];
+  const int cx = threadIdx.x & 15, q = threadIdx.x >> 4;
+  const int c = blockIdx.x * 16 + cx;
+  float acc = 0.f;
+  if (c < d) {
+    for (int64_t r = q; r < n; r += 16) {
+      float v = a[r * lda + c];
+      if (b) v *= b[r * ldb + c];
+      if (rs) v *= rs[r];
+      acc += v;
+    }
+  }
+  part[q][cx] = acc;
+  __syncthreads();
+  if (q == 0 && c < d) {
+    float sum = part[0][cx];
+    for (int k = 1; k < 16; ++k) sum += part[k][cx];
+    dst[c] += sum;
+  }
+}
+
 inline unsigned nblk(int64_t n) { return (unsigned)((n + 255) / 256); }
 
 }  // namespace
@@ -436,14 +463,21 @@ void rms_fwd(const float* x, int64_t ldx, const float* gain, float* y, int64_t l
 }
 
 void rms_bwd(const float* x, int64_t ldx, const float* gain, const float* rstd, const float* dy, int64_t ldy,
-             float* dx, int64_t lddx, int n, int d, bool accumulate, hipStream_t s) {
+             float* dx, int64_t lddx, int n, int d, bool accumulate, hipStream_t s, const float* base, int64_t ldb) {
   if (n > 0)
-    hipLaunchKernelGGL(k_rms_bwd, dim3(n), dim3(256), 0, s, x, ldx, gain, rstd, dy, ldy, dx, lddx, d, (int)accumulate);
+    hipLaunchKernelGGL(k_rms_bwd, dim3(n), dim3(256), 0, s, x, ldx, gain, rstd, dy, ldy, dx, lddx, d, (int)accumulate,
+                       base, ldb);
 }
 
 void colsum(float* dst, const float* a, int64_t lda, const float* b, int64_t ldb, const float* rs, int n, int d,
             hipStream_t s) {
   if (n > 0 && dst) hipLaunchKernelGGL(k_colsum, dim3(nblk(d)), dim3(256), 0, s, dst, a, lda, b, ldb, rs, n, d);
+}
+
+void colsum_rows(float* dst, const float* a, int64_t lda, const float* b, int64_t ldb, const float* rs, int64_t n,
+                 int d, hipStream_t s) {
+  if (n > 0 && dst)
+    hipLaunchKernelGGL(k_colsum_rows, dim3((d + 15) / 16), dim3(256), 0, s, dst, a, lda, b, ldb, rs, n, d);
 }
 
 void rope(float* x, int64_t ld, int n, int d, int dh, int t, const double* inv_freq, int sign, hipStream_t s) {

@@ -82,64 +82,79 @@ int replay_backward(const Model& m, const rlt_backward_io* io, const rlt_grads* 
   float* VT = buf.f((size_t)L * Tm * Bd);                   // decoder values
   float* dKT = buf.f((size_t)L * Tm * Bd);                  // their gradients
   float* dVT = buf.f((size_t)L * Tm * Bd);
-  // activations of a step (all layers), in one slot per step when they fit
-  // the budget (the backward pass then reads the forward pass's values), else
-  // in one slot that every step overwrites (recomputed in the backward pass,
-  // by the same kernels, so the values are the same bits either way)
-  auto pad = [](size_t n) { return (n + 63) / 64 * 64; };  // 256-byte sub-buffers
-  const size_t sz[] = {2 * Bd, (size_t)B, Bd, Bd, (size_t)(L + 1) * Bd, (size_t)L * Bd, (size_t)L * Bd,
-                       (size_t)L * Bd, (size_t)L * Bd, (size_t)L * Bd, (size_t)L * Bd, (size_t)L * Bd,
-                       (size_t)L * Bd, (size_t)L * Bd, (size_t)4 * L * B + B, (size_t)L * BF, (size_t)L * BF,
-                       (size_t)L * BF};
+
+  // Per-step values the backward pass reads: the step's activations and the
+  // gradients that feed the weight-gradient products. Each is a field of
+  // `nl` layers x slots x B rows x `width`, layer-major, so that one layer's
+  // rows of consecutive steps are evenly strided. With one slot per step
+  // (kept: the backward pass reads the forward pass's activations, and every
+  // weight gradient is one product over all steps' rows at the end) when they
+  // fit a quarter of the free device memory; else one slot that every step
+  // overwrites (activations recomputed in the backward pass by the same
+  // kernels, weight gradients accumulated step by step).
+  struct Field {
+    int nl;
+    size_t width;
+    float* base;
+  };
+  enum {
+    CAT, RR, GG, WSR, ZIN, HS, Q, O, ZB, HM, QM, OM, ZA, HD, RS, GA, GU, ACT,  // activations
+    NO, DLOG, DPRE, DWM, DZV, DF2, DF3, DQM, DQS,                            // weight-gradient operands
+    T1O, T1D, T2M, T2S, DCAT, NFIELD                                         // gain-gradient operands
+  };
+  Field fl[NFIELD] = {
+      {1, 2 * (size_t)d, nullptr}, {1, 1, nullptr}, {1, (size_t)d, nullptr}, {1, (size_t)d, nullptr},
+      {L + 1, (size_t)d, nullptr},  // layer inputs; layer L: s_t
+      {L, (size_t)d, nullptr}, {L, (size_t)d, nullptr}, {L, (size_t)d, nullptr}, {L, (size_t)d, nullptr},
+      {L, (size_t)d, nullptr}, {L, (size_t)d, nullptr}, {L, (size_t)d, nullptr}, {L, (size_t)d, nullptr},
+      {L, (size_t)d, nullptr},
+      {4 * L + 1, 1, nullptr},  // rstd of RMSNorm_S (layers 0..L-1), _M (L..), _D (2L..), _o (4L)
+      {L, (size_t)F, nullptr}, {L, (size_t)F, nullptr}, {L, (size_t)F, nullptr},
+      {1, (size_t)d, nullptr}, {1, (size_t)V, nullptr}, {1, (size_t)d, nullptr}, {1, (size_t)d, nullptr},
+      {3 * L + 1, (size_t)d, nullptr},  // dL/dz at each sublayer boundary of the step
+      {L, (size_t)F, nullptr}, {L, (size_t)F, nullptr}, {L, (size_t)d, nullptr}, {L, (size_t)d, nullptr},
+      {1, (size_t)d, nullptr}, {L, (size_t)d, nullptr}, {L, (size_t)d, nullptr}, {L, (size_t)d, nullptr},
+      {1, 2 * (size_t)d, nullptr}};
   size_t per_step = 0;
-  for (size_t n : sz) per_step += pad(n);
+  for (const Field& f : fl) per_step += (size_t)f.nl * B * f.width;
   bool keep = m.keep_acts == 2;
   if (m.keep_acts == 0) {
     size_t free_b = 0, total_b = 0;
     keep = hipMemGetInfo(&free_b, &total_b) == hipSuccess && (size_t)Tm * per_step * sizeof(float) <= free_b / 4;
   }
-  float* acts = buf.f((keep ? (size_t)Tm : 1) * per_step);
-  struct Act {
-    float *cat, *rr, *g, *wsr, *zin, *hs, *q, *o, *zb, *hm, *qm, *om, *za, *hd, *rs, *ga, *gu, *act;
-  };
-  // cat: [e_t; r] or [e_t; s_{t-1}]; zin: layer inputs, zin[L] = s_t; rs: rstd
-  // of RMSNorm_S, _M, _D per layer, then _o
-  auto act_at = [&](int t) {
-    float* p = acts + (keep ? (size_t)(t - 1) * per_step : 0);
-    Act a;
-    float** dst[] = {&a.cat, &a.rr, &a.g, &a.wsr, &a.zin, &a.hs, &a.q, &a.o, &a.zb, &a.hm, &a.qm, &a.om,
-                     &a.za, &a.hd, &a.rs, &a.ga, &a.gu, &a.act};
-    for (size_t i = 0; i < sizeof(sz) / sizeof(sz[0]); ++i) {
-      *dst[i] = p;
-      p += pad(sz[i]);
+  const size_t nslot = keep ? (size_t)Tm : 1;
+  float* fields = buf.f(nslot * per_step);
+  {
+    float* p = fields;
+    for (Field& f : fl) {
+      f.base = p;
+      p += (size_t)f.nl * nslot * B * f.width;
     }
-    return a;
+  }
+  // layer l of field f at step t
+  auto at = [&](int f, int l, int t) {
+    const Field& x = fl[f];
+    return x.base + ((size_t)l * nslot + (keep ? (size_t)(t - 1) : 0)) * B * x.width;
   };
-  float* no = buf.f(Bd);
   float* logits = buf.f((size_t)B * V);
   // gradient temporaries
   float* ds = buf.f(Bd);
-  float* dz = buf.f(Bd);
   float* t1 = buf.f(Bd);
-  float* t2 = buf.f(Bd);
-  float* dq = buf.f(Bd);
   float* dF1 = buf.f(BF);
-  float* dF2 = buf.f(BF);
-  float* dF3 = buf.f(BF);
-  float* dlog = buf.f((size_t)B * V);
-  float* dcat = buf.f(2 * Bd);
-  float* dpre = buf.f(Bd);
-  float* dw = buf.f(Bd);
   float* det = buf.f(Bd);
   if (!buf.ok) {
     (void)hipGetLastError();
     err = "work buffers of the replay backward do not fit";
     return RLT_ENOMEM;
   }
+  // with one slot per step, rows past a step's active prefix are never
+  // written: zero (S too), so that they add nothing to the sums over all slots
   if (hipMemcpyAsync(map, order.data(), B * sizeof(int), hipMemcpyHostToDevice, s) != hipSuccess ||
       hipMemcpyAsync(split, split_sorted.data(), B * sizeof(int), hipMemcpyHostToDevice, s) != hipSuccess ||
       hipMemsetAsync(dKT, 0, (size_t)L * Tm * Bd * sizeof(float), s) != hipSuccess ||
       hipMemsetAsync(dVT, 0, (size_t)L * Tm * Bd * sizeof(float), s) != hipSuccess ||
+      hipMemsetAsync(fields, 0, nslot * per_step * sizeof(float), s) != hipSuccess ||
+      hipMemsetAsync(S, 0, (size_t)(Tm + 1) * Bd * sizeof(float), s) != hipSuccess ||
       hipMemsetAsync(ds, 0, Bd * sizeof(float), s) != hipSuccess) {
     err = "upload of the schedule failed";
     return RLT_EHIP;
@@ -175,17 +190,18 @@ int replay_backward(const Model& m, const rlt_backward_io* io, const rlt_grads* 
   auto lin_dx = [&](int n, int N, int K, const float* dY, int64_t ldy, const void* Wt, float* dX, int64_t ldx, bool acc) {
     mm(n, K, N, dY, ldy, 1, Wt, dt, K, 1, dX, ldx, acc, s);
   };
-  // dW[N][K] += dY^T X (rows summed in order)
-  auto lin_dw = [&](int n, int N, int K, const float* dY, int64_t ldy, const float* X, int64_t ldx, float* dW) {
-    if (dW) mm(N, K, n, dY, 1, ldy, X, 0, ldx, 1, dW, K, true, s);
+  // dW[N][K] += dY^T X over n rows, in order
+  auto lin_dw = [&](int64_t n, int N, int K, const float* dY, int64_t ldy, const float* X, int64_t ldx, float* dW) {
+    if (dW) mm(N, K, (int)n, dY, 1, ldy, X, 0, ldx, 1, dW, K, true, s);
   };
 
-  // one transition of the n active rows at step t, keeping its activations in a
-  auto step_forward = [&](int t, int n, const Act& a) {
-    float *cat = a.cat, *rr = a.rr, *g = a.g, *wsr = a.wsr, *zin = a.zin, *hs = a.hs, *q = a.q, *o = a.o;
-    float *zb = a.zb, *hm = a.hm, *qm = a.qm, *om = a.om, *za = a.za, *hd = a.hd, *ga = a.ga, *gu = a.gu;
-    float* act = a.act;
-    float *rs_s = a.rs, *rs_m = a.rs + (size_t)L * B, *rs_d = a.rs + (size_t)2 * L * B;
+  // one transition of the n active rows at step t, keeping its activations
+  // in the step's slots
+  auto step_forward = [&](int t, int n) {
+    float* cat = at(CAT, 0, t);
+    float* rr = at(RR, 0, t);
+    float* g = at(GG, 0, t);
+    float* wsr = at(WSR, 0, t);
     const float* sp = S + (size_t)(t - 1) * Bd;
     gather_e(cat, 2 * d, io->e, dt, io->e_stride_b, io->e_stride_t, map, t, n, d, s);
     if (gated)
@@ -196,96 +212,134 @@ int replay_backward(const Model& m, const rlt_backward_io* io, const rlt_grads* 
     sigmoid_bias(g, d, m.merge_bg, n, d, s);
     if (gated) {
       lin(n, d, d, cat + d, 2 * d, m.merge_ws, wsr, d, false);
-      merge_fwd(1, zin, cat, 2 * d, g, wsr, d, c.alpha, n, d, s);
+      merge_fwd(1, at(ZIN, 0, t), cat, 2 * d, g, wsr, d, c.alpha, n, d, s);
     } else {
-      merge_fwd(0, zin, cat, 2 * d, g, sp, d, c.alpha, n, d, s);
+      merge_fwd(0, at(ZIN, 0, t), cat, 2 * d, g, sp, d, c.alpha, n, d, s);
     }
     for (int l = 0; l < L; ++l) {
-      const size_t o_l = (size_t)l * Bd;
-      float* z = zin + o_l;
+      float* z = at(ZIN, l, t);
+      float *hs = at(HS, l, t), *q = at(Q, l, t), *o = at(O, l, t), *zb = at(ZB, l, t);
+      float *hm = at(HM, l, t), *qm = at(QM, l, t), *om = at(OM, l, t), *za = at(ZA, l, t), *hd = at(HD, l, t);
+      float *ga = at(GA, l, t), *gu = at(GU, l, t), *act = at(ACT, l, t);
       // SWA [eqs. (2.12)-(2.14)]
-      rms_fwd(z, d, m.norm_s[l], hs + o_l, d, rs_s + (size_t)l * B, n, d, c.rms_eps, s);
+      rms_fwd(z, d, m.norm_s[l], hs, d, at(RS, l, t), n, d, c.rms_eps, s);
       float* kt = kt_at(KT, l, t);
       float* vt = kt_at(VT, l, t);
-      lin(n, d, d, hs + o_l, d, m.wq[l], q + o_l, d, false);
-      lin(n, d, d, hs + o_l, d, m.wk[l], kt, d, false);
-      lin(n, d, d, hs + o_l, d, m.wv[l], vt, d, false);
+      lin(n, d, d, hs, d, m.wq[l], q, d, false);
+      lin(n, d, d, hs, d, m.wk[l], kt, d, false);
+      lin(n, d, d, hs, d, m.wv[l], vt, d, false);
       if (rope_on) {
-        rope(q + o_l, d, n, d, dh, t, m.inv_freq, 1, s);
+        rope(q, d, n, d, dh, t, m.inv_freq, 1, s);
         rope(kt, d, n, d, dh, t, m.inv_freq, 1, s);
       }
-      attn_fwd(q + o_l, d, trace_kv(l), std::max(1, t - W + 1), t, o + o_l, d, n, H, dh, s);
-      add(zb + o_l, d, z, d, nullptr, 0, n, d, s);
-      lin(n, d, d, o + o_l, d, m.wo[l], zb + o_l, d, true);
+      attn_fwd(q, d, trace_kv(l), std::max(1, t - W + 1), t, o, d, n, H, dh, s);
+      add(zb, d, z, d, nullptr, 0, n, d, s);
+      lin(n, d, d, o, d, m.wo[l], zb, d, true);
       // cross-attention to M_{<=t} [eq. (2.15)]
-      rms_fwd(zb + o_l, d, m.norm_m[l], hm + o_l, d, rs_m + (size_t)l * B, n, d, c.rms_eps, s);
-      lin(n, d, d, hm + o_l, d, m.wqm[l], qm + o_l, d, false);
-      if (rope_on) rope(qm + o_l, d, n, d, dh, t, m.inv_freq, 1, s);
-      attn_fwd(qm + o_l, d, mem_kv(l), 1, t, om + o_l, d, n, H, dh, s);
-      add(za + o_l, d, zb + o_l, d, nullptr, 0, n, d, s);
-      lin(n, d, d, om + o_l, d, m.wom[l], za + o_l, d, true);
+      rms_fwd(zb, d, m.norm_m[l], hm, d, at(RS, L + l, t), n, d, c.rms_eps, s);
+      lin(n, d, d, hm, d, m.wqm[l], qm, d, false);
+      if (rope_on) rope(qm, d, n, d, dh, t, m.inv_freq, 1, s);
+      attn_fwd(qm, d, mem_kv(l), 1, t, om, d, n, H, dh, s);
+      add(za, d, zb, d, nullptr, 0, n, d, s);
+      lin(n, d, d, om, d, m.wom[l], za, d, true);
       // SwiGLU FFN [eq. (2.16)]
-      rms_fwd(za + o_l, d, m.norm_d[l], hd + o_l, d, rs_d + (size_t)l * B, n, d, c.rms_eps, s);
-      lin(n, F, d, hd + o_l, d, m.w_gate[l], ga + (size_t)l * BF, F, false);
-      lin(n, F, d, hd + o_l, d, m.w_up[l], gu + (size_t)l * BF, F, false);
-      swiglu_fwd(ga + (size_t)l * BF, gu + (size_t)l * BF, act + (size_t)l * BF, n, F, s);
-      add(zin + o_l + Bd, d, za + o_l, d, nullptr, 0, n, d, s);
-      lin(n, d, F, act + (size_t)l * BF, F, m.w_down[l], zin + o_l + Bd, d, true);
+      rms_fwd(za, d, m.norm_d[l], hd, d, at(RS, 2 * L + l, t), n, d, c.rms_eps, s);
+      lin(n, F, d, hd, d, m.w_gate[l], ga, F, false);
+      lin(n, F, d, hd, d, m.w_up[l], gu, F, false);
+      swiglu_fwd(ga, gu, act, n, F, s);
+      float* zn = at(ZIN, l + 1, t);
+      add(zn, d, za, d, nullptr, 0, n, d, s);
+      lin(n, d, F, act, F, m.w_down[l], zn, d, true);
     }
   };
   // readout [eq. (2.6)]: log p and its gradient w (onehot - softmax)
-  auto readout = [&](int t, int n, float* logp_out, const Act& a) {
-    const float* st = a.zin + (size_t)L * Bd;
-    rms_fwd(st, d, m.out_norm, no, d, a.rs + (size_t)4 * L * B, n, d, c.rms_eps, s);
+  auto readout = [&](int t, int n, float* logp_out) {
+    const float* st = at(ZIN, L, t);
+    float* no = at(NO, 0, t);
+    rms_fwd(st, d, m.out_norm, no, d, at(RS, 4 * L, t), n, d, c.rms_eps, s);
     lin(n, V, d, no, d, m.w_out, logits, V, false);
     logsoftmax_bwd(logits, V, io->tokens, io->tok_stride_b, io->w, io->w_stride_b, map, split, t, logp_out,
-                   io->logp_stride_b, dlog, n, s);
+                   io->logp_stride_b, at(DLOG, 0, t), n, s);
+  };
+  // weight gradients: over every step's slot at once (t = 0, kept; rows past
+  // a step's prefix are zero there, never written) or over the n_t active
+  // rows of step t's slot
+  auto weight_grads = [&](int t) {
+    const int tt = t > 0 ? t : 1;
+    const int64_t R = t > 0 ? (int64_t)n_at[t] : (int64_t)nslot * B;
+    lin_dw(R, V, d, at(DLOG, 0, tt), V, at(NO, 0, tt), d, gr->w_out);
+    for (int l = 0; l < L; ++l) {
+      const int iv = 3 * (L - 1 - l);
+      lin_dw(R, d, F, at(DZV, iv, tt), d, at(ACT, l, tt), F, layer_ptr(gr->w_down, l));
+      lin_dw(R, F, d, at(DF2, l, tt), F, at(HD, l, tt), d, layer_ptr(gr->w_gate, l));
+      lin_dw(R, F, d, at(DF3, l, tt), F, at(HD, l, tt), d, layer_ptr(gr->w_up, l));
+      lin_dw(R, d, d, at(DZV, iv + 1, tt), d, at(OM, l, tt), d, layer_ptr(gr->wom, l));
+      lin_dw(R, d, d, at(DQM, l, tt), d, at(HM, l, tt), d, layer_ptr(gr->wqm, l));
+      lin_dw(R, d, d, at(DZV, iv + 2, tt), d, at(O, l, tt), d, layer_ptr(gr->wo, l));
+      lin_dw(R, d, d, at(DQS, l, tt), d, at(HS, l, tt), d, layer_ptr(gr->wq, l));
+      lin_dw(R, d, d, kt_at(dKT, l, tt), d, at(HS, l, tt), d, layer_ptr(gr->wk, l));
+      lin_dw(R, d, d, kt_at(dVT, l, tt), d, at(HS, l, tt), d, layer_ptr(gr->wv, l));
+    }
+    lin_dw(R, d, 2 * d, at(DPRE, 0, tt), d, at(CAT, 0, tt), 2 * d, gr->merge_wg);
+    if (gated) lin_dw(R, d, d, at(DWM, 0, tt), d, at(CAT, 0, tt) + d, 2 * d, gr->merge_ws);
+  };
+
+  // gain and bias gradients (column sums): step by step in the backward
+  // pass (one slot), or over every step's slot at once (kept)
+  auto colsum_at = [&](float* dst, const float* a, int64_t lda, const float* b, int64_t ldb, const float* rs, int n) {
+    if (!keep) colsum(dst, a, lda, b, ldb, rs, n, d, s);
+  };
+  auto gain_grads = [&]() {
+    const int64_t R = (int64_t)nslot * B;
+    colsum_rows(gr->out_norm, at(T1O, 0, 1), d, at(ZIN, L, 1), d, at(RS, 4 * L, 1), R, d, s);
+    for (int l = 0; l < L; ++l) {
+      colsum_rows(layer_ptr(gr->norm_d, l), at(T1D, l, 1), d, at(ZA, l, 1), d, at(RS, 2 * L + l, 1), R, d, s);
+      colsum_rows(layer_ptr(gr->norm_m, l), at(T2M, l, 1), d, at(ZB, l, 1), d, at(RS, L + l, 1), R, d, s);
+      colsum_rows(layer_ptr(gr->norm_s, l), at(T2S, l, 1), d, at(ZIN, l, 1), d, at(RS, l, 1), R, d, s);
+    }
+    colsum_rows(gr->merge_bg, at(DPRE, 0, 1), d, nullptr, 0, nullptr, R, d, s);
+    // s_{t-1} of step t is S[t - 1]: rows of S[0 .. Tm - 1] in step order
+    if (gated) colsum_rows(gr->merge_norm, at(DCAT, 0, 1) + d, 2 * d, S, d, at(RR, 0, 1), R, d, s);
   };
 
   // forward pass: s_t and the decoder keys/values of every step
   add(S, d, m.s_star, 0, nullptr, 0, B, d, s);
   for (int t = 1; t <= Tm; ++t) {
     const int n = n_at[t];
-    const Act a = act_at(t);
-    step_forward(t, n, a);
-    add(S + (size_t)t * Bd, d, a.zin + (size_t)L * Bd, d, nullptr, 0, n, d, s);
-    if (io->logp) readout(t, n, io->logp, a);
+    step_forward(t, n);
+    add(S + (size_t)t * Bd, d, at(ZIN, L, t), d, nullptr, 0, n, d, s);
+    if (io->logp) readout(t, n, io->logp);
   }
 
   // backward pass
   for (int t = Tm; t >= 1; --t) {
     const int n = n_at[t];
-    const Act a = act_at(t);
-    if (!keep) step_forward(t, n, a);
-    float *cat = a.cat, *rr = a.rr, *g = a.g, *wsr = a.wsr, *zin = a.zin, *hs = a.hs, *q = a.q, *o = a.o;
-    float *zb = a.zb, *hm = a.hm, *qm = a.qm, *om = a.om, *za = a.za, *hd = a.hd, *ga = a.ga, *gu = a.gu;
-    float* act = a.act;
-    float *rs_s = a.rs, *rs_m = a.rs + (size_t)L * B, *rs_d = a.rs + (size_t)2 * L * B;
-    float* rs_o = a.rs + (size_t)4 * L * B;
-    add(dz, d, ds, d, nullptr, 0, n, d, s);  // dL/ds_t from step t+1 (zero rows past n_{t+1})
-    const float* st = zin + (size_t)L * Bd;
-    readout(t, n, nullptr, a);
-    lin_dw(n, V, d, dlog, V, no, d, gr->w_out);
-    lin_dx(n, V, d, dlog, V, m.w_out, t1, d, false);
-    colsum(gr->out_norm, t1, d, st, d, rs_o, n, d, s);
-    rms_bwd(st, d, m.out_norm, rs_o, t1, d, dz, d, n, d, true, s);
+    if (!keep) step_forward(t, n);
+    const float* st = at(ZIN, L, t);
+    readout(t, n, nullptr);
+    // dL/ds_t: from step t+1 (zero rows past n_{t+1}) and the readout
+    float* dz0 = at(DZV, 0, t);
+    add(dz0, d, ds, d, nullptr, 0, n, d, s);
+    float* t1o = at(T1O, 0, t);
+    lin_dx(n, V, d, at(DLOG, 0, t), V, m.w_out, t1o, d, false);
+    colsum_at(gr->out_norm, t1o, d, st, d, at(RS, 4 * L, t), n);
+    rms_bwd(st, d, m.out_norm, at(RS, 4 * L, t), t1o, d, dz0, d, n, d, true, s);
     for (int l = L - 1; l >= 0; --l) {
-      const size_t o_l = (size_t)l * Bd;
-      float* gal = ga + (size_t)l * BF;
-      float* gul = gu + (size_t)l * BF;
+      // dL/dz entering the layer's FFN, cross-attention and SWA backward, and leaving it
+      const int iv = 3 * (L - 1 - l);
+      float *dzF = at(DZV, iv, t), *dzX = at(DZV, iv + 1, t), *dzS = at(DZV, iv + 2, t), *dzN = at(DZV, iv + 3, t);
+      float *za = at(ZA, l, t), *zb = at(ZB, l, t), *z = at(ZIN, l, t);
+      float *dF2 = at(DF2, l, t), *dF3 = at(DF3, l, t), *dqm = at(DQM, l, t), *dqs = at(DQS, l, t);
       // FFN: z_out = za + W_down act
-      lin_dx(n, d, F, dz, d, m.w_down[l], dF1, F, false);
-      lin_dw(n, d, F, dz, d, act + (size_t)l * BF, F, layer_ptr(gr->w_down, l));
-      swiglu_bwd(gal, gul, dF1, dF2, dF3, n, F, s);
-      lin_dx(n, F, d, dF2, F, m.w_gate[l], t1, d, false);
-      lin_dx(n, F, d, dF3, F, m.w_up[l], t1, d, true);
-      lin_dw(n, F, d, dF2, F, hd + o_l, d, layer_ptr(gr->w_gate, l));
-      lin_dw(n, F, d, dF3, F, hd + o_l, d, layer_ptr(gr->w_up, l));
-      colsum(layer_ptr(gr->norm_d, l), t1, d, za + o_l, d, rs_d + (size_t)l * B, n, d, s);
-      rms_bwd(za + o_l, d, m.norm_d[l], rs_d + (size_t)l * B, t1, d, dz, d, n, d, true, s);
+      lin_dx(n, d, F, dzF, d, m.w_down[l], dF1, F, false);
+      swiglu_bwd(at(GA, l, t), at(GU, l, t), dF1, dF2, dF3, n, F, s);
+      float* t1d = at(T1D, l, t);
+      lin_dx(n, F, d, dF2, F, m.w_gate[l], t1d, d, false);
+      lin_dx(n, F, d, dF3, F, m.w_up[l], t1d, d, true);
+      colsum_at(layer_ptr(gr->norm_d, l), t1d, d, za, d, at(RS, 2 * L + l, t), n);
+      rms_bwd(za, d, m.norm_d[l], at(RS, 2 * L + l, t), t1d, d, dzX, d, n, d, false, s, dzF, d);
       // cross-attention: za = zb + W_om om
-      lin_dx(n, d, d, dz, d, m.wom[l], t1, d, false);
-      lin_dw(n, d, d, dz, d, om + o_l, d, layer_ptr(gr->wom, l));
+      lin_dx(n, d, d, dzX, d, m.wom[l], t1, d, false);
       DKV dm{};
       if (io->dmem_k) {
         const int gi = (l * G) / L;
@@ -295,50 +349,56 @@ int replay_backward(const Model& m, const rlt_backward_io* io, const rlt_grads* 
         dm.s_pos = io->dmem_stride_t;
         dm.map = map;
       }
-      attn_bwd(qm + o_l, d, mem_kv(l), 1, t, t1, d, dq, d, dm, n, H, dh, s);
-      if (rope_on) rope(dq, d, n, d, dh, t, m.inv_freq, -1, s);
-      lin_dx(n, d, d, dq, d, m.wqm[l], t2, d, false);
-      lin_dw(n, d, d, dq, d, hm + o_l, d, layer_ptr(gr->wqm, l));
-      colsum(layer_ptr(gr->norm_m, l), t2, d, zb + o_l, d, rs_m + (size_t)l * B, n, d, s);
-      rms_bwd(zb + o_l, d, m.norm_m[l], rs_m + (size_t)l * B, t2, d, dz, d, n, d, true, s);
+      attn_bwd(at(QM, l, t), d, mem_kv(l), 1, t, t1, d, dqm, d, dm, n, H, dh, s);
+      if (rope_on) rope(dqm, d, n, d, dh, t, m.inv_freq, -1, s);
+      float* t2m = at(T2M, l, t);
+      lin_dx(n, d, d, dqm, d, m.wqm[l], t2m, d, false);
+      colsum_at(layer_ptr(gr->norm_m, l), t2m, d, zb, d, at(RS, L + l, t), n);
+      rms_bwd(zb, d, m.norm_m[l], at(RS, L + l, t), t2m, d, dzS, d, n, d, false, s, dzX, d);
       // SWA: zb = z + W_o o; the window's keys/values take their gradients in the trace
-      lin_dx(n, d, d, dz, d, m.wo[l], t1, d, false);
-      lin_dw(n, d, d, dz, d, o + o_l, d, layer_ptr(gr->wo, l));
+      lin_dx(n, d, d, dzS, d, m.wo[l], t1, d, false);
       DKV dtr{dKT + (size_t)l * LT, dVT + (size_t)l * LT, d, (int64_t)Bd, nullptr};
-      attn_bwd(q + o_l, d, trace_kv(l), std::max(1, t - W + 1), t, t1, d, dq, d, dtr, n, H, dh, s);
+      attn_bwd(at(Q, l, t), d, trace_kv(l), std::max(1, t - W + 1), t, t1, d, dqs, d, dtr, n, H, dh, s);
       // the current key/value has now received the gradient of every step that read it
       float* dk = kt_at(dKT, l, t);
       float* dv = kt_at(dVT, l, t);
       if (rope_on) {
-        rope(dq, d, n, d, dh, t, m.inv_freq, -1, s);
+        rope(dqs, d, n, d, dh, t, m.inv_freq, -1, s);
         rope(dk, d, n, d, dh, t, m.inv_freq, -1, s);
       }
-      lin_dx(n, d, d, dq, d, m.wq[l], t2, d, false);
-      lin_dx(n, d, d, dk, d, m.wk[l], t2, d, true);
-      lin_dx(n, d, d, dv, d, m.wv[l], t2, d, true);
-      lin_dw(n, d, d, dq, d, hs + o_l, d, layer_ptr(gr->wq, l));
-      lin_dw(n, d, d, dk, d, hs + o_l, d, layer_ptr(gr->wk, l));
-      lin_dw(n, d, d, dv, d, hs + o_l, d, layer_ptr(gr->wv, l));
-      colsum(layer_ptr(gr->norm_s, l), t2, d, zin + o_l, d, rs_s + (size_t)l * B, n, d, s);
-      rms_bwd(zin + o_l, d, m.norm_s[l], rs_s + (size_t)l * B, t2, d, dz, d, n, d, true, s);
+      float* t2s = at(T2S, l, t);
+      lin_dx(n, d, d, dqs, d, m.wq[l], t2s, d, false);
+      lin_dx(n, d, d, dk, d, m.wk[l], t2s, d, true);
+      lin_dx(n, d, d, dv, d, m.wv[l], t2s, d, true);
+      colsum_at(layer_ptr(gr->norm_s, l), t2s, d, z, d, at(RS, l, t), n);
+      rms_bwd(z, d, m.norm_s[l], at(RS, l, t), t2s, d, dzN, d, n, d, false, s, dzS, d);
     }
     // merge [eqs. (2.9)-(2.11)] back to e_t and s_{t-1}
+    const float* dz = at(DZV, 3 * L, t);
     const float* sp = S + (size_t)(t - 1) * Bd;
-    merge_bwd(gated ? 1 : 0, dz, cat, 2 * d, g, gated ? wsr : sp, d, c.alpha, dpre, dw, det, d, n, d, s);
-    lin_dw(n, d, 2 * d, dpre, d, cat, 2 * d, gr->merge_wg);
-    colsum(gr->merge_bg, dpre, d, nullptr, 0, nullptr, n, d, s);
+    float* cat = at(CAT, 0, t);
+    float* dpre = at(DPRE, 0, t);
+    float* dw = at(DWM, 0, t);
+    merge_bwd(gated ? 1 : 0, dz, cat, 2 * d, at(GG, 0, t), gated ? at(WSR, 0, t) : sp, d, c.alpha, dpre, dw, det, d,
+              n, d, s);
+    float* dcat = at(DCAT, 0, t);
+    colsum_at(gr->merge_bg, dpre, d, nullptr, 0, nullptr, n);
     lin_dx(n, d, 2 * d, dpre, d, m.merge_wg, dcat, 2 * d, false);
     add(det, d, det, d, dcat, 2 * d, n, d, s);
     scatter_add_e(io->de, io->de_stride_b, io->de_stride_t, det, d, map, t, n, d, s);
     if (gated) {
-      lin_dw(n, d, d, dw, d, cat + d, 2 * d, gr->merge_ws);
       lin_dx(n, d, d, dw, d, m.merge_ws, dcat + d, 2 * d, true);
-      colsum(gr->merge_norm, dcat + d, 2 * d, sp, d, rr, n, d, s);
-      rms_bwd(sp, d, m.merge_norm, rr, dcat + d, 2 * d, ds, d, n, d, false, s);
+      colsum_at(gr->merge_norm, dcat + d, 2 * d, sp, d, at(RR, 0, t), n);
+      rms_bwd(sp, d, m.merge_norm, at(RR, 0, t), dcat + d, 2 * d, ds, d, n, d, false, s);
     } else {
       add(ds, d, dw, d, dcat + d, 2 * d, n, d, s);
     }
     if (t == 1) colsum(gr->s_star, ds, d, nullptr, 0, nullptr, n, d, s);
+    if (!keep) weight_grads(t);
+  }
+  if (keep) {
+    weight_grads(0);
+    gain_grads();
   }
   if (hipGetLastError() != hipSuccess || hipStreamSynchronize(s) != hipSuccess) {
     err = "replay backward kernels failed";

@@ -146,11 +146,13 @@ def test_backward_logp_matches_replay_sequence():
         assert np.allclose(logp[b, sp:n], ref[b, sp:n], atol=2e-5, rtol=0), b
 
 
-def test_backward_kept_and_recomputed_activations_bit_identical():
+def test_backward_kept_and_recomputed_activations():
     """Activations kept from the forward pass (the choice when they fit) and
-    recomputed per step (per-step checkpointing) give the same gradients,
-    log-probabilities, e and memory gradients bit for bit: the recompute runs
-    the same kernels on the same inputs [RLT §5.4, App. C]."""
+    recomputed per step (per-step checkpointing) [RLT §5.4, App. C]: the
+    recompute runs the same kernels on the same inputs, so log-probabilities,
+    e and memory gradients are the same bits; the parameter gradients differ
+    only in summation order (one product or column sum over every step's rows
+    when kept, step by step otherwise)."""
     require_gpu()
     wl = synth.SMALL
     lens, splits = [12, 7, 10, 3], [3, 1, 9, 2]
@@ -163,7 +165,7 @@ def test_backward_kept_and_recomputed_activations_bit_identical():
         run.dec.close()
     (g1, *r1), (g2, *r2) = outs
     for k in g1:
-        assert np.array_equal(g1[k], g2[k]), k
+        assert rel_l2(g2[k], g1[k]) < 1e-6, k
     for a, b in zip(r1, r2):
         assert np.array_equal(a, b)
 

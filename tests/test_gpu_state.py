@@ -577,6 +577,12 @@ def test_cross_attention_many_chunks(dtype):
     k.init()
     Sk, Zk = k.run(T)
     assert np.array_equal(Sk, S) and np.array_equal(Zk, Z)
+    # the library's own choice in one context: the two-row call merges with
+    # the combine kernel, a one-row call inside the launch; same bits
+    one = GpuRun(wl, raw=sep.raw, launch=dict(xattn_chunk=16, no_packed=1))
+    one.init([1])
+    S1, Z1 = one.run(T, [1])
+    assert np.array_equal(S1[:, 0], S[:, 1]) and np.array_equal(Z1[:, 0], Z[:, 1])
     if dtype == "bf16":
         f = GpuRun(wl, raw=sep.raw, launch=dict(xattn_chunk=16, no_packed=1, fused_rows=16))
         f.init()
