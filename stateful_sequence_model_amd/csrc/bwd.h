@@ -20,6 +20,14 @@ namespace bwd {
 // B(k,j) = b[k*b_sk + j*b_sj] (element type bdt), C[i][j] at c[i*c_si + j].
 void mm(int M, int N, int K, const float* a, int64_t a_si, int64_t a_sk, const void* b, int bdt, int64_t b_sk,
         int64_t b_sj, float* c, int64_t c_si, bool accumulate, hipStream_t s);
+// nseg (<= 3) products of one launch, each the same bits as its own mm call:
+// one A, B and C per segment (mm_outputs), or A and B per segment added into
+// one C in segment order (mm_summed: C (+)= A_0 B_0, then += A_1 B_1, ...)
+void mm_outputs(int nseg, int M, int N, int K, const float* a, int64_t a_si, int64_t a_sk, const void* const* b,
+                int bdt, int64_t b_sk, int64_t b_sj, float* const* c, int64_t c_si, bool accumulate, hipStream_t s);
+void mm_summed(int nseg, int M, int N, int K, const float* const* a, int64_t a_si, int64_t a_sk,
+               const void* const* b, int bdt, int64_t b_sk, int64_t b_sj, float* c, int64_t c_si, bool accumulate,
+               hipStream_t s);
 
 // y = RMSNorm(x) * gain (rows of width d, leading dimensions ld), rstd[r] saved
 void rms_fwd(const float* x, int64_t ldx, const float* gain, float* y, int64_t ldy, float* rstd, int n, int d,

@@ -55,10 +55,21 @@ __device__ __forceinline__ float sigm(float x) { return 1.0f / (1.0f + expf(-x))
 // runs along the fastest thread index when its tile is loaded; the next
 // step's elements are loaded into registers while the current step is
 // multiplied.
+// Up to three products in one launch (MmSeg): segments with their own B
+// operand and either their own output (sum = 0: blockIdx.z picks the
+// segment) or their own A operand and one shared output that they are added
+// into in segment order (sum = 1). Each segment's product is the k_mm sum
+// above, so the results equal separate launches bit for bit.
+struct MmSeg {
+  const float* a[3];
+  const void* b[3];
+  float* c[3];
+  int nseg, sum;
+};
+
 template <typename TB>
-__global__ __launch_bounds__(1024) void k_mm(int M, int N, int K, const float* a, int64_t a_si, int64_t a_sk,
-                                            const TB* b, int64_t b_sk, int64_t b_sj, float* c, int64_t c_si,
-                                            int accumulate) {
+__global__ __launch_bounds__(1024) void k_mm(int M, int N, int K, MmSeg sg, int64_t a_si, int64_t a_sk,
+                                            int64_t b_sk, int64_t b_sj, int64_t c_si, int accumulate) {
   constexpr int KG = 8;
   __shared__ float As[KG][16][17], Bs[KG][16][17];
   __shared__ float red[KG - 1][256];
@@ -66,70 +77,89 @@ __global__ __launch_bounds__(1024) void k_mm(int M, int N, int K, const float* a
   const int tx = t & 7, ty = t >> 3;  // outputs (ty, 2 tx) and (ty, 2 tx + 1)
   const int i0 = blockIdx.y * 16, j0 = blockIdx.x * 16;
   const bool a_k_fast = a_sk == 1, b_j_fast = b_sj == 1;
-  // tile loads: element e = t + 128 h (h < 2) of a 16 x 16 tile, fastest index e % 16
-  auto lda = [&](int k0, int h) {
-    const int e = t + 128 * h, f = e & 15, o = e >> 4;
-    const int i = i0 + (a_k_fast ? o : f), k = k0 + (a_k_fast ? f : o);
-    return (i < M && k < K) ? a[(int64_t)i * a_si + (int64_t)k * a_sk] : 0.f;
-  };
-  auto ldb = [&](int k0, int h) {
-    const int e = t + 128 * h, f = e & 15, o = e >> 4;
-    const int k = k0 + (b_j_fast ? o : f), j = j0 + (b_j_fast ? f : o);
-    return (k < K && j < N) ? to_f<TB>(b[(int64_t)k * b_sk + (int64_t)j * b_sj]) : 0.f;
-  };
-  auto sta = [&](int h, float v) {
-    const int e = t + 128 * h, f = e & 15, o = e >> 4;
-    if (a_k_fast) As[q][o][f] = v;
-    else As[q][f][o] = v;
-  };
-  auto stb = [&](int h, float v) {
-    const int e = t + 128 * h, f = e & 15, o = e >> 4;
-    if (b_j_fast) Bs[q][o][f] = v;
-    else Bs[q][f][o] = v;
-  };
-  const int nst = (K + 15) / 16;
-  const int steps = (nst + KG - 1) / KG;  // the same trip count in every group (barriers)
-  float acc0 = 0.f, acc1 = 0.f;
-  float an0 = lda(16 * q, 0), an1 = lda(16 * q, 1), bn0 = ldb(16 * q, 0), bn1 = ldb(16 * q, 1);
-  for (int s = 0; s < steps; ++s) {
-    const int k0 = 16 * (q + KG * s);
-    sta(0, an0);
-    sta(1, an1);
-    stb(0, bn0);
-    stb(1, bn1);
-    __syncthreads();
-    if (s + 1 < steps) {
-      an0 = lda(k0 + 16 * KG, 0);
-      an1 = lda(k0 + 16 * KG, 1);
-      bn0 = ldb(k0 + 16 * KG, 0);
-      bn1 = ldb(k0 + 16 * KG, 1);
-    }
-    if (k0 < K) {
+  const int seg0 = sg.sum ? 0 : blockIdx.z, seg1 = sg.sum ? sg.nseg : blockIdx.z + 1;
+  float* c = sg.c[sg.sum ? 0 : blockIdx.z];
+  float out0 = 0.f, out1 = 0.f;  // running output of the summed segments
+  for (int sgi = seg0; sgi < seg1; ++sgi) {
+    const float* a = sg.a[sgi];
+    const TB* b = (const TB*)sg.b[sgi];
+    // tile loads: element e = t + 128 h (h < 2) of a 16 x 16 tile, fastest index e % 16
+    auto lda = [&](int k0, int h) {
+      const int e = t + 128 * h, f = e & 15, o = e >> 4;
+      const int i = i0 + (a_k_fast ? o : f), k = k0 + (a_k_fast ? f : o);
+      return (i < M && k < K) ? a[(int64_t)i * a_si + (int64_t)k * a_sk] : 0.f;
+    };
+    auto ldb = [&](int k0, int h) {
+      const int e = t + 128 * h, f = e & 15, o = e >> 4;
+      const int k = k0 + (b_j_fast ? o : f), j = j0 + (b_j_fast ? f : o);
+      return (k < K && j < N) ? to_f<TB>(b[(int64_t)k * b_sk + (int64_t)j * b_sj]) : 0.f;
+    };
+    auto sta = [&](int h, float v) {
+      const int e = t + 128 * h, f = e & 15, o = e >> 4;
+      if (a_k_fast) As[q][o][f] = v;
+      else As[q][f][o] = v;
+    };
+    auto stb = [&](int h, float v) {
+      const int e = t + 128 * h, f = e & 15, o = e >> 4;
+      if (b_j_fast) Bs[q][o][f] = v;
+      else Bs[q][f][o] = v;
+    };
+    const int nst = (K + 15) / 16;
+    const int steps = (nst + KG - 1) / KG;  // the same trip count in every group (barriers)
+    float acc0 = 0.f, acc1 = 0.f;
+    float an0 = lda(16 * q, 0), an1 = lda(16 * q, 1), bn0 = ldb(16 * q, 0), bn1 = ldb(16 * q, 1);
+    for (int s = 0; s < steps; ++s) {
+      const int k0 = 16 * (q + KG * s);
+      sta(0, an0);
+      sta(1, an1);
+      stb(0, bn0);
+      stb(1, bn1);
+      __syncthreads();
+      if (s + 1 < steps) {
+        an0 = lda(k0 + 16 * KG, 0);
+        an1 = lda(k0 + 16 * KG, 1);
+        bn0 = ldb(k0 + 16 * KG, 0);
+        bn1 = ldb(k0 + 16 * KG, 1);
+      }
+      if (k0 < K) {
 #pragma unroll
-      for (int kk = 0; kk < 16; ++kk) {
-        const float av = As[q][ty][kk];
-        acc0 = fmaf(av, Bs[q][kk][2 * tx], acc0);
-        acc1 = fmaf(av, Bs[q][kk][2 * tx + 1], acc1);
+        for (int kk = 0; kk < 16; ++kk) {
+          const float av = As[q][ty][kk];
+          acc0 = fmaf(av, Bs[q][kk][2 * tx], acc0);
+          acc1 = fmaf(av, Bs[q][kk][2 * tx + 1], acc1);
+        }
+      }
+      __syncthreads();
+    }
+    if (q > 0) {
+      red[q - 1][2 * t] = acc0;
+      red[q - 1][2 * t + 1] = acc1;
+    }
+    __syncthreads();
+    if (q == 0) {
+#pragma unroll
+      for (int g = 0; g < KG - 1; ++g) {
+        acc0 += red[g][2 * t];
+        acc1 += red[g][2 * t + 1];
+      }
+      const int i = i0 + ty, j = j0 + 2 * tx;
+      if (i < M) {
+        const float* p = c + (int64_t)i * c_si + j;
+        const bool first = sgi == seg0;
+        // the first segment starts from the output (accumulate) or zero;
+        // later ones add to the running value
+        if (j < N) out0 = first ? (accumulate ? p[0] + acc0 : acc0) : out0 + acc0;
+        if (j + 1 < N) out1 = first ? (accumulate ? p[1] + acc1 : acc1) : out1 + acc1;
       }
     }
-    __syncthreads();
+    __syncthreads();  // red is reused by the next segment
   }
-  if (q > 0) {
-    red[q - 1][2 * t] = acc0;
-    red[q - 1][2 * t + 1] = acc1;
-  }
-  __syncthreads();
   if (q == 0) {
-#pragma unroll
-    for (int g = 0; g < KG - 1; ++g) {
-      acc0 += red[g][2 * t];
-      acc1 += red[g][2 * t + 1];
-    }
     const int i = i0 + ty, j = j0 + 2 * tx;
     if (i < M) {
       float* p = c + (int64_t)i * c_si + j;
-      if (j < N) p[0] = accumulate ? p[0] + acc0 : acc0;
-      if (j + 1 < N) p[1] = accumulate ? p[1] + acc1 : acc1;
+      if (j < N) p[0] = out0;
+      if (j + 1 < N) p[1] = out1;
     }
   }
 }
@@ -445,16 +475,52 @@ inline unsigned nblk(int64_t n) { return (unsigned)((n + 255) / 256); }
 
 }  // namespace
 
+static void mm_launch(int M, int N, int K, const MmSeg& sg, int64_t a_si, int64_t a_sk, int bdt, int64_t b_sk,
+                      int64_t b_sj, int64_t c_si, bool accumulate, hipStream_t s) {
+  if (M <= 0 || N <= 0 || sg.nseg <= 0) return;
+  dim3 grid((N + 15) / 16, (M + 15) / 16, sg.sum ? 1 : sg.nseg);
+  if (bdt)
+    hipLaunchKernelGGL(k_mm<uint16_t>, grid, dim3(1024), 0, s, M, N, K, sg, a_si, a_sk, b_sk, b_sj, c_si,
+                       (int)accumulate);
+  else
+    hipLaunchKernelGGL(k_mm<float>, grid, dim3(1024), 0, s, M, N, K, sg, a_si, a_sk, b_sk, b_sj, c_si,
+                       (int)accumulate);
+}
+
 void mm(int M, int N, int K, const float* a, int64_t a_si, int64_t a_sk, const void* b, int bdt, int64_t b_sk,
         int64_t b_sj, float* c, int64_t c_si, bool accumulate, hipStream_t s) {
-  if (M <= 0 || N <= 0) return;
-  dim3 grid((N + 15) / 16, (M + 15) / 16);
-  if (bdt)
-    hipLaunchKernelGGL(k_mm<uint16_t>, grid, dim3(1024), 0, s, M, N, K, a, a_si, a_sk, (const uint16_t*)b, b_sk, b_sj, c,
-                       c_si, (int)accumulate);
-  else
-    hipLaunchKernelGGL(k_mm<float>, grid, dim3(1024), 0, s, M, N, K, a, a_si, a_sk, (const float*)b, b_sk, b_sj, c,
-                       c_si, (int)accumulate);
+  MmSeg sg{};
+  sg.a[0] = a;
+  sg.b[0] = b;
+  sg.c[0] = c;
+  sg.nseg = 1;
+  mm_launch(M, N, K, sg, a_si, a_sk, bdt, b_sk, b_sj, c_si, accumulate, s);
+}
+
+void mm_outputs(int nseg, int M, int N, int K, const float* a, int64_t a_si, int64_t a_sk, const void* const* b,
+                int bdt, int64_t b_sk, int64_t b_sj, float* const* c, int64_t c_si, bool accumulate, hipStream_t s) {
+  MmSeg sg{};
+  for (int i = 0; i < nseg && i < 3; ++i) {
+    sg.a[i] = a;
+    sg.b[i] = b[i];
+    sg.c[i] = c[i];
+  }
+  sg.nseg = nseg < 3 ? nseg : 3;
+  mm_launch(M, N, K, sg, a_si, a_sk, bdt, b_sk, b_sj, c_si, accumulate, s);
+}
+
+void mm_summed(int nseg, int M, int N, int K, const float* const* a, int64_t a_si, int64_t a_sk,
+               const void* const* b, int bdt, int64_t b_sk, int64_t b_sj, float* c, int64_t c_si, bool accumulate,
+               hipStream_t s) {
+  MmSeg sg{};
+  for (int i = 0; i < nseg && i < 3; ++i) {
+    sg.a[i] = a[i];
+    sg.b[i] = b[i];
+  }
+  sg.c[0] = c;
+  sg.nseg = nseg < 3 ? nseg : 3;
+  sg.sum = 1;
+  mm_launch(M, N, K, sg, a_si, a_sk, bdt, b_sk, b_sj, c_si, accumulate, s);
 }
 
 void rms_fwd(const float* x, int64_t ldx, const float* gain, float* y, int64_t ldy, float* rstd, int n, int d,

@@ -225,9 +225,11 @@ int replay_backward(const Model& m, const rlt_backward_io* io, const rlt_grads* 
       rms_fwd(z, d, m.norm_s[l], hs, d, at(RS, l, t), n, d, c.rms_eps, s);
       float* kt = kt_at(KT, l, t);
       float* vt = kt_at(VT, l, t);
-      lin(n, d, d, hs, d, m.wq[l], q, d, false);
-      lin(n, d, d, hs, d, m.wk[l], kt, d, false);
-      lin(n, d, d, hs, d, m.wv[l], vt, d, false);
+      {  // q, k, v in one launch
+        const void* wt[3] = {m.wq[l], m.wk[l], m.wv[l]};
+        float* ys[3] = {q, kt, vt};
+        mm_outputs(3, n, d, d, hs, d, 1, wt, dt, 1, d, ys, d, false, s);
+      }
       if (rope_on) {
         rope(q, d, n, d, dh, t, m.inv_freq, 1, s);
         rope(kt, d, n, d, dh, t, m.inv_freq, 1, s);
@@ -244,8 +246,11 @@ int replay_backward(const Model& m, const rlt_backward_io* io, const rlt_grads* 
       lin(n, d, d, om, d, m.wom[l], za, d, true);
       // SwiGLU FFN [eq. (2.16)]
       rms_fwd(za, d, m.norm_d[l], hd, d, at(RS, 2 * L + l, t), n, d, c.rms_eps, s);
-      lin(n, F, d, hd, d, m.w_gate[l], ga, F, false);
-      lin(n, F, d, hd, d, m.w_up[l], gu, F, false);
+      {  // gate and up in one launch
+        const void* wt[2] = {m.w_gate[l], m.w_up[l]};
+        float* ys[2] = {ga, gu};
+        mm_outputs(2, n, F, d, hd, d, 1, wt, dt, 1, d, ys, F, false, s);
+      }
       swiglu_fwd(ga, gu, act, n, F, s);
       float* zn = at(ZIN, l + 1, t);
       add(zn, d, za, d, nullptr, 0, n, d, s);
@@ -334,8 +339,11 @@ int replay_backward(const Model& m, const rlt_backward_io* io, const rlt_grads* 
       lin_dx(n, d, F, dzF, d, m.w_down[l], dF1, F, false);
       swiglu_bwd(at(GA, l, t), at(GU, l, t), dF1, dF2, dF3, n, F, s);
       float* t1d = at(T1D, l, t);
-      lin_dx(n, F, d, dF2, F, m.w_gate[l], t1d, d, false);
-      lin_dx(n, F, d, dF3, F, m.w_up[l], t1d, d, true);
+      {  // t1d = dF2 W_gate + dF3 W_up, one launch
+        const float* dys[2] = {dF2, dF3};
+        const void* wt[2] = {m.w_gate[l], m.w_up[l]};
+        mm_summed(2, n, d, F, dys, F, 1, wt, dt, d, 1, t1d, d, false, s);
+      }
       colsum_at(layer_ptr(gr->norm_d, l), t1d, d, za, d, at(RS, 2 * L + l, t), n);
       rms_bwd(za, d, m.norm_d[l], at(RS, 2 * L + l, t), t1d, d, dzX, d, n, d, false, s, dzF, d);
       // cross-attention: za = zb + W_om om
@@ -367,9 +375,11 @@ int replay_backward(const Model& m, const rlt_backward_io* io, const rlt_grads* 
         rope(dk, d, n, d, dh, t, m.inv_freq, -1, s);
       }
       float* t2s = at(T2S, l, t);
-      lin_dx(n, d, d, dqs, d, m.wq[l], t2s, d, false);
-      lin_dx(n, d, d, dk, d, m.wk[l], t2s, d, true);
-      lin_dx(n, d, d, dv, d, m.wv[l], t2s, d, true);
+      {  // t2s = dq W_q + dk W_k + dv W_v, one launch
+        const float* dys[3] = {dqs, dk, dv};
+        const void* wt[3] = {m.wq[l], m.wk[l], m.wv[l]};
+        mm_summed(3, n, d, d, dys, d, 1, wt, dt, d, 1, t2s, d, false, s);
+      }
       colsum_at(layer_ptr(gr->norm_s, l), t2s, d, z, d, at(RS, l, t), n);
       rms_bwd(z, d, m.norm_s[l], at(RS, l, t), t2s, d, dzN, d, n, d, false, s, dzS, d);
     }
