@@ -304,6 +304,26 @@ def test_reference_depth_bench_configuration():
     top.check()
 
 
+@pytest.mark.timeout(900)
+def test_reference_width_one_row_chunks_merged_in_launch():
+    """Reference width (d=2048, 16x128 heads, W=256, a 4096-position memory)
+    with L_D=4, one row at t = 3000..3002: a one-row context splits the prefix
+    into 256-position chunks (12 of its 16) and merges them inside the
+    cross-attention launch; against both oracles, and bit-identical to the
+    same steps merged by the combine kernel [RLT §2.5 eq. (2.15)]."""
+    require_gpu()
+    wl = synth.REF.with_(L=4)
+    out = _prefilled(wl, 1, 3000, (0,), nsteps=3)
+    ker = _prefilled(wl, 1, 3000, (0,), nsteps=3, launch={"xattn_combine_kernel": 1})
+    assert np.array_equal(out["S"], ker["S"]) and np.array_equal(out["Z"], ker["Z"])
+    orc, emu = _oracles(wl, out["raw"])
+    top = Top1("reference width, one row, t~3000")
+    for b, (So, Zo, Ze) in _oracle_rows(wl, out, 3, orc, emu).items():
+        for i in range(3):
+            top.add(out["S"][i, b], out["Z"][i, b], So[i], Zo[i], Ze[i], (b, i))
+    top.check()
+
+
 @pytest.mark.timeout(1200)
 def test_ragged_workload_prefilled_at_shape():
     """Ragged RL workload dimensions (L_D=24, d=1536, 12x128, W=512 so the
