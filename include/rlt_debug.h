@@ -60,6 +60,9 @@ typedef struct rlt_dbg_launch {
                            kernel, 2 always inside the launch */
   int32_t one_row_pf;   /* weight chunks in flight per wave in one-row products, 2 .. 4
                            (other values: the default; timing only, same results) */
+  int32_t no_lt_dma;    /* 1: the staged product tile of 64 x 128 stages its chunks through
+                           registers (three LDS buffers) instead of copying them from memory
+                           straight into LDS (four buffers; same summation order, same results) */
   int32_t bwd_activations; /* rlt_replay_backward: 0 keep every step's activations when they
                            fit a quarter of the free device memory, else recompute them per step;
                            1 always recompute; 2 always keep (same results) */

@@ -112,7 +112,8 @@ class rlt_dbg_launch(C.Structure):
     _fields_ = [("xattn_chunk", i32), ("swa_hpw", i32), ("xattn_hpw", i32), ("fused_rows", i32),
                 ("no_packed", i32), ("one_term", i32), ("replay_graph_min", i32),
                 ("no_big_tile", i32), ("xattn_combine_kernel", i32),
-                ("one_row_pf", i32), ("bwd_activations", i32)]
+                ("one_row_pf", i32), ("no_lt_dma", i32),
+                ("bwd_activations", i32)]
 
 
 _lib = None

@@ -878,6 +878,205 @@ __global__ __launch_bounds__(512) void k_gemm_bf16_lt(GemmArgs g, Epi<uint16_t> 
   }
 }
 
+// The staged tile of 64 rows x 4 column pairs (RBK = 2 of k_gemm_bf16_lt)
+// with each chunk copied from memory straight into LDS (global_load_lds,
+// 16 bytes per lane: a wave's copy writes 1 KB of consecutive LDS, the layout
+// k_gemm_bf16_lt writes from registers) and four LDS buffers: chunk i + 3 is
+// requested while chunk i is multiplied and chunk i + 1's fragments are read,
+// so a chunk's copy has two chunk times to land, and no register set or LDS
+// write instruction stages it. The chunk's closing barrier waits for this
+// wave's copy of chunk i + 2 (chunk i + 3's may stay in flight) and, as in
+// k_gemm_bf16_lt, leaves the NF fragment reads of chunk i + 1 outstanding:
+// they target buffer (i + 1) % 4, which the next copy into it (chunk i + 5,
+// requested in chunk i + 2, after two more barriers) cannot overtake.
+// Buffer (i + 3) % 4 = (i - 1) % 4 is free when chunk i starts: its last
+// reads (chunk i - 1's fragments, issued in chunk i - 2) completed before
+// the barrier that closed chunk i - 1. The buffers are four LDS arrays
+// indexed at compile time (the chunk loop is unrolled by four), so that the
+// compiler can tell a copy in flight from the fragment reads of another
+// buffer and does not wait for the copy before them. Same fragments, MFMAs
+// and stream folds in the same order as k_gemm_bf16_lt: the same bits.
+// grid and block as k_gemm_bf16_lt with RBK = 2.
+constexpr int CPOL_NT = 2;  // cache-policy operand of global_load_lds: non-temporal
+template <int Q, bool TWO>
+__global__ __launch_bounds__(512) void k_gemm_bf16_ltd(GemmArgs g, Epi<uint16_t> epi) {
+  constexpr int RBK = 2, NT = 512, R = 32 * RBK, NCB = 8 / RBK, G = 8 / Q, TERMS = TWO ? 2 : 1;
+  constexpr int NF = 4 * (TERMS + 1), NB = 4;
+  constexpr int A_PIECES = RBK * TERMS * 256, PIECES = A_PIECES + NCB * 256, PPT = PIECES / NT;
+  static_assert(PIECES % NT == 0, "16-byte pieces per thread");
+  constexpr int TILE = RBK * NCB * 16 * 64;
+  constexpr bool RED_IN_STAGE = TILE * 4 <= PIECES * 16;  // the epilogue's block sums fit buffer 0
+  __shared__ u32x4_t st0[PIECES], st1[PIECES], st2[PIECES], st3[PIECES];
+  __shared__ float red_own[RED_IN_STAGE ? 1 : TILE];
+  __shared__ float s_rstd[R];
+  __shared__ float s_part[rowrstd_lds<R, NT>()];
+  const int mtiles = (g.M + R - 1) / R, ntiles = g.npairs / NCB;
+  const int b = blockIdx.x, q = b >> 3, per = mtiles * G;
+  const int sub = q % per, nt = 8 * (q / per) + (b & 7);
+  if (nt >= ntiles) return;  // whole workgroup, before any barrier
+  const int mt = sub / G, grp = sub - mt * G;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int m0 = mt * R, nchunk = g.K >> 6;
+  const int lastblk = (g.M - 1) >> 5;
+  // this thread's pieces (piece tid + NT k of a stage buffer): global element
+  // offsets at chunk 0 (a chunk adds 4 KB)
+  const uint16_t* gp[PPT];
+#pragma unroll
+  for (int k = 0; k < PPT; ++k) {
+    const int pc = tid + NT * k;
+    if (pc < A_PIECES) {
+      const int rbk = pc / (TERMS * 256), rem = pc - rbk * TERMS * 256, term = rem >> 8, sl = rem & 255;
+      const int blk = mt * RBK + rbk < lastblk ? mt * RBK + rbk : lastblk;
+      gp[k] = (const uint16_t*)g.A + (term ? g.a_lo : 0) + ((int64_t)blk * nchunk * 256 + sl) * 8;
+    } else {
+      const int pw = pc - A_PIECES, cbk = pw >> 8, sl = pw & 255;
+      gp[k] = (const uint16_t*)g.Wp + ((int64_t)(nt * NCB + cbk) * nchunk * 256 + sl) * 8;
+    }
+  }
+  const bool norm_here = (Q == 8) && g.ssq_in != nullptr;
+  const int cb = stream_begin(nchunk, grp * Q), ce = stream_begin(nchunk, grp * Q + Q), n = ce - cb;
+  const int clast = n > 0 ? ce - 1 : cb;
+  auto sbuf = [&](int buf) __attribute__((always_inline)) -> u32x4_t* {
+    return buf == 0 ? st0 : buf == 1 ? st1 : buf == 2 ? st2 : st3;
+  };
+  static_assert(NB == 4, "four buffers");
+  // chunk cb + i (clamped) into LDS buffer `buf`; the weights (read once
+  // per call) streamed past the caches
+  auto copy = [&](int buf, int i) __attribute__((always_inline)) {
+    const int c = cb + i < clast ? cb + i : clast;
+    u32x4_t* dst = sbuf(buf);
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+      if (k * NT >= A_PIECES)
+        __builtin_amdgcn_global_load_lds((const void*)(gp[k] + (int64_t)c * 2048),
+                                         (__attribute__((address_space(3))) void*)(dst + NT * k + wv * 64), 16, 0,
+                                         CPOL_NT);
+      else
+        __builtin_amdgcn_global_load_lds((const void*)(gp[k] + (int64_t)c * 2048),
+                                         (__attribute__((address_space(3))) void*)(dst + NT * k + wv * 64), 16, 0, 0);
+    }
+  };
+  u32x4_t fr[2][NF];  // one chunk's fragments of this wave, from LDS
+  const int rw = wave / NCB, cw = wave % NCB;
+  auto frag = [&](int f, int buf) __attribute__((always_inline)) {
+    const u32x4_t* sa = sbuf(buf) + rw * TERMS * 256 + lane;
+    const u32x4_t* sw = sbuf(buf) + A_PIECES + cw * 256 + lane;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      fr[f][s * (TERMS + 1)] = sa[s * 64];
+      if (TWO) fr[f][s * (TERMS + 1) + 1] = sa[256 + s * 64];
+      fr[f][s * (TERMS + 1) + TERMS] = sw[s * 64];
+    }
+  };
+  f32x16_t r, st[fold_levels<Q>()];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) r[e] = 0.f;
+  auto mma = [&](int f) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const bf16x8_t w = __builtin_bit_cast(bf16x8_t, fr[f][s * (TERMS + 1) + TERMS]);
+      r = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fr[f][s * (TERMS + 1)]), w, r, 0, 0, 0);
+      if (TWO)
+        r = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fr[f][s * (TERMS + 1) + 1]), w, r, 0, 0,
+                                                    0);
+    }
+  };
+  int j = 0, nb = stream_begin(nchunk, grp * Q + 1);
+  auto fold_until = [&](int c) __attribute__((always_inline)) {
+    while (j < Q && nb <= c) {
+      stream_fold<Q>(j, r, st);
+      ++j;
+      nb = stream_begin(nchunk, grp * Q + j + 1);
+    }
+  };
+  // the row statistics' loads go first and stay in registers through the
+  // loop (it stages nothing in registers); then chunks 0, 1, 2 are requested
+  GemmArgs gs = g;
+  if (!norm_here) gs.ssq_in = nullptr;
+  RowRstd<R, NT> rr(gs, m0);
+  copy(0, 0);
+  copy(1, 1);
+  copy(2, 2);
+  // s_waitcnt immediates (gfx9 encoding) that wait for vmcnt only: the
+  // compiler sees them, so it knows which copies have landed and inserts no
+  // wait of its own before the fragment reads
+  constexpr int VM_PPT = 0xF70 | (PPT & 15) | ((PPT >> 4) << 14), VM_0 = 0xF70;
+  // chunks 0 and 1 in LDS for every wave (chunk 0 is multiplied and chunk
+  // 1's fragments are read in the first chunk; chunk 2 may be in flight)
+  __builtin_amdgcn_s_waitcnt(VM_PPT);
+  __builtin_amdgcn_s_barrier();
+  frag(0, 0);
+  // chunk i, u = i % 4 (a compile-time constant); more: chunk i + 3 exists
+  auto chunk = [&](int u, int i, bool more) __attribute__((always_inline)) {
+    fold_until(cb + i);
+    if (more) copy((u + 3) & 3, i + 3);
+    frag((u + 1) & 1, (u + 1) & 3);
+    mma(u & 1);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, TERMS + 1, 0);  // fragment reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA
+    }
+    static_assert(NF <= 15, "lgkmcnt field");
+    if (more)
+      __builtin_amdgcn_s_waitcnt(VM_PPT);
+    else
+      __builtin_amdgcn_s_waitcnt(VM_0);
+    asm volatile("s_waitcnt lgkmcnt(%0)\n\ts_barrier" ::"n"(NF) : "memory");
+  };
+  int i = 0;
+  for (; i + 7 <= n; i += 4) {  // every chunk of these four requests chunk i + u + 3
+#pragma unroll
+    for (int u = 0; u < 4; ++u) chunk(u, i + u, true);
+  }
+  for (; i < n; i += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i + u < n) chunk(u, i + u, i + u + 3 < n);
+  }
+  __syncthreads();      // every wave's fragment reads done before the stage buffers are reused
+  fold_until(ce + 1);  // the group's remaining streams (empty ones included)
+  if (Q < 8) {
+    // group sum of block (rw, cw), rows below M, to the partial buffer
+    int ba, bbk;
+    pair_blocks(g, nt * NCB + cw, ba, bbk);
+    const int col = (lane & 16) ? bbk * 16 + (lane & 15) : ba * 16 + (lane & 15);
+    float* P = g.partial + (int64_t)grp * g.M_pad * g.Nv + col;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int m = m0 + rw * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+      if (m < g.M) P[(int64_t)m * g.Nv] = r[e];
+    }
+    return;
+  }
+  float* red = RED_IN_STAGE ? (float*)st0 : red_own;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) red[((rw * NCB + cw) * 16 + e) * 64 + lane] = r[e];
+  if (norm_here) {  // uniform branch: contains barriers
+    rr.finish(g, m0, s_part, s_rstd);
+  }
+  __syncthreads();
+  constexpr int NU = R * NCB, NG = NT / 16, NI = NU / NG;
+  const int c16 = tid & 15, grp16 = tid >> 4;
+  for (int jj = 0; jj < NI; ++jj) {
+    const int it = grp16 + NG * jj;
+    const int row = it / NCB, pc = it - row * NCB;
+    const int m = m0 + row, pair = nt * NCB + pc;
+    const int r32 = row & 31;
+    const int ia = (((row >> 5) * NCB + pc) * 16 + 4 * (r32 >> 3) + (r32 & 3)) * 64 + ((r32 >> 2) & 1) * 32 + c16;
+    int ba, bbk;
+    pair_blocks(g, pair, ba, bbk);
+    float sq = 0.f;
+    if (m < g.M) sq = epi(m, ba * 16 + c16, red[ia], bbk * 16 + c16, red[ia + 16], norm_here ? s_rstd[row] : 1.f);
+    if (g.ssq_out) {
+      sq = sum16(sq);
+      if (c16 == 0 && m < g.M) g.ssq_out[(int64_t)pair * g.M_pad + m] = sq;
+    }
+  }
+}
+
 // Combine the G group sums of k_gemm_bf16_lt by the stream tree's top levels
 // (neighbours, then pairs 2 apart, then 4 apart) and apply the epilogue.
 // grid: (pairs, 16-row tiles); block 256 (16 rows x 16 columns of a pair).
@@ -1033,9 +1232,15 @@ void launch_gemm(int dtype, const GemmArgs& g0, const EpiArgs& e, hipStream_t s)
     if (two) hipLaunchKernelGGL((k_gemm_bf16_lt<Q_, true, RBK_>), grid, dim3(512), 0, s, g, epi);     \
     else hipLaunchKernelGGL((k_gemm_bf16_lt<Q_, false, RBK_>), grid, dim3(512), 0, s, g, epi);        \
   } while (0)
+#define RLT_LTD(Q_)                                                                                   \
+  do {                                                                                                \
+    if (two) hipLaunchKernelGGL((k_gemm_bf16_ltd<Q_, true>), grid, dim3(512), 0, s, g, epi);         \
+    else hipLaunchKernelGGL((k_gemm_bf16_ltd<Q_, false>), grid, dim3(512), 0, s, g, epi);            \
+  } while (0)
 #define RLT_LT(Q_)                       \
   do {                                   \
-    if (rbk == 2) RLT_LT2(Q_, 2);         \
+    if (rbk == 2 && g.lt_dma) RLT_LTD(Q_); \
+    else if (rbk == 2) RLT_LT2(Q_, 2);    \
     else RLT_LT2(Q_, 4);                  \
   } while (0)
       switch (G) {
@@ -1045,6 +1250,7 @@ void launch_gemm(int dtype, const GemmArgs& g0, const EpiArgs& e, hipStream_t s)
         default: RLT_LT(1); break;
       }
 #undef RLT_LT
+#undef RLT_LTD
 #undef RLT_LT2
       if (G > 1) {
         dim3 g2(g.npairs, (g.M + 15) / 16);

@@ -141,6 +141,7 @@ struct rlt_ctx {
   int* tick_dev;        // replay: the current tick, advanced on the device
   int replay_graph_min;  // replay: runs of at least this many ticks of one active set are captured (0: never)
   bool big_tile;         // the memory construction's K/V product on the 256 x 256 tile
+  bool lt_dma;           // staged 64 x 128 product tile with its chunks copied straight into LDS
   double* inv_freq;
   float2* rope_tab;  // [rope_tmax + 1][d_head / 2] rotary (cos, sin)
   int rope_tmax;
@@ -591,6 +592,7 @@ static int create_ctx(const rlt_config* cfg, const rlt_weights* w, int32_t max_r
   c->one_term = o.one_term != 0;
   c->replay_graph_min = o.replay_graph_min < 0 ? 0 : (o.replay_graph_min > 0 ? o.replay_graph_min : 4);
   c->big_tile = o.no_big_tile == 0;
+  c->lt_dma = o.no_lt_dma == 0;
   c->xcomb_mode = (o.xattn_combine_kernel >= 0 && o.xattn_combine_kernel <= 2) ? o.xattn_combine_kernel : 0;
   c->one_row_pf = (o.one_row_pf >= 2 && o.one_row_pf <= 4) ? o.one_row_pf : 2;
   c->bwd_keep = (o.bwd_activations >= 0 && o.bwd_activations <= 2) ? o.bwd_activations : 0;
@@ -695,6 +697,7 @@ struct Gemm {
       g.pf = n > 32 ? 3 : 2;
       g.lt_groups = 0;
       g.lt_rbk = 4;
+      g.lt_dma = c->lt_dma ? 1 : 0;
       // one-row calls: activations staged in LDS (the K loop then issues
       // weight loads only; at 4 and 8 rows measured slower)
       g.a_lds = (n == 1 && K / 64 <= PK_LDS_CHUNKS) ? 1 : 0;

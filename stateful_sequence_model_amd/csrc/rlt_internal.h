@@ -112,6 +112,8 @@ struct GemmArgs {
   int lt_groups;          // fragment order, > 0: staged tile, this many workgroups
                           // per tile over the stream groups (1, 2, 4 or 8); 0: register tile
   int lt_rbk;             // staged tile: 32-row blocks per tile, 4 (128 x 64) or 2 (64 x 128)
+  int lt_dma;             // staged tile of 64 x 128: chunks copied straight into LDS (k_gemm_bf16_ltd;
+                          // else through registers, k_gemm_bf16_lt)
   int a_lds;              // register tile: 1 (M = 1, K <= 64 PK_LDS_CHUNKS): the
                           // activations staged in LDS for the whole K
   int pre;                // fragment-order tile: -1 = by epilogue kind, 0/1 = epilogue values after / before the K loop
@@ -183,13 +185,14 @@ struct RowRstd {
     for (int j = 0; j < RU; ++j) v[j] = 0.f;
     if (!g.ssq_in) return;  // uniform
     // no branches around the loads (rows clamped below M: those rows' rstd
-    // is never used; units clamped, then zeroed past the last)
+    // is never used; units clamped to the last one: units past it are
+    // staged but never read, reduce() stops at ssq_units), and no use of the
+    // values before they are staged, so the loads stay in flight until then
     const int m = m0 + row < g.M ? m0 + row : g.M - 1;
 #pragma unroll
     for (int j = 0; j < RU; ++j) {
       const int u = sl + PA * j;
-      const float x = g.ssq_in[(int64_t)(u < g.ssq_units ? u : g.ssq_units - 1) * g.M_pad + m];
-      v[j] = u < g.ssq_units ? x : 0.f;
+      v[j] = g.ssq_in[(int64_t)(u < g.ssq_units ? u : g.ssq_units - 1) * g.M_pad + m];
     }
   }
   // the loaded units to s_part (LDS [NU][R] floats)

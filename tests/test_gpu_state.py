@@ -266,6 +266,34 @@ def test_every_product_shape_bit_identical():
                 run.dec.close()
 
 
+def test_staged_tile_copied_straight_into_lds_bit_identical():
+    """The staged product tile of 64 rows x 4 column pairs with its chunks
+    copied from memory straight into LDS (the default) gives the bits of the
+    register-staged tile (launch option no_lt_dma): default shapes at 128 and
+    96 rows (one and two stream groups), and forced shapes over 1, 2, 4 and 8
+    groups (group lengths of 2 to 44 chunks, every tail of the four-chunk
+    loop), two and one activation terms."""
+    require_gpu()
+    from stateful_sequence_model_amd import _abi
+    wl = synth.MID.with_(T=24, L=2)
+    raw = synth.make_weights(wl)
+    for one in (0, 1):
+        for B in (96, 128):
+            base = GpuRun(wl, raw=raw, B=B, T=wl.T, launch={"one_term": one, "no_lt_dma": 1})
+            base.init()
+            S, Z = base.run(3)
+            base.dec.close()
+            for sh in (None, (1, 4, 1, 1, 0), (1, 4, 2, 1, 0), (1, 4, 4, 1, 0), (1, 4, 8, 1, 0)):
+                run = GpuRun(wl, raw=raw, B=B, T=wl.T, launch={"one_term": one})
+                if sh:
+                    _abi.check(_abi.rlt_dbg_product_shape(run.dec.ctx, *sh), "product shape")
+                run.init()
+                S2, Z2 = run.run(3)
+                assert run.dec.sync_error() == 0
+                assert np.array_equal(S2, S) and np.array_equal(Z2, Z), (one, B, sh)
+                run.dec.close()
+
+
 def test_one_term_activations_shapes_and_closeness():
     """The one-term activation mode (launch option one_term: the products'
     activations as one bf16 value, the kernels' single-term instantiations)

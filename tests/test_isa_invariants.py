@@ -10,7 +10,9 @@ every path into the barrier, at least NF LDS reads follow the last LDS
 write. The kernel asks the scheduler for that order; this test reads the
 compiler's output and checks it on the control-flow graph of every
 instantiation, so a compiler change cannot break the barrier's meaning
-unnoticed."""
+unnoticed. The tile that copies its chunks straight into LDS is checked
+likewise for its memory waits: each chunk's closing barrier may leave only
+the copy issued in that chunk in flight."""
 import os
 import re
 import shutil
@@ -122,6 +124,67 @@ def test_staged_tile_barrier_waits_cover_the_lds_writes(gemm_asm):
     assert seen == 16  # Q in 1, 2, 4, 8 with one and two activation terms, 128 x 64 and 64 x 128 tiles
 
 
+def _min_vmem_since_barrier(blocks, preds, k, pos, need):
+    """Walking back from instruction pos of block k over every path to the
+    previous barrier: the fewest memory instructions (global/buffer loads,
+    stores and LDS copies) issued on the way (need or more counts as
+    enough)."""
+    best, seen, stack = need, set(), [(k, pos, 0)]
+    while stack:
+        b, p, n = stack.pop()
+        ins = blocks[b][1]
+        hit = False
+        for q in range(p - 1, -1, -1):
+            x = ins[q]
+            if x.startswith("s_barrier"):
+                best = min(best, n)
+                hit = True
+                break
+            if x.startswith(("global_", "buffer_")):
+                n += 1
+                if n >= need:
+                    hit = True
+                    break
+        if hit:
+            continue
+        if not preds[b]:
+            best = min(best, n)
+        for pb in preds[b]:
+            key = (pb, n)
+            if key not in seen:
+                seen.add(key)
+                stack.append((pb, len(blocks[pb][1]), n))
+    return best
+
+
+def test_copied_staged_tile_barriers_leave_only_this_chunks_copy_in_flight(gemm_asm):
+    """The tile that copies its chunks straight into LDS closes each chunk
+    with s_waitcnt vmcnt(x), lgkmcnt(NF), s_barrier: the copy of the chunk
+    whose fragments the next chunk reads was issued before the previous
+    barrier, so it has landed once at most x memory operations remain -- as
+    long as, on every path from the previous barrier, at least x memory
+    instructions were issued (the copy issued in this chunk)."""
+    seen = 0
+    for name, body in _kernels(gemm_asm, r"_ZN3rlt15k_gemm_bf16_ltdILi\dELb\dEEEvNS_8GemmArgsENS_3EpiItEE"):
+        two = re.search(r"ILi\dELb(\d)", name).group(1) == "1"
+        nf = 4 * (3 if two else 2)
+        blocks, preds = _blocks(body)
+        closing = 0
+        for k, (_, ins) in enumerate(blocks):
+            for p, x in enumerate(ins):
+                if x.startswith("s_barrier") and p > 1 and ins[p - 1] == "s_waitcnt lgkmcnt(%d)" % nf:
+                    m = re.match(r"s_waitcnt vmcnt\((\d+)\)$", ins[p - 2])
+                    assert m, (name, "no vmcnt wait before a chunk barrier", ins[p - 2])
+                    x_left = int(m.group(1))
+                    closing += 1
+                    if x_left:
+                        r = _min_vmem_since_barrier(blocks, preds, k, p - 2, x_left)
+                        assert r >= x_left, (name, "a path with only %d memory operations since the last barrier" % r)
+        assert closing >= 2, (name, "chunk barriers not found")
+        seen += 1
+    assert seen == 8  # Q in 1, 2, 4, 8 with one and two activation terms
+
+
 def test_checker_finds_a_short_path():
     """The path walk itself: a loop whose header (laid out after the body)
     holds the LDS writes, once with enough reads after them and once with a
@@ -149,3 +212,27 @@ def test_checker_finds_a_short_path():
         blocks, preds = _blocks(listing(side))
         k, p = next((k, p) for k, (_, ins) in enumerate(blocks) for p, x in enumerate(ins) if x == "s_barrier")
         assert _min_reads_after_last_write(blocks, preds, k, p - 1, 4) == want
+
+
+def test_memory_count_walk_finds_a_short_path():
+    """The memory-operation walk: four copies between two barriers, once on
+    every path and once with a branch around two of them."""
+    def listing(skip):
+        return [
+            "\ts_barrier",
+            "\tglobal_load_lds_dwordx4 v[0:1], off",
+            "\tglobal_load_lds_dwordx4 v[2:3], off",
+            "\ts_cbranch_scc1 .LBB0_1" if skip else "\ts_nop 0",
+            "\tglobal_load_lds_dwordx4 v[4:5], off nt",
+            "\tglobal_load_lds_dwordx4 v[6:7], off nt",
+            ".LBB0_1:",
+            "\ts_waitcnt vmcnt(4)",
+            "\ts_waitcnt lgkmcnt(12)",
+            "\ts_barrier",
+            "\ts_endpgm",
+        ]
+    for skip, want in ((False, 4), (True, 2)):
+        blocks, preds = _blocks(listing(skip))
+        k, p = next((k, p) for k, (_, ins) in enumerate(blocks) for p, x in enumerate(ins)
+                    if x == "s_waitcnt vmcnt(4)")
+        assert _min_vmem_since_barrier(blocks, preds, k, p, 4) == want
