@@ -1036,7 +1036,11 @@ __global__ __launch_bounds__(512) void k_gemm_bf16_ltd(GemmArgs g, Epi<uint16_t>
     for (int u = 0; u < 4; ++u)
       if (i + u < n) chunk(u, i + u, i + u + 3 < n);
   }
-  __syncthreads();      // every wave's fragment reads done before the stage buffers are reused
+  // every copy landed (a group of fewer than three chunks leaves prologue
+  // copies in flight) and every wave's fragment reads done before the stage
+  // buffers are reused or the workgroup ends
+  __builtin_amdgcn_s_waitcnt(VM_0);
+  __syncthreads();
   fold_until(ce + 1);  // the group's remaining streams (empty ones included)
   if (Q < 8) {
     // group sum of block (rw, cw), rows below M, to the partial buffer

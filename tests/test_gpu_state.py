@@ -272,13 +272,18 @@ def test_staged_tile_copied_straight_into_lds_bit_identical():
     register-staged tile (launch option no_lt_dma): default shapes at 128 and
     96 rows (one and two stream groups), and forced shapes over 1, 2, 4 and 8
     groups (group lengths of 2 to 44 chunks, every tail of the four-chunk
-    loop), two and one activation terms."""
+    loop; at the small width, K of 256 and 704, groups of 0 and 1 chunks),
+    two and one activation terms."""
     require_gpu()
     from stateful_sequence_model_amd import _abi
-    wl = synth.MID.with_(T=24, L=2)
+    for wl, sizes in ((synth.MID.with_(T=24, L=2), (96, 128)), (synth.SMALL.with_(T=24, B=128), (128,))):
+        _copied_tile_case(_abi, wl, sizes)
+
+
+def _copied_tile_case(_abi, wl, sizes):
     raw = synth.make_weights(wl)
     for one in (0, 1):
-        for B in (96, 128):
+        for B in sizes:
             base = GpuRun(wl, raw=raw, B=B, T=wl.T, launch={"one_term": one, "no_lt_dma": 1})
             base.init()
             S, Z = base.run(3)
