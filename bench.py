@@ -276,6 +276,11 @@ def main():
                          "in turn (rlt_dbg_product_shape), against the library's own choice")
     ap.add_argument("--replay-max-len", type=int, default=1024,
                     help="replay mode: upper end of the uniform length draw (the preset's lower end kept)")
+    ap.add_argument("--replay-waves", type=int, default=1,
+                    help="replay mode: the sequences (longest first) replayed as this many calls of "
+                         "B / waves sequences each, whose dense memory [G][B/waves][T][d] is reused "
+                         "(the preset's full draw, U[64, 8192] over 256 sequences, needs 309 GB as one "
+                         "buffer: two waves fit one GPU); timed once, with graphs")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -595,6 +600,8 @@ def bench_replay(args, wl):
 
     wl = wl.with_(len_hi=min(wl.len_hi, args.replay_max_len)) if wl.ragged else wl
     lens, splits = synth.make_lengths(wl)
+    if args.replay_waves > 1:
+        return bench_replay_waves(args, wl, lens, splits)
     B, T, d, G = wl.B, int(lens.max()), wl.d, wl.G
     steps = max(1, min(args.steps, 3))
     torch.cuda.set_device(0)
@@ -642,6 +649,88 @@ def bench_replay(args, wl):
                    "max_len": T, "transitions": trans},
         "direct_launch_ms_per_call": round(res["direct"], 3),
         "graph_speedup": round(res["direct"] / ms, 3),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_replay_waves(args, wl, lens, splits):
+    """The replay of bench_replay at the preset's own length draw: sequences
+    sorted longest first and replayed in --replay-waves calls of B / waves
+    sequences (each call batches its own ragged set tick by tick, as the whole
+    batch would), through one context and one memory buffer sized for the
+    longest wave; value = all calls' transitions / their summed time."""
+    import numpy as np
+    import torch
+    import synth
+    from stateful_sequence_model_amd import Decoder, DecoderState, ModelConfig, _abi
+
+    nw = args.replay_waves
+    order = np.argsort(-lens, kind="stable")
+    B, d, G = wl.B, wl.d, wl.G
+    Bw = (B + nw - 1) // nw
+    T = int(lens.max())
+    torch.cuda.set_device(0)
+    raw = synth.make_weights(wl)
+    cfg = ModelConfig(L=wl.L, d=d, H=wl.H, dh=wl.dh, W=wl.W, G=G, F=wl.F, V=wl.V, dtype=wl.dtype,
+                      merge=wl.merge, alpha=wl.alpha, eps=wl.eps, rope_theta=wl.rope_theta, pos=wl.pos)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(wl.seed)
+    tdt = cfg.torch_dtype
+    log("replay waves: %d x %d sequences, T = %d, memory %.1f GB" % (nw, Bw, T, 2 * G * Bw * T * d * 2 / 1e9))
+    e = torch.empty((Bw, T, d), device="cuda", dtype=tdt).normal_(generator=gen)
+    mk = torch.empty((G, Bw, T, d), device="cuda", dtype=tdt)
+    mv = torch.empty((G, Bw, T, d), device="cuda", dtype=tdt)
+    for g in range(G):  # per group, so that no temporary of the whole buffer is needed
+        mk[g].normal_(generator=gen)
+        mv[g].normal_(generator=gen)
+    log("memory filled")
+    tokens = torch.randint(0, wl.V, (Bw, T), generator=gen, device="cuda", dtype=torch.int32)
+    logp = torch.empty((Bw, T), device="cuda")
+    dec = Decoder(cfg, raw, max_rows=Bw, max_ctx=T)
+    st = DecoderState(cfg, Bw)
+    stream = torch.cuda.Stream()
+    total_ms, trans, per_wave, alg = 0.0, 0, [], 0.0
+    with torch.cuda.stream(stream):
+        for w in range(nw):
+            idx = order[w * Bw:(w + 1) * Bw]
+            lw, sw = np.ascontiguousarray(lens[idx]), np.ascontiguousarray(splits[idx])
+            mem_len = torch.from_numpy(lw).cuda()  # kept alive: the memory struct holds its pointer
+            # the whole buffer's strides (a group spans Bw rows); the wave uses its first rows
+            mem = _abi.rlt_memory(mk.data_ptr(), mv.data_ptr(), Bw * T * d, T * d, d, mem_len.data_ptr())
+            stream.synchronize()
+            t0 = time.perf_counter()
+            _abi.check(dec.replay(st, lw, sw, e[:len(idx)], mem, tokens[:len(idx)], logp[:len(idx)],
+                                  stream=stream.cuda_stream), "replay")
+            stream.synchronize()
+            ms = (time.perf_counter() - t0) * 1e3
+            tw = int((lw - 1).sum())
+            # algorithmic bytes: the weights once per tick, each active row's
+            # retained window and memory prefix once per layer
+            wb = 0.0
+            for t in range(1, int(lw.max())):
+                n = int((lw - 1 >= t).sum())
+                wb += matrix_params(wl) * 2 + n * wl.L * (min(t - 1, wl.W - 1) + 1 + t) * 2 * d * 2
+            per_wave.append({"sequences": int(len(idx)), "lengths": [int(lw.min()), int(lw.max())],
+                             "transitions": tw, "ms": round(ms, 1), "algorithmic_bytes": int(wb),
+                             "achieved_GBs": round(wb / (ms / 1e3) / 1e9, 1)})
+            alg += wb
+            log("wave %d: %d sequences, lengths %d..%d, %d transitions in %.1f ms (%.1f transitions/s)"
+                % (w, len(idx), lw.min(), lw.max(), tw, ms, tw / (ms / 1e3)))
+            total_ms += ms
+            trans += tw
+    _abi.check(dec.sync_error(), "device error")
+    dec.close()
+    out = {
+        "metric": "replay transitions/sec (ragged, from H_0, seq*token)",
+        "value": round(trans / (total_ms / 1e3), 1), "unit": "transitions/s", "n_gpus": 1, "steps": 1,
+        "warmup": 0, "ms_per_step": round(total_ms, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name + " replay", "L_D": wl.L, "d": d, "heads": "%dx%d" % (wl.H, wl.dh),
+                   "W": wl.W, "G": G, "batch": B, "waves": nw, "lengths": "U[%d, %d]" % (wl.len_lo, wl.len_hi),
+                   "max_len": T, "transitions": trans},
+        "waves": per_wave,
+        "step_roofline": {"algorithmic_bytes": int(alg), "achieved_GBs": round(alg / (total_ms / 1e3) / 1e9, 1),
+                          "frac": round(alg / (total_ms / 1e3) / (HBM_PEAK_GBS * 1e9), 4)},
     }
     print(json.dumps(out), flush=True)
 
