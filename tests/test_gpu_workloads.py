@@ -309,11 +309,13 @@ def test_reference_width_one_row_chunks_merged_in_launch():
     """Reference width (d=2048, 16x128 heads, W=256, a 4096-position memory)
     with L_D=4, one row at t = 3000..3002: a one-row context splits the prefix
     into 256-position chunks (12 of its 16) and merges them inside the
-    cross-attention launch; against both oracles, and bit-identical to the
-    same steps merged by the combine kernel [RLT §2.5 eq. (2.15)]."""
+    cross-attention launch (steps replayed from one captured graph, so the
+    arrival counters must reset between replays); against both oracles, and
+    bit-identical to the same steps launched directly with the chunks merged
+    by the combine kernel [RLT §2.5 eq. (2.15)]."""
     require_gpu()
     wl = synth.REF.with_(L=4)
-    out = _prefilled(wl, 1, 3000, (0,), nsteps=3)
+    out = _prefilled(wl, 1, 3000, (0,), nsteps=3, graph=True)
     ker = _prefilled(wl, 1, 3000, (0,), nsteps=3, launch={"xattn_combine_kernel": 1})
     assert np.array_equal(out["S"], ker["S"]) and np.array_equal(out["Z"], ker["Z"])
     orc, emu = _oracles(wl, out["raw"])
