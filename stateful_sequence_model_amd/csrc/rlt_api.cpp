@@ -688,13 +688,14 @@ struct Gemm {
       // (64 with K of 4096 or more) take the staged tile (64 x 128 where the
       // columns allow), in one workgroup per tile from 150 tiles, else split
       // over two stream groups (four below 96 tiles); the others the
-      // register tile of 32 rows, two chunks in flight per wave (three past
-      // 32 rows)
+      // register tile of 32 rows, two chunks in flight per wave (three or
+      // four past 32 rows measured no faster: 64 rows 13.64 / 13.70 / 13.74
+      // ms per step with 2 / 3 / 4, 128 rows 21.73 / 21.75 / 21.77)
       g.Wp = Wp;
       g.rb = 1;
       g.cb = 1;
       g.pre = -1;
-      g.pf = n > 32 ? 3 : 2;
+      g.pf = 2;
       g.lt_groups = 0;
       g.lt_rbk = 4;
       g.lt_dma = c->lt_dma ? 1 : 0;
