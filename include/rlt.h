@@ -247,7 +247,10 @@ typedef struct rlt_ctx rlt_ctx;
  * memory again as those) in the operand order of the gfx950 32x32x16 bf16
  * matrix instruction, read by calls of more than 32 rows. The copy is made
  * here: after changing those weights in place, call rlt_refresh_weights
- * before the next call. Returns RLT_ENOMEM if it does not fit. */
+ * before the next call. Returns RLT_ENOMEM if it does not fit. The workspace
+ * (activations, partial sums, arrival counters that kernels reset for the
+ * next launch) is shared by every call on the context: calls on one context
+ * must not overlap (issue them on one stream, or order the streams). */
 int rlt_create(const rlt_config* cfg, const rlt_weights* w, int32_t max_rows, int32_t max_ctx,
                rlt_ctx** out);
 void rlt_destroy(rlt_ctx* ctx);
