@@ -20,6 +20,10 @@ namespace bwd {
 // B(k,j) = b[k*b_sk + j*b_sj] (element type bdt), C[i][j] at c[i*c_si + j].
 void mm(int M, int N, int K, const float* a, int64_t a_si, int64_t a_sk, const void* b, int bdt, int64_t b_sk,
         int64_t b_sj, float* c, int64_t c_si, bool accumulate, hipStream_t s);
+// C = base + A B (base with C's row stride): the bits of copying base to C
+// and then accumulating
+void mm_base(int M, int N, int K, const float* a, int64_t a_si, int64_t a_sk, const void* b, int bdt, int64_t b_sk,
+             int64_t b_sj, const float* base, float* c, int64_t c_si, hipStream_t s);
 // nseg (<= 3) products of one launch, each the same bits as its own mm call:
 // one A, B and C per segment (mm_outputs), or A and B per segment added into
 // one C in segment order (mm_summed: C (+)= A_0 B_0, then += A_1 B_1, ...)

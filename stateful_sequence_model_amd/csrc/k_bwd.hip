@@ -65,6 +65,7 @@ struct MmSeg {
   const void* b[3];
   float* c[3];
   int nseg, sum;
+  const float* base;  // if set: the first segment starts from base (row stride c_si) instead of C or zero
 };
 
 template <typename TB>
@@ -144,12 +145,12 @@ __global__ __launch_bounds__(1024) void k_mm(int M, int N, int K, MmSeg sg, int6
       }
       const int i = i0 + ty, j = j0 + 2 * tx;
       if (i < M) {
-        const float* p = c + (int64_t)i * c_si + j;
-        const bool first = sgi == seg0;
-        // the first segment starts from the output (accumulate) or zero;
-        // later ones add to the running value
-        if (j < N) out0 = first ? (accumulate ? p[0] + acc0 : acc0) : out0 + acc0;
-        if (j + 1 < N) out1 = first ? (accumulate ? p[1] + acc1 : acc1) : out1 + acc1;
+        const float* p = (sg.base ? sg.base : c) + (int64_t)i * c_si + j;
+        const bool first = sgi == seg0, from = accumulate || sg.base;
+        // the first segment starts from the output (accumulate), the base or
+        // zero; later ones add to the running value
+        if (j < N) out0 = first ? (from ? p[0] + acc0 : acc0) : out0 + acc0;
+        if (j + 1 < N) out1 = first ? (from ? p[1] + acc1 : acc1) : out1 + acc1;
       }
     }
     __syncthreads();  // red is reused by the next segment
@@ -495,6 +496,17 @@ void mm(int M, int N, int K, const float* a, int64_t a_si, int64_t a_sk, const v
   sg.c[0] = c;
   sg.nseg = 1;
   mm_launch(M, N, K, sg, a_si, a_sk, bdt, b_sk, b_sj, c_si, accumulate, s);
+}
+
+void mm_base(int M, int N, int K, const float* a, int64_t a_si, int64_t a_sk, const void* b, int bdt, int64_t b_sk,
+             int64_t b_sj, const float* base, float* c, int64_t c_si, hipStream_t s) {
+  MmSeg sg{};
+  sg.a[0] = a;
+  sg.b[0] = b;
+  sg.c[0] = c;
+  sg.nseg = 1;
+  sg.base = base;
+  mm_launch(M, N, K, sg, a_si, a_sk, bdt, b_sk, b_sj, c_si, false, s);
 }
 
 void mm_outputs(int nseg, int M, int N, int K, const float* a, int64_t a_si, int64_t a_sk, const void* const* b,

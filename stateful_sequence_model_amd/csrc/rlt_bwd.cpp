@@ -186,6 +186,9 @@ int replay_backward(const Model& m, const rlt_backward_io* io, const rlt_grads* 
   auto lin = [&](int n, int N, int K, const float* X, int64_t ldx, const void* Wt, float* Y, int64_t ldy, bool acc) {
     mm(n, N, K, X, ldx, 1, Wt, dt, 1, K, Y, ldy, acc, s);
   };
+  // Y[n][N] = base + X W^T (the residual add and the projection in one launch)
+  auto lin_res = [&](int n, int N, int K, const float* X, int64_t ldx, const void* Wt, const float* base, float* Y,
+                     int64_t ldy) { mm_base(n, N, K, X, ldx, 1, Wt, dt, 1, K, base, Y, ldy, s); };
   // dX[n][K] (+)= dY[n][N] W
   auto lin_dx = [&](int n, int N, int K, const float* dY, int64_t ldy, const void* Wt, float* dX, int64_t ldx, bool acc) {
     mm(n, K, N, dY, ldy, 1, Wt, dt, K, 1, dX, ldx, acc, s);
@@ -235,15 +238,13 @@ int replay_backward(const Model& m, const rlt_backward_io* io, const rlt_grads* 
         rope(kt, d, n, d, dh, t, m.inv_freq, 1, s);
       }
       attn_fwd(q, d, trace_kv(l), std::max(1, t - W + 1), t, o, d, n, H, dh, s);
-      add(zb, d, z, d, nullptr, 0, n, d, s);
-      lin(n, d, d, o, d, m.wo[l], zb, d, true);
+      lin_res(n, d, d, o, d, m.wo[l], z, zb, d);
       // cross-attention to M_{<=t} [eq. (2.15)]
       rms_fwd(zb, d, m.norm_m[l], hm, d, at(RS, L + l, t), n, d, c.rms_eps, s);
       lin(n, d, d, hm, d, m.wqm[l], qm, d, false);
       if (rope_on) rope(qm, d, n, d, dh, t, m.inv_freq, 1, s);
       attn_fwd(qm, d, mem_kv(l), 1, t, om, d, n, H, dh, s);
-      add(za, d, zb, d, nullptr, 0, n, d, s);
-      lin(n, d, d, om, d, m.wom[l], za, d, true);
+      lin_res(n, d, d, om, d, m.wom[l], zb, za, d);
       // SwiGLU FFN [eq. (2.16)]
       rms_fwd(za, d, m.norm_d[l], hd, d, at(RS, 2 * L + l, t), n, d, c.rms_eps, s);
       {  // gate and up in one launch
@@ -253,8 +254,7 @@ int replay_backward(const Model& m, const rlt_backward_io* io, const rlt_grads* 
       }
       swiglu_fwd(ga, gu, act, n, F, s);
       float* zn = at(ZIN, l + 1, t);
-      add(zn, d, za, d, nullptr, 0, n, d, s);
-      lin(n, d, F, act, F, m.w_down[l], zn, d, true);
+      lin_res(n, d, F, act, F, m.w_down[l], za, zn, d);
     }
   };
   // readout [eq. (2.6)]: log p and its gradient w (onehot - softmax)
