@@ -48,6 +48,9 @@ void colsum_rows(float* dst, const float* a, int64_t lda, const float* b, int64_
                  int d, hipStream_t s);
 // rotary transform of every head of n rows at position t (sign -1: inverse)
 void rope(float* x, int64_t ld, int n, int d, int dh, int t, const double* inv_freq, int sign, hipStream_t s);
+// the same on two distinct arrays of the same shape and position, one launch
+void rope2(float* x, float* x2, int64_t ld, int n, int d, int dh, int t, const double* inv_freq, int sign,
+           hipStream_t s);
 
 // Keys / values of one row over positions lo..hi (1-based): row r reads
 // base + row_off(r) + (j-1)*s_pos, row_off(r) = (map ? map[r] : r) * s_row.

@@ -215,8 +215,10 @@ __global__ __launch_bounds__(256) void k_colsum(float* dst, const float* a, int6
 }
 
 // thread per (row, head, i < dh/2): rotate (x_i, x_{i+dh/2}) by sign * t * w_i
-__global__ __launch_bounds__(256) void k_rope(float* x, int64_t ld, int n, int d, int dh, int t,
+// blockIdx.y selects x (0) or x2 (1): two arrays of one position in one launch
+__global__ __launch_bounds__(256) void k_rope(float* x, float* x2, int64_t ld, int n, int d, int dh, int t,
                                              const double* inv_freq, int sign) {
+  if (blockIdx.y) x = x2;
   const int half = dh / 2;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (int64_t)n * (d / 2)) return;
@@ -559,7 +561,15 @@ void colsum_rows(float* dst, const float* a, int64_t lda, const float* b, int64_
 }
 
 void rope(float* x, int64_t ld, int n, int d, int dh, int t, const double* inv_freq, int sign, hipStream_t s) {
-  if (n > 0) hipLaunchKernelGGL(k_rope, dim3(nblk((int64_t)n * (d / 2))), dim3(256), 0, s, x, ld, n, d, dh, t, inv_freq, sign);
+  if (n > 0)
+    hipLaunchKernelGGL(k_rope, dim3(nblk((int64_t)n * (d / 2))), dim3(256), 0, s, x, x, ld, n, d, dh, t, inv_freq, sign);
+}
+
+void rope2(float* x, float* x2, int64_t ld, int n, int d, int dh, int t, const double* inv_freq, int sign,
+           hipStream_t s) {
+  if (n > 0)
+    hipLaunchKernelGGL(k_rope, dim3(nblk((int64_t)n * (d / 2)), 2), dim3(256), 0, s, x, x2, ld, n, d, dh, t, inv_freq,
+                       sign);
 }
 
 void attn_fwd(const float* q, int64_t ldq, KV kv, int lo, int hi, float* o, int64_t ldo, int n, int H, int dh,

@@ -233,10 +233,7 @@ int replay_backward(const Model& m, const rlt_backward_io* io, const rlt_grads* 
         float* ys[3] = {q, kt, vt};
         mm_outputs(3, n, d, d, hs, d, 1, wt, dt, 1, d, ys, d, false, s);
       }
-      if (rope_on) {
-        rope(q, d, n, d, dh, t, m.inv_freq, 1, s);
-        rope(kt, d, n, d, dh, t, m.inv_freq, 1, s);
-      }
+      if (rope_on) rope2(q, kt, d, n, d, dh, t, m.inv_freq, 1, s);
       attn_fwd(q, d, trace_kv(l), std::max(1, t - W + 1), t, o, d, n, H, dh, s);
       lin_res(n, d, d, o, d, m.wo[l], z, zb, d);
       // cross-attention to M_{<=t} [eq. (2.15)]
@@ -370,10 +367,7 @@ int replay_backward(const Model& m, const rlt_backward_io* io, const rlt_grads* 
       // the current key/value has now received the gradient of every step that read it
       float* dk = kt_at(dKT, l, t);
       float* dv = kt_at(dVT, l, t);
-      if (rope_on) {
-        rope(dqs, d, n, d, dh, t, m.inv_freq, -1, s);
-        rope(dk, d, n, d, dh, t, m.inv_freq, -1, s);
-      }
+      if (rope_on) rope2(dqs, dk, d, n, d, dh, t, m.inv_freq, -1, s);
       float* t2s = at(T2S, l, t);
       {  // t2s = dq W_q + dk W_k + dv W_v, one launch
         const float* dys[3] = {dqs, dk, dv};
